@@ -1,0 +1,116 @@
+"""CPU oracle of the SDM write/read forward. TEST INFRASTRUCTURE, NOT PRODUCT.
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may import or
+run anything here. The product path (chunked_sparse_delta_amd) never does, and this
+package shares no code with it; both take their inputs from ``workloads``.
+
+  O1  token_loop.c      the per-token recurrence in fp64 (the definition)
+  O2  chunk_algebra.py  the chunked three-part form in fp64, for tiny inputs
+
+Pins: tests/test_oracle.py checks O1 against O2 (two independent derivations),
+against closed forms (decay-only, scalar EMA, one-token delta update, overwrite
+under a large negative log-decay, a hand-worked rational example in tests/golden/)
+and against invariants (padding, chunk-size, stream and column independence).
+Parity unpinned: none.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from . import chunk_algebra  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "token_loop.c")
+_LIB = os.path.join(_HERE, "libsdm_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+ERRORS = {-1: "slot id out of range", -2: "write slot repeated within a token",
+          -3: "bad argument", -4: "out of memory"}
+
+
+def build(force: bool = False) -> str:
+    """Compile token_loop.c with gcc into oracle/libsdm_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-o", tmp, _SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            f = lib.sdm_oracle_token_loop
+            i64, p = ctypes.c_int64, ctypes.c_void_p
+            f.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 10
+            f.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def as_f64_inputs(inputs: dict) -> dict:
+    """fp64 copies of a ``workloads.generate`` dict (bank-dtype arrays widened exactly)."""
+    from workloads import to_float
+    dt = inputs["dtype"]
+    return dict(
+        bank=to_float(inputs["bank"], dt),
+        k_idx=np.ascontiguousarray(inputs["k_idx"], dtype=np.int32),
+        k_val=to_float(inputs["k_val"], dt),
+        v=to_float(inputs["v"], dt),
+        beta=np.asarray(inputs["beta"], dtype=np.float64),
+        g=np.asarray(inputs["log_decay"], dtype=np.float64),
+        q_idx=np.ascontiguousarray(inputs["q_idx"], dtype=np.int32),
+        q_val=to_float(inputs["q_val"], dt),
+        valid=np.ascontiguousarray(inputs["valid"], dtype=np.int32),
+    )
+
+
+def token_loop(f64: dict, threads: int = 1, streams=None):
+    """O1 over the streams of fp64 inputs (``as_f64_inputs``). Returns (readings
+    [P, T, hd], final bank [P, M, hd]) in fp64; ``streams`` restricts the work to a
+    subset (the other streams' outputs are left zero / unchanged)."""
+    lib = _load()
+    bank = np.array(f64["bank"], dtype=np.float64, copy=True, order="C")
+    P, M, hd = bank.shape
+    k_idx = np.ascontiguousarray(f64["k_idx"], dtype=np.int32)
+    T, W = k_idx.shape[1], k_idx.shape[2]
+    R = f64["q_idx"].shape[2]
+    g = np.ascontiguousarray(f64["g"], dtype=np.float64)
+    G = g.shape[2]
+    arrs = dict(k_val=np.ascontiguousarray(f64["k_val"], dtype=np.float64),
+                v=np.ascontiguousarray(f64["v"], dtype=np.float64),
+                beta=np.ascontiguousarray(f64["beta"], dtype=np.float64),
+                q_idx=np.ascontiguousarray(f64["q_idx"], dtype=np.int32),
+                q_val=np.ascontiguousarray(f64["q_val"], dtype=np.float64))
+    valid = f64.get("valid")
+    valid = None if valid is None else np.ascontiguousarray(valid, dtype=np.int32)
+    out = np.zeros((P, T, hd), dtype=np.float64)
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+
+    def run(p):
+        rc = lib.sdm_oracle_token_loop(p, p + 1, T, W, R, G, hd, M, ptr(k_idx), ptr(arrs["k_val"]),
+                                       ptr(arrs["v"]), ptr(arrs["beta"]), ptr(g), ptr(arrs["q_idx"]),
+                                       ptr(arrs["q_val"]), ptr(valid), ptr(bank), ptr(out))
+        if rc:
+            raise ValueError(f"oracle: stream {p}: {ERRORS.get(rc, rc)}")
+
+    todo = list(range(P)) if streams is None else [int(p) for p in streams]
+    if threads <= 1:
+        for p in todo:
+            run(p)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, todo))
+    return out, bank

@@ -1,0 +1,112 @@
+/*
+ * Oracle O1: the SDM write/read forward as a token-by-token recurrence, in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU
+ * baseline load this file's library. It shares no code, header or constant with the
+ * HIP path.
+ *
+ * Definition followed: the per-token loop in the SDMWriteRead class docstring of
+ * memory_ops.py (sparse-delta-memory 2.0.0 wheel, diffend page 21). For each token,
+ * each written bank row is first multiplied by the exponential of its log-decay
+ * (only written rows decay); the retrieved vector is the k-weighted sum of those
+ * decayed rows; the write error is beta times (v minus retrieved); each written row
+ * then becomes its decayed value plus its weight times that error; the reading is
+ * the q-weighted sum of the read rows after the write. The chunked form on the
+ * pages reproduces this loop up to floating-point rounding.
+ *
+ * Layout (all row-major, one stream after another):
+ *   k_idx  int32  [P, T, W]   write slots, stream-local rows in [0, M)
+ *   k_val  double [P, T, W]
+ *   v      double [P, T, hd]
+ *   beta   double [P, T]
+ *   g      double [P, T, G]   G = 1 (one log-decay per token) or W (one per write)
+ *   q_idx  int32  [P, T, R]
+ *   q_val  double [P, T, R]
+ *   valid  int32  [P] or NULL (NULL: every token valid). Tokens t >= valid[p] are
+ *          padding: they touch no row and their reading is 0 (the module docstring
+ *          of memory_ops.py: padding is inert and outputs zeros).
+ *   bank   double [P, M, hd]  advanced in place to its final state
+ *   out    double [P, T, hd]  readings
+ *
+ * Streams [p0, p1) are processed; each stream owns its bank [M, hd] (the per-stream
+ * slot ranges of sdm_write_read's num_memory_slots argument).
+ *
+ * Returns 0, or a negative code on a violated caller contract: -1 a slot id out of
+ * range, -2 a write slot repeated within one token (the op requires distinct write
+ * slots per token), -3 a bad argument, -4 out of memory.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+int sdm_oracle_token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
+                          int64_t hd, int64_t M, const int32_t *k_idx, const double *k_val,
+                          const double *v, const double *beta, const double *g,
+                          const int32_t *q_idx, const double *q_val, const int32_t *valid,
+                          double *bank, double *out)
+{
+    if (p0 < 0 || p1 < p0 || T < 0 || W < 1 || R < 1 || hd < 1 || M < 1 || (G != 1 && G != W))
+        return -3;
+    double *retrieved = (double *)malloc(sizeof(double) * (size_t)hd);
+    double *delta = (double *)malloc(sizeof(double) * (size_t)hd);
+    if (!retrieved || !delta) {
+        free(retrieved);
+        free(delta);
+        return -4;
+    }
+    int rc = 0;
+    for (int64_t p = p0; p < p1 && rc == 0; ++p) {
+        double *B = bank + p * M * hd;
+        int64_t nvalid = valid ? valid[p] : T;
+        for (int64_t t = 0; t < T && rc == 0; ++t) {
+            int64_t tok = p * T + t;
+            double *o = out + tok * hd;
+            if (t >= nvalid) {
+                for (int64_t c = 0; c < hd; ++c) o[c] = 0.0;
+                continue;
+            }
+            const int32_t *ks = k_idx + tok * W;
+            const double *kv = k_val + tok * W;
+            const int32_t *qs = q_idx + tok * R;
+            const double *qv = q_val + tok * R;
+            for (int64_t w = 0; w < W; ++w) {
+                if (ks[w] < 0 || ks[w] >= M) { rc = -1; break; }
+                for (int64_t w2 = 0; w2 < w; ++w2)
+                    if (ks[w2] == ks[w]) { rc = -2; break; }
+            }
+            for (int64_t r = 0; r < R && rc == 0; ++r)
+                if (qs[r] < 0 || qs[r] >= M) rc = -1;
+            if (rc) break;
+
+            /* decay the written rows: bank[k] = exp(g) * bank[k] (the "read" rows) */
+            for (int64_t w = 0; w < W; ++w) {
+                double gamma = exp(g[tok * G + (G == 1 ? 0 : w)]);
+                double *row = B + (int64_t)ks[w] * hd;
+                for (int64_t c = 0; c < hd; ++c) row[c] *= gamma;
+            }
+            /* retrieved = sum_w k_w * read_w */
+            for (int64_t c = 0; c < hd; ++c) retrieved[c] = 0.0;
+            for (int64_t w = 0; w < W; ++w) {
+                const double *row = B + (int64_t)ks[w] * hd;
+                for (int64_t c = 0; c < hd; ++c) retrieved[c] += kv[w] * row[c];
+            }
+            /* delta_v = beta * (v - retrieved) */
+            for (int64_t c = 0; c < hd; ++c) delta[c] = beta[tok] * (v[tok * hd + c] - retrieved[c]);
+            /* bank[k] = read + k (x) delta_v */
+            for (int64_t w = 0; w < W; ++w) {
+                double *row = B + (int64_t)ks[w] * hd;
+                for (int64_t c = 0; c < hd; ++c) row[c] += kv[w] * delta[c];
+            }
+            /* reading = sum_r q_r * bank[q_r], after the write */
+            for (int64_t c = 0; c < hd; ++c) o[c] = 0.0;
+            for (int64_t r = 0; r < R; ++r) {
+                const double *row = B + (int64_t)qs[r] * hd;
+                for (int64_t c = 0; c < hd; ++c) o[c] += qv[r] * row[c];
+            }
+        }
+    }
+    free(retrieved);
+    free(delta);
+    return rc;
+}
