@@ -1,0 +1,212 @@
+"""Benchmark of the SDM forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu-baseline]
+
+A step is one sdm_fwd call over the whole workload (every chunk step of every stream)
+with all inputs resident in HBM. The bank is advanced in place from step to step, as a
+caller carrying the memory across calls would; the kernels are data-oblivious, so the
+timing equals that of a restored bank. Prints one JSON line: tokens/s, the per-kernel
+breakdown from HIP events recorded by the library on its stream, the roofline of the
+dominant kernel, and the CPU oracle's throughput on the host as a reference.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, datasheet
+KERNELS = ("p1_sort", "p1_groups", "p1_reads", "p1_gram", "wy_solve", "phase2")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="1", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def chunk_stats(inp: dict, wl) -> dict:
+    """Exact distinct-row counts per live chunk: U (rows read: write or read slots) and
+    U_w (rows written), summed over chunks, plus live token rows."""
+    P, T, C, M = wl.P, wl.T, wl.C, wl.M
+    valid = np.asarray(inp["valid"], dtype=np.int64)
+    U = Uw = live = 0
+    for p in range(P):
+        nv = int(valid[p])
+        if nv == 0:
+            continue
+        tok_chunk = (np.arange(nv) // C).astype(np.int64)
+        kw = inp["k_idx"][p, :nv].astype(np.int64)
+        kr = inp["q_idx"][p, :nv].astype(np.int64)
+        wkeys = (tok_chunk[:, None] * M + kw).ravel()
+        rkeys = (tok_chunk[:, None] * M + kr).ravel()
+        uw = np.unique(wkeys)
+        Uw += uw.size
+        U += np.union1d(uw, np.unique(rkeys)).size
+        live += nv
+    return dict(U=int(U), Uw=int(Uw), live_tokens=int(live))
+
+
+def hip_runtime():
+    """The HIP runtime already loaded by torch (one runtime per process)."""
+    maps = open("/proc/self/maps").read()
+    paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so[.\d]*)", maps)))
+    lib = ctypes.CDLL(paths[0] if paths else "libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def to_torch(inp: dict, device) -> dict:
+    import torch
+    dt = inp["dtype"]
+
+    def bank_dtype(a):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    return dict(bank=bank_dtype(inp["bank"]), k_idx=torch.from_numpy(inp["k_idx"]).to(device),
+                q_idx=torch.from_numpy(inp["q_idx"]).to(device), k_val=bank_dtype(inp["k_val"]),
+                q_val=bank_dtype(inp["q_val"]), v=bank_dtype(inp["v"]), beta=torch.from_numpy(inp["beta"]).to(device),
+                log_decay=torch.from_numpy(inp["log_decay"]).to(device),
+                valid=torch.from_numpy(np.ascontiguousarray(inp["valid"], dtype=np.int32)).to(device))
+
+
+def cpu_baseline(inp: dict, wl, seconds: float) -> dict:
+    import oracle
+    f = oracle.as_f64_inputs(inp)
+    threads = max(1, min(wl.P, os.cpu_count() or 1, 16))
+    tokens = int(np.sum(inp["valid"]))
+    oracle.token_loop(f, threads=threads)      # build / warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.token_loop(f, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": reps * tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({wl.P} streams, {tokens} valid tokens) x {reps} passes of the fp64 "
+                      f"token loop, {threads} threads, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU (the forward shards with no exchange across "
+              "streams or columns, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from chunked_sparse_delta_amd import TIMING_EVENTS, sdm_fwd, workspace_bytes
+
+    wl = workloads.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"bench: generating workload {workloads.workload_name(wl)}", file=sys.stderr, flush=True)
+    inp = workloads.generate(wl)
+    stats = chunk_stats(inp, wl)
+    t = to_torch(inp, dev)
+    es = 4 if wl.dtype == "f32" else 2
+    torch.cuda.synchronize()
+
+    ws = torch.empty(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0), dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.P, wl.T, wl.hd), dtype=t["bank"].dtype, device=dev)
+    bank = t["bank"]
+    hip = hip_runtime()
+    nev = TIMING_EVENTS
+    ev_sets = []
+    for _ in range(args.steps):
+        arr = (ctypes.c_void_p * nev)()
+        for k in range(nev):
+            ev = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[k] = ev.value
+        ev_sets.append(arr)
+
+    def step(events=None):
+        sdm_fwd(bank, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
+                chunk=wl.C, valid_tokens=t["valid"], out=out, workspace=ws, events=events)
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev_sets[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per = np.zeros((args.steps, nev - 1))
+    for k, arr in enumerate(ev_sets):
+        for j in range(nev - 1):
+            ms = ctypes.c_float()
+            hip.hipEventElapsedTime(ctypes.byref(ms), arr[j], arr[j + 1])
+            per[k, j] = ms.value
+        for j in range(nev):
+            hip.hipEventDestroy(arr[j])
+    kern_ms = dict(zip(KERNELS, per.mean(axis=0).round(5).tolist()))
+
+    tokens = stats["live_tokens"]
+    ms_step = 1000.0 * elapsed / args.steps
+    value = tokens * args.steps / elapsed
+    row = es * wl.hd
+    p2_bytes = row * (stats["U"] + stats["Uw"]) + row * tokens + row * wl.P * wl.T
+    entry_bytes = tokens * (wl.W * (4 + es + 4) + wl.R * (4 + es) + 4)
+    path_bytes = p2_bytes + entry_bytes
+    dom = max(kern_ms, key=kern_ms.get)
+    if dom == "phase2":
+        achieved = p2_bytes / (kern_ms["phase2"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "phase2", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": int(p2_bytes)}
+    else:
+        roof = {"bound": "alu", "kernel": dom, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None, "note": "dominant kernel is a Phase-1 kernel; see kernel_ms"}
+    path_gbs = path_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": "SDM fwd tokens/sec at 1 MI355X; achieved HBM GB/s fraction of peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": workloads.workload_name(wl), "streams": wl.P, "tokens": wl.T, "chunk": wl.C,
+                   "head_dim": wl.hd, "rows_per_stream": wl.M, "bank_dtype": wl.dtype, "W": wl.W, "R": wl.R,
+                   "valid_tokens": tokens, "distinct_rows_read": stats["U"], "rows_written": stats["Uw"]},
+        "kernel_ms": kern_ms,
+        "roofline": roof,
+        "path_hbm": {"algorithmic_bytes": int(path_bytes), "achieved": round(path_gbs, 1), "unit": "GB/s",
+                     "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        sample = inp
+        if wl.name in ("2", "3", "4", "4p"):
+            keep = [0]
+            sample = workloads.generate(wl.name == "4" and workloads.CONFIGS["4p"] or wl, streams=keep)
+        res["cpu_baseline"] = cpu_baseline(sample, wl.replace(P=len(sample["valid"])), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,246 @@
+"""MI355X-native forward of the chunked sparse-delta-memory write/read op.
+
+A thin ctypes binding of libsdm.so (include/sdm.h). This module marshals torch tensors
+into the C ABI: it checks that shapes, dtypes and devices agree (so that the library's
+pointer arguments describe the tensors it is handed), allocates the output and the
+workspace with torch, and passes the current HIP stream. Every step of the computation
+runs in the library's HIP kernels; there is no other path. If libsdm.so is missing or
+cannot be loaded, every call raises.
+
+    out = sdm_fwd(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, chunk=64)
+
+mirrors sdm_write_read's no-grad forward (memory_ops.py, sparse-delta-memory 2.0.0
+wheel, diffend page 21) with per-stream banks: bank [P, M, hd] is advanced in place and
+the readings [P, T, hd] are returned.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "workspace_bytes", "library_path",
+           "SDM_ERRORS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("SDM_LIBRARY", os.path.join(_HERE, "libsdm.so"))
+
+SDM_ERRORS = {0: "SDM_OK", -1: "SDM_ERR_DTYPE", -2: "SDM_ERR_SHAPE", -3: "SDM_ERR_RANGE", -4: "SDM_ERR_NULL",
+              -5: "SDM_ERR_ALIGN", -6: "SDM_ERR_WORKSPACE", -7: "SDM_ERR_UNSUPPORTED", -8: "SDM_ERR_HIP"}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class SdmError(RuntimeError):
+    """A negative return code of libsdm; ``code`` holds it, the message holds sdm_last_error()."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{SDM_ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Slots(ctypes.Structure):
+    _fields_ = [("write", ctypes.c_void_p), ("read", ctypes.c_void_p), ("W", ctypes.c_int32), ("R", ctypes.c_int32)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("write", ctypes.c_void_p), ("read", ctypes.c_void_p)]
+
+
+class _Bank(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int64), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class _Exec(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("events", ctypes.c_void_p), ("num_events", ctypes.c_int32)]
+
+
+TIMING_EVENTS = 7   # SDM_TIMING_EVENTS
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(f"libsdm.so not found at {_LIB_PATH}: build it first "
+                                   "(python -m chunked_sparse_delta_amd.build)")
+            lib = ctypes.CDLL(_LIB_PATH)
+            i32, i64, p, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+            lib.sdm_fwd_workspace_bytes.argtypes = [i32] * 7
+            lib.sdm_fwd_workspace_bytes.restype = sz
+            lib.sdm_fwd.argtypes = [i32, i32, i32, p, p, p, p, i32, p, p, p, p, p]
+            lib.sdm_fwd.restype = ctypes.c_int
+            lib.sdm_chunk_mats.argtypes = [i32, i32, i32, p, p, p, p, i32, i64, i32, i32, p, p, p, p, p, p, p, p]
+            lib.sdm_chunk_mats.restype = ctypes.c_int
+            lib.sdm_wy_solve.argtypes = [i64, i32, p, p, p, p, p, p]
+            lib.sdm_wy_solve.restype = ctypes.c_int
+            lib.sdm_error_string.argtypes = [ctypes.c_int]
+            lib.sdm_error_string.restype = ctypes.c_char_p
+            lib.sdm_last_error.argtypes = []
+            lib.sdm_last_error.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _check_rc(lib, rc: int) -> None:
+    if rc != 0:
+        raise SdmError(rc, lib.sdm_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the bank on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(P: int, T: int, C: int, W: int, R: int, hd: int, slab_steps: int = 0) -> int:
+    """Bytes of scratch sdm_fwd needs for slabs of ``slab_steps`` steps (0: all steps)."""
+    return int(_load().sdm_fwd_workspace_bytes(P, T, C, W, R, hd, slab_steps))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes.
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("workspace allocation is not 256-byte aligned")
+    return ws
+
+
+DEFAULT_WORKSPACE_CAP = 8 << 30
+
+
+def _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, valid_tokens):
+    if bank.dtype not in _DTYPES:
+        raise TypeError(f"bank must be float32 or bfloat16, got {bank.dtype}")
+    if bank.dim() != 3:
+        raise ValueError(f"bank must be [P, M, head_dim], got shape {tuple(bank.shape)}")
+    if k_idx.dim() != 3 or q_idx.dim() != 3:
+        raise ValueError("k_idx and q_idx must be [P, T, W] and [P, T, R]")
+    P, M, hd = bank.shape
+    T, W = k_idx.shape[1], k_idx.shape[2]
+    R = q_idx.shape[2]
+    G = log_decay.shape[-1] if log_decay.dim() == 3 else -1
+    dev = bank.device
+    if dev.type != "cuda":
+        raise ValueError("bank must be a GPU tensor")
+    _expect(bank, "bank", (P, M, hd), bank.dtype, dev)
+    _expect(k_idx, "k_idx", (P, T, W), torch.int32, dev)
+    _expect(q_idx, "q_idx", (P, T, R), torch.int32, dev)
+    _expect(k_val, "k_val", (P, T, W), bank.dtype, dev)
+    _expect(q_val, "q_val", (P, T, R), bank.dtype, dev)
+    _expect(v, "v", (P, T, hd), bank.dtype, dev)
+    _expect(beta, "beta", (P, T), torch.float32, dev)
+    _expect(log_decay, "log_decay", (P, T, G), torch.float32, dev)
+    if valid_tokens is not None:
+        _expect(valid_tokens, "valid_tokens", (P,), torch.int32, dev)
+    slots = _Slots(k_idx.data_ptr(), q_idx.data_ptr(), W, R)
+    weights = _Weights(k_val.data_ptr(), q_val.data_ptr())
+    return P, M, hd, T, W, R, G, slots, weights
+
+
+def sdm_fwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+            log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, *, chunk: int = 64,
+            valid_tokens: torch.Tensor | None = None, out: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None, max_workspace_bytes: int = DEFAULT_WORKSPACE_CAP,
+            stream=None, events=None) -> torch.Tensor:
+    """SDM forward on the GPU. Returns the readings [P, T, hd] (bank dtype); ``bank``
+    [P, M, hd] is advanced in place. ``valid_tokens`` (int32 [P], on the GPU) marks the
+    tokens at and past each stream's end as padding. ``workspace`` (uint8, GPU) is used if
+    given, else one of at most ``max_workspace_bytes`` (at least one step) is allocated.
+    ``events``: optional ctypes array of TIMING_EVENTS hipEvent_t handles recorded at the
+    kernel boundaries of the first slab (see sdm_exec in include/sdm.h)."""
+    lib = _load()
+    P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
+                                                   valid_tokens)
+    if out is None:
+        out = torch.empty((P, T, hd), dtype=bank.dtype, device=bank.device)
+    else:
+        _expect(out, "out", (P, T, hd), bank.dtype, bank.device)
+    if workspace is None:
+        need_all = workspace_bytes(P, T, chunk, W, R, hd, 0)
+        need_one = workspace_bytes(P, T, chunk, W, R, hd, 1)
+        nbytes = need_all if need_all <= max_workspace_bytes else max(need_one,
+                                                                      max_workspace_bytes // need_one * need_one)
+        workspace = _workspace(nbytes, bank.device)
+    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype])
+    ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+               None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events))
+    rc = lib.sdm_fwd(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
+                     _ptr(v), ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
+    _check_rc(lib, rc)
+    return out
+
+
+def chunk_mats(k_idx, k_val, beta, log_decay, q_idx, q_val, *, rows: int, head_dim: int, chunk: int,
+               valid_tokens=None, stream=None) -> dict:
+    """Phase-1 and solve intermediates of every chunk (chunk n = p * Nt + ti): A, QK, X,
+    QX float32 [P * Nt, C, C]; gw [P * Nt, C, W]; gr [P * Nt, C, R]."""
+    lib = _load()
+    if k_val.dtype not in _DTYPES:
+        raise TypeError(f"k_val must be float32 or bfloat16, got {k_val.dtype}")
+    P, T, W = k_idx.shape
+    R = q_idx.shape[2]
+    dev = k_idx.device
+    dummy = torch.empty((P, 1, head_dim), dtype=k_val.dtype, device=dev)
+    _, _, _, _, W, R, G, slots, weights = _inputs(dummy, k_idx, k_val, torch.empty((P, T, head_dim),
+                                                  dtype=k_val.dtype, device=dev), beta, log_decay, q_idx, q_val,
+                                                  valid_tokens)
+    Nt = -(-T // chunk)
+    N = P * Nt
+    f = dict(dtype=torch.float32, device=dev)
+    res = dict(A=torch.empty((N, chunk, chunk), **f), QK=torch.empty((N, chunk, chunk), **f),
+               X=torch.empty((N, chunk, chunk), **f), QX=torch.empty((N, chunk, chunk), **f),
+               gw=torch.empty((N, chunk, W), **f), gr=torch.empty((N, chunk, R), **f))
+    ws = _workspace(workspace_bytes(P, T, chunk, W, R, head_dim, 1), dev)
+    ex = _Exec(_stream_ptr(stream), ws.data_ptr(), ws.numel(), None, 0)
+    rc = lib.sdm_chunk_mats(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
+                            rows, head_dim, _DTYPES[k_val.dtype], _ptr(valid_tokens), _ptr(res["A"]), _ptr(res["QK"]),
+                            _ptr(res["X"]), _ptr(res["QX"]), _ptr(res["gw"]), _ptr(res["gr"]), ctypes.byref(ex))
+    _check_rc(lib, rc)
+    return res
+
+
+def wy_solve(A: torch.Tensor, beta: torch.Tensor, QK: torch.Tensor, stream=None):
+    """X = (I + tril(beta[:, None] * A, -1))^-1 and QX = QK @ X per chunk (A, QK [n, C, C]
+    float32, beta [n, C] float32, all on the GPU)."""
+    lib = _load()
+    if A.dim() != 3 or A.shape[1] != A.shape[2] or QK.shape != A.shape:
+        raise ValueError(f"A and QK must be [n, C, C], got {tuple(A.shape)} and {tuple(QK.shape)}")
+    n, C, _ = A.shape
+    for t, name, shape in ((A, "A", (n, C, C)), (QK, "QK", (n, C, C)), (beta, "beta", (n, C))):
+        _expect(t, name, shape, torch.float32, A.device)
+    X = torch.empty_like(A)
+    QX = torch.empty_like(A)
+    ex = _Exec(_stream_ptr(stream), None, 0, None, 0)
+    rc = lib.sdm_wy_solve(n, C, _ptr(A), _ptr(beta), _ptr(QK), _ptr(X), _ptr(QX), ctypes.byref(ex))
+    _check_rc(lib, rc)
+    return X, QX

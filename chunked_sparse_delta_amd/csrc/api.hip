@@ -1,0 +1,328 @@
+// C ABI of the SDM forward (include/sdm.h): argument checks on the host, slab planning
+// from shapes only, and the launch sequence per slab:
+//     Phase 1 (sort, groups, reads, Gram) -> solve -> Phase 2 (all steps of the slab).
+// Everything is enqueued on the caller's stream; nothing is allocated, nothing synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/sdm.h"
+#include "common.h"
+
+namespace sdm {
+hipError_t phase1_prepare();
+hipError_t phase2_prepare();
+hipError_t wy_prepare();
+hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev);
+hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
+                     int64_t stride, int64_t bstride, hipStream_t st);
+hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, int nv, hipStream_t st);
+size_t gram_lds_bytes(int C);
+size_t phase2_lds_bytes(int C, int nv, int V);
+}  // namespace sdm
+
+using namespace sdm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(SDM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Per-device one-time setup: the large-LDS kernel attributes and the LDS limit.
+struct DeviceInfo {
+    bool ready = false;
+    int lds_per_block = 0;
+};
+DeviceInfo g_dev[64];
+std::mutex g_dev_mu;
+
+int device_info(DeviceInfo **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(SDM_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.ready) {
+        if ((e = hipDeviceGetAttribute(&d.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess)
+            return hip_fail(e, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock)");
+        if ((e = phase1_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 1)");
+        if ((e = phase2_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 2)");
+        if ((e = wy_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (solve)");
+        d.ready = true;
+    }
+    *out = &d;
+    return SDM_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int sort_passes(int64_t M) {
+    int bits = 0;
+    for (int64_t m = M - 1; m > 0; m >>= 1) ++bits;
+    int passes = (bits + 7) / 8;
+    return passes < 1 ? 1 : passes;
+}
+
+struct Checked {
+    Problem pb;
+    ChunkLayout lay;
+    int V;       // elements per vector move (16 B, or 1)
+    int es;      // bank element bytes
+};
+
+// Shape checks shared by sdm_fwd, sdm_chunk_mats and the workspace query.
+int check_shape(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t hd) {
+    if (P < 1 || T < 1) return fail(SDM_ERR_SHAPE, "need streams >= 1 and tokens >= 1, got %d and %d", P, T);
+    if (C < 16 || C > kMaxChunk) return fail(SDM_ERR_RANGE, "chunk must be in 16..256, got %d", C);
+    if (W < 1 || W > kMaxWidth || R < 1 || R > kMaxWidth)
+        return fail(SDM_ERR_SHAPE, "need 1..256 write and read slots per token, got W=%d R=%d", W, R);
+    if (hd < 1) return fail(SDM_ERR_SHAPE, "head_dim must be >= 1, got %d", hd);
+    if (hd > (1 << 20)) return fail(SDM_ERR_RANGE, "head_dim %d is above 2^20", hd);
+    const int64_t Nt = (int64_t(T) + C - 1) / C;
+    if (int64_t(P) * Nt * C >= (int64_t(1) << 31))
+        return fail(SDM_ERR_RANGE, "%d streams of %d tokens padded to chunks of %d exceed 2^31 - 1 token rows", P, T, C);
+    return SDM_OK;
+}
+
+int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
+               const float *g, int32_t G, const void *v, int64_t M, int32_t hd, int32_t dtype, void *bank_data,
+               const int32_t *valid, void *out, bool need_bank, Checked *ck) {
+    if (!slots || !weights) return fail(SDM_ERR_NULL, "slots and weights must not be NULL");
+    int rc = check_shape(P, T, C, slots->W, slots->R, hd);
+    if (rc) return rc;
+    if (dtype != SDM_F32 && dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "bank dtype must be SDM_F32 or SDM_BF16, got %d", dtype);
+    const int W = slots->W, R = slots->R;
+    if (G != 1 && G != W) return fail(SDM_ERR_SHAPE, "log_decay must hold 1 or W=%d gates per token, got %d", W, G);
+    if (M < 1) return fail(SDM_ERR_SHAPE, "the bank needs at least one row per stream, got %lld", (long long)M);
+    if (int64_t(P) * M >= (int64_t(1) << 31))
+        return fail(SDM_ERR_RANGE, "%d streams of %lld rows: the bank has 2^31 or more slots", P, (long long)M);
+    if (!slots->write || !slots->read || !weights->write || !weights->read || !beta || !g)
+        return fail(SDM_ERR_NULL, "slot ids, weights, beta and log_decay must not be NULL");
+    if (need_bank && (!v || !bank_data || !out)) return fail(SDM_ERR_NULL, "v, bank and out must not be NULL");
+    const int es = dtype == SDM_F32 ? 4 : 2;
+    const void *ptr4[] = {slots->write, slots->read, beta, g, valid};
+    for (const void *q : ptr4)
+        if (q && !aligned(q, 4)) return fail(SDM_ERR_ALIGN, "int32/float32 arrays must be 4-byte aligned");
+    const void *ptre[] = {weights->write, weights->read, v, bank_data, out};
+    for (const void *q : ptre)
+        if (q && !aligned(q, size_t(es))) return fail(SDM_ERR_ALIGN, "bank-dtype arrays must be %d-byte aligned", es);
+    if (need_bank) {
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank_data), b1 = b0 + uintptr_t(P) * M * hd * es;
+        const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + uintptr_t(P) * T * hd * es;
+        if (o0 < b1 && b0 < o1) return fail(SDM_ERR_SHAPE, "out overlaps the bank");
+    }
+    const int vec = 16 / es;
+    int V = 1;
+    if (hd % vec == 0 && (!need_bank || (aligned(v, 16) && aligned(bank_data, 16) && aligned(out, 16)))) V = vec;
+    Problem pb{};
+    pb.P = P; pb.T = T; pb.C = C; pb.Nt = int32_t((int64_t(T) + C - 1) / C); pb.W = W; pb.R = R; pb.G = G; pb.hd = hd;
+    pb.M = M; pb.dtype = dtype; pb.sort_passes = sort_passes(M);
+    pb.k_idx = slots->write; pb.q_idx = slots->read; pb.k_val = weights->write; pb.q_val = weights->read;
+    pb.beta = beta; pb.g = g; pb.v = v; pb.valid = valid; pb.bank = bank_data; pb.out = out;
+    ck->pb = pb;
+    ck->lay = make_layout(C, W, R);
+    ck->V = V;
+    ck->es = es;
+    return SDM_OK;
+}
+
+// Vectors per column slice: 128-byte slices where that leaves enough workgroups to fill
+// the chip (about two per CU), narrower otherwise; bounded by LDS.
+int pick_nv(const Problem &pb, int V, int es, int lds_limit) {
+    const int hv = pb.hd / V;
+    int nv = (128 / (V * es)) < 1 ? 1 : 128 / (V * es);
+    if (nv > hv) nv = hv;
+    const int64_t target = 512;
+    while (nv > 1 && int64_t(pb.P) * ((hv + nv - 1) / nv) < target) nv >>= 1;
+    while (nv > 1 && phase2_lds_bytes(pb.C, nv, V) > size_t(lds_limit)) nv >>= 1;
+    return nv < 1 ? 1 : nv;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sdm_error_string(int code) {
+    switch (code) {
+        case SDM_OK: return "success";
+        case SDM_ERR_DTYPE: return "unsupported dtype";
+        case SDM_ERR_SHAPE: return "invalid shape";
+        case SDM_ERR_RANGE: return "size out of range";
+        case SDM_ERR_NULL: return "null pointer";
+        case SDM_ERR_ALIGN: return "misaligned pointer";
+        case SDM_ERR_WORKSPACE: return "workspace missing or too small";
+        case SDM_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SDM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown error";
+    }
+}
+
+const char *sdm_last_error(void) { return g_err; }
+
+size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t hd, int32_t slab_steps) {
+    if (check_shape(P, T, C, W, R, hd) != SDM_OK) return 0;
+    const int32_t Nt = int32_t((int64_t(T) + C - 1) / C);
+    if (slab_steps <= 0 || slab_steps > Nt) slab_steps = Nt;
+    const ChunkLayout lay = make_layout(C, W, R);
+    return size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
+}
+
+int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
+            const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank, const int32_t *valid_tokens,
+            void *out, const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!bank || !exec) return fail(SDM_ERR_NULL, "bank and exec must not be NULL");
+    Checked ck;
+    int rc = check_call(P, T, C, slots, weights, beta, log_decay, gate_width, v, bank->rows, bank->head_dim, bank->dtype,
+                        bank->data, valid_tokens, out, true, &ck);
+    if (rc) return rc;
+    const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
+    if (!exec->workspace || exec->workspace_bytes < per_step)
+        return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
+                    exec->workspace ? exec->workspace_bytes : size_t(0), per_step);
+    if (!aligned(exec->workspace, 256)) return fail(SDM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    DeviceInfo *dev = nullptr;
+    if ((rc = device_info(&dev)) != SDM_OK) return rc;
+    if (gram_lds_bytes(C) > size_t(dev->lds_per_block))
+        return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
+                    gram_lds_bytes(C), dev->lds_per_block);
+    const int nv = pick_nv(ck.pb, ck.V, ck.es, dev->lds_per_block);
+    if (phase2_lds_bytes(C, nv, ck.V) > size_t(dev->lds_per_block))
+        return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs more LDS than the device has", C);
+    const int32_t Nt = ck.pb.Nt;
+    int32_t slab = int32_t(exec->workspace_bytes / per_step);
+    if (slab > Nt) slab = Nt;
+    hipStream_t st = static_cast<hipStream_t>(exec->stream);
+    hipEvent_t *ev = nullptr;
+    if (exec->events && exec->num_events >= SDM_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
+    for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
+        Slab sl{};
+        sl.ti0 = ti0;
+        sl.steps = Nt - ti0 < slab ? Nt - ti0 : slab;
+        sl.ws = static_cast<uint32_t *>(exec->workspace);
+        sl.lay = ck.lay;
+        hipEvent_t *sev = ti0 == 0 ? ev : nullptr;
+        hipError_t e = launch_phase1(ck.pb, sl, st, sev);
+        if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
+        if (sev && (e = hipEventRecord(sev[4], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        float *w = reinterpret_cast<float *>(sl.ws);
+        e = launch_wy(w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X, w + sl.lay.off_QX, C,
+                      int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
+        if (e != hipSuccess) return hip_fail(e, "solve launch");
+        if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        e = launch_phase2(ck.pb, sl, ck.V, nv, st);
+        if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
+        if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    return SDM_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Intermediates out (sdm_chunk_mats)
+// ---------------------------------------------------------------------------------------
+namespace sdm {
+struct MatsOut {
+    float *A, *QK, *X, *QX, *gw, *gr;
+};
+
+__global__ void copy_mats_kernel(Slab sl, int32_t P, int32_t Nt, MatsOut o) {
+    const int64_t n = blockIdx.y;
+    const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
+    const int64_t dst = int64_t(p) * Nt + ti;
+    const ChunkLayout &L = sl.lay;
+    const float *cb = reinterpret_cast<const float *>(sl.chunk(n));
+    for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < L.C2; k += int64_t(gridDim.x) * blockDim.x) {
+        o.A[dst * L.C2 + k] = cb[L.off_A + k];
+        o.QK[dst * L.C2 + k] = cb[L.off_QK + k];
+        o.X[dst * L.C2 + k] = cb[L.off_X + k];
+        o.QX[dst * L.C2 + k] = cb[L.off_QX + k];
+    }
+    for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < L.E; k += int64_t(gridDim.x) * blockDim.x)
+        o.gw[dst * L.E + k] = cb[L.off_gw + k];
+    for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < L.F; k += int64_t(gridDim.x) * blockDim.x)
+        o.gr[dst * L.F + k] = cb[L.off_gr + k];
+}
+}  // namespace sdm
+
+extern "C" {
+
+int sdm_chunk_mats(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
+                   const float *log_decay, int32_t gate_width, int64_t rows, int32_t head_dim, int32_t dtype,
+                   const int32_t *valid_tokens, float *A, float *QK, float *X, float *QX, float *gw, float *gr,
+                   const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!exec) return fail(SDM_ERR_NULL, "exec must not be NULL");
+    if (!A || !QK || !X || !QX || !gw || !gr) return fail(SDM_ERR_NULL, "output arrays must not be NULL");
+    Checked ck;
+    int rc = check_call(P, T, C, slots, weights, beta, log_decay, gate_width, nullptr, rows, head_dim, dtype, nullptr,
+                        valid_tokens, nullptr, false, &ck);
+    if (rc) return rc;
+    const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
+    if (!exec->workspace || exec->workspace_bytes < per_step)
+        return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
+                    exec->workspace ? exec->workspace_bytes : size_t(0), per_step);
+    if (!aligned(exec->workspace, 256)) return fail(SDM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    DeviceInfo *dev = nullptr;
+    if ((rc = device_info(&dev)) != SDM_OK) return rc;
+    const int32_t Nt = ck.pb.Nt;
+    int32_t slab = int32_t(exec->workspace_bytes / per_step);
+    if (slab > Nt) slab = Nt;
+    hipStream_t st = static_cast<hipStream_t>(exec->stream);
+    MatsOut o{A, QK, X, QX, gw, gr};
+    for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
+        Slab sl{};
+        sl.ti0 = ti0;
+        sl.steps = Nt - ti0 < slab ? Nt - ti0 : slab;
+        sl.ws = static_cast<uint32_t *>(exec->workspace);
+        sl.lay = ck.lay;
+        hipError_t e = launch_phase1(ck.pb, sl, st, nullptr);
+        if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
+        float *w = reinterpret_cast<float *>(sl.ws);
+        e = launch_wy(w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X, w + sl.lay.off_QX, C,
+                      int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
+        if (e != hipSuccess) return hip_fail(e, "solve launch");
+        hipLaunchKernelGGL(copy_mats_kernel, dim3(64, unsigned(int64_t(P) * sl.steps)), dim3(256), 0, st, sl, P, Nt, o);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "copy launch");
+    }
+    return SDM_OK;
+}
+
+int sdm_wy_solve(int64_t n, int32_t C, const float *A, const float *beta, const float *QK, float *X, float *QX,
+                 const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!exec) return fail(SDM_ERR_NULL, "exec must not be NULL");
+    if (n < 0) return fail(SDM_ERR_SHAPE, "chunk count must be >= 0, got %lld", (long long)n);
+    if (C < 1 || C > kMaxChunk) return fail(SDM_ERR_RANGE, "chunk must be in 1..256, got %d", C);
+    if (n == 0) return SDM_OK;
+    if (!A || !beta || !QK || !X || !QX) return fail(SDM_ERR_NULL, "A, beta, QK, X and QX must not be NULL");
+    const void *ps[] = {A, beta, QK, X, QX};
+    for (const void *q : ps)
+        if (!aligned(q, 4)) return fail(SDM_ERR_ALIGN, "float32 arrays must be 4-byte aligned");
+    if (n > int64_t(0x7fffffff)) return fail(SDM_ERR_RANGE, "too many chunks (%lld)", (long long)n);
+    DeviceInfo *dev = nullptr;
+    int rc = device_info(&dev);
+    if (rc != SDM_OK) return rc;
+    const int64_t C2 = int64_t(C) * C;
+    hipError_t e = launch_wy(A, beta, QK, X, QX, C, n, C2, C, static_cast<hipStream_t>(exec->stream));
+    if (e != hipSuccess) return hip_fail(e, "solve launch");
+    return SDM_OK;
+}
+
+}  // extern "C"

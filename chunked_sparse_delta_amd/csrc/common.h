@@ -1,0 +1,179 @@
+// Internal definitions shared by the SDM kernels and the C-ABI host code (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm {
+
+constexpr int kWave = 64;          // CDNA4 wavefront
+constexpr int kMaxChunk = 256;
+constexpr int kMaxWidth = 256;
+constexpr int kXcds = 8;           // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
+
+// ---------------------------------------------------------------------------------------
+// Element types. bf16 is carried as its 16-bit pattern.
+// ---------------------------------------------------------------------------------------
+struct bf16 {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    bf16 r;
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
+        r.bits = uint16_t((u >> 16) | 0x40u);
+    } else {
+        r.bits = uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
+    return r;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32_to_bf16(x); }
+
+// A vector of V elements of T moved as one load/store (V * sizeof(T) is 16 B on the
+// vector path, or one element on the scalar path for rows that are not 16 B multiples).
+template <typename T, int V> struct Vec;
+
+template <> struct Vec<float, 4> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[4]) {
+        float4 x = *reinterpret_cast<const float4 *>(p);
+        o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&o)[4]) {
+        *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+};
+template <> struct Vec<bf16, 8> {
+    static __device__ __forceinline__ void load(const bf16 *p, float (&o)[8]) {
+        uint4 x = *reinterpret_cast<const uint4 *>(p);
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(bf16 *p, const float (&o)[8]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = uint32_t(f32_to_bf16(o[2 * i]).bits) | (uint32_t(f32_to_bf16(o[2 * i + 1]).bits) << 16);
+        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+template <typename T> struct Vec<T, 1> {
+    static __device__ __forceinline__ void load(const T *p, float (&o)[1]) { o[0] = to_f32(*p); }
+    static __device__ __forceinline__ void store(T *p, const float (&o)[1]) { *p = from_f32<T>(o[0]); }
+};
+
+// ---------------------------------------------------------------------------------------
+// Problem description passed by value to every kernel.
+// ---------------------------------------------------------------------------------------
+struct Problem {
+    int32_t P, T, C, Nt, W, R, G, hd;
+    int64_t M;
+    int32_t dtype;           // 0 f32, 1 bf16
+    int32_t sort_passes;     // 8-bit LSD radix passes over the slot id
+    const int32_t *k_idx;    // [P, T, W]
+    const int32_t *q_idx;    // [P, T, R]
+    const void *k_val;       // [P, T, W] bank dtype
+    const void *q_val;       // [P, T, R] bank dtype
+    const float *beta;       // [P, T]
+    const float *g;          // [P, T, G]
+    const void *v;           // [P, T, hd]
+    const int32_t *valid;    // [P] or nullptr
+    void *bank;              // [P, M, hd]
+    void *out;               // [P, T, hd]
+};
+
+__device__ __forceinline__ int32_t n_live_tokens(const Problem &pb, int p, int ti) {
+    int32_t vt = pb.valid ? pb.valid[p] : pb.T;
+    vt = vt < 0 ? 0 : (vt > pb.T ? pb.T : vt);
+    int32_t n = vt - ti * pb.C;
+    return n < 0 ? 0 : (n > pb.C ? pb.C : n);
+}
+
+__device__ __forceinline__ float load_weight(const void *base, int64_t i, int32_t dtype) {
+    return dtype == 0 ? static_cast<const float *>(base)[i] : to_f32(static_cast<const bf16 *>(base)[i]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Workspace of one slab: `nchunks` chunks, chunk n = p * slab_steps + (ti - ti0).
+// Every array is 256-byte aligned. E = C * W write entries, F = C * R read entries.
+// ---------------------------------------------------------------------------------------
+struct ChunkLayout {
+    int64_t E, F, C2;
+    // per-chunk strides (elements)
+    int64_t off_key0, off_val0, off_key1, off_val1;   // radix-sort double buffer (u32)
+    int64_t off_spos;     // [E] i32: sorted position of write entry e
+    int64_t off_stok;     // [E] i32: token of sorted position
+    int64_t off_sL;       // [E] f32: cumulative log-decay at sorted position
+    int64_t off_shead;    // [E] i32: first sorted position of the group
+    int64_t off_scw;      // [E] f32: DW coefficient k exp(L_last - L)
+    int64_t off_sk;       // [E] f32: k at sorted position
+    int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
+    int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
+    int64_t off_rpos;     // [F] i32: sorted position of the latest write of the read slot, or -1
+    int64_t off_rL;       // [F] f32: that write's cumulative log-decay (0 if none)
+    int64_t off_gpos;     // [E+1] i32: group start positions
+    int64_t off_gslot;    // [E] i32: group slot
+    int64_t off_gdecay;   // [E] f32: exp(L_last)
+    int64_t off_meta;     // [4] i32: n_live, E_live, ngroups, pad
+    int64_t off_beta;     // [C] f32: beta (0 for padding)
+    int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
+    int64_t words;        // 4-byte words per chunk
+};
+
+inline int64_t align_words(int64_t w) { return (w + 63) & ~int64_t(63); }   // 256 B
+
+inline ChunkLayout make_layout(int C, int W, int R) {
+    ChunkLayout L{};
+    L.E = int64_t(C) * W;
+    L.F = int64_t(C) * R;
+    L.C2 = int64_t(C) * C;
+    int64_t o = 0;
+    auto take = [&](int64_t n) { int64_t r = o; o += align_words(n); return r; };
+    L.off_key0 = take(L.E);
+    L.off_val0 = take(L.E);
+    L.off_key1 = take(L.E);
+    L.off_val1 = take(L.E);
+    L.off_spos = take(L.E);
+    L.off_stok = take(L.E);
+    L.off_sL = take(L.E);
+    L.off_shead = take(L.E);
+    L.off_scw = take(L.E);
+    L.off_sk = take(L.E);
+    L.off_gw = take(L.E);
+    L.off_gr = take(L.F);
+    L.off_rpos = take(L.F);
+    L.off_rL = take(L.F);
+    L.off_gpos = take(L.E + 1);
+    L.off_gslot = take(L.E);
+    L.off_gdecay = take(L.E);
+    L.off_meta = take(4);
+    L.off_beta = take(C);
+    L.off_A = take(L.C2);
+    L.off_QK = take(L.C2);
+    L.off_X = take(L.C2);
+    L.off_QX = take(L.C2);
+    L.words = o;
+    return L;
+}
+
+struct Slab {
+    int32_t ti0;        // first step of the slab
+    int32_t steps;      // steps in the slab
+    uint32_t *ws;       // workspace base
+    ChunkLayout lay;
+    // Chunk pointer helpers
+    __host__ __device__ uint32_t *chunk(int64_t n) const { return ws + n * lay.words; }
+};
+
+}  // namespace sdm

@@ -1,0 +1,180 @@
+/*
+ * sdm.h — C ABI of the MI355X (gfx950) chunked sparse-delta-memory (SDM) forward.
+ *
+ * The operation. P streams each own a bank of M rows by head_dim columns. Every token
+ * writes W weighted slots and then reads R weighted slots:
+ *     each written row decays by exp(log_decay), the retrieved vector is the weighted
+ *     sum of the decayed written rows, the write error is beta * (v - retrieved), each
+ *     written row gains weight * error, and the reading is the weighted sum of the read
+ *     rows after the write.
+ * This is the per-token definition in the SDMWriteRead class docstring (memory_ops.py,
+ * sparse-delta-memory 2.0.0 wheel, diffend page 21). The library computes it in the
+ * chunked three-part form of that module's docstring: Phase 1 (per-slot log-decays,
+ * dedup groups, gather weights, Gram matrices A and QK), the solve
+ * X = (I + tril(beta A, -1))^-1, QX = QK X (wy_solve.py docstring, page 23), and Phase 2,
+ * Nt sequential steps of gather, dual matmul and decay-and-write (phase2_kernels.py
+ * docstring, page 23).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named "device" are HIP device (or managed) memory on the current device;
+ *     the library never dereferences them on the host, never allocates device memory
+ *     and never synchronizes. Work is enqueued on exec->stream (a hipStream_t; NULL is
+ *     the null stream) and runs asynchronously; a fault in it surfaces at the caller's
+ *     next synchronization.
+ *   - All arrays are dense row-major with no padding. Token arrays are stream-major:
+ *     element (p, t, j) of a [P, T, J] array sits at ((p * T) + t) * J + j.
+ *   - Every argument is checked on the host before anything is enqueued; on a failed
+ *     check nothing is enqueued and a negative SDM_ERR_* code is returned
+ *     (sdm_last_error() then describes it). The pages raise TypeError / ValueError /
+ *     UnsupportedConfigurationError before any work for the same classes of mistakes
+ *     (_layout and _admit in memory_ops.py, page 21).
+ *   - Caller contract NOT checked (it would need a device read): every slot id lies in
+ *     [0, M), and the W write slots of a token are distinct (sdm_write_read's docstring
+ *     requires distinct write slots). A violation gives unspecified (but in-bounds for
+ *     reads of ids in range) results.
+ *   - Results are bitwise reproducible for fixed inputs and shapes on one GPU type: every
+ *     bank element has one writer per step and every sum runs in a fixed order (the
+ *     determinism contract of memory_ops.py and phase2_kernels.py). A stream's results do
+ *     not depend on the other streams, on the column slicing, or on the workspace size.
+ *   - Calls that share a workspace or a bank must be ordered on one stream.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SDM_OK = 0,
+    SDM_ERR_DTYPE = -1,       /* bank dtype not SDM_F32 / SDM_BF16 */
+    SDM_ERR_SHAPE = -2,       /* P, T, W, R, head_dim, M < 1; W or R > 256; gate width not 1 or W */
+    SDM_ERR_RANGE = -3,       /* chunk outside [16, 256]; P*M >= 2^31 rows; P*Nt*C >= 2^31; head_dim > 2^20 */
+    SDM_ERR_NULL = -4,        /* a required pointer is NULL */
+    SDM_ERR_ALIGN = -5,       /* a device pointer is not aligned to its element size (16 B for vector rows) */
+    SDM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than one step needs */
+    SDM_ERR_UNSUPPORTED = -7, /* no kernel plan for this shape on this device */
+    SDM_ERR_HIP = -8          /* a HIP runtime call failed (launch, attribute query) */
+};
+
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+/* Slot ids, device int32. write: [P, T, W]; read: [P, T, R]. Stream-local rows in [0, M). */
+typedef struct {
+    const int32_t *write;
+    const int32_t *read;
+    int32_t W;
+    int32_t R;
+} sdm_slots;
+
+/* Slot weights, device, in the bank dtype. write: [P, T, W] (k_val); read: [P, T, R] (q_val). */
+typedef struct {
+    const void *write;
+    const void *read;
+} sdm_weights;
+
+/* The bank, device [P, rows, head_dim] in dtype; read and advanced in place to its final
+ * state. Stream p owns rows [p * rows, (p + 1) * rows) of the flat [P * rows, head_dim]
+ * array (sdm_write_read's per-stream slot ranges, num_memory_slots = rows). */
+typedef struct {
+    void *data;
+    int64_t rows;
+    int32_t head_dim;
+    int32_t dtype; /* sdm_dtype */
+} sdm_bank;
+
+/* Where and with what scratch the call runs. stream: hipStream_t (NULL = null stream).
+ * workspace: device scratch of workspace_bytes, 256-byte aligned, owned by the caller,
+ * no initial contents required; the call uses the largest slab of steps that fits.
+ * events: optional (NULL = none) array of num_events >= SDM_TIMING_EVENTS hipEvent_t
+ * created by the caller; sdm_fwd then records them on `stream` at the kernel boundaries
+ * of its first slab, in order: before the radix sort, before the group scan, before the
+ * read lookup, before the Gram kernel, before the solve, before Phase 2, after Phase 2.
+ * Recording is asynchronous; the caller reads the elapsed times after synchronizing. */
+typedef struct {
+    void *stream;
+    void *workspace;
+    size_t workspace_bytes;
+    void **events;
+    int32_t num_events;
+} sdm_exec;
+
+#define SDM_TIMING_EVENTS 7
+
+/*
+ * Workspace bytes sdm_fwd needs to run its steps in slabs of `slab_steps` steps
+ * (0 = all Nt = ceil(tokens / chunk) steps in one slab). A slab holds every Phase-1
+ * quantity and both solve outputs of its P * slab_steps chunks: 56 B per write entry,
+ * 12 B per read entry and 16 B per chunk-matrix element
+ * (the pages budget the same kinds of state, SLAB_BYTES in memory_ops.py).
+ * Returns 0 for arguments sdm_fwd would reject with SDM_ERR_SHAPE or SDM_ERR_RANGE.
+ * Results never depend on the slab size.
+ */
+size_t sdm_fwd_workspace_bytes(int32_t streams, int32_t tokens, int32_t chunk, int32_t W, int32_t R,
+                               int32_t head_dim, int32_t slab_steps);
+
+/*
+ * The SDM forward (sdm_write_read's no-grad forward, memory_ops.py, page 21).
+ *   streams P >= 1, tokens T >= 1, chunk C in [16, 256] (T need not be a multiple of C).
+ *   slots, weights: as above. beta: device float32 [P, T]. log_decay: device float32
+ *   [P, T, gate_width], gate_width 1 (one log-decay per token, applied to each of its
+ *   writes) or W (one per write slot).
+ *   v: device [P, T, head_dim] in the bank dtype. bank: in/out.
+ *   valid_tokens: device int32 [P], each in [0, T], or NULL (= T for every stream).
+ *     Tokens t >= valid_tokens[p] are padding: they touch no bank row and read 0.
+ *   out: device [P, T, head_dim] in the bank dtype; every element is written (padding
+ *     rows +0). out must not overlap the bank or any input.
+ * Arithmetic: inputs widened to float32; accumulation in float32; the readings and each
+ * written bank row are rounded once to the bank dtype (round to nearest even for bf16).
+ */
+int sdm_fwd(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
+            const sdm_weights *weights, const float *beta, const float *log_decay,
+            int32_t gate_width, const void *v, const sdm_bank *bank,
+            const int32_t *valid_tokens, void *out, const sdm_exec *exec);
+
+/*
+ * Phase 1 and the solve only, for every chunk, into caller buffers (for checking the
+ * intermediates; sdm_fwd keeps them in its workspace). Chunk (p, ti) is n = p * Nt + ti.
+ *   rows, head_dim, dtype: the bank the call would run on (rows bounds the ids; dtype is
+ *   the weights' dtype).
+ *   A, QK, X, QX: device float32 [P * Nt, C, C]. A: strict lower triangle of the
+ *   decay-weighted write x write Gram matrix, +0 elsewhere; QK: lower triangle (diagonal
+ *   included) of the read x write Gram matrix, +0 above; X = (I + tril(beta A, -1))^-1,
+ *   QX = QK X, both +0 above the diagonal (wy_solve.py docstring, page 23).
+ *   gw: device float32 [P * Nt, C, W] gather weights k * exp(L) of the write entries;
+ *   gr: device float32 [P * Nt, C, R] gather weights q * exp(L) of the read entries;
+ *   0 for padding tokens.
+ *   exec->workspace must hold sdm_fwd_workspace_bytes(..., slab_steps = 1).
+ */
+int sdm_chunk_mats(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
+                   const sdm_weights *weights, const float *beta, const float *log_decay,
+                   int32_t gate_width, int64_t rows, int32_t head_dim, int32_t dtype,
+                   const int32_t *valid_tokens, float *A, float *QK, float *X, float *QX,
+                   float *gw, float *gr, const sdm_exec *exec);
+
+/*
+ * The per-chunk solve on its own (wy_solve, wy_solve.py, page 23):
+ *   X = (I + tril(beta[:, None] * A, -1))^-1 and QX = QK @ X for each of n chunks.
+ *   A, QK: device float32 [n, C, C]; only the strict lower triangle of A and the lower
+ *   triangle (diagonal included) of QK are read. beta: device float32 [n, C].
+ *   X, QX: device float32 [n, C, C], +0 above the diagonal; must not overlap the inputs
+ *   (not checked).
+ *   C in [1, 256]. exec->workspace is not used (may be NULL).
+ */
+int sdm_wy_solve(int64_t n, int32_t chunk, const float *A, const float *beta, const float *QK,
+                 float *X, float *QX, const sdm_exec *exec);
+
+/* Static text for an SDM_* code. */
+const char *sdm_error_string(int code);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char *sdm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

@@ -1,0 +1,153 @@
+"""The C ABI on the host: the library loads, exports every function include/sdm.h
+declares, and rejects malformed calls with the documented code before any device work
+(no GPU needed: rejected calls never touch a HIP API)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+LIB = os.path.join(ROOT, "chunked_sparse_delta_amd", "libsdm.so")
+
+OK, DTYPE, SHAPE, RANGE, NULL, ALIGN, WORKSPACE, UNSUPPORTED, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from chunked_sparse_delta_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["sdm_chunk_mats", "sdm_error_string", "sdm_fwd", "sdm_fwd_workspace_bytes",
+                                    "sdm_last_error", "sdm_wy_solve"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_error_strings(lib):
+    lib.sdm_error_string.restype = ctypes.c_char_p
+    for code in (OK, DTYPE, SHAPE, RANGE, NULL, ALIGN, WORKSPACE, UNSUPPORTED, HIP):
+        assert lib.sdm_error_string(code) and lib.sdm_error_string(code) != b"unknown error"
+    assert lib.sdm_error_string(-99) == b"unknown error"
+
+
+def test_workspace_bytes(lib):
+    f = lib.sdm_fwd_workspace_bytes
+    f.restype = ctypes.c_size_t
+    one = f(8, 2048, 64, 8, 8, 64, 1)
+    assert one > 0 and one % 256 == 0
+    assert f(8, 2048, 64, 8, 8, 64, 0) == 32 * one       # Nt = 32 steps
+    assert f(8, 2048, 64, 8, 8, 64, 5) == 5 * one
+    assert f(8, 2048, 64, 8, 8, 64, 999) == 32 * one
+    assert f(8, 2048, 8, 8, 8, 64, 0) == 0                # chunk out of range
+    assert f(8, 2048, 64, 0, 8, 64, 0) == 0               # W < 1
+    assert f(8, 2048, 64, 8, 257, 64, 0) == 0             # R > 256
+    # 56 B per write entry, 12 B per read entry, 16 B per chunk-matrix element (+ alignment)
+    per_chunk = one / 8
+    E, F, C2 = 64 * 8, 64 * 8, 64 * 64
+    assert 56 * E + 12 * F + 16 * C2 <= per_chunk <= 56 * E + 12 * F + 16 * C2 + 24 * 256
+
+
+class Call:
+    """A well-formed sdm_fwd call on fake (never dereferenced) aligned pointers."""
+
+    FAKE = 0x7f0000000000
+
+    def __init__(self, lib):
+        self.lib = lib
+        lib.sdm_last_error.restype = ctypes.c_char_p
+        self.P, self.T, self.C, self.W, self.R, self.G, self.hd, self.M = 2, 100, 32, 4, 3, 4, 64, 50
+        self.dtype = 0
+        self.ws_bytes = None
+        self.ptr = {k: self.FAKE + (i << 32) for i, k in enumerate(
+            ["kidx", "qidx", "kval", "qval", "beta", "g", "v", "bank", "out", "ws", "valid"])}
+
+    def run(self):
+        from chunked_sparse_delta_amd import _Bank, _Exec, _Slots, _Weights
+        lib = self.lib
+        lib.sdm_fwd.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 5
+        slots = _Slots(self.ptr["kidx"], self.ptr["qidx"], self.W, self.R)
+        weights = _Weights(self.ptr["kval"], self.ptr["qval"])
+        bank = _Bank(self.ptr["bank"], self.M, self.hd, self.dtype)
+        lib.sdm_fwd_workspace_bytes.restype = ctypes.c_size_t
+        need = lib.sdm_fwd_workspace_bytes(self.P, self.T, self.C, self.W, self.R, self.hd, 0)
+        ex = _Exec(None, self.ptr["ws"], need if self.ws_bytes is None else self.ws_bytes, None, 0)
+        rc = lib.sdm_fwd(self.P, self.T, self.C, ctypes.byref(slots), ctypes.byref(weights), self.ptr["beta"],
+                         self.ptr["g"], self.G, self.ptr["v"], ctypes.byref(bank), self.ptr["valid"],
+                         self.ptr["out"], ctypes.byref(ex))
+        return rc, lib.sdm_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("P", 0, SHAPE), ("T", 0, SHAPE), ("C", 15, RANGE), ("C", 257, RANGE), ("W", 0, SHAPE), ("W", 257, SHAPE),
+    ("R", 0, SHAPE), ("R", 300, SHAPE), ("G", 2, SHAPE), ("hd", 0, SHAPE), ("hd", (1 << 20) + 1, RANGE),
+    ("M", 0, SHAPE), ("M", 1 << 30, RANGE), ("dtype", 2, DTYPE), ("ws_bytes", 1024, WORKSPACE),
+])
+def test_fwd_rejects_before_any_work(lib, field, value, code):
+    c = Call(lib)
+    setattr(c, field, value)
+    rc, msg = c.run()
+    assert rc == code, msg
+    assert msg
+
+
+@pytest.mark.parametrize("name", ["kidx", "qidx", "kval", "qval", "beta", "g", "v", "bank", "out", "ws"])
+def test_fwd_rejects_null(lib, name):
+    c = Call(lib)
+    c.ptr[name] = None
+    rc, msg = c.run()
+    assert rc == (WORKSPACE if name == "ws" else NULL), msg
+
+
+@pytest.mark.parametrize("name,off,dtype", [("kidx", 2, 0), ("beta", 1, 0), ("bank", 2, 0), ("v", 1, 1),
+                                           ("ws", 16, 0), ("valid", 2, 0)])
+def test_fwd_rejects_misaligned(lib, name, off, dtype):
+    c = Call(lib)
+    c.dtype = dtype
+    c.ptr[name] += off
+    rc, msg = c.run()
+    assert rc == ALIGN, msg
+
+
+def test_fwd_rejects_out_overlapping_bank(lib):
+    c = Call(lib)
+    c.ptr["out"] = c.ptr["bank"] + 256
+    rc, msg = c.run()
+    assert rc == SHAPE and "overlap" in msg
+
+
+def test_fwd_rejects_too_many_token_rows(lib):
+    c = Call(lib)
+    c.P, c.T, c.C = 4096, 1 << 20, 256
+    rc, _ = c.run()
+    assert rc == RANGE
+
+
+def test_wy_solve_rejects(lib):
+    from chunked_sparse_delta_amd import _Exec
+    f = lib.sdm_wy_solve
+    f.argtypes = [ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 6
+    ex = _Exec(None, None, 0, None, 0)
+    fake = Call.FAKE
+    assert f(4, 0, fake, fake, fake, fake, fake, ctypes.byref(ex)) == RANGE
+    assert f(4, 257, fake, fake, fake, fake, fake, ctypes.byref(ex)) == RANGE
+    assert f(-1, 16, fake, fake, fake, fake, fake, ctypes.byref(ex)) == SHAPE
+    assert f(4, 16, None, fake, fake, fake, fake, ctypes.byref(ex)) == NULL
+    assert f(4, 16, fake + 2, fake, fake, fake, fake, ctypes.byref(ex)) == ALIGN
+    assert f(0, 16, None, None, None, None, None, ctypes.byref(ex)) == OK   # nothing to do
+    assert f(4, 16, fake, fake, fake, fake, fake, None) == NULL

@@ -1,0 +1,198 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Bar: infinity-norm relative error per output tensor (readings, final bank) within 1e-4
+for float32 banks and 2e-2 for bfloat16 banks; padding rows exactly +0; bitwise-identical
+reruns."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import small
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ the solve on its own
+
+@pytest.mark.parametrize("C", [1, 16, 37, 64, 65, 128, 200, 256])
+def test_wy_solve_matches_inverse(gpu, C):
+    from chunked_sparse_delta_amd import wy_solve
+    rng = np.random.default_rng(C)
+    n = 3
+    A = rng.uniform(0.0, 2.0 / np.sqrt(C), (n, C, C)).astype(np.float32)
+    A[:, np.triu_indices(C)[0], np.triu_indices(C)[1]] = np.nan   # never read
+    QK = rng.normal(size=(n, C, C)).astype(np.float32)
+    QK[:, np.triu_indices(C, 1)[0], np.triu_indices(C, 1)[1]] = np.nan
+    beta = rng.uniform(0, 1, (n, C)).astype(np.float32)
+    X, QX = wy_solve(torch.from_numpy(A).to(gpu), torch.from_numpy(beta).to(gpu), torch.from_numpy(QK).to(gpu))
+    X, QX = X.cpu().numpy(), QX.cpu().numpy()
+    for k in range(n):
+        Lm = np.tril(beta[k, :, None].astype(np.float64) * np.nan_to_num(A[k].astype(np.float64)), -1)
+        Xr = np.linalg.inv(np.eye(C) + Lm)
+        QXr = np.tril(np.nan_to_num(QK[k].astype(np.float64))) @ Xr
+        assert gu.rel_err(X[k].astype(np.float64), np.tril(Xr)) < 1e-5
+        assert gu.rel_err(QX[k].astype(np.float64), np.tril(QXr)) < 1e-5
+        up = np.triu_indices(C, 1)
+        assert np.all(X[k][up] == 0) and not np.signbit(X[k][up]).any()
+        assert np.all(QX[k][up] == 0) and not np.signbit(QX[k][up]).any()
+        assert np.all(np.diag(X[k]) == 1.0)
+
+
+# ------------------------------------------------------------------ Phase 1 and the solve vs the chunk algebra
+
+@pytest.mark.parametrize("wl", [
+    small(P=2, T=37, C=16, hd=8, M=12, W=3, R=2),
+    small(P=1, T=40, C=20, hd=8, M=9, W=4, R=3, gate_width=1, ragged=True, index=3),
+    small(P=2, T=33, C=32, hd=8, M=30, W=5, R=4, dtype="bf16", ids="zipf", index=4),
+])
+def test_chunk_intermediates_match_chunk_algebra(gpu, wl):
+    import oracle
+    from oracle import chunk_algebra
+    from chunked_sparse_delta_amd import chunk_mats
+    inp = gu.generate(wl)
+    f = oracle.as_f64_inputs(inp)
+    _, _, inter = chunk_algebra.forward(f, wl.C, emit=True)
+    t = gu.to_torch(inp, gpu)
+    res = chunk_mats(t["k_idx"], t["k_val"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], rows=wl.M,
+                     head_dim=wl.hd, chunk=wl.C, valid_tokens=t["valid"])
+    res = {k: v.cpu().numpy().astype(np.float64) for k, v in res.items()}
+    Nt = wl.Nt
+    for p in range(wl.P):
+        for ti in range(Nt):
+            c = inter[p][ti]
+            n = p * Nt + ti
+            for key, ref in (("A", np.tril(c["A"], -1)), ("QK", np.tril(c["QK"])), ("X", c["X"]), ("QX", c["QX"]),
+                             ("gw", c["gw"]), ("gr", c["gr"])):
+                got = res[key][n]
+                assert gu.rel_err(got, ref) < 2e-5, (p, ti, key, gu.rel_err(got, ref))
+            up = np.triu_indices(wl.C, 1)
+            for key in ("QK", "X", "QX"):
+                assert np.all(res[key][n][up] == 0), (p, ti, key)
+            assert np.all(res["A"][n][np.triu_indices(wl.C)] == 0)
+
+
+# ------------------------------------------------------------------ end to end, small shapes
+
+SMALL = [
+    small(P=2, T=37, C=16, hd=8, M=24, W=3, R=2, index=10),                                  # ragged last chunk
+    small(P=3, T=100, C=32, hd=64, M=40, W=5, R=4, dtype="bf16", ids="zipf", index=11),
+    small(P=2, T=64, C=64, hd=3, M=20, W=2, R=3, index=12),                                  # scalar path, f32
+    small(P=2, T=70, C=17, hd=5, M=30, W=4, R=4, dtype="bf16", ragged=True, index=13),       # odd C, scalar bf16
+    small(P=1, T=300, C=128, hd=16, M=300, W=16, R=8, ids="zipf", ragged=True, weight_scale=-1.0, index=14),
+    small(P=2, T=513, C=256, hd=32, M=1000, W=32, R=32, ids="mixed", weight_scale=-1.0, index=15),
+    small(P=2, T=50, C=16, hd=8, M=30, W=3, R=3, gate_width=1, index=16),                    # one gate per token
+    small(P=8, T=130, C=100, hd=8, M=60, W=4, R=4, index=17, ragged=True),                   # P % 8 == 0 layout
+    small(P=16, T=96, C=48, hd=24, M=100, W=6, R=6, dtype="bf16", index=18),
+    small(P=1, T=16, C=16, hd=4, M=2, W=1, R=1, index=19),                                   # one chunk, tiny bank
+    small(P=2, T=200, C=64, hd=256, M=300, W=256, R=256, dtype="bf16", weight_scale=-1.0, index=20),  # max width
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[f"P{w.P}T{w.T}C{w.C}hd{w.hd}W{w.W}{w.dtype}{w.ids}G{w.G}" for w in SMALL])
+def test_forward_small(gpu, wl):
+    inp = gu.generate(wl)
+    ref_out, ref_bank = gu.oracle_ref(inp)
+    t = gu.to_torch(inp, gpu)
+    out, bank = gu.run(t, wl.C)
+    gu.assert_parity(out, bank, ref_out, ref_bank, wl.dtype, wl.name)
+    o = gu.f64(out)
+    for p in range(wl.P):
+        pad = o[p, int(inp["valid"][p]):]
+        assert np.all(pad == 0) and not np.signbit(pad).any()
+
+
+def test_forward_g_positive(gpu):
+    """Positive log-decays (rows grow between writes) take the same path."""
+    wl = small(P=2, T=60, C=16, hd=8, M=10, W=2, R=2, decay_scale=-0.05, index=21)
+    inp = gu.generate(wl)
+    assert (inp["log_decay"] > 0).all()
+    ref_out, ref_bank = gu.oracle_ref(inp)
+    out, bank = gu.run(gu.to_torch(inp, gpu), wl.C)
+    gu.assert_parity(out, bank, ref_out, ref_bank, wl.dtype, "g>0")
+
+
+def test_all_padding_and_zero_valid(gpu):
+    wl = small(P=3, T=40, C=16, hd=8, M=16, W=2, R=2, index=22)
+    inp = gu.generate(wl)
+    inp["valid"] = np.array([0, 40, 17], np.int32)
+    ref_out, ref_bank = gu.oracle_ref(inp)
+    t = gu.to_torch(inp, gpu)
+    out, bank = gu.run(t, wl.C)
+    gu.assert_parity(out, bank, ref_out, ref_bank, wl.dtype, "valid 0/40/17")
+    assert torch.equal(bank[0], t["bank"][0])          # stream 0 untouched
+    assert (gu.f64(out[0]) == 0).all()
+
+
+@pytest.mark.parametrize("C", [16, 32, 64, 128, 256])
+def test_result_does_not_depend_on_chunk_size(gpu, C):
+    wl = small(P=2, T=300, C=C, hd=16, M=50, W=4, R=4, ragged=True, index=23)
+    inp = gu.generate(wl)
+    ref_out, ref_bank = gu.oracle_ref(inp)
+    out, bank = gu.run(gu.to_torch(inp, gpu), C)
+    gu.assert_parity(out, bank, ref_out, ref_bank, wl.dtype, f"C={C}")
+
+
+# ------------------------------------------------------------------ determinism and independence
+
+def test_bitwise_reruns_workspace_and_stream_independence(gpu):
+    wl = small(P=8, T=256, C=64, hd=64, M=200, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=24)
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    o1, b1 = gu.run(t, wl.C)
+    o2, b2 = gu.run(t, wl.C)
+    assert np.array_equal(gu.bits(o1), gu.bits(o2)) and np.array_equal(gu.bits(b1), gu.bits(b2))
+    # smallest workspace (one step per slab) gives the same bits
+    from chunked_sparse_delta_amd import workspace_bytes
+    one = workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 1)
+    o3, b3 = gu.run(t, wl.C, max_workspace_bytes=one)
+    assert np.array_equal(gu.bits(o1), gu.bits(o3)) and np.array_equal(gu.bits(b1), gu.bits(b3))
+    # stream 5 alone gives the same bits as inside the batch
+    t5 = {k: v[5:6].contiguous() for k, v in t.items()}
+    o5, b5 = gu.run(t5, wl.C)
+    assert np.array_equal(gu.bits(o5[0]), gu.bits(o1[5])) and np.array_equal(gu.bits(b5[0]), gu.bits(b1[5]))
+
+
+def test_poisoned_output_and_workspace(gpu):
+    wl = small(P=2, T=90, C=32, hd=32, M=40, W=4, R=4, ragged=True, index=25)
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    o1, b1 = gu.run(t, wl.C)
+    from chunked_sparse_delta_amd import workspace_bytes
+    ws = torch.full((workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0),), 0xFF, dtype=torch.uint8, device=gpu)
+    out = torch.full((wl.P, wl.T, wl.hd), float("nan"), dtype=torch.float32, device=gpu)
+    o2, b2 = gu.run(t, wl.C, out=out, workspace=ws)
+    assert np.array_equal(gu.bits(o1), gu.bits(o2)) and np.array_equal(gu.bits(b1), gu.bits(b2))
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+
+@pytest.mark.parametrize("name", ["0", "1", "2", "3"])
+def test_workload_full_size(gpu, name):
+    wl = workloads.CONFIGS[name]
+    inp = gu.generate(wl)
+    ref_out, ref_bank = gu.oracle_ref(inp, threads=16)
+    t = gu.to_torch(inp, gpu)
+    out, bank = gu.run(t, wl.C)
+    gu.assert_parity(out, bank, ref_out, ref_bank, wl.dtype, f"config {name}")
+    o2, b2 = gu.run(t, wl.C)
+    assert np.array_equal(gu.bits(out), gu.bits(o2)) and np.array_equal(gu.bits(bank), gu.bits(b2))
+
+
+def test_workload_4p_sampled_streams(gpu):
+    """Config 4's shapes (timed literally) at full size; the oracle checks two sampled
+    streams of the finite twin 4p (weights / sqrt(256)) computed in the full launch."""
+    wl = workloads.CONFIGS["4p"]
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    del inp
+    out, bank = gu.run(t, wl.C)
+    sample = [0, 37]
+    sub = gu.generate(wl, streams=sample)
+    ref_out, ref_bank = gu.oracle_ref(sub, threads=2)
+    for k, p in enumerate(sample):
+        gu.assert_parity(out[p], bank[p], ref_out[k], ref_bank[k], wl.dtype, f"config 4p stream {p}")
+    o2, b2 = gu.run(t, wl.C)
+    assert np.array_equal(gu.bits(out), gu.bits(o2)) and np.array_equal(gu.bits(bank), gu.bits(b2))
