@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <stdlib.h>
+
 #include <mutex>
 
 #include "../../include/sdm.h"
@@ -18,9 +20,11 @@ hipError_t wy_prepare();
 hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev);
 hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
                      int64_t stride, int64_t bstride, hipStream_t st);
-hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, int nv, hipStream_t st);
+hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, uint32_t *control, hipStream_t st);
+hipError_t phase2_max_resident(int dtype, int V, const P2Geom &g, int C, int cus, int64_t *out);
 size_t gram_lds_bytes(int C);
-size_t phase2_lds_bytes(int C, int nv, int V);
+size_t phase2_lds_bytes(int C, int nv, int V, int K);
+int64_t phase2_control_words(int P, int C, int hd);
 }  // namespace sdm
 
 using namespace sdm;
@@ -46,6 +50,7 @@ int hip_fail(hipError_t e, const char *what) {
 struct DeviceInfo {
     bool ready = false;
     int lds_per_block = 0;
+    int cus = 0;
 };
 DeviceInfo g_dev[64];
 std::mutex g_dev_mu;
@@ -60,6 +65,8 @@ int device_info(DeviceInfo **out) {
     if (!d.ready) {
         if ((e = hipDeviceGetAttribute(&d.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess)
             return hip_fail(e, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock)");
+        if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+            return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
         if ((e = phase1_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 1)");
         if ((e = phase2_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 2)");
         if ((e = wy_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (solve)");
@@ -141,16 +148,41 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     return SDM_OK;
 }
 
-// Vectors per column slice: 128-byte slices where that leaves enough workgroups to fill
-// the chip (about two per CU), narrower otherwise; bounded by LDS.
-int pick_nv(const Problem &pb, int V, int es, int lds_limit) {
+// Phase-2 geometry from shapes only (the bits never depend on it): 128-byte column
+// slices (one cache line of each row), halved down to 32 bytes while that leaves fewer
+// than about one workgroup per CU; one workgroup per (stream, slice). Teams (K > 1) are
+// only taken from SDM_P2_GEOM="nv,K,block", which overrides the whole choice (for tuning
+// sweeps): their barriers need device-scope fences that write back and invalidate the
+// per-XCD L2, which costs more than they save on the shapes measured.
+P2Geom plan_phase2(const Problem &pb, int V, int es, int cus, int lds_limit) {
     const int hv = pb.hd / V;
-    int nv = (128 / (V * es)) < 1 ? 1 : 128 / (V * es);
-    if (nv > hv) nv = hv;
-    const int64_t target = 512;
-    while (nv > 1 && int64_t(pb.P) * ((hv + nv - 1) / nv) < target) nv >>= 1;
-    while (nv > 1 && phase2_lds_bytes(pb.C, nv, V) > size_t(lds_limit)) nv >>= 1;
-    return nv < 1 ? 1 : nv;
+    P2Geom g{};
+    g.nv = 128 / (V * es) < 1 ? 1 : 128 / (V * es);
+    if (g.nv > hv) g.nv = hv;
+    g.K = 1;
+    const char *env = getenv("SDM_P2_GEOM");
+    int enk = 0, ekk = 0, ebb = 0;
+    if (env && sscanf(env, "%d,%d,%d", &enk, &ekk, &ebb) == 3 && enk >= 1 && ekk >= 1 &&
+        (ebb == 256 || ebb == 512 || ebb == 1024)) {
+        g.nv = enk > hv ? hv : enk;
+        g.K = ekk > pb.C ? pb.C : ekk;
+        g.S = (hv + g.nv - 1) / g.nv;
+        g.block = ebb;
+        return g;
+    }
+    g.S = (hv + g.nv - 1) / g.nv;
+    while (g.nv > 1 && g.nv * V * es > 32 && int64_t(pb.P) * g.S < cus) {
+        g.nv >>= 1;
+        g.S = (hv + g.nv - 1) / g.nv;
+    }
+    while (g.nv > 1 && phase2_lds_bytes(pb.C, g.nv, V, g.K) + 256 > size_t(lds_limit)) {
+        g.nv >>= 1;
+        g.S = (hv + g.nv - 1) / g.nv;
+    }
+    // threads: about two gather items (token x vector) per thread
+    const int items = 2 * pb.C * g.nv;
+    g.block = items >= 2048 ? 1024 : (items >= 1024 ? 512 : 256);
+    return g;
 }
 
 }  // namespace
@@ -179,7 +211,7 @@ size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32
     const int32_t Nt = int32_t((int64_t(T) + C - 1) / C);
     if (slab_steps <= 0 || slab_steps > Nt) slab_steps = Nt;
     const ChunkLayout lay = make_layout(C, W, R);
-    return size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
+    return size_t(phase2_control_words(P, C, hd)) * 4 + size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
 }
 
 int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
@@ -192,29 +224,39 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
                         bank->data, valid_tokens, out, true, &ck);
     if (rc) return rc;
     const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
-    if (!exec->workspace || exec->workspace_bytes < per_step)
+    const size_t control = size_t(phase2_control_words(P, C, bank->head_dim)) * 4;
+    if (!exec->workspace || exec->workspace_bytes < control + per_step)
         return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
-                    exec->workspace ? exec->workspace_bytes : size_t(0), per_step);
+                    exec->workspace ? exec->workspace_bytes : size_t(0), control + per_step);
     if (!aligned(exec->workspace, 256)) return fail(SDM_ERR_ALIGN, "workspace must be 256-byte aligned");
     DeviceInfo *dev = nullptr;
     if ((rc = device_info(&dev)) != SDM_OK) return rc;
     if (gram_lds_bytes(C) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
                     gram_lds_bytes(C), dev->lds_per_block);
-    const int nv = pick_nv(ck.pb, ck.V, ck.es, dev->lds_per_block);
-    if (phase2_lds_bytes(C, nv, ck.V) > size_t(dev->lds_per_block))
+    const P2Geom geom = plan_phase2(ck.pb, ck.V, ck.es, dev->cus, dev->lds_per_block);
+    if (phase2_lds_bytes(C, geom.nv, ck.V, geom.K) + 256 > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs more LDS than the device has", C);
+    if (geom.K > 1) {
+        int64_t resident = 0;
+        hipError_t e = phase2_max_resident(ck.pb.dtype, ck.V, geom, C, dev->cus, &resident);
+        if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+        if (int64_t(P) * geom.S * geom.K > resident)
+            return fail(SDM_ERR_UNSUPPORTED, "phase-2 teams of %d need %lld resident workgroups, the device holds %lld",
+                        geom.K, (long long)(int64_t(P) * geom.S * geom.K), (long long)resident);
+    }
     const int32_t Nt = ck.pb.Nt;
-    int32_t slab = int32_t(exec->workspace_bytes / per_step);
+    int32_t slab = int32_t((exec->workspace_bytes - control) / per_step);
     if (slab > Nt) slab = Nt;
     hipStream_t st = static_cast<hipStream_t>(exec->stream);
     hipEvent_t *ev = nullptr;
     if (exec->events && exec->num_events >= SDM_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
+    uint32_t *ctl = static_cast<uint32_t *>(exec->workspace);
     for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
         Slab sl{};
         sl.ti0 = ti0;
         sl.steps = Nt - ti0 < slab ? Nt - ti0 : slab;
-        sl.ws = static_cast<uint32_t *>(exec->workspace);
+        sl.ws = ctl + control / 4;
         sl.lay = ck.lay;
         hipEvent_t *sev = ti0 == 0 ? ev : nullptr;
         hipError_t e = launch_phase1(ck.pb, sl, st, sev);
@@ -225,7 +267,7 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
                       int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
         if (e != hipSuccess) return hip_fail(e, "solve launch");
         if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        e = launch_phase2(ck.pb, sl, ck.V, nv, st);
+        e = launch_phase2(ck.pb, sl, ck.V, geom, ctl, st);
         if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
         if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }

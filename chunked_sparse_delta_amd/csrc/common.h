@@ -42,6 +42,11 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return f32
 template <typename T, int V> struct Vec;
 
 template <> struct Vec<float, 4> {
+    using raw_t = float4;
+    static __device__ __forceinline__ raw_t load_raw(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+    static __device__ __forceinline__ void unpack(const raw_t &x, float (&o)[4]) {
+        o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    }
     static __device__ __forceinline__ void load(const float *p, float (&o)[4]) {
         float4 x = *reinterpret_cast<const float4 *>(p);
         o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
@@ -51,6 +56,16 @@ template <> struct Vec<float, 4> {
     }
 };
 template <> struct Vec<bf16, 8> {
+    using raw_t = uint4;
+    static __device__ __forceinline__ raw_t load_raw(const bf16 *p) { return *reinterpret_cast<const uint4 *>(p); }
+    static __device__ __forceinline__ void unpack(const raw_t &x, float (&o)[8]) {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
     static __device__ __forceinline__ void load(const bf16 *p, float (&o)[8]) {
         uint4 x = *reinterpret_cast<const uint4 *>(p);
         uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -69,6 +84,9 @@ template <> struct Vec<bf16, 8> {
     }
 };
 template <typename T> struct Vec<T, 1> {
+    using raw_t = T;
+    static __device__ __forceinline__ raw_t load_raw(const T *p) { return *p; }
+    static __device__ __forceinline__ void unpack(const raw_t &x, float (&o)[1]) { o[0] = to_f32(x); }
     static __device__ __forceinline__ void load(const T *p, float (&o)[1]) { o[0] = to_f32(*p); }
     static __device__ __forceinline__ void store(T *p, const float (&o)[1]) { *p = from_f32<T>(o[0]); }
 };
@@ -116,15 +134,14 @@ struct ChunkLayout {
     int64_t off_stok;     // [E] i32: token of sorted position
     int64_t off_sL;       // [E] f32: cumulative log-decay at sorted position
     int64_t off_shead;    // [E] i32: first sorted position of the group
-    int64_t off_scw;      // [E] f32: DW coefficient k exp(L_last - L)
+    int64_t off_mrec;     // [E] int2: DW member record {token, bits of k exp(L_last - L)}
     int64_t off_sk;       // [E] f32: k at sorted position
     int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
     int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
     int64_t off_rpos;     // [F] i32: sorted position of the latest write of the read slot, or -1
     int64_t off_rL;       // [F] f32: that write's cumulative log-decay (0 if none)
     int64_t off_gpos;     // [E+1] i32: group start positions
-    int64_t off_gslot;    // [E] i32: group slot
-    int64_t off_gdecay;   // [E] f32: exp(L_last)
+    int64_t off_grec;     // [E] int4: DW group record {slot, first position, members, bits of exp(L_last)}
     int64_t off_meta;     // [4] i32: n_live, E_live, ngroups, pad
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
@@ -148,15 +165,14 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_stok = take(L.E);
     L.off_sL = take(L.E);
     L.off_shead = take(L.E);
-    L.off_scw = take(L.E);
+    L.off_mrec = take(2 * L.E);
     L.off_sk = take(L.E);
     L.off_gw = take(L.E);
     L.off_gr = take(L.F);
     L.off_rpos = take(L.F);
     L.off_rL = take(L.F);
     L.off_gpos = take(L.E + 1);
-    L.off_gslot = take(L.E);
-    L.off_gdecay = take(L.E);
+    L.off_grec = take(4 * L.E);
     L.off_meta = take(4);
     L.off_beta = take(C);
     L.off_A = take(L.C2);
@@ -166,6 +182,12 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.words = o;
     return L;
 }
+
+// Phase-2 launch geometry: vectors per column slice, slices per row, workgroups per
+// (stream, slice) team, threads per workgroup.
+struct P2Geom {
+    int nv, S, K, block;
+};
 
 struct Slab {
     int32_t ti0;        // first step of the slab

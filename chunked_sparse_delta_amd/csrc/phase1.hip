@@ -7,9 +7,10 @@
 //   p1_sort    stable LSD radix sort of the chunk's write entries by slot id
 //              (entries enter in token order, so equal slots end in token order:
 //              each run of one slot is that slot's write group)
-//   p1_groups  group table (start, slot), per-entry cumulative log-decay L as a
-//              sequential scan over each group in token order, DW coefficients
-//              k exp(L_last - L), group decay exp(L_last), gather weights k exp(L)
+//   p1_groups  group table, per-entry cumulative log-decay L as a sequential scan over
+//              each group in token order, gather weights k exp(L), and the DW records:
+//              per group {slot, first position, members, exp(L_last)}, per member
+//              {token, k exp(L_last - L)}
 //   p1_reads   for each read entry, the latest write of its slot at or before its token
 //              (binary search), its L and gather weight q exp(L)
 //   p1_gram    A (strict lower) and QK (lower with diagonal) by row ownership: the
@@ -137,12 +138,11 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
     int32_t *stok = reinterpret_cast<int32_t *>(cb + L.off_stok);
     float *sL = reinterpret_cast<float *>(cb + L.off_sL);
     int32_t *shead = reinterpret_cast<int32_t *>(cb + L.off_shead);
-    float *scw = reinterpret_cast<float *>(cb + L.off_scw);
+    int2 *mrec = reinterpret_cast<int2 *>(cb + L.off_mrec);
     float *sk = reinterpret_cast<float *>(cb + L.off_sk);
     float *gw = reinterpret_cast<float *>(cb + L.off_gw);
     int32_t *gpos = reinterpret_cast<int32_t *>(cb + L.off_gpos);
-    int32_t *gslot = reinterpret_cast<int32_t *>(cb + L.off_gslot);
-    float *gdecay = reinterpret_cast<float *>(cb + L.off_gdecay);
+    int4 *grec = reinterpret_cast<int4 *>(cb + L.off_grec);
     int32_t *meta = reinterpret_cast<int32_t *>(cb + L.off_meta);
     float *beta_c = reinterpret_cast<float *>(cb + L.off_beta);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -171,7 +171,6 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
         if (head) {
             const int32_t g = woff[wv] + __popcll(b & lt);
             gpos[g] = int32_t(pos);
-            gslot[g] = int32_t(skey[pos]);
         }
         __syncthreads();
     }
@@ -200,11 +199,11 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
             spos[e] = m;
             shead[m] = a;
         }
-        gdecay[g] = expf(Lc);
+        grec[g] = make_int4(int32_t(skey[a]), a, e_end - a, __float_as_int(expf(Lc)));
         for (int32_t m = a; m < e_end; ++m) {
             const int32_t e = int32_t(sval[m]);
             const float Lm = sL[m], kv = sk[m];
-            scw[m] = kv * expf(Lc - Lm);
+            mrec[m] = make_int2(stok[m], __float_as_int(kv * expf(Lc - Lm)));
             gw[e] = kv * expf(Lm);
         }
     }

@@ -107,8 +107,9 @@ typedef struct {
 /*
  * Workspace bytes sdm_fwd needs to run its steps in slabs of `slab_steps` steps
  * (0 = all Nt = ceil(tokens / chunk) steps in one slab). A slab holds every Phase-1
- * quantity and both solve outputs of its P * slab_steps chunks: 56 B per write entry,
- * 12 B per read entry and 16 B per chunk-matrix element
+ * quantity and both solve outputs of its P * slab_steps chunks (68 B per write entry,
+ * 12 B per read entry and 16 B per chunk-matrix element), after a fixed control area
+ * (exchange rows and barrier counters of the Phase-2 teams)
  * (the pages budget the same kinds of state, SLAB_BYTES in memory_ops.py).
  * Returns 0 for arguments sdm_fwd would reject with SDM_ERR_SHAPE or SDM_ERR_RANGE.
  * Results never depend on the slab size.

@@ -50,17 +50,18 @@ def test_workspace_bytes(lib):
     f = lib.sdm_fwd_workspace_bytes
     f.restype = ctypes.c_size_t
     one = f(8, 2048, 64, 8, 8, 64, 1)
-    assert one > 0 and one % 256 == 0
-    assert f(8, 2048, 64, 8, 8, 64, 0) == 32 * one       # Nt = 32 steps
-    assert f(8, 2048, 64, 8, 8, 64, 5) == 5 * one
-    assert f(8, 2048, 64, 8, 8, 64, 999) == 32 * one
+    step = f(8, 2048, 64, 8, 8, 64, 2) - one             # one step of chunks; the rest is a fixed control area
+    assert one > step > 0 and one % 256 == 0 and step % 256 == 0
+    assert f(8, 2048, 64, 8, 8, 64, 0) == one + 31 * step    # Nt = 32 steps
+    assert f(8, 2048, 64, 8, 8, 64, 5) == one + 4 * step
+    assert f(8, 2048, 64, 8, 8, 64, 999) == one + 31 * step
     assert f(8, 2048, 8, 8, 8, 64, 0) == 0                # chunk out of range
     assert f(8, 2048, 64, 0, 8, 64, 0) == 0               # W < 1
     assert f(8, 2048, 64, 8, 257, 64, 0) == 0             # R > 256
-    # 56 B per write entry, 12 B per read entry, 16 B per chunk-matrix element (+ alignment)
-    per_chunk = one / 8
+    # 68 B per write entry, 12 B per read entry, 16 B per chunk-matrix element (+ alignment)
+    per_chunk = step / 8
     E, F, C2 = 64 * 8, 64 * 8, 64 * 64
-    assert 56 * E + 12 * F + 16 * C2 <= per_chunk <= 56 * E + 12 * F + 16 * C2 + 24 * 256
+    assert 68 * E + 12 * F + 16 * C2 <= per_chunk <= 68 * E + 12 * F + 16 * C2 + 24 * 256
 
 
 class Call:

@@ -196,3 +196,32 @@ def test_workload_4p_sampled_streams(gpu):
         gu.assert_parity(out[p], bank[p], ref_out[k], ref_bank[k], wl.dtype, f"config 4p stream {p}")
     o2, b2 = gu.run(t, wl.C)
     assert np.array_equal(gu.bits(out), gu.bits(o2)) and np.array_equal(gu.bits(bank), gu.bits(b2))
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=8, T=300, C=64, hd=64, M=200, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=26),
+    small(P=3, T=260, C=128, hd=32, M=300, W=16, R=16, ragged=True, index=27),
+], ids=["bf16_P8", "f32_P3"])
+def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
+    """Column slicing, team size and block size change only the schedule: every
+    geometry gives the same bits, and no team barrier times out (flag word 0 of the
+    workspace stays 0)."""
+    from chunked_sparse_delta_amd import workspace_bytes
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    ref_out, ref_bank = gu.oracle_ref(inp)
+    V = 4 if wl.dtype == "f32" else 8
+    hv = wl.hd // V
+    results = []
+    for geom in (None, "1,1,256", f"{hv},1,1024", f"{hv},4,256", "2,2,512", f"1,{wl.C // 16},256", "1,3,512"):
+        if geom is None:
+            monkeypatch.delenv("SDM_P2_GEOM", raising=False)
+        else:
+            monkeypatch.setenv("SDM_P2_GEOM", geom)
+        ws = torch.zeros(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0), dtype=torch.uint8, device=gpu)
+        o, b = gu.run(t, wl.C, workspace=ws)
+        assert int(ws[:4].view(torch.int32).item()) == 0, f"barrier timeout flag set with geometry {geom}"
+        results.append((geom, gu.bits(o), gu.bits(b)))
+    gu.assert_parity(torch.from_numpy(gu.f64(o)), torch.from_numpy(gu.f64(b)), ref_out, ref_bank, wl.dtype, "geometry")
+    for geom, ob, bb in results[1:]:
+        assert np.array_equal(ob, results[0][1]) and np.array_equal(bb, results[0][2]), geom
