@@ -59,7 +59,7 @@ class _Exec(ctypes.Structure):
                 ("events", ctypes.c_void_p), ("num_events", ctypes.c_int32)]
 
 
-TIMING_EVENTS = 7   # SDM_TIMING_EVENTS
+TIMING_EVENTS = 8   # SDM_TIMING_EVENTS
 
 
 _lock = threading.Lock()

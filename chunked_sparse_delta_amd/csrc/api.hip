@@ -10,7 +10,7 @@
 
 #include <mutex>
 
-#include "../../include/sdm.h"
+#include "sdm.h"
 #include "common.h"
 
 namespace sdm {
@@ -261,15 +261,15 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
         hipEvent_t *sev = ti0 == 0 ? ev : nullptr;
         hipError_t e = launch_phase1(ck.pb, sl, st, sev);
         if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
-        if (sev && (e = hipEventRecord(sev[4], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         float *w = reinterpret_cast<float *>(sl.ws);
         e = launch_wy(w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X, w + sl.lay.off_QX, C,
                       int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
         if (e != hipSuccess) return hip_fail(e, "solve launch");
-        if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         e = launch_phase2(ck.pb, sl, ck.V, geom, ctl, st);
         if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
-        if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if (sev && (e = hipEventRecord(sev[7], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     return SDM_OK;
 }

@@ -10,6 +10,8 @@ constexpr int kWave = 64;          // CDNA4 wavefront
 constexpr int kMaxChunk = 256;
 constexpr int kMaxWidth = 256;
 constexpr int kXcds = 8;           // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
+constexpr int kHotMin = 16;        // write groups of at least this many members go to the dense Gram
+constexpr float kHotSpan = 60.0f;  // ... if their log-decays stay within this of the first member's
 
 // ---------------------------------------------------------------------------------------
 // Element types. bf16 is carried as its 16-bit pattern.
@@ -142,7 +144,16 @@ struct ChunkLayout {
     int64_t off_rL;       // [F] f32: that write's cumulative log-decay (0 if none)
     int64_t off_gpos;     // [E+1] i32: group start positions
     int64_t off_grec;     // [E] int4: DW group record {slot, first position, members, bits of exp(L_last)}
-    int64_t off_meta;     // [4] i32: n_live, E_live, ngroups, pad
+    int64_t off_sgrp;     // [E] i32: group of sorted position
+    int64_t off_ghot;     // [E] i32: hot index of group, or -1
+    int64_t off_whot;     // [E] i32: hot index of write entry's group, or -1 (entry order)
+    int64_t off_ka;       // [E] f32: k exp(L - L_ref) of a hot write entry (entry order)
+    int64_t off_kb;       // [E] f32: k exp(L_ref - L) of a hot write entry (entry order)
+    int64_t off_crange;   // [E] int2: sorted positions [a, m) of the earlier members of a cold group
+    int64_t off_rhot;     // [F] i32: hot index of the read slot's group, or -1
+    int64_t off_rval;     // [F] f32: q exp(Lr - L_ref) of a hot read entry
+    int64_t off_rcrange;  // [F] int2: sorted positions [a, rpos + 1) of a cold read's members
+    int64_t off_meta;     // [4] i32: n_live, E_live, ngroups, hot groups
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
     int64_t words;        // 4-byte words per chunk
@@ -173,6 +184,15 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_rL = take(L.F);
     L.off_gpos = take(L.E + 1);
     L.off_grec = take(4 * L.E);
+    L.off_sgrp = take(L.E);
+    L.off_ghot = take(L.E);
+    L.off_whot = take(L.E);
+    L.off_ka = take(L.E);
+    L.off_kb = take(L.E);
+    L.off_crange = take(2 * L.E);
+    L.off_rhot = take(L.F);
+    L.off_rval = take(L.F);
+    L.off_rcrange = take(2 * L.F);
     L.off_meta = take(4);
     L.off_beta = take(C);
     L.off_A = take(L.C2);

@@ -5,12 +5,18 @@ run anything here. The product path (chunked_sparse_delta_amd) never does, and t
 package shares no code with it; both take their inputs from ``workloads``.
 
   O1  token_loop.c      the per-token recurrence in fp64 (the definition)
+  O1b token_loop.c      the same recurrence under the bfloat16 storage contract: written
+                        rows rounded to bfloat16 once per chunk, readings rounded to
+                        bfloat16 (token_loop(..., bf16_chunk=C))
   O2  chunk_algebra.py  the chunked three-part form in fp64, for tiny inputs
 
 Pins: tests/test_oracle.py checks O1 against O2 (two independent derivations),
 against closed forms (decay-only, scalar EMA, one-token delta update, overwrite
 under a large negative log-decay, a hand-worked rational example in tests/golden/)
-and against invariants (padding, chunk-size, stream and column independence).
+and against invariants (padding, chunk-size, stream and column independence). O1b is
+pinned by its rounding (ties to even, no double rounding, against an independent
+float32 bit-level rounding), by its reduction to O1 with one rounding when one chunk
+spans the stream, and by its equality with O1 when every value is bfloat16-exact.
 Parity unpinned: none.
 """
 
@@ -56,6 +62,11 @@ def _load():
             i64, p = ctypes.c_int64, ctypes.c_void_p
             f.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 10
             f.restype = ctypes.c_int
+            fb = lib.sdm_oracle_token_loop_bf16
+            fb.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 10
+            fb.restype = ctypes.c_int
+            lib.sdm_oracle_round_bf16.argtypes = [ctypes.c_double]
+            lib.sdm_oracle_round_bf16.restype = ctypes.c_double
             _lib = lib
     return _lib
 
@@ -77,10 +88,18 @@ def as_f64_inputs(inputs: dict) -> dict:
     )
 
 
-def token_loop(f64: dict, threads: int = 1, streams=None):
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 of each finite double (ties to even), as doubles."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.vectorize(lib.sdm_oracle_round_bf16, otypes=[np.float64])(x) if x.size else x.copy()
+
+
+def token_loop(f64: dict, threads: int = 1, streams=None, bf16_chunk: int | None = None):
     """O1 over the streams of fp64 inputs (``as_f64_inputs``). Returns (readings
     [P, T, hd], final bank [P, M, hd]) in fp64; ``streams`` restricts the work to a
-    subset (the other streams' outputs are left zero / unchanged)."""
+    subset (the other streams' outputs are left zero / unchanged). With ``bf16_chunk``
+    = C it runs O1b, the loop under the bfloat16 storage contract for chunks of C."""
     lib = _load()
     bank = np.array(f64["bank"], dtype=np.float64, copy=True, order="C")
     P, M, hd = bank.shape
@@ -100,9 +119,12 @@ def token_loop(f64: dict, threads: int = 1, streams=None):
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
 
     def run(p):
-        rc = lib.sdm_oracle_token_loop(p, p + 1, T, W, R, G, hd, M, ptr(k_idx), ptr(arrs["k_val"]),
-                                       ptr(arrs["v"]), ptr(arrs["beta"]), ptr(g), ptr(arrs["q_idx"]),
-                                       ptr(arrs["q_val"]), ptr(valid), ptr(bank), ptr(out))
+        args = (ptr(k_idx), ptr(arrs["k_val"]), ptr(arrs["v"]), ptr(arrs["beta"]), ptr(g), ptr(arrs["q_idx"]),
+                ptr(arrs["q_val"]), ptr(valid), ptr(bank), ptr(out))
+        if bf16_chunk is None:
+            rc = lib.sdm_oracle_token_loop(p, p + 1, T, W, R, G, hd, M, *args)
+        else:
+            rc = lib.sdm_oracle_token_loop_bf16(p, p + 1, T, W, R, G, hd, M, int(bf16_chunk), *args)
         if rc:
             raise ValueError(f"oracle: stream {p}: {ERRORS.get(rc, rc)}")
 

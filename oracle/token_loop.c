@@ -34,25 +34,48 @@
  * Returns 0, or a negative code on a violated caller contract: -1 a slot id out of
  * range, -2 a write slot repeated within one token (the op requires distinct write
  * slots per token), -3 a bad argument, -4 out of memory.
+ *
+ * O1b, the same loop under the bf16 storage contract (sdm_oracle_token_loop_bf16): the
+ * pages keep a bfloat16 bank in bfloat16 and round each written bank row once per chunk,
+ * at its decay-and-write store, and return the readings in the bank dtype (phase2_kernels
+ * .py docstring and _sdm_dual_matmul, diffend page 23; sdm_write_read's docstring, page
+ * 21). O1b therefore runs the exact fp64 token loop and, at the end of every chunk of
+ * `chunk` tokens (and at the last token), rounds every row written in that chunk to the
+ * nearest bfloat16 (ties to even); each reading is rounded to bfloat16. It isolates the
+ * error that bfloat16 storage itself causes from arithmetic error.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-int sdm_oracle_token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
-                          int64_t hd, int64_t M, const int32_t *k_idx, const double *k_val,
-                          const double *v, const double *beta, const double *g,
-                          const int32_t *q_idx, const double *q_val, const int32_t *valid,
-                          double *bank, double *out)
+/* Nearest bfloat16 (8 significant bits, ties to even) of a finite double, exactly
+ * (one rounding: no intermediate float). */
+double sdm_oracle_round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double m = frexp(x, &e);                 /* x = m 2^e, 0.5 <= |m| < 1 */
+    double s = ldexp(m, 8);                  /* 128 <= |s| < 256: the 8 kept bits */
+    double r = nearbyint(s);                 /* default rounding mode: ties to even */
+    return ldexp(r, e - 8);
+}
+
+static int token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
+                      int64_t hd, int64_t M, const int32_t *k_idx, const double *k_val,
+                      const double *v, const double *beta, const double *g,
+                      const int32_t *q_idx, const double *q_val, const int32_t *valid,
+                      double *bank, double *out, int64_t round_chunk)
 {
     if (p0 < 0 || p1 < p0 || T < 0 || W < 1 || R < 1 || hd < 1 || M < 1 || (G != 1 && G != W))
         return -3;
     double *retrieved = (double *)malloc(sizeof(double) * (size_t)hd);
     double *delta = (double *)malloc(sizeof(double) * (size_t)hd);
-    if (!retrieved || !delta) {
+    char *touched = round_chunk > 0 ? (char *)calloc((size_t)M, 1) : NULL;
+    if (!retrieved || !delta || (round_chunk > 0 && !touched)) {
         free(retrieved);
         free(delta);
+        free(touched);
         return -4;
     }
     int rc = 0;
@@ -84,6 +107,7 @@ int sdm_oracle_token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t 
                 double gamma = exp(g[tok * G + (G == 1 ? 0 : w)]);
                 double *row = B + (int64_t)ks[w] * hd;
                 for (int64_t c = 0; c < hd; ++c) row[c] *= gamma;
+                if (touched) touched[ks[w]] = 1;
             }
             /* retrieved = sum_w k_w * read_w */
             for (int64_t c = 0; c < hd; ++c) retrieved[c] = 0.0;
@@ -104,9 +128,42 @@ int sdm_oracle_token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t 
                 const double *row = B + (int64_t)qs[r] * hd;
                 for (int64_t c = 0; c < hd; ++c) o[c] += qv[r] * row[c];
             }
+            if (touched) {
+                for (int64_t c = 0; c < hd; ++c) o[c] = sdm_oracle_round_bf16(o[c]);
+                if ((t + 1) % round_chunk == 0 || t + 1 == nvalid) {
+                    for (int64_t s = 0; s < M; ++s) {
+                        if (!touched[s]) continue;
+                        double *row = B + s * hd;
+                        for (int64_t c = 0; c < hd; ++c) row[c] = sdm_oracle_round_bf16(row[c]);
+                        touched[s] = 0;
+                    }
+                }
+            }
         }
     }
     free(retrieved);
     free(delta);
+    free(touched);
     return rc;
+}
+
+int sdm_oracle_token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
+                          int64_t hd, int64_t M, const int32_t *k_idx, const double *k_val,
+                          const double *v, const double *beta, const double *g,
+                          const int32_t *q_idx, const double *q_val, const int32_t *valid,
+                          double *bank, double *out)
+{
+    return token_loop(p0, p1, T, W, R, G, hd, M, k_idx, k_val, v, beta, g, q_idx, q_val, valid,
+                      bank, out, 0);
+}
+
+int sdm_oracle_token_loop_bf16(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
+                               int64_t hd, int64_t M, int64_t chunk, const int32_t *k_idx,
+                               const double *k_val, const double *v, const double *beta,
+                               const double *g, const int32_t *q_idx, const double *q_val,
+                               const int32_t *valid, double *bank, double *out)
+{
+    if (chunk < 1) return -3;
+    return token_loop(p0, p1, T, W, R, G, hd, M, k_idx, k_val, v, beta, g, q_idx, q_val, valid,
+                      bank, out, chunk);
 }

@@ -8,7 +8,13 @@ import torch
 
 import workloads
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}   # infinity-norm relative error per output tensor
+TOL = {"f32": 1e-4, "bf16": 2e-2}   # infinity-norm relative error per output tensor, vs O1
+# bf16 banks are also compared with O1b, the token loop under the bfloat16 storage
+# contract (rows rounded once per chunk, readings rounded): the GPU must stay within
+# TOL_CONTRACT of it, and within max(TOL, SLACK x |O1b - O1|) of O1, since the contract
+# itself can exceed TOL on a bank that grows by many orders of magnitude.
+TOL_CONTRACT = 2e-2
+SLACK = 1.25
 
 
 def to_torch(inp: dict, device) -> dict:
@@ -53,18 +59,41 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref)) / scale)
 
 
-def oracle_ref(inp: dict, threads: int = 8):
+def oracle_ref(inp: dict, threads: int = 8, bf16_chunk=None):
     import oracle
-    return oracle.token_loop(oracle.as_f64_inputs(inp), threads=threads)
+    return oracle.token_loop(oracle.as_f64_inputs(inp), threads=threads, bf16_chunk=bf16_chunk)
 
 
-def assert_parity(out, bank, ref_out, ref_bank, dtype: str, what: str = ""):
+def parity(out, bank, inp: dict, C: int, what: str = "", threads: int = 8, streams=None):
+    """Check GPU readings and bank against O1 (and, for bf16 banks, O1b) on the given
+    streams of ``inp`` (all by default; ``out``/``bank`` hold exactly those streams)."""
+    ref = oracle_ref(inp, threads)
+    con = oracle_ref(inp, threads, bf16_chunk=C) if inp["dtype"] == "bf16" else None
+    check(out, bank, ref, con, inp["dtype"], what)
+
+
+def check(out, bank, ref, con, dtype: str, what: str = ""):
+    got = [f64(x) if isinstance(x, torch.Tensor) else x for x in (out, bank)]
     tol = TOL[dtype]
-    e_out = rel_err(f64(out) if isinstance(out, torch.Tensor) else out, ref_out)
-    e_bank = rel_err(f64(bank) if isinstance(bank, torch.Tensor) else bank, ref_bank)
-    print(f"{what}: readings rel err {e_out:.3e}, bank rel err {e_bank:.3e} (tol {tol})", flush=True)
-    assert np.isfinite(e_out) and e_out <= tol, (what, "readings", e_out)
-    assert np.isfinite(e_bank) and e_bank <= tol, (what, "bank", e_bank)
+    msg, checks = [], []
+    for name, g, r, c in zip(("readings", "bank"), got, ref, con if con is not None else (None, None)):
+        e = rel_err(g, r)
+        bar = tol
+        line = f"{name} vs O1 {e:.3e}"
+        if c is not None:
+            e_c, e_m = rel_err(g, c), rel_err(c, r)
+            bar = max(tol, SLACK * e_m)
+            line += f", vs O1b {e_c:.3e} (O1b vs O1 {e_m:.3e})"
+            checks.append((e_c, TOL_CONTRACT, name + " vs O1b"))
+        checks.append((e, bar, name + " vs O1"))
+        msg.append(line)
+    print(f"{what}: " + "; ".join(msg) + f" (tol {tol})", flush=True)
+    for e, bar, label in checks:
+        assert np.isfinite(e) and e <= bar, (what, label, e, bar)
+
+
+def assert_parity(out, bank, ref_out, ref_bank, dtype: str, what: str = "", con=None):
+    check(out, bank, (ref_out, ref_bank), con, dtype, what)
 
 
 def generate(wl, streams=None):

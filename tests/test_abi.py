@@ -58,10 +58,10 @@ def test_workspace_bytes(lib):
     assert f(8, 2048, 8, 8, 8, 64, 0) == 0                # chunk out of range
     assert f(8, 2048, 64, 0, 8, 64, 0) == 0               # W < 1
     assert f(8, 2048, 64, 8, 257, 64, 0) == 0             # R > 256
-    # 68 B per write entry, 12 B per read entry, 16 B per chunk-matrix element (+ alignment)
+    # 96 B per write entry, 28 B per read entry, 16 B per chunk-matrix element (+ alignment)
     per_chunk = step / 8
     E, F, C2 = 64 * 8, 64 * 8, 64 * 64
-    assert 68 * E + 12 * F + 16 * C2 <= per_chunk <= 68 * E + 12 * F + 16 * C2 + 24 * 256
+    assert 96 * E + 28 * F + 16 * C2 <= per_chunk <= 96 * E + 28 * F + 16 * C2 + 40 * 256
 
 
 class Call:

@@ -295,3 +295,64 @@ def test_pins_catch_a_dropped_decay(monkeypatch):
     monkeypatch.setattr(chunk_algebra, "phase1", wrong)
     o2, _, _ = chunk_algebra.forward(inp, 5)
     assert _rel(o2, o1) > 1e-6
+
+
+# ---------------------------------------------------------------- O1b: the bfloat16 storage contract
+
+def test_round_bf16_ties_to_even_without_double_rounding():
+    one = 1.0
+    assert oracle.round_bf16(one + 2 ** -8) == one                   # tie -> even
+    assert oracle.round_bf16(one + 3 * 2 ** -8) == one + 2 ** -6     # tie -> even (up)
+    assert oracle.round_bf16(one + 2 ** -8 + 2 ** -40) == one + 2 ** -7   # just above the tie: up
+    assert oracle.round_bf16(-(one + 2 ** -8 + 2 ** -40)) == -(one + 2 ** -7)
+    assert oracle.round_bf16(0.0) == 0.0 and oracle.round_bf16(3.0) == 3.0
+
+
+def test_round_bf16_matches_float32_bit_rounding():
+    """On float32 inputs (no double rounding possible) it equals the bit-level
+    float32 -> bfloat16 rounding of the input generator, an independent routine."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(4000) * np.exp(rng.uniform(-20, 20, 4000))).astype(np.float32)
+    ref = workloads.bf16_bits_to_f32(workloads.round_bf16_bits(x)).astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_bf16_loop_with_one_chunk_is_rounded_o1():
+    """With one chunk spanning the stream, no row is rounded before the end: readings
+    are O1's rounded, written rows are O1's rounded, other rows are untouched."""
+    inp = tiny_inputs(47, P=2, T=20, W=3, R=2, M=12, ragged=True)
+    o1, b1 = oracle.token_loop(inp)
+    ob, bb = oracle.token_loop(inp, bf16_chunk=64)
+    assert np.array_equal(ob, oracle.round_bf16(o1))
+    for p in range(2):
+        written = np.unique(inp["k_idx"][p, :inp["valid"][p]])
+        assert np.array_equal(bb[p, written], oracle.round_bf16(b1[p, written]))
+        rest = np.setdiff1d(np.arange(12), written)
+        assert np.array_equal(bb[p, rest], inp["bank"][p, rest])
+
+
+@pytest.mark.parametrize("C", [1, 2, 4])
+def test_bf16_loop_equals_o1_on_bf16_exact_values(C):
+    """Small integers, k = 1, no decay and beta = 1/2 keep every value a short dyadic
+    fraction: rounding is the identity and O1b equals O1 exactly."""
+    T, M, hd = 4, 2, 2
+    rng = np.random.default_rng(2)
+    inp = dict(bank=rng.integers(-4, 5, (1, M, hd)).astype(np.float64),
+               k_idx=rng.integers(0, M, (1, T, 1)).astype(np.int32), k_val=np.ones((1, T, 1)),
+               v=rng.integers(-4, 5, (1, T, hd)).astype(np.float64), beta=np.full((1, T), 0.5),
+               g=np.zeros((1, T, 1)), q_idx=rng.integers(0, M, (1, T, 1)).astype(np.int32),
+               q_val=np.ones((1, T, 1)), valid=np.array([T], np.int32))
+    o1, b1 = oracle.token_loop(inp)
+    ob, bb = oracle.token_loop(inp, bf16_chunk=C)
+    assert np.array_equal(o1, oracle.round_bf16(o1)) and np.array_equal(b1, oracle.round_bf16(b1))
+    assert np.array_equal(ob, o1) and np.array_equal(bb, b1)
+
+
+def test_bf16_loop_rounds_at_chunk_ends():
+    """Rounding a row at a chunk end changes what later chunks read: with a value that
+    is not bfloat16-exact, chunk size 1 and chunk size T disagree."""
+    inp = tiny_inputs(53, P=1, T=12, W=2, R=2, M=4, ragged=False)
+    o_a, _ = oracle.token_loop(inp, bf16_chunk=1)
+    o_b, _ = oracle.token_loop(inp, bf16_chunk=12)
+    assert not np.array_equal(o_a, o_b)
+    assert _rel(o_a, o_b) < 5e-2
