@@ -149,8 +149,8 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
 }
 
 // Phase-2 geometry from shapes only (the bits never depend on it): 128-byte column
-// slices (one cache line of each row), halved down to 32 bytes while that leaves fewer
-// than about one workgroup per CU; one workgroup per (stream, slice). Teams (K > 1) are
+// slices (one cache line of each row), halved while that leaves fewer than one
+// workgroup per CU; one workgroup per (stream, slice). Teams (K > 1) are
 // only taken from SDM_P2_GEOM="nv,K,block", which overrides the whole choice (for tuning
 // sweeps): their barriers need device-scope fences that write back and invalidate the
 // per-XCD L2, which costs more than they save on the shapes measured.
@@ -171,7 +171,7 @@ P2Geom plan_phase2(const Problem &pb, int V, int es, int cus, int lds_limit) {
         return g;
     }
     g.S = (hv + g.nv - 1) / g.nv;
-    while (g.nv > 1 && g.nv * V * es > 32 && int64_t(pb.P) * g.S < cus) {
+    while (g.nv > 1 && int64_t(pb.P) * g.S < cus) {
         g.nv >>= 1;
         g.S = (hv + g.nv - 1) / g.nv;
     }
@@ -179,8 +179,9 @@ P2Geom plan_phase2(const Problem &pb, int V, int es, int cus, int lds_limit) {
         g.nv >>= 1;
         g.S = (hv + g.nv - 1) / g.nv;
     }
-    // threads: about two gather items (token x vector) per thread
-    const int items = 2 * pb.C * g.nv;
+    // about two gather items (token x vector x part) per thread, 4 to 16 waves
+    const int parts = int64_t(pb.C) * pb.W >= 16384 ? 1 : (pb.W >= 32 ? 4 : (pb.W >= 16 ? 2 : 1));
+    const int items = 2 * pb.C * g.nv * parts;
     g.block = items >= 2048 ? 1024 : (items >= 1024 ? 512 : 256);
     return g;
 }

@@ -106,6 +106,7 @@ __device__ __forceinline__ void dot_row(const float *xrow, int n, const float *u
                                         float (&acc)[V]) {
     int j = 0;
     if (vec4) {
+#pragma unroll 4
         for (; j + 4 <= n; j += 4) {
             const float4 x = *reinterpret_cast<const float4 *>(xrow + j);
             const float *u0 = u + j * pitch;
@@ -123,6 +124,44 @@ __device__ __forceinline__ void dot_row(const float *xrow, int n, const float *u
         const float x = xrow[j];
 #pragma unroll
         for (int c = 0; c < V; ++c) acc[c] = fmaf(x, u[j * pitch + c], acc[c]);
+    }
+}
+
+// Reductions are cut into a shape-only number of contiguous parts (never the launch
+// geometry): each part is summed in order by one lane, and the parts of one output are
+// combined by a fixed xor butterfly, ((p0 + p1) + (p2 + p3)); every lane of the group ends
+// with the same bits (additions only, no fused products). Items come in wavefront-sized
+// chunks of 64: lane l of a chunk holds part l / (64 / parts) of output
+// chunk * (64 / parts) + l % (64 / parts), so the lanes of one part read neighbouring
+// outputs (broadcast / consecutive LDS words) and the partners sit 16 or 32 lanes apart.
+__host__ __device__ __forceinline__ int split_parts(int n) { return n >= 32 ? 4 : (n >= 16 ? 2 : 1); }
+// Gather: entries of one token; no split once a chunk has plenty of entries (C * width).
+__host__ __device__ __forceinline__ int gather_parts(int C, int width) {
+    return int64_t(C) * width >= 16384 ? 1 : split_parts(width);
+}
+// Matmul: columns of one row; no split for the largest chunks.
+__host__ __device__ __forceinline__ int matmul_parts(int C) { return C >= 256 ? 1 : split_parts(C); }
+
+__device__ __forceinline__ void split_item(int it, int parts, int &out, int &part) {
+    const int G = kWave / parts, ch = it >> 6, l = it & 63;
+    part = l / G;
+    out = ch * G + (l - part * G);
+}
+
+__host__ __device__ __forceinline__ int split_items(int outputs, int parts) {
+    const int G = kWave / parts;
+    return (outputs + G - 1) / G * kWave;
+}
+
+template <int V>
+__device__ __forceinline__ void combine_parts(float (&acc)[V], int parts) {
+    if (parts >= 4) {
+#pragma unroll
+        for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 16, 64);
+    }
+    if (parts >= 2) {
+#pragma unroll
+        for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
     }
 }
 
@@ -187,23 +226,35 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
         const int64_t tok0 = int64_t(p) * pb.T + int64_t(ti) * C;
         const int own_live = max(0, min(i1, nl) - i0);
 
-        // ---- gather of own live tokens: retrieved -> ub[i], inter -> ib[i - i0]
+        // ---- gather of own live tokens: retrieved -> ub[i], inter -> ib[i - i0]. Outputs
+        //      (token, vector) of the writes, then of the reads, each region in whole
+        //      wavefront chunks (split_item).
         const float *gw = reinterpret_cast<const float *>(cb + L.off_gw);
         const float *gr = reinterpret_cast<const float *>(cb + L.off_gr);
-        const int nitem = own_live * nvs;
-        for (int it = tid; it < 2 * nitem; it += BLOCK) {
-            const bool rd = it >= nitem;
-            const int k2 = rd ? it - nitem : it;
-            const int li = k2 / nvs, vq = k2 - li * nvs;
+        const int sfw = gather_parts(C, W), sfr = gather_parts(C, R);
+        const int nout = own_live * nvs;
+        const int nwp = split_items(nout, sfw), nrp = split_items(nout, sfr);
+        for (int it = tid; it < nwp + nrp; it += BLOCK) {
+            const bool rd = it >= nwp;
+            const int sf = rd ? sfr : sfw;
+            int o, blk;
+            split_item(rd ? it - nwp : it, sf, o, blk);
+            const bool live = o < nout;
+            const int li = live ? o / nvs : 0, vq = live ? o - li * nvs : 0;
             const int i = i0 + li;
             const int width = rd ? R : W;
-            const int32_t *ids = (rd ? pb.q_idx : pb.k_idx) + (tok0 + i) * width;
-            const float *wts = (rd ? gr : gw) + int64_t(i) * width;
+            const int per = (width + sf - 1) / sf;
+            const int w0 = min(width, blk * per), w1 = live ? min(width, w0 + per) : w0;
+            const int32_t *ids = (rd ? pb.q_idx : pb.k_idx) + (tok0 + i) * width + w0;
+            const float *wts = (rd ? gr : gw) + int64_t(i) * width + w0;
             float acc[V];
-            gather_row<T, V>(bank, hd, ids, wts, width, int64_t(vq0 + vq) * V, acc);
-            float *dst = rd ? ib + li * cw + vq * V : ub + i * cw + vq * V;
+            gather_row<T, V>(bank, hd, ids, wts, w1 - w0, int64_t(vq0 + vq) * V, acc);
+            combine_parts<V>(acc, sf);
+            if (live && blk == 0) {
+                float *dst = rd ? ib + li * cw + vq * V : ub + i * cw + vq * V;
 #pragma unroll
-            for (int c = 0; c < V; ++c) dst[c] = acc[c];
+                for (int c = 0; c < V; ++c) dst[c] = acc[c];
+            }
         }
         __syncthreads();
 
@@ -242,27 +293,41 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
         const float *QX = reinterpret_cast<const float *>(cb + L.off_QX);
         const float *X = reinterpret_cast<const float *>(cb + L.off_X);
         const int own_rows = max(0, min(i1, rows) - i0);
-        for (int it = tid; it < own_rows * nvs; it += BLOCK) {
-            const int li = it / nvs, vq = it - li * nvs;
+        // Output (row, vector); part p sums columns [p * cq, (p + 1) * cq) of the row.
+        const int sfm = matmul_parts(C), cq = (((C + sfm - 1) / sfm) + 3) & ~3;
+        const int nmo = own_rows * nvs;
+        for (int it = tid; it < split_items(nmo, sfm); it += BLOCK) {
+            int k3, blk;
+            split_item(it, sfm, k3, blk);
+            const bool exists = k3 < nmo;
+            const int li = exists ? k3 / nvs : 0, vq = exists ? k3 - li * nvs : 0;
             const int i = i0 + li;
+            const bool live = exists && i < nl;
+            const int j0 = min(i + 1, blk * cq), j1 = live ? min(i + 1, j0 + cq) : j0;
             float o[V];
 #pragma unroll
             for (int c = 0; c < V; ++c) o[c] = 0.0f;
-            if (i < nl) {
-                dot_row<V>(QX + int64_t(i) * C, i + 1, ub + vq * V, cw, vec4, o);
-                const float *ir = ib + li * cw + vq * V;
+            dot_row<V>(QX + int64_t(i) * C + j0, j1 - j0, ub + j0 * cw + vq * V, cw, vec4, o);
+            combine_parts<V>(o, sfm);
+            float d[V];
+            if (K > 1) {
 #pragma unroll
-                for (int c = 0; c < V; ++c) o[c] += ir[c];
-                if (K > 1) {
-                    float d[V];
-#pragma unroll
-                    for (int c = 0; c < V; ++c) d[c] = 0.0f;
-                    dot_row<V>(X + int64_t(i) * C, i + 1, ub + vq * V, cw, vec4, d);
-#pragma unroll
-                    for (int c = 0; c < V; ++c) xd[i * cw + vq * V + c] = d[c];
-                }
+                for (int c = 0; c < V; ++c) d[c] = 0.0f;
+                dot_row<V>(X + int64_t(i) * C + j0, j1 - j0, ub + j0 * cw + vq * V, cw, vec4, d);
+                combine_parts<V>(d, sfm);
             }
-            Vec<T, V>::store(out + (tok0 + i) * hd + int64_t(vq0 + vq) * V, o);
+            if (exists && blk == 0) {
+                if (live) {
+                    const float *ir = ib + li * cw + vq * V;
+#pragma unroll
+                    for (int c = 0; c < V; ++c) o[c] += ir[c];
+                    if (K > 1) {
+#pragma unroll
+                        for (int c = 0; c < V; ++c) xd[i * cw + vq * V + c] = d[c];
+                    }
+                }
+                Vec<T, V>::store(out + (tok0 + i) * hd + int64_t(vq0 + vq) * V, o);
+            }
         }
         const float *D;
         if (K > 1) {
@@ -272,15 +337,23 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
         } else {
             __syncthreads();
             // delta_v = X u into ib (inter is no longer needed)
-            for (int it = tid; it < nl * nvs; it += BLOCK) {
-                const int i = it / nvs, vq = it - i * nvs;
+            const int ndo = nl * nvs;
+            for (int it = tid; it < split_items(ndo, sfm); it += BLOCK) {
+                int k3, blk;
+                split_item(it, sfm, k3, blk);
+                const bool exists = k3 < ndo;
+                const int i = exists ? k3 / nvs : 0, vq = exists ? k3 - i * nvs : 0;
+                const int j0 = min(i + 1, blk * cq), j1 = exists ? min(i + 1, j0 + cq) : j0;
                 float d[V];
 #pragma unroll
                 for (int c = 0; c < V; ++c) d[c] = 0.0f;
-                dot_row<V>(X + int64_t(i) * C, i + 1, ub + vq * V, cw, vec4, d);
-                float *dr = ib + i * cw + vq * V;
+                dot_row<V>(X + int64_t(i) * C + j0, j1 - j0, ub + j0 * cw + vq * V, cw, vec4, d);
+                combine_parts<V>(d, sfm);
+                if (exists && blk == 0) {
+                    float *dr = ib + i * cw + vq * V;
 #pragma unroll
-                for (int c = 0; c < V; ++c) dr[c] = d[c];
+                    for (int c = 0; c < V; ++c) dr[c] = d[c];
+                }
             }
             D = ib;
         }
