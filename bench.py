@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, datasheet
-KERNELS = ("p1_sort", "p1_groups", "p1_reads", "p1_gram_sparse", "p1_gram_hot", "wy_solve", "phase2")
+KERNELS = ("p1_sort", "p1_groups", "p1_reads", "p1_gram_cold", "p1_gram_hot", "wy_solve", "phase2")
 
 
 def parse():

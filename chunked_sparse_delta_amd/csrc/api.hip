@@ -78,10 +78,14 @@ int device_info(DeviceInfo **out) {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int sort_passes(int64_t M) {
+int key_bits(int64_t M) {
     int bits = 0;
     for (int64_t m = M - 1; m > 0; m >>= 1) ++bits;
-    int passes = (bits + 7) / 8;
+    return bits;
+}
+
+int sort_passes(int64_t M) {
+    int passes = (key_bits(M) + 7) / 8;
     return passes < 1 ? 1 : passes;
 }
 
@@ -138,7 +142,7 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     if (hd % vec == 0 && (!need_bank || (aligned(v, 16) && aligned(bank_data, 16) && aligned(out, 16)))) V = vec;
     Problem pb{};
     pb.P = P; pb.T = T; pb.C = C; pb.Nt = int32_t((int64_t(T) + C - 1) / C); pb.W = W; pb.R = R; pb.G = G; pb.hd = hd;
-    pb.M = M; pb.dtype = dtype; pb.sort_passes = sort_passes(M);
+    pb.M = M; pb.dtype = dtype; pb.sort_passes = sort_passes(M); pb.key_bits = key_bits(M);
     pb.k_idx = slots->write; pb.q_idx = slots->read; pb.k_val = weights->write; pb.q_val = weights->read;
     pb.beta = beta; pb.g = g; pb.v = v; pb.valid = valid; pb.bank = bank_data; pb.out = out;
     ck->pb = pb;

@@ -101,6 +101,7 @@ struct Problem {
     int64_t M;
     int32_t dtype;           // 0 f32, 1 bf16
     int32_t sort_passes;     // 8-bit LSD radix passes over the slot id
+    int32_t key_bits;        // bits of the largest slot id (M - 1)
     const int32_t *k_idx;    // [P, T, W]
     const int32_t *q_idx;    // [P, T, R]
     const void *k_val;       // [P, T, W] bank dtype
@@ -127,33 +128,33 @@ __device__ __forceinline__ float load_weight(const void *base, int64_t i, int32_
 // ---------------------------------------------------------------------------------------
 // Workspace of one slab: `nchunks` chunks, chunk n = p * slab_steps + (ti - ti0).
 // Every array is 256-byte aligned. E = C * W write entries, F = C * R read entries.
+// "Sorted position" m indexes the chunk's write entries sorted by (slot, token); the
+// entries of one slot form a contiguous write group, members in token order.
+// Transposed per-entry arrays hold entry (token i, slot index x) at x * C + i, so that
+// threads owning consecutive tokens read consecutive records.
 // ---------------------------------------------------------------------------------------
 struct ChunkLayout {
-    int64_t E, F, C2;
+    int64_t E, F, C2, NB, HMAX;
     // per-chunk strides (elements)
     int64_t off_key0, off_val0, off_key1, off_val1;   // radix-sort double buffer (u32)
-    int64_t off_spos;     // [E] i32: sorted position of write entry e
-    int64_t off_stok;     // [E] i32: token of sorted position
-    int64_t off_sL;       // [E] f32: cumulative log-decay at sorted position
+    int64_t off_spk;      // [E] int4 per sorted position: {slot, token, bits k, bits L}
     int64_t off_shead;    // [E] i32: first sorted position of the group
-    int64_t off_mrec;     // [E] int2: DW member record {token, bits of k exp(L_last - L)}
-    int64_t off_sk;       // [E] f32: k at sorted position
-    int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
-    int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
-    int64_t off_rpos;     // [F] i32: sorted position of the latest write of the read slot, or -1
-    int64_t off_rL;       // [F] f32: that write's cumulative log-decay (0 if none)
+    int64_t off_sgrp;     // [E] i32: group of sorted position
     int64_t off_gpos;     // [E+1] i32: group start positions
     int64_t off_grec;     // [E] int4: DW group record {slot, first position, members, bits of exp(L_last)}
-    int64_t off_sgrp;     // [E] i32: group of sorted position
+    int64_t off_mrec;     // [E] int2: DW member record {token, bits of k exp(L_last - L)}
+    int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
+    int64_t off_ecr;      // [E] int4 transposed: cold write entry {a, m, bits k, bits L} (a == m: none)
     int64_t off_ghot;     // [E] i32: hot index of group, or -1
-    int64_t off_whot;     // [E] i32: hot index of write entry's group, or -1 (entry order)
-    int64_t off_ka;       // [E] f32: k exp(L - L_ref) of a hot write entry (entry order)
-    int64_t off_kb;       // [E] f32: k exp(L_ref - L) of a hot write entry (entry order)
-    int64_t off_crange;   // [E] int2: sorted positions [a, m) of the earlier members of a cold group
-    int64_t off_rhot;     // [F] i32: hot index of the read slot's group, or -1
-    int64_t off_rval;     // [F] f32: q exp(Lr - L_ref) of a hot read entry
-    int64_t off_rcrange;  // [F] int2: sorted positions [a, rpos + 1) of a cold read's members
-    int64_t off_meta;     // [4] i32: n_live, E_live, ngroups, hot groups
+    int64_t off_ska;      // [E] f32 per sorted position of a hot group: k exp(L - L_ref)
+    int64_t off_skb;      // [E] f32 per sorted position of a hot group: k exp(L_ref - L)
+    int64_t off_hgrp;     // [HMAX] i32: group of hot index
+    int64_t off_bstart;   // [NB+1] i32: first sorted position of each slot bucket
+    int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
+    int64_t off_rcr;      // [F] int4 transposed: cold read {a, end, bits q, bits Lr} (a == end: none)
+    int64_t off_rhot;     // [F] i32 transposed: hot index of the read slot's group, or -1
+    int64_t off_rval;     // [F] f32 transposed: q exp(Lr - L_ref) of a hot read
+    int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
     int64_t words;        // 4-byte words per chunk
@@ -161,39 +162,45 @@ struct ChunkLayout {
 
 inline int64_t align_words(int64_t w) { return (w + 63) & ~int64_t(63); }   // 256 B
 
+// Number of slot buckets of the search index of a chunk of E write entries: about one
+// bucket per entry, at most 2^14.
+__host__ __device__ inline int bucket_bits(int64_t E) {
+    int b = 1;
+    while (b < 14 && (int64_t(1) << b) < E) ++b;
+    return b;
+}
+
 inline ChunkLayout make_layout(int C, int W, int R) {
     ChunkLayout L{};
     L.E = int64_t(C) * W;
     L.F = int64_t(C) * R;
     L.C2 = int64_t(C) * C;
+    L.NB = int64_t(1) << bucket_bits(L.E);
+    L.HMAX = L.E / kHotMin + 1;
     int64_t o = 0;
     auto take = [&](int64_t n) { int64_t r = o; o += align_words(n); return r; };
     L.off_key0 = take(L.E);
     L.off_val0 = take(L.E);
     L.off_key1 = take(L.E);
     L.off_val1 = take(L.E);
-    L.off_spos = take(L.E);
-    L.off_stok = take(L.E);
-    L.off_sL = take(L.E);
+    L.off_spk = take(4 * L.E);
     L.off_shead = take(L.E);
-    L.off_mrec = take(2 * L.E);
-    L.off_sk = take(L.E);
-    L.off_gw = take(L.E);
-    L.off_gr = take(L.F);
-    L.off_rpos = take(L.F);
-    L.off_rL = take(L.F);
+    L.off_sgrp = take(L.E);
     L.off_gpos = take(L.E + 1);
     L.off_grec = take(4 * L.E);
-    L.off_sgrp = take(L.E);
+    L.off_mrec = take(2 * L.E);
+    L.off_gw = take(L.E);
+    L.off_ecr = take(4 * L.E);
     L.off_ghot = take(L.E);
-    L.off_whot = take(L.E);
-    L.off_ka = take(L.E);
-    L.off_kb = take(L.E);
-    L.off_crange = take(2 * L.E);
+    L.off_ska = take(L.E);
+    L.off_skb = take(L.E);
+    L.off_hgrp = take(L.HMAX);
+    L.off_bstart = take(L.NB + 1);
+    L.off_gr = take(L.F);
+    L.off_rcr = take(4 * L.F);
     L.off_rhot = take(L.F);
     L.off_rval = take(L.F);
-    L.off_rcrange = take(2 * L.F);
-    L.off_meta = take(4);
+    L.off_meta = take(8);
     L.off_beta = take(C);
     L.off_A = take(L.C2);
     L.off_QK = take(L.C2);

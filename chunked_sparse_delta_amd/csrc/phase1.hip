@@ -7,18 +7,19 @@
 //   p1_sort    stable LSD radix sort of the chunk's write entries by slot id
 //              (entries enter in token order, so equal slots end in token order:
 //              each run of one slot is that slot's write group)
-//   p1_groups  group table, per-entry cumulative log-decay L as a sequential scan over
-//              each group in token order, gather weights k exp(L), and the DW records:
-//              per group {slot, first position, members, exp(L_last)}, per member
-//              {token, k exp(L_last - L)}
-//              and the split of the groups into hot (many members: their pair terms go
-//              to the matrix cores) and cold (their pair terms are summed directly)
+//   p1_groups  block-parallel passes over the sorted entries: group table, the
+//              cumulative log-decay L of each member (a segmented scan over each group in
+//              token order), gather weights k exp(L), the DW records (per group {slot,
+//              first position, members, exp(L_last)}, per member {token, k exp(L_last -
+//              L)}), a bucket index of the sorted slots for the read lookups, and the split
+//              of the groups into hot (many members, bounded decay span: their pair terms
+//              go to the matrix cores) and cold (their pair terms are summed directly)
 //   p1_reads   for each read entry, the latest write of its slot at or before its token
-//              (binary search), its L and gather weight q exp(L)
-//   p1_gram_sparse  the cold pair terms of A (strict lower) and QK (lower with diagonal)
-//              by row ownership: the thread of row i adds its entries' pair terms in a
-//              fixed order into an LDS window of columns
-//   p1_gram_hot     the hot pair terms as dense products on the matrix cores
+//              (bucketed binary search), its L and gather weight q exp(L)
+//   p1_gram_cold  the cold pair terms of A (strict lower) and QK (lower with diagonal) by
+//              row ownership: the thread of row i adds its entries' pair terms in a fixed
+//              order into an LDS window of columns
+//   p1_gram_hot   the hot pair terms as dense products on the matrix cores
 // No float atomics anywhere: every element has one writer and a fixed summation order.
 #include "common.h"
 
@@ -122,146 +123,259 @@ __global__ __launch_bounds__(BLOCK) void p1_sort_kernel(Problem pb, Slab sl) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Block scans over one tile of BLOCK elements (one per thread, thread order), continuing
+// the previous tile's inclusive value. Wave scans by shuffles, then each wave adds the
+// totals of the waves before it; every sum has a fixed shape, so the bits depend only on
+// the data.
+// ---------------------------------------------------------------------------------------
+template <int NW>
+struct TileScan {
+    int32_t cnt[NW];
+    int32_t mx[NW];
+    float val[NW];
+    int32_t flag[NW];
+    int32_t carry_cnt, carry_mx;
+    float carry_val;
+};
+
+// One tile of three inclusive scans: a count (head flags), a running maximum (head
+// positions) and a sum of x restarted at every head (segmented). Updates the carries.
+template <int NW>
+__device__ __forceinline__ void tile_scan3(TileScan<NW> &ts, int32_t &cnt, int32_t &mx, float &x, int head) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int f = head;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t c = __shfl_up(cnt, d, 64);
+        const int32_t m = __shfl_up(mx, d, 64);
+        const float y = __shfl_up(x, d, 64);
+        const int fy = __shfl_up(f, d, 64);
+        if (lane >= d) {
+            cnt += c;
+            mx = max(mx, m);
+            if (!f) x = y + x;
+            f |= fy;
+        }
+    }
+    if (lane == 63) {
+        ts.cnt[wv] = cnt;
+        ts.mx[wv] = mx;
+        ts.val[wv] = x;
+        ts.flag[wv] = f;
+    }
+    __syncthreads();
+    int32_t pc = ts.carry_cnt, pm = ts.carry_mx;
+    float pv = ts.carry_val;
+    for (int k = 0; k < wv; ++k) {
+        pc += ts.cnt[k];
+        pm = max(pm, ts.mx[k]);
+        pv = ts.flag[k] ? ts.val[k] : pv + ts.val[k];
+    }
+    cnt += pc;
+    mx = max(mx, pm);
+    if (!f) x = pv + x;
+    __syncthreads();
+    if (tid == NW * kWave - 1) {
+        ts.carry_cnt = cnt;
+        ts.carry_mx = mx;
+        ts.carry_val = x;
+    }
+    __syncthreads();
+}
+
+// Exclusive ballot compaction of one tile: returns the rank of a set flag among the set
+// flags of the tile (thread order) plus the running total, which it advances.
+template <int NW>
+__device__ __forceinline__ int32_t tile_compact(bool flag, int32_t *wsum, int32_t *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint64_t b = __ballot(flag);
+    if (lane == 0) wsum[wv] = __popcll(b);
+    __syncthreads();
+    int32_t off = *total;
+    for (int k = 0; k < wv; ++k) off += wsum[k];
+    const int32_t rank = off + __popcll(b & lanemask_lt(lane));
+    __syncthreads();
+    if (tid == 0) {
+        int32_t t = *total;
+        for (int k = 0; k < NW; ++k) t += wsum[k];
+        *total = t;
+    }
+    __syncthreads();
+    return rank;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    return v;
+}
+
+__device__ __forceinline__ int bucket_shift(const Problem &pb, int64_t E) {
+    const int s = pb.key_bits - bucket_bits(E);
+    return s > 0 ? s : 0;
+}
+
+constexpr int kMaxHot = kMaxChunk * kMaxWidth / kHotMin;   // hot groups of a chunk, at most
+
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
     constexpr int NW = BLOCK / kWave;
+    __shared__ TileScan<NW> ts;
     __shared__ int32_t wsum[NW];
-    __shared__ int32_t woff[NW];
-    __shared__ int32_t gcount, hcount;
+    __shared__ int32_t ncand, nhot;
+    __shared__ int32_t cand[kMaxHot];
+    __shared__ uint8_t cand_hot[kMaxHot];
     const int64_t n = blockIdx.x;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     const int W = pb.W, C = pb.C;
-    const int64_t El = int64_t(nl) * W;
+    const int32_t El = nl * W;
     const ChunkLayout &L = sl.lay;
     uint32_t *cb = sl.chunk(n);
     const int fin = (pb.sort_passes - 1) & 1;
     const uint32_t *skey = cb + (fin ? L.off_key1 : L.off_key0);
     const uint32_t *sval = cb + (fin ? L.off_val1 : L.off_val0);
-    int32_t *spos = reinterpret_cast<int32_t *>(cb + L.off_spos);
-    int32_t *stok = reinterpret_cast<int32_t *>(cb + L.off_stok);
-    float *sL = reinterpret_cast<float *>(cb + L.off_sL);
+    int4 *spk = reinterpret_cast<int4 *>(cb + L.off_spk);
     int32_t *shead = reinterpret_cast<int32_t *>(cb + L.off_shead);
-    int2 *mrec = reinterpret_cast<int2 *>(cb + L.off_mrec);
-    float *sk = reinterpret_cast<float *>(cb + L.off_sk);
-    float *gw = reinterpret_cast<float *>(cb + L.off_gw);
+    int32_t *sgrp = reinterpret_cast<int32_t *>(cb + L.off_sgrp);
     int32_t *gpos = reinterpret_cast<int32_t *>(cb + L.off_gpos);
     int4 *grec = reinterpret_cast<int4 *>(cb + L.off_grec);
-    int32_t *sgrp = reinterpret_cast<int32_t *>(cb + L.off_sgrp);
+    int2 *mrec = reinterpret_cast<int2 *>(cb + L.off_mrec);
+    float *gw = reinterpret_cast<float *>(cb + L.off_gw);
+    int4 *ecr = reinterpret_cast<int4 *>(cb + L.off_ecr);
     int32_t *ghot = reinterpret_cast<int32_t *>(cb + L.off_ghot);
-    int32_t *whot = reinterpret_cast<int32_t *>(cb + L.off_whot);
-    float *ka = reinterpret_cast<float *>(cb + L.off_ka);
-    float *kb = reinterpret_cast<float *>(cb + L.off_kb);
-    int2 *crange = reinterpret_cast<int2 *>(cb + L.off_crange);
+    float *ska = reinterpret_cast<float *>(cb + L.off_ska);
+    float *skb = reinterpret_cast<float *>(cb + L.off_skb);
+    int32_t *hgrp = reinterpret_cast<int32_t *>(cb + L.off_hgrp);
+    int32_t *bstart = reinterpret_cast<int32_t *>(cb + L.off_bstart);
     int32_t *meta = reinterpret_cast<int32_t *>(cb + L.off_meta);
     float *beta_c = reinterpret_cast<float *>(cb + L.off_beta);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const uint64_t lt = lanemask_lt(lane);
     const int64_t tok0 = int64_t(p) * pb.T + int64_t(ti) * C;
+    const int bsh = bucket_shift(pb, L.E);
+    const int32_t NB = int32_t(L.NB);
 
     if (tid == 0) {
-        gcount = 0;
-        hcount = 0;
+        ts.carry_cnt = 0;
+        ts.carry_mx = -1;
+        ts.carry_val = 0.0f;
+        ncand = 0;
+        nhot = 0;
     }
     for (int i = tid; i < C; i += BLOCK) beta_c[i] = i < nl ? pb.beta[tok0 + i] : 0.0f;
+    for (int64_t e = El + tid; e < L.E; e += BLOCK) gw[e] = 0.0f;
     __syncthreads();
-    // Group starts: positions whose slot differs from the previous position's.
-    for (int64_t t0 = 0; t0 < El; t0 += BLOCK) {
-        const int64_t pos = t0 + tid;
-        const bool head = pos < El && (pos == 0 || skey[pos] != skey[pos - 1]);
-        const uint64_t b = __ballot(head);
-        if (lane == 0) wsum[wv] = __popcll(b);
-        __syncthreads();
-        if (tid == 0) {
-            int32_t run = gcount;
-            for (int w = 0; w < NW; ++w) {
-                woff[w] = run;
-                run += wsum[w];
-            }
-            gcount = run;
+
+    // Pass 1, tile by tile over the sorted positions: group starts, group index, last
+    // group start, cumulative log-decay L, the per-position record, bucket starts.
+    for (int32_t t0 = 0; t0 < El; t0 += BLOCK) {
+        const int32_t m = t0 + tid;
+        const bool ok = m < El;
+        uint32_t key = 0;
+        int head = 0;
+        int32_t i = 0;
+        float gv = 0.0f, kv = 0.0f;
+        if (ok) {
+            key = skey[m];
+            const uint32_t prev = m > 0 ? skey[m - 1] : ~key;
+            head = prev != key;
+            const int32_t e = int32_t(sval[m]);
+            i = e / W;
+            const int32_t w = e - i * W;
+            const int64_t tg = tok0 + i;
+            gv = pb.g[tg * pb.G + (pb.G == 1 ? 0 : w)];
+            kv = load_weight(pb.k_val, tg * W + w, pb.dtype);
+            const int32_t bp = m > 0 ? min(int32_t(prev >> bsh), NB - 1) : -1, bc = min(int32_t(key >> bsh), NB - 1);
+            for (int32_t b = bp + 1; b <= bc; ++b) bstart[b] = m;
         }
-        __syncthreads();
-        if (head) gpos[woff[wv] + __popcll(b & lt)] = int32_t(pos);
-        __syncthreads();
+        int32_t cnt = head, mx = head ? m : -1;
+        float Lc = gv;
+        tile_scan3<NW>(ts, cnt, mx, Lc, head);
+        if (ok) {
+            spk[m] = make_int4(int32_t(key), i, __float_as_int(kv), __float_as_int(Lc));
+            sgrp[m] = cnt - 1;
+            shead[m] = mx;
+            if (head) gpos[cnt - 1] = m;
+        }
     }
-    const int32_t ng = gcount;
+    const int32_t ng = ts.carry_cnt;
+    {
+        const int32_t bl = El > 0 ? min(int32_t(skey[El - 1] >> bsh), NB - 1) : -1;
+        for (int32_t b = bl + 1 + tid; b <= NB; b += BLOCK) bstart[b] = El;
+    }
     if (tid == 0) {
-        gpos[ng] = int32_t(El);
+        gpos[ng] = El;
         meta[0] = nl;
-        meta[1] = int32_t(El);
+        meta[1] = El;
         meta[2] = ng;
     }
+    for (int32_t g = tid; g < ng; g += BLOCK) ghot[g] = -1;
     __syncthreads();
-    // Walk 1, one thread per group in token order: cumulative log-decay L, gather weights,
-    // DW records, and whether the group is hot (many members, bounded decay span).
-    for (int32_t g = tid; g < ng; g += BLOCK) {
-        const int32_t a = gpos[g], e_end = gpos[g + 1];
-        float Lc = 0.0f, Lref = 0.0f, dev = 0.0f;
-        for (int32_t m = a; m < e_end; ++m) {
-            const int32_t e = int32_t(sval[m]);
-            const int32_t i = e / W, w = e - i * W;
-            const int64_t tg = tok0 + i;
-            Lc += pb.g[tg * pb.G + (pb.G == 1 ? 0 : w)];
-            if (m == a) Lref = Lc;
-            dev = fmaxf(dev, fabsf(Lc - Lref));
-            sL[m] = Lc;
-            stok[m] = i;
-            sk[m] = load_weight(pb.k_val, tg * W + w, pb.dtype);
-            spos[e] = m;
-            shead[m] = a;
-            sgrp[m] = g;
-        }
-        grec[g] = make_int4(int32_t(skey[a]), a, e_end - a, __float_as_int(expf(Lc)));
-        for (int32_t m = a; m < e_end; ++m) {
-            const int32_t e = int32_t(sval[m]);
-            const float Lm = sL[m], kv = sk[m];
-            mrec[m] = make_int2(stok[m], __float_as_int(kv * expf(Lc - Lm)));
-            gw[e] = kv * expf(Lm);
-        }
-        ghot[g] = (e_end - a >= kHotMin && dev <= kHotSpan) ? 1 : 0;
+
+    // Pass 2, per sorted position: DW records and gather weights.
+    for (int32_t m = tid; m < El; m += BLOCK) {
+        const int4 pk = spk[m];
+        const int32_t g = sgrp[m], a = shead[m], b = gpos[g + 1];
+        const float Lm = __int_as_float(pk.w), kv = __int_as_float(pk.z);
+        const float Llast = __int_as_float(spk[b - 1].w);
+        mrec[m] = make_int2(pk.y, __float_as_int(kv * expf(Llast - Lm)));
+        gw[int32_t(sval[m])] = kv * expf(Lm);
+        if (m == a) grec[g] = make_int4(pk.x, a, b - a, __float_as_int(expf(Llast)));
     }
-    __syncthreads();
-    // Hot indices in group order.
+
+    // Pass 3: hot groups. Candidates (at least kHotMin members) in group order; a wave
+    // per candidate finds its largest |L - L_first|; hot ones are numbered in order.
     for (int32_t t0 = 0; t0 < ng; t0 += BLOCK) {
         const int32_t g = t0 + tid;
-        const bool hot = g < ng && ghot[g] != 0;
-        const uint64_t b = __ballot(hot);
-        if (lane == 0) wsum[wv] = __popcll(b);
-        __syncthreads();
-        if (tid == 0) {
-            int32_t run = hcount;
-            for (int w = 0; w < NW; ++w) {
-                woff[w] = run;
-                run += wsum[w];
-            }
-            hcount = run;
-        }
-        __syncthreads();
-        if (g < ng) ghot[g] = hot ? woff[wv] + __popcll(b & lt) : -1;
-        __syncthreads();
+        const bool c = g < ng && gpos[g + 1] - gpos[g] >= kHotMin;
+        const int32_t r = tile_compact<NW>(c, wsum, &ncand);
+        if (c) cand[r] = g;
     }
-    if (tid == 0) meta[3] = hcount;
-    // Walk 2: per write entry, its hot index and factored decays, or its cold predecessors.
-    for (int32_t g = tid; g < ng; g += BLOCK) {
-        const int32_t a = gpos[g], e_end = gpos[g + 1];
-        const int32_t h = ghot[g];
-        const float Lref = sL[a];
-        for (int32_t m = a; m < e_end; ++m) {
-            const int32_t e = int32_t(sval[m]);
-            whot[e] = h;
-            if (h >= 0) {
-                const float d = sL[m] - Lref;
-                ka[e] = sk[m] * expf(d);
-                kb[e] = sk[m] * expf(-d);
-                crange[e] = make_int2(0, 0);
-            } else {
-                crange[e] = make_int2(a, m);
-            }
+    __syncthreads();
+    const int32_t nc = ncand;
+    for (int32_t c = wv; c < nc; c += NW) {
+        const int32_t g = cand[c], a = gpos[g], b = gpos[g + 1];
+        const float Lref = __int_as_float(spk[a].w);
+        float dev = 0.0f;
+        for (int32_t m = a + lane; m < b; m += kWave) dev = fmaxf(dev, fabsf(__int_as_float(spk[m].w) - Lref));
+        dev = wave_max(dev);
+        if (lane == 0) cand_hot[c] = dev <= kHotSpan ? 1 : 0;
+    }
+    __syncthreads();
+    for (int32_t t0 = 0; t0 < nc; t0 += BLOCK) {
+        const int32_t c = t0 + tid;
+        const bool h = c < nc && cand_hot[c];
+        const int32_t r = tile_compact<NW>(h, wsum, &nhot);
+        if (h) {
+            ghot[cand[c]] = r;
+            hgrp[r] = cand[c];
         }
     }
-    for (int64_t e = El + tid; e < L.E; e += BLOCK) gw[e] = 0.0f;
+    __syncthreads();
+    if (tid == 0) meta[3] = nhot;
+
+    // Pass 4, per sorted position: factored decays of hot members; the cold pair ranges
+    // (earlier members of the group) by token-major transposed entry.
+    for (int32_t m = tid; m < El; m += BLOCK) {
+        const int4 pk = spk[m];
+        const int32_t g = sgrp[m], a = shead[m];
+        const int32_t e = int32_t(sval[m]), w = e - pk.y * W;
+        int4 rec = make_int4(m, m, 0, 0);
+        if (ghot[g] >= 0) {
+            const float d = __int_as_float(pk.w) - __int_as_float(spk[a].w), kv = __int_as_float(pk.z);
+            ska[m] = kv * expf(d);
+            skb[m] = kv * expf(-d);
+        } else {
+            rec = make_int4(a, m, pk.z, pk.w);
+        }
+        ecr[int64_t(w) * C + pk.y] = rec;
+    }
 }
 
+// One thread per read entry. The latest write of the read slot at or before the read's
+// token is the last sorted position with (slot, token) <= (q, i), searched inside the
+// slot's bucket.
 __global__ __launch_bounds__(256) void p1_reads_kernel(Problem pb, Slab sl) {
     const int64_t n = blockIdx.y;
     const int64_t er = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -269,130 +383,111 @@ __global__ __launch_bounds__(256) void p1_reads_kernel(Problem pb, Slab sl) {
     if (er >= L.F) return;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
-    const int R = pb.R;
-    const int64_t El = int64_t(nl) * pb.W;
+    const int R = pb.R, C = pb.C;
     uint32_t *cb = sl.chunk(n);
-    const int fin = (pb.sort_passes - 1) & 1;
-    const uint32_t *skey = cb + (fin ? L.off_key1 : L.off_key0);
-    const int32_t *stok = reinterpret_cast<const int32_t *>(cb + L.off_stok);
-    const float *sL = reinterpret_cast<const float *>(cb + L.off_sL);
+    const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
     const int32_t *shead = reinterpret_cast<const int32_t *>(cb + L.off_shead);
     const int32_t *sgrp = reinterpret_cast<const int32_t *>(cb + L.off_sgrp);
     const int32_t *ghot = reinterpret_cast<const int32_t *>(cb + L.off_ghot);
+    const int32_t *bstart = reinterpret_cast<const int32_t *>(cb + L.off_bstart);
     float *gr = reinterpret_cast<float *>(cb + L.off_gr);
-    int32_t *rpos = reinterpret_cast<int32_t *>(cb + L.off_rpos);
-    float *rL = reinterpret_cast<float *>(cb + L.off_rL);
+    int4 *rcr = reinterpret_cast<int4 *>(cb + L.off_rcr);
     int32_t *rhot = reinterpret_cast<int32_t *>(cb + L.off_rhot);
     float *rval = reinterpret_cast<float *>(cb + L.off_rval);
-    int2 *rcrange = reinterpret_cast<int2 *>(cb + L.off_rcrange);
     const int32_t i = int32_t(er / R), r = int32_t(er - int64_t(i) * R);
+    const int64_t tr = int64_t(r) * C + i;
     if (i >= nl) {
         gr[er] = 0.0f;
-        rpos[er] = -1;
-        rL[er] = 0.0f;
-        rhot[er] = -1;
-        rcrange[er] = make_int2(0, 0);
+        rcr[tr] = make_int4(0, 0, 0, 0);
+        rhot[tr] = -1;
+        rval[tr] = 0.0f;
         return;
     }
-    const int64_t tg = int64_t(p) * pb.T + int64_t(ti) * pb.C + i;
-    const uint32_t q = uint32_t(pb.q_idx[tg * R + r]);
-    // First sorted position whose (slot, token) exceeds (q, i).
-    int64_t lo = 0, hi = El;
+    const int64_t tg = int64_t(p) * pb.T + int64_t(ti) * C + i;
+    const int32_t q = pb.q_idx[tg * R + r];
+    const int32_t b = min(int32_t(uint32_t(q) >> bucket_shift(pb, L.E)), int32_t(L.NB) - 1);
+    const int32_t b0 = bstart[b];
+    int32_t lo = b0, hi = bstart[b + 1];
     while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        const uint32_t km = skey[mid];
-        if (km < q || (km == q && stok[mid] <= i)) lo = mid + 1;
+        const int32_t mid = (lo + hi) >> 1;
+        const int4 pk = spk[mid];
+        if (pk.x < q || (pk.x == q && pk.y <= i)) lo = mid + 1;
         else hi = mid;
     }
-    const int64_t pos = lo - 1;
+    const int32_t pos = lo - 1;
     const float qv = load_weight(pb.q_val, tg * R + r, pb.dtype);
-    float l = 0.0f;
-    int32_t rp = -1, h = -1;
-    int2 cr = make_int2(0, 0);
-    float rv = 0.0f;
-    if (pos >= 0 && skey[pos] == q) {
-        rp = int32_t(pos);
-        l = sL[pos];
-        const int32_t a = shead[pos];
-        h = ghot[sgrp[pos]];
-        if (h >= 0) rv = qv * expf(l - sL[a]);
-        else cr = make_int2(a, rp + 1);
+    float l = 0.0f, rv = 0.0f;
+    int32_t h = -1;
+    int4 cr = make_int4(0, 0, 0, 0);
+    if (pos >= b0) {
+        const int4 pk = spk[pos];
+        if (pk.x == q) {
+            l = __int_as_float(pk.w);
+            const int32_t a = shead[pos];
+            h = ghot[sgrp[pos]];
+            if (h >= 0) rv = qv * expf(l - __int_as_float(spk[a].w));
+            else cr = make_int4(a, pos + 1, __float_as_int(qv), pk.w);
+        }
     }
     gr[er] = qv * expf(l);
-    rpos[er] = rp;
-    rL[er] = l;
-    rhot[er] = h;
-    rval[er] = rv;
-    rcrange[er] = cr;
+    rcr[tr] = cr;
+    rhot[tr] = h;
+    rval[tr] = rv;
 }
 
-// The cold part of A and QK (pairs of write groups that are not hot). Thread i owns row
-// i. Columns are covered in windows of WIN held in LDS (row pitch WIN + 1); each window
-// is written out whole, zeros included, so A and QK are fully defined here (+0 outside
-// their triangles) and the hot part is added afterwards. Row i sums its pair terms in
-// entry order: writes w = 0..W-1, then reads r = 0..R-1.
+// The cold part of A (blockIdx.y = 0: write entries) or QK (blockIdx.y = 1: read
+// entries). Thread i owns row i. Columns are covered in windows of WIN held in LDS (row
+// pitch WIN + 1); each window is written out whole, zeros included, so A and QK are fully
+// defined here (+0 outside their triangles) and the hot part is added afterwards. Row i
+// sums its pair terms in entry order, each entry's earlier group members in token order.
 template <int WIN>
-__global__ __launch_bounds__(256) void p1_gram_sparse_kernel(Problem pb, Slab sl) {
+__global__ __launch_bounds__(256) void p1_gram_cold_kernel(Problem pb, Slab sl) {
     extern __shared__ float lds[];
-    const int C = pb.C, W = pb.W, R = pb.R;
-    float *accA = lds;
-    float *accQ = lds + C * (WIN + 1);
+    const int C = pb.C;
     const int64_t n = blockIdx.x;
+    const bool qk = blockIdx.y != 0;
+    const int width = qk ? pb.R : pb.W;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     const ChunkLayout &L = sl.lay;
     uint32_t *cb = sl.chunk(n);
-    const int32_t *stok = reinterpret_cast<const int32_t *>(cb + L.off_stok);
-    const float *sL = reinterpret_cast<const float *>(cb + L.off_sL);
-    const float *sk = reinterpret_cast<const float *>(cb + L.off_sk);
-    const int2 *crange = reinterpret_cast<const int2 *>(cb + L.off_crange);
-    const int2 *rcrange = reinterpret_cast<const int2 *>(cb + L.off_rcrange);
-    float *A = reinterpret_cast<float *>(cb + L.off_A);
-    float *QK = reinterpret_cast<float *>(cb + L.off_QK);
-    const int tid = threadIdx.x;
-    const int i = tid;
-    const int64_t tg = int64_t(p) * pb.T + int64_t(ti) * C + i;
+    const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
+    const int4 *cr = reinterpret_cast<const int4 *>(cb + (qk ? L.off_rcr : L.off_ecr));
+    float *Mout = reinterpret_cast<float *>(cb + (qk ? L.off_QK : L.off_A));
+    const int i = threadIdx.x;
+    float *row = lds + i * (WIN + 1);
 
     for (int c0 = 0; c0 < C; c0 += WIN) {
         const int cw = C - c0 < WIN ? C - c0 : WIN;
         const int c1 = c0 + cw;
         if (i < C) {
-            float *ra = accA + i * (WIN + 1);
-            float *rq = accQ + i * (WIN + 1);
-            for (int j = 0; j < WIN; ++j) {
-                ra[j] = 0.0f;
-                rq[j] = 0.0f;
-            }
+            for (int j = 0; j < WIN; ++j) row[j] = 0.0f;
             if (i < nl && c0 <= i) {
-                for (int w = 0; w < W; ++w) {
-                    const int2 cr = crange[int64_t(i) * W + w];
-                    if (cr.y <= cr.x) continue;
-                    const float ki = sk[cr.y], Li = sL[cr.y];
-                    for (int32_t mm = cr.x; mm < cr.y; ++mm) {
-                        const int32_t tj = stok[mm];
-                        if (tj < c0) continue;
-                        if (tj >= c1) break;
-                        ra[tj - c0] += (ki * sk[mm]) * expf(Li - sL[mm]);
-                    }
-                }
-                for (int r = 0; r < R; ++r) {
-                    const int2 cr = rcrange[int64_t(i) * R + r];
-                    if (cr.y <= cr.x) continue;
-                    const float qv = load_weight(pb.q_val, tg * R + r, pb.dtype), Lr = sL[cr.y - 1];
-                    for (int32_t mm = cr.x; mm < cr.y; ++mm) {
-                        const int32_t tj = stok[mm];
-                        if (tj < c0) continue;
-                        if (tj >= c1) break;
-                        rq[tj - c0] += (qv * sk[mm]) * expf(Lr - sL[mm]);
+                for (int x0 = 0; x0 < width; x0 += 8) {
+                    int4 rec[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        rec[u] = x0 + u < width ? cr[int64_t(x0 + u) * C + i] : make_int4(0, 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int4 r = rec[u];
+                        if (r.y <= r.x) continue;
+                        const float kv = __int_as_float(r.z), Lv = __int_as_float(r.w);
+                        for (int32_t mm = r.x; mm < r.y; ++mm) {
+                            const int4 pk = spk[mm];
+                            const int32_t tj = pk.y;
+                            if (tj < c0) continue;
+                            if (tj >= c1) break;
+                            row[tj - c0] += (kv * __int_as_float(pk.z)) * expf(Lv - __int_as_float(pk.w));
+                        }
                     }
                 }
             }
         }
         __syncthreads();
-        for (int idx = tid; idx < C * cw; idx += blockDim.x) {
+        for (int idx = threadIdx.x; idx < C * cw; idx += blockDim.x) {
             const int r = idx / cw, c = idx - r * cw;
-            A[int64_t(r) * C + c0 + c] = accA[r * (WIN + 1) + c];
-            QK[int64_t(r) * C + c0 + c] = accQ[r * (WIN + 1) + c];
+            Mout[int64_t(r) * C + c0 + c] = lds[r * (WIN + 1) + c];
         }
         __syncthreads();
     }
@@ -401,12 +496,14 @@ __global__ __launch_bounds__(256) void p1_gram_sparse_kernel(Problem pb, Slab sl
 // The hot part of A and QK on the matrix cores. For hot write group h with reference
 // log-decay L_ref (its first member's), token t writing it carries Ka[t][h] = k e^(L-L_ref)
 // and Kb[t][h] = k e^(L_ref-L); a token reading it after a write carries
-// Qa[t][h] = q e^(Lr-L_ref). Then A += tril(Ka Kb^T, -1) and QK += tril(Qa Kb^T), the
-// factored exponents multiplying back to the pair decays e^(L_t - L_t'). One workgroup per
-// chunk; the hot slots are taken HS at a time into LDS; every wave owns a fixed set of
-// 16 x 16 lower output tiles and accumulates them with v_mfma_f32_16x16x4_f32 over the
-// slots in ascending order (a fixed order), then adds them to the cold part in memory.
-constexpr int kHS = 16;            // hot slots per LDS slice
+// Qa[t][h] = q e^(Lr-L_ref) (summed over its reads of the slot). Then A += tril(Ka Kb^T, -1)
+// and QK += tril(Qa Kb^T), the factored exponents multiplying back to the pair decays
+// e^(L_t - L_t'). One workgroup per chunk; the hot groups are taken HS at a time into LDS
+// (Ka, Kb from the groups' member ranges, Qa from each token's reads in read order);
+// every wave owns a fixed set of 16 x 16 lower output tiles and accumulates them with
+// v_mfma_f32_16x16x4_f32 over the hot groups in ascending order (a fixed order), then
+// adds them to the cold part in memory.
+constexpr int kHS = 32;            // hot groups per LDS slice
 constexpr int kHP = kHS + 1;       // LDS row pitch
 constexpr int kHotBlock = 512;
 constexpr int kHotMaxTiles = 34;   // per wave: 2 * 136 lower 16x16 tiles of C = 256 over 8 waves
@@ -424,13 +521,15 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
     if (nl == 0) return;
     const int nhot = meta[3];
     if (nhot == 0) return;
-    const int C = pb.C, W = pb.W, R = pb.R;
+    const int C = pb.C, R = pb.R;
     const int nt = (C + 15) / 16, rows = nt * 16;
     const int T1 = nt * (nt + 1) / 2, T2 = 2 * T1;
     float *Ka = lds, *Kb = lds + rows * kHP, *Qa = lds + 2 * rows * kHP;
-    const int32_t *whot = reinterpret_cast<const int32_t *>(cb + L.off_whot);
-    const float *ka = reinterpret_cast<const float *>(cb + L.off_ka);
-    const float *kbv = reinterpret_cast<const float *>(cb + L.off_kb);
+    const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
+    const int32_t *gpos = reinterpret_cast<const int32_t *>(cb + L.off_gpos);
+    const int32_t *hgrp = reinterpret_cast<const int32_t *>(cb + L.off_hgrp);
+    const float *ska = reinterpret_cast<const float *>(cb + L.off_ska);
+    const float *skb = reinterpret_cast<const float *>(cb + L.off_skb);
     const int32_t *rhot = reinterpret_cast<const int32_t *>(cb + L.off_rhot);
     const float *rval = reinterpret_cast<const float *>(cb + L.off_rval);
     float *A = reinterpret_cast<float *>(cb + L.off_A);
@@ -454,20 +553,23 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
     for (int h0 = 0; h0 < nhot; h0 += kHS) {
         for (int idx = tid; idx < 3 * rows * kHP; idx += kHotBlock) lds[idx] = 0.0f;
         __syncthreads();
-        if (tid < nl) {
-            const int i = tid;
-            for (int w = 0; w < W; ++w) {
-                const int64_t e = int64_t(i) * W + w;
-                const int h = whot[e] - h0;
-                if (h >= 0 && h < kHS) {
-                    Ka[i * kHP + h] = ka[e];
-                    Kb[i * kHP + h] = kbv[e];
-                }
+        // Ka, Kb: a wave per hot group of the slice, lanes over its members.
+        for (int hh = wv; hh < kHS; hh += NWAVE) {
+            const int h = h0 + hh;
+            if (h >= nhot) break;
+            const int32_t g = hgrp[h], a = gpos[g], b = gpos[g + 1];
+            for (int32_t m = a + lane; m < b; m += kWave) {
+                const int t = spk[m].y;
+                Ka[t * kHP + hh] = ska[m];
+                Kb[t * kHP + hh] = skb[m];
             }
+        }
+        // Qa: the thread of token t adds its hot reads of the slice in read order.
+        if (tid < nl) {
             for (int r = 0; r < R; ++r) {
-                const int64_t er = int64_t(i) * R + r;
-                const int h = rhot[er] - h0;
-                if (h >= 0 && h < kHS) Qa[i * kHP + h] += rval[er];
+                const int64_t x = int64_t(r) * C + tid;
+                const int h = rhot[x] - h0;
+                if (h >= 0 && h < kHS) Qa[tid * kHP + h] += rval[x];
             }
         }
         __syncthreads();
@@ -480,9 +582,9 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
                 if (t < T2) {
                     const float *Aop = t < T1 ? Ka : Qa;
                     const int ij = tile_ij[t < T1 ? t : t - T1];
-                    const float a = Aop[((ij >> 4) * 16 + rr) * kHP + kk];
-                    const float b = Kb[((ij & 15) * 16 + rr) * kHP + kk];
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[q], 0, 0, 0);
+                    const float av = Aop[((ij >> 4) * 16 + rr) * kHP + kk];
+                    const float bv = Kb[((ij & 15) * 16 + rr) * kHP + kk];
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[q], 0, 0, 0);
                 }
             }
         }
@@ -510,17 +612,17 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
 constexpr int kSortBlock = 1024;
 constexpr int kGroupBlock = 1024;
 
-static int gram_win(int C) { return C > 128 ? 32 : 64; }
+static int gram_win(int C) { return C > 128 ? 128 : (C > 64 ? 128 : 64); }
 
-size_t gram_lds_bytes(int C) { return size_t(2) * C * (gram_win(C) + 1) * sizeof(float); }
+size_t gram_lds_bytes(int C) { return size_t(C) * (gram_win(C) + 1) * sizeof(float); }
 
 static size_t hot_lds_bytes(int C) { return size_t(3) * ((C + 15) / 16 * 16) * kHP * sizeof(float); }
 
 hipError_t phase1_prepare() {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_sparse_kernel<64>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(gram_lds_bytes(128)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_cold_kernel<64>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(gram_lds_bytes(64)));
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_sparse_kernel<32>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_cold_kernel<128>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(gram_lds_bytes(kMaxChunk)));
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_hot_kernel),
@@ -539,11 +641,11 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
     const unsigned fx = unsigned((sl.lay.F + 255) / 256);
     hipLaunchKernelGGL(p1_reads_kernel, dim3(fx, nch), dim3(256), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
-    const int gb = pb.C <= 64 ? 64 : (pb.C <= 128 ? 128 : 256);
+    const int gb = (pb.C + 63) / 64 * 64;
     if (gram_win(pb.C) == 64)
-        hipLaunchKernelGGL(p1_gram_sparse_kernel<64>, dim3(nch), dim3(gb), gram_lds_bytes(pb.C), st, pb, sl);
+        hipLaunchKernelGGL(p1_gram_cold_kernel<64>, dim3(nch, 2), dim3(gb), gram_lds_bytes(pb.C), st, pb, sl);
     else
-        hipLaunchKernelGGL(p1_gram_sparse_kernel<32>, dim3(nch), dim3(gb), gram_lds_bytes(pb.C), st, pb, sl);
+        hipLaunchKernelGGL(p1_gram_cold_kernel<128>, dim3(nch, 2), dim3(gb), gram_lds_bytes(pb.C), st, pb, sl);
     if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch), dim3(kHotBlock), hot_lds_bytes(pb.C), st, pb, sl);
     return hipGetLastError();

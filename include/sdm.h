@@ -92,7 +92,7 @@ typedef struct {
  * events: optional (NULL = none) array of num_events >= SDM_TIMING_EVENTS hipEvent_t
  * created by the caller; sdm_fwd then records them on `stream` at the kernel boundaries
  * of its first slab, in order: before the radix sort, before the group scan, before the
- * read lookup, before the sparse Gram kernel, before the dense (hot-slot) Gram kernel,
+ * read lookup, before the cold-pair Gram kernel, before the dense (hot-slot) Gram kernel,
  * before the solve, before Phase 2, after Phase 2.
  * Recording is asynchronous; the caller reads the elapsed times after synchronizing. */
 typedef struct {
@@ -108,8 +108,9 @@ typedef struct {
 /*
  * Workspace bytes sdm_fwd needs to run its steps in slabs of `slab_steps` steps
  * (0 = all Nt = ceil(tokens / chunk) steps in one slab). A slab holds every Phase-1
- * quantity and both solve outputs of its P * slab_steps chunks (96 B per write entry,
- * 28 B per read entry and 16 B per chunk-matrix element), after a fixed control area
+ * quantity and both solve outputs of its P * slab_steps chunks (100 B per write entry,
+ * 28 B per read entry, 16 B per chunk-matrix element and a slot search index of up to
+ * 64 KiB per chunk), after a fixed control area
  * (exchange rows and barrier counters of the Phase-2 teams)
  * (the pages budget the same kinds of state, SLAB_BYTES in memory_ops.py).
  * Returns 0 for arguments sdm_fwd would reject with SDM_ERR_SHAPE or SDM_ERR_RANGE.

@@ -58,10 +58,14 @@ def test_workspace_bytes(lib):
     assert f(8, 2048, 8, 8, 8, 64, 0) == 0                # chunk out of range
     assert f(8, 2048, 64, 0, 8, 64, 0) == 0               # W < 1
     assert f(8, 2048, 64, 8, 257, 64, 0) == 0             # R > 256
-    # 96 B per write entry, 28 B per read entry, 16 B per chunk-matrix element (+ alignment)
+    # 100 B per write entry, 28 B per read entry, 16 B per chunk-matrix element, a slot
+    # search index of about one word per write entry (a power of two, at most 2^14) and
+    # one word per possible hot group (+ alignment)
     per_chunk = step / 8
     E, F, C2 = 64 * 8, 64 * 8, 64 * 64
-    assert 96 * E + 28 * F + 16 * C2 <= per_chunk <= 96 * E + 28 * F + 16 * C2 + 40 * 256
+    NB = 512
+    base = 100 * E + 28 * F + 16 * C2 + 4 * (NB + 1) + 4 * (E // 16 + 1)
+    assert base <= per_chunk <= base + 40 * 256
 
 
 class Call:
