@@ -20,11 +20,9 @@ hipError_t wy_prepare();
 hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev);
 hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
                      int64_t stride, int64_t bstride, hipStream_t st);
-hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, uint32_t *control, hipStream_t st);
-hipError_t phase2_max_resident(int dtype, int V, const P2Geom &g, int C, int cus, int64_t *out);
+hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st);
 size_t gram_lds_bytes(int C);
-size_t phase2_lds_bytes(int C, int nv, int V, int K);
-int64_t phase2_control_words(int P, int C, int hd);
+size_t phase2_lds_bytes(int C, int nv, int V);
 }  // namespace sdm
 
 using namespace sdm;
@@ -84,9 +82,15 @@ int key_bits(int64_t M) {
     return bits;
 }
 
+// Radix passes of at most 9 bits over the slot id, as even as possible.
 int sort_passes(int64_t M) {
-    int passes = (key_bits(M) + 7) / 8;
+    const int passes = (key_bits(M) + 8) / 9;
     return passes < 1 ? 1 : passes;
+}
+
+int sort_digit(int64_t M) {
+    const int p = sort_passes(M), d = (key_bits(M) + p - 1) / p;
+    return d < 1 ? 1 : d;
 }
 
 struct Checked {
@@ -142,7 +146,7 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     if (hd % vec == 0 && (!need_bank || (aligned(v, 16) && aligned(bank_data, 16) && aligned(out, 16)))) V = vec;
     Problem pb{};
     pb.P = P; pb.T = T; pb.C = C; pb.Nt = int32_t((int64_t(T) + C - 1) / C); pb.W = W; pb.R = R; pb.G = G; pb.hd = hd;
-    pb.M = M; pb.dtype = dtype; pb.sort_passes = sort_passes(M); pb.key_bits = key_bits(M);
+    pb.M = M; pb.dtype = dtype; pb.sort_passes = sort_passes(M); pb.sort_digit = sort_digit(M); pb.key_bits = key_bits(M);
     pb.k_idx = slots->write; pb.q_idx = slots->read; pb.k_val = weights->write; pb.q_val = weights->read;
     pb.beta = beta; pb.g = g; pb.v = v; pb.valid = valid; pb.bank = bank_data; pb.out = out;
     ck->pb = pb;
@@ -152,26 +156,20 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     return SDM_OK;
 }
 
-// Phase-2 geometry from shapes only (the bits never depend on it): 128-byte column
-// slices (one cache line of each row), halved while that leaves fewer than one
-// workgroup per CU; one workgroup per (stream, slice). Teams (K > 1) are
-// only taken from SDM_P2_GEOM="nv,K,block", which overrides the whole choice (for tuning
-// sweeps): their barriers need device-scope fences that write back and invalidate the
-// per-XCD L2, which costs more than they save on the shapes measured.
-P2Geom plan_phase2(const Problem &pb, int V, int es, int cus, int lds_limit) {
+// Phase-2 geometry from shapes only (the bits never depend on it): slices of NV vectors,
+// NV the largest power of two with NV * V * es <= 128 bytes (one cache line of a row),
+// halved while that leaves fewer than one workgroup per CU; one workgroup per
+// (stream, slice). SDM_P2_GEOM="nv" overrides NV (1, 2, 4 or 8; for tuning sweeps).
+P2Geom plan_phase2(const Problem &pb, int V, int es, int cus) {
     const int hv = pb.hd / V;
     P2Geom g{};
-    g.nv = 128 / (V * es) < 1 ? 1 : 128 / (V * es);
-    if (g.nv > hv) g.nv = hv;
-    g.K = 1;
+    g.nv = 8;
+    while (g.nv > 1 && (g.nv * V * es > 128 || g.nv > hv)) g.nv >>= 1;
     const char *env = getenv("SDM_P2_GEOM");
-    int enk = 0, ekk = 0, ebb = 0;
-    if (env && sscanf(env, "%d,%d,%d", &enk, &ekk, &ebb) == 3 && enk >= 1 && ekk >= 1 &&
-        (ebb == 256 || ebb == 512 || ebb == 1024)) {
-        g.nv = enk > hv ? hv : enk;
-        g.K = ekk > pb.C ? pb.C : ekk;
+    int enk = 0;
+    if (env && sscanf(env, "%d", &enk) == 1 && (enk == 1 || enk == 2 || enk == 4 || enk == 8)) {
+        g.nv = enk;
         g.S = (hv + g.nv - 1) / g.nv;
-        g.block = ebb;
         return g;
     }
     g.S = (hv + g.nv - 1) / g.nv;
@@ -179,14 +177,6 @@ P2Geom plan_phase2(const Problem &pb, int V, int es, int cus, int lds_limit) {
         g.nv >>= 1;
         g.S = (hv + g.nv - 1) / g.nv;
     }
-    while (g.nv > 1 && phase2_lds_bytes(pb.C, g.nv, V, g.K) + 256 > size_t(lds_limit)) {
-        g.nv >>= 1;
-        g.S = (hv + g.nv - 1) / g.nv;
-    }
-    // about two gather items (token x vector x part) per thread, 4 to 16 waves
-    const int parts = int64_t(pb.C) * pb.W >= 16384 ? 1 : (pb.W >= 32 ? 4 : (pb.W >= 16 ? 2 : 1));
-    const int items = 2 * pb.C * g.nv * parts;
-    g.block = items >= 2048 ? 1024 : (items >= 1024 ? 512 : 256);
     return g;
 }
 
@@ -216,7 +206,7 @@ size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32
     const int32_t Nt = int32_t((int64_t(T) + C - 1) / C);
     if (slab_steps <= 0 || slab_steps > Nt) slab_steps = Nt;
     const ChunkLayout lay = make_layout(C, W, R);
-    return size_t(phase2_control_words(P, C, hd)) * 4 + size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
+    return size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
 }
 
 int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
@@ -229,39 +219,30 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
                         bank->data, valid_tokens, out, true, &ck);
     if (rc) return rc;
     const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
-    const size_t control = size_t(phase2_control_words(P, C, bank->head_dim)) * 4;
-    if (!exec->workspace || exec->workspace_bytes < control + per_step)
+    if (!exec->workspace || exec->workspace_bytes < per_step)
         return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
-                    exec->workspace ? exec->workspace_bytes : size_t(0), control + per_step);
+                    exec->workspace ? exec->workspace_bytes : size_t(0), per_step);
     if (!aligned(exec->workspace, 256)) return fail(SDM_ERR_ALIGN, "workspace must be 256-byte aligned");
     DeviceInfo *dev = nullptr;
     if ((rc = device_info(&dev)) != SDM_OK) return rc;
     if (gram_lds_bytes(C) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
                     gram_lds_bytes(C), dev->lds_per_block);
-    const P2Geom geom = plan_phase2(ck.pb, ck.V, ck.es, dev->cus, dev->lds_per_block);
-    if (phase2_lds_bytes(C, geom.nv, ck.V, geom.K) + 256 > size_t(dev->lds_per_block))
-        return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs more LDS than the device has", C);
-    if (geom.K > 1) {
-        int64_t resident = 0;
-        hipError_t e = phase2_max_resident(ck.pb.dtype, ck.V, geom, C, dev->cus, &resident);
-        if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-        if (int64_t(P) * geom.S * geom.K > resident)
-            return fail(SDM_ERR_UNSUPPORTED, "phase-2 teams of %d need %lld resident workgroups, the device holds %lld",
-                        geom.K, (long long)(int64_t(P) * geom.S * geom.K), (long long)resident);
-    }
+    const P2Geom geom = plan_phase2(ck.pb, ck.V, ck.es, dev->cus);
+    if (phase2_lds_bytes(C, geom.nv, ck.V) + 256 > size_t(dev->lds_per_block))
+        return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup in phase 2, the device has %d", C,
+                    phase2_lds_bytes(C, geom.nv, ck.V), dev->lds_per_block);
     const int32_t Nt = ck.pb.Nt;
-    int32_t slab = int32_t((exec->workspace_bytes - control) / per_step);
-    if (slab > Nt) slab = Nt;
+    int64_t slab64 = int64_t(exec->workspace_bytes / per_step);
+    int32_t slab = slab64 > Nt ? Nt : int32_t(slab64);
     hipStream_t st = static_cast<hipStream_t>(exec->stream);
     hipEvent_t *ev = nullptr;
     if (exec->events && exec->num_events >= SDM_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
-    uint32_t *ctl = static_cast<uint32_t *>(exec->workspace);
     for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
         Slab sl{};
         sl.ti0 = ti0;
         sl.steps = Nt - ti0 < slab ? Nt - ti0 : slab;
-        sl.ws = ctl + control / 4;
+        sl.ws = static_cast<uint32_t *>(exec->workspace);
         sl.lay = ck.lay;
         hipEvent_t *sev = ti0 == 0 ? ev : nullptr;
         hipError_t e = launch_phase1(ck.pb, sl, st, sev);
@@ -272,7 +253,7 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
                       int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
         if (e != hipSuccess) return hip_fail(e, "solve launch");
         if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        e = launch_phase2(ck.pb, sl, ck.V, geom, ctl, st);
+        e = launch_phase2(ck.pb, sl, ck.V, geom, st);
         if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
         if (sev && (e = hipEventRecord(sev[7], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }

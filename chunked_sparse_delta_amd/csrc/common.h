@@ -100,7 +100,8 @@ struct Problem {
     int32_t P, T, C, Nt, W, R, G, hd;
     int64_t M;
     int32_t dtype;           // 0 f32, 1 bf16
-    int32_t sort_passes;     // 8-bit LSD radix passes over the slot id
+    int32_t sort_passes;     // LSD radix passes over the slot id ...
+    int32_t sort_digit;      // ... of this many bits each (the last one may use fewer)
     int32_t key_bits;        // bits of the largest slot id (M - 1)
     const int32_t *k_idx;    // [P, T, W]
     const int32_t *q_idx;    // [P, T, R]
@@ -210,10 +211,9 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     return L;
 }
 
-// Phase-2 launch geometry: vectors per column slice, slices per row, workgroups per
-// (stream, slice) team, threads per workgroup.
+// Phase-2 launch geometry: vectors per column slice, slices per row.
 struct P2Geom {
-    int nv, S, K, block;
+    int nv, S;
 };
 
 struct Slab {

@@ -27,99 +27,121 @@ namespace sdm {
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
 
-// Exclusive scan of hist[0..255] in place by the first four wavefronts; block-wide barrier
-// semantics are the caller's.
-__device__ __forceinline__ void scan256_exclusive(int32_t *hist, int32_t *wtot) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int32_t x = 0, incl = 0;
-    if (tid < 256) {
-        x = hist[tid];
-        incl = x;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int32_t y = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += y;
-        }
-        if (lane == 63) wtot[wv] = incl;
+// Stable LSD radix sort of one chunk's write entries by slot id, in passes of at most
+// kSortDigit bits. Wave w owns a fixed contiguous segment of the input of every pass: it
+// counts the digits of its segment (wave-private LDS row), the block turns the counts into
+// each wave's first output position per digit (digits ascending, waves in order), and the
+// wave scatters its segment in order, ranking equal digits within a wavefront by lane
+// (ballot match) and advancing its own per-digit positions. Two block barriers per pass.
+constexpr int kSortDigit = 9;
+
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool ok, int db) {
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < db; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
     }
-    __syncthreads();
-    if (tid < 256) {
-        int32_t off = 0;
-        for (int w = 0; w < wv; ++w) off += wtot[w];
-        hist[tid] = off + incl - x;
-    }
-    __syncthreads();
+    return peers;
 }
 
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void p1_sort_kernel(Problem pb, Slab sl) {
     constexpr int NW = BLOCK / kWave;
-    __shared__ int32_t hist[256];
-    __shared__ int32_t wtot[4];
-    __shared__ int32_t wcnt[NW][256];
+    constexpr int NBK = 1 << kSortDigit;
+    static_assert(BLOCK >= NBK, "one thread per digit");
+    __shared__ int32_t cnt[NW][NBK];
+    __shared__ int32_t dsum[NBK / kWave];
     const int64_t n = blockIdx.x;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
-    const int64_t El = int64_t(nl) * pb.W;
+    const int32_t El = nl * pb.W;
     uint32_t *cb = sl.chunk(n);
     uint32_t *key[2] = {cb + sl.lay.off_key0, cb + sl.lay.off_key1};
     uint32_t *val[2] = {cb + sl.lay.off_val0, cb + sl.lay.off_val1};
-    const int32_t *kin = pb.k_idx + (int64_t(p) * pb.T + int64_t(ti) * pb.C) * pb.W;
+    const uint32_t *kin = reinterpret_cast<const uint32_t *>(pb.k_idx) + (int64_t(p) * pb.T + int64_t(ti) * pb.C) * pb.W;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint64_t lt = lanemask_lt(lane);
+    const int32_t seg = ((El + NW - 1) / NW + 63) & ~63;
+    const int32_t s0 = min(El, wv * seg), s1 = min(El, s0 + seg);
 
     for (int q = 0; q < pb.sort_passes; ++q) {
-        const int shift = 8 * q;
-        const uint32_t *sk = key[(q + 1) & 1];
+        const int shift = q * pb.sort_digit;
+        const int db = max(1, min(pb.sort_digit, pb.key_bits - shift));
+        const int nd = 1 << db;
+        const uint32_t dmask = uint32_t(nd - 1);
+        const uint32_t *sk = q == 0 ? kin : key[(q + 1) & 1];
         const uint32_t *sv = val[(q + 1) & 1];
         uint32_t *dk = key[q & 1];
         uint32_t *dv = val[q & 1];
-        for (int d = tid; d < 256; d += BLOCK) hist[d] = 0;
-        __syncthreads();
-        for (int64_t e = tid; e < El; e += BLOCK) {
-            uint32_t k = q == 0 ? uint32_t(kin[e]) : sk[e];
-            atomicAdd(&hist[(k >> shift) & 255u], 1);
-        }
-        __syncthreads();
-        scan256_exclusive(hist, wtot);
-        for (int64_t t0 = 0; t0 < El; t0 += BLOCK) {
-            const int64_t e = t0 + tid;
-            const bool ok = e < El;
-            uint32_t k = 0, vv = 0;
-            if (ok) {
-                k = q == 0 ? uint32_t(kin[e]) : sk[e];
-                vv = q == 0 ? uint32_t(e) : sv[e];
-            }
-            const uint32_t d = (k >> shift) & 255u;
-            uint64_t peers = __ballot(ok);
+
+        // Count the digits of this wave's segment.
+        for (int d = lane; d < nd; d += kWave) cnt[wv][d] = 0;
+        for (int32_t b0 = s0; b0 < s1; b0 += 4 * kWave) {
+            uint32_t kk[4];
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const bool bit = (d >> b) & 1u;
-                const uint64_t bb = __ballot(bit);
-                peers &= bit ? bb : ~bb;
+            for (int u = 0; u < 4; ++u) {
+                const int32_t e = b0 + u * kWave + lane;
+                kk[u] = e < s1 ? sk[e] : 0u;
             }
-            const int rank = __popcll(peers & lt);
-            for (int i = tid; i < NW * 256; i += BLOCK) (&wcnt[0][0])[i] = 0;
-            __syncthreads();
-            if (ok && rank == 0) wcnt[wv][d] = __popcll(peers);
-            __syncthreads();
-            if (tid < 256) {
-                int32_t run = hist[tid];
-                for (int w = 0; w < NW; ++w) {
-                    const int32_t c = wcnt[w][tid];
-                    wcnt[w][tid] = run;
-                    run += c;
-                }
-                hist[tid] = run;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = b0 + u * kWave + lane < s1;
+                const uint32_t d = (kk[u] >> shift) & dmask;
+                const uint64_t peers = match_digit(d, ok, db);
+                if (ok && (peers & lt) == 0) cnt[wv][d] += __popcll(peers);
             }
-            __syncthreads();
-            if (ok) {
-                const int32_t dst = wcnt[wv][d] + rank;
-                dk[dst] = k;
-                dv[dst] = vv;
-            }
-            __syncthreads();
         }
+        __syncthreads();
+        // First output position of every (wave, digit): digits ascending, waves in order.
+        int32_t tot = 0, incl = 0;
+        if (tid < NBK) {
+            if (tid < nd)
+                for (int w = 0; w < NW; ++w) tot += cnt[w][tid];
+            incl = tot;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int32_t y = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += y;
+            }
+            if (lane == kWave - 1) dsum[wv] = incl;
+        }
+        __syncthreads();
+        if (tid < nd) {
+            int32_t run = incl - tot;
+            for (int w = 0; w < wv; ++w) run += dsum[w];
+            for (int w = 0; w < NW; ++w) {
+                const int32_t c = cnt[w][tid];
+                cnt[w][tid] = run;
+                run += c;
+            }
+        }
+        __syncthreads();
+        // Scatter this wave's segment in order.
+        for (int32_t b0 = s0; b0 < s1; b0 += 4 * kWave) {
+            uint32_t kk[4], vv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int32_t e = b0 + u * kWave + lane;
+                const bool ok = e < s1;
+                kk[u] = ok ? sk[e] : 0u;
+                vv[u] = ok ? (q == 0 ? uint32_t(e) : sv[e]) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = b0 + u * kWave + lane < s1;
+                const uint32_t d = (kk[u] >> shift) & dmask;
+                const uint64_t peers = match_digit(d, ok, db);
+                const int32_t rank = __popcll(peers & lt);
+                const int32_t base = cnt[wv][d];
+                if (ok && rank == 0) cnt[wv][d] = base + __popcll(peers);
+                if (ok) {
+                    dk[base + rank] = kk[u];
+                    dv[base + rank] = vv[u];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 

@@ -6,481 +6,472 @@
 //     DW           each written slot s: B[s] = exp(L_last) B[s] + sum_members cw delta_v[t]
 //
 // Every column of the bank evolves on its own (all Phase-1 quantities are column-free),
-// so the work of a stream splits by column slices with no exchange at all. A slice is a
-// 128-byte segment of each row (one cache line), or the whole row if shorter: narrower
-// slices would make every workgroup re-read the chunk's ids, weights, X and QX.
-//
-// Where slices alone leave too few workgroups to cover the chip, a TEAM of K workgroups
-// shares one (stream, slice): member k gathers and multiplies the tokens of its share of
-// the chunk and writes the bank rows of its share of the groups. The u and delta_v rows
-// pass between members through L2 (the team's exchange rows), and three team barriers
-// per step order gather -> matmul -> DW -> next gather. Teams run as a cooperative
-// launch (all workgroups resident); a barrier gives up after a bounded spin and raises a
-// flag word, so every wave always terminates. With K = 1 the barriers are plain
-// workgroup barriers.
-//
+// so the work of a stream splits by column slices with no exchange at all: one
+// persistent workgroup per (stream, slice) runs every step of a slab. A slice is NV
+// vectors of V elements (V * NV * sizeof(T) <= 128 bytes, one cache line of a row).
 // Workgroups of one stream are placed on one XCD (blocks are dealt round-robin to the
-// 8 XCDs) so that its slices and team members share one L2.
+// 8 XCDs) so that its slices share one L2 for the chunk's ids, weights and matrices.
 //
-// Determinism: each output element has exactly one writer, and every sum runs in a fixed
-// order (gather: entry order; matmul: column index ascending; DW: decay term first, then
-// the group's members in token order), so the bits do not depend on the slicing, the team
-// size or the launch size.
+// Per step, with 16 wavefronts:
+//   gather   a wavefront takes whole tokens; each load instruction fetches one slice of
+//            64 / NV rows (8 entry classes x 8 / NV tokens), eight instructions in flight,
+//            the next batch's ids and weights loaded under the current batch's rows
+//   u        u = beta (v - retrieved) in LDS, v prefetched before the gather
+//   matmul   D^T = u^T QX^T and u^T X^T on v_mfma_f32_16x16x4f32: 16 x 16 output tiles
+//            (16 columns x 16 tokens), lower-triangular tiles only; readings (+ inter)
+//            go straight to memory, delta_v to LDS
+//   DW       64 / NV groups per load instruction, four in flight per lane, member
+//            records eight at a time
+//
+// Determinism: each output element has exactly one writer, and every sum runs in an order
+// fixed by the shapes W, R and C only (never by the slicing or the launch):
+//   gather  token t's entries e are summed per class e % 8 in ascending e (one fmaf chain),
+//           and the classes combine as ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7));
+//   matmul  16-wide k blocks ascending, each one MFMA chain of four k-steps;
+//   DW      decay term first, then the group's members in token order.
 #include "common.h"
 
 namespace sdm {
 
-constexpr int kSpinLimit = 1 << 22;   // about 0.2 s of polling before a barrier gives up
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kP2Block = 1024;
+constexpr int kP2Waves = kP2Block / kWave;
+constexpr int kBatch = 8;      // gather row loads in flight per lane
+constexpr int kDwBatch = 4;    // DW groups in flight per lane
+constexpr int kMaxTilesPerWave = (kMaxChunk / 16) * 4 / kP2Waves;   // 16 x 16 tiles, 64 columns at most
+
+// Only what Phase 2 reads: every field is uniform and stays in scalar registers.
 struct P2Args {
-    Problem pb;
-    Slab sl;
-    int32_t nv;        // vectors per column slice
-    int32_t S;         // slices per row
-    int32_t K;         // workgroups per (stream, slice) team
-    int32_t hv;        // vectors per row (hd / V)
-    float *xchg;       // team exchange rows: [teams][2][C][nv * V]
-    int32_t *ctr;      // [teams] barrier counters, zero at launch
-    int32_t *err;      // set to 1 by a barrier that timed out
+    const int32_t *k_idx, *q_idx;   // [P, T, W], [P, T, R]
+    const void *v;                  // [P, T, hd]
+    void *bank;                     // [P, M, hd]
+    void *out;                      // [P, T, hd]
+    const int32_t *valid;           // [P] or nullptr
+    const uint32_t *ws;             // slab base: chunk n at ws + n * words
+    int64_t M, words;
+    int32_t T, C, W, R, hd, P;
+    int32_t S, hv;                  // slices per row, vectors per row (hd / V)
+    int32_t ti0, steps;             // the slab
+    int32_t off_gw, off_gr, off_beta, off_X, off_QX, off_meta, off_grec, off_mrec;   // words within a chunk
 };
 
-// Team barrier: every global write of the workgroup before it is visible to the team
-// after it.
-__device__ __forceinline__ void team_barrier(int32_t *ctr, int32_t target, int32_t *err, int *broken) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0 && !*broken) {
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        int spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++spins > kSpinLimit) {
-                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                *broken = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    __syncthreads();
-    __threadfence();
+__device__ __forceinline__ int32_t live_tokens(const P2Args &a, int p, int ti) {
+    int32_t vt = a.valid ? a.valid[p] : a.T;
+    vt = vt < 0 ? 0 : (vt > a.T ? a.T : vt);
+    const int32_t n = vt - ti * a.C;
+    return n < 0 ? 0 : (n > a.C ? a.C : n);
 }
 
-// acc[c] = sum_w wts[w] * bank[ids[w]][col + c], w ascending; eight rows in flight.
-template <typename T, int V>
-__device__ __forceinline__ void gather_row(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
-                                           int64_t col, float (&acc)[V]) {
+// Element pointer + 32-bit element offset (the host bounds every offset below 2^31 bytes).
+template <typename T>
+__device__ __forceinline__ const T *at(const T *base, uint32_t off) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + uint64_t(off) * sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ T *at(T *base, uint32_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + uint64_t(off) * sizeof(T));
+}
+
+// LDS row pitch (floats) of a slice of cw columns: 16-byte aligned rows, 4 mod 8 words.
+__host__ __device__ inline int p2_pitch(int cw) { return ((cw + 3) & ~3) + 4; }
+__host__ __device__ inline int p2_rows(int C) { return (C + 15) & ~15; }
+
+// Combine the eight entry classes of a lane's sum (classes are lane bits NV, 2NV, 4NV).
+template <int V, int NV>
+__device__ __forceinline__ void combine_classes(float (&acc)[V]) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], NV, 64);
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 2 * NV, 64);
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 4 * NV, 64);
+}
+
+template <int V>
+__device__ __forceinline__ void lds_store_vec(float *p, const float (&x)[V]) {
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < V; c += 4) *reinterpret_cast<float4 *>(p + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+    } else {
+#pragma unroll
+        for (int c = 0; c < V; ++c) p[c] = x[c];
+    }
+}
+
+template <int V>
+__device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
+    if constexpr (V % 4 == 0) {
+#pragma unroll
+        for (int c = 0; c < V; c += 4) {
+            const float4 y = *reinterpret_cast<const float4 *>(p + c);
+            x[c] = y.x; x[c + 1] = y.y; x[c + 2] = y.z; x[c + 3] = y.w;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < V; ++c) x[c] = p[c];
+    }
+}
+
+// Weighted row sums of one region (the write entries or the read entries) for the live
+// tokens of the chunk, into dst[t * pitch + vq * V + c]. Lane layout: vq = lane % NV (the
+// vector of the slice), class r = (lane / NV) % 8, ts = lane / (8 NV) (the token within a
+// group of TPI = 8 / NV tokens). Instruction j of a token group loads entries 8 j + r.
+// The wave walks its token groups (wave, wave + 16, ...) as one flat list of
+// instructions, kBatch at a time.
+template <typename T, int V, int NV>
+__device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
+                                              int nl, int col0, int nvs, float *dst, int pitch, int wave, int lane) {
+    constexpr int TPI = 8 / NV;
+    const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
+    const int NI = (width + 7) >> 3;
+    const int NG = (nl + TPI - 1) / TPI;
+    const int ngw = NG > wave ? (NG - wave + kP2Waves - 1) / kP2Waves : 0;
+    const int total = ngw * NI;
+    if (total == 0) return;
+    const bool vok = vq < nvs;
+    const uint32_t col = uint32_t(col0 + vq * V);
+
+    // (k, j) of the first instruction of the next batch whose pairs are to be loaded
+    int pk = 0, pj = 0;
+    int32_t id[kBatch], nid[kBatch];
+    float wt[kBatch], nwt[kBatch];
+    auto load_pairs = [&](int32_t (&di)[kBatch], float (&dw)[kBatch]) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            di[u] = -1;
+            dw[u] = 0.0f;
+            if (pk < ngw) {
+                const int t = (wave + pk * kP2Waves) * TPI + ts, e = 8 * pj + r;
+                if (t < nl && e < width) {
+                    di[u] = *at(ids, uint32_t(t * width + e));
+                    dw[u] = *at(wts, uint32_t(t * width + e));
+                }
+            }
+            if (++pj == NI) { pj = 0; ++pk; }
+        }
+    };
+    load_pairs(id, wt);
+
+    float acc[V];
 #pragma unroll
     for (int c = 0; c < V; ++c) acc[c] = 0.0f;
-    int w = 0;
-    for (; w + 8 <= width; w += 8) {
-        int32_t s[8];
-        float wt[8];
-        typename Vec<T, V>::raw_t raw[8];
+    int ck = 0, cj = 0;   // (k, j) of the instruction being consumed
+    for (int i0 = 0; i0 < total; i0 += kBatch) {
+        typename Vec<T, V>::raw_t raw[kBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            s[u] = ids[w + u];
-            wt[u] = wts[w + u];
+        for (int u = 0; u < kBatch; ++u)
+            if (id[u] >= 0 && vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(id[u]) * uint32_t(hd) + col));
+        load_pairs(nid, nwt);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (i0 + u >= total) break;
+            if (id[u] >= 0 && vok) {
+                float row[V];
+                Vec<T, V>::unpack(raw[u], row);
+#pragma unroll
+                for (int c = 0; c < V; ++c) acc[c] = fmaf(wt[u], row[c], acc[c]);
+            }
+            if (cj == NI - 1) {
+                combine_classes<V, NV>(acc);
+                const int t = (wave + ck * kP2Waves) * TPI + ts;
+                if (r == 0 && t < nl && vok) lds_store_vec<V>(dst + t * pitch + vq * V, acc);
+#pragma unroll
+                for (int c = 0; c < V; ++c) acc[c] = 0.0f;
+                cj = 0;
+                ++ck;
+            } else {
+                ++cj;
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) raw[u] = Vec<T, V>::load_raw(bank + int64_t(s[u]) * hd + col);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            float row[V];
-            Vec<T, V>::unpack(raw[u], row);
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = fmaf(wt[u], row[c], acc[c]);
+        for (int u = 0; u < kBatch; ++u) {
+            id[u] = nid[u];
+            wt[u] = nwt[u];
         }
     }
-    for (; w < width; ++w) {
-        float row[V];
-        Vec<T, V>::load(bank + int64_t(ids[w]) * hd + col, row);
-        const float wt = wts[w];
-#pragma unroll
-        for (int c = 0; c < V; ++c) acc[c] = fmaf(wt, row[c], acc[c]);
-    }
 }
 
-// acc[c] += sum_{j < n} xrow[j] * u[j * pitch + c], j ascending.
-template <int V>
-__device__ __forceinline__ void dot_row(const float *xrow, int n, const float *u, int pitch, bool vec4,
-                                        float (&acc)[V]) {
-    int j = 0;
-    if (vec4) {
-#pragma unroll 4
-        for (; j + 4 <= n; j += 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(xrow + j);
-            const float *u0 = u + j * pitch;
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = fmaf(x.x, u0[c], acc[c]);
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = fmaf(x.y, u0[pitch + c], acc[c]);
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = fmaf(x.z, u0[2 * pitch + c], acc[c]);
-#pragma unroll
-            for (int c = 0; c < V; ++c) acc[c] = fmaf(x.w, u0[3 * pitch + c], acc[c]);
+template <typename T>
+__device__ __forceinline__ void store_out4(T *p, const f32x4 &y, int n) {
+    // n (1..4) consecutive elements; n == 4 takes one vector store
+    if constexpr (sizeof(T) == 4) {
+        if (n == 4) {
+            *reinterpret_cast<float4 *>(p) = make_float4(y[0], y[1], y[2], y[3]);
+            return;
         }
-    }
-    for (; j < n; ++j) {
-        const float x = xrow[j];
-#pragma unroll
-        for (int c = 0; c < V; ++c) acc[c] = fmaf(x, u[j * pitch + c], acc[c]);
-    }
-}
-
-// Reductions are cut into a shape-only number of contiguous parts (never the launch
-// geometry): each part is summed in order by one lane, and the parts of one output are
-// combined by a fixed xor butterfly, ((p0 + p1) + (p2 + p3)); every lane of the group ends
-// with the same bits (additions only, no fused products). Items come in wavefront-sized
-// chunks of 64: lane l of a chunk holds part l / (64 / parts) of output
-// chunk * (64 / parts) + l % (64 / parts), so the lanes of one part read neighbouring
-// outputs (broadcast / consecutive LDS words) and the partners sit 16 or 32 lanes apart.
-__host__ __device__ __forceinline__ int split_parts(int n) { return n >= 32 ? 4 : (n >= 16 ? 2 : 1); }
-// Gather: entries of one token; no split once a chunk has plenty of entries (C * width).
-__host__ __device__ __forceinline__ int gather_parts(int C, int width) {
-    return int64_t(C) * width >= 16384 ? 1 : split_parts(width);
-}
-// Matmul: columns of one row; no split for the largest chunks.
-__host__ __device__ __forceinline__ int matmul_parts(int C) { return C >= 256 ? 1 : split_parts(C); }
-
-__device__ __forceinline__ void split_item(int it, int parts, int &out, int &part) {
-    const int G = kWave / parts, ch = it >> 6, l = it & 63;
-    part = l / G;
-    out = ch * G + (l - part * G);
-}
-
-__host__ __device__ __forceinline__ int split_items(int outputs, int parts) {
-    const int G = kWave / parts;
-    return (outputs + G - 1) / G * kWave;
-}
-
-template <int V>
-__device__ __forceinline__ void combine_parts(float (&acc)[V], int parts) {
-    if (parts >= 4) {
-#pragma unroll
-        for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 16, 64);
-    }
-    if (parts >= 2) {
-#pragma unroll
-        for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
-    }
-}
-
-__device__ __forceinline__ void copy_rows(float *dst, const float *src, int rows, int nvs, int pitch, int V, int BLOCK) {
-    // rows x (nvs * V) floats, both with row pitch `pitch`
-    const int per = nvs * V;
-    for (int it = threadIdx.x; it < rows * per; it += BLOCK) {
-        const int r = it / per, c = it - r * per;
-        dst[r * pitch + c] = src[r * pitch + c];
-    }
-}
-
-template <typename T, int V, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
-    extern __shared__ float lds[];
-    __shared__ int broken;
-    const Problem &pb = a.pb;
-    const Slab &sl = a.sl;
-    const int C = pb.C, W = pb.W, R = pb.R, hd = pb.hd;
-    const int nv = a.nv, S = a.S, K = a.K;
-    const int cw = nv * V;                  // LDS / exchange row pitch in floats
-    const int tpw = (C + K - 1) / K;        // tokens per team member
-
-    // Decode (stream, slice, member); streams stay on one XCD when P % 8 == 0.
-    const int bid = blockIdx.x, per_stream = S * K;
-    int p, r;
-    if (pb.P % kXcds == 0) {
-        const int xcd = bid % kXcds, m = bid / kXcds;
-        p = xcd + kXcds * (m / per_stream);
-        r = m % per_stream;
     } else {
-        p = bid / per_stream;
-        r = bid % per_stream;
+        if (n == 4) {
+            uint2 w;
+            w.x = uint32_t(f32_to_bf16(y[0]).bits) | (uint32_t(f32_to_bf16(y[1]).bits) << 16);
+            w.y = uint32_t(f32_to_bf16(y[2]).bits) | (uint32_t(f32_to_bf16(y[3]).bits) << 16);
+            *reinterpret_cast<uint2 *>(p) = w;
+            return;
+        }
     }
-    const int slice = r / K, k = r % K;
-    const int team = p * S + slice;
-    const int vq0 = slice * nv;
-    const int nvs = min(nv, a.hv - vq0);
-    const int i0 = min(C, k * tpw), i1 = min(C, i0 + tpw);
-    const int tid = threadIdx.x;
-    T *bank = static_cast<T *>(pb.bank) + int64_t(p) * pb.M * hd;
-    const T *vin = static_cast<const T *>(pb.v);
-    T *out = static_cast<T *>(pb.out);
-    const ChunkLayout &L = sl.lay;
+    for (int v = 0; v < n; ++v) p[v] = from_f32<T>(y[v]);
+}
+
+// The B operand of one 16 x 16 x 16 block: lane l holds M[i0 + (l & 15)][k0 + 4 (l >> 4) + kk]
+// for kk = 0..3 (0 outside the C x C matrix).
+__device__ __forceinline__ void load_bop(const float *M, int C, int i, int k, bool vec4, float (&b)[4]) {
+    if (i < C && k + 3 < C && vec4) {
+        const float4 x = *reinterpret_cast<const float4 *>(M + int64_t(i) * C + k);
+        b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b[kk] = (i < C && k + kk < C) ? M[int64_t(i) * C + k + kk] : 0.0f;
+    }
+}
+
+template <typename T, int V, int NV>
+__global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
+    extern __shared__ float lds[];
+    const int C = a.C, hd = a.hd, S = a.S;
+    constexpr int CW = V * NV;                // columns of a full slice
+    const int pitch = p2_pitch(CW);
+    const int CP = p2_rows(C);
+
+    // Decode (stream, slice); a stream's slices stay on one XCD when P % 8 == 0.
+    const int bid = blockIdx.x;
+    int p, slice;
+    if (a.P % kXcds == 0) {
+        const int xcd = bid % kXcds, m = bid / kXcds;
+        p = xcd + kXcds * (m / S);
+        slice = m % S;
+    } else {
+        p = bid / S;
+        slice = bid % S;
+    }
+    const int vq0 = slice * NV;
+    const int nvs = min(NV, a.hv - vq0);      // vectors of this slice
+    const int cwv = nvs * V;                  // valid columns of this slice
+    const int col0 = vq0 * V;
+    T *bank = static_cast<T *>(a.bank) + int64_t(p) * a.M * hd;
     const bool vec4 = (C & 3) == 0;
 
-    float *ub = lds;                        // [C][cw]: u of every token (K = 1: own), then delta (K > 1)
-    float *ib = lds + C * cw;               // [K == 1 ? C : tpw][cw]: inter of own tokens (K = 1: then delta)
-    float *xu = a.xchg + int64_t(team) * 2 * C * cw;
-    float *xd = xu + int64_t(C) * cw;
-    int32_t *ctr = a.ctr + team;
-    int32_t bar = 0;
-    if (tid == 0) broken = 0;
-    __syncthreads();
+    float *ub = lds;                  // [CP][pitch]: retrieved, then u
+    float *ib = lds + CP * pitch;     // [CP][pitch]: inter, then delta_v
 
-    for (int s = 0; s < sl.steps; ++s) {
-        const int ti = sl.ti0 + s;
-        const int64_t n = int64_t(p) * sl.steps + s;
-        const uint32_t *cb = sl.chunk(n);
-        const int nl = n_live_tokens(pb, p, ti);
-        const int rows = min(C, pb.T - ti * C);
-        const int64_t tok0 = int64_t(p) * pb.T + int64_t(ti) * C;
-        const int own_live = max(0, min(i1, nl) - i0);
+    // MFMA tiles of this wave: (it, ct) dealt in a snake order over tiles sorted by it,
+    // so that every wave gets a similar share of the triangular work.
+    const int NIT = CP / 16, NCT = (cwv + 15) / 16, NT = NIT * NCT;
 
-        // ---- gather of own live tokens: retrieved -> ub[i], inter -> ib[i - i0]. Outputs
-        //      (token, vector) of the writes, then of the reads, each region in whole
-        //      wavefront chunks (split_item).
-        const float *gw = reinterpret_cast<const float *>(cb + L.off_gw);
-        const float *gr = reinterpret_cast<const float *>(cb + L.off_gr);
-        const int sfw = gather_parts(C, W), sfr = gather_parts(C, R);
-        const int nout = own_live * nvs;
-        const int nwp = split_items(nout, sfw), nrp = split_items(nout, sfr);
-        for (int it = tid; it < nwp + nrp; it += BLOCK) {
-            const bool rd = it >= nwp;
-            const int sf = rd ? sfr : sfw;
-            int o, blk;
-            split_item(rd ? it - nwp : it, sf, o, blk);
-            const bool live = o < nout;
-            const int li = live ? o / nvs : 0, vq = live ? o - li * nvs : 0;
-            const int i = i0 + li;
-            const int width = rd ? R : W;
-            const int per = (width + sf - 1) / sf;
-            const int w0 = min(width, blk * per), w1 = live ? min(width, w0 + per) : w0;
-            const int32_t *ids = (rd ? pb.q_idx : pb.k_idx) + (tok0 + i) * width + w0;
-            const float *wts = (rd ? gr : gw) + int64_t(i) * width + w0;
-            float acc[V];
-            gather_row<T, V>(bank, hd, ids, wts, w1 - w0, int64_t(vq0 + vq) * V, acc);
-            combine_parts<V>(acc, sf);
-            if (live && blk == 0) {
-                float *dst = rd ? ib + li * cw + vq * V : ub + i * cw + vq * V;
-#pragma unroll
-                for (int c = 0; c < V; ++c) dst[c] = acc[c];
-            }
+    // u items: (t, vq) = (item / NV, item % NV) for item = tid + kP2Block * x
+    constexpr int kUItems = (kMaxChunk * 8 + kP2Block - 1) / kP2Block;
+
+    for (int s = 0; s < a.steps; ++s) {
+        // Thread ids are re-read opaquely every step, so that the per-lane address
+        // arithmetic of all phases is not hoisted out of the step loop (it would be held
+        // in registers across the whole loop and spill).
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        asm volatile("" : "+s"(wave));
+        const int lane = tid & 63;
+        const int ti = a.ti0 + s;
+        const uint32_t *cb = a.ws + (int64_t(p) * a.steps + s) * a.words;
+        const int nl = live_tokens(a, p, ti);
+        const int rows = min(C, a.T - ti * C);
+        const int64_t tok0 = int64_t(p) * a.T + int64_t(ti) * C;
+        const T *vin = static_cast<const T *>(a.v) + tok0 * hd;     // this chunk's rows of v and out
+        T *out = static_cast<T *>(a.out) + tok0 * hd;
+
+        // ---- gather: retrieved -> ub, inter -> ib (live tokens)
+        {
+            const float *gw = reinterpret_cast<const float *>(cb + a.off_gw);
+            const float *gr = reinterpret_cast<const float *>(cb + a.off_gr);
+            gather_region<T, V, NV>(bank, hd, a.k_idx + tok0 * a.W, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
+            gather_region<T, V, NV>(bank, hd, a.q_idx + tok0 * a.R, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
         }
         __syncthreads();
 
-        // ---- u = beta (v - retrieved) on own rows; 0 for padding rows
-        const float *beta_c = reinterpret_cast<const float *>(cb + L.off_beta);
-        for (int it = tid; it < (i1 - i0) * nvs; it += BLOCK) {
-            const int li = it / nvs, vq = it - li * nvs;
-            const int i = i0 + li;
-            float *ur = ub + i * cw + vq * V;
-            float uu[V];
-            if (i < nl) {
-                float vv[V];
-                Vec<T, V>::load(vin + (tok0 + i) * hd + int64_t(vq0 + vq) * V, vv);
-                const float b = beta_c[i];
+        // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1
+        const float *beta_c = reinterpret_cast<const float *>(cb + a.off_beta);
 #pragma unroll
-                for (int c = 0; c < V; ++c) uu[c] = b * (vv[c] - ur[c]);
+        for (int x = 0; x < kUItems; ++x) {
+            const int item = tid + kP2Block * x, t = item / NV, vq = item % NV;
+            if (t >= CP) continue;
+            float *ur = ub + t * pitch + vq * V;
+            float uu[V];
+            if (t < nl && vq < nvs) {
+                float vv[V], rr[V];
+                Vec<T, V>::load(at(vin, uint32_t(t * hd + col0 + vq * V)), vv);
+                const float b = beta_c[t];
+                lds_load_vec<V>(ur, rr);
+#pragma unroll
+                for (int c = 0; c < V; ++c) uu[c] = b * (vv[c] - rr[c]);
             } else {
 #pragma unroll
                 for (int c = 0; c < V; ++c) uu[c] = 0.0f;
             }
-#pragma unroll
-            for (int c = 0; c < V; ++c) ur[c] = uu[c];
-            if (K > 1) {
-#pragma unroll
-                for (int c = 0; c < V; ++c) xu[i * cw + vq * V + c] = uu[c];
-            }
-        }
-        if (K > 1) {
-            team_barrier(ctr, ++bar * K, a.err, &broken);
-            copy_rows(ub, xu, nl, nvs, cw, V, BLOCK);   // rows >= nl are never read
+            lds_store_vec<V>(ur, uu);
         }
         __syncthreads();
 
-        // ---- readings = QX u + inter on own rows that exist (padding rows +0);
-        //      K > 1: delta_v = X u of own live rows into the exchange rows
-        const float *QX = reinterpret_cast<const float *>(cb + L.off_QX);
-        const float *X = reinterpret_cast<const float *>(cb + L.off_X);
-        const int own_rows = max(0, min(i1, rows) - i0);
-        // Output (row, vector); part p sums columns [p * cq, (p + 1) * cq) of the row.
-        const int sfm = matmul_parts(C), cq = (((C + sfm - 1) / sfm) + 3) & ~3;
-        const int nmo = own_rows * nvs;
-        for (int it = tid; it < split_items(nmo, sfm); it += BLOCK) {
-            int k3, blk;
-            split_item(it, sfm, k3, blk);
-            const bool exists = k3 < nmo;
-            const int li = exists ? k3 / nvs : 0, vq = exists ? k3 - li * nvs : 0;
-            const int i = i0 + li;
-            const bool live = exists && i < nl;
-            const int j0 = min(i + 1, blk * cq), j1 = live ? min(i + 1, j0 + cq) : j0;
-            float o[V];
+        // ---- dual matmul on the matrix cores
+        const float *QX = reinterpret_cast<const float *>(cb + a.off_QX);
+        const float *X = reinterpret_cast<const float *>(cb + a.off_X);
+        f32x4 dacc[kMaxTilesPerWave];
 #pragma unroll
-            for (int c = 0; c < V; ++c) o[c] = 0.0f;
-            dot_row<V>(QX + int64_t(i) * C + j0, j1 - j0, ub + j0 * cw + vq * V, cw, vec4, o);
-            combine_parts<V>(o, sfm);
-            float d[V];
-            if (K > 1) {
-#pragma unroll
-                for (int c = 0; c < V; ++c) d[c] = 0.0f;
-                dot_row<V>(X + int64_t(i) * C + j0, j1 - j0, ub + j0 * cw + vq * V, cw, vec4, d);
-                combine_parts<V>(d, sfm);
+        for (int q = 0; q < kMaxTilesPerWave; ++q) {
+            dacc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int tau = q * kP2Waves + ((q & 1) ? kP2Waves - 1 - wave : wave);
+            if (tau >= NT) continue;
+            const int it = tau / NCT, ct = tau - it * NCT;
+            const int ti_row = 16 * it + (lane & 15);          // token of the B operand / output
+            const int cu = 16 * ct + (lane & 15);              // column of the A operand
+            const int co = 16 * ct + 4 * (lane >> 4);          // first output column of this lane
+            const int ko = 4 * (lane >> 4);
+            f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (co < cwv) {
+                const float4 iv = *reinterpret_cast<const float4 *>(ib + ti_row * pitch + co);
+                y = f32x4{iv.x, iv.y, iv.z, iv.w};
             }
-            if (exists && blk == 0) {
-                if (live) {
-                    const float *ir = ib + li * cw + vq * V;
+            f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            float bq[4], bx[4];
+            load_bop(QX, C, ti_row, ko, vec4, bq);
+            load_bop(X, C, ti_row, ko, vec4, bx);
+            for (int kt = 0; kt <= it; ++kt) {
+                float nq[4], nx[4];
+                if (kt < it) {
+                    load_bop(QX, C, ti_row, 16 * (kt + 1) + ko, vec4, nq);
+                    load_bop(X, C, ti_row, 16 * (kt + 1) + ko, vec4, nx);
+                }
 #pragma unroll
-                    for (int c = 0; c < V; ++c) o[c] += ir[c];
-                    if (K > 1) {
+                for (int kk = 0; kk < 4; ++kk) {
+                    const float av = cu < cwv ? ub[(16 * kt + ko + kk) * pitch + cu] : 0.0f;
+                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bq[kk], y, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx[kk], d, 0, 0, 0);
+                }
+                if (kt < it) {
 #pragma unroll
-                        for (int c = 0; c < V; ++c) xd[i * cw + vq * V + c] = d[c];
+                    for (int kk = 0; kk < 4; ++kk) {
+                        bq[kk] = nq[kk];
+                        bx[kk] = nx[kk];
                     }
                 }
-                Vec<T, V>::store(out + (tok0 + i) * hd + int64_t(vq0 + vq) * V, o);
+            }
+            dacc[q] = d;
+            if (ti_row < rows && co < cwv) {
+                if (ti_row >= nl) y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                store_out4<T>(at(out, uint32_t(ti_row * hd + col0 + co)), y, min(4, cwv - co));
             }
         }
-        const float *D;
-        if (K > 1) {
-            team_barrier(ctr, ++bar * K, a.err, &broken);
-            copy_rows(ub, xd, nl, nvs, cw, V, BLOCK);
-            D = ub;
-        } else {
-            __syncthreads();
-            // delta_v = X u into ib (inter is no longer needed)
-            const int ndo = nl * nvs;
-            for (int it = tid; it < split_items(ndo, sfm); it += BLOCK) {
-                int k3, blk;
-                split_item(it, sfm, k3, blk);
-                const bool exists = k3 < ndo;
-                const int i = exists ? k3 / nvs : 0, vq = exists ? k3 - i * nvs : 0;
-                const int j0 = min(i + 1, blk * cq), j1 = exists ? min(i + 1, j0 + cq) : j0;
-                float d[V];
+        __syncthreads();
+        // delta_v -> ib
 #pragma unroll
-                for (int c = 0; c < V; ++c) d[c] = 0.0f;
-                dot_row<V>(X + int64_t(i) * C + j0, j1 - j0, ub + j0 * cw + vq * V, cw, vec4, d);
-                combine_parts<V>(d, sfm);
-                if (exists && blk == 0) {
-                    float *dr = ib + i * cw + vq * V;
-#pragma unroll
-                    for (int c = 0; c < V; ++c) dr[c] = d[c];
-                }
-            }
-            D = ib;
+        for (int q = 0; q < kMaxTilesPerWave; ++q) {
+            const int tau = q * kP2Waves + ((q & 1) ? kP2Waves - 1 - wave : wave);
+            if (tau >= NT) continue;
+            const int it = tau / NCT, ct = tau - it * NCT;
+            const int ti_row = 16 * it + (lane & 15), co = 16 * ct + 4 * (lane >> 4);
+            if (ti_row < C && co < cwv)
+                *reinterpret_cast<float4 *>(ib + ti_row * pitch + co) = make_float4(dacc[q][0], dacc[q][1], dacc[q][2], dacc[q][3]);
         }
         __syncthreads();
 
-        // ---- DW on own groups: one writer per written row, members in token order
-        const int32_t *meta = reinterpret_cast<const int32_t *>(cb + L.off_meta);
-        const int32_t ng = nl > 0 ? meta[2] : 0;
-        const int32_t g0 = int32_t(int64_t(ng) * k / K), g1 = int32_t(int64_t(ng) * (k + 1) / K);
-        const int4 *grec = reinterpret_cast<const int4 *>(cb + L.off_grec);
-        const int2 *mrec = reinterpret_cast<const int2 *>(cb + L.off_mrec);
-        const int64_t nit = int64_t(g1 - g0) * nvs;
-        for (int64_t base = tid; base < nit; base += 4 * BLOCK) {
-            int4 rec[4];
-            int vq[4];
-            bool ok[4];
-            typename Vec<T, V>::raw_t raw[4];
+        // ---- DW: one writer per written row, members in token order
+        {
+            const int32_t *meta = reinterpret_cast<const int32_t *>(cb + a.off_meta);
+            const int32_t ng = nl > 0 ? meta[2] : 0;
+            const int4 *grec = reinterpret_cast<const int4 *>(cb + a.off_grec);
+            const int2 *mrec = reinterpret_cast<const int2 *>(cb + a.off_mrec);
+            constexpr int GPI = kWave / NV;                       // groups per load instruction
+            const int gs = lane / NV, vq = lane % NV;
+            const bool vok = vq < nvs;
+            const uint32_t col = uint32_t(col0 + vq * V);
+            for (int32_t gb = wave * GPI * kDwBatch; gb < ng; gb += kP2Waves * GPI * kDwBatch) {
+                int4 rec[kDwBatch];
+                typename Vec<T, V>::raw_t raw[kDwBatch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t it = base + int64_t(u) * BLOCK;
-                ok[u] = it < nit;
-                const int32_t g = ok[u] ? g0 + int32_t(it / nvs) : g0;
-                vq[u] = ok[u] ? int(it % nvs) : 0;
-                rec[u] = ok[u] ? grec[g] : make_int4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (ok[u]) raw[u] = Vec<T, V>::load_raw(bank + int64_t(rec[u].x) * hd + int64_t(vq0 + vq[u]) * V);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (!ok[u]) continue;
-                float acc[V];
-                Vec<T, V>::unpack(raw[u], acc);
-                const float dec = __int_as_float(rec[u].w);
-#pragma unroll
-                for (int c = 0; c < V; ++c) acc[c] *= dec;
-                const int32_t m1 = rec[u].y + rec[u].z;
-                for (int32_t m = rec[u].y; m < m1; ++m) {
-                    const int2 mr = mrec[m];
-                    const float cwv = __int_as_float(mr.y);
-                    const float *dr = D + mr.x * cw + vq[u] * V;
-#pragma unroll
-                    for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dr[c], acc[c]);
+                for (int u = 0; u < kDwBatch; ++u) {
+                    const int32_t g = gb + u * GPI + gs;
+                    rec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(0, 0, 0, 0);
                 }
-                Vec<T, V>::store(bank + int64_t(rec[u].x) * hd + int64_t(vq0 + vq[u]) * V, acc);
+#pragma unroll
+                for (int u = 0; u < kDwBatch; ++u)
+                    if (rec[u].z > 0 && vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col));
+#pragma unroll
+                for (int u = 0; u < kDwBatch; ++u) {
+                    if (rec[u].z == 0) continue;
+                    float acc[V];
+                    if (vok) Vec<T, V>::unpack(raw[u], acc);
+                    const float dec = __int_as_float(rec[u].w);
+#pragma unroll
+                    for (int c = 0; c < V; ++c) acc[c] *= dec;
+                    const int32_t m1 = rec[u].y + rec[u].z;
+                    for (int32_t m = rec[u].y; m < m1; m += 8) {
+                        int2 mr[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) mr[q] = m + q < m1 ? *at(mrec, uint32_t(m + q)) : make_int2(0, 0);
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            if (m + q >= m1) break;
+                            const float cwv = __int_as_float(mr[q].y);
+                            float dv[V];
+                            lds_load_vec<V>(ib + mr[q].x * pitch + vq * V, dv);
+#pragma unroll
+                            for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+                        }
+                    }
+                    if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col), acc);
+                }
             }
         }
-        if (K > 1) team_barrier(ctr, ++bar * K, a.err, &broken);
-        else __syncthreads();
+        __syncthreads();
     }
-}
-
-__global__ void zero_words_kernel(int32_t *p, int64_t n) {
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
-        p[i] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------
-template <typename T, int V, int B>
+template <typename T, int V, int NV>
 static const void *p2_fn() {
-    return reinterpret_cast<const void *>(&phase2_kernel<T, V, B>);
+    return reinterpret_cast<const void *>(&phase2_kernel<T, V, NV>);
 }
 
-static const void *phase2_fn(int dtype, int V, int block) {
-    if (dtype == 0) {
-        if (V == 4) return block == 256 ? p2_fn<float, 4, 256>() : block == 512 ? p2_fn<float, 4, 512>() : p2_fn<float, 4, 1024>();
-        return block == 256 ? p2_fn<float, 1, 256>() : block == 512 ? p2_fn<float, 1, 512>() : p2_fn<float, 1, 1024>();
+template <typename T, int V>
+static const void *p2_fn_nv(int nv) {
+    switch (nv) {
+        case 1: return p2_fn<T, V, 1>();
+        case 2: return p2_fn<T, V, 2>();
+        case 4: return p2_fn<T, V, 4>();
+        default: return p2_fn<T, V, 8>();
     }
-    if (V == 8) return block == 256 ? p2_fn<bf16, 8, 256>() : block == 512 ? p2_fn<bf16, 8, 512>() : p2_fn<bf16, 8, 1024>();
-    return block == 256 ? p2_fn<bf16, 1, 256>() : block == 512 ? p2_fn<bf16, 1, 512>() : p2_fn<bf16, 1, 1024>();
+}
+
+static const void *phase2_fn(int dtype, int V, int nv) {
+    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4>(nv) : p2_fn_nv<float, 1>(nv);
+    return V == 8 ? p2_fn_nv<bf16, 8>(nv) : p2_fn_nv<bf16, 1>(nv);
 }
 
 hipError_t phase2_prepare() {
     for (int dt = 0; dt < 2; ++dt)
         for (int V : {1, dt == 0 ? 4 : 8})
-            for (int b : {256, 512, 1024}) {
-                hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, b), hipFuncAttributeMaxDynamicSharedMemorySize,
+            for (int nv : {1, 2, 4, 8}) {
+                hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv), hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    160 * 1024 - 256);
                 if (e != hipSuccess) return e;
             }
     return hipSuccess;
 }
 
-size_t phase2_lds_bytes(int C, int nv, int V, int K) {
-    const int tpw = (C + K - 1) / K;
-    return size_t(C + (K == 1 ? C : tpw)) * nv * V * sizeof(float);
-}
+size_t phase2_lds_bytes(int C, int nv, int V) { return size_t(2) * p2_rows(C) * p2_pitch(nv * V) * sizeof(float); }
 
-// Words of the workspace's Phase-2 control area: flag word, barrier counters and
-// exchange rows, bounded for any slicing of a head of hd columns.
-int64_t phase2_control_words(int P, int C, int hd) {
-    const int64_t ctr = align_words(int64_t(P) * (hd + 1));
-    const int64_t xch = align_words(int64_t(2) * C * P * (int64_t(hd) + 256));
-    return 64 + ctr + xch;
-}
-
-
-hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, uint32_t *control,
-                         hipStream_t st) {
-    P2Args a{pb, sl, g.nv, g.S, g.K, pb.hd / V, nullptr, nullptr, nullptr};
-    a.err = reinterpret_cast<int32_t *>(control);
-    a.ctr = reinterpret_cast<int32_t *>(control + 64);
-    a.xchg = reinterpret_cast<float *>(control + 64 + align_words(int64_t(pb.P) * (pb.hd + 1)));
-    const int64_t teams = int64_t(pb.P) * g.S;
-    const dim3 grid(unsigned(teams * g.K)), block(unsigned(g.block));
-    const size_t lds = phase2_lds_bytes(pb.C, g.nv, V, g.K);
-    const void *fn = phase2_fn(pb.dtype, V, g.block);
-    if (g.K > 1) {
-        hipLaunchKernelGGL(zero_words_kernel, dim3(unsigned((teams + 255) / 256)), dim3(256), 0, st, a.ctr, teams);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        void *args[] = {&a};
-        return hipLaunchCooperativeKernel(fn, grid, block, args, unsigned(lds), st);
-    }
+hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st) {
+    const ChunkLayout &L = sl.lay;
+    P2Args a{};
+    a.k_idx = pb.k_idx; a.q_idx = pb.q_idx; a.v = pb.v; a.bank = pb.bank; a.out = pb.out; a.valid = pb.valid;
+    a.ws = sl.ws; a.M = pb.M; a.words = L.words;
+    a.T = pb.T; a.C = pb.C; a.W = pb.W; a.R = pb.R; a.hd = pb.hd; a.P = pb.P;
+    a.S = g.S; a.hv = pb.hd / V; a.ti0 = sl.ti0; a.steps = sl.steps;
+    a.off_gw = int32_t(L.off_gw); a.off_gr = int32_t(L.off_gr); a.off_beta = int32_t(L.off_beta);
+    a.off_X = int32_t(L.off_X); a.off_QX = int32_t(L.off_QX); a.off_meta = int32_t(L.off_meta);
+    a.off_grec = int32_t(L.off_grec); a.off_mrec = int32_t(L.off_mrec);
+    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
     void *args[] = {&a};
-    return hipLaunchKernel(fn, grid, block, args, lds, st);
-}
-
-// Occupancy of a geometry: workgroups that fit on the device at once.
-hipError_t phase2_max_resident(int dtype, int V, const P2Geom &g, int C, int cus, int64_t *out) {
-    int per_cu = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, phase2_fn(dtype, V, g.block), g.block,
-                                                                phase2_lds_bytes(C, g.nv, V, g.K));
-    *out = int64_t(per_cu) * cus;
-    return e;
+    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv), grid, block, args, phase2_lds_bytes(pb.C, g.nv, V), st);
 }
 
 }  // namespace sdm

@@ -110,9 +110,8 @@ typedef struct {
  * (0 = all Nt = ceil(tokens / chunk) steps in one slab). A slab holds every Phase-1
  * quantity and both solve outputs of its P * slab_steps chunks (100 B per write entry,
  * 28 B per read entry, 16 B per chunk-matrix element and a slot search index of up to
- * 64 KiB per chunk), after a fixed control area
- * (exchange rows and barrier counters of the Phase-2 teams)
- * (the pages budget the same kinds of state, SLAB_BYTES in memory_ops.py).
+ * 64 KiB per chunk) (the pages budget the same kinds of state, SLAB_BYTES in
+ * memory_ops.py).
  * Returns 0 for arguments sdm_fwd would reject with SDM_ERR_SHAPE or SDM_ERR_RANGE.
  * Results never depend on the slab size.
  */

@@ -200,25 +200,20 @@ def test_workload_4p_sampled_streams(gpu):
 @pytest.mark.parametrize("wl", [
     small(P=8, T=300, C=64, hd=64, M=200, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=26),
     small(P=3, T=260, C=128, hd=32, M=300, W=16, R=16, ragged=True, index=27),
-], ids=["bf16_P8", "f32_P3"])
+    small(P=2, T=100, C=48, hd=40, M=80, W=5, R=3, ids="zipf", index=28),
+], ids=["bf16_P8", "f32_P3", "f32_partial_slice"])
 def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
-    """Column slicing, team size and block size change only the schedule: every
-    geometry gives the same bits, and no team barrier times out (flag word 0 of the
-    workspace stays 0)."""
-    from chunked_sparse_delta_amd import workspace_bytes
+    """The column slicing changes only the schedule: every slice width gives the same
+    bits (the gather, matmul and DW sums run in orders fixed by W, R and C)."""
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
-    V = 4 if wl.dtype == "f32" else 8
-    hv = wl.hd // V
     results = []
-    for geom in (None, "1,1,256", f"{hv},1,1024", f"{hv},4,256", "2,2,512", f"1,{wl.C // 16},256", "1,3,512"):
+    for geom in (None, "1", "2", "4", "8"):
         if geom is None:
             monkeypatch.delenv("SDM_P2_GEOM", raising=False)
         else:
             monkeypatch.setenv("SDM_P2_GEOM", geom)
-        ws = torch.zeros(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0), dtype=torch.uint8, device=gpu)
-        o, b = gu.run(t, wl.C, workspace=ws)
-        assert int(ws[:4].view(torch.int32).item()) == 0, f"barrier timeout flag set with geometry {geom}"
+        o, b = gu.run(t, wl.C)
         results.append((geom, gu.bits(o), gu.bits(b)))
     gu.parity(o, b, inp, wl.C, "geometry")
     for geom, ob, bb in results[1:]:
