@@ -126,6 +126,8 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     if (M < 1) return fail(SDM_ERR_SHAPE, "the bank needs at least one row per stream, got %lld", (long long)M);
     if (int64_t(P) * M >= (int64_t(1) << 31))
         return fail(SDM_ERR_RANGE, "%d streams of %lld rows: the bank has 2^31 or more slots", P, (long long)M);
+    if (M * hd * (dtype == SDM_F32 ? 4 : 2) >= (int64_t(1) << 31))
+        return fail(SDM_ERR_RANGE, "a stream's bank of %lld rows x %d columns is 2 GiB or more", (long long)M, hd);
     if (!slots->write || !slots->read || !weights->write || !weights->read || !beta || !g)
         return fail(SDM_ERR_NULL, "slot ids, weights, beta and log_decay must not be NULL");
     if (need_bank && (!v || !bank_data || !out)) return fail(SDM_ERR_NULL, "v, bank and out must not be NULL");
@@ -159,16 +161,20 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
 // Phase-2 geometry from shapes only (the bits never depend on it): slices of NV vectors,
 // NV the largest power of two with NV * V * es <= 128 bytes (one cache line of a row),
 // halved while that leaves fewer than one workgroup per CU; one workgroup per
-// (stream, slice). SDM_P2_GEOM="nv" overrides NV (1, 2, 4 or 8; for tuning sweeps).
+// (stream, slice) of 1024 threads. SDM_P2_GEOM="nv[,block]" overrides NV (1, 2, 4 or 8)
+// and the block size (512 or 1024), for tuning sweeps.
 P2Geom plan_phase2(const Problem &pb, int V, int es, int cus) {
     const int hv = pb.hd / V;
     P2Geom g{};
     g.nv = 8;
+    g.block = 1024;
     while (g.nv > 1 && (g.nv * V * es > 128 || g.nv > hv)) g.nv >>= 1;
     const char *env = getenv("SDM_P2_GEOM");
-    int enk = 0;
-    if (env && sscanf(env, "%d", &enk) == 1 && (enk == 1 || enk == 2 || enk == 4 || enk == 8)) {
+    int enk = 0, eb = 0;
+    const int got = env ? sscanf(env, "%d,%d", &enk, &eb) : 0;
+    if (got >= 1 && (enk == 1 || enk == 2 || enk == 4 || enk == 8)) {
         g.nv = enk;
+        if (got == 2 && (eb == 512 || eb == 1024)) g.block = eb;
         g.S = (hv + g.nv - 1) / g.nv;
         return g;
     }

@@ -142,7 +142,9 @@ struct ChunkLayout {
     int64_t off_shead;    // [E] i32: first sorted position of the group
     int64_t off_sgrp;     // [E] i32: group of sorted position
     int64_t off_gpos;     // [E+1] i32: group start positions
-    int64_t off_grec;     // [E] int4: DW group record {slot, first position, members, bits of exp(L_last)}
+    int64_t off_grec;     // [E] int4: DW group record {slot, first position | (members - 1) << 16 |
+                          //   first member's token << 24, bits of exp(L_last), bits of the first member's
+                          //   k exp(L_last - L)}
     int64_t off_mrec;     // [E] int2: DW member record {token, bits of k exp(L_last - L)}
     int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
     int64_t off_ecr;      // [E] int4 transposed: cold write entry {a, m, bits k, bits L} (a == m: none)
@@ -150,12 +152,13 @@ struct ChunkLayout {
     int64_t off_ska;      // [E] f32 per sorted position of a hot group: k exp(L - L_ref)
     int64_t off_skb;      // [E] f32 per sorted position of a hot group: k exp(L_ref - L)
     int64_t off_hgrp;     // [HMAX] i32: group of hot index
+    int64_t off_brec;     // [HMAX] int4: DW group records of the groups with >= kHotMin members
     int64_t off_bstart;   // [NB+1] i32: first sorted position of each slot bucket
     int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
     int64_t off_rcr;      // [F] int4 transposed: cold read {a, end, bits q, bits Lr} (a == end: none)
     int64_t off_rhot;     // [F] i32 transposed: hot index of the read slot's group, or -1
     int64_t off_rval;     // [F] f32 transposed: q exp(Lr - L_ref) of a hot read
-    int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups
+    int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups, groups with >= kHotMin members
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
     int64_t words;        // 4-byte words per chunk
@@ -196,6 +199,7 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_ska = take(L.E);
     L.off_skb = take(L.E);
     L.off_hgrp = take(L.HMAX);
+    L.off_brec = take(4 * L.HMAX);
     L.off_bstart = take(L.NB + 1);
     L.off_gr = take(L.F);
     L.off_rcr = take(4 * L.F);
@@ -211,9 +215,9 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     return L;
 }
 
-// Phase-2 launch geometry: vectors per column slice, slices per row.
+// Phase-2 launch geometry: vectors per column slice, slices per row, threads per workgroup.
 struct P2Geom {
-    int nv, S;
+    int nv, S, block;
 };
 
 struct Slab {

@@ -270,6 +270,7 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
     float *ska = reinterpret_cast<float *>(cb + L.off_ska);
     float *skb = reinterpret_cast<float *>(cb + L.off_skb);
     int32_t *hgrp = reinterpret_cast<int32_t *>(cb + L.off_hgrp);
+    int4 *brec = reinterpret_cast<int4 *>(cb + L.off_brec);
     int32_t *bstart = reinterpret_cast<int32_t *>(cb + L.off_bstart);
     int32_t *meta = reinterpret_cast<int32_t *>(cb + L.off_meta);
     float *beta_c = reinterpret_cast<float *>(cb + L.off_beta);
@@ -341,9 +342,12 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
         const int32_t g = sgrp[m], a = shead[m], b = gpos[g + 1];
         const float Lm = __int_as_float(pk.w), kv = __int_as_float(pk.z);
         const float Llast = __int_as_float(spk[b - 1].w);
-        mrec[m] = make_int2(pk.y, __float_as_int(kv * expf(Llast - Lm)));
+        const float cwm = kv * expf(Llast - Lm);
+        mrec[m] = make_int2(pk.y, __float_as_int(cwm));
         gw[int32_t(sval[m])] = kv * expf(Lm);
-        if (m == a) grec[g] = make_int4(pk.x, a, b - a, __float_as_int(expf(Llast)));
+        // first member inline: position (< 2^16), members - 1 (< 2^8) and token (< 2^8) in one word
+        if (m == a) grec[g] = make_int4(pk.x, a | ((b - a - 1) << 16) | (pk.y << 24), __float_as_int(expf(Llast)),
+                                        __float_as_int(cwm));
     }
 
     // Pass 3: hot groups. Candidates (at least kHotMin members) in group order; a wave
@@ -362,7 +366,10 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
         float dev = 0.0f;
         for (int32_t m = a + lane; m < b; m += kWave) dev = fmaxf(dev, fabsf(__int_as_float(spk[m].w) - Lref));
         dev = wave_max(dev);
-        if (lane == 0) cand_hot[c] = dev <= kHotSpan ? 1 : 0;
+        if (lane == 0) {
+            cand_hot[c] = dev <= kHotSpan ? 1 : 0;
+            brec[c] = grec[g];   // the big groups' DW records, in group order
+        }
     }
     __syncthreads();
     for (int32_t t0 = 0; t0 < nc; t0 += BLOCK) {
@@ -375,7 +382,10 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
         }
     }
     __syncthreads();
-    if (tid == 0) meta[3] = nhot;
+    if (tid == 0) {
+        meta[3] = nhot;
+        meta[4] = nc;
+    }
 
     // Pass 4, per sorted position: factored decays of hot members; the cold pair ranges
     // (earlier members of the group) by token-major transposed entry.

@@ -12,16 +12,17 @@
 // Workgroups of one stream are placed on one XCD (blocks are dealt round-robin to the
 // 8 XCDs) so that its slices share one L2 for the chunk's ids, weights and matrices.
 //
-// Per step, with 16 wavefronts:
+// Per step, with 8 wavefronts of up to 256 VGPRs each:
 //   gather   a wavefront takes whole tokens; each load instruction fetches one slice of
-//            64 / NV rows (8 entry classes x 8 / NV tokens), eight instructions in flight,
-//            the next batch's ids and weights loaded under the current batch's rows
-//   u        u = beta (v - retrieved) in LDS, v prefetched before the gather
+//            64 / NV rows (8 entry classes x 8 / NV tokens), 12 to 16 instructions in
+//            flight, the next batch's ids and weights loaded under the current batch's rows
+//   u        u = beta (v - retrieved) in LDS
 //   matmul   D^T = u^T QX^T and u^T X^T on v_mfma_f32_16x16x4f32: 16 x 16 output tiles
 //            (16 columns x 16 tokens), lower-triangular tiles only; readings (+ inter)
 //            go straight to memory, delta_v to LDS
-//   DW       64 / NV groups per load instruction, four in flight per lane, member
-//            records eight at a time
+//   DW       64 / NV groups per load instruction, eight in flight per lane; the first
+//            member rides in the group record, the second comes with the bank row, the
+//            rest four at a time; the next batch's records load under the current one
 //
 // Determinism: each output element has exactly one writer, and every sum runs in an order
 // fixed by the shapes W, R and C only (never by the slicing or the launch):
@@ -35,13 +36,18 @@ namespace sdm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kP2Block = 1024;
-constexpr int kP2Waves = kP2Block / kWave;
-constexpr int kBatch = 8;      // gather row loads in flight per lane
-constexpr int kDwBatch = 4;    // DW groups in flight per lane
-constexpr int kMaxTilesPerWave = (kMaxChunk / 16) * 4 / kP2Waves;   // 16 x 16 tiles, 64 columns at most
+// Per block size: wavefronts, gather row loads in flight per lane, DW groups in flight per
+// lane, 16 x 16 matmul tiles per wavefront (C <= 256, slices of <= 64 columns), k blocks of
+// matrix operands loaded at once. 1024 threads leave 128 VGPRs per lane, 512 threads 256.
+template <int BLOCK, int V> struct P2Cfg {
+    static constexpr int NW = BLOCK / kWave;
+    static constexpr int kBatch = BLOCK == 1024 ? (V == 1 ? 8 : 6) : (V == 1 ? 16 : 12);
+    static constexpr int kDwBatch = BLOCK == 1024 ? 4 : 8;
+    static constexpr int kMaxTiles = (kMaxChunk / 16) * 4 / NW;
+    static constexpr int kMmDepth = BLOCK == 1024 ? 2 : 3;
+    static constexpr int kUItems = (kMaxChunk * 8 + BLOCK - 1) / BLOCK;
+};
 
-// Only what Phase 2 reads: every field is uniform and stays in scalar registers.
 struct P2Args {
     const int32_t *k_idx, *q_idx;   // [P, T, W], [P, T, R]
     const void *v;                  // [P, T, hd]
@@ -53,7 +59,7 @@ struct P2Args {
     int32_t T, C, W, R, hd, P;
     int32_t S, hv;                  // slices per row, vectors per row (hd / V)
     int32_t ti0, steps;             // the slab
-    int32_t off_gw, off_gr, off_beta, off_X, off_QX, off_meta, off_grec, off_mrec;   // words within a chunk
+    int32_t off_gw, off_gr, off_beta, off_X, off_QX, off_meta, off_grec, off_mrec, off_brec;   // words within a chunk
 };
 
 __device__ __forceinline__ int32_t live_tokens(const P2Args &a, int p, int ti) {
@@ -117,12 +123,14 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
 // tokens of the chunk, into dst[t * pitch + vq * V + c]. Lane layout: vq = lane % NV (the
 // vector of the slice), class r = (lane / NV) % 8, ts = lane / (8 NV) (the token within a
 // group of TPI = 8 / NV tokens). Instruction j of a token group loads entries 8 j + r.
-// The wave walks its token groups (wave, wave + 16, ...) as one flat list of
+// The wave walks its token groups (wave, wave + NW, ...) as one flat list of
 // instructions, kBatch at a time.
-template <typename T, int V, int NV>
+template <typename T, int V, int NV, int BLOCK>
 __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
                                               int nl, int col0, int nvs, float *dst, int pitch, int wave, int lane) {
     constexpr int TPI = 8 / NV;
+    constexpr int kBatch = P2Cfg<BLOCK, V>::kBatch;
+    constexpr int kP2Waves = P2Cfg<BLOCK, V>::NW;
     const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
     const int NI = (width + 7) >> 3;
     const int NG = (nl + TPI - 1) / TPI;
@@ -165,7 +173,7 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
         load_pairs(nid, nwt);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (i0 + u >= total) break;
+            if (i0 + u >= total) continue;
             if (id[u] >= 0 && vok) {
                 float row[V];
                 Vec<T, V>::unpack(raw[u], row);
@@ -224,8 +232,69 @@ __device__ __forceinline__ void load_bop(const float *M, int C, int i, int k, bo
     }
 }
 
-template <typename T, int V, int NV>
-__global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
+// DW of one group with many members (>= kHotMin) by a whole wavefront: lane (r, p) =
+// (lane / 8, lane % 8) sums the members m = r, r + 8, ... of the group in token order for
+// vector p of the slice; the eight classes combine as in the gather, and the decay term
+// comes first: B[s] = exp(L_last) B[s] + ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)). The member
+// records (at most 256) are loaded once, four per lane, and broadcast by lane shuffles.
+template <typename T, int V>
+__device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, const int2 *mrec, const float *dl,
+                                             int pitch, int col0, int nvs, int lane) {
+    const int r = lane >> 3, p = lane & 7;
+    const bool pok = p < nvs;
+    const int32_t m0 = rec.y & 0xFFFF, n = ((rec.y >> 16) & 0xFF) + 1;
+    const uint32_t col = uint32_t(col0 + p * V);
+    typename Vec<T, V>::raw_t raw;
+    if (pok) raw = Vec<T, V>::load_raw(at(bank, uint32_t(rec.x) * uint32_t(hd) + col));
+    int32_t rt[4], rc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = lane + 64 * q;
+        int2 x = make_int2(0, 0);
+        if (m < n) x = *at(mrec, uint32_t(m0 + m));
+        rt[q] = x.x;
+        rc[q] = x.y;
+    }
+    float acc[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] = 0.0f;
+    // member j of class r is m = r + 8 j: lane m % 64 = r + 8 (j % 8), register j / 8
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (64 * q >= n) break;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int src = r + 8 * jj;
+            const int32_t t = __shfl(rt[q], src, 64);
+            const float cw = __int_as_float(__shfl(rc[q], src, 64));
+            if (64 * q + src < n && pok) {
+                float dv[V];
+                lds_load_vec<V>(dl + t * pitch + p * V, dv);
+#pragma unroll
+                for (int c = 0; c < V; ++c) acc[c] = fmaf(cw, dv[c], acc[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 8, 64);
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 16, 64);
+#pragma unroll
+    for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
+    if (r == 0 && pok) {
+        float b[V];
+        Vec<T, V>::unpack(raw, b);
+        const float dec = __int_as_float(rec.z);
+#pragma unroll
+        for (int c = 0; c < V; ++c) b[c] = b[c] * dec + acc[c];
+        Vec<T, V>::store(at(bank, uint32_t(rec.x) * uint32_t(hd) + col), b);
+    }
+}
+
+template <typename T, int V, int NV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
+    using Cfg = P2Cfg<BLOCK, V>;
+    constexpr int NW = Cfg::NW;
     extern __shared__ float lds[];
     const int C = a.C, hd = a.hd, S = a.S;
     constexpr int CW = V * NV;                // columns of a full slice
@@ -257,9 +326,6 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     // so that every wave gets a similar share of the triangular work.
     const int NIT = CP / 16, NCT = (cwv + 15) / 16, NT = NIT * NCT;
 
-    // u items: (t, vq) = (item / NV, item % NV) for item = tid + kP2Block * x
-    constexpr int kUItems = (kMaxChunk * 8 + kP2Block - 1) / kP2Block;
-
     for (int s = 0; s < a.steps; ++s) {
         // Thread ids are re-read opaquely every step, so that the per-lane address
         // arithmetic of all phases is not hoisted out of the step loop (it would be held
@@ -268,7 +334,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         asm volatile("" : "+v"(tid));
         int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         asm volatile("" : "+s"(wave));
-        const int lane = tid & 63;
+        int lane = tid & 63;
         const int ti = a.ti0 + s;
         const uint32_t *cb = a.ws + (int64_t(p) * a.steps + s) * a.words;
         const int nl = live_tokens(a, p, ti);
@@ -281,16 +347,16 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         {
             const float *gw = reinterpret_cast<const float *>(cb + a.off_gw);
             const float *gr = reinterpret_cast<const float *>(cb + a.off_gr);
-            gather_region<T, V, NV>(bank, hd, a.k_idx + tok0 * a.W, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
-            gather_region<T, V, NV>(bank, hd, a.q_idx + tok0 * a.R, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
+            gather_region<T, V, NV, BLOCK>(bank, hd, a.k_idx + tok0 * a.W, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
+            gather_region<T, V, NV, BLOCK>(bank, hd, a.q_idx + tok0 * a.R, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
         }
         __syncthreads();
 
         // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1
         const float *beta_c = reinterpret_cast<const float *>(cb + a.off_beta);
 #pragma unroll
-        for (int x = 0; x < kUItems; ++x) {
-            const int item = tid + kP2Block * x, t = item / NV, vq = item % NV;
+        for (int x = 0; x < Cfg::kUItems; ++x) {
+            const int item = tid + BLOCK * x, t = item / NV, vq = item % NV;
             if (t >= CP) continue;
             float *ur = ub + t * pitch + vq * V;
             float uu[V];
@@ -310,13 +376,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         __syncthreads();
 
         // ---- dual matmul on the matrix cores
+        asm volatile("" : "+v"(lane));
         const float *QX = reinterpret_cast<const float *>(cb + a.off_QX);
         const float *X = reinterpret_cast<const float *>(cb + a.off_X);
-        f32x4 dacc[kMaxTilesPerWave];
+        f32x4 dacc[Cfg::kMaxTiles];
 #pragma unroll
-        for (int q = 0; q < kMaxTilesPerWave; ++q) {
+        for (int q = 0; q < Cfg::kMaxTiles; ++q) {
             dacc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const int tau = q * kP2Waves + ((q & 1) ? kP2Waves - 1 - wave : wave);
+            const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
             if (tau >= NT) continue;
             const int it = tau / NCT, ct = tau - it * NCT;
             const int ti_row = 16 * it + (lane & 15);          // token of the B operand / output
@@ -329,26 +396,24 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 y = f32x4{iv.x, iv.y, iv.z, iv.w};
             }
             f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            float bq[4], bx[4];
-            load_bop(QX, C, ti_row, ko, vec4, bq);
-            load_bop(X, C, ti_row, ko, vec4, bx);
-            for (int kt = 0; kt <= it; ++kt) {
-                float nq[4], nx[4];
-                if (kt < it) {
-                    load_bop(QX, C, ti_row, 16 * (kt + 1) + ko, vec4, nq);
-                    load_bop(X, C, ti_row, 16 * (kt + 1) + ko, vec4, nx);
+            // k blocks kMmDepth at a time: the operands of those blocks are loaded together
+            for (int kb = 0; kb <= it; kb += Cfg::kMmDepth) {
+                float bq[Cfg::kMmDepth][4], bx[Cfg::kMmDepth][4];
+#pragma unroll
+                for (int j = 0; j < Cfg::kMmDepth; ++j) {
+                    if (kb + j > it) continue;
+                    load_bop(QX, C, ti_row, 16 * (kb + j) + ko, vec4, bq[j]);
+                    load_bop(X, C, ti_row, 16 * (kb + j) + ko, vec4, bx[j]);
                 }
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const float av = cu < cwv ? ub[(16 * kt + ko + kk) * pitch + cu] : 0.0f;
-                    y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bq[kk], y, 0, 0, 0);
-                    d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx[kk], d, 0, 0, 0);
-                }
-                if (kt < it) {
+                for (int j = 0; j < Cfg::kMmDepth; ++j) {
+                    if (kb + j > it) continue;
+                    const float *urow = ub + (16 * (kb + j) + ko) * pitch + cu;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        bq[kk] = nq[kk];
-                        bx[kk] = nx[kk];
+                        const float av = cu < cwv ? urow[kk * pitch] : 0.0f;
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bq[j][kk], y, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx[j][kk], d, 0, 0, 0);
                     }
                 }
             }
@@ -361,8 +426,8 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         __syncthreads();
         // delta_v -> ib
 #pragma unroll
-        for (int q = 0; q < kMaxTilesPerWave; ++q) {
-            const int tau = q * kP2Waves + ((q & 1) ? kP2Waves - 1 - wave : wave);
+        for (int q = 0; q < Cfg::kMaxTiles; ++q) {
+            const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
             if (tau >= NT) continue;
             const int it = tau / NCT, ct = tau - it * NCT;
             const int ti_row = 16 * it + (lane & 15), co = 16 * ct + 4 * (lane >> 4);
@@ -371,52 +436,100 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         }
         __syncthreads();
 
-        // ---- DW: one writer per written row, members in token order
+        // ---- DW: one writer per written row. Groups with >= kHotMin members go to whole
+        //      wavefronts (dw_big_group, from the list of their records); the others are
+        //      summed in token order by the NV lanes of their slice: lane (gs, vq) takes
+        //      group gb + u * GPI + gs of each batch, the first member rides in the group
+        //      record, the second loads with the bank row, the rest four at a time.
         {
+            int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
+            asm volatile("" : "+v"(dlane));
             const int32_t *meta = reinterpret_cast<const int32_t *>(cb + a.off_meta);
-            const int32_t ng = nl > 0 ? meta[2] : 0;
+            const int32_t ng = nl > 0 ? meta[2] : 0, nbig = nl > 0 ? meta[4] : 0;
             const int4 *grec = reinterpret_cast<const int4 *>(cb + a.off_grec);
+            const int4 *brec = reinterpret_cast<const int4 *>(cb + a.off_brec);
             const int2 *mrec = reinterpret_cast<const int2 *>(cb + a.off_mrec);
+            for (int32_t bi = wave; bi < nbig; bi += NW) {
+                const int4 rec = *at(brec, uint32_t(bi));
+                dw_big_group<T, V>(bank, hd, rec, mrec, ib, pitch, col0, nvs, dlane);
+            }
             constexpr int GPI = kWave / NV;                       // groups per load instruction
-            const int gs = lane / NV, vq = lane % NV;
+            constexpr int kB = Cfg::kDwBatch;
+            constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
+            const int gs = dlane / NV, vq = dlane % NV;
             const bool vok = vq < nvs;
             const uint32_t col = uint32_t(col0 + vq * V);
-            for (int32_t gb = wave * GPI * kDwBatch; gb < ng; gb += kP2Waves * GPI * kDwBatch) {
-                int4 rec[kDwBatch];
-                typename Vec<T, V>::raw_t raw[kDwBatch];
+            // a record of a group with fewer than kHotMin members (slot -1: no group)
+            auto small = [](const int4 &r) { return r.x >= 0 && ((r.y >> 16) & 0xFF) < kHotMin - 1; };
+            int4 rec[kB];
 #pragma unroll
-                for (int u = 0; u < kDwBatch; ++u) {
-                    const int32_t g = gb + u * GPI + gs;
-                    rec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(0, 0, 0, 0);
+            for (int u = 0; u < kB; ++u) {
+                const int32_t g = wave * GPI * kB + u * GPI + gs;
+                rec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(-1, 0, 0, 0);
+            }
+            for (int32_t gb = wave * GPI * kB; gb < ng; gb += kStride) {
+                typename Vec<T, V>::raw_t raw[kB];
+                int2 mr[kB];
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    if (!small(rec[u])) continue;
+                    if (vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col));
+                    const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
+                    mr[u] = n1 > 0 ? *at(mrec, uint32_t(m0 + 1)) : make_int2(0, 0);
+                }
+                int4 nrec[kB];
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const int32_t g = gb + kStride + u * GPI + gs;
+                    nrec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(-1, 0, 0, 0);
                 }
 #pragma unroll
-                for (int u = 0; u < kDwBatch; ++u)
-                    if (rec[u].z > 0 && vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col));
-#pragma unroll
-                for (int u = 0; u < kDwBatch; ++u) {
-                    if (rec[u].z == 0) continue;
+                for (int u = 0; u < kB; ++u) {
+                    if (!small(rec[u])) continue;
+                    const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF, t0 = (rec[u].y >> 24) & 0xFF;
                     float acc[V];
-                    if (vok) Vec<T, V>::unpack(raw[u], acc);
-                    const float dec = __int_as_float(rec[u].w);
+                    if (vok) {
+                        Vec<T, V>::unpack(raw[u], acc);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < V; ++c) acc[c] = 0.0f;
+                    }
+                    const float dec = __int_as_float(rec[u].z);
 #pragma unroll
                     for (int c = 0; c < V; ++c) acc[c] *= dec;
-                    const int32_t m1 = rec[u].y + rec[u].z;
-                    for (int32_t m = rec[u].y; m < m1; m += 8) {
-                        int2 mr[8];
+                    {
+                        const float cwv = __int_as_float(rec[u].w);
+                        float dv[V];
+                        lds_load_vec<V>(ib + t0 * pitch + vq * V, dv);
 #pragma unroll
-                        for (int q = 0; q < 8; ++q) mr[q] = m + q < m1 ? *at(mrec, uint32_t(m + q)) : make_int2(0, 0);
+                        for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+                    }
+                    if (n1 > 0) {
+                        const float cwv = __int_as_float(mr[u].y);
+                        float dv[V];
+                        lds_load_vec<V>(ib + mr[u].x * pitch + vq * V, dv);
 #pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            if (m + q >= m1) break;
-                            const float cwv = __int_as_float(mr[q].y);
+                        for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+                    }
+                    // members 2.. (at most kHotMin - 2 of them), four records at a time
+                    for (int32_t m = m0 + 2; m <= m0 + n1; m += 4) {
+                        int2 mb[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) mb[q] = m + q <= m0 + n1 ? *at(mrec, uint32_t(m + q)) : make_int2(0, 0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if (m + q > m0 + n1) break;
+                            const float cwv = __int_as_float(mb[q].y);
                             float dv[V];
-                            lds_load_vec<V>(ib + mr[q].x * pitch + vq * V, dv);
+                            lds_load_vec<V>(ib + mb[q].x * pitch + vq * V, dv);
 #pragma unroll
                             for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                         }
                     }
                     if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col), acc);
                 }
+#pragma unroll
+                for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
             }
         }
         __syncthreads();
@@ -426,34 +539,35 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
 // ---------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------
-template <typename T, int V, int NV>
-static const void *p2_fn() {
-    return reinterpret_cast<const void *>(&phase2_kernel<T, V, NV>);
-}
-
-template <typename T, int V>
+template <typename T, int V, int B>
 static const void *p2_fn_nv(int nv) {
     switch (nv) {
-        case 1: return p2_fn<T, V, 1>();
-        case 2: return p2_fn<T, V, 2>();
-        case 4: return p2_fn<T, V, 4>();
-        default: return p2_fn<T, V, 8>();
+        case 1: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 1, B>);
+        case 2: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 2, B>);
+        case 4: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 4, B>);
+        default: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 8, B>);
     }
 }
 
-static const void *phase2_fn(int dtype, int V, int nv) {
-    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4>(nv) : p2_fn_nv<float, 1>(nv);
-    return V == 8 ? p2_fn_nv<bf16, 8>(nv) : p2_fn_nv<bf16, 1>(nv);
+template <int B>
+static const void *phase2_fn_b(int dtype, int V, int nv) {
+    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, B>(nv) : p2_fn_nv<float, 1, B>(nv);
+    return V == 8 ? p2_fn_nv<bf16, 8, B>(nv) : p2_fn_nv<bf16, 1, B>(nv);
+}
+
+static const void *phase2_fn(int dtype, int V, int nv, int block) {
+    return block == 512 ? phase2_fn_b<512>(dtype, V, nv) : phase2_fn_b<1024>(dtype, V, nv);
 }
 
 hipError_t phase2_prepare() {
     for (int dt = 0; dt < 2; ++dt)
         for (int V : {1, dt == 0 ? 4 : 8})
-            for (int nv : {1, 2, 4, 8}) {
-                hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   160 * 1024 - 256);
-                if (e != hipSuccess) return e;
-            }
+            for (int nv : {1, 2, 4, 8})
+                for (int b : {512, 1024}) {
+                    hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv, b),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
+                    if (e != hipSuccess) return e;
+                }
     return hipSuccess;
 }
 
@@ -468,10 +582,10 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
     a.S = g.S; a.hv = pb.hd / V; a.ti0 = sl.ti0; a.steps = sl.steps;
     a.off_gw = int32_t(L.off_gw); a.off_gr = int32_t(L.off_gr); a.off_beta = int32_t(L.off_beta);
     a.off_X = int32_t(L.off_X); a.off_QX = int32_t(L.off_QX); a.off_meta = int32_t(L.off_meta);
-    a.off_grec = int32_t(L.off_grec); a.off_mrec = int32_t(L.off_mrec);
-    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
+    a.off_grec = int32_t(L.off_grec); a.off_mrec = int32_t(L.off_mrec); a.off_brec = int32_t(L.off_brec);
+    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(unsigned(g.block));
     void *args[] = {&a};
-    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv), grid, block, args, phase2_lds_bytes(pb.C, g.nv, V), st);
+    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv, g.block), grid, block, args, phase2_lds_bytes(pb.C, g.nv, V), st);
 }
 
 }  // namespace sdm
