@@ -4,22 +4,22 @@
 //     QX = QK X          (QK lower triangular with its diagonal)
 // Both are written dense [C, C] with +0 above the diagonal.
 //
-// One workgroup of 256 threads per chunk, 64 x 64 blocks (nb = ceil(C / 64) <= 4 block
+// One workgroup per chunk. The matrices are cut into 16 x 16 tiles (nb = ceil(C / 16) tile
 // rows; rows and columns >= C act as identity rows of I + Lm, so any C is exact: the
-// leading block of a lower-triangular inverse is the inverse of the leading block).
-//   1. Diagonal blocks: thread (b, j) solves (I + Lm_bb) x = e_j by forward substitution
-//      with the column kept in LDS; all nb diagonal blocks at once.
-//   2. Blocks below the diagonal, one column block j at a time, going down:
-//      X_ij = -X_ii (sum_{k=j}^{i-1} Lm_ik X_kj).
-//   3. QX_ij = sum_{k=j}^{i} QK_ik X_kj for i >= j.
-// Block products stage 64 x 64 tiles in LDS; each thread owns a 4 x 4 output tile and
-// accumulates in float32 FMAs over k in ascending order, a fixed order for every launch.
+// leading block of a lower-triangular inverse is the inverse of the leading block). X is
+// held in LDS as its nb (nb + 1) / 2 lower tiles.
+//   1. Diagonal tiles: 16 lanes per tile, lane j solves (I + Lm_bb) x = e_j by forward
+//      substitution, fully unrolled (x_r = -sum_{k<r} Lm[r][k] x_k, k ascending).
+//   2. Recursive doubling: for block sizes s = 16, 32, 64, 128, each pair of neighbouring
+//      diagonal blocks [[X11, 0], [N21, X22]] gets X21 = -X22 (N21 X11), N21 = beta A21.
+//   3. QX_IJ = sum_{K=J}^{I} QK_IK X_KJ.
+// Tile products run on v_mfma_f32_16x16x4f32, k blocks of 16 ascending: a fixed order for
+// every launch.
 #include "common.h"
 
 namespace sdm {
 
-constexpr int kB = 64;        // block edge
-constexpr int kP = kB + 1;    // LDS row pitch
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct WyArgs {
     const float *A, *beta, *QK;
@@ -29,59 +29,60 @@ struct WyArgs {
     int64_t bstride;  // floats between consecutive chunks' beta
 };
 
-// tile <- rows r0.., cols c0.. of M (C x C, row-major); zero outside [C, C], and above
-// the diagonal when `lower` (so that part of M is never read). rowscale (if given)
-// multiplies row r by rowscale[r].
-__device__ __forceinline__ void wy_load_tile(float *tile, const float *M, const float *rowscale, int C, int r0, int c0,
-                                             bool lower = false) {
-    for (int idx = threadIdx.x; idx < kB * kB; idx += blockDim.x) {
-        const int r = idx >> 6, c = idx & 63;
-        const int gr = r0 + r, gc = c0 + c;
-        float v = 0.0f;
-        if (gr < C && gc < C && (!lower || gc <= gr)) {
-            v = M[int64_t(gr) * C + gc];
-            if (rowscale) v *= rowscale[gr];
-        }
-        tile[r * kP + c] = v;
+constexpr int kTile = 256;   // floats of a 16 x 16 tile (row-major, pitch 16)
+
+__device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// A-operand of a 16 x 16 x 16 block from global memory: lane l holds
+// rs[r] * M[r][k0 + 4 (l >> 4) + kk], r = r0 + (l & 15), kk = 0..3, zero outside [C, C]
+// and, with `lower`, above the diagonal (k > r).
+__device__ __forceinline__ void wy_gop(const float *M, const float *rs, int C, int r0, int k0, bool lower, int lane,
+                                       float (&o)[4]) {
+    const int r = r0 + (lane & 15), k = k0 + 4 * (lane >> 4);
+    const float sc = (rs && r < C) ? rs[r] : 1.0f;
+    if (r < C && k + 3 < C && (C & 3) == 0) {
+        const float4 x = *reinterpret_cast<const float4 *>(M + int64_t(r) * C + k);
+        o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) o[kk] = (r < C && k + kk < C) ? M[int64_t(r) * C + k + kk] : 0.0f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        o[kk] *= sc;
+        if (lower && k + kk > r) o[kk] = 0.0f;
     }
 }
 
-__device__ __forceinline__ void wy_mma(float (&acc)[4][4], const float *Ta, const float *Tb) {
-    const int rr = (threadIdx.x >> 4) * 4, cc = (threadIdx.x & 15) * 4;
-#pragma unroll 8
-    for (int k = 0; k < kB; ++k) {
-        float a[4], b[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) a[x] = Ta[(rr + x) * kP + k];
-#pragma unroll
-        for (int y = 0; y < 4; ++y) b[y] = Tb[k * kP + cc + y];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(a[x], b[y], acc[x][y]);
-    }
+// A-operand from an LDS tile (row l & 15, columns 4 (l >> 4) .. + 3).
+__device__ __forceinline__ void wy_lop_a(const float *T, int lane, float (&o)[4]) {
+    const float4 x = *reinterpret_cast<const float4 *>(T + (lane & 15) * 16 + 4 * (lane >> 4));
+    o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
 }
 
-__device__ __forceinline__ void wy_store_tile(float *M, const float (&acc)[4][4], float sign, int C, int r0, int c0) {
-    const int rr = (threadIdx.x >> 4) * 4, cc = (threadIdx.x & 15) * 4;
+// B-operand from an LDS tile: lane l holds T[4 (l >> 4) + kk][l & 15].
+__device__ __forceinline__ void wy_lop_b(const float *T, int lane, float (&o)[4]) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int gr = r0 + rr + x, gc = c0 + cc + y;
-            if (gr < C && gc < C) M[int64_t(gr) * C + gc] = sign * acc[x][y];
-        }
+    for (int kk = 0; kk < 4; ++kk) o[kk] = T[(4 * (lane >> 4) + kk) * 16 + (lane & 15)];
 }
 
-__device__ __forceinline__ void wy_acc_to_tile(float *tile, const float (&acc)[4][4]) {
-    const int rr = (threadIdx.x >> 4) * 4, cc = (threadIdx.x & 15) * 4;
+__device__ __forceinline__ f32x4 mfma4(const float (&a)[4], const float (&b)[4], f32x4 acc) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) tile[(rr + x) * kP + cc + y] = acc[x][y];
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b[kk], acc, 0, 0, 0);
+    return acc;
 }
 
-__global__ __launch_bounds__(256) void wy_kernel(WyArgs a) {
+// Accumulator tile (lane l holds rows 4 (l >> 4) + v, column l & 15) to an LDS tile.
+__device__ __forceinline__ void wy_store_tile(float *T, const f32x4 &d, float sign, int lane) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) T[(4 * (lane >> 4) + v) * 16 + (lane & 15)] = sign * d[v];
+}
+
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void wy_kernel(WyArgs a) {
+    constexpr int NW = BLOCK / kWave;
+    constexpr int kMaxNb = BLOCK == 1024 ? 16 : 4;           // tile rows this block size serves
+    constexpr int kMaxPer = (kMaxNb / 2) * (kMaxNb / 2) / NW > 0 ? (kMaxNb / 2) * (kMaxNb / 2) / NW : 1;
     extern __shared__ float lds[];
     const int64_t n = blockIdx.x;
     const int C = a.C;
@@ -90,116 +91,144 @@ __global__ __launch_bounds__(256) void wy_kernel(WyArgs a) {
     const float *beta = a.beta + n * a.bstride;
     float *X = a.X + n * a.stride;
     float *QX = a.QX + n * a.stride;
-    const int nb = (C + kB - 1) / kB;
-    const int tid = threadIdx.x;
-    float *xs_all = lds + nb * kB * kP;   // [nb][64][64] column solutions
+    const int nb = (C + 15) >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float *Xt = lds;   // lower tiles of X
 
-    // 1. diagonal blocks: stage Lm_bb (strict lower, beta-scaled) for every block b < nb.
-    for (int idx = tid; idx < nb * kB * kB; idx += 256) {
-        const int b = idx >> 12, r = (idx >> 6) & 63, c = idx & 63;
-        const int gr = b * kB + r, gc = b * kB + c;
+    // 1. diagonal tiles: stage Lm_bb (strict lower, beta-scaled), then invert in place.
+    for (int idx = tid; idx < nb * kTile; idx += BLOCK) {
+        const int b = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+        const int gr = 16 * b + r, gc = 16 * b + c;
         float v = 0.0f;
         if (c < r && gr < C) v = beta[gr] * A[int64_t(gr) * C + gc];
-        lds[b * kB * kP + r * kP + c] = v;
+        Xt[tri_index(b, b) * kTile + r * 16 + c] = v;
     }
     __syncthreads();
     {
-        // Thread (b, j) solves column j of block b: x_r = -sum_{k=j}^{r-1} Lm[r][k] x_k.
-        const int b = tid >> 6, j = tid & 63;
+        const int b = wave * 4 + (lane >> 4), j = lane & 15;
+        float x[16];
         if (b < nb) {
-            const float *Lb = lds + b * kB * kP;
-            float *xs = xs_all + b * kB * kB;
-            const int gc = b * kB + j;
-            for (int r = 0; r < kB; ++r) {
-                float xr;
-                if (r < j) {
-                    xr = 0.0f;
-                } else if (r == j) {
-                    xr = 1.0f;
-                } else {
-                    float s = 0.0f;
-                    for (int k = j; k < r; ++k) s = fmaf(Lb[r * kP + k], xs[k * kB + j], s);
-                    xr = -s;
-                }
-                xs[r * kB + j] = xr;
-                const int gr = b * kB + r;
-                if (gr < C && gc < C) X[int64_t(gr) * C + gc] = xr;
+            const float *L = Xt + tri_index(b, b) * kTile;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = 0.0f;
+#pragma unroll
+                for (int k = 0; k < r; ++k) s = fmaf(L[r * 16 + k], x[k], s);   // x_k = 0 for k < j
+                x[r] = r < j ? 0.0f : (r == j ? 1.0f : -s);
             }
         }
-    }
-    // +0 above the diagonal blocks.
-    for (int64_t idx = tid; idx < int64_t(C) * C; idx += 256) {
-        const int r = int(idx / C), c = int(idx - int64_t(r) * C);
-        if (c / kB > r / kB) {
-            X[idx] = 0.0f;
-            QX[idx] = 0.0f;
+        __syncthreads();
+        if (b < nb) {
+            float *T = Xt + tri_index(b, b) * kTile;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) T[r * 16 + j] = x[r];
         }
     }
     __syncthreads();
 
-    float *T0 = lds, *T1 = lds + kB * kP, *T2 = lds + 2 * kB * kP;
-    // 2. blocks below the diagonal
-    for (int j = 0; j < nb; ++j) {
-        for (int i = j + 1; i < nb; ++i) {
-            float acc[4][4] = {};
-            for (int k = j; k < i; ++k) {
-                wy_load_tile(T0, A, beta, C, i * kB, k * kB);   // Lm_ik = beta_i A_ik (k < i: whole block)
-                wy_load_tile(T1, X, nullptr, C, k * kB, j * kB);
-                __syncthreads();
-                wy_mma(acc, T0, T1);
-                __syncthreads();
+    // 2. doubling: blocks of h tiles, pairs starting at tile row P0 = 2 h p.
+    for (int h = 1; h < nb; h <<= 1) {
+        const int npairs = (nb + 2 * h - 1) / (2 * h);
+        // items of the level: (pair, I, J) with I in [P0 + h, min(P0 + 2h, nb)), J in [P0, P0 + h)
+        const int per = h * h, items = npairs * per;
+        // 2a. T_IJ = sum_{K=J}^{P0+h-1} N_IK X_KJ -> slot (I, J)
+        for (int it = wave; it < items; it += NW) {
+            const int pr = it / per, q = it - pr * per, P0 = 2 * h * pr;
+            const int I = P0 + h + q / h, J = P0 + q % h;
+            if (I >= nb) continue;
+            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int K = J; K < P0 + h; ++K) {
+                float ao[4], bo[4];
+                wy_gop(A, beta, C, 16 * I, 16 * K, false, lane, ao);
+                wy_lop_b(Xt + tri_index(K, J) * kTile, lane, bo);
+                acc = mfma4(ao, bo, acc);
             }
-            wy_acc_to_tile(T2, acc);
-            wy_load_tile(T0, X, nullptr, C, i * kB, i * kB);
-            __syncthreads();
-            float acc2[4][4] = {};
-            wy_mma(acc2, T0, T2);
-            wy_store_tile(X, acc2, -1.0f, C, i * kB, j * kB);
-            __syncthreads();
+            wy_store_tile(Xt + tri_index(I, J) * kTile, acc, 1.0f, lane);
+        }
+        __syncthreads();
+        // 2b. X21_IJ = -sum_{K=P0+h}^{I} X_IK T_KJ (into registers, then over T)
+        f32x4 res[kMaxPer];
+#pragma unroll
+        for (int m = 0; m < kMaxPer; ++m) {
+            res[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int it = wave + m * NW;
+            if (it >= items) continue;
+            const int pr = it / per, q = it - pr * per, P0 = 2 * h * pr;
+            const int I = P0 + h + q / h, J = P0 + q % h;
+            if (I >= nb) continue;
+            for (int K = P0 + h; K <= I; ++K) {
+                float ao[4], bo[4];
+                wy_lop_a(Xt + tri_index(I, K) * kTile, lane, ao);
+                wy_lop_b(Xt + tri_index(K, J) * kTile, lane, bo);
+                res[m] = mfma4(ao, bo, res[m]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < kMaxPer; ++m) {
+            const int it = wave + m * NW;
+            if (it >= items) continue;
+            const int pr = it / per, q = it - pr * per, P0 = 2 * h * pr;
+            const int I = P0 + h + q / h, J = P0 + q % h;
+            if (I >= nb) continue;
+            wy_store_tile(Xt + tri_index(I, J) * kTile, res[m], -1.0f, lane);
+        }
+        __syncthreads();
+    }
+
+    // X out: lower tiles from LDS, +0 above the diagonal.
+    for (int64_t idx = tid; idx < int64_t(C) * C; idx += BLOCK) {
+        const int r = int(idx / C), c = int(idx - int64_t(r) * C);
+        X[idx] = c <= r ? Xt[tri_index(r >> 4, c >> 4) * kTile + (r & 15) * 16 + (c & 15)] : 0.0f;
+    }
+
+    // 3. QX_IJ = sum_{K=J}^{I} QK_IK X_KJ for I >= J; +0 above the diagonal.
+    const int ntiles = nb * (nb + 1) / 2;
+    for (int t = wave; t < ntiles; t += NW) {
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= t) ++I;
+        const int J = t - I * (I + 1) / 2;
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int K = J; K <= I; ++K) {
+            float ao[4], bo[4];
+            wy_gop(QK, nullptr, C, 16 * I, 16 * K, K == I, lane, ao);
+            wy_lop_b(Xt + tri_index(K, J) * kTile, lane, bo);
+            acc = mfma4(ao, bo, acc);
+        }
+        const int c = 16 * J + (lane & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * I + 4 * (lane >> 4) + v;
+            if (r < C && c < C) QX[int64_t(r) * C + c] = c <= r ? acc[v] : 0.0f;
         }
     }
-    // 3. QX on and below the diagonal
-    for (int j = 0; j < nb; ++j) {
-        for (int i = j; i < nb; ++i) {
-            float acc[4][4] = {};
-            for (int k = j; k <= i; ++k) {
-                wy_load_tile(T0, QK, nullptr, C, i * kB, k * kB, k == i);
-                wy_load_tile(T1, X, nullptr, C, k * kB, j * kB);
-                __syncthreads();
-                wy_mma(acc, T0, T1);
-                __syncthreads();
-            }
-            if (i == j) {
-                // QK_ii X_ii is lower triangular: keep +0 above the diagonal exactly.
-                const int rr = (tid >> 4) * 4, cc = (tid & 15) * 4;
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int y = 0; y < 4; ++y)
-                        if (cc + y > rr + x) acc[x][y] = 0.0f;
-            }
-            wy_store_tile(QX, acc, 1.0f, C, i * kB, j * kB);
-        }
+    for (int64_t idx = tid; idx < int64_t(C) * C; idx += BLOCK) {
+        const int r = int(idx / C), c = int(idx - int64_t(r) * C);
+        if ((c >> 4) > (r >> 4)) QX[idx] = 0.0f;
     }
 }
 
 size_t wy_lds_bytes(int C) {
-    const int nb = (C + kB - 1) / kB;
-    const size_t need = size_t(nb) * kB * (kP + kB) * sizeof(float);
-    const size_t tiles = size_t(3) * kB * kP * sizeof(float);
-    return need > tiles ? need : tiles;
+    const int nb = (C + 15) / 16;
+    return size_t(nb) * (nb + 1) / 2 * kTile * sizeof(float);
 }
 
 hipError_t wy_prepare() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&wy_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               int(wy_lds_bytes(kMaxChunk)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&wy_kernel<1024>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(wy_lds_bytes(kMaxChunk)));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&wy_kernel<256>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(wy_lds_bytes(64)));
 }
 
 hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
                      int64_t stride, int64_t bstride, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     WyArgs a{A, beta, QK, X, QX, C, stride, bstride};
-    hipLaunchKernelGGL(wy_kernel, dim3(unsigned(n)), dim3(256), wy_lds_bytes(C), st, a);
+    if (C <= 64)
+        hipLaunchKernelGGL(wy_kernel<256>, dim3(unsigned(n)), dim3(256), wy_lds_bytes(C), st, a);
+    else
+        hipLaunchKernelGGL(wy_kernel<1024>, dim3(unsigned(n)), dim3(1024), wy_lds_bytes(C), st, a);
     return hipGetLastError();
 }
 
