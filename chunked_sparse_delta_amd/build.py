@@ -5,6 +5,7 @@
 
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -26,18 +27,37 @@ def sources() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libsdm.so."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    noise = "is not a recognized feature for this target"
+
+    def compile_one(src: str) -> str:
+        obj = os.path.join(objdir, os.path.basename(src) + f".{os.getpid()}.o")
+        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({res.returncode}):\n{err}")
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+        return obj
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = list(ex.map(compile_one, srcs))
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc, *FLAGS, "-o", tmp, *sources()]
+    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    for o in objs:
+        os.remove(o)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, LIB)
     return LIB
 
