@@ -17,8 +17,8 @@
 //   p1_reads   for each read entry, the latest write of its slot at or before its token
 //              (bucketed binary search), its L and gather weight q exp(L)
 //   p1_gram_cold  the cold pair terms of A (strict lower) and QK (lower with diagonal) by
-//              row ownership: the thread of row i adds its entries' pair terms in a fixed
-//              order into an LDS window of columns
+//              row ownership: the wavefront of row i lists its entries' pair terms in a
+//              fixed order and replays them into the lanes that own their columns
 //   p1_gram_hot   the hot pair terms as dense products on the matrix cores
 // No float atomics anywhere: every element has one writer and a fixed summation order.
 #include "common.h"
@@ -468,13 +468,21 @@ __global__ __launch_bounds__(256) void p1_reads_kernel(Problem pb, Slab sl) {
 }
 
 // The cold part of A (blockIdx.y = 0: write entries) or QK (blockIdx.y = 1: read
-// entries). Thread i owns row i. Columns are covered in windows of WIN held in LDS (row
-// pitch WIN + 1); each window is written out whole, zeros included, so A and QK are fully
-// defined here (+0 outside their triangles) and the hot part is added afterwards. Row i
-// sums its pair terms in entry order, each entry's earlier group members in token order.
-template <int WIN>
-__global__ __launch_bounds__(256) void p1_gram_cold_kernel(Problem pb, Slab sl) {
-    extern __shared__ float lds[];
+// entries), one wavefront per row i. Lane l holds columns 4l .. 4l + 3 of the row. The
+// row's entries are taken 64 at a time (entry x = x0 + lane); each lane with earlier cold
+// members writes its pair terms (column, value) into the wavefront's LDS list at its
+// prefix-summed offset, and then every lane replays the list in order, adding the terms of
+// its own columns. The sum of each element therefore runs in entry order, each entry's
+// earlier group members in token order. Every row is written whole, zeros included, so A
+// and QK are fully defined here (+0 outside their triangles) and the hot part is added
+// afterwards.
+constexpr int kColdBlock = 512;
+constexpr int kTermCap = 512;   // terms per wavefront per round (>= 255 earlier members of one entry)
+
+__global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Slab sl) {
+    constexpr int NW = kColdBlock / kWave;
+    __shared__ int32_t tcol[NW][kTermCap];
+    __shared__ float tval[NW][kTermCap];
     const int C = pb.C;
     const int64_t n = blockIdx.x;
     const bool qk = blockIdx.y != 0;
@@ -486,42 +494,68 @@ __global__ __launch_bounds__(256) void p1_gram_cold_kernel(Problem pb, Slab sl) 
     const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
     const int4 *cr = reinterpret_cast<const int4 *>(cb + (qk ? L.off_rcr : L.off_ecr));
     float *Mout = reinterpret_cast<float *>(cb + (qk ? L.off_QK : L.off_A));
-    const int i = threadIdx.x;
-    float *row = lds + i * (WIN + 1);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t *mcol = tcol[wave];
+    float *mval = tval[wave];
 
-    for (int c0 = 0; c0 < C; c0 += WIN) {
-        const int cw = C - c0 < WIN ? C - c0 : WIN;
-        const int c1 = c0 + cw;
-        if (i < C) {
-            for (int j = 0; j < WIN; ++j) row[j] = 0.0f;
-            if (i < nl && c0 <= i) {
-                for (int x0 = 0; x0 < width; x0 += 8) {
-                    int4 rec[8];
+    for (int i = wave; i < C; i += NW) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int x0 = 0; i < nl && x0 < width; x0 += kWave) {
+            const int x = x0 + lane;
+            const int4 r = x < width ? cr[int64_t(x) * C + i] : make_int4(0, 0, 0, 0);
+            const int cnt = r.y > r.x ? r.y - r.x : 0;
+            // inclusive prefix of the counts over the lanes
+            int incl = cnt;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        rec[u] = x0 + u < width ? cr[int64_t(x0 + u) * C + i] : make_int4(0, 0, 0, 0);
+            for (int d = 1; d < kWave; d <<= 1) {
+                const int y = __shfl_up(incl, d, 64);
+                if (lane >= d) incl += y;
+            }
+            const int excl = incl - cnt, total = __shfl(incl, 63, 64);
+            const float kv = __int_as_float(r.z), Lv = __int_as_float(r.w);
+            for (int base = 0; base < total;) {
+                // this round: the lanes (in order) whose terms fit below base + kTermCap
+                const bool in = cnt > 0 && excl >= base && incl <= base + kTermCap;
+                int end = in ? incl : base;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int4 r = rec[u];
-                        if (r.y <= r.x) continue;
-                        const float kv = __int_as_float(r.z), Lv = __int_as_float(r.w);
-                        for (int32_t mm = r.x; mm < r.y; ++mm) {
-                            const int4 pk = spk[mm];
-                            const int32_t tj = pk.y;
-                            if (tj < c0) continue;
-                            if (tj >= c1) break;
-                            row[tj - c0] += (kv * __int_as_float(pk.z)) * expf(Lv - __int_as_float(pk.w));
+                for (int d = 32; d >= 1; d >>= 1) end = max(end, __shfl_xor(end, d, 64));
+                if (in) {
+                    for (int32_t j0 = 0; j0 < cnt; j0 += 4) {
+                        int4 pk[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) pk[u] = j0 + u < cnt ? spk[r.x + j0 + u] : make_int4(0, 0, 0, 0);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            if (j0 + u >= cnt) break;
+                            mcol[excl - base + j0 + u] = pk[u].y;
+                            mval[excl - base + j0 + u] = (kv * __int_as_float(pk[u].z)) * expf(Lv - __int_as_float(pk[u].w));
                         }
                     }
                 }
+                __builtin_amdgcn_wave_barrier();
+                for (int j = 0; j < end - base; ++j) {
+                    const int c = mcol[j];
+                    const float v = mval[j];
+                    if ((c >> 2) == lane) {
+                        const int q = c & 3;
+                        if (q == 0) acc[0] += v;
+                        else if (q == 1) acc[1] += v;
+                        else if (q == 2) acc[2] += v;
+                        else acc[3] += v;
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+                base = end;
             }
         }
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < C * cw; idx += blockDim.x) {
-            const int r = idx / cw, c = idx - r * cw;
-            Mout[int64_t(r) * C + c0 + c] = lds[r * (WIN + 1) + c];
+        const int c0 = 4 * lane;
+        if (c0 + 3 < C && (C & 3) == 0) {
+            *reinterpret_cast<float4 *>(Mout + int64_t(i) * C + c0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c0 + q < C) Mout[int64_t(i) * C + c0 + q] = acc[q];
         }
-        __syncthreads();
     }
 }
 
@@ -644,19 +678,11 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
 constexpr int kSortBlock = 1024;
 constexpr int kGroupBlock = 1024;
 
-static int gram_win(int C) { return C > 128 ? 128 : (C > 64 ? 128 : 64); }
-
-size_t gram_lds_bytes(int C) { return size_t(C) * (gram_win(C) + 1) * sizeof(float); }
+size_t gram_lds_bytes(int) { return 0; }   // the cold Gram uses static LDS only
 
 static size_t hot_lds_bytes(int C) { return size_t(3) * ((C + 15) / 16 * 16) * kHP * sizeof(float); }
 
 hipError_t phase1_prepare() {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_cold_kernel<64>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(gram_lds_bytes(64)));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_cold_kernel<128>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(gram_lds_bytes(kMaxChunk)));
-    if (e != hipSuccess) return e;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_hot_kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(hot_lds_bytes(kMaxChunk)));
 }
@@ -673,11 +699,7 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
     const unsigned fx = unsigned((sl.lay.F + 255) / 256);
     hipLaunchKernelGGL(p1_reads_kernel, dim3(fx, nch), dim3(256), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
-    const int gb = (pb.C + 63) / 64 * 64;
-    if (gram_win(pb.C) == 64)
-        hipLaunchKernelGGL(p1_gram_cold_kernel<64>, dim3(nch, 2), dim3(gb), gram_lds_bytes(pb.C), st, pb, sl);
-    else
-        hipLaunchKernelGGL(p1_gram_cold_kernel<128>, dim3(nch, 2), dim3(gb), gram_lds_bytes(pb.C), st, pb, sl);
+    hipLaunchKernelGGL(p1_gram_cold_kernel, dim3(nch, 2), dim3(kColdBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch), dim3(kHotBlock), hot_lds_bytes(pb.C), st, pb, sl);
     return hipGetLastError();

@@ -11,11 +11,12 @@ import workloads
 TOL = {"f32": 1e-4, "bf16": 2e-2}   # infinity-norm relative error per output tensor, vs O1
 # bf16 banks are also compared with O1b, the token loop under the bfloat16 storage
 # contract (rows rounded once per chunk, readings rounded). The GPU must stay within
-# max(TOL, SLACK x |O1b - O1|) of O1 and within max(TOL_CONTRACT, SLACK x |O1b - O1|) of
-# O1b: the contract itself can exceed TOL on a bank that grows by many orders of
-# magnitude, and there one-ulp bf16 rounding differences between two correct evaluations
-# of the same contract (fp32 chunked on the GPU, fp64 token loop in O1b) compound to the
-# size of the contract's own error.
+# bar = max(TOL, SLACK x |O1b - O1|) of O1: the contract itself can exceed TOL on a bank
+# that grows by many orders of magnitude. Against O1b: within TOL_CONTRACT where the
+# contract meets TOL (SLACK x |O1b - O1| <= TOL); where it does not, one-ulp bf16 rounding
+# differences between two correct evaluations of the contract (fp32 chunked on the GPU,
+# fp64 token loop in O1b) compound to the contract's own error, and the bound is the
+# triangle inequality through the exact result, bar + |O1b - O1|.
 TOL_CONTRACT = 2e-2
 SLACK = 1.25
 
@@ -87,7 +88,7 @@ def check(out, bank, ref, con, dtype: str, what: str = ""):
             e_c, e_m = rel_err(g, c), rel_err(c, r)
             bar = max(tol, SLACK * e_m)
             line += f", vs O1b {e_c:.3e} (O1b vs O1 {e_m:.3e})"
-            checks.append((e_c, max(TOL_CONTRACT, SLACK * e_m), name + " vs O1b"))
+            checks.append((e_c, TOL_CONTRACT if SLACK * e_m <= tol else bar + e_m, name + " vs O1b"))
         checks.append((e, bar, name + " vs O1"))
         msg.append(line)
     print(f"{what}: " + "; ".join(msg) + f" (tol {tol})", flush=True)
