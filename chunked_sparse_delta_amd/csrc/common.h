@@ -12,6 +12,7 @@ constexpr int kMaxWidth = 256;
 constexpr int kXcds = 8;           // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 constexpr int kHotMin = 16;        // write groups of at least this many members go to the dense Gram
 constexpr float kHotSpan = 60.0f;  // ... if their log-decays stay within this of the first member's
+constexpr int kHotCap = 256;       // at most this many hot groups per chunk (the rest stay cold)
 
 // ---------------------------------------------------------------------------------------
 // Element types. bf16 is carried as its 16-bit pattern.
@@ -135,7 +136,7 @@ __device__ __forceinline__ float load_weight(const void *base, int64_t i, int32_
 // threads owning consecutive tokens read consecutive records.
 // ---------------------------------------------------------------------------------------
 struct ChunkLayout {
-    int64_t E, F, C2, NB, HMAX;
+    int64_t E, F, C2, NB, HMAX, HCAP;
     // per-chunk strides (elements)
     int64_t off_key0, off_val0, off_key1, off_val1;   // radix-sort double buffer (u32)
     int64_t off_spk;      // [E] int4 per sorted position: {slot, token, bits k, bits L}
@@ -149,16 +150,16 @@ struct ChunkLayout {
     int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
     int64_t off_ecr;      // [E] int4 transposed: cold write entry {a, m, bits k, bits L} (a == m: none)
     int64_t off_ghot;     // [E] i32: hot index of group, or -1
-    int64_t off_ska;      // [E] f32 per sorted position of a hot group: k exp(L - L_ref)
-    int64_t off_skb;      // [E] f32 per sorted position of a hot group: k exp(L_ref - L)
     int64_t off_hgrp;     // [HMAX] i32: group of hot index
     int64_t off_brec;     // [HMAX] int4: DW group records of the groups with >= kHotMin members
     int64_t off_bstart;   // [NB+1] i32: first sorted position of each slot bucket
     int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
     int64_t off_rcr;      // [F] int4 transposed: cold read {a, end, bits q, bits Lr} (a == end: none)
-    int64_t off_rhot;     // [F] i32 transposed: hot index of the read slot's group, or -1
-    int64_t off_rval;     // [F] f32 transposed: q exp(Lr - L_ref) of a hot read
-    int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups, groups with >= kHotMin members
+    int64_t off_ka;       // [C][HP] f32, HP = meta[5] (<= HCAP): token t's write of hot group h, k exp(L - L_ref)
+    int64_t off_kb;       // [C][HP] f32: the same write's k exp(L_ref - L)
+    int64_t off_qa;       // [C][HP] f32: token t's reads of hot group h, sum of q exp(Lr - L_ref) in read order
+    int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups, groups with >= kHotMin members,
+                          //   HP (hot groups rounded up to 16)
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
     int64_t words;        // 4-byte words per chunk
@@ -181,6 +182,7 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.C2 = int64_t(C) * C;
     L.NB = int64_t(1) << bucket_bits(L.E);
     L.HMAX = L.E / kHotMin + 1;
+    L.HCAP = ((L.HMAX + 15) / 16) * 16 < kHotCap ? ((L.HMAX + 15) / 16) * 16 : kHotCap;
     int64_t o = 0;
     auto take = [&](int64_t n) { int64_t r = o; o += align_words(n); return r; };
     L.off_key0 = take(L.E);
@@ -196,15 +198,14 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_gw = take(L.E);
     L.off_ecr = take(4 * L.E);
     L.off_ghot = take(L.E);
-    L.off_ska = take(L.E);
-    L.off_skb = take(L.E);
     L.off_hgrp = take(L.HMAX);
     L.off_brec = take(4 * L.HMAX);
     L.off_bstart = take(L.NB + 1);
     L.off_gr = take(L.F);
     L.off_rcr = take(4 * L.F);
-    L.off_rhot = take(L.F);
-    L.off_rval = take(L.F);
+    L.off_ka = take(int64_t(C) * L.HCAP);
+    L.off_kb = take(int64_t(C) * L.HCAP);
+    L.off_qa = take(int64_t(C) * L.HCAP);
     L.off_meta = take(8);
     L.off_beta = take(C);
     L.off_A = take(L.C2);

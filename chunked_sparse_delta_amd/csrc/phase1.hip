@@ -267,8 +267,8 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
     float *gw = reinterpret_cast<float *>(cb + L.off_gw);
     int4 *ecr = reinterpret_cast<int4 *>(cb + L.off_ecr);
     int32_t *ghot = reinterpret_cast<int32_t *>(cb + L.off_ghot);
-    float *ska = reinterpret_cast<float *>(cb + L.off_ska);
-    float *skb = reinterpret_cast<float *>(cb + L.off_skb);
+    float *Ka = reinterpret_cast<float *>(cb + L.off_ka);
+    float *Kb = reinterpret_cast<float *>(cb + L.off_kb);
     int32_t *hgrp = reinterpret_cast<int32_t *>(cb + L.off_hgrp);
     int4 *brec = reinterpret_cast<int4 *>(cb + L.off_brec);
     int32_t *bstart = reinterpret_cast<int32_t *>(cb + L.off_bstart);
@@ -376,28 +376,37 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
         const int32_t c = t0 + tid;
         const bool h = c < nc && cand_hot[c];
         const int32_t r = tile_compact<NW>(h, wsum, &nhot);
-        if (h) {
+        if (h && r < L.HCAP) {   // past the cap a group stays cold
             ghot[cand[c]] = r;
             hgrp[r] = cand[c];
         }
     }
     __syncthreads();
+    const int32_t nh = min(nhot, int32_t(L.HCAP)), HP = (nh + 15) & ~15;
     if (tid == 0) {
-        meta[3] = nhot;
+        meta[3] = nh;
         meta[4] = nc;
+        meta[5] = HP;
     }
+    for (int32_t x = tid; x < C * HP; x += BLOCK) {
+        Ka[x] = 0.0f;
+        Kb[x] = 0.0f;
+    }
+    __syncthreads();
 
-    // Pass 4, per sorted position: factored decays of hot members; the cold pair ranges
-    // (earlier members of the group) by token-major transposed entry.
+    // Pass 4, per sorted position: factored decays of hot members into the dense
+    // operands; the cold pair ranges (earlier members of the group) by token-major
+    // transposed entry.
     for (int32_t m = tid; m < El; m += BLOCK) {
         const int4 pk = spk[m];
         const int32_t g = sgrp[m], a = shead[m];
         const int32_t e = int32_t(sval[m]), w = e - pk.y * W;
         int4 rec = make_int4(m, m, 0, 0);
-        if (ghot[g] >= 0) {
+        const int32_t h = ghot[g];
+        if (h >= 0) {
             const float d = __int_as_float(pk.w) - __int_as_float(spk[a].w), kv = __int_as_float(pk.z);
-            ska[m] = kv * expf(d);
-            skb[m] = kv * expf(-d);
+            Ka[pk.y * HP + h] = kv * expf(d);
+            Kb[pk.y * HP + h] = kv * expf(-d);
         } else {
             rec = make_int4(a, m, pk.z, pk.w);
         }
@@ -405,66 +414,84 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
     }
 }
 
-// One thread per read entry. The latest write of the read slot at or before the read's
-// token is the last sorted position with (slot, token) <= (q, i), searched inside the
-// slot's bucket.
-__global__ __launch_bounds__(256) void p1_reads_kernel(Problem pb, Slab sl) {
+// One wavefront per token i of the chunk, lanes over its reads r. The latest write of the
+// read slot at or before the read's token is the last sorted position with
+// (slot, token) <= (q, i), searched inside the slot's bucket. Reads of hot groups add
+// q exp(Lr - L_ref) into the token's row of the dense operand Qa in read order (one lane
+// at a time, lanes ascending), so duplicate reads of a slot sum in a fixed order.
+constexpr int kReadWaves = 4;
+
+__global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb, Slab sl) {
+    __shared__ float qrow[kReadWaves][kHotCap];
     const int64_t n = blockIdx.y;
-    const int64_t er = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = blockIdx.x * kReadWaves + wave;
     const ChunkLayout &L = sl.lay;
-    if (er >= L.F) return;
+    const int R = pb.R, C = pb.C;
+    if (i >= C) return;   // whole wavefronts; no workgroup barrier below
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
-    const int R = pb.R, C = pb.C;
     uint32_t *cb = sl.chunk(n);
     const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
     const int32_t *shead = reinterpret_cast<const int32_t *>(cb + L.off_shead);
     const int32_t *sgrp = reinterpret_cast<const int32_t *>(cb + L.off_sgrp);
     const int32_t *ghot = reinterpret_cast<const int32_t *>(cb + L.off_ghot);
     const int32_t *bstart = reinterpret_cast<const int32_t *>(cb + L.off_bstart);
+    const int32_t *meta = reinterpret_cast<const int32_t *>(cb + L.off_meta);
     float *gr = reinterpret_cast<float *>(cb + L.off_gr);
     int4 *rcr = reinterpret_cast<int4 *>(cb + L.off_rcr);
-    int32_t *rhot = reinterpret_cast<int32_t *>(cb + L.off_rhot);
-    float *rval = reinterpret_cast<float *>(cb + L.off_rval);
-    const int32_t i = int32_t(er / R), r = int32_t(er - int64_t(i) * R);
-    const int64_t tr = int64_t(r) * C + i;
-    if (i >= nl) {
-        gr[er] = 0.0f;
-        rcr[tr] = make_int4(0, 0, 0, 0);
-        rhot[tr] = -1;
-        rval[tr] = 0.0f;
-        return;
-    }
+    float *Qa = reinterpret_cast<float *>(cb + L.off_qa);
+    const int HP = meta[5];
+    float *qr = qrow[wave];
+    for (int h = lane; h < HP; h += kWave) qr[h] = 0.0f;
+    __builtin_amdgcn_wave_barrier();
     const int64_t tg = int64_t(p) * pb.T + int64_t(ti) * C + i;
-    const int32_t q = pb.q_idx[tg * R + r];
-    const int32_t b = min(int32_t(uint32_t(q) >> bucket_shift(pb, L.E)), int32_t(L.NB) - 1);
-    const int32_t b0 = bstart[b];
-    int32_t lo = b0, hi = bstart[b + 1];
-    while (lo < hi) {
-        const int32_t mid = (lo + hi) >> 1;
-        const int4 pk = spk[mid];
-        if (pk.x < q || (pk.x == q && pk.y <= i)) lo = mid + 1;
-        else hi = mid;
-    }
-    const int32_t pos = lo - 1;
-    const float qv = load_weight(pb.q_val, tg * R + r, pb.dtype);
-    float l = 0.0f, rv = 0.0f;
-    int32_t h = -1;
-    int4 cr = make_int4(0, 0, 0, 0);
-    if (pos >= b0) {
-        const int4 pk = spk[pos];
-        if (pk.x == q) {
-            l = __int_as_float(pk.w);
-            const int32_t a = shead[pos];
-            h = ghot[sgrp[pos]];
-            if (h >= 0) rv = qv * expf(l - __int_as_float(spk[a].w));
-            else cr = make_int4(a, pos + 1, __float_as_int(qv), pk.w);
+    const int bsh = bucket_shift(pb, L.E);
+    for (int r0 = 0; r0 < R; r0 += kWave) {
+        const int r = r0 + lane;
+        const bool ok = r < R;
+        float g = 0.0f, rv = 0.0f;
+        int32_t h = -1;
+        int4 cr = make_int4(0, 0, 0, 0);
+        if (ok && i < nl) {
+            const int32_t q = pb.q_idx[tg * R + r];
+            const int32_t b = min(int32_t(uint32_t(q) >> bsh), int32_t(L.NB) - 1);
+            const int32_t b0 = bstart[b];
+            int32_t lo = b0, hi = bstart[b + 1];
+            while (lo < hi) {
+                const int32_t mid = (lo + hi) >> 1;
+                const int4 pk = spk[mid];
+                if (pk.x < q || (pk.x == q && pk.y <= i)) lo = mid + 1;
+                else hi = mid;
+            }
+            const int32_t pos = lo - 1;
+            const float qv = load_weight(pb.q_val, tg * R + r, pb.dtype);
+            float l = 0.0f;
+            if (pos >= b0) {
+                const int4 pk = spk[pos];
+                if (pk.x == q) {
+                    l = __int_as_float(pk.w);
+                    const int32_t a = shead[pos];
+                    h = ghot[sgrp[pos]];
+                    if (h >= 0) rv = qv * expf(l - __int_as_float(spk[a].w));
+                    else cr = make_int4(a, pos + 1, __float_as_int(qv), pk.w);
+                }
+            }
+            g = qv * expf(l);
+        }
+        if (ok) {
+            gr[int64_t(i) * R + r] = g;
+            rcr[int64_t(r) * C + i] = cr;
+        }
+        // hot reads into the row, lanes ascending
+        for (uint64_t m = __ballot(h >= 0); m; m &= m - 1) {
+            const int src = __ffsll(static_cast<unsigned long long>(m)) - 1;
+            if (lane == src) qr[h] += rv;
+            __builtin_amdgcn_wave_barrier();
         }
     }
-    gr[er] = qv * expf(l);
-    rcr[tr] = cr;
-    rhot[tr] = h;
-    rval[tr] = rv;
+    __builtin_amdgcn_wave_barrier();
+    for (int h = lane; h < HP; h += kWave) Qa[int64_t(i) * HP + h] = qr[h];
 }
 
 // The cold part of A (blockIdx.y = 0: write entries) or QK (blockIdx.y = 1: read
@@ -559,25 +586,21 @@ __global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Sl
     }
 }
 
-// The hot part of A and QK on the matrix cores. For hot write group h with reference
+// The hot part of A and QK on the matrix cores, from the dense operands of Phase 1
+// ([C][HP] in the workspace, HP a multiple of 16): for hot write group h with reference
 // log-decay L_ref (its first member's), token t writing it carries Ka[t][h] = k e^(L-L_ref)
-// and Kb[t][h] = k e^(L_ref-L); a token reading it after a write carries
-// Qa[t][h] = q e^(Lr-L_ref) (summed over its reads of the slot). Then A += tril(Ka Kb^T, -1)
-// and QK += tril(Qa Kb^T), the factored exponents multiplying back to the pair decays
-// e^(L_t - L_t'). One workgroup per chunk; the hot groups are taken HS at a time into LDS
-// (Ka, Kb from the groups' member ranges, Qa from each token's reads in read order);
-// every wave owns a fixed set of 16 x 16 lower output tiles and accumulates them with
-// v_mfma_f32_16x16x4_f32 over the hot groups in ascending order (a fixed order), then
-// adds them to the cold part in memory.
-constexpr int kHS = 32;            // hot groups per LDS slice
-constexpr int kHP = kHS + 1;       // LDS row pitch
-constexpr int kHotBlock = 512;
-constexpr int kHotMaxTiles = 34;   // per wave: 2 * 136 lower 16x16 tiles of C = 256 over 8 waves
+// and Kb[t][h] = k e^(L_ref-L); a token reading it after a write carries Qa[t][h] =
+// q e^(Lr-L_ref) (summed over its reads of the slot). Then A += tril(Ka Kb^T, -1) and
+// QK += tril(Qa Kb^T): the factored exponents multiply back to the pair decays
+// e^(L_t - L_t'). Each wavefront takes lower 16 x 16 tiles of A and QK in turn and
+// accumulates them with v_mfma_f32_16x16x4_f32 over h in blocks of 16 ascending (a fixed
+// order), operands read straight from memory, then adds them to the cold part.
+constexpr int kHotBlock = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab sl) {
-    extern __shared__ float lds[];
+    constexpr int NWAVE = kHotBlock / kWave;
     const int64_t n = blockIdx.x;
     const ChunkLayout &L = sl.lay;
     uint32_t *cb = sl.chunk(n);
@@ -585,89 +608,41 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     if (nl == 0) return;
-    const int nhot = meta[3];
+    const int nhot = meta[3], HP = meta[5];
     if (nhot == 0) return;
-    const int C = pb.C, R = pb.R;
-    const int nt = (C + 15) / 16, rows = nt * 16;
-    const int T1 = nt * (nt + 1) / 2, T2 = 2 * T1;
-    float *Ka = lds, *Kb = lds + rows * kHP, *Qa = lds + 2 * rows * kHP;
-    const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
-    const int32_t *gpos = reinterpret_cast<const int32_t *>(cb + L.off_gpos);
-    const int32_t *hgrp = reinterpret_cast<const int32_t *>(cb + L.off_hgrp);
-    const float *ska = reinterpret_cast<const float *>(cb + L.off_ska);
-    const float *skb = reinterpret_cast<const float *>(cb + L.off_skb);
-    const int32_t *rhot = reinterpret_cast<const int32_t *>(cb + L.off_rhot);
-    const float *rval = reinterpret_cast<const float *>(cb + L.off_rval);
+    const int C = pb.C;
+    const int nt = (C + 15) / 16, T1 = nt * (nt + 1) / 2;
+    const float *Ka = reinterpret_cast<const float *>(cb + L.off_ka);
+    const float *Kb = reinterpret_cast<const float *>(cb + L.off_kb);
+    const float *Qa = reinterpret_cast<const float *>(cb + L.off_qa);
     float *A = reinterpret_cast<float *>(cb + L.off_A);
     float *QK = reinterpret_cast<float *>(cb + L.off_QK);
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    constexpr int NWAVE = kHotBlock / kWave;
-
-    // This wave's tiles: t = wv + NWAVE q; t < T1 is A tile t, else QK tile t - T1;
-    // lower tile index tt maps to (I, J), J <= I, row-major over the lower triangle
-    // (tile_ij[tt] = 16 I + J, rows and columns in units of 16).
-    __shared__ int32_t tile_ij[136];
-    for (int tt = tid; tt < T1; tt += kHotBlock) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ko = 4 * (lane >> 4);
+    for (int t = blockIdx.y * NWAVE + wave; t < 2 * T1; t += gridDim.y * NWAVE) {
+        const bool isA = t < T1;
+        const int tt = isA ? t : t - T1;
         int I = 0;
         while ((I + 1) * (I + 2) / 2 <= tt) ++I;
-        tile_ij[tt] = 16 * I + (tt - I * (I + 1) / 2);
-    }
-    f32x4 acc[kHotMaxTiles];
-#pragma unroll
-    for (int q = 0; q < kHotMaxTiles; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    for (int h0 = 0; h0 < nhot; h0 += kHS) {
-        for (int idx = tid; idx < 3 * rows * kHP; idx += kHotBlock) lds[idx] = 0.0f;
-        __syncthreads();
-        // Ka, Kb: a wave per hot group of the slice, lanes over its members.
-        for (int hh = wv; hh < kHS; hh += NWAVE) {
-            const int h = h0 + hh;
-            if (h >= nhot) break;
-            const int32_t g = hgrp[h], a = gpos[g], b = gpos[g + 1];
-            for (int32_t m = a + lane; m < b; m += kWave) {
-                const int t = spk[m].y;
-                Ka[t * kHP + hh] = ska[m];
-                Kb[t * kHP + hh] = skb[m];
-            }
+        const int J = tt - I * (I + 1) / 2;
+        const float *Aop = isA ? Ka : Qa;
+        const int ra = 16 * I + (lane & 15), rb = 16 * J + (lane & 15);
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int hb = 0; hb < HP; hb += 16) {
+            float4 av = make_float4(0.0f, 0.0f, 0.0f, 0.0f), bv = av;
+            if (ra < C) av = *reinterpret_cast<const float4 *>(Aop + int64_t(ra) * HP + hb + ko);
+            if (rb < C) bv = *reinterpret_cast<const float4 *>(Kb + int64_t(rb) * HP + hb + ko);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
         }
-        // Qa: the thread of token t adds its hot reads of the slice in read order.
-        if (tid < nl) {
-            for (int r = 0; r < R; ++r) {
-                const int64_t x = int64_t(r) * C + tid;
-                const int h = rhot[x] - h0;
-                if (h >= 0 && h < kHS) Qa[tid * kHP + h] += rval[x];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k0 = 0; k0 < kHS; k0 += 4) {
-            const int kk = k0 + (lane >> 4), rr = lane & 15;
-#pragma unroll
-            for (int q = 0; q < kHotMaxTiles; ++q) {
-                const int t = wv + NWAVE * q;
-                if (t < T2) {
-                    const float *Aop = t < T1 ? Ka : Qa;
-                    const int ij = tile_ij[t < T1 ? t : t - T1];
-                    const float av = Aop[((ij >> 4) * 16 + rr) * kHP + kk];
-                    const float bv = Kb[((ij & 15) * 16 + rr) * kHP + kk];
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[q], 0, 0, 0);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    // Add the hot part to the cold part, inside the triangles only.
-#pragma unroll
-    for (int q = 0; q < kHotMaxTiles; ++q) {
-        const int t = wv + NWAVE * q;
-        if (t >= T2) continue;
-        float *M = t < T1 ? A : QK;
-        const bool strict = t < T1;
-        const int ij = tile_ij[t < T1 ? t : t - T1];
+        // Add the hot part to the cold part, inside the triangles only.
+        float *M = isA ? A : QK;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int r = (ij >> 4) * 16 + 4 * (lane >> 4) + v, c = (ij & 15) * 16 + (lane & 15);
-            if (r < C && c < C && (strict ? c < r : c <= r)) M[int64_t(r) * C + c] += acc[q][v];
+            const int r = 16 * I + 4 * (lane >> 4) + v, c = 16 * J + (lane & 15);
+            if (r < C && c < C && (isA ? c < r : c <= r)) M[int64_t(r) * C + c] += acc[v];
         }
     }
 }
@@ -680,12 +655,8 @@ constexpr int kGroupBlock = 1024;
 
 size_t gram_lds_bytes(int) { return 0; }   // the cold Gram uses static LDS only
 
-static size_t hot_lds_bytes(int C) { return size_t(3) * ((C + 15) / 16 * 16) * kHP * sizeof(float); }
 
-hipError_t phase1_prepare() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_hot_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, int(hot_lds_bytes(kMaxChunk)));
-}
+hipError_t phase1_prepare() { return hipSuccess; }
 
 // ev: nullptr, or 5 events recorded before each of the five kernels.
 hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev) {
@@ -696,12 +667,15 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_groups_kernel<kGroupBlock>, dim3(nch), dim3(kGroupBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-    const unsigned fx = unsigned((sl.lay.F + 255) / 256);
-    hipLaunchKernelGGL(p1_reads_kernel, dim3(fx, nch), dim3(256), 0, st, pb, sl);
+    hipLaunchKernelGGL(p1_reads_kernel, dim3(unsigned((pb.C + kReadWaves - 1) / kReadWaves), nch),
+                       dim3(kReadWaves * kWave), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_gram_cold_kernel, dim3(nch, 2), dim3(kColdBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch), dim3(kHotBlock), hot_lds_bytes(pb.C), st, pb, sl);
+    // tiles of A and QK split over enough workgroups per chunk to fill the device
+    const int nt = (pb.C + 15) / 16, tiles = nt * (nt + 1);
+    const unsigned gy = unsigned(min(8, max(1, tiles / (2 * (kHotBlock / kWave)))));
+    hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch, gy), dim3(kHotBlock), 0, st, pb, sl);
     return hipGetLastError();
 }
 
