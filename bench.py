@@ -1,6 +1,7 @@
 """Benchmark of the SDM forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu-baseline]
+    python bench.py --copy-calibration      # plain 1 GiB device copy, for scaling HBM counters
 
 A step is one sdm_fwd call over the whole workload (every chunk step of every stream)
 with all inputs resident in HBM. The bank is advanced in place from step to step, as a
@@ -8,12 +9,18 @@ caller carrying the memory across calls would; the kernels are data-oblivious, s
 timing equals that of a restored bank. Prints one JSON line: tokens/s, the per-kernel
 breakdown from HIP events recorded by the library on its stream, the roofline of the
 dominant kernel, and the CPU oracle's throughput on the host as a reference.
+
+The roofline's `traffic` (HBM bytes per Phase-2 launch) comes from the committed counter
+summary profiles/traffic_<workload>.md (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by the
+same counters' reading for a plain copy) and is reported only while the Phase-2 sources
+hash to the value recorded there; otherwise it is null.
 """
 
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import re
@@ -40,7 +47,46 @@ def parse():
     ap.add_argument("--workload", default="1", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (3 launches)")
     return ap.parse_args()
+
+
+PHASE2_SOURCES = ("chunked_sparse_delta_amd/csrc/phase2.hip", "chunked_sparse_delta_amd/csrc/common.h")
+
+
+def phase2_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in PHASE2_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per Phase-2 launch from profiles/traffic_<workload>.md, if it was taken
+    on the current Phase-2 sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", open(path).read(), flags=re.M))
+    if fields.get("phase2_source_sha256") != phase2_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28   # 1 GiB of float32
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": 4 * n, "copy_bytes_written_per_launch": 4 * n}), flush=True)
 
 
 def chunk_stats(inp: dict, wl) -> dict:
@@ -112,6 +158,9 @@ def cpu_baseline(inp: dict, wl, seconds: float) -> dict:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on exactly one GPU (the forward shards with no exchange across "
               "streams or columns, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
@@ -179,7 +228,7 @@ def main():
     if dom == "phase2":
         achieved = p2_bytes / (kern_ms["phase2"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "phase2", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
                 "bytes_per_launch": int(p2_bytes)}
     else:
         roof = {"bound": "alu", "kernel": dom, "achieved": None, "peak": None, "unit": None, "frac": None,
