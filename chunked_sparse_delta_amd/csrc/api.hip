@@ -22,7 +22,8 @@ hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *
                      int64_t stride, int64_t bstride, hipStream_t st);
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st);
 size_t gram_lds_bytes(int C);
-size_t phase2_lds_bytes(int C, int nv, int V);
+size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, bool staged);
+bool phase2_staged(const ChunkLayout &L, int C, int nv, int V, int es, int lds_limit);
 }  // namespace sdm
 
 using namespace sdm;
@@ -161,28 +162,29 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
 // Phase-2 geometry from shapes only (the bits never depend on it): slices of NV vectors,
 // NV the largest power of two with NV * V * es <= 128 bytes (one cache line of a row),
 // halved while that leaves fewer than one workgroup per CU; one workgroup per
-// (stream, slice) of 1024 threads. SDM_P2_GEOM="nv[,block]" overrides NV (1, 2, 4 or 8)
-// and the block size (512 or 1024), for tuning sweeps.
-P2Geom plan_phase2(const Problem &pb, int V, int es, int cus) {
+// (stream, slice); the chunk's Phase-2 block staged in LDS when it fits.
+// SDM_P2_GEOM="nv[,staged]" overrides NV (1, 2, 4 or 8) and staging (0 or 1, where it
+// fits), for tuning sweeps.
+P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int cus, int lds_limit) {
     const int hv = pb.hd / V;
     P2Geom g{};
     g.nv = 8;
-    g.block = 1024;
     while (g.nv > 1 && (g.nv * V * es > 128 || g.nv > hv)) g.nv >>= 1;
     const char *env = getenv("SDM_P2_GEOM");
-    int enk = 0, eb = 0;
-    const int got = env ? sscanf(env, "%d,%d", &enk, &eb) : 0;
+    int enk = 0, est = -1;
+    const int got = env ? sscanf(env, "%d,%d", &enk, &est) : 0;
     if (got >= 1 && (enk == 1 || enk == 2 || enk == 4 || enk == 8)) {
         g.nv = enk;
-        if (got == 2 && (eb == 512 || eb == 1024)) g.block = eb;
+    } else {
         g.S = (hv + g.nv - 1) / g.nv;
-        return g;
+        while (g.nv > 1 && int64_t(pb.P) * g.S < cus) {
+            g.nv >>= 1;
+            g.S = (hv + g.nv - 1) / g.nv;
+        }
     }
     g.S = (hv + g.nv - 1) / g.nv;
-    while (g.nv > 1 && int64_t(pb.P) * g.S < cus) {
-        g.nv >>= 1;
-        g.S = (hv + g.nv - 1) / g.nv;
-    }
+    g.staged = phase2_staged(L, pb.C, g.nv, V, es, lds_limit);
+    if (got == 2 && est == 0) g.staged = false;
     return g;
 }
 
@@ -234,10 +236,11 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
     if (gram_lds_bytes(C) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
                     gram_lds_bytes(C), dev->lds_per_block);
-    const P2Geom geom = plan_phase2(ck.pb, ck.V, ck.es, dev->cus);
-    if (phase2_lds_bytes(C, geom.nv, ck.V) + 256 > size_t(dev->lds_per_block))
+    const P2Geom geom = plan_phase2(ck.pb, ck.lay, ck.V, ck.es, dev->cus, dev->lds_per_block);
+    const size_t p2lds = phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.staged);
+    if (p2lds + 256 > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup in phase 2, the device has %d", C,
-                    phase2_lds_bytes(C, geom.nv, ck.V), dev->lds_per_block);
+                    p2lds, dev->lds_per_block);
     const int32_t Nt = ck.pb.Nt;
     int64_t slab64 = int64_t(exec->workspace_bytes / per_step);
     int32_t slab = slab64 > Nt ? Nt : int32_t(slab64);

@@ -148,12 +148,14 @@ struct ChunkLayout {
                           //   k exp(L_last - L)}
     int64_t off_mrec;     // [E] int2: DW member record {token, bits of k exp(L_last - L)}
     int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
+    int64_t off_kid;      // [E] i32: write slot ids of the chunk, entry order (copy of the input)
     int64_t off_ecr;      // [E] int4 transposed: cold write entry {a, m, bits k, bits L} (a == m: none)
     int64_t off_ghot;     // [E] i32: hot index of group, or -1
     int64_t off_hgrp;     // [HMAX] i32: group of hot index
     int64_t off_brec;     // [HMAX] int4: DW group records of the groups with >= kHotMin members
     int64_t off_bstart;   // [NB+1] i32: first sorted position of each slot bucket
     int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
+    int64_t off_qid;      // [F] i32: read slot ids of the chunk, entry order (copy of the input)
     int64_t off_rcr;      // [F] int4 transposed: cold read {a, end, bits q, bits Lr} (a == end: none)
     int64_t off_ka;       // [C][HP] f32, HP = meta[5] (<= HCAP): token t's write of hot group h, k exp(L - L_ref)
     int64_t off_kb;       // [C][HP] f32: the same write's k exp(L_ref - L)
@@ -162,6 +164,9 @@ struct ChunkLayout {
                           //   HP (hot groups rounded up to 16)
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
+    // [stage0, stage1): every array Phase 2 reads (records, weights, ids, meta, beta, X, QX),
+    // contiguous, so that small chunks can be copied into LDS whole
+    int64_t off_stage0, off_stage1;
     int64_t words;        // 4-byte words per chunk
 };
 
@@ -193,32 +198,38 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_shead = take(L.E);
     L.off_sgrp = take(L.E);
     L.off_gpos = take(L.E + 1);
-    L.off_grec = take(4 * L.E);
-    L.off_mrec = take(2 * L.E);
-    L.off_gw = take(L.E);
     L.off_ecr = take(4 * L.E);
     L.off_ghot = take(L.E);
     L.off_hgrp = take(L.HMAX);
-    L.off_brec = take(4 * L.HMAX);
     L.off_bstart = take(L.NB + 1);
-    L.off_gr = take(L.F);
     L.off_rcr = take(4 * L.F);
     L.off_ka = take(int64_t(C) * L.HCAP);
     L.off_kb = take(int64_t(C) * L.HCAP);
     L.off_qa = take(int64_t(C) * L.HCAP);
-    L.off_meta = take(8);
-    L.off_beta = take(C);
     L.off_A = take(L.C2);
     L.off_QK = take(L.C2);
+    L.off_stage0 = o;
+    L.off_grec = take(4 * L.E);
+    L.off_mrec = take(2 * L.E);
+    L.off_brec = take(4 * L.HMAX);
+    L.off_gw = take(L.E);
+    L.off_gr = take(L.F);
+    L.off_kid = take(L.E);
+    L.off_qid = take(L.F);
+    L.off_meta = take(8);
+    L.off_beta = take(C);
     L.off_X = take(L.C2);
     L.off_QX = take(L.C2);
+    L.off_stage1 = o;
     L.words = o;
     return L;
 }
 
-// Phase-2 launch geometry: vectors per column slice, slices per row, threads per workgroup.
+// Phase-2 launch geometry: vectors per column slice, slices per row, whether the chunk's
+// Phase-2 block is staged in LDS.
 struct P2Geom {
-    int nv, S, block;
+    int nv, S;
+    bool staged;
 };
 
 struct Slab {

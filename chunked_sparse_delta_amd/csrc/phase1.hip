@@ -64,6 +64,8 @@ __global__ __launch_bounds__(BLOCK) void p1_sort_kernel(Problem pb, Slab sl) {
     const uint64_t lt = lanemask_lt(lane);
     const int32_t seg = ((El + NW - 1) / NW + 63) & ~63;
     const int32_t s0 = min(El, wv * seg), s1 = min(El, s0 + seg);
+    uint32_t *kid = cb + sl.lay.off_kid;
+    for (int32_t e = threadIdx.x; e < El; e += BLOCK) kid[e] = kin[e];   // ids in entry order, for Phase 2
 
     for (int q = 0; q < pb.sort_passes; ++q) {
         const int shift = q * pb.sort_digit;
@@ -441,6 +443,7 @@ __global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb
     float *gr = reinterpret_cast<float *>(cb + L.off_gr);
     int4 *rcr = reinterpret_cast<int4 *>(cb + L.off_rcr);
     float *Qa = reinterpret_cast<float *>(cb + L.off_qa);
+    int32_t *qid = reinterpret_cast<int32_t *>(cb + L.off_qid);
     const int HP = meta[5];
     float *qr = qrow[wave];
     for (int h = lane; h < HP; h += kWave) qr[h] = 0.0f;
@@ -455,6 +458,7 @@ __global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb
         int4 cr = make_int4(0, 0, 0, 0);
         if (ok && i < nl) {
             const int32_t q = pb.q_idx[tg * R + r];
+            qid[int64_t(i) * R + r] = q;   // ids in entry order, for Phase 2
             const int32_t b = min(int32_t(uint32_t(q) >> bsh), int32_t(L.NB) - 1);
             const int32_t b0 = bstart[b];
             int32_t lo = b0, hi = bstart[b + 1];

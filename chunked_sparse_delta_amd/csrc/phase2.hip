@@ -60,6 +60,7 @@ struct P2Args {
     int32_t S, hv;                  // slices per row, vectors per row (hd / V)
     int32_t ti0, steps;             // the slab
     int32_t off_gw, off_gr, off_beta, off_X, off_QX, off_meta, off_grec, off_mrec, off_brec;   // words within a chunk
+    int32_t off_kid, off_qid, off_stage0, off_stage1;
 };
 
 __device__ __forceinline__ int32_t live_tokens(const P2Args &a, int p, int ti) {
@@ -291,8 +292,16 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
     }
 }
 
-template <typename T, int V, int NV, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
+// SM ("small"): the chunk's whole Phase-2 block of the workspace (records, weights, ids,
+// meta, beta, X, QX) fits in LDS next to the two row regions; it is copied there at the
+// start of every step with one sweep of 16-byte loads (and this slice of v with it), so
+// that a step waits on memory only for its gather and its DW bank rows.
+constexpr int kP2Block = 1024;
+constexpr int kStageUnits = 4;   // 16-byte units of the staged block per thread per round
+
+template <typename T, int V, int NV, bool SM>
+__global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
+    constexpr int BLOCK = kP2Block;
     using Cfg = P2Cfg<BLOCK, V>;
     constexpr int NW = Cfg::NW;
     extern __shared__ float lds[];
@@ -321,6 +330,9 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
 
     float *ub = lds;                  // [CP][pitch]: retrieved, then u
     float *ib = lds + CP * pitch;     // [CP][pitch]: inter, then delta_v
+    float *stg = ib + CP * pitch;     // SM: the staged block, then [C][NV] vectors of v
+    const int nstage = a.off_stage1 - a.off_stage0;           // words (a multiple of 64)
+    typename Vec<T, V>::raw_t *vst = reinterpret_cast<typename Vec<T, V>::raw_t *>(stg + nstage);
 
     // MFMA tiles of this wave: (it, ct) dealt in a snake order over tiles sorted by it,
     // so that every wave gets a similar share of the triangular work.
@@ -336,24 +348,55 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
         asm volatile("" : "+s"(wave));
         int lane = tid & 63;
         const int ti = a.ti0 + s;
-        const uint32_t *cb = a.ws + (int64_t(p) * a.steps + s) * a.words;
+        const uint32_t *cbg = a.ws + (int64_t(p) * a.steps + s) * a.words;
+        // Phase-2 arrays of the chunk: in LDS (SM) or in the workspace
+        auto arr = [&](int32_t off) -> const uint32_t * {
+            if constexpr (SM) return reinterpret_cast<const uint32_t *>(stg) + (off - a.off_stage0);
+            else return cbg + off;
+        };
         const int nl = live_tokens(a, p, ti);
         const int rows = min(C, a.T - ti * C);
         const int64_t tok0 = int64_t(p) * a.T + int64_t(ti) * C;
         const T *vin = static_cast<const T *>(a.v) + tok0 * hd;     // this chunk's rows of v and out
         T *out = static_cast<T *>(a.out) + tok0 * hd;
+        if constexpr (SM) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.off_stage0);
+            uint4 *dst = reinterpret_cast<uint4 *>(stg);
+            const int nu = nstage >> 2;
+            typename Vec<T, V>::raw_t vr;
+            const int vt = tid / NV, vv = tid % NV;
+            const bool vok = tid < C * NV && vt < rows && vv < nvs;
+            if (vok) vr = Vec<T, V>::load_raw(at(vin, uint32_t(vt * hd + col0 + vv * V)));
+            // rounds of kStageUnits 16-byte loads in flight per thread, then their stores
+            for (int u0 = tid; u0 < nu; u0 += BLOCK * kStageUnits) {
+                uint4 t0, t1, t2, t3;
+                static_assert(kStageUnits == 4, "unrolled by hand");
+                if (u0 < nu) t0 = src[u0];
+                if (u0 + BLOCK < nu) t1 = src[u0 + BLOCK];
+                if (u0 + 2 * BLOCK < nu) t2 = src[u0 + 2 * BLOCK];
+                if (u0 + 3 * BLOCK < nu) t3 = src[u0 + 3 * BLOCK];
+                if (u0 < nu) dst[u0] = t0;
+                if (u0 + BLOCK < nu) dst[u0 + BLOCK] = t1;
+                if (u0 + 2 * BLOCK < nu) dst[u0 + 2 * BLOCK] = t2;
+                if (u0 + 3 * BLOCK < nu) dst[u0 + 3 * BLOCK] = t3;
+            }
+            if (vok) vst[tid] = vr;
+            __syncthreads();
+        }
 
         // ---- gather: retrieved -> ub, inter -> ib (live tokens)
         {
-            const float *gw = reinterpret_cast<const float *>(cb + a.off_gw);
-            const float *gr = reinterpret_cast<const float *>(cb + a.off_gr);
-            gather_region<T, V, NV, BLOCK>(bank, hd, a.k_idx + tok0 * a.W, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
-            gather_region<T, V, NV, BLOCK>(bank, hd, a.q_idx + tok0 * a.R, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
+            const float *gw = reinterpret_cast<const float *>(arr(a.off_gw));
+            const float *gr = reinterpret_cast<const float *>(arr(a.off_gr));
+            const int32_t *kid = reinterpret_cast<const int32_t *>(arr(a.off_kid));
+            const int32_t *qid = reinterpret_cast<const int32_t *>(arr(a.off_qid));
+            gather_region<T, V, NV, BLOCK>(bank, hd, kid, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
+            gather_region<T, V, NV, BLOCK>(bank, hd, qid, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
         }
         __syncthreads();
 
         // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1
-        const float *beta_c = reinterpret_cast<const float *>(cb + a.off_beta);
+        const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
 #pragma unroll
         for (int x = 0; x < Cfg::kUItems; ++x) {
             const int item = tid + BLOCK * x, t = item / NV, vq = item % NV;
@@ -362,7 +405,8 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
             float uu[V];
             if (t < nl && vq < nvs) {
                 float vv[V], rr[V];
-                Vec<T, V>::load(at(vin, uint32_t(t * hd + col0 + vq * V)), vv);
+                if constexpr (SM) Vec<T, V>::unpack(vst[t * NV + vq], vv);
+                else Vec<T, V>::load(at(vin, uint32_t(t * hd + col0 + vq * V)), vv);
                 const float b = beta_c[t];
                 lds_load_vec<V>(ur, rr);
 #pragma unroll
@@ -377,8 +421,8 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
 
         // ---- dual matmul on the matrix cores
         asm volatile("" : "+v"(lane));
-        const float *QX = reinterpret_cast<const float *>(cb + a.off_QX);
-        const float *X = reinterpret_cast<const float *>(cb + a.off_X);
+        const float *QX = reinterpret_cast<const float *>(arr(a.off_QX));
+        const float *X = reinterpret_cast<const float *>(arr(a.off_X));
         f32x4 dacc[Cfg::kMaxTiles];
 #pragma unroll
         for (int q = 0; q < Cfg::kMaxTiles; ++q) {
@@ -444,11 +488,11 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
         {
             int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
             asm volatile("" : "+v"(dlane));
-            const int32_t *meta = reinterpret_cast<const int32_t *>(cb + a.off_meta);
+            const int32_t *meta = reinterpret_cast<const int32_t *>(arr(a.off_meta));
             const int32_t ng = nl > 0 ? meta[2] : 0, nbig = nl > 0 ? meta[4] : 0;
-            const int4 *grec = reinterpret_cast<const int4 *>(cb + a.off_grec);
-            const int4 *brec = reinterpret_cast<const int4 *>(cb + a.off_brec);
-            const int2 *mrec = reinterpret_cast<const int2 *>(cb + a.off_mrec);
+            const int4 *grec = reinterpret_cast<const int4 *>(arr(a.off_grec));
+            const int4 *brec = reinterpret_cast<const int4 *>(arr(a.off_brec));
+            const int2 *mrec = reinterpret_cast<const int2 *>(arr(a.off_mrec));
             for (int32_t bi = wave; bi < nbig; bi += NW) {
                 const int4 rec = *at(brec, uint32_t(bi));
                 dw_big_group<T, V>(bank, hd, rec, mrec, ib, pitch, col0, nvs, dlane);
@@ -539,39 +583,52 @@ __global__ __launch_bounds__(BLOCK) void phase2_kernel(P2Args a) {
 // ---------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------
-template <typename T, int V, int B>
+template <typename T, int V, bool SM>
 static const void *p2_fn_nv(int nv) {
     switch (nv) {
-        case 1: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 1, B>);
-        case 2: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 2, B>);
-        case 4: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 4, B>);
-        default: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 8, B>);
+        case 1: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 1, SM>);
+        case 2: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 2, SM>);
+        case 4: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 4, SM>);
+        default: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 8, SM>);
     }
 }
 
-template <int B>
-static const void *phase2_fn_b(int dtype, int V, int nv) {
-    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, B>(nv) : p2_fn_nv<float, 1, B>(nv);
-    return V == 8 ? p2_fn_nv<bf16, 8, B>(nv) : p2_fn_nv<bf16, 1, B>(nv);
+template <bool SM>
+static const void *phase2_fn_s(int dtype, int V, int nv) {
+    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, SM>(nv) : p2_fn_nv<float, 1, SM>(nv);
+    return V == 8 ? p2_fn_nv<bf16, 8, SM>(nv) : p2_fn_nv<bf16, 1, SM>(nv);
 }
 
-static const void *phase2_fn(int dtype, int V, int nv, int block) {
-    return block == 512 ? phase2_fn_b<512>(dtype, V, nv) : phase2_fn_b<1024>(dtype, V, nv);
+static const void *phase2_fn(int dtype, int V, int nv, bool sm) {
+    return sm ? phase2_fn_s<true>(dtype, V, nv) : phase2_fn_s<false>(dtype, V, nv);
 }
 
 hipError_t phase2_prepare() {
     for (int dt = 0; dt < 2; ++dt)
         for (int V : {1, dt == 0 ? 4 : 8})
             for (int nv : {1, 2, 4, 8})
-                for (int b : {512, 1024}) {
-                    hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv, b),
+                for (bool sm : {false, true}) {
+                    hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv, sm),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
                     if (e != hipSuccess) return e;
                 }
     return hipSuccess;
 }
 
-size_t phase2_lds_bytes(int C, int nv, int V) { return size_t(2) * p2_rows(C) * p2_pitch(nv * V) * sizeof(float); }
+// LDS of a Phase-2 workgroup: the two row regions, plus (staged) the chunk's Phase-2 block
+// and C x NV vectors of v.
+size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, bool staged) {
+    size_t b = size_t(2) * p2_rows(C) * p2_pitch(nv * V) * sizeof(float);
+    if (staged) b += size_t(L.off_stage1 - L.off_stage0) * 4 + size_t(C) * nv * V * es;
+    return b;
+}
+
+// Whether the chunk's Phase-2 block is staged in LDS: it must fit the device's LDS, and
+// v's C x NV vectors one per thread.
+bool phase2_staged(const ChunkLayout &L, int C, int nv, int V, int es, int lds_limit) {
+    if (int64_t(C) * nv > kP2Block) return false;
+    return phase2_lds_bytes(L, C, nv, V, es, true) + 256 <= size_t(lds_limit);
+}
 
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st) {
     const ChunkLayout &L = sl.lay;
@@ -583,9 +640,13 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
     a.off_gw = int32_t(L.off_gw); a.off_gr = int32_t(L.off_gr); a.off_beta = int32_t(L.off_beta);
     a.off_X = int32_t(L.off_X); a.off_QX = int32_t(L.off_QX); a.off_meta = int32_t(L.off_meta);
     a.off_grec = int32_t(L.off_grec); a.off_mrec = int32_t(L.off_mrec); a.off_brec = int32_t(L.off_brec);
-    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(unsigned(g.block));
+    a.off_kid = int32_t(L.off_kid); a.off_qid = int32_t(L.off_qid);
+    a.off_stage0 = int32_t(L.off_stage0); a.off_stage1 = int32_t(L.off_stage1);
+    const int es = pb.dtype == 0 ? 4 : 2;
+    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
     void *args[] = {&a};
-    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv, g.block), grid, block, args, phase2_lds_bytes(pb.C, g.nv, V), st);
+    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv, g.staged), grid, block, args,
+                           phase2_lds_bytes(L, pb.C, g.nv, V, es, g.staged), st);
 }
 
 }  // namespace sdm

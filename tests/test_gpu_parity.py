@@ -203,12 +203,12 @@ def test_workload_4p_sampled_streams(gpu):
     small(P=2, T=100, C=48, hd=40, M=80, W=5, R=3, ids="zipf", index=28),
 ], ids=["bf16_P8", "f32_P3", "f32_partial_slice"])
 def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
-    """The column slicing and the block size change only the schedule: every geometry gives the same
+    """The column slicing and the LDS staging change only the schedule: every geometry gives the same
     bits (the gather, matmul and DW sums run in orders fixed by W, R and C)."""
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
     results = []
-    for geom in (None, "1", "2", "4", "8", "2,512", "8,512"):
+    for geom in (None, "1", "2", "4", "8", "1,0", "8,0"):
         if geom is None:
             monkeypatch.delenv("SDM_P2_GEOM", raising=False)
         else:
