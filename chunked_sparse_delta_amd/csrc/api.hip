@@ -12,12 +12,15 @@
 
 #include "sdm.h"
 #include "common.h"
+#include "wy_impl.h"
 
 namespace sdm {
 hipError_t phase1_prepare();
 hipError_t phase2_prepare();
 hipError_t wy_prepare();
-hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev);
+hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev, bool fused,
+                         const WyArgs &wa);
+bool phase1_fused(const ChunkLayout &L, int C, int lds_limit);
 hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
                      int64_t stride, int64_t bstride, hipStream_t st);
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st);
@@ -245,6 +248,7 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
     int64_t slab64 = int64_t(exec->workspace_bytes / per_step);
     int32_t slab = slab64 > Nt ? Nt : int32_t(slab64);
     hipStream_t st = static_cast<hipStream_t>(exec->stream);
+    const bool fused = phase1_fused(ck.lay, C, dev->lds_per_block);
     hipEvent_t *ev = nullptr;
     if (exec->events && exec->num_events >= SDM_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
     for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
@@ -254,13 +258,16 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
         sl.ws = static_cast<uint32_t *>(exec->workspace);
         sl.lay = ck.lay;
         hipEvent_t *sev = ti0 == 0 ? ev : nullptr;
-        hipError_t e = launch_phase1(ck.pb, sl, st, sev);
+        float *w = reinterpret_cast<float *>(sl.ws);
+        const WyArgs wa{w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X,
+                        w + sl.lay.off_QX, C, sl.lay.words, sl.lay.words};
+        hipError_t e = launch_phase1(ck.pb, sl, st, sev, fused, wa);
         if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
         if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        float *w = reinterpret_cast<float *>(sl.ws);
-        e = launch_wy(w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X, w + sl.lay.off_QX, C,
-                      int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
-        if (e != hipSuccess) return hip_fail(e, "solve launch");
+        if (!fused) {
+            e = launch_wy(wa.A, wa.beta, wa.QK, wa.X, wa.QX, C, int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
+            if (e != hipSuccess) return hip_fail(e, "solve launch");
+        }
         if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         e = launch_phase2(ck.pb, sl, ck.V, geom, st);
         if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
@@ -329,12 +336,16 @@ int sdm_chunk_mats(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, cons
         sl.steps = Nt - ti0 < slab ? Nt - ti0 : slab;
         sl.ws = static_cast<uint32_t *>(exec->workspace);
         sl.lay = ck.lay;
-        hipError_t e = launch_phase1(ck.pb, sl, st, nullptr);
-        if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
         float *w = reinterpret_cast<float *>(sl.ws);
-        e = launch_wy(w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X, w + sl.lay.off_QX, C,
-                      int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
-        if (e != hipSuccess) return hip_fail(e, "solve launch");
+        const WyArgs wa{w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X,
+                        w + sl.lay.off_QX, C, sl.lay.words, sl.lay.words};
+        const bool fused = phase1_fused(ck.lay, C, dev->lds_per_block);
+        hipError_t e = launch_phase1(ck.pb, sl, st, nullptr, fused, wa);
+        if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
+        if (!fused) {
+            e = launch_wy(wa.A, wa.beta, wa.QK, wa.X, wa.QX, C, int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
+            if (e != hipSuccess) return hip_fail(e, "solve launch");
+        }
         hipLaunchKernelGGL(copy_mats_kernel, dim3(64, unsigned(int64_t(P) * sl.steps)), dim3(256), 0, st, sl, P, Nt, o);
         if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "copy launch");
     }

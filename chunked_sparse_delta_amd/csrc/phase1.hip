@@ -21,7 +21,12 @@
 //              fixed order and replays them into the lanes that own their columns
 //   p1_gram_hot   the hot pair terms as dense products on the matrix cores
 // No float atomics anywhere: every element has one writer and a fixed summation order.
+#include <stdlib.h>
+
+#include <algorithm>
+
 #include "common.h"
+#include "wy_impl.h"
 
 namespace sdm {
 
@@ -46,13 +51,16 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool ok, int db) {
 }
 
 template <int BLOCK>
-__global__ __launch_bounds__(BLOCK) void p1_sort_kernel(Problem pb, Slab sl) {
+constexpr size_t sort_smem_bytes() { return size_t(BLOCK / kWave) * (1 << kSortDigit) * 4 + (1 << kSortDigit) / kWave * 4; }
+
+// The sort of chunk n by one workgroup of BLOCK threads; smem: sort_smem_bytes<BLOCK>().
+template <int BLOCK>
+__device__ __forceinline__ void sort_chunk(const Problem &pb, const Slab &sl, int64_t n, char *smem) {
     constexpr int NW = BLOCK / kWave;
     constexpr int NBK = 1 << kSortDigit;
     static_assert(BLOCK >= NBK, "one thread per digit");
-    __shared__ int32_t cnt[NW][NBK];
-    __shared__ int32_t dsum[NBK / kWave];
-    const int64_t n = blockIdx.x;
+    int32_t(*cnt)[NBK] = reinterpret_cast<int32_t(*)[NBK]>(smem);
+    int32_t *dsum = reinterpret_cast<int32_t *>(smem + NW * NBK * 4);
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     const int32_t El = nl * pb.W;
@@ -242,15 +250,24 @@ __device__ __forceinline__ int bucket_shift(const Problem &pb, int64_t E) {
 
 constexpr int kMaxHot = kMaxChunk * kMaxWidth / kHotMin;   // hot groups of a chunk, at most
 
+template <int NW> struct GroupsSmem {
+    TileScan<NW> ts;
+    int32_t wsum[NW];
+    int32_t ncand, nhot;
+    int32_t cand[kMaxHot];
+    uint8_t cand_hot[kMaxHot];
+};
+
+// The group scan of chunk n by one workgroup of BLOCK threads; smem: GroupsSmem.
 template <int BLOCK>
-__global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
+__device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, int64_t n, char *smem) {
     constexpr int NW = BLOCK / kWave;
-    __shared__ TileScan<NW> ts;
-    __shared__ int32_t wsum[NW];
-    __shared__ int32_t ncand, nhot;
-    __shared__ int32_t cand[kMaxHot];
-    __shared__ uint8_t cand_hot[kMaxHot];
-    const int64_t n = blockIdx.x;
+    GroupsSmem<NW> &gs = *reinterpret_cast<GroupsSmem<NW> *>(smem);
+    TileScan<NW> &ts = gs.ts;
+    int32_t *wsum = gs.wsum;
+    int32_t &ncand = gs.ncand, &nhot = gs.nhot;
+    int32_t *cand = gs.cand;
+    uint8_t *cand_hot = gs.cand_hot;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     const int W = pb.W, C = pb.C;
@@ -423,14 +440,12 @@ __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
 // at a time, lanes ascending), so duplicate reads of a slot sum in a fixed order.
 constexpr int kReadWaves = 4;
 
-__global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb, Slab sl) {
-    __shared__ float qrow[kReadWaves][kHotCap];
-    const int64_t n = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int i = blockIdx.x * kReadWaves + wave;
+// The reads of token i of chunk n by one wavefront; qr: kHotCap floats of LDS.
+__device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr) {
+    const int lane = threadIdx.x & 63;
     const ChunkLayout &L = sl.lay;
     const int R = pb.R, C = pb.C;
-    if (i >= C) return;   // whole wavefronts; no workgroup barrier below
+    if (i >= C) return;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     uint32_t *cb = sl.chunk(n);
@@ -445,7 +460,6 @@ __global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb
     float *Qa = reinterpret_cast<float *>(cb + L.off_qa);
     int32_t *qid = reinterpret_cast<int32_t *>(cb + L.off_qid);
     const int HP = meta[5];
-    float *qr = qrow[wave];
     for (int h = lane; h < HP; h += kWave) qr[h] = 0.0f;
     __builtin_amdgcn_wave_barrier();
     const int64_t tg = int64_t(p) * pb.T + int64_t(ti) * C + i;
@@ -510,13 +524,11 @@ __global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb
 constexpr int kColdBlock = 512;
 constexpr int kTermCap = 512;   // terms per wavefront per round (>= 255 earlier members of one entry)
 
-__global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Slab sl) {
-    constexpr int NW = kColdBlock / kWave;
-    __shared__ int32_t tcol[NW][kTermCap];
-    __shared__ float tval[NW][kTermCap];
+// Row i of the cold part of A (qk false) or QK (qk true) of chunk n by one wavefront;
+// mcol, mval: kTermCap entries each of LDS.
+__device__ __forceinline__ void cold_row(const Problem &pb, const Slab &sl, int64_t n, bool qk, int i, int32_t *mcol,
+                                         float *mval) {
     const int C = pb.C;
-    const int64_t n = blockIdx.x;
-    const bool qk = blockIdx.y != 0;
     const int width = qk ? pb.R : pb.W;
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
@@ -525,11 +537,8 @@ __global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Sl
     const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
     const int4 *cr = reinterpret_cast<const int4 *>(cb + (qk ? L.off_rcr : L.off_ecr));
     float *Mout = reinterpret_cast<float *>(cb + (qk ? L.off_QK : L.off_A));
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t *mcol = tcol[wave];
-    float *mval = tval[wave];
-
-    for (int i = wave; i < C; i += NW) {
+    const int lane = threadIdx.x & 63;
+    {
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int x0 = 0; i < nl && x0 < width; x0 += kWave) {
             const int x = x0 + lane;
@@ -603,9 +612,9 @@ constexpr int kHotBlock = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab sl) {
-    constexpr int NWAVE = kHotBlock / kWave;
-    const int64_t n = blockIdx.x;
+// Hot tiles t0, t0 + tstep, ... (of the 2 T1 lower tiles of A and QK) of chunk n, one
+// wavefront.
+__device__ __forceinline__ void hot_tiles(const Problem &pb, const Slab &sl, int64_t n, int t0, int tstep) {
     const ChunkLayout &L = sl.lay;
     uint32_t *cb = sl.chunk(n);
     const int32_t *meta = reinterpret_cast<const int32_t *>(cb + L.off_meta);
@@ -621,9 +630,9 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
     const float *Qa = reinterpret_cast<const float *>(cb + L.off_qa);
     float *A = reinterpret_cast<float *>(cb + L.off_A);
     float *QK = reinterpret_cast<float *>(cb + L.off_QK);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int ko = 4 * (lane >> 4);
-    for (int t = blockIdx.y * NWAVE + wave; t < 2 * T1; t += gridDim.y * NWAVE) {
+    for (int t = t0; t < 2 * T1; t += tstep) {
         const bool isA = t < T1;
         const int tt = isA ? t : t - T1;
         int I = 0;
@@ -652,6 +661,85 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
 }
 
 // ---------------------------------------------------------------------------------------
+// Kernels: one stage per launch (large chunks), or every stage and the solve in one
+// workgroup per chunk (small chunks), so that a small chunk pays one launch instead of six.
+// ---------------------------------------------------------------------------------------
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void p1_sort_kernel(Problem pb, Slab sl) {
+    __shared__ __align__(16) char smem[sort_smem_bytes<BLOCK>()];
+    sort_chunk<BLOCK>(pb, sl, blockIdx.x, smem);
+}
+
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
+    __shared__ __align__(16) char smem[sizeof(GroupsSmem<BLOCK / kWave>)];
+    groups_chunk<BLOCK>(pb, sl, blockIdx.x, smem);
+}
+
+__global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb, Slab sl) {
+    __shared__ float qrow[kReadWaves][kHotCap];
+    const int wave = threadIdx.x >> 6;
+    reads_token(pb, sl, blockIdx.y, blockIdx.x * kReadWaves + wave, qrow[wave]);
+}
+
+__global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Slab sl) {
+    constexpr int NW = kColdBlock / kWave;
+    __shared__ int32_t tcol[NW][kTermCap];
+    __shared__ float tval[NW][kTermCap];
+    const int wave = threadIdx.x >> 6;
+    for (int i = wave; i < pb.C; i += NW) cold_row(pb, sl, blockIdx.x, blockIdx.y != 0, i, tcol[wave], tval[wave]);
+}
+
+__global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab sl) {
+    constexpr int NWAVE = kHotBlock / kWave;
+    hot_tiles(pb, sl, blockIdx.x, blockIdx.y * NWAVE + (threadIdx.x >> 6), gridDim.y * NWAVE);
+}
+
+constexpr int kFusedBlock = 1024;
+
+__global__ __launch_bounds__(kFusedBlock) void p1_fused_kernel(Problem pb, Slab sl, WyArgs wa) {
+    extern __shared__ __align__(16) char fsm[];
+    constexpr int NW = kFusedBlock / kWave;
+    const int64_t n = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    sort_chunk<kFusedBlock>(pb, sl, n, fsm);
+    __syncthreads();
+    groups_chunk<kFusedBlock>(pb, sl, n, fsm);
+    __syncthreads();
+    {
+        float *qr = reinterpret_cast<float *>(fsm) + wave * kHotCap;
+        for (int i = wave; i < pb.C; i += NW) reads_token(pb, sl, n, i, qr);
+    }
+    __syncthreads();
+    {
+        int32_t *mcol = reinterpret_cast<int32_t *>(fsm) + wave * 2 * kTermCap;
+        float *mval = reinterpret_cast<float *>(mcol + kTermCap);
+        for (int k = wave; k < 2 * pb.C; k += NW) cold_row(pb, sl, n, k >= pb.C, k >= pb.C ? k - pb.C : k, mcol, mval);
+    }
+    __syncthreads();
+    hot_tiles(pb, sl, n, wave, NW);
+    __syncthreads();
+    wy_chunk<kFusedBlock>(wa, n, reinterpret_cast<float *>(fsm));
+}
+
+static size_t fused_smem_bytes(int C) {
+    size_t b = sort_smem_bytes<kFusedBlock>();
+    b = std::max(b, sizeof(GroupsSmem<kFusedBlock / kWave>));
+    b = std::max(b, size_t(kFusedBlock / kWave) * kHotCap * 4);
+    b = std::max(b, size_t(kFusedBlock / kWave) * 2 * kTermCap * 4);
+    return std::max(b, wy_lds_bytes(C));
+}
+
+// Whether a chunk's Phase 1 and solve run fused: small chunks (E, F <= 1024) whose stages
+// fit the device's LDS. SDM_P1_FUSED=0 or 1 overrides (where it fits), for sweeps.
+bool phase1_fused(const ChunkLayout &L, int C, int lds_limit) {
+    if (fused_smem_bytes(C) > size_t(lds_limit)) return false;
+    const char *env = getenv("SDM_P1_FUSED");
+    if (env && (env[0] == '0' || env[0] == '1')) return env[0] == '1';
+    return L.E <= 1024 && L.F <= 1024;
+}
+
+// ---------------------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------------------
 constexpr int kSortBlock = 1024;
@@ -660,13 +748,25 @@ constexpr int kGroupBlock = 1024;
 size_t gram_lds_bytes(int) { return 0; }   // the cold Gram uses static LDS only
 
 
-hipError_t phase1_prepare() { return hipSuccess; }
+hipError_t phase1_prepare() {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_fused_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(fused_smem_bytes(kMaxChunk)));
+}
 
-// ev: nullptr, or 5 events recorded before each of the five kernels.
-hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev) {
+// ev: nullptr, or 5 events recorded before each of the five kernels (fused: the first
+// before the fused kernel, the other four after it). fused: Phase 1 and the solve in one
+// kernel (wa: the solve's arguments); otherwise the caller launches the solve.
+hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev, bool fused,
+                         const WyArgs &wa) {
     const unsigned nch = unsigned(int64_t(pb.P) * sl.steps);
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+    if (fused) {
+        hipLaunchKernelGGL(p1_fused_kernel, dim3(nch), dim3(kFusedBlock), fused_smem_bytes(pb.C), st, pb, sl, wa);
+        for (int k = 1; ev && k < 5; ++k)
+            if ((e = hipEventRecord(ev[k], st)) != hipSuccess) return e;
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(p1_sort_kernel<kSortBlock>, dim3(nch), dim3(kSortBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_groups_kernel<kGroupBlock>, dim3(nch), dim3(kGroupBlock), 0, st, pb, sl);

@@ -84,6 +84,14 @@ __device__ __forceinline__ T *at(T *base, uint32_t off) {
 __host__ __device__ inline int p2_pitch(int cw) { return ((cw + 3) & ~3) + 4; }
 __host__ __device__ inline int p2_rows(int C) { return (C + 15) & ~15; }
 
+// Workgroup barrier for data exchanged through LDS only: unlike __syncthreads() it does
+// not wait for this wave's outstanding global stores (the readings, the bank rows).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Combine the eight entry classes of a lane's sum (classes are lane bits NV, 2NV, 4NV).
 template <int V, int NV>
 __device__ __forceinline__ void combine_classes(float (&acc)[V]) {
@@ -381,7 +389,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 if (u0 + 3 * BLOCK < nu) dst[u0 + 3 * BLOCK] = t3;
             }
             if (vok) vst[tid] = vr;
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- gather: retrieved -> ub, inter -> ib (live tokens)
@@ -393,7 +401,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             gather_region<T, V, NV, BLOCK>(bank, hd, kid, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
             gather_region<T, V, NV, BLOCK>(bank, hd, qid, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1
         const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             }
             lds_store_vec<V>(ur, uu);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- dual matmul on the matrix cores
         asm volatile("" : "+v"(lane));
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 store_out4<T>(at(out, uint32_t(ti_row * hd + col0 + co)), y, min(4, cwv - co));
             }
         }
-        __syncthreads();
+        lds_barrier();
         // delta_v -> ib
 #pragma unroll
         for (int q = 0; q < Cfg::kMaxTiles; ++q) {
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             if (ti_row < C && co < cwv)
                 *reinterpret_cast<float4 *>(ib + ti_row * pitch + co) = make_float4(dacc[q][0], dacc[q][1], dacc[q][2], dacc[q][3]);
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- DW: one writer per written row. Groups with >= kHotMin members go to whole
         //      wavefronts (dw_big_group, from the list of their records); the others are
@@ -576,7 +584,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
             }
         }
-        __syncthreads();
+        __syncthreads();   // the DW's bank stores are visible to the next step's gather
     }
 }
 

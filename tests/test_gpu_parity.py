@@ -218,3 +218,21 @@ def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
     gu.parity(o, b, inp, wl.C, "geometry")
     for geom, ob, bb in results[1:]:
         assert np.array_equal(ob, results[0][1]) and np.array_equal(bb, results[0][2]), geom
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=8, T=300, C=64, hd=64, M=200, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=29),
+    small(P=3, T=260, C=48, hd=32, M=60, W=16, R=16, ids="zipf", zipf_s=1.3, ragged=True, index=30),
+], ids=["bf16_P8", "f32_hot"])
+def test_phase1_fusion_does_not_change_bits(gpu, wl, monkeypatch):
+    """Phase 1 and the solve fused into one workgroup per chunk give the same bits as the
+    separate kernels (the per-chunk arithmetic is the same; only the launch differs)."""
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    results = []
+    for fused in ("0", "1"):
+        monkeypatch.setenv("SDM_P1_FUSED", fused)
+        o, b = gu.run(t, wl.C)
+        results.append((gu.bits(o), gu.bits(b)))
+    gu.parity(o, b, inp, wl.C, "fused phase 1")
+    assert np.array_equal(results[0][0], results[1][0]) and np.array_equal(results[0][1], results[1][1])
