@@ -166,7 +166,7 @@ def main():
               "streams or columns, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
-    from chunked_sparse_delta_amd import TIMING_EVENTS, sdm_fwd, workspace_bytes
+    from chunked_sparse_delta_amd import TIMING_EVENTS, plan, sdm_fwd, workspace_bytes
 
     wl = workloads.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
@@ -243,6 +243,7 @@ def main():
                    "head_dim": wl.hd, "rows_per_stream": wl.M, "bank_dtype": wl.dtype, "W": wl.W, "R": wl.R,
                    "valid_tokens": tokens, "distinct_rows_read": stats["U"], "rows_written": stats["Uw"]},
         "kernel_ms": kern_ms,
+        "plan": plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, bank.dtype),
         "roofline": roof,
         "path_hbm": {"algorithmic_bytes": int(path_bytes), "achieved": round(path_gbs, 1), "unit": "GB/s",
                      "frac": round(path_gbs / HBM_PEAK_GBS, 4)},

@@ -22,7 +22,7 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "workspace_bytes", "library_path",
+__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "workspace_bytes", "plan", "library_path",
            "SDM_ERRORS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +87,8 @@ def _load():
             lib.sdm_chunk_mats.restype = ctypes.c_int
             lib.sdm_wy_solve.argtypes = [i64, i32, p, p, p, p, p, p]
             lib.sdm_wy_solve.restype = ctypes.c_int
+            lib.sdm_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, p]
+            lib.sdm_fwd_plan.restype = ctypes.c_int
             lib.sdm_error_string.argtypes = [ctypes.c_int]
             lib.sdm_error_string.restype = ctypes.c_char_p
             lib.sdm_last_error.argtypes = []
@@ -125,6 +127,26 @@ def _expect(t: torch.Tensor, name: str, shape, dtype, device) -> None:
 def workspace_bytes(P: int, T: int, C: int, W: int, R: int, hd: int, slab_steps: int = 0) -> int:
     """Bytes of scratch sdm_fwd needs for slabs of ``slab_steps`` steps (0: all steps)."""
     return int(_load().sdm_fwd_workspace_bytes(P, T, C, W, R, hd, slab_steps))
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("vec", "slice_vectors", "slices", "phase2_mode",
+                                               "phase2_lds_bytes", "phase1_fused", "lds_limit", "lds_default")]
+
+
+PHASE2_MODES = ("memory", "staged", "resident")
+
+
+def plan(P: int, T: int, C: int, W: int, R: int, hd: int, M: int, dtype: torch.dtype) -> dict:
+    """The launch plan sdm_fwd takes for these shapes on the current device (sdm_fwd_plan)."""
+    lib = _load()
+    if dtype not in _DTYPES:
+        raise TypeError(f"bank dtype must be float32 or bfloat16, got {dtype}")
+    out = _Plan()
+    _check_rc(lib, lib.sdm_fwd_plan(P, T, C, W, R, hd, M, _DTYPES[dtype], ctypes.byref(out)))
+    d = {n: int(getattr(out, n)) for n, _ in _Plan._fields_}
+    d["phase2_mode"] = PHASE2_MODES[d["phase2_mode"]]
+    return d
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:

@@ -25,8 +25,8 @@ hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *
                      int64_t stride, int64_t bstride, hipStream_t st);
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st);
 size_t gram_lds_bytes(int C);
-size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, bool staged);
-bool phase2_staged(const ChunkLayout &L, int C, int nv, int V, int es, int lds_limit);
+size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M);
+int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, int lds_limit);
 }  // namespace sdm
 
 using namespace sdm;
@@ -51,9 +51,12 @@ int hip_fail(hipError_t e, const char *what) {
 // Per-device one-time setup: the large-LDS kernel attributes and the LDS limit.
 struct DeviceInfo {
     bool ready = false;
-    int lds_per_block = 0;
+    int lds_per_block = 0;   // the limit the plans use
+    int lds_default = 0;     // the device's default per-block limit (reported by sdm_fwd_plan)
     int cus = 0;
 };
+// The kernels' opt-in LDS attribute is set to at most this many bytes.
+constexpr int kMaxLdsPerBlock = 160 * 1024 - 256;
 DeviceInfo g_dev[64];
 std::mutex g_dev_mu;
 
@@ -65,8 +68,16 @@ int device_info(DeviceInfo **out) {
     std::lock_guard<std::mutex> lk(g_dev_mu);
     DeviceInfo &d = g_dev[dev];
     if (!d.ready) {
+        // LDS per workgroup: the default per-block limit, or the larger limit a kernel may opt
+        // into with hipFuncAttributeMaxDynamicSharedMemorySize (every kernel here does)
+        int optin = 0;
         if ((e = hipDeviceGetAttribute(&d.lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess)
             return hip_fail(e, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock)");
+        if ((e = hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev)) != hipSuccess)
+            return hip_fail(e, "hipDeviceGetAttribute(SharedMemPerBlockOptin)");
+        d.lds_default = d.lds_per_block;
+        if (optin > d.lds_per_block) d.lds_per_block = optin;
+        if (d.lds_per_block > kMaxLdsPerBlock) d.lds_per_block = kMaxLdsPerBlock;
         if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
             return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
         if ((e = phase1_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 1)");
@@ -165,9 +176,10 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
 // Phase-2 geometry from shapes only (the bits never depend on it): slices of NV vectors,
 // NV the largest power of two with NV * V * es <= 128 bytes (one cache line of a row),
 // halved while that leaves fewer than one workgroup per CU; one workgroup per
-// (stream, slice); the chunk's Phase-2 block staged in LDS when it fits.
-// SDM_P2_GEOM="nv[,staged]" overrides NV (1, 2, 4 or 8) and staging (0 or 1, where it
-// fits), for tuning sweeps.
+// (stream, slice); the chunk's Phase-2 block staged in LDS when it fits, and the slice of
+// the bank resident in LDS when that fits too.
+// SDM_P2_GEOM="nv[,mode]" overrides NV (1, 2, 4 or 8) and caps the mode (0 from memory,
+// 1 staged, 2 resident; the largest that fits is taken below the cap), for tuning sweeps.
 P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int cus, int lds_limit) {
     const int hv = pb.hd / V;
     P2Geom g{};
@@ -186,8 +198,8 @@ P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int c
         }
     }
     g.S = (hv + g.nv - 1) / g.nv;
-    g.staged = phase2_staged(L, pb.C, g.nv, V, es, lds_limit);
-    if (got == 2 && est == 0) g.staged = false;
+    g.mode = phase2_mode(L, pb.C, g.nv, V, es, pb.M, lds_limit);
+    if (got == 2 && est >= 0 && est < g.mode) g.mode = est;
     return g;
 }
 
@@ -211,6 +223,33 @@ const char *sdm_error_string(int code) {
 }
 
 const char *sdm_last_error(void) { return g_err; }
+
+int sdm_fwd_plan(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t hd, int64_t M, int32_t dtype,
+                 sdm_plan *plan) {
+    g_err[0] = 0;
+    if (!plan) return fail(SDM_ERR_NULL, "plan must not be NULL");
+    int rc = check_shape(P, T, C, W, R, hd);
+    if (rc) return rc;
+    if (dtype != SDM_F32 && dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "bank dtype must be SDM_F32 or SDM_BF16, got %d", dtype);
+    if (M < 1 || int64_t(P) * M >= (int64_t(1) << 31)) return fail(SDM_ERR_RANGE, "rows per stream out of range");
+    DeviceInfo *dev = nullptr;
+    if ((rc = device_info(&dev)) != SDM_OK) return rc;
+    const int es = dtype == SDM_F32 ? 4 : 2, vec = 16 / es;
+    const int V = hd % vec == 0 ? vec : 1;
+    Problem pb{};
+    pb.P = P; pb.T = T; pb.C = C; pb.W = W; pb.R = R; pb.hd = hd; pb.M = M; pb.dtype = dtype;
+    const ChunkLayout lay = make_layout(C, W, R);
+    const P2Geom g = plan_phase2(pb, lay, V, es, dev->cus, dev->lds_per_block);
+    plan->vec = V;
+    plan->slice_vectors = g.nv;
+    plan->slices = g.S;
+    plan->phase2_mode = g.mode;
+    plan->phase2_lds_bytes = int32_t(phase2_lds_bytes(lay, C, g.nv, V, es, g.mode, M));
+    plan->phase1_fused = phase1_fused(lay, C, dev->lds_per_block) ? 1 : 0;
+    plan->lds_limit = dev->lds_per_block;
+    plan->lds_default = dev->lds_default;
+    return SDM_OK;
+}
 
 size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t hd, int32_t slab_steps) {
     if (check_shape(P, T, C, W, R, hd) != SDM_OK) return 0;
@@ -240,7 +279,7 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
                     gram_lds_bytes(C), dev->lds_per_block);
     const P2Geom geom = plan_phase2(ck.pb, ck.lay, ck.V, ck.es, dev->cus, dev->lds_per_block);
-    const size_t p2lds = phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.staged);
+    const size_t p2lds = phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.mode, ck.pb.M);
     if (p2lds + 256 > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup in phase 2, the device has %d", C,
                     p2lds, dev->lds_per_block);

@@ -225,11 +225,12 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     return L;
 }
 
-// Phase-2 launch geometry: vectors per column slice, slices per row, whether the chunk's
-// Phase-2 block is staged in LDS.
+// Phase-2 launch geometry: vectors per column slice, slices per row, and the mode: 0 all
+// from memory, 1 the chunk's Phase-2 block staged in LDS, 2 staged and the bank slice
+// resident in LDS.
 struct P2Geom {
     int nv, S;
-    bool staged;
+    int mode;
 };
 
 struct Slab {

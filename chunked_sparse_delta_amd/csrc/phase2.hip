@@ -92,9 +92,40 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Combine the eight entry classes of a lane's sum (classes are lane bits NV, 2NV, 4NV).
+// End of a Phase-2 step: a bank held in LDS needs an LDS barrier only; a bank in memory
+// needs the DW's global stores visible to the whole workgroup.
+template <bool RB>
+__device__ __forceinline__ void step_end_barrier() {
+    if constexpr (RB) lds_barrier();
+    else __syncthreads();
+}
+
+// x + x of lane (lane ^ k) for k = 1, 2 (quad permutations), and x + x of lane
+// (lane ^ 7) within each group of 8 lanes (the row half-mirror), all on the VALU.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // lane i of a group of 8 reads lane 7 - i
+
+// Combine the eight entry classes of a lane's sum (classes are lane bits NV, 2NV, 4NV)
+// as ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)). With NV = 1 the classes are lanes 0..7 of a
+// group: after the xor-1 and xor-2 rounds the four lanes of a quad hold the same value
+// (each sum is formed from the same two operands), so the half-mirror lane of the other
+// quad is as good a partner as lane ^ 4. Every lane of the wavefront must be active.
 template <int V, int NV>
 __device__ __forceinline__ void combine_classes(float (&acc)[V]) {
+    if constexpr (NV == 1) {
+#pragma unroll
+        for (int c = 0; c < V; ++c) acc[c] = add_dpp<kDppXor1>(acc[c]);
+#pragma unroll
+        for (int c = 0; c < V; ++c) acc[c] = add_dpp<kDppXor2>(acc[c]);
+#pragma unroll
+        for (int c = 0; c < V; ++c) acc[c] = add_dpp<kDppHalfMirror>(acc[c]);
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], NV, 64);
 #pragma unroll
@@ -133,17 +164,17 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
 // vector of the slice), class r = (lane / NV) % 8, ts = lane / (8 NV) (the token within a
 // group of TPI = 8 / NV tokens). Instruction j of a token group loads entries 8 j + r.
 // The wave walks its token groups (wave, wave + NW, ...) as one flat list of
-// instructions, kBatch at a time.
+// instructions, kBatch at a time. The calling waves are wave = 0 .. nw - 1 of the region.
 template <typename T, int V, int NV, int BLOCK>
 __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
-                                              int nl, int col0, int nvs, float *dst, int pitch, int wave, int lane) {
+                                              int nl, int col0, int nvs, float *dst, int pitch, int wave, int nw,
+                                              int lane) {
     constexpr int TPI = 8 / NV;
     constexpr int kBatch = P2Cfg<BLOCK, V>::kBatch;
-    constexpr int kP2Waves = P2Cfg<BLOCK, V>::NW;
     const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
     const int NI = (width + 7) >> 3;
     const int NG = (nl + TPI - 1) / TPI;
-    const int ngw = NG > wave ? (NG - wave + kP2Waves - 1) / kP2Waves : 0;
+    const int ngw = NG > wave ? (NG - wave + nw - 1) / nw : 0;
     const int total = ngw * NI;
     if (total == 0) return;
     const bool vok = vq < nvs;
@@ -159,7 +190,7 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
             di[u] = -1;
             dw[u] = 0.0f;
             if (pk < ngw) {
-                const int t = (wave + pk * kP2Waves) * TPI + ts, e = 8 * pj + r;
+                const int t = (wave + pk * nw) * TPI + ts, e = 8 * pj + r;
                 if (t < nl && e < width) {
                     di[u] = *at(ids, uint32_t(t * width + e));
                     dw[u] = *at(wts, uint32_t(t * width + e));
@@ -191,7 +222,7 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
             }
             if (cj == NI - 1) {
                 combine_classes<V, NV>(acc);
-                const int t = (wave + ck * kP2Waves) * TPI + ts;
+                const int t = (wave + ck * nw) * TPI + ts;
                 if (r == 0 && t < nl && vok) lds_store_vec<V>(dst + t * pitch + vq * V, acc);
 #pragma unroll
                 for (int c = 0; c < V; ++c) acc[c] = 0.0f;
@@ -300,16 +331,29 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
     }
 }
 
-// SM ("small"): the chunk's whole Phase-2 block of the workspace (records, weights, ids,
-// meta, beta, X, QX) fits in LDS next to the two row regions; it is copied there at the
-// start of every step with one sweep of 16-byte loads (and this slice of v with it), so
-// that a step waits on memory only for its gather and its DW bank rows.
+// Modes:
+//   kP2Global    every array is read from the workspace, every bank row from memory.
+//   kP2Staged    the chunk's whole Phase-2 block of the workspace (records, weights, ids,
+//                meta, beta, X, QX) fits in LDS next to the two row regions; it is copied
+//                there at the start of every step with one sweep of 16-byte loads (and this
+//                slice of v with it), so that a step waits on memory only for its gather
+//                and its DW bank rows.
+//   kP2Resident  staged, and this workgroup's column slice of the stream's bank (M rows x
+//                NV vectors, in the bank dtype) also fits: it is loaded into LDS once per
+//                slab and written back at its end, and the gather and the DW run on it.
+//                Rows are held in the bank dtype, so every value is rounded exactly where
+//                the other modes round it on the way to memory: the bits are the same.
 constexpr int kP2Block = 1024;
 constexpr int kStageUnits = 4;   // 16-byte units of the staged block per thread per round
+constexpr int kP2Global = 0, kP2Staged = 1, kP2Resident = 2;
 
-template <typename T, int V, int NV, bool SM>
+// Bytes of the staged copy of C x NV vectors of v, rounded up to 16 bytes.
+__host__ __device__ inline int p2_vst_bytes(int C, int nv, int V, int es) { return (C * nv * V * es + 15) & ~15; }
+
+template <typename T, int V, int NV, int MODE>
 __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     constexpr int BLOCK = kP2Block;
+    constexpr bool SM = MODE >= kP2Staged, RB = MODE == kP2Resident;
     using Cfg = P2Cfg<BLOCK, V>;
     constexpr int NW = Cfg::NW;
     extern __shared__ float lds[];
@@ -333,14 +377,29 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     const int nvs = min(NV, a.hv - vq0);      // vectors of this slice
     const int cwv = nvs * V;                  // valid columns of this slice
     const int col0 = vq0 * V;
-    T *bank = static_cast<T *>(a.bank) + int64_t(p) * a.M * hd;
+    using raw_t = typename Vec<T, V>::raw_t;
+    T *gbank = static_cast<T *>(a.bank) + int64_t(p) * a.M * hd + col0;   // this slice, row stride hd
     const bool vec4 = (C & 3) == 0;
 
     float *ub = lds;                  // [CP][pitch]: retrieved, then u
     float *ib = lds + CP * pitch;     // [CP][pitch]: inter, then delta_v
     float *stg = ib + CP * pitch;     // SM: the staged block, then [C][NV] vectors of v
     const int nstage = a.off_stage1 - a.off_stage0;           // words (a multiple of 64)
-    typename Vec<T, V>::raw_t *vst = reinterpret_cast<typename Vec<T, V>::raw_t *>(stg + nstage);
+    raw_t *vst = reinterpret_cast<raw_t *>(stg + nstage);
+    // RB: [M][CW] elements of the bank slice, after v's vectors
+    T *lbank = reinterpret_cast<T *>(reinterpret_cast<char *>(vst) + p2_vst_bytes(C, NV, V, int(sizeof(T))));
+    // the bank the gather and the DW work on: the slice in LDS (row stride CW) or in memory
+    T *bank = RB ? lbank : gbank;
+    const int bst = RB ? CW : hd;
+    const int32_t Mr = int32_t(a.M);
+    if constexpr (RB) {
+        for (int i = threadIdx.x; i < Mr * NV; i += BLOCK) {
+            const int row = i / NV, vq = i % NV;
+            if (vq < nvs) *reinterpret_cast<raw_t *>(lbank + row * CW + vq * V) =
+                Vec<T, V>::load_raw(at(gbank, uint32_t(row) * uint32_t(hd) + uint32_t(vq * V)));
+        }
+        // the first step's staging barrier orders these stores before any gather
+    }
 
     // MFMA tiles of this wave: (it, ct) dealt in a snake order over tiles sorted by it,
     // so that every wave gets a similar share of the triangular work.
@@ -398,8 +457,13 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             const float *gr = reinterpret_cast<const float *>(arr(a.off_gr));
             const int32_t *kid = reinterpret_cast<const int32_t *>(arr(a.off_kid));
             const int32_t *qid = reinterpret_cast<const int32_t *>(arr(a.off_qid));
-            gather_region<T, V, NV, BLOCK>(bank, hd, kid, gw, a.W, nl, col0, nvs, ub, pitch, wave, lane);
-            gather_region<T, V, NV, BLOCK>(bank, hd, qid, gr, a.R, nl, col0, nvs, ib, pitch, wave, lane);
+            // the write entries on the first nww waves, the read entries on the others
+            // (waves in proportion to W : R)
+            int nww = (NW * a.W + (a.W + a.R) / 2) / (a.W + a.R);
+            nww = nww < 1 ? 1 : (nww > NW - 1 ? NW - 1 : nww);
+            const bool wr = wave < nww;   // wave-uniform: one inlined copy of the gather
+            gather_region<T, V, NV, BLOCK>(bank, bst, wr ? kid : qid, wr ? gw : gr, wr ? a.W : a.R, nl, 0, nvs,
+                                           wr ? ub : ib, pitch, wr ? wave : wave - nww, wr ? nww : NW - nww, lane);
         }
         lds_barrier();
 
@@ -490,9 +554,9 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
 
         // ---- DW: one writer per written row. Groups with >= kHotMin members go to whole
         //      wavefronts (dw_big_group, from the list of their records); the others are
-        //      summed in token order by the NV lanes of their slice: lane (gs, vq) takes
-        //      group gb + u * GPI + gs of each batch, the first member rides in the group
-        //      record, the second loads with the bank row, the rest four at a time.
+        //      summed in token order by the NV lanes of their slice: lane (gs, vq) of slot u
+        //      takes group gb + u * NW * GPI + gs of each batch, the first member rides in
+        //      the group record, the second loads with the bank row, the rest four at a time.
         {
             int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
             asm volatile("" : "+v"(dlane));
@@ -503,36 +567,38 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             const int2 *mrec = reinterpret_cast<const int2 *>(arr(a.off_mrec));
             for (int32_t bi = wave; bi < nbig; bi += NW) {
                 const int4 rec = *at(brec, uint32_t(bi));
-                dw_big_group<T, V>(bank, hd, rec, mrec, ib, pitch, col0, nvs, dlane);
+                dw_big_group<T, V>(bank, bst, rec, mrec, ib, pitch, 0, nvs, dlane);
             }
             constexpr int GPI = kWave / NV;                       // groups per load instruction
             constexpr int kB = Cfg::kDwBatch;
             constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
             const int gs = dlane / NV, vq = dlane % NV;
             const bool vok = vq < nvs;
-            const uint32_t col = uint32_t(col0 + vq * V);
+            const uint32_t col = uint32_t(vq * V);
             // a record of a group with fewer than kHotMin members (slot -1: no group)
             auto small = [](const int4 &r) { return r.x >= 0 && ((r.y >> 16) & 0xFF) < kHotMin - 1; };
+            // slot u of a batch takes groups gb + u * NW * GPI + gs: the instructions of a batch
+            // are dealt to all waves first, so that a few groups still keep every wave busy
             int4 rec[kB];
 #pragma unroll
             for (int u = 0; u < kB; ++u) {
-                const int32_t g = wave * GPI * kB + u * GPI + gs;
+                const int32_t g = wave * GPI + u * NW * GPI + gs;
                 rec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(-1, 0, 0, 0);
             }
-            for (int32_t gb = wave * GPI * kB; gb < ng; gb += kStride) {
+            for (int32_t gb = wave * GPI; gb < ng; gb += kStride) {
                 typename Vec<T, V>::raw_t raw[kB];
                 int2 mr[kB];
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
                     if (!small(rec[u])) continue;
-                    if (vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col));
+                    if (vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col));
                     const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
                     mr[u] = n1 > 0 ? *at(mrec, uint32_t(m0 + 1)) : make_int2(0, 0);
                 }
                 int4 nrec[kB];
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
-                    const int32_t g = gb + kStride + u * GPI + gs;
+                    const int32_t g = gb + kStride + u * NW * GPI + gs;
                     nrec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(-1, 0, 0, 0);
                 }
 #pragma unroll
@@ -578,64 +644,78 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                             for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                         }
                     }
-                    if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(hd) + col), acc);
+                    if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
                 }
 #pragma unroll
                 for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
             }
         }
-        __syncthreads();   // the DW's bank stores are visible to the next step's gather
+        step_end_barrier<RB>();   // the DW's bank stores are visible to the next step's gather
+    }
+    if constexpr (RB) {
+        for (int i = threadIdx.x; i < Mr * NV; i += BLOCK) {
+            const int row = i / NV, vq = i % NV;
+            if (vq < nvs) *reinterpret_cast<raw_t *>(at(gbank, uint32_t(row) * uint32_t(hd) + uint32_t(vq * V))) =
+                *reinterpret_cast<const raw_t *>(lbank + row * CW + vq * V);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------
-template <typename T, int V, bool SM>
+template <typename T, int V, int MODE>
 static const void *p2_fn_nv(int nv) {
     switch (nv) {
-        case 1: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 1, SM>);
-        case 2: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 2, SM>);
-        case 4: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 4, SM>);
-        default: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 8, SM>);
+        case 1: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 1, MODE>);
+        case 2: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 2, MODE>);
+        case 4: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 4, MODE>);
+        default: return reinterpret_cast<const void *>(&phase2_kernel<T, V, 8, MODE>);
     }
 }
 
-template <bool SM>
-static const void *phase2_fn_s(int dtype, int V, int nv) {
-    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, SM>(nv) : p2_fn_nv<float, 1, SM>(nv);
-    return V == 8 ? p2_fn_nv<bf16, 8, SM>(nv) : p2_fn_nv<bf16, 1, SM>(nv);
+template <int MODE>
+static const void *phase2_fn_m(int dtype, int V, int nv) {
+    if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, MODE>(nv) : p2_fn_nv<float, 1, MODE>(nv);
+    return V == 8 ? p2_fn_nv<bf16, 8, MODE>(nv) : p2_fn_nv<bf16, 1, MODE>(nv);
 }
 
-static const void *phase2_fn(int dtype, int V, int nv, bool sm) {
-    return sm ? phase2_fn_s<true>(dtype, V, nv) : phase2_fn_s<false>(dtype, V, nv);
+static const void *phase2_fn(int dtype, int V, int nv, int mode) {
+    switch (mode) {
+        case kP2Global: return phase2_fn_m<kP2Global>(dtype, V, nv);
+        case kP2Staged: return phase2_fn_m<kP2Staged>(dtype, V, nv);
+        default: return phase2_fn_m<kP2Resident>(dtype, V, nv);
+    }
 }
 
 hipError_t phase2_prepare() {
     for (int dt = 0; dt < 2; ++dt)
         for (int V : {1, dt == 0 ? 4 : 8})
             for (int nv : {1, 2, 4, 8})
-                for (bool sm : {false, true}) {
-                    hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv, sm),
+                for (int mode : {kP2Global, kP2Staged, kP2Resident}) {
+                    hipError_t e = hipFuncSetAttribute(phase2_fn(dt, V, nv, mode),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
                     if (e != hipSuccess) return e;
                 }
     return hipSuccess;
 }
 
-// LDS of a Phase-2 workgroup: the two row regions, plus (staged) the chunk's Phase-2 block
-// and C x NV vectors of v.
-size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, bool staged) {
+// LDS of a Phase-2 workgroup: the two row regions; staged, the chunk's Phase-2 block and
+// C x NV vectors of v; resident, the M x NV vectors of the bank slice besides.
+size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M) {
     size_t b = size_t(2) * p2_rows(C) * p2_pitch(nv * V) * sizeof(float);
-    if (staged) b += size_t(L.off_stage1 - L.off_stage0) * 4 + size_t(C) * nv * V * es;
+    if (mode >= kP2Staged) b += size_t(L.off_stage1 - L.off_stage0) * 4 + size_t(p2_vst_bytes(C, nv, V, es));
+    if (mode == kP2Resident) b += size_t(M) * nv * V * es;
     return b;
 }
 
-// Whether the chunk's Phase-2 block is staged in LDS: it must fit the device's LDS, and
-// v's C x NV vectors one per thread.
-bool phase2_staged(const ChunkLayout &L, int C, int nv, int V, int es, int lds_limit) {
-    if (int64_t(C) * nv > kP2Block) return false;
-    return phase2_lds_bytes(L, C, nv, V, es, true) + 256 <= size_t(lds_limit);
+// The largest mode whose LDS fits the device (v's C x NV vectors staged one per thread).
+int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, int lds_limit) {
+    if (int64_t(C) * nv > kP2Block) return kP2Global;
+    if (M <= int64_t(lds_limit) && phase2_lds_bytes(L, C, nv, V, es, kP2Resident, M) + 256 <= size_t(lds_limit))
+        return kP2Resident;
+    if (phase2_lds_bytes(L, C, nv, V, es, kP2Staged, M) + 256 <= size_t(lds_limit)) return kP2Staged;
+    return kP2Global;
 }
 
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st) {
@@ -653,8 +733,8 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
     const int es = pb.dtype == 0 ? 4 : 2;
     const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
     void *args[] = {&a};
-    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv, g.staged), grid, block, args,
-                           phase2_lds_bytes(L, pb.C, g.nv, V, es, g.staged), st);
+    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv, g.mode), grid, block, args,
+                           phase2_lds_bytes(L, pb.C, g.nv, V, es, g.mode, pb.M), st);
 }
 
 }  // namespace sdm

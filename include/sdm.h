@@ -169,6 +169,28 @@ int sdm_chunk_mats(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slo
 int sdm_wy_solve(int64_t n, int32_t chunk, const float *A, const float *beta, const float *QK,
                  float *X, float *QX, const sdm_exec *exec);
 
+/*
+ * The launch plan sdm_fwd takes for these shapes on the current device, for reports and
+ * tuning (the results never depend on it). It assumes 16-byte aligned v, bank and out, as
+ * sdm_fwd does when it picks `vec`. Returns SDM_OK, or the error sdm_fwd would return for
+ * these shapes (SDM_ERR_SHAPE, SDM_ERR_RANGE, SDM_ERR_DTYPE), or SDM_ERR_HIP.
+ */
+typedef struct {
+    int32_t vec;               /* bank elements per vector access */
+    int32_t slice_vectors;     /* vectors per column slice of Phase 2 */
+    int32_t slices;            /* column slices per stream: Phase 2 runs streams * slices workgroups */
+    int32_t phase2_mode;       /* 0: Phase-2 arrays and bank rows read from memory; 1: the chunk's
+                                  Phase-2 block staged in LDS; 2: staged, and the workgroup's
+                                  column slice of the bank held in LDS for the whole call */
+    int32_t phase2_lds_bytes;  /* LDS per Phase-2 workgroup */
+    int32_t phase1_fused;      /* 1: Phase 1 and the solve run as one kernel, one workgroup per chunk */
+    int32_t lds_limit;         /* LDS bytes per workgroup the plan may use */
+    int32_t lds_default;       /* the device's default per-workgroup LDS limit */
+} sdm_plan;
+
+int sdm_fwd_plan(int32_t streams, int32_t tokens, int32_t chunk, int32_t W, int32_t R, int32_t head_dim,
+                 int64_t rows, int32_t dtype, sdm_plan *plan);
+
 /* Static text for an SDM_* code. */
 const char *sdm_error_string(int code);
 

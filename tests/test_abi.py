@@ -30,8 +30,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sdm_chunk_mats", "sdm_error_string", "sdm_fwd", "sdm_fwd_workspace_bytes",
-                                    "sdm_last_error", "sdm_wy_solve"]
+    assert declared_functions() == ["sdm_chunk_mats", "sdm_error_string", "sdm_fwd", "sdm_fwd_plan",
+                                    "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_wy_solve"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -159,3 +159,15 @@ def test_wy_solve_rejects(lib):
     assert f(4, 16, fake + 2, fake, fake, fake, fake, ctypes.byref(ex)) == ALIGN
     assert f(0, 16, None, None, None, None, None, ctypes.byref(ex)) == OK   # nothing to do
     assert f(4, 16, fake, fake, fake, fake, fake, None) == NULL
+
+
+def test_plan_rejects_before_any_device_query(lib):
+    from chunked_sparse_delta_amd import _Plan
+    f = lib.sdm_fwd_plan
+    f.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    pl = _Plan()
+    assert f(8, 2048, 64, 8, 8, 64, 4096, 1, None) == NULL
+    assert f(0, 2048, 64, 8, 8, 64, 4096, 1, ctypes.byref(pl)) == SHAPE
+    assert f(8, 2048, 8, 8, 8, 64, 4096, 1, ctypes.byref(pl)) == RANGE
+    assert f(8, 2048, 64, 8, 8, 64, 4096, 7, ctypes.byref(pl)) == DTYPE
+    assert f(8, 2048, 64, 8, 8, 64, 0, 1, ctypes.byref(pl)) == RANGE

@@ -203,12 +203,13 @@ def test_workload_4p_sampled_streams(gpu):
     small(P=2, T=100, C=48, hd=40, M=80, W=5, R=3, ids="zipf", index=28),
 ], ids=["bf16_P8", "f32_P3", "f32_partial_slice"])
 def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
-    """The column slicing and the LDS staging change only the schedule: every geometry gives the same
-    bits (the gather, matmul and DW sums run in orders fixed by W, R and C)."""
+    """The column slicing, the LDS staging and the LDS-resident bank slice change only the schedule:
+    every geometry gives the same bits (the gather, matmul and DW sums run in orders fixed by W, R
+    and C, and a resident bank row is held in the bank dtype, rounded where memory would round it)."""
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
     results = []
-    for geom in (None, "1", "2", "4", "8", "1,0", "8,0"):
+    for geom in (None, "1", "2", "4", "8", "1,1", "8,1", "1,0", "8,0"):
         if geom is None:
             monkeypatch.delenv("SDM_P2_GEOM", raising=False)
         else:
@@ -218,6 +219,19 @@ def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
     gu.parity(o, b, inp, wl.C, "geometry")
     for geom, ob, bb in results[1:]:
         assert np.array_equal(ob, results[0][1]) and np.array_equal(bb, results[0][2]), geom
+
+
+def test_plan_reports_phase2_modes(gpu, monkeypatch):
+    """The plan query follows the mode cap of the tuning override, and the headline shape
+    (C=64, hd=64 bf16, 4096 rows, W=R=8) keeps its bank slice resident in LDS."""
+    from chunked_sparse_delta_amd import plan
+    monkeypatch.delenv("SDM_P2_GEOM", raising=False)
+    p = plan(8, 2048, 64, 8, 8, 64, 4096, torch.bfloat16)
+    assert p["phase2_mode"] == "resident" and p["phase2_lds_bytes"] <= p["lds_limit"], p
+    for cap, mode in (("1,1", "staged"), ("1,0", "memory")):
+        monkeypatch.setenv("SDM_P2_GEOM", cap)
+        q = plan(8, 2048, 64, 8, 8, 64, 4096, torch.bfloat16)
+        assert q["phase2_mode"] == mode and q["slice_vectors"] == 1, q
 
 
 @pytest.mark.parametrize("wl", [
