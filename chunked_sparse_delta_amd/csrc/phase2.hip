@@ -165,10 +165,13 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
 // group of TPI = 8 / NV tokens). Instruction j of a token group loads entries 8 j + r.
 // The wave walks its token groups (wave, wave + NW, ...) as one flat list of
 // instructions, kBatch at a time. The calling waves are wave = 0 .. nw - 1 of the region.
-template <typename T, int V, int NV, int BLOCK>
+// UFT && uf: the sums are the write entries' retrieved rows, and u = beta (v - retrieved)
+// is stored in their place (v from vsrc[t * NV + vq], beta from beta[t]).
+template <typename T, int V, int NV, int BLOCK, bool UFT>
 __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
                                               int nl, int col0, int nvs, float *dst, int pitch, int wave, int nw,
-                                              int lane) {
+                                              int lane, bool uf, const typename Vec<T, V>::raw_t *vsrc,
+                                              const float *beta) {
     constexpr int TPI = 8 / NV;
     constexpr int kBatch = P2Cfg<BLOCK, V>::kBatch;
     const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
@@ -223,7 +226,18 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
             if (cj == NI - 1) {
                 combine_classes<V, NV>(acc);
                 const int t = (wave + ck * nw) * TPI + ts;
-                if (r == 0 && t < nl && vok) lds_store_vec<V>(dst + t * pitch + vq * V, acc);
+                if (r == 0 && t < nl && vok) {
+                    if constexpr (UFT) {
+                        if (uf) {   // u = beta (v - retrieved), as the separate u pass computes it
+                            float vv[V];
+                            Vec<T, V>::unpack(vsrc[t * NV + vq], vv);
+                            const float b = beta[t];
+#pragma unroll
+                            for (int c = 0; c < V; ++c) acc[c] = b * (vv[c] - acc[c]);
+                        }
+                    }
+                    lds_store_vec<V>(dst + t * pitch + vq * V, acc);
+                }
 #pragma unroll
                 for (int c = 0; c < V; ++c) acc[c] = 0.0f;
                 cj = 0;
@@ -381,11 +395,17 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     T *gbank = static_cast<T *>(a.bank) + int64_t(p) * a.M * hd + col0;   // this slice, row stride hd
     const bool vec4 = (C & 3) == 0;
 
-    float *ub = lds;                  // [CP][pitch]: retrieved, then u
-    float *ib = lds + CP * pitch;     // [CP][pitch]: inter, then delta_v
-    float *stg = ib + CP * pitch;     // SM: the staged block, then [C][NV] vectors of v
+    float *ub = lds;                  // [CP][pitch]: u (retrieved first, without staging)
+    float *ib = lds + CP * pitch;     // [CP][pitch]: inter (without staging, then delta_v)
+    float *db = SM ? ib + CP * pitch : ib;   // [CP][pitch]: delta_v
+    float *stg = ib + (SM ? 2 : 1) * CP * pitch;   // SM: the staged block, then [C][NV] vectors of v
     const int nstage = a.off_stage1 - a.off_stage0;           // words (a multiple of 64)
+    const int nu = nstage >> 2;                               // 16-byte units of the staged block
     raw_t *vst = reinterpret_cast<raw_t *>(stg + nstage);
+    // Prefetch (SM, a staged block of at most one round of kStageUnits units per thread):
+    // the next step's block and vector of v are loaded into registers during this step's
+    // DW, and stored to LDS after its final barrier.
+    const bool pf = SM && nu <= BLOCK * kStageUnits;
     // RB: [M][CW] elements of the bank slice, after v's vectors
     T *lbank = reinterpret_cast<T *>(reinterpret_cast<char *>(vst) + p2_vst_bytes(C, NV, V, int(sizeof(T))));
     // the bank the gather and the DW work on: the slice in LDS (row stride CW) or in memory
@@ -427,9 +447,9 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         const T *vin = static_cast<const T *>(a.v) + tok0 * hd;     // this chunk's rows of v and out
         T *out = static_cast<T *>(a.out) + tok0 * hd;
         if constexpr (SM) {
+          uint4 *dst = reinterpret_cast<uint4 *>(stg);
+          if (s == 0 || !pf) {   // otherwise the previous step has stored this one's block
             const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.off_stage0);
-            uint4 *dst = reinterpret_cast<uint4 *>(stg);
-            const int nu = nstage >> 2;
             typename Vec<T, V>::raw_t vr;
             const int vt = tid / NV, vv = tid % NV;
             const bool vok = tid < C * NV && vt < rows && vv < nvs;
@@ -448,11 +468,20 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 if (u0 + 3 * BLOCK < nu) dst[u0 + 3 * BLOCK] = t3;
             }
             if (vok) vst[tid] = vr;
+          }
             lds_barrier();
+            // u rows of padding tokens and rows C..CP-1: +0 (the gather writes rows < nl)
+            for (int i = tid; i < (CP - nl) * NV; i += BLOCK) {
+                float z[V];
+#pragma unroll
+                for (int c = 0; c < V; ++c) z[c] = 0.0f;
+                lds_store_vec<V>(ub + (nl + i / NV) * pitch + (i % NV) * V, z);
+            }
         }
 
-        // ---- gather: retrieved -> ub, inter -> ib (live tokens)
+        // ---- gather: u (staged; retrieved otherwise) -> ub, inter -> ib (live tokens)
         {
+            const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
             const float *gw = reinterpret_cast<const float *>(arr(a.off_gw));
             const float *gr = reinterpret_cast<const float *>(arr(a.off_gr));
             const int32_t *kid = reinterpret_cast<const int32_t *>(arr(a.off_kid));
@@ -462,12 +491,15 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             int nww = (NW * a.W + (a.W + a.R) / 2) / (a.W + a.R);
             nww = nww < 1 ? 1 : (nww > NW - 1 ? NW - 1 : nww);
             const bool wr = wave < nww;   // wave-uniform: one inlined copy of the gather
-            gather_region<T, V, NV, BLOCK>(bank, bst, wr ? kid : qid, wr ? gw : gr, wr ? a.W : a.R, nl, 0, nvs,
-                                           wr ? ub : ib, pitch, wr ? wave : wave - nww, wr ? nww : NW - nww, lane);
+            gather_region<T, V, NV, BLOCK, SM>(bank, bst, wr ? kid : qid, wr ? gw : gr, wr ? a.W : a.R, nl, 0, nvs,
+                                               wr ? ub : ib, pitch, wr ? wave : wave - nww, wr ? nww : NW - nww, lane,
+                                               wr, vst, beta_c);
         }
         lds_barrier();
 
-        // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1
+        // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1 (without
+        //      staging; staged, the gather has done it)
+        if constexpr (!SM) {
         const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
 #pragma unroll
         for (int x = 0; x < Cfg::kUItems; ++x) {
@@ -477,8 +509,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             float uu[V];
             if (t < nl && vq < nvs) {
                 float vv[V], rr[V];
-                if constexpr (SM) Vec<T, V>::unpack(vst[t * NV + vq], vv);
-                else Vec<T, V>::load(at(vin, uint32_t(t * hd + col0 + vq * V)), vv);
+                Vec<T, V>::load(at(vin, uint32_t(t * hd + col0 + vq * V)), vv);
                 const float b = beta_c[t];
                 lds_load_vec<V>(ur, rr);
 #pragma unroll
@@ -490,15 +521,15 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             lds_store_vec<V>(ur, uu);
         }
         lds_barrier();
+        }
 
-        // ---- dual matmul on the matrix cores
+        // ---- dual matmul on the matrix cores: readings to memory, delta_v to db
         asm volatile("" : "+v"(lane));
         const float *QX = reinterpret_cast<const float *>(arr(a.off_QX));
         const float *X = reinterpret_cast<const float *>(arr(a.off_X));
-        f32x4 dacc[Cfg::kMaxTiles];
+        [[maybe_unused]] f32x4 dacc[Cfg::kMaxTiles];   // without staging: delta_v until inter is read
 #pragma unroll
         for (int q = 0; q < Cfg::kMaxTiles; ++q) {
-            dacc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
             if (tau >= NT) continue;
             const int it = tau / NCT, ct = tau - it * NCT;
@@ -533,24 +564,47 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                     }
                 }
             }
-            dacc[q] = d;
+            if constexpr (SM) {
+                if (ti_row < C && co < cwv) *reinterpret_cast<float4 *>(db + ti_row * pitch + co) = make_float4(d[0], d[1], d[2], d[3]);
+            } else {
+                dacc[q] = d;
+            }
             if (ti_row < rows && co < cwv) {
                 if (ti_row >= nl) y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 store_out4<T>(at(out, uint32_t(ti_row * hd + col0 + co)), y, min(4, cwv - co));
             }
         }
         lds_barrier();
-        // delta_v -> ib
+        if constexpr (!SM) {   // delta_v over inter, now that every tile has read it
 #pragma unroll
-        for (int q = 0; q < Cfg::kMaxTiles; ++q) {
-            const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
-            if (tau >= NT) continue;
-            const int it = tau / NCT, ct = tau - it * NCT;
-            const int ti_row = 16 * it + (lane & 15), co = 16 * ct + 4 * (lane >> 4);
-            if (ti_row < C && co < cwv)
-                *reinterpret_cast<float4 *>(ib + ti_row * pitch + co) = make_float4(dacc[q][0], dacc[q][1], dacc[q][2], dacc[q][3]);
+            for (int q = 0; q < Cfg::kMaxTiles; ++q) {
+                const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
+                if (tau >= NT) continue;
+                const int it = tau / NCT, ct = tau - it * NCT;
+                const int ti_row = 16 * it + (lane & 15), co = 16 * ct + 4 * (lane >> 4);
+                if (ti_row < C && co < cwv)
+                    *reinterpret_cast<float4 *>(db + ti_row * pitch + co) = make_float4(dacc[q][0], dacc[q][1], dacc[q][2], dacc[q][3]);
+            }
+            lds_barrier();
         }
-        lds_barrier();
+
+        // the next step's staged block and vector of v, loaded under the DW
+        const bool pfn = pf && s + 1 < a.steps;
+        uint4 pf0, pf1, pf2, pf3;
+        raw_t pfv;
+        bool pfvok = false;
+        if constexpr (SM) {
+            if (pfn) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.words + a.off_stage0);
+                if (tid < nu) pf0 = src[tid];
+                if (tid + BLOCK < nu) pf1 = src[tid + BLOCK];
+                if (tid + 2 * BLOCK < nu) pf2 = src[tid + 2 * BLOCK];
+                if (tid + 3 * BLOCK < nu) pf3 = src[tid + 3 * BLOCK];
+                const int rows_n = min(C, a.T - (ti + 1) * C), vt = tid / NV, vv = tid % NV;
+                pfvok = tid < C * NV && vt < rows_n && vv < nvs;
+                if (pfvok) pfv = Vec<T, V>::load_raw(at(vin, uint32_t((C + vt) * hd + col0 + vv * V)));
+            }
+        }
 
         // ---- DW: one writer per written row. Groups with >= kHotMin members go to whole
         //      wavefronts (dw_big_group, from the list of their records); the others are
@@ -567,10 +621,10 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             const int2 *mrec = reinterpret_cast<const int2 *>(arr(a.off_mrec));
             for (int32_t bi = wave; bi < nbig; bi += NW) {
                 const int4 rec = *at(brec, uint32_t(bi));
-                dw_big_group<T, V>(bank, bst, rec, mrec, ib, pitch, 0, nvs, dlane);
+                dw_big_group<T, V>(bank, bst, rec, mrec, db, pitch, 0, nvs, dlane);
             }
             constexpr int GPI = kWave / NV;                       // groups per load instruction
-            constexpr int kB = Cfg::kDwBatch;
+            constexpr int kB = SM ? 2 : Cfg::kDwBatch;   // staged: room for the prefetch registers
             constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
             const int gs = dlane / NV, vq = dlane % NV;
             const bool vok = vq < nvs;
@@ -618,14 +672,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                     {
                         const float cwv = __int_as_float(rec[u].w);
                         float dv[V];
-                        lds_load_vec<V>(ib + t0 * pitch + vq * V, dv);
+                        lds_load_vec<V>(db + t0 * pitch + vq * V, dv);
 #pragma unroll
                         for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                     }
                     if (n1 > 0) {
                         const float cwv = __int_as_float(mr[u].y);
                         float dv[V];
-                        lds_load_vec<V>(ib + mr[u].x * pitch + vq * V, dv);
+                        lds_load_vec<V>(db + mr[u].x * pitch + vq * V, dv);
 #pragma unroll
                         for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                     }
@@ -639,7 +693,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                             if (m + q > m0 + n1) break;
                             const float cwv = __int_as_float(mb[q].y);
                             float dv[V];
-                            lds_load_vec<V>(ib + mb[q].x * pitch + vq * V, dv);
+                            lds_load_vec<V>(db + mb[q].x * pitch + vq * V, dv);
 #pragma unroll
                             for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                         }
@@ -651,6 +705,16 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             }
         }
         step_end_barrier<RB>();   // the DW's bank stores are visible to the next step's gather
+        if constexpr (SM) {
+            if (pfn) {   // the DW has read its records: the next step's block takes their place
+                uint4 *dst = reinterpret_cast<uint4 *>(stg);
+                if (tid < nu) dst[tid] = pf0;
+                if (tid + BLOCK < nu) dst[tid + BLOCK] = pf1;
+                if (tid + 2 * BLOCK < nu) dst[tid + 2 * BLOCK] = pf2;
+                if (tid + 3 * BLOCK < nu) dst[tid + 3 * BLOCK] = pf3;
+                if (pfvok) vst[tid] = pfv;
+            }
+        }
     }
     if constexpr (RB) {
         for (int i = threadIdx.x; i < Mr * NV; i += BLOCK) {
@@ -700,10 +764,10 @@ hipError_t phase2_prepare() {
     return hipSuccess;
 }
 
-// LDS of a Phase-2 workgroup: the two row regions; staged, the chunk's Phase-2 block and
+// LDS of a Phase-2 workgroup: the row regions (u, inter; staged, delta_v too); staged, the chunk's Phase-2 block and
 // C x NV vectors of v; resident, the M x NV vectors of the bank slice besides.
 size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M) {
-    size_t b = size_t(2) * p2_rows(C) * p2_pitch(nv * V) * sizeof(float);
+    size_t b = size_t(mode >= kP2Staged ? 3 : 2) * p2_rows(C) * p2_pitch(nv * V) * sizeof(float);
     if (mode >= kP2Staged) b += size_t(L.off_stage1 - L.off_stage0) * 4 + size_t(p2_vst_bytes(C, nv, V, es));
     if (mode == kP2Resident) b += size_t(M) * nv * V * es;
     return b;
