@@ -30,6 +30,8 @@
 //           and the classes combine as ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7));
 //   matmul  16-wide k blocks ascending, each one MFMA chain of four k-steps;
 //   DW      decay term first, then the group's members in token order.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sdm {
@@ -164,16 +166,16 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
 // vector of the slice), class r = (lane / NV) % 8, ts = lane / (8 NV) (the token within a
 // group of TPI = 8 / NV tokens). Instruction j of a token group loads entries 8 j + r.
 // The wave walks its token groups (wave, wave + NW, ...) as one flat list of
-// instructions, kBatch at a time. The calling waves are wave = 0 .. nw - 1 of the region.
+// instructions, kBatch at a time (the next batch's ids and weights load under the current
+// batch's rows). The calling waves are wave = 0 .. nw - 1 of the region.
 // UFT && uf: the sums are the write entries' retrieved rows, and u = beta (v - retrieved)
 // is stored in their place (v from vsrc[t * NV + vq], beta from beta[t]).
-template <typename T, int V, int NV, int BLOCK, bool UFT>
+template <typename T, int V, int NV, int kBatch, bool UFT>
 __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
                                               int nl, int col0, int nvs, float *dst, int pitch, int wave, int nw,
                                               int lane, bool uf, const typename Vec<T, V>::raw_t *vsrc,
                                               const float *beta) {
     constexpr int TPI = 8 / NV;
-    constexpr int kBatch = P2Cfg<BLOCK, V>::kBatch;
     const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
     const int NI = (width + 7) >> 3;
     const int NG = (nl + TPI - 1) / TPI;
@@ -275,15 +277,31 @@ __device__ __forceinline__ void store_out4(T *p, const f32x4 &y, int n) {
 }
 
 // The B operand of one 16 x 16 x 16 block: lane l holds M[i0 + (l & 15)][k0 + 4 (l >> 4) + kk]
-// for kk = 0..3 (0 outside the C x C matrix).
+// for kk = 0..3 (0 outside the C x C matrix). FULL: C is a multiple of 16, so every lane's
+// four elements are inside the matrix and 16-byte aligned.
+template <bool FULL>
 __device__ __forceinline__ void load_bop(const float *M, int C, int i, int k, bool vec4, float (&b)[4]) {
-    if (i < C && k + 3 < C && vec4) {
+    if constexpr (FULL) {
+        const float4 x = *reinterpret_cast<const float4 *>(M + i * C + k);
+        b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
+    } else if (i < C && k + 3 < C && vec4) {
         const float4 x = *reinterpret_cast<const float4 *>(M + int64_t(i) * C + k);
         b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
     } else {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) b[kk] = (i < C && k + kk < C) ? M[int64_t(i) * C + k + kk] : 0.0f;
     }
+}
+
+// The A operand of one 16 x 16 x 16 block: lane l holds u[k0 + 4 (l >> 4) + kk][c0 + (l & 15)]
+// for kk = 0..3, or 0 for a column outside the slice (ok false). The four loads are
+// unconditional, so that they issue together: a column past the slice reads inside the
+// next row, or for the last row a few words into the LDS region after u.
+__device__ __forceinline__ void load_aop(const float *p, int pitch, bool ok, float (&a)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk] = p[kk * pitch];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk] = ok ? a[kk] : 0.0f;
 }
 
 // DW of one group with many members (>= kHotMin) by a whole wavefront: lane (r, p) =
@@ -393,7 +411,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     const int col0 = vq0 * V;
     using raw_t = typename Vec<T, V>::raw_t;
     T *gbank = static_cast<T *>(a.bank) + int64_t(p) * a.M * hd + col0;   // this slice, row stride hd
-    const bool vec4 = (C & 3) == 0;
+    const bool vec4 = (C & 3) == 0, full = (C & 15) == 0;
 
     float *ub = lds;                  // [CP][pitch]: u (retrieved first, without staging)
     float *ib = lds + CP * pitch;     // [CP][pitch]: inter (without staging, then delta_v)
@@ -491,7 +509,10 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             int nww = (NW * a.W + (a.W + a.R) / 2) / (a.W + a.R);
             nww = nww < 1 ? 1 : (nww > NW - 1 ? NW - 1 : nww);
             const bool wr = wave < nww;   // wave-uniform: one inlined copy of the gather
-            gather_region<T, V, NV, BLOCK, SM>(bank, bst, wr ? kid : qid, wr ? gw : gr, wr ? a.W : a.R, nl, 0, nvs,
+            // rows from memory: kBatch loads in flight per lane; from LDS one at a time (the
+            // predicated slots of a deep batch cost more than LDS latency when a wave has
+            // one or two instructions of work)
+            gather_region<T, V, NV, RB ? 1 : Cfg::kBatch, SM>(bank, bst, wr ? kid : qid, wr ? gw : gr, wr ? a.W : a.R, nl, 0, nvs,
                                                wr ? ub : ib, pitch, wr ? wave : wave - nww, wr ? nww : NW - nww, lane,
                                                wr, vst, beta_c);
         }
@@ -527,7 +548,55 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         asm volatile("" : "+v"(lane));
         const float *QX = reinterpret_cast<const float *>(arr(a.off_QX));
         const float *X = reinterpret_cast<const float *>(arr(a.off_X));
-        [[maybe_unused]] f32x4 dacc[Cfg::kMaxTiles];   // without staging: delta_v until inter is read
+        [[maybe_unused]] f32x4 dacc[SM ? 1 : Cfg::kMaxTiles];   // memory mode: delta_v until inter is read
+        // FULL (C a multiple of 16) is decided once per step, for straight-line operand loads
+        auto matmul = [&](auto fullc) {
+        constexpr bool FULL = decltype(fullc)::value;
+        if constexpr (SM) {
+            // Staged: each tile's two products are separate items, y0 .. y(NT-1) then
+            // d(NT-1) .. d0, dealt to waves in turn, so that a heavy readings tile shares a
+            // SIMD with a light delta tile. Each item runs the same MFMA chain as below.
+            const int NI2 = 2 * NT;
+            for (int iota = wave; iota < NI2; iota += NW) {
+                const bool isy = iota < NT;
+                const int tau = isy ? iota : NI2 - 1 - iota;
+                const int it = tau / NCT, ct = tau - it * NCT;
+                const int ti_row = 16 * it + (lane & 15);
+                const int cu = 16 * ct + (lane & 15);
+                const int co = 16 * ct + 4 * (lane >> 4);
+                const int ko = 4 * (lane >> 4);
+                const float *Bm = isy ? QX : X;
+                f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (isy && co < cwv) {
+                    const float4 iv = *reinterpret_cast<const float4 *>(ib + ti_row * pitch + co);
+                    y = f32x4{iv.x, iv.y, iv.z, iv.w};
+                }
+                for (int kb = 0; kb <= it; kb += Cfg::kMmDepth) {
+                    float bm[Cfg::kMmDepth][4], av[Cfg::kMmDepth][4];
+#pragma unroll
+                    for (int j = 0; j < Cfg::kMmDepth; ++j) {
+                        if (kb + j > it) continue;
+                        load_bop<FULL>(Bm, C, ti_row, 16 * (kb + j) + ko, vec4, bm[j]);
+                        load_aop(ub + (16 * (kb + j) + ko) * pitch + cu, pitch, cu < cwv, av[j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < Cfg::kMmDepth; ++j) {
+                        if (kb + j > it) continue;
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][kk], bm[j][kk], y, 0, 0, 0);
+                    }
+                }
+                if (isy) {
+                    if (ti_row < rows && co < cwv) {
+                        if (ti_row >= nl) y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        store_out4<T>(at(out, uint32_t(ti_row * hd + col0 + co)), y, min(4, cwv - co));
+                    }
+                } else if (ti_row < C && co < cwv) {
+                    *reinterpret_cast<float4 *>(db + ti_row * pitch + co) = make_float4(y[0], y[1], y[2], y[3]);
+                }
+            }
+        } else {
 #pragma unroll
         for (int q = 0; q < Cfg::kMaxTiles; ++q) {
             const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
@@ -545,35 +614,34 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             // k blocks kMmDepth at a time: the operands of those blocks are loaded together
             for (int kb = 0; kb <= it; kb += Cfg::kMmDepth) {
-                float bq[Cfg::kMmDepth][4], bx[Cfg::kMmDepth][4];
+                float bq[Cfg::kMmDepth][4], bx[Cfg::kMmDepth][4], av[Cfg::kMmDepth][4];
 #pragma unroll
                 for (int j = 0; j < Cfg::kMmDepth; ++j) {
                     if (kb + j > it) continue;
-                    load_bop(QX, C, ti_row, 16 * (kb + j) + ko, vec4, bq[j]);
-                    load_bop(X, C, ti_row, 16 * (kb + j) + ko, vec4, bx[j]);
+                    load_bop<FULL>(QX, C, ti_row, 16 * (kb + j) + ko, vec4, bq[j]);
+                    load_bop<FULL>(X, C, ti_row, 16 * (kb + j) + ko, vec4, bx[j]);
+                    load_aop(ub + (16 * (kb + j) + ko) * pitch + cu, pitch, cu < cwv, av[j]);
                 }
 #pragma unroll
                 for (int j = 0; j < Cfg::kMmDepth; ++j) {
                     if (kb + j > it) continue;
-                    const float *urow = ub + (16 * (kb + j) + ko) * pitch + cu;
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const float av = cu < cwv ? urow[kk * pitch] : 0.0f;
-                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bq[j][kk], y, 0, 0, 0);
-                        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bx[j][kk], d, 0, 0, 0);
+                        y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][kk], bq[j][kk], y, 0, 0, 0);
+                        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][kk], bx[j][kk], d, 0, 0, 0);
                     }
                 }
             }
-            if constexpr (SM) {
-                if (ti_row < C && co < cwv) *reinterpret_cast<float4 *>(db + ti_row * pitch + co) = make_float4(d[0], d[1], d[2], d[3]);
-            } else {
-                dacc[q] = d;
-            }
+            dacc[q] = d;
             if (ti_row < rows && co < cwv) {
                 if (ti_row >= nl) y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 store_out4<T>(at(out, uint32_t(ti_row * hd + col0 + co)), y, min(4, cwv - co));
             }
         }
+        }
+        };
+        if (full) matmul(std::true_type{});
+        else matmul(std::false_type{});
         lds_barrier();
         if constexpr (!SM) {   // delta_v over inter, now that every tile has read it
 #pragma unroll
@@ -624,7 +692,9 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 dw_big_group<T, V>(bank, bst, rec, mrec, db, pitch, 0, nvs, dlane);
             }
             constexpr int GPI = kWave / NV;                       // groups per load instruction
-            constexpr int kB = SM ? 2 : Cfg::kDwBatch;   // staged: room for the prefetch registers
+            // groups per lane in flight: the bank in LDS needs no batching; staged, two leave
+            // room for the prefetch registers
+            constexpr int kB = RB ? 1 : (SM ? 2 : Cfg::kDwBatch);
             constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
             const int gs = dlane / NV, vq = dlane % NV;
             const bool vok = vq < nvs;
