@@ -26,7 +26,8 @@
 //
 // Determinism: each output element has exactly one writer, and every sum runs in an order
 // fixed by the shapes W, R and C only (never by the slicing or the launch):
-//   gather  token t's entries e are summed per class e % 8 in ascending e (one fmaf chain),
+//   gather  token t's entries are split into eight classes of consecutive entries (class r:
+//           entries r ceil(W/8) ..), each summed in ascending order (one fmaf chain),
 //           and the classes combine as ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7));
 //   matmul  16-wide k blocks ascending, each one MFMA chain of four k-steps;
 //   DW      decay term first, then the group's members in token order.
@@ -164,44 +165,61 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
 // Weighted row sums of one region (the write entries or the read entries) for the live
 // tokens of the chunk, into dst[t * pitch + vq * V + c]. Lane layout: vq = lane % NV (the
 // vector of the slice), class r = (lane / NV) % 8, ts = lane / (8 NV) (the token within a
-// group of TPI = 8 / NV tokens). Instruction j of a token group loads entries 8 j + r.
-// The wave walks its token groups (wave, wave + NW, ...) as one flat list of
-// instructions, kBatch at a time (the next batch's ids and weights load under the current
-// batch's rows). The calling waves are wave = 0 .. nw - 1 of the region.
+// group of TPI = 8 / NV tokens). Class r owns the run of entries r NI .. r NI + NI - 1 of
+// its token (NI = ceil(width / 8); entries past width are empty) and sums them in
+// ascending order. A slot is Q consecutive entries of a class run, one id / weight load
+// of Q elements (Q = 4 needs width % 32 == 0, so that every run is a whole number of
+// 16-byte aligned quads); a token group takes NI / Q slots. The wave walks its token
+// groups (wave, wave + nw, ...) as one flat list of slots, kBatch at a time (the next
+// batch's ids and weights load under the current batch's rows). The calling waves are
+// wave = 0 .. nw - 1 of the region.
 // UFT && uf: the sums are the write entries' retrieved rows, and u = beta (v - retrieved)
 // is stored in their place (v from vsrc[t * NV + vq], beta from beta[t]).
-template <typename T, int V, int NV, int kBatch, bool UFT>
+template <typename T, int V, int NV, int kBatch, int Q, bool UFT>
 __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
                                               int nl, int col0, int nvs, float *dst, int pitch, int wave, int nw,
                                               int lane, bool uf, const typename Vec<T, V>::raw_t *vsrc,
                                               const float *beta) {
+    static_assert(Q == 1 || Q == 4, "one or four entries per id load");
     constexpr int TPI = 8 / NV;
     const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
     const int NI = (width + 7) >> 3;
+    const int NS = Q == 1 ? NI : NI >> 2;     // slots per token group
     const int NG = (nl + TPI - 1) / TPI;
     const int ngw = NG > wave ? (NG - wave + nw - 1) / nw : 0;
-    const int total = ngw * NI;
+    const int total = ngw * NS;
     if (total == 0) return;
     const bool vok = vq < nvs;
     const uint32_t col = uint32_t(col0 + vq * V);
 
-    // (k, j) of the first instruction of the next batch whose pairs are to be loaded
+    // (k, j) of the first slot of the next batch whose pairs are to be loaded
     int pk = 0, pj = 0;
-    int32_t id[kBatch], nid[kBatch];
-    float wt[kBatch], nwt[kBatch];
-    auto load_pairs = [&](int32_t (&di)[kBatch], float (&dw)[kBatch]) {
+    int32_t id[kBatch][Q], nid[kBatch][Q];
+    float wt[kBatch][Q], nwt[kBatch][Q];
+    // Every load below is issued unconditionally (an unused slot reads entry 0, row 0 or the
+    // slice's first vector, all in bounds), so that the compiler can count the loads in
+    // flight exactly; a load under a branch makes it wait for all of them.
+    auto load_pairs = [&](int32_t (&di)[kBatch][Q], float (&dw)[kBatch][Q]) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            di[u] = -1;
-            dw[u] = 0.0f;
-            if (pk < ngw) {
-                const int t = (wave + pk * nw) * TPI + ts, e = 8 * pj + r;
-                if (t < nl && e < width) {
-                    di[u] = *at(ids, uint32_t(t * width + e));
-                    dw[u] = *at(wts, uint32_t(t * width + e));
-                }
+            const int t = (wave + pk * nw) * TPI + ts, e = r * NI + Q * pj;
+            if constexpr (Q == 1) {
+                const bool ok = pk < ngw && t < nl && e < width;
+                const uint32_t x = ok ? uint32_t(t * width + e) : 0u;
+                const int32_t iv = *at(ids, x);
+                const float wv = *at(wts, x);
+                di[u][0] = ok ? iv : -1;
+                dw[u][0] = ok ? wv : 0.0f;
+            } else {
+                const bool ok = pk < ngw && t < nl;
+                const uint32_t x = ok ? uint32_t(t * width + e) : 0u;
+                const int4 iv = *reinterpret_cast<const int4 *>(at(ids, x));
+                const float4 wv = *reinterpret_cast<const float4 *>(at(wts, x));
+                di[u][0] = ok ? iv.x : -1; di[u][1] = ok ? iv.y : -1;
+                di[u][2] = ok ? iv.z : -1; di[u][3] = ok ? iv.w : -1;
+                dw[u][0] = wv.x; dw[u][1] = wv.y; dw[u][2] = wv.z; dw[u][3] = wv.w;
             }
-            if (++pj == NI) { pj = 0; ++pk; }
+            if (++pj == NS) { pj = 0; ++pk; }
         }
     };
     load_pairs(id, wt);
@@ -209,23 +227,31 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
     float acc[V];
 #pragma unroll
     for (int c = 0; c < V; ++c) acc[c] = 0.0f;
-    int ck = 0, cj = 0;   // (k, j) of the instruction being consumed
+    int ck = 0, cj = 0;   // (k, j) of the slot being consumed
     for (int i0 = 0; i0 < total; i0 += kBatch) {
-        typename Vec<T, V>::raw_t raw[kBatch];
+        typename Vec<T, V>::raw_t raw[kBatch][Q];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-            if (id[u] >= 0 && vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(id[u]) * uint32_t(hd) + col));
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const bool ok = id[u][q] >= 0 && vok;
+                raw[u][q] = Vec<T, V>::load_raw(
+                    at(bank, uint32_t(ok ? id[u][q] : 0) * uint32_t(hd) + (vok ? col : uint32_t(col0))));
+            }
         load_pairs(nid, nwt);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             if (i0 + u >= total) continue;
-            if (id[u] >= 0 && vok) {
-                float row[V];
-                Vec<T, V>::unpack(raw[u], row);
 #pragma unroll
-                for (int c = 0; c < V; ++c) acc[c] = fmaf(wt[u], row[c], acc[c]);
+            for (int q = 0; q < Q; ++q) {
+                if (id[u][q] >= 0 && vok) {
+                    float row[V];
+                    Vec<T, V>::unpack(raw[u][q], row);
+#pragma unroll
+                    for (int c = 0; c < V; ++c) acc[c] = fmaf(wt[u][q], row[c], acc[c]);
+                }
             }
-            if (cj == NI - 1) {
+            if (cj == NS - 1) {
                 combine_classes<V, NV>(acc);
                 const int t = (wave + ck * nw) * TPI + ts;
                 if (r == 0 && t < nl && vok) {
@@ -249,10 +275,12 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
             }
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            id[u] = nid[u];
-            wt[u] = nwt[u];
-        }
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                id[u][q] = nid[u][q];
+                wt[u][q] = nwt[u][q];
+            }
     }
 }
 
@@ -316,16 +344,15 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
     const bool pok = p < nvs;
     const int32_t m0 = rec.y & 0xFFFF, n = ((rec.y >> 16) & 0xFF) + 1;
     const uint32_t col = uint32_t(col0 + p * V);
-    typename Vec<T, V>::raw_t raw;
-    if (pok) raw = Vec<T, V>::load_raw(at(bank, uint32_t(rec.x) * uint32_t(hd) + col));
+    // loads unconditional (in-bounds fallbacks), as in the gather
+    const typename Vec<T, V>::raw_t raw = Vec<T, V>::load_raw(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
     int32_t rt[4], rc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int m = lane + 64 * q;
-        int2 x = make_int2(0, 0);
-        if (m < n) x = *at(mrec, uint32_t(m0 + m));
-        rt[q] = x.x;
-        rc[q] = x.y;
+        const int2 x = *at(mrec, uint32_t(m0 + (m < n ? m : 0)));
+        rt[q] = m < n ? x.x : 0;
+        rc[q] = m < n ? x.y : 0;
     }
     float acc[V];
 #pragma unroll
@@ -468,18 +495,18 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
           uint4 *dst = reinterpret_cast<uint4 *>(stg);
           if (s == 0 || !pf) {   // otherwise the previous step has stored this one's block
             const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.off_stage0);
-            typename Vec<T, V>::raw_t vr;
             const int vt = tid / NV, vv = tid % NV;
             const bool vok = tid < C * NV && vt < rows && vv < nvs;
-            if (vok) vr = Vec<T, V>::load_raw(at(vin, uint32_t(vt * hd + col0 + vv * V)));
+            // unconditional loads (clamped in-bounds indices), as in the gather
+            const typename Vec<T, V>::raw_t vr =
+                Vec<T, V>::load_raw(at(vin, vok ? uint32_t(vt * hd + col0 + vv * V) : uint32_t(col0)));
             // rounds of kStageUnits 16-byte loads in flight per thread, then their stores
             for (int u0 = tid; u0 < nu; u0 += BLOCK * kStageUnits) {
-                uint4 t0, t1, t2, t3;
                 static_assert(kStageUnits == 4, "unrolled by hand");
-                if (u0 < nu) t0 = src[u0];
-                if (u0 + BLOCK < nu) t1 = src[u0 + BLOCK];
-                if (u0 + 2 * BLOCK < nu) t2 = src[u0 + 2 * BLOCK];
-                if (u0 + 3 * BLOCK < nu) t3 = src[u0 + 3 * BLOCK];
+                const uint4 t0 = src[u0];
+                const uint4 t1 = src[min(u0 + BLOCK, nu - 1)];
+                const uint4 t2 = src[min(u0 + 2 * BLOCK, nu - 1)];
+                const uint4 t3 = src[min(u0 + 3 * BLOCK, nu - 1)];
                 if (u0 < nu) dst[u0] = t0;
                 if (u0 + BLOCK < nu) dst[u0 + BLOCK] = t1;
                 if (u0 + 2 * BLOCK < nu) dst[u0 + 2 * BLOCK] = t2;
@@ -511,10 +538,18 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             const bool wr = wave < nww;   // wave-uniform: one inlined copy of the gather
             // rows from memory: kBatch loads in flight per lane; from LDS one at a time (the
             // predicated slots of a deep batch cost more than LDS latency when a wave has
-            // one or two instructions of work)
-            gather_region<T, V, NV, RB ? 1 : Cfg::kBatch, SM>(bank, bst, wr ? kid : qid, wr ? gw : gr, wr ? a.W : a.R, nl, 0, nvs,
-                                               wr ? ub : ib, pitch, wr ? wave : wave - nww, wr ? nww : NW - nww, lane,
-                                               wr, vst, beta_c);
+            // one or two instructions of work). Widths that are multiples of 32 load ids
+            // and weights four at a time.
+            const int32_t *rid = wr ? kid : qid;
+            const float *rwt = wr ? gw : gr;
+            const int rwidth = wr ? a.W : a.R, rwave = wr ? wave : wave - nww, rnw = wr ? nww : NW - nww;
+            float *rdst = wr ? ub : ib;
+            if (((a.W | a.R) & 31) == 0)
+                gather_region<T, V, NV, RB ? 1 : 2, 4, SM>(bank, bst, rid, rwt, rwidth, nl, 0, nvs, rdst, pitch,
+                                                          rwave, rnw, lane, wr, vst, beta_c);
+            else
+                gather_region<T, V, NV, RB ? 1 : Cfg::kBatch, 1, SM>(bank, bst, rid, rwt, rwidth, nl, 0, nvs, rdst,
+                                                                    pitch, rwave, rnw, lane, wr, vst, beta_c);
         }
         lds_barrier();
 
@@ -528,10 +563,12 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             if (t >= CP) continue;
             float *ur = ub + t * pitch + vq * V;
             float uu[V];
-            if (t < nl && vq < nvs) {
-                float vv[V], rr[V];
-                Vec<T, V>::load(at(vin, uint32_t(t * hd + col0 + vq * V)), vv);
-                const float b = beta_c[t];
+            const bool live = t < nl && vq < nvs;
+            float vv[V];   // unconditional load (in-bounds fallback), as in the gather
+            Vec<T, V>::load(at(vin, live ? uint32_t(t * hd + col0 + vq * V) : uint32_t(col0)), vv);
+            const float b = beta_c[live ? t : 0];
+            if (live) {
+                float rr[V];
                 lds_load_vec<V>(ur, rr);
 #pragma unroll
                 for (int c = 0; c < V; ++c) uu[c] = b * (vv[c] - rr[c]);
@@ -663,14 +700,15 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         bool pfvok = false;
         if constexpr (SM) {
             if (pfn) {
+                // unconditional loads (clamped in-bounds indices), as in the gather
                 const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.words + a.off_stage0);
-                if (tid < nu) pf0 = src[tid];
-                if (tid + BLOCK < nu) pf1 = src[tid + BLOCK];
-                if (tid + 2 * BLOCK < nu) pf2 = src[tid + 2 * BLOCK];
-                if (tid + 3 * BLOCK < nu) pf3 = src[tid + 3 * BLOCK];
+                pf0 = src[min(tid, nu - 1)];
+                pf1 = src[min(tid + BLOCK, nu - 1)];
+                pf2 = src[min(tid + 2 * BLOCK, nu - 1)];
+                pf3 = src[min(tid + 3 * BLOCK, nu - 1)];
                 const int rows_n = min(C, a.T - (ti + 1) * C), vt = tid / NV, vv = tid % NV;
                 pfvok = tid < C * NV && vt < rows_n && vv < nvs;
-                if (pfvok) pfv = Vec<T, V>::load_raw(at(vin, uint32_t((C + vt) * hd + col0 + vv * V)));
+                pfv = Vec<T, V>::load_raw(at(vin, pfvok ? uint32_t((C + vt) * hd + col0 + vv * V) : uint32_t(C * hd + col0)));
             }
         }
 
@@ -703,28 +741,29 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             auto small = [](const int4 &r) { return r.x >= 0 && ((r.y >> 16) & 0xFF) < kHotMin - 1; };
             // slot u of a batch takes groups gb + u * NW * GPI + gs: the instructions of a batch
             // are dealt to all waves first, so that a few groups still keep every wave busy
+            // loads unconditional (in-bounds fallbacks), as in the gather
+            auto load_rec = [&](int32_t g) {
+                const int4 x = *at(grec, uint32_t(g < ng ? g : 0));
+                return g < ng ? x : make_int4(-1, 0, 0, 0);
+            };
             int4 rec[kB];
 #pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const int32_t g = wave * GPI + u * NW * GPI + gs;
-                rec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(-1, 0, 0, 0);
-            }
+            for (int u = 0; u < kB; ++u) rec[u] = load_rec(wave * GPI + u * NW * GPI + gs);
             for (int32_t gb = wave * GPI; gb < ng; gb += kStride) {
                 typename Vec<T, V>::raw_t raw[kB];
                 int2 mr[kB];
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
-                    if (!small(rec[u])) continue;
-                    if (vok) raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col));
+                    const bool sm = small(rec[u]);
+                    raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
                     const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
-                    mr[u] = n1 > 0 ? *at(mrec, uint32_t(m0 + 1)) : make_int2(0, 0);
+                    const bool two = sm && n1 > 0;
+                    const int2 x = *at(mrec, uint32_t(two ? m0 + 1 : 0));
+                    mr[u] = two ? x : make_int2(0, 0);
                 }
                 int4 nrec[kB];
 #pragma unroll
-                for (int u = 0; u < kB; ++u) {
-                    const int32_t g = gb + kStride + u * NW * GPI + gs;
-                    nrec[u] = g < ng ? *at(grec, uint32_t(g)) : make_int4(-1, 0, 0, 0);
-                }
+                for (int u = 0; u < kB; ++u) nrec[u] = load_rec(gb + kStride + u * NW * GPI + gs);
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
                     if (!small(rec[u])) continue;
@@ -757,7 +796,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                     for (int32_t m = m0 + 2; m <= m0 + n1; m += 4) {
                         int2 mb[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) mb[q] = m + q <= m0 + n1 ? *at(mrec, uint32_t(m + q)) : make_int2(0, 0);
+                        for (int q = 0; q < 4; ++q) mb[q] = *at(mrec, uint32_t(min(m + q, m0 + n1)));
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             if (m + q > m0 + n1) break;
