@@ -42,7 +42,8 @@ class SdmError(RuntimeError):
 
 
 class _Slots(ctypes.Structure):
-    _fields_ = [("write", ctypes.c_void_p), ("read", ctypes.c_void_p), ("W", ctypes.c_int32), ("R", ctypes.c_int32)]
+    _fields_ = [("write", ctypes.c_void_p), ("read", ctypes.c_void_p), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("write_id_bytes", ctypes.c_int32), ("read_id_bytes", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -51,12 +52,15 @@ class _Weights(ctypes.Structure):
 
 class _Bank(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int64), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("shared", ctypes.c_int32)]
 
 
 class _Exec(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("events", ctypes.c_void_p), ("num_events", ctypes.c_int32)]
+                ("events", ctypes.c_void_p), ("num_events", ctypes.c_int32), ("repeated_writes", ctypes.c_void_p)]
+
+
+_ID_BYTES = {torch.int32: 4, torch.int64: 8}
 
 
 TIMING_EVENTS = 8   # SDM_TIMING_EVENTS
@@ -160,23 +164,34 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 DEFAULT_WORKSPACE_CAP = 8 << 30
 
 
-def _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, valid_tokens):
+def _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, valid_tokens, shared_bank=False):
     if bank.dtype not in _DTYPES:
         raise TypeError(f"bank must be float32 or bfloat16, got {bank.dtype}")
-    if bank.dim() != 3:
-        raise ValueError(f"bank must be [P, M, head_dim], got shape {tuple(bank.shape)}")
     if k_idx.dim() != 3 or q_idx.dim() != 3:
         raise ValueError("k_idx and q_idx must be [P, T, W] and [P, T, R]")
-    P, M, hd = bank.shape
-    T, W = k_idx.shape[1], k_idx.shape[2]
+    P, T, W = k_idx.shape
+    if bank.dim() == 2:   # one bank for every stream
+        if P > 1 and not shared_bank:
+            raise ValueError(f"{P} streams over one bank of {bank.shape[0]} slots: pass shared_bank=True to assert "
+                             "that the streams select disjoint slots for the whole call (not checked), or give "
+                             "each stream its own bank [P, M, head_dim]")
+        M, hd = bank.shape
+        shape = (M, hd)
+    elif bank.dim() == 3:
+        _, M, hd = bank.shape
+        shape = (P, M, hd)
+    else:
+        raise ValueError(f"bank must be [P, M, head_dim] or a shared [M, head_dim], got shape {tuple(bank.shape)}")
     R = q_idx.shape[2]
     G = log_decay.shape[-1] if log_decay.dim() == 3 else -1
     dev = bank.device
     if dev.type != "cuda":
         raise ValueError("bank must be a GPU tensor")
-    _expect(bank, "bank", (P, M, hd), bank.dtype, dev)
-    _expect(k_idx, "k_idx", (P, T, W), torch.int32, dev)
-    _expect(q_idx, "q_idx", (P, T, R), torch.int32, dev)
+    _expect(bank, "bank", shape, bank.dtype, dev)
+    for t, name, shp in ((k_idx, "k_idx", (P, T, W)), (q_idx, "q_idx", (P, T, R))):
+        if t.dtype not in _ID_BYTES:
+            raise TypeError(f"{name} must be int32 or int64, got {t.dtype}")
+        _expect(t, name, shp, t.dtype, dev)
     _expect(k_val, "k_val", (P, T, W), bank.dtype, dev)
     _expect(q_val, "q_val", (P, T, R), bank.dtype, dev)
     _expect(v, "v", (P, T, hd), bank.dtype, dev)
@@ -184,7 +199,7 @@ def _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, valid_tokens):
     _expect(log_decay, "log_decay", (P, T, G), torch.float32, dev)
     if valid_tokens is not None:
         _expect(valid_tokens, "valid_tokens", (P,), torch.int32, dev)
-    slots = _Slots(k_idx.data_ptr(), q_idx.data_ptr(), W, R)
+    slots = _Slots(k_idx.data_ptr(), q_idx.data_ptr(), W, R, _ID_BYTES[k_idx.dtype], _ID_BYTES[q_idx.dtype])
     weights = _Weights(k_val.data_ptr(), q_val.data_ptr())
     return P, M, hd, T, W, R, G, slots, weights
 
@@ -193,16 +208,23 @@ def sdm_fwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
             log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, *, chunk: int = 64,
             valid_tokens: torch.Tensor | None = None, out: torch.Tensor | None = None,
             workspace: torch.Tensor | None = None, max_workspace_bytes: int = DEFAULT_WORKSPACE_CAP,
-            stream=None, events=None) -> torch.Tensor:
+            stream=None, events=None, shared_bank: bool = False,
+            repeated_writes: torch.Tensor | None = None) -> torch.Tensor:
     """SDM forward on the GPU. Returns the readings [P, T, hd] (bank dtype); ``bank``
-    [P, M, hd] is advanced in place. ``valid_tokens`` (int32 [P], on the GPU) marks the
-    tokens at and past each stream's end as padding. ``workspace`` (uint8, GPU) is used if
-    given, else one of at most ``max_workspace_bytes`` (at least one step) is allocated.
+    [P, M, hd] (one bank per stream) or [M, hd] (one bank for all streams; with P > 1 it
+    needs ``shared_bank=True``, asserting disjoint slot sets) is advanced in place. Slot
+    ids are int32 or int64. ``valid_tokens`` (int32 [P], on the GPU) marks the tokens at
+    and past each stream's end as padding. ``workspace`` (uint8, GPU) is used if given,
+    else one of at most ``max_workspace_bytes`` (at least one step) is allocated.
     ``events``: optional ctypes array of TIMING_EVENTS hipEvent_t handles recorded at the
-    kernel boundaries of the first slab (see sdm_exec in include/sdm.h)."""
+    kernel boundaries of the first slab (see sdm_exec in include/sdm.h).
+    ``repeated_writes``: optional int64 [1] GPU tensor; the call adds the number of write
+    entries repeating a slot of their own token."""
     lib = _load()
     P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
-                                                   valid_tokens)
+                                                   valid_tokens, shared_bank)
+    if repeated_writes is not None:
+        _expect(repeated_writes, "repeated_writes", (1,), torch.int64, bank.device)
     if out is None:
         out = torch.empty((P, T, hd), dtype=bank.dtype, device=bank.device)
     else:
@@ -213,9 +235,10 @@ def sdm_fwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
         nbytes = need_all if need_all <= max_workspace_bytes else max(need_one,
                                                                       max_workspace_bytes // need_one * need_one)
         workspace = _workspace(nbytes, bank.device)
-    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype])
+    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 1 if bank.dim() == 2 else 0)
     ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-               None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events))
+               None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events),
+               None if repeated_writes is None else repeated_writes.data_ptr())
     rc = lib.sdm_fwd(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
                      _ptr(v), ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
     _check_rc(lib, rc)
@@ -243,7 +266,7 @@ def chunk_mats(k_idx, k_val, beta, log_decay, q_idx, q_val, *, rows: int, head_d
                X=torch.empty((N, chunk, chunk), **f), QX=torch.empty((N, chunk, chunk), **f),
                gw=torch.empty((N, chunk, W), **f), gr=torch.empty((N, chunk, R), **f))
     ws = _workspace(workspace_bytes(P, T, chunk, W, R, head_dim, 1), dev)
-    ex = _Exec(_stream_ptr(stream), ws.data_ptr(), ws.numel(), None, 0)
+    ex = _Exec(_stream_ptr(stream), ws.data_ptr(), ws.numel(), None, 0, None)
     rc = lib.sdm_chunk_mats(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
                             rows, head_dim, _DTYPES[k_val.dtype], _ptr(valid_tokens), _ptr(res["A"]), _ptr(res["QK"]),
                             _ptr(res["X"]), _ptr(res["QX"]), _ptr(res["gw"]), _ptr(res["gr"]), ctypes.byref(ex))
@@ -262,7 +285,7 @@ def wy_solve(A: torch.Tensor, beta: torch.Tensor, QK: torch.Tensor, stream=None)
         _expect(t, name, shape, torch.float32, A.device)
     X = torch.empty_like(A)
     QX = torch.empty_like(A)
-    ex = _Exec(_stream_ptr(stream), None, 0, None, 0)
+    ex = _Exec(_stream_ptr(stream), None, 0, None, 0, None)
     rc = lib.sdm_wy_solve(n, C, _ptr(A), _ptr(beta), _ptr(QK), _ptr(X), _ptr(QX), ctypes.byref(ex))
     _check_rc(lib, rc)
     return X, QX

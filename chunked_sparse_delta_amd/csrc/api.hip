@@ -131,30 +131,36 @@ int check_shape(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t h
 
 int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
                const float *g, int32_t G, const void *v, int64_t M, int32_t hd, int32_t dtype, void *bank_data,
-               const int32_t *valid, void *out, bool need_bank, Checked *ck) {
+               bool shared, const int32_t *valid, void *out, bool need_bank, Checked *ck) {
     if (!slots || !weights) return fail(SDM_ERR_NULL, "slots and weights must not be NULL");
     int rc = check_shape(P, T, C, slots->W, slots->R, hd);
     if (rc) return rc;
     if (dtype != SDM_F32 && dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "bank dtype must be SDM_F32 or SDM_BF16, got %d", dtype);
+    const int kb = slots->write_id_bytes ? slots->write_id_bytes : 4, qb = slots->read_id_bytes ? slots->read_id_bytes : 4;
+    if ((kb != 4 && kb != 8) || (qb != 4 && qb != 8))
+        return fail(SDM_ERR_DTYPE, "slot ids must be int32 or int64 (4 or 8 bytes), got %d and %d", kb, qb);
     const int W = slots->W, R = slots->R;
     if (G != 1 && G != W) return fail(SDM_ERR_SHAPE, "log_decay must hold 1 or W=%d gates per token, got %d", W, G);
     if (M < 1) return fail(SDM_ERR_SHAPE, "the bank needs at least one row per stream, got %lld", (long long)M);
-    if (int64_t(P) * M >= (int64_t(1) << 31))
-        return fail(SDM_ERR_RANGE, "%d streams of %lld rows: the bank has 2^31 or more slots", P, (long long)M);
+    if ((shared ? 1 : int64_t(P)) * M >= (int64_t(1) << 31))
+        return fail(SDM_ERR_RANGE, "a bank of %lld rows (x %d streams) has 2^31 or more slots", (long long)M,
+                    shared ? 1 : P);
     if (M * hd * (dtype == SDM_F32 ? 4 : 2) >= (int64_t(1) << 31))
         return fail(SDM_ERR_RANGE, "a stream's bank of %lld rows x %d columns is 2 GiB or more", (long long)M, hd);
     if (!slots->write || !slots->read || !weights->write || !weights->read || !beta || !g)
         return fail(SDM_ERR_NULL, "slot ids, weights, beta and log_decay must not be NULL");
     if (need_bank && (!v || !bank_data || !out)) return fail(SDM_ERR_NULL, "v, bank and out must not be NULL");
     const int es = dtype == SDM_F32 ? 4 : 2;
-    const void *ptr4[] = {slots->write, slots->read, beta, g, valid};
+    const void *ptr4[] = {beta, g, valid};
     for (const void *q : ptr4)
         if (q && !aligned(q, 4)) return fail(SDM_ERR_ALIGN, "int32/float32 arrays must be 4-byte aligned");
+    if (!aligned(slots->write, size_t(kb)) || !aligned(slots->read, size_t(qb)))
+        return fail(SDM_ERR_ALIGN, "slot id arrays must be aligned to their element size");
     const void *ptre[] = {weights->write, weights->read, v, bank_data, out};
     for (const void *q : ptre)
         if (q && !aligned(q, size_t(es))) return fail(SDM_ERR_ALIGN, "bank-dtype arrays must be %d-byte aligned", es);
     if (need_bank) {
-        const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank_data), b1 = b0 + uintptr_t(P) * M * hd * es;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank_data), b1 = b0 + uintptr_t(shared ? 1 : P) * M * hd * es;
         const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + uintptr_t(P) * T * hd * es;
         if (o0 < b1 && b0 < o1) return fail(SDM_ERR_SHAPE, "out overlaps the bank");
     }
@@ -164,8 +170,11 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     Problem pb{};
     pb.P = P; pb.T = T; pb.C = C; pb.Nt = int32_t((int64_t(T) + C - 1) / C); pb.W = W; pb.R = R; pb.G = G; pb.hd = hd;
     pb.M = M; pb.dtype = dtype; pb.sort_passes = sort_passes(M); pb.sort_digit = sort_digit(M); pb.key_bits = key_bits(M);
-    pb.k_idx = slots->write; pb.q_idx = slots->read; pb.k_val = weights->write; pb.q_val = weights->read;
+    pb.k_idx = slots->write; pb.q_idx = slots->read; pb.k_id8 = kb == 8; pb.q_id8 = qb == 8;
+    pb.k_val = weights->write; pb.q_val = weights->read;
     pb.beta = beta; pb.g = g; pb.v = v; pb.valid = valid; pb.bank = bank_data; pb.out = out;
+    pb.bank_stride = shared ? 0 : M * hd;
+    pb.repeats = nullptr;
     ck->pb = pb;
     ck->lay = make_layout(C, W, R);
     ck->V = V;
@@ -199,6 +208,9 @@ P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int c
     }
     g.S = (hv + g.nv - 1) / g.nv;
     g.mode = phase2_mode(L, pb.C, g.nv, V, es, pb.M, lds_limit);
+    // A shared bank is never held resident: each workgroup writes its whole slice back at
+    // the end of a slab, which would overwrite the rows of the other streams.
+    if (pb.bank_stride == 0 && g.mode > 1) g.mode = 1;
     if (got == 2 && est >= 0 && est < g.mode) g.mode = est;
     return g;
 }
@@ -238,6 +250,7 @@ int sdm_fwd_plan(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t 
     const int V = hd % vec == 0 ? vec : 1;
     Problem pb{};
     pb.P = P; pb.T = T; pb.C = C; pb.W = W; pb.R = R; pb.hd = hd; pb.M = M; pb.dtype = dtype;
+    pb.bank_stride = M * hd;   // per-stream banks
     const ChunkLayout lay = make_layout(C, W, R);
     const P2Geom g = plan_phase2(pb, lay, V, es, dev->cus, dev->lds_per_block);
     plan->vec = V;
@@ -265,9 +278,13 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
     g_err[0] = 0;
     if (!bank || !exec) return fail(SDM_ERR_NULL, "bank and exec must not be NULL");
     Checked ck;
+    if (bank->shared != 0 && bank->shared != 1) return fail(SDM_ERR_SHAPE, "bank.shared must be 0 or 1, got %d", bank->shared);
     int rc = check_call(P, T, C, slots, weights, beta, log_decay, gate_width, v, bank->rows, bank->head_dim, bank->dtype,
-                        bank->data, valid_tokens, out, true, &ck);
+                        bank->data, bank->shared == 1, valid_tokens, out, true, &ck);
     if (rc) return rc;
+    if (exec->repeated_writes && !aligned(exec->repeated_writes, 8))
+        return fail(SDM_ERR_ALIGN, "the repeated-writes counter must be 8-byte aligned");
+    ck.pb.repeats = reinterpret_cast<unsigned long long *>(exec->repeated_writes);
     const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
     if (!exec->workspace || exec->workspace_bytes < per_step)
         return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
@@ -355,7 +372,7 @@ int sdm_chunk_mats(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, cons
     if (!A || !QK || !X || !QX || !gw || !gr) return fail(SDM_ERR_NULL, "output arrays must not be NULL");
     Checked ck;
     int rc = check_call(P, T, C, slots, weights, beta, log_decay, gate_width, nullptr, rows, head_dim, dtype, nullptr,
-                        valid_tokens, nullptr, false, &ck);
+                        false, valid_tokens, nullptr, false, &ck);
     if (rc) return rc;
     const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
     if (!exec->workspace || exec->workspace_bytes < per_step)

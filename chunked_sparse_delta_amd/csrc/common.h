@@ -104,17 +104,25 @@ struct Problem {
     int32_t sort_passes;     // LSD radix passes over the slot id ...
     int32_t sort_digit;      // ... of this many bits each (the last one may use fewer)
     int32_t key_bits;        // bits of the largest slot id (M - 1)
-    const int32_t *k_idx;    // [P, T, W]
-    const int32_t *q_idx;    // [P, T, R]
+    const void *k_idx;       // [P, T, W] int32, or int64 when k_id8
+    const void *q_idx;       // [P, T, R] int32, or int64 when q_id8
+    int32_t k_id8, q_id8;
     const void *k_val;       // [P, T, W] bank dtype
     const void *q_val;       // [P, T, R] bank dtype
     const float *beta;       // [P, T]
     const float *g;          // [P, T, G]
     const void *v;           // [P, T, hd]
     const int32_t *valid;    // [P] or nullptr
-    void *bank;              // [P, M, hd]
+    void *bank;              // [P, M, hd], or one shared [M, hd]
+    int64_t bank_stride;     // elements from one stream's bank to the next (0: shared bank)
     void *out;               // [P, T, hd]
+    unsigned long long *repeats;   // optional device counter of repeated write slots
 };
+
+// Slot id i of an int32 or int64 id array (ids of valid calls lie in [0, M), M < 2^31).
+__device__ __forceinline__ int32_t load_id(const void *base, int64_t i, int32_t id8) {
+    return id8 ? int32_t(static_cast<const int64_t *>(base)[i]) : static_cast<const int32_t *>(base)[i];
+}
 
 __device__ __forceinline__ int32_t n_live_tokens(const Problem &pb, int p, int ti) {
     int32_t vt = pb.valid ? pb.valid[p] : pb.T;

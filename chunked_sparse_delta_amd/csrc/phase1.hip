@@ -67,20 +67,22 @@ __device__ __forceinline__ void sort_chunk(const Problem &pb, const Slab &sl, in
     uint32_t *cb = sl.chunk(n);
     uint32_t *key[2] = {cb + sl.lay.off_key0, cb + sl.lay.off_key1};
     uint32_t *val[2] = {cb + sl.lay.off_val0, cb + sl.lay.off_val1};
-    const uint32_t *kin = reinterpret_cast<const uint32_t *>(pb.k_idx) + (int64_t(p) * pb.T + int64_t(ti) * pb.C) * pb.W;
+    const int64_t kin0 = (int64_t(p) * pb.T + int64_t(ti) * pb.C) * pb.W;   // the chunk's first write id
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint64_t lt = lanemask_lt(lane);
     const int32_t seg = ((El + NW - 1) / NW + 63) & ~63;
     const int32_t s0 = min(El, wv * seg), s1 = min(El, s0 + seg);
     uint32_t *kid = cb + sl.lay.off_kid;
-    for (int32_t e = threadIdx.x; e < El; e += BLOCK) kid[e] = kin[e];   // ids in entry order, for Phase 2
+    // ids in entry order (int32), for Phase 2 and as the first pass's keys
+    for (int32_t e = threadIdx.x; e < El; e += BLOCK) kid[e] = uint32_t(load_id(pb.k_idx, kin0 + e, pb.k_id8));
+    __syncthreads();
 
     for (int q = 0; q < pb.sort_passes; ++q) {
         const int shift = q * pb.sort_digit;
         const int db = max(1, min(pb.sort_digit, pb.key_bits - shift));
         const int nd = 1 << db;
         const uint32_t dmask = uint32_t(nd - 1);
-        const uint32_t *sk = q == 0 ? kin : key[(q + 1) & 1];
+        const uint32_t *sk = q == 0 ? kid : key[(q + 1) & 1];
         const uint32_t *sv = val[(q + 1) & 1];
         uint32_t *dk = key[q & 1];
         uint32_t *dv = val[q & 1];
@@ -254,6 +256,7 @@ template <int NW> struct GroupsSmem {
     TileScan<NW> ts;
     int32_t wsum[NW];
     int32_t ncand, nhot;
+    int32_t nrep;              // write entries repeating a slot of their own token
     int32_t cand[kMaxHot];
     uint8_t cand_hot[kMaxHot];
 };
@@ -304,13 +307,17 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
         ts.carry_val = 0.0f;
         ncand = 0;
         nhot = 0;
+        gs.nrep = 0;
     }
     for (int i = tid; i < C; i += BLOCK) beta_c[i] = i < nl ? pb.beta[tok0 + i] : 0.0f;
     for (int64_t e = El + tid; e < L.E; e += BLOCK) gw[e] = 0.0f;
     __syncthreads();
 
     // Pass 1, tile by tile over the sorted positions: group starts, group index, last
-    // group start, cumulative log-decay L, the per-position record, bucket starts.
+    // group start, cumulative log-decay L, the per-position record, bucket starts; and,
+    // when counted, the entries repeating a slot of their own token (the sort is stable,
+    // so such entries sit right after an entry of the same slot and token).
+    int32_t nrep = 0;
     for (int32_t t0 = 0; t0 < El; t0 += BLOCK) {
         const int32_t m = t0 + tid;
         const bool ok = m < El;
@@ -330,6 +337,7 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
             kv = load_weight(pb.k_val, tg * W + w, pb.dtype);
             const int32_t bp = m > 0 ? min(int32_t(prev >> bsh), NB - 1) : -1, bc = min(int32_t(key >> bsh), NB - 1);
             for (int32_t b = bp + 1; b <= bc; ++b) bstart[b] = m;
+            if (pb.repeats && !head && int32_t(sval[m - 1]) / W == i) ++nrep;
         }
         int32_t cnt = head, mx = head ? m : -1;
         float Lc = gv;
@@ -353,7 +361,9 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
         meta[2] = ng;
     }
     for (int32_t g = tid; g < ng; g += BLOCK) ghot[g] = -1;
+    if (nrep) atomicAdd(&gs.nrep, nrep);
     __syncthreads();
+    if (tid == 0 && pb.repeats && gs.nrep > 0) atomicAdd(pb.repeats, static_cast<unsigned long long>(gs.nrep));
 
     // Pass 2, per sorted position: DW records and gather weights.
     for (int32_t m = tid; m < El; m += BLOCK) {
@@ -471,7 +481,7 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
         int32_t h = -1;
         int4 cr = make_int4(0, 0, 0, 0);
         if (ok && i < nl) {
-            const int32_t q = pb.q_idx[tg * R + r];
+            const int32_t q = load_id(pb.q_idx, tg * R + r, pb.q_id8);
             qid[int64_t(i) * R + r] = q;   // ids in entry order, for Phase 2
             const int32_t b = min(int32_t(uint32_t(q) >> bsh), int32_t(L.NB) - 1);
             const int32_t b0 = bstart[b];
@@ -526,24 +536,20 @@ constexpr int kTermCap = 512;   // terms per wavefront per round (>= 255 earlier
 
 // Row i of the cold part of A (qk false) or QK (qk true) of chunk n by one wavefront;
 // mcol, mval: kTermCap entries each of LDS.
-__device__ __forceinline__ void cold_row(const Problem &pb, const Slab &sl, int64_t n, bool qk, int i, int32_t *mcol,
-                                         float *mval) {
-    const int C = pb.C;
-    const int width = qk ? pb.R : pb.W;
-    const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
-    const int nl = n_live_tokens(pb, p, ti);
-    const ChunkLayout &L = sl.lay;
-    uint32_t *cb = sl.chunk(n);
-    const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
-    const int4 *cr = reinterpret_cast<const int4 *>(cb + (qk ? L.off_rcr : L.off_ecr));
-    float *Mout = reinterpret_cast<float *>(cb + (qk ? L.off_QK : L.off_A));
+// Row i from explicit arrays: spk the sorted member records, cr the transposed cold
+// records of the row's region (width entries per token), Mout the C x C output.
+__device__ __forceinline__ void cold_row_at(int C, int nl, const int4 *spk, const int4 *cr, float *Mout, int width,
+                                            int i, int32_t *mcol, float *mval) {
     const int lane = threadIdx.x & 63;
     {
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int x0 = 0; i < nl && x0 < width; x0 += kWave) {
             const int x = x0 + lane;
             const int4 r = x < width ? cr[int64_t(x) * C + i] : make_int4(0, 0, 0, 0);
-            const int cnt = r.y > r.x ? r.y - r.x : 0;
+            // earlier members of the entry's group; at most C - 1 <= 255 when the write slots
+            // of a token are distinct, clamped so that a call breaking that contract still
+            // advances through its rounds
+            const int cnt = r.y > r.x ? min(r.y - r.x, kTermCap) : 0;
             // inclusive prefix of the counts over the lanes
             int incl = cnt;
 #pragma unroll
@@ -597,6 +603,17 @@ __device__ __forceinline__ void cold_row(const Problem &pb, const Slab &sl, int6
                 if (c0 + q < C) Mout[int64_t(i) * C + c0 + q] = acc[q];
         }
     }
+}
+
+// Row i of the cold part of A (qk false) or QK (qk true) of chunk n, arrays in the workspace.
+__device__ __forceinline__ void cold_row(const Problem &pb, const Slab &sl, int64_t n, bool qk, int i, int32_t *mcol,
+                                         float *mval) {
+    const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
+    const ChunkLayout &L = sl.lay;
+    uint32_t *cb = sl.chunk(n);
+    cold_row_at(pb.C, n_live_tokens(pb, p, ti), reinterpret_cast<const int4 *>(cb + L.off_spk),
+                reinterpret_cast<const int4 *>(cb + (qk ? L.off_rcr : L.off_ecr)),
+                reinterpret_cast<float *>(cb + (qk ? L.off_QK : L.off_A)), qk ? pb.R : pb.W, i, mcol, mval);
 }
 
 // The hot part of A and QK on the matrix cores, from the dense operands of Phase 1
@@ -696,6 +713,9 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab
 }
 
 constexpr int kFusedBlock = 1024;
+constexpr int kFusedMaxEntries = 1024;   // write and read entries per chunk of the fused path
+// the cold pass's term lists: two kTermCap arrays per wavefront
+constexpr int kColdTermBytes = (kFusedBlock / kWave) * 2 * kTermCap * 4;
 
 __global__ __launch_bounds__(kFusedBlock) void p1_fused_kernel(Problem pb, Slab sl, WyArgs wa) {
     extern __shared__ __align__(16) char fsm[];
@@ -712,9 +732,31 @@ __global__ __launch_bounds__(kFusedBlock) void p1_fused_kernel(Problem pb, Slab 
     }
     __syncthreads();
     {
+        // The cold pass reads its inputs (sorted member records, cold write and read records)
+        // from LDS: one coalesced sweep instead of dependent memory round trips per row.
+        const ChunkLayout &L = sl.lay;
+        const uint32_t *cb = sl.chunk(n);
+        int4 *lspk = reinterpret_cast<int4 *>(fsm + kColdTermBytes);
+        int4 *lecr = lspk + L.E, *lrcr = lecr + L.E;
+        const int4 *gspk = reinterpret_cast<const int4 *>(cb + L.off_spk);
+        const int4 *gecr = reinterpret_cast<const int4 *>(cb + L.off_ecr);
+        const int4 *grcr = reinterpret_cast<const int4 *>(cb + L.off_rcr);
+        for (int e = threadIdx.x; e < L.E; e += kFusedBlock) {
+            lspk[e] = gspk[e];
+            lecr[e] = gecr[e];
+        }
+        for (int e = threadIdx.x; e < L.F; e += kFusedBlock) lrcr[e] = grcr[e];
+        __syncthreads();
+        const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
+        const int nl = n_live_tokens(pb, p, ti);
+        float *A = reinterpret_cast<float *>(sl.chunk(n) + L.off_A);
+        float *QK = reinterpret_cast<float *>(sl.chunk(n) + L.off_QK);
         int32_t *mcol = reinterpret_cast<int32_t *>(fsm) + wave * 2 * kTermCap;
         float *mval = reinterpret_cast<float *>(mcol + kTermCap);
-        for (int k = wave; k < 2 * pb.C; k += NW) cold_row(pb, sl, n, k >= pb.C, k >= pb.C ? k - pb.C : k, mcol, mval);
+        for (int k = wave; k < 2 * pb.C; k += NW) {
+            const bool qk = k >= pb.C;
+            cold_row_at(pb.C, nl, lspk, qk ? lrcr : lecr, qk ? QK : A, qk ? pb.R : pb.W, qk ? k - pb.C : k, mcol, mval);
+        }
     }
     __syncthreads();
     hot_tiles(pb, sl, n, wave, NW);
@@ -726,17 +768,17 @@ static size_t fused_smem_bytes(int C) {
     size_t b = sort_smem_bytes<kFusedBlock>();
     b = std::max(b, sizeof(GroupsSmem<kFusedBlock / kWave>));
     b = std::max(b, size_t(kFusedBlock / kWave) * kHotCap * 4);
-    b = std::max(b, size_t(kFusedBlock / kWave) * 2 * kTermCap * 4);
+    b = std::max(b, size_t(kColdTermBytes) + 16 * size_t(2 * kFusedMaxEntries + kFusedMaxEntries));
     return std::max(b, wy_lds_bytes(C));
 }
 
 // Whether a chunk's Phase 1 and solve run fused: small chunks (E, F <= 1024) whose stages
-// fit the device's LDS. SDM_P1_FUSED=0 or 1 overrides (where it fits), for sweeps.
+// fit the device's LDS. SDM_P1_FUSED=0 turns it off, for sweeps and tests.
 bool phase1_fused(const ChunkLayout &L, int C, int lds_limit) {
-    if (fused_smem_bytes(C) > size_t(lds_limit)) return false;
+    // the fused cold pass stages at most kFusedMaxEntries write and read records in LDS
+    if (fused_smem_bytes(C) > size_t(lds_limit) || L.E > kFusedMaxEntries || L.F > kFusedMaxEntries) return false;
     const char *env = getenv("SDM_P1_FUSED");
-    if (env && (env[0] == '0' || env[0] == '1')) return env[0] == '1';
-    return L.E <= 1024 && L.F <= 1024;
+    return !(env && env[0] == '0');
 }
 
 // ---------------------------------------------------------------------------------------

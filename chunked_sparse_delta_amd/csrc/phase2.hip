@@ -52,13 +52,13 @@ template <int BLOCK, int V> struct P2Cfg {
 };
 
 struct P2Args {
-    const int32_t *k_idx, *q_idx;   // [P, T, W], [P, T, R]
     const void *v;                  // [P, T, hd]
     void *bank;                     // [P, M, hd]
     void *out;                      // [P, T, hd]
     const int32_t *valid;           // [P] or nullptr
     const uint32_t *ws;             // slab base: chunk n at ws + n * words
     int64_t M, words;
+    int64_t bstride;                // elements between the streams' banks (0: one shared bank)
     int32_t T, C, W, R, hd, P;
     int32_t S, hv;                  // slices per row, vectors per row (hd / V)
     int32_t ti0, steps;             // the slab
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     const int cwv = nvs * V;                  // valid columns of this slice
     const int col0 = vq0 * V;
     using raw_t = typename Vec<T, V>::raw_t;
-    T *gbank = static_cast<T *>(a.bank) + int64_t(p) * a.M * hd + col0;   // this slice, row stride hd
+    T *gbank = static_cast<T *>(a.bank) + int64_t(p) * a.bstride + col0;   // this slice, row stride hd
     const bool vec4 = (C & 3) == 0, full = (C & 15) == 0;
 
     float *ub = lds;                  // [CP][pitch]: u (retrieved first, without staging)
@@ -894,8 +894,8 @@ int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, i
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st) {
     const ChunkLayout &L = sl.lay;
     P2Args a{};
-    a.k_idx = pb.k_idx; a.q_idx = pb.q_idx; a.v = pb.v; a.bank = pb.bank; a.out = pb.out; a.valid = pb.valid;
-    a.ws = sl.ws; a.M = pb.M; a.words = L.words;
+    a.v = pb.v; a.bank = pb.bank; a.out = pb.out; a.valid = pb.valid;
+    a.ws = sl.ws; a.M = pb.M; a.words = L.words; a.bstride = pb.bank_stride;
     a.T = pb.T; a.C = pb.C; a.W = pb.W; a.R = pb.R; a.hd = pb.hd; a.P = pb.P;
     a.S = g.S; a.hv = pb.hd / V; a.ti0 = sl.ti0; a.steps = sl.steps;
     a.off_gw = int32_t(L.off_gw); a.off_gr = int32_t(L.off_gr); a.off_beta = int32_t(L.off_beta);

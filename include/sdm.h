@@ -62,12 +62,18 @@ enum {
 
 typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
 
-/* Slot ids, device int32. write: [P, T, W]; read: [P, T, R]. Stream-local rows in [0, M). */
+/* Slot ids, device int32 or int64 (sdm_write_read takes either, page 21, memory_ops.py,
+ * _layout). write: [P, T, W]; read: [P, T, R]. Rows in [0, M) of the stream's bank, or of
+ * the one bank in shared mode (sdm_bank.shared).
+ * write_id_bytes, read_id_bytes: 4 (int32; 0 means 4) or 8 (int64); an int64 id must lie in
+ * [0, M) like an int32 one (not checked on the device). */
 typedef struct {
-    const int32_t *write;
-    const int32_t *read;
+    const void *write;
+    const void *read;
     int32_t W;
     int32_t R;
+    int32_t write_id_bytes;
+    int32_t read_id_bytes;
 } sdm_slots;
 
 /* Slot weights, device, in the bank dtype. write: [P, T, W] (k_val); read: [P, T, R] (q_val). */
@@ -76,14 +82,19 @@ typedef struct {
     const void *read;
 } sdm_weights;
 
-/* The bank, device [P, rows, head_dim] in dtype; read and advanced in place to its final
- * state. Stream p owns rows [p * rows, (p + 1) * rows) of the flat [P * rows, head_dim]
- * array (sdm_write_read's per-stream slot ranges, num_memory_slots = rows). */
+/* The bank, device, in dtype; read and advanced in place to its final state.
+ * shared = 0: [P, rows, head_dim]; stream p owns rows [p * rows, (p + 1) * rows) of the
+ *   flat [P * rows, head_dim] array (sdm_write_read's per-stream slot ranges,
+ *   num_memory_slots = rows).
+ * shared = 1: one [rows, head_dim] bank read and written by every stream (sdm_write_read
+ *   with shared_bank=True, page 21, memory_ops.py docstring): the streams' slot sets must
+ *   be disjoint over the whole call (caller contract, not checked). */
 typedef struct {
     void *data;
     int64_t rows;
     int32_t head_dim;
     int32_t dtype; /* sdm_dtype */
+    int32_t shared;
 } sdm_bank;
 
 /* Where and with what scratch the call runs. stream: hipStream_t (NULL = null stream).
@@ -101,6 +112,12 @@ typedef struct {
     size_t workspace_bytes;
     void **events;
     int32_t num_events;
+    /* optional device int64 counter (NULL = none): sdm_fwd adds the number of live write
+     * entries that repeat a slot of their own token (the counter sdm_write_read keeps for
+     * repeated_write_slots, page 21, memory_ops.py; such calls break the distinct-slots
+     * contract and their results are unspecified). Ordered on `stream`; the caller zeroes
+     * and reads it. */
+    int64_t *repeated_writes;
 } sdm_exec;
 
 #define SDM_TIMING_EVENTS 8

@@ -9,6 +9,9 @@ package shares no code with it; both take their inputs from ``workloads``.
                         rows rounded to bfloat16 once per chunk, readings rounded to
                         bfloat16 (token_loop(..., bf16_chunk=C))
   O2  chunk_algebra.py  the chunked three-part form in fp64, for tiny inputs
+  token_loop over a [M, hd] bank: one bank shared by every stream (slot sets disjoint,
+                        checked); repeated_write_slots: the pages' count of write entries
+                        repeating a slot of their own token
 
 Pins: tests/test_oracle.py checks O1 against O2 (two independent derivations),
 against closed forms (decay-only, scalar EMA, one-token delta update, overwrite
@@ -16,7 +19,9 @@ under a large negative log-decay, a hand-worked rational example in tests/golden
 and against invariants (padding, chunk-size, stream and column independence). O1b is
 pinned by its rounding (ties to even, no double rounding, against an independent
 float32 bit-level rounding), by its reduction to O1 with one rounding when one chunk
-spans the stream, and by its equality with O1 when every value is bfloat16-exact.
+spans the stream, and by its equality with O1 when every value is bfloat16-exact. The
+shared-bank loop is pinned to the per-stream loop on interleaved relabeled slots (equal
+bit for bit, O1 and O1b), the repeat count to hand-counted tokens.
 Parity unpinned: none.
 """
 
@@ -65,6 +70,9 @@ def _load():
             fb = lib.sdm_oracle_token_loop_bf16
             fb.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 10
             fb.restype = ctypes.c_int
+            fs = lib.sdm_oracle_token_loop_shared
+            fs.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 10
+            fs.restype = ctypes.c_int
             lib.sdm_oracle_round_bf16.argtypes = [ctypes.c_double]
             lib.sdm_oracle_round_bf16.restype = ctypes.c_double
             _lib = lib
@@ -97,14 +105,21 @@ def round_bf16(x) -> np.ndarray:
 
 def token_loop(f64: dict, threads: int = 1, streams=None, bf16_chunk: int | None = None):
     """O1 over the streams of fp64 inputs (``as_f64_inputs``). Returns (readings
-    [P, T, hd], final bank [P, M, hd]) in fp64; ``streams`` restricts the work to a
-    subset (the other streams' outputs are left zero / unchanged). With ``bf16_chunk``
-    = C it runs O1b, the loop under the bfloat16 storage contract for chunks of C."""
+    [P, T, hd], final bank) in fp64; ``streams`` restricts the work to a subset (the other
+    streams' outputs are left zero / unchanged). With ``bf16_chunk`` = C it runs O1b, the
+    loop under the bfloat16 storage contract for chunks of C.
+
+    The bank is [P, M, hd] (one bank per stream) or [M, hd]: one bank for every stream
+    (page 21, memory_ops.py, sdm_write_read with shared_bank=True), whose streams must
+    select disjoint slots over the whole call; that contract is checked here."""
     lib = _load()
     bank = np.array(f64["bank"], dtype=np.float64, copy=True, order="C")
-    P, M, hd = bank.shape
+    shared = bank.ndim == 2
     k_idx = np.ascontiguousarray(f64["k_idx"], dtype=np.int32)
-    T, W = k_idx.shape[1], k_idx.shape[2]
+    P, T, W = k_idx.shape
+    M, hd = bank.shape[-2], bank.shape[-1]
+    if shared:
+        _check_disjoint_streams(k_idx, f64["q_idx"], f64.get("valid"))
     R = f64["q_idx"].shape[2]
     g = np.ascontiguousarray(f64["g"], dtype=np.float64)
     G = g.shape[2]
@@ -121,7 +136,9 @@ def token_loop(f64: dict, threads: int = 1, streams=None, bf16_chunk: int | None
     def run(p):
         args = (ptr(k_idx), ptr(arrs["k_val"]), ptr(arrs["v"]), ptr(arrs["beta"]), ptr(g), ptr(arrs["q_idx"]),
                 ptr(arrs["q_val"]), ptr(valid), ptr(bank), ptr(out))
-        if bf16_chunk is None:
+        if shared:
+            rc = lib.sdm_oracle_token_loop_shared(p, p + 1, T, W, R, G, hd, M, int(bf16_chunk or 0), *args)
+        elif bf16_chunk is None:
             rc = lib.sdm_oracle_token_loop(p, p + 1, T, W, R, G, hd, M, *args)
         else:
             rc = lib.sdm_oracle_token_loop_bf16(p, p + 1, T, W, R, G, hd, M, int(bf16_chunk), *args)
@@ -136,3 +153,29 @@ def token_loop(f64: dict, threads: int = 1, streams=None, bf16_chunk: int | None
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(run, todo))
     return out, bank
+
+
+def _check_disjoint_streams(k_idx, q_idx, valid) -> None:
+    """Raise unless no slot is selected (written or read) by two streams over their live
+    tokens: the shared-bank contract."""
+    P, T = k_idx.shape[0], k_idx.shape[1]
+    owner = {}
+    for p in range(P):
+        n = T if valid is None else int(valid[p])
+        for s in set(np.asarray(k_idx[p, :n]).ravel().tolist()) | set(np.asarray(q_idx[p, :n]).ravel().tolist()):
+            if owner.setdefault(int(s), p) != p:
+                raise ValueError(f"oracle: slot {s} is selected by streams {owner[int(s)]} and {p} of a shared bank")
+
+
+def repeated_write_slots(k_idx, valid=None) -> int:
+    """The number of live write entries that repeat a slot of their own token (page 21,
+    memory_ops.py, repeated_write_slots): for each live token, its W entries minus its
+    distinct slots. Plain loops over the tokens."""
+    k_idx = np.asarray(k_idx)
+    P, T, W = k_idx.shape
+    total = 0
+    for p in range(P):
+        n = T if valid is None else int(valid[p])
+        for t in range(n):
+            total += W - len(set(k_idx[p, t].tolist()))
+    return total

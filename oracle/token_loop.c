@@ -61,9 +61,12 @@ double sdm_oracle_round_bf16(double x)
     return ldexp(r, e - 8);
 }
 
+/* bank_stride: elements from stream p's bank to stream p + 1's (M * hd for one bank per
+ * stream; 0 for one bank shared by every stream, whose slot sets the caller keeps
+ * disjoint). */
 static int token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
-                      int64_t hd, int64_t M, const int32_t *k_idx, const double *k_val,
-                      const double *v, const double *beta, const double *g,
+                      int64_t hd, int64_t M, int64_t bank_stride, const int32_t *k_idx,
+                      const double *k_val, const double *v, const double *beta, const double *g,
                       const int32_t *q_idx, const double *q_val, const int32_t *valid,
                       double *bank, double *out, int64_t round_chunk)
 {
@@ -80,7 +83,7 @@ static int token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, i
     }
     int rc = 0;
     for (int64_t p = p0; p < p1 && rc == 0; ++p) {
-        double *B = bank + p * M * hd;
+        double *B = bank + p * bank_stride;
         int64_t nvalid = valid ? valid[p] : T;
         for (int64_t t = 0; t < T && rc == 0; ++t) {
             int64_t tok = p * T + t;
@@ -153,8 +156,8 @@ int sdm_oracle_token_loop(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t 
                           const int32_t *q_idx, const double *q_val, const int32_t *valid,
                           double *bank, double *out)
 {
-    return token_loop(p0, p1, T, W, R, G, hd, M, k_idx, k_val, v, beta, g, q_idx, q_val, valid,
-                      bank, out, 0);
+    return token_loop(p0, p1, T, W, R, G, hd, M, M * hd, k_idx, k_val, v, beta, g, q_idx, q_val,
+                      valid, bank, out, 0);
 }
 
 int sdm_oracle_token_loop_bf16(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R, int64_t G,
@@ -164,6 +167,19 @@ int sdm_oracle_token_loop_bf16(int64_t p0, int64_t p1, int64_t T, int64_t W, int
                                const int32_t *valid, double *bank, double *out)
 {
     if (chunk < 1) return -3;
-    return token_loop(p0, p1, T, W, R, G, hd, M, k_idx, k_val, v, beta, g, q_idx, q_val, valid,
-                      bank, out, chunk);
+    return token_loop(p0, p1, T, W, R, G, hd, M, M * hd, k_idx, k_val, v, beta, g, q_idx, q_val,
+                      valid, bank, out, chunk);
+}
+
+/* Either loop over one [M, hd] bank shared by every stream (chunk 0: O1, else O1b). */
+int sdm_oracle_token_loop_shared(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R,
+                                 int64_t G, int64_t hd, int64_t M, int64_t chunk,
+                                 const int32_t *k_idx, const double *k_val, const double *v,
+                                 const double *beta, const double *g, const int32_t *q_idx,
+                                 const double *q_val, const int32_t *valid, double *bank,
+                                 double *out)
+{
+    if (chunk < 0) return -3;
+    return token_loop(p0, p1, T, W, R, G, hd, M, 0, k_idx, k_val, v, beta, g, q_idx, q_val,
+                      valid, bank, out, chunk);
 }

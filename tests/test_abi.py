@@ -82,6 +82,7 @@ class Call:
         self.P, self.T, self.C, self.W, self.R, self.G, self.hd, self.M = 2, 100, 32, 4, 3, 4, 64, 50
         self.dtype = 0
         self.ws_bytes = None
+        self.kb, self.qb, self.shared, self.rep = 4, 4, 0, None
         self.ptr = {k: self.FAKE + (i << 32) for i, k in enumerate(
             ["kidx", "qidx", "kval", "qval", "beta", "g", "v", "bank", "out", "ws", "valid"])}
 
@@ -89,12 +90,12 @@ class Call:
         from chunked_sparse_delta_amd import _Bank, _Exec, _Slots, _Weights
         lib = self.lib
         lib.sdm_fwd.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 5
-        slots = _Slots(self.ptr["kidx"], self.ptr["qidx"], self.W, self.R)
+        slots = _Slots(self.ptr["kidx"], self.ptr["qidx"], self.W, self.R, self.kb, self.qb)
         weights = _Weights(self.ptr["kval"], self.ptr["qval"])
-        bank = _Bank(self.ptr["bank"], self.M, self.hd, self.dtype)
+        bank = _Bank(self.ptr["bank"], self.M, self.hd, self.dtype, self.shared)
         lib.sdm_fwd_workspace_bytes.restype = ctypes.c_size_t
         need = lib.sdm_fwd_workspace_bytes(self.P, self.T, self.C, self.W, self.R, self.hd, 0)
-        ex = _Exec(None, self.ptr["ws"], need if self.ws_bytes is None else self.ws_bytes, None, 0)
+        ex = _Exec(None, self.ptr["ws"], need if self.ws_bytes is None else self.ws_bytes, None, 0, self.rep)
         rc = lib.sdm_fwd(self.P, self.T, self.C, ctypes.byref(slots), ctypes.byref(weights), self.ptr["beta"],
                          self.ptr["g"], self.G, self.ptr["v"], ctypes.byref(bank), self.ptr["valid"],
                          self.ptr["out"], ctypes.byref(ex))
@@ -105,6 +106,7 @@ class Call:
     ("P", 0, SHAPE), ("T", 0, SHAPE), ("C", 15, RANGE), ("C", 257, RANGE), ("W", 0, SHAPE), ("W", 257, SHAPE),
     ("R", 0, SHAPE), ("R", 300, SHAPE), ("G", 2, SHAPE), ("hd", 0, SHAPE), ("hd", (1 << 20) + 1, RANGE),
     ("M", 0, SHAPE), ("M", 1 << 30, RANGE), ("dtype", 2, DTYPE), ("ws_bytes", 1024, WORKSPACE),
+    ("kb", 2, DTYPE), ("qb", 16, DTYPE), ("shared", 2, SHAPE),
 ])
 def test_fwd_rejects_before_any_work(lib, field, value, code):
     c = Call(lib)
@@ -128,6 +130,22 @@ def test_fwd_rejects_misaligned(lib, name, off, dtype):
     c = Call(lib)
     c.dtype = dtype
     c.ptr[name] += off
+    rc, msg = c.run()
+    assert rc == ALIGN, msg
+
+
+@pytest.mark.parametrize("name,off,kb", [("kidx", 4, 8), ("qidx", 4, 8)])
+def test_fwd_rejects_misaligned_int64_ids(lib, name, off, kb):
+    c = Call(lib)
+    c.kb = c.qb = kb
+    c.ptr[name] += off
+    rc, msg = c.run()
+    assert rc == ALIGN, msg
+
+
+def test_fwd_rejects_misaligned_repeat_counter(lib):
+    c = Call(lib)
+    c.rep = Call.FAKE + 4
     rc, msg = c.run()
     assert rc == ALIGN, msg
 

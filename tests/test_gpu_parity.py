@@ -250,3 +250,82 @@ def test_phase1_fusion_does_not_change_bits(gpu, wl, monkeypatch):
         results.append((gu.bits(o), gu.bits(b)))
     gu.parity(o, b, inp, wl.C, "fused phase 1")
     assert np.array_equal(results[0][0], results[1][0]) and np.array_equal(results[0][1], results[1][1])
+
+
+# ------------------------------------------------------------------ forward variants
+
+@pytest.mark.parametrize("wl", [
+    small(P=3, T=150, C=32, hd=24, M=40, W=5, R=4, dtype="bf16", ids="zipf", ragged=True, index=33),
+    small(P=2, T=130, C=64, hd=16, M=300, W=32, R=32, index=34),
+], ids=["bf16_zipf", "f32_w32"])
+def test_int64_ids_give_the_same_bits(gpu, wl):
+    """Slot ids may be int32 or int64 (page 21, memory_ops.py, _layout): the values are the
+    same rows, so every combination gives the same bits."""
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    o, b = gu.run(t, wl.C)
+    gu.parity(o, b, inp, wl.C, "int32 ids")
+    for kd, qd in ((torch.int64, torch.int64), (torch.int64, torch.int32), (torch.int32, torch.int64)):
+        t2 = dict(t, k_idx=t["k_idx"].to(kd), q_idx=t["q_idx"].to(qd))
+        o2, b2 = gu.run(t2, wl.C)
+        assert np.array_equal(gu.bits(o2), gu.bits(o)) and np.array_equal(gu.bits(b2), gu.bits(b)), (kd, qd)
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=4, T=200, C=64, hd=64, M=64, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=35),
+    small(P=3, T=100, C=32, hd=20, M=50, W=4, R=3, ragged=True, index=36),
+    small(P=2, T=300, C=128, hd=32, M=700, W=16, R=16, index=37),
+], ids=["bf16_staged", "f32_partial", "f32_memory"])
+def test_shared_bank_matches_per_stream_banks(gpu, wl):
+    """One bank shared by every stream (sdm_write_read with shared_bank=True, page 21,
+    memory_ops.py docstring), the streams' slots interleaved and disjoint: the readings and
+    each stream's rows equal those of per-stream banks bit for bit. (A workgroup writing a
+    whole slice back, as the resident mode does, would overwrite the other streams' rows.)"""
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    o, b = gu.run(t, wl.C)
+    gu.parity(o, b, inp, wl.C, "per-stream banks")
+    sh = gu.to_torch(dict(workloads.shared_bank_inputs(inp), dtype=inp["dtype"]), gpu)
+    assert sh["bank"].shape == (wl.P * wl.M, wl.hd)
+    o2, b2 = gu.run(sh, wl.C, shared_bank=True)
+    P, M, hd = wl.P, wl.M, wl.hd
+    assert np.array_equal(gu.bits(o2), gu.bits(o))
+    assert np.array_equal(gu.bits(b2.reshape(M, P, hd).permute(1, 0, 2).contiguous()), gu.bits(b))
+
+
+def test_shared_bank_needs_the_opt_in(gpu):
+    from chunked_sparse_delta_amd import sdm_fwd
+    wl = small(P=2, T=40, C=16, hd=8, M=20, W=2, R=2, index=38)
+    sh = gu.to_torch(dict(workloads.shared_bank_inputs(gu.generate(wl)), dtype="f32"), gpu)
+    with pytest.raises(ValueError, match="shared_bank=True"):
+        sdm_fwd(sh["bank"], sh["k_idx"], sh["k_val"], sh["v"], sh["beta"], sh["log_decay"], sh["q_idx"],
+                sh["q_val"], chunk=16)
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+def test_repeated_write_counter(gpu, fused, monkeypatch):
+    """The device counter of write entries repeating a slot of their own token (page 21,
+    memory_ops.py, repeated_write_slots) equals the oracle's count, and accumulates over
+    calls. Such calls break the distinct-slots contract, so only the count is checked."""
+    import oracle
+    monkeypatch.setenv("SDM_P1_FUSED", fused)
+    wl = small(P=3, T=70, C=32, hd=8, M=30, W=4, R=2, ragged=True, index=39)
+    inp = gu.generate(wl)
+    k = inp["k_idx"].copy()
+    k[0, 3, 1] = k[0, 3, 0]               # one repeat
+    k[1, 10, 1:] = k[1, 10, 0]            # three repeats in one token
+    k[2, 40, 2] = k[2, 40, 3]             # one repeat (counted only if token 40 is live)
+    k[0, 69, 3] = k[0, 69, 0]             # last token of stream 0 (counted only if live)
+    inp["k_idx"] = k
+    want = oracle.repeated_write_slots(k, inp["valid"])
+    assert want >= 4
+    t = gu.to_torch(inp, gpu)
+    cnt = torch.zeros(1, dtype=torch.int64, device=gpu)
+    gu.run(t, wl.C, repeated_writes=cnt)
+    assert int(cnt.item()) == want
+    gu.run(t, wl.C, repeated_writes=cnt)
+    assert int(cnt.item()) == 2 * want
+    gen = gu.generate(wl)                 # distinct slots: nothing counted
+    cnt.zero_()
+    gu.run(gu.to_torch(gen, gpu), wl.C, repeated_writes=cnt)
+    assert int(cnt.item()) == 0

@@ -356,3 +356,38 @@ def test_bf16_loop_rounds_at_chunk_ends():
     o_b, _ = oracle.token_loop(inp, bf16_chunk=12)
     assert not np.array_equal(o_a, o_b)
     assert _rel(o_a, o_b) < 5e-2
+
+
+# ---------------------------------------------------------------- shared bank, repeated writes
+
+@pytest.mark.parametrize("bf16_chunk", [None, 4])
+def test_shared_bank_equals_per_stream_banks(bf16_chunk):
+    """One bank shared by streams with disjoint slots (page 21, sdm_write_read with
+    shared_bank=True) computes what per-stream banks compute, row for row."""
+    inp = tiny_inputs(41, P=3, T=30, M=7)
+    out, bank = oracle.token_loop(inp, bf16_chunk=bf16_chunk)
+    sh = workloads.shared_bank_inputs(inp)
+    o2, b2 = oracle.token_loop(sh, bf16_chunk=bf16_chunk)
+    assert b2.shape == (21, 4)
+    assert np.array_equal(o2, out)
+    assert np.array_equal(workloads.per_stream_bank(b2, 3), bank)
+
+
+def test_shared_bank_rejects_streams_sharing_a_slot():
+    sh = workloads.shared_bank_inputs(tiny_inputs(43, P=2, T=10, M=5))
+    sh["q_idx"] = sh["q_idx"].copy()
+    sh["q_idx"][1, 0, 0] = sh["k_idx"][0, 0, 0]   # stream 1 reads a slot stream 0 writes
+    with pytest.raises(ValueError, match="selected by streams"):
+        oracle.token_loop(sh)
+
+
+def test_repeated_write_slots_hand_count():
+    """Entries that repeat a slot of their own token (page 21, repeated_write_slots):
+    [3, 5, 3, 3] repeats twice, [7, 7, 8, 9] once, distinct tokens never."""
+    k = np.array([[[3, 5, 3, 3], [1, 2, 3, 4], [7, 7, 8, 9]],
+                  [[0, 1, 2, 3], [6, 6, 6, 6], [5, 4, 3, 2]]], np.int32)
+    assert oracle.repeated_write_slots(k) == 2 + 1 + 3
+    assert oracle.repeated_write_slots(k, valid=[1, 2]) == 2 + 3
+    assert oracle.repeated_write_slots(k, valid=[0, 0]) == 0
+    inp = tiny_inputs(47, P=2, T=30)
+    assert oracle.repeated_write_slots(inp["k_idx"], inp["valid"]) == 0

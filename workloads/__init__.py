@@ -270,3 +270,27 @@ def small(name: str = "tiny", *, P=2, T=37, C=16, hd=8, M=24, dtype="f32", W=3, 
     return Workload(name, index, P=P, T=T, C=C, hd=hd, M=M, dtype=dtype, W=W, R=R, ids=ids,
                     zipf_s=zipf_s, decay_scale=decay_scale, decay_mu=decay_mu, ragged=ragged,
                     weight_scale=weight_scale, gate_width=gate_width)
+
+
+def shared_bank_inputs(inputs: dict) -> dict:
+    """The same work over one bank shared by every stream: local slot s of stream p becomes
+    row s * P + p of a [P * M, hd] bank (streams interleaved, slot sets disjoint), ids
+    relabeled to match. A pure relabeling of ``inputs`` (any dict with ``bank`` [P, M, hd],
+    ``k_idx`` and ``q_idx``); the other arrays are shared, not copied."""
+    bank = np.asarray(inputs["bank"])
+    P, M, hd = bank.shape
+    shared = np.empty((M * P, hd), dtype=bank.dtype)
+    for p in range(P):
+        shared[np.arange(M) * P + p] = bank[p]
+    off = np.arange(P, dtype=np.int64)[:, None, None]
+    out = dict(inputs)
+    out["bank"] = shared
+    out["k_idx"] = (np.asarray(inputs["k_idx"], dtype=np.int64) * P + off).astype(np.int32)
+    out["q_idx"] = (np.asarray(inputs["q_idx"], dtype=np.int64) * P + off).astype(np.int32)
+    return out
+
+
+def per_stream_bank(shared: np.ndarray, P: int) -> np.ndarray:
+    """[P, M, hd] view order of a bank interleaved by ``shared_bank_inputs``."""
+    MP, hd = shared.shape
+    return shared.reshape(MP // P, P, hd).transpose(1, 0, 2)
