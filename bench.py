@@ -49,7 +49,68 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 launches)")
+    ap.add_argument("--op", default="sdm_fwd", choices=("sdm_fwd", "topk"),
+                    help="sdm_fwd: the memory op (default); topk: the product-key top-k that selects "
+                         "its slots, on the workload TOPK_WORKLOAD")
     return ap.parse_args()
+
+
+# The product-key top-k workload: the write-slot selection of workload 2's tokens (32 x 4096
+# rows), its 16384 slots as two factors of 128, k = W = 32, bfloat16 scores ~ N(0, 1).
+TOPK_WORKLOAD = dict(rows=32 * 4096, factors=(128, 128), k=32, dtype="bf16", seed=20261202)
+
+
+def bench_topk(args):
+    import torch
+    from chunked_sparse_delta_amd import product_key_topk
+    from oracle import product_key_topk as pko
+    w = TOPK_WORKLOAD
+    D, kk = sum(w["factors"]), min(w["k"], int(np.prod(w["factors"])))
+    rng = np.random.default_rng(w["seed"])
+    x32 = rng.standard_normal((w["rows"], D), dtype=np.float32)
+    bits = workloads.round_bf16_bits(x32)
+    dev = torch.device("cuda:0")
+    raw = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    for _ in range(args.warmup):
+        product_key_topk(raw, w["factors"], w["k"])
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(args.steps):
+        product_key_topk(raw, w["factors"], w["k"])
+    e1.record(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    es = 2
+    alg = w["rows"] * (D * es + kk * (es + 8))   # scores in, values and slot ids out
+    gbs = alg / (kern_ms * 1e-3) / 1e9
+    name = f"pktopk_rows{w['rows']}_f{'x'.join(map(str, w['factors']))}_k{w['k']}_{w['dtype']}"
+    res = {
+        "metric": "product-key top-k rows/sec at 1 MI355X", "value": round(w["rows"] * args.steps / elapsed, 1),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * elapsed / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "rows": w["rows"], "factors": list(w["factors"]), "k": w["k"],
+                   "score_dtype": w["dtype"]},
+        "kernel_ms": {"topk": round(kern_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "topk", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(alg),
+                     "note": "in-LDS sorts per row bound the kernel; the bytes are what the rows must move"},
+    }
+    if not args.no_cpu_baseline:
+        sample = workloads.bf16_bits_to_f32(bits[:256])
+        reps, c0 = 0, time.perf_counter()
+        while time.perf_counter() - c0 < args.cpu_seconds:
+            pko.product_key_topk(sample, w["factors"], w["k"], bf16=True)
+            reps += 1
+        el = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": round(256 * reps / el, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the first 256 rows x {reps} passes of the Python oracle, 1 thread, {el:.1f} s"}
+    print(json.dumps(res), flush=True)
 
 
 PHASE2_SOURCES = ("chunked_sparse_delta_amd/csrc/phase2.hip", "chunked_sparse_delta_amd/csrc/common.h")
@@ -165,6 +226,9 @@ def main():
         print("bench.py: this build runs on exactly one GPU (the forward shards with no exchange across "
               "streams or columns, but no multi-GPU path is built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.op == "topk":
+        bench_topk(args)
+        return
     import torch
     from chunked_sparse_delta_amd import TIMING_EVENTS, plan, sdm_fwd, workspace_bytes
 

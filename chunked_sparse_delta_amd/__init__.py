@@ -17,12 +17,14 @@ the readings [P, T, hd] are returned.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "workspace_bytes", "plan", "library_path",
+__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "product_key_topk", "workspace_bytes", "plan",
+           "library_path",
            "SDM_ERRORS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +95,8 @@ def _load():
             lib.sdm_wy_solve.restype = ctypes.c_int
             lib.sdm_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, p]
             lib.sdm_fwd_plan.restype = ctypes.c_int
+            lib.sdm_product_key_topk.argtypes = [i64, p, i32, p, i32, i32, p, p, p]
+            lib.sdm_product_key_topk.restype = ctypes.c_int
             lib.sdm_error_string.argtypes = [ctypes.c_int]
             lib.sdm_error_string.restype = ctypes.c_char_p
             lib.sdm_last_error.argtypes = []
@@ -289,3 +293,29 @@ def wy_solve(A: torch.Tensor, beta: torch.Tensor, QK: torch.Tensor, stream=None)
     rc = lib.sdm_wy_solve(n, C, _ptr(A), _ptr(beta), _ptr(QK), _ptr(X), _ptr(QX), ctypes.byref(ex))
     _check_rc(lib, rc)
     return X, QX
+
+
+def product_key_topk(raw: torch.Tensor, factors, k: int, stream=None):
+    """Exact top-k over all sums of one value from each product-key factor
+    (sdm_product_key_topk). raw [..., sum(factors)] float32 or bfloat16 on the GPU.
+    Returns (val [..., kk] in raw's dtype, lin [..., kk] int64 ascending),
+    kk = min(k, prod(factors))."""
+    lib = _load()
+    if raw.dtype not in _DTYPES:
+        raise TypeError(f"raw must be float32 or bfloat16, got {raw.dtype}")
+    factors = [int(f) for f in factors]
+    D = sum(factors)
+    if raw.dim() < 1 or raw.shape[-1] != D:
+        raise ValueError(f"raw must be [..., {D}] for factors {factors}, got {tuple(raw.shape)}")
+    if raw.device.type != "cuda" or not raw.is_contiguous():
+        raise ValueError("raw must be a contiguous GPU tensor")
+    kk = min(int(k), math.prod(factors)) if factors else 0
+    lead = tuple(raw.shape[:-1])
+    rows = math.prod(lead) if lead else 1
+    val = torch.empty(lead + (max(kk, 0),), dtype=raw.dtype, device=raw.device)
+    lin = torch.empty(lead + (max(kk, 0),), dtype=torch.int64, device=raw.device)
+    fac = (ctypes.c_int32 * max(1, len(factors)))(*factors)
+    ex = _Exec(_stream_ptr(stream), None, 0, None, 0, None)
+    _check_rc(lib, lib.sdm_product_key_topk(rows, _ptr(raw), _DTYPES[raw.dtype], fac, len(factors), int(k), _ptr(val),
+                                            _ptr(lin), ctypes.byref(ex)))
+    return val, lin

@@ -25,6 +25,9 @@ hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *
                      int64_t stride, int64_t bstride, hipStream_t st);
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st);
 size_t gram_lds_bytes(int C);
+hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, int32_t D, int32_t F, int32_t k,
+                       int32_t kk, bool bf16, const int32_t *fw, hipStream_t st);
+constexpr int kTopkMaxK = 256, kTopkMaxFactor = 4096, kTopkMaxFactors = 8;
 size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M);
 int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, int lds_limit);
 }  // namespace sdm
@@ -262,6 +265,37 @@ int sdm_fwd_plan(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t 
     plan->lds_limit = dev->lds_per_block;
     plan->lds_default = dev->lds_default;
     return SDM_OK;
+}
+
+int sdm_product_key_topk(int64_t rows, const void *raw, int32_t dtype, const int32_t *factors, int32_t num_factors,
+                         int32_t k, void *val, int64_t *lin, const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!exec) return fail(SDM_ERR_NULL, "exec must not be NULL");
+    if (!factors) return fail(SDM_ERR_NULL, "factors must not be NULL");
+    if (dtype != SDM_F32 && dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "raw must be SDM_F32 or SDM_BF16, got %d", dtype);
+    if (rows < 0) return fail(SDM_ERR_SHAPE, "rows must be >= 0, got %lld", (long long)rows);
+    if (rows > int64_t(0x7FFFFFFF)) return fail(SDM_ERR_RANGE, "at most 2^31 - 1 rows, got %lld", (long long)rows);
+    if (num_factors < 1 || num_factors > kTopkMaxFactors)
+        return fail(SDM_ERR_SHAPE, "1 to %d factors, got %d", kTopkMaxFactors, num_factors);
+    if (k < 1 || k > kTopkMaxK) return fail(SDM_ERR_SHAPE, "k must be in 1..%d, got %d", kTopkMaxK, k);
+    int64_t D = 0, prod = 1;
+    for (int f = 0; f < num_factors; ++f) {
+        if (factors[f] < 1) return fail(SDM_ERR_SHAPE, "factor %d has %d columns", f, factors[f]);
+        if (factors[f] > kTopkMaxFactor)
+            return fail(SDM_ERR_UNSUPPORTED, "factor %d has %d columns; at most %d", f, factors[f], kTopkMaxFactor);
+        D += factors[f];
+        if (prod > (int64_t(1) << 55) / factors[f])
+            return fail(SDM_ERR_UNSUPPORTED, "the factors address 2^55 or more slots");
+        prod *= factors[f];
+    }
+    if (rows > 0 && (!raw || !val || !lin)) return fail(SDM_ERR_NULL, "raw, val and lin must not be NULL");
+    const int es = dtype == SDM_F32 ? 4 : 2;
+    if (!aligned(raw, size_t(es)) || !aligned(val, size_t(es)) || !aligned(lin, 8))
+        return fail(SDM_ERR_ALIGN, "raw and val must be aligned to their element size, lin to 8 bytes");
+    const int32_t kk = int32_t(prod < k ? prod : k);
+    const hipError_t e = launch_topk(raw, val, lin, rows, int32_t(D), num_factors, k, kk, dtype == SDM_BF16, factors,
+                                     static_cast<hipStream_t>(exec->stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "top-k launch");
 }
 
 size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t hd, int32_t slab_steps) {

@@ -1,0 +1,197 @@
+// Exact top-k over all sums of product-key factor values, forward (product_key_topk, page
+// 23, product_key_topk.py, the function's docstring): the selection that turns a layer's
+// factor scores into slot ids for the memory op.
+//
+// Rule (restated): a slot takes one column of each of the F factors and scores the float32
+// sum of its values in factor order (bfloat16 input with F > 2: each partial sum rounded to
+// bfloat16 before the next factor is added); scores compare as float32 with -0 below +0 and
+// NaN as -inf. Each factor is ranked by value, larger column first on ties; stage 0 keeps
+// the first n = min(k, f_0) ranks of factor 0; stage f keeps the best c = min(k, n m) pairs
+// (i, j), i < n a rank of the previous stage, j < m = min(k, f_f) a rank of factor f, with
+// (i + 1)(j + 1) <= c, exact ties to the larger i + j, then the larger i. The kept slots
+// are returned by ascending linear index, with their scores rounded to the input dtype.
+//
+// One workgroup of 256 threads per row; every ordering is a bitonic sort in LDS of 64-bit
+// keys whose high word is the float32 order and whose low word encodes the tie rule, so
+// each comparison is one unsigned compare and the result is unique:
+//   factor ranks   key = order(value) << 32 | column               (descending)
+//   stage pairs    key = order(score) << 32 | (i + j) << 8 | i      (descending)
+//   output         key = lin << 8 | position in the last stage      (ascending)
+#include "common.h"
+
+namespace sdm {
+
+// Limits (the host entry point checks them before any launch).
+constexpr int kTopkBlock = 256;
+constexpr int kTopkMaxK = 256;
+constexpr int kTopkMaxFactor = 4096;      // columns per factor
+constexpr int kTopkMaxFactors = 8;
+constexpr int kTopkPairs = 2048;          // >= sum over i < 256 of min(256, 256 / (i + 1)) = 1567
+
+// The float32 order of the rule as an unsigned key: NaN as -inf, -0 below +0.
+__device__ __forceinline__ uint32_t topk_order(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) u = 0xFF800000u;   // NaN -> -inf
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_round(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7F800000u) == 0x7F800000u) return x;   // inf, NaN
+    const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    return __uint_as_float(r);
+}
+
+// Bitonic sort of n (a power of two) keys in LDS by the whole workgroup; descending when
+// desc. Ends with a barrier.
+__device__ void topk_bitonic(uint64_t *key, int n, bool desc) {
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = threadIdx.x; t < (n >> 1); t += kTopkBlock) {
+                // t-th pair of this step: i has bit `stride` clear, partner i + stride
+                const int i = ((t / stride) * (stride << 1)) + (t % stride);
+                const int jx = i + stride;
+                const bool up = ((i & size) == 0) != desc;   // ascending block unless desc
+                const uint64_t a = key[i], b = key[jx];
+                if ((a > b) == up) {
+                    key[i] = b;
+                    key[jx] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+struct TopkArgs {
+    const void *raw;          // [rows, D]
+    void *val;                // [rows, kk] in the input dtype
+    int64_t *lin;             // [rows, kk]
+    int64_t rows;
+    int32_t D, F, k, kk, bf16;
+    int32_t fw[kTopkMaxFactors];   // factor widths
+    int32_t f0[kTopkMaxFactors];   // first column of each factor
+};
+
+__global__ __launch_bounds__(kTopkBlock) void topk_kernel(TopkArgs a) {
+    __shared__ uint64_t key[kTopkMaxFactor > kTopkPairs ? kTopkMaxFactor : kTopkPairs];
+    __shared__ float rval[kTopkMaxFactors][kTopkMaxK];   // factor f's rank r: value
+    __shared__ int32_t rcol[kTopkMaxFactors][kTopkMaxK];  //                    column
+    __shared__ float cs[2][kTopkMaxK];                    // current / next stage: scores
+    __shared__ int64_t cl[2][kTopkMaxK];                  //                       linear indices
+    __shared__ int32_t off[kTopkMaxK + 1];                // pair offsets per rank i
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const char *rowp = static_cast<const char *>(a.raw) + row * int64_t(a.D) * (a.bf16 ? 2 : 4);
+    auto value = [&](int c) -> float {
+        return a.bf16 ? __uint_as_float(uint32_t(reinterpret_cast<const uint16_t *>(rowp)[c]) << 16)
+                      : reinterpret_cast<const float *>(rowp)[c];
+    };
+
+    // Rank every factor: the first min(k, f) entries of (value desc, column desc).
+    for (int f = 0; f < a.F; ++f) {
+        const int w = a.fw[f], n2 = w <= 1 ? 1 : 1 << (32 - __clz(w - 1));
+        for (int c = tid; c < n2; c += kTopkBlock)
+            key[c] = c < w ? (uint64_t(topk_order(value(a.f0[f] + c))) << 32) | uint32_t(c) : 0ull;
+        __syncthreads();
+        topk_bitonic(key, n2, true);
+        const int m = min(a.k, w);
+        for (int r = tid; r < m; r += kTopkBlock) {
+            const int c = int(uint32_t(key[r]));
+            rcol[f][r] = c;
+            rval[f][r] = value(a.f0[f] + c);
+        }
+        __syncthreads();
+    }
+    // Stage 0
+    int n = min(a.k, a.fw[0]);
+    for (int r = tid; r < n; r += kTopkBlock) {
+        cs[0][r] = rval[0][r];
+        cl[0][r] = rcol[0][r];
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int f = 1; f < a.F; ++f) {
+        const int m = min(a.k, a.fw[f]);
+        const int c = int(min(int64_t(a.k), int64_t(n) * m));
+        const bool rnd = a.bf16 && a.F > 2 && f < a.F - 1;
+        // pairs of rank i: j < min(m, c / (i + 1)); offsets by a serial scan (n <= 256)
+        if (tid == 0) {
+            int s = 0;
+            for (int i = 0; i < n; ++i) {
+                off[i] = s;
+                s += min(m, c / (i + 1));
+            }
+            off[n] = s;
+        }
+        __syncthreads();
+        const int np = off[n];
+        const int n2 = np <= 1 ? 1 : 1 << (32 - __clz(np - 1));
+        for (int q = tid; q < n2; q += kTopkBlock) {
+            uint64_t kv = 0ull;
+            if (q < np) {
+                int lo = 0, hi = n - 1;   // the rank i whose pairs hold q
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (off[mid] <= q) lo = mid;
+                    else hi = mid - 1;
+                }
+                const int i = lo, j = q - off[i];
+                float s = cs[cur][i] + rval[f][j];
+                if (rnd) s = bf16_round(s);
+                kv = (uint64_t(topk_order(s)) << 32) | uint32_t(((i + j) << 8) | i);
+            }
+            key[q] = kv;
+        }
+        __syncthreads();
+        topk_bitonic(key, n2, true);
+        for (int r = tid; r < c; r += kTopkBlock) {
+            const uint32_t lo32 = uint32_t(key[r]);
+            const int i = int(lo32 & 0xFFu), j = int((lo32 >> 8) & 0x1FFu) - i;
+            float s = cs[cur][i] + rval[f][j];
+            if (rnd) s = bf16_round(s);
+            cs[cur ^ 1][r] = s;
+            cl[cur ^ 1][r] = cl[cur][i] * a.fw[f] + rcol[f][j];
+        }
+        __syncthreads();
+        cur ^= 1;
+        n = c;
+    }
+    // Output by ascending linear index (unique, < 2^55)
+    const int n2 = n <= 1 ? 1 : 1 << (32 - __clz(n - 1));
+    for (int r = tid; r < n2; r += kTopkBlock) key[r] = r < n ? (uint64_t(cl[cur][r]) << 8) | uint32_t(r) : ~0ull;
+    __syncthreads();
+    topk_bitonic(key, n2, false);
+    for (int r = tid; r < n; r += kTopkBlock) {
+        const int src = int(key[r] & 0xFFu);
+        const float s = cs[cur][src];
+        a.lin[row * a.kk + r] = cl[cur][src];
+        if (a.bf16) reinterpret_cast<uint16_t *>(a.val)[row * a.kk + r] = uint16_t(__float_as_uint(bf16_round(s)) >> 16);
+        else reinterpret_cast<float *>(a.val)[row * a.kk + r] = s;
+    }
+}
+
+hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, int32_t D, int32_t F, int32_t k,
+                       int32_t kk, bool bf16, const int32_t *fw, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    TopkArgs a{};
+    a.raw = raw;
+    a.val = val;
+    a.lin = lin;
+    a.rows = rows;
+    a.D = D;
+    a.F = F;
+    a.k = k;
+    a.kk = kk;
+    a.bf16 = bf16 ? 1 : 0;
+    int32_t c0 = 0;
+    for (int f = 0; f < F; ++f) {
+        a.fw[f] = fw[f];
+        a.f0[f] = c0;
+        c0 += fw[f];
+    }
+    hipLaunchKernelGGL(topk_kernel, dim3(unsigned(rows)), dim3(kTopkBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace sdm

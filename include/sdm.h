@@ -208,6 +208,29 @@ typedef struct {
 int sdm_fwd_plan(int32_t streams, int32_t tokens, int32_t chunk, int32_t W, int32_t R, int32_t head_dim,
                  int64_t rows, int32_t dtype, sdm_plan *plan);
 
+/*
+ * Exact top-k over all sums of one value from each product-key factor (product_key_topk,
+ * page 23, product_key_topk.py docstring): the slot selection that feeds write and read
+ * slot ids.
+ *   raw: device [rows, sum(factors)] in dtype (SDM_F32 or SDM_BF16), the factors side by
+ *     side. factors: HOST array of num_factors (1..8) widths, each 1..4096 columns, their
+ *     product below 2^55. k: 1..256; kk = min(k, product of the factors).
+ *   val: device [rows, kk] in dtype: the selected slots' scores (float32 sums of their
+ *     factor values in factor order; bfloat16 with more than two factors rounds each
+ *     partial sum to bfloat16 before the next factor), rounded to dtype.
+ *   lin: device int64 [rows, kk]: the selected slots (c_0 .. c_{F-1}) as
+ *     (..(c_0 factors[1] + c_1) ..) factors[F-1] + c_{F-1}, strictly ascending per row.
+ *   Selection rule (exact ties included): scores compare as float32, -0 below +0, NaN as
+ *   -inf; each factor is ranked by value, larger column first on ties; stage f = 1.. keeps
+ *   the best c = min(k, n m) pairs (i, j) of a previous rank i < n and a rank j < m =
+ *   min(k, factors[f]) with (i + 1)(j + 1) <= c, ties to the larger i + j, then larger i.
+ *   exec->stream only (no workspace). rows = 0 does nothing. Returns SDM_OK or a negative
+ *   SDM_ERR_* before any launch (SDM_ERR_UNSUPPORTED for factors past the limits).
+ */
+int sdm_product_key_topk(int64_t rows, const void *raw, int32_t dtype, const int32_t *factors,
+                         int32_t num_factors, int32_t k, void *val, int64_t *lin,
+                         const sdm_exec *exec);
+
 /* Static text for an SDM_* code. */
 const char *sdm_error_string(int code);
 

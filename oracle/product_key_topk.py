@@ -1,0 +1,123 @@
+"""Product-key exact top-k, forward, on the CPU. TEST INFRASTRUCTURE, NOT PRODUCT.
+
+The selection rule of ``product_key_topk`` (page 23, product_key_topk.py, the function's
+docstring), taken step by step in plain Python:
+
+  * a slot (c_0, .., c_{F-1}) takes one column of each factor; its score is the float32 sum
+    of its factor values in factor order; with bfloat16 input and more than two factors each
+    partial sum is rounded to bfloat16 before the next factor is added;
+  * scores compare as float32 numbers with -0 below +0 and NaN counted as -inf;
+  * each factor is ranked by value, larger column first on ties; one factor selects its
+    first kk ranks;
+  * stage f = 1 .. F-1 keeps the best c = min(k, n m) of the pairs (i, j) of a rank i < n of
+    the previous stage and a rank j < m = min(k, factors[f]) of factor f with
+    (i + 1)(j + 1) <= c, exact ties going to the larger i + j, then the larger i;
+  * the result is lin = (..(c_0 factors[1] + c_1) ..) factors[F-1] + c_{F-1} strictly
+    ascending, and val = the slot's score rounded to the input dtype.
+
+Readings where the text leaves a step open (also listed in the design doc): the stage that adds
+a factor other than the last one ranks its pairs by the partial sum it carries forward (the
+bfloat16-rounded one when rounding applies); the last stage ranks by the float32 sum.
+
+Pins (tests/test_topk_oracle.py): the brute-force top-k over every slot on tie-free inputs,
+hand-worked tie cases, one factor, k at and above the slot count, the -0 / NaN order, and the
+rounding of partial sums.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MAX_K = 256
+
+
+def order_key(x: float) -> tuple:
+    """The float32 comparison of the rule as a sortable key: NaN as -inf, -0 below +0."""
+    x = float(np.float32(x))
+    if math.isnan(x):
+        x = -math.inf
+    return (x, 0 if (x == 0.0 and math.copysign(1.0, x) < 0) else 1)
+
+
+def round_bf16(x: np.float32) -> np.float32:
+    """Nearest bfloat16 of a float32 (ties to even), as a float32."""
+    u = np.array([x], dtype=np.float32).view(np.uint32)[0]
+    if (u & 0x7F800000) == 0x7F800000:   # inf or NaN: keep (NaN stays NaN)
+        return np.float32(x)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) & np.uint32(0xFFFF0000)
+    return np.array([r], dtype=np.uint32).view(np.float32)[0]
+
+
+def topk_row(row: np.ndarray, factors, k: int, bf16: bool):
+    """One row: ``row`` float32 values of the factors side by side (exact copies of the
+    input, bfloat16 inputs widened). Returns (val list of float32, lin list of int), lin
+    ascending; val not yet rounded to the input dtype."""
+    F = len(factors)
+    assert F >= 1 and 1 <= k <= MAX_K and len(row) == sum(factors)
+    starts = np.cumsum([0] + list(factors))[:-1]
+    ranks = []
+    for f, w in enumerate(factors):
+        vals = [np.float32(row[starts[f] + c]) for c in range(w)]
+        # value descending, larger column first on ties
+        order = sorted(range(w), key=lambda c: (order_key(vals[c]), c), reverse=True)
+        ranks.append([(vals[c], c) for c in order])
+    kk = min(k, math.prod(factors))
+    # stage 0: the first ranks of factor 0
+    n = min(k, factors[0])
+    cur = [(ranks[0][i][0], ranks[0][i][1]) for i in range(n)]   # (score, lin) in rank order
+    for f in range(1, F):
+        m = min(k, factors[f])
+        c = min(k, len(cur) * m)
+        pairs = []
+        for i in range(len(cur)):
+            for j in range(m):
+                if (i + 1) * (j + 1) > c:
+                    break
+                with np.errstate(invalid="ignore", over="ignore"):   # inf - inf is NaN, as on the GPU
+                    s = np.float32(cur[i][0] + ranks[f][j][0])
+                if bf16 and F > 2 and f < F - 1:
+                    s = round_bf16(s)
+                pairs.append((s, i, j))
+        # score descending; exact ties to the larger i + j, then the larger i
+        pairs.sort(key=lambda q: (order_key(q[0]), q[1] + q[2], q[1]), reverse=True)
+        cur = [(s, cur[i][1] * factors[f] + ranks[f][j][1]) for s, i, j in pairs[:c]]
+    assert len(cur) == kk
+    cur.sort(key=lambda q: q[1])
+    return [s for s, _ in cur], [lin for _, lin in cur]
+
+
+def product_key_topk(raw: np.ndarray, factors, k: int, bf16: bool = False):
+    """raw [N, sum(factors)] float32 (bfloat16 inputs widened exactly, ``bf16`` set).
+    Returns (val [N, kk] float32 holding the scores rounded to the input dtype, lin [N, kk]
+    int64)."""
+    raw = np.asarray(raw, dtype=np.float32)
+    N = raw.shape[0]
+    kk = min(k, math.prod(factors))
+    val = np.zeros((N, kk), dtype=np.float32)
+    lin = np.zeros((N, kk), dtype=np.int64)
+    for r in range(N):
+        v, l = topk_row(raw[r], factors, k, bf16)
+        val[r] = [round_bf16(x) if bf16 else x for x in v]
+        lin[r] = l
+    return val, lin
+
+
+def brute_force_topk(row: np.ndarray, factors, k: int):
+    """The kk best slots of one row over every slot (float32 sums in factor order, no
+    rounding), as a set of lin. Only meaningful where no two scores tie."""
+    starts = np.cumsum([0] + list(factors))[:-1]
+    scores = []
+    for idx in np.ndindex(*factors):
+        s = np.float32(0.0)
+        for f, c in enumerate(idx):
+            s = np.float32(s + np.float32(row[starts[f] + c])) if f else np.float32(row[starts[f] + c])
+        lin = 0
+        for f, c in enumerate(idx):
+            lin = lin * factors[f] + c
+        scores.append((order_key(s), lin))
+    scores.sort(reverse=True)
+    kk = min(k, math.prod(factors))
+    return {lin for _, lin in scores[:kk]}

@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["sdm_chunk_mats", "sdm_error_string", "sdm_fwd", "sdm_fwd_plan",
-                                    "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_wy_solve"]
+                                    "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_product_key_topk",
+                                    "sdm_wy_solve"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -189,3 +190,28 @@ def test_plan_rejects_before_any_device_query(lib):
     assert f(8, 2048, 8, 8, 8, 64, 4096, 1, ctypes.byref(pl)) == RANGE
     assert f(8, 2048, 64, 8, 8, 64, 4096, 7, ctypes.byref(pl)) == DTYPE
     assert f(8, 2048, 64, 8, 8, 64, 0, 1, ctypes.byref(pl)) == RANGE
+
+
+def test_topk_rejects_before_any_launch(lib):
+    from chunked_sparse_delta_amd import _Exec
+    f = lib.sdm_product_key_topk
+    f.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    ex = _Exec(None, None, 0, None, 0, None)
+    fake = Call.FAKE
+
+    def call(rows=4, dtype=0, factors=(16, 16), k=8, raw=fake, val=fake, lin=fake, e=ex):
+        fa = (ctypes.c_int32 * len(factors))(*factors)
+        return f(rows, raw, dtype, fa, len(factors), k, val, lin, None if e is None else ctypes.byref(e))
+
+    assert call(e=None) == NULL
+    assert call(dtype=3) == DTYPE
+    assert call(rows=-1) == SHAPE
+    assert call(factors=()) == SHAPE and call(factors=(2,) * 9) == SHAPE
+    assert call(factors=(16, 0)) == SHAPE
+    assert call(k=0) == SHAPE and call(k=257) == SHAPE
+    assert call(factors=(4097, 2)) == UNSUPPORTED
+    assert call(factors=(4096,) * 5) == UNSUPPORTED         # 2^60 slots
+    assert call(raw=None) == NULL and call(lin=None) == NULL
+    assert call(raw=fake + 2) == ALIGN and call(dtype=1, raw=fake + 1) == ALIGN and call(lin=fake + 4) == ALIGN
+    assert call(rows=0, raw=None, val=None, lin=None) == OK

@@ -1,0 +1,81 @@
+"""Product-key exact top-k on the GPU (sdm_product_key_topk through the C ABI) against the
+oracle (oracle/product_key_topk.py): the selected slots and their scores bit for bit,
+including exact ties (integer-valued rows), -0 / +0, infinities and NaN."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import product_key_topk as pk
+
+pytestmark = pytest.mark.gpu
+
+
+def _raw(kind, rows, D, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        x = rng.normal(size=(rows, D))
+    elif kind == "ties":               # few distinct values: exact ties everywhere
+        x = rng.integers(-3, 4, size=(rows, D)).astype(np.float64)
+    else:                              # signed zeros, infinities and NaN among normals
+        x = rng.normal(size=(rows, D))
+        pick = rng.random((rows, D))
+        x[pick < 0.05] = 0.0
+        x[(pick >= 0.05) & (pick < 0.10)] = -0.0
+        x[(pick >= 0.10) & (pick < 0.12)] = np.inf
+        x[(pick >= 0.12) & (pick < 0.14)] = -np.inf
+        x[(pick >= 0.14) & (pick < 0.16)] = np.nan
+    return x.astype(np.float32)
+
+
+def _to_dtype(x32, dtype, device):
+    if dtype == "bf16":
+        bits = workloads.round_bf16_bits(x32)
+        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+        return t, workloads.bf16_bits_to_f32(bits)
+    return torch.from_numpy(x32).to(device), x32
+
+
+def _bits(t):
+    y = t.detach().cpu()
+    return (y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)).numpy()
+
+
+def _oracle_val_bits(val, dtype):
+    if dtype == "bf16":
+        return (val.view(np.uint32) >> 16).astype(np.uint16).view(np.int16)
+    return val.view(np.int32)
+
+
+CASES = [("f32", (16, 16), 8), ("f32", (33, 70), 40), ("bf16", (64, 64), 32), ("bf16", (5, 7, 9), 20),
+         ("bf16", (4, 3, 5, 2), 50), ("f32", (300,), 17), ("f32", (2, 3), 10), ("bf16", (512, 512), 256),
+         ("f32", (1000, 4096), 64), ("f32", (3, 3, 3), 27), ("f32", (7, 5, 3, 2, 2), 33)]
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special"])
+@pytest.mark.parametrize("dtype,factors,k", CASES, ids=[f"{d}-{'x'.join(map(str, f))}-k{k}" for d, f, k in CASES])
+def test_topk_matches_oracle(gpu, dtype, factors, k, kind):
+    from chunked_sparse_delta_amd import product_key_topk
+    rows = 12
+    x32 = _raw(kind, rows, sum(factors), seed=sum(factors) + 7 * k + len(kind))
+    t, exact = _to_dtype(x32, dtype, gpu)
+    val, lin = product_key_topk(t, factors, k)
+    torch.cuda.synchronize()
+    ov, ol = pk.product_key_topk(exact, factors, k, bf16=dtype == "bf16")
+    assert lin.shape == ol.shape and val.dtype == t.dtype
+    assert np.array_equal(lin.cpu().numpy(), ol), kind
+    got, want = _bits(val), _oracle_val_bits(ov, dtype)
+    both_nan = np.isnan(val.float().cpu().numpy()) & np.isnan(ov)
+    assert np.array_equal(np.where(both_nan, 0, got), np.where(both_nan, 0, want)), kind
+
+
+def test_topk_leading_dims_and_empty(gpu):
+    from chunked_sparse_delta_amd import product_key_topk
+    x = torch.randn(2, 3, 40, device=gpu)
+    val, lin = product_key_topk(x, (8, 32), 12)
+    assert val.shape == (2, 3, 12) and lin.shape == (2, 3, 12)
+    v2, l2 = product_key_topk(x.reshape(6, 40), (8, 32), 12)
+    assert torch.equal(lin.reshape(6, 12), l2) and torch.equal(val.reshape(6, 12), v2)
+    v0, l0 = product_key_topk(torch.empty(0, 40, device=gpu), (8, 32), 12)
+    assert v0.shape == (0, 12) and l0.shape == (0, 12)

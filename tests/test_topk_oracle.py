@@ -1,0 +1,72 @@
+"""Pins of the product-key top-k oracle (oracle/product_key_topk.py) against what the rule
+of page 23 (product_key_topk.py, product_key_topk docstring) fixes: the brute-force top-k
+over every slot where no scores tie, hand-worked tie cases, the -0 / NaN order, one factor,
+k at and above the slot count, and bfloat16 rounding of partial sums."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import product_key_topk as pk
+
+
+@pytest.mark.parametrize("factors,k", [
+    ((5, 7), 1), ((5, 7), 3), ((5, 7), 10), ((5, 7), 35), ((5, 7), 200),
+    ((4, 3, 5), 7), ((4, 3, 5), 60), ((3, 3, 2, 4), 11), ((9,), 4), ((2, 17), 16), ((16, 16), 40),
+])
+def test_staged_rule_equals_brute_force_without_ties(factors, k):
+    rng = np.random.default_rng(sum(factors) * 131 + k)
+    raw = rng.normal(size=(6, sum(factors))).astype(np.float32)
+    val, lin = pk.product_key_topk(raw, factors, k)
+    kk = min(k, math.prod(factors))
+    assert val.shape == (6, kk) and lin.shape == (6, kk)
+    starts = np.cumsum([0] + list(factors))[:-1]
+    for r in range(6):
+        assert set(lin[r].tolist()) == pk.brute_force_topk(raw[r], factors, k)
+        assert np.all(np.diff(lin[r]) > 0)
+        for x, l in zip(val[r], lin[r]):   # the score of the slot, summed in factor order
+            cols = np.unravel_index(int(l), factors)
+            s = np.float32(raw[r, starts[0] + cols[0]])
+            for f in range(1, len(factors)):
+                s = np.float32(s + raw[r, starts[f] + cols[f]])
+            assert x == s
+
+
+def test_ties_follow_the_stated_order():
+    """factors (2, 2), k = 2, all four scores 1: factor ranks put the larger column first
+    (col 1, col 0); stage 1 keeps c = 2 of the pairs (0,0), (0,1), (1,0) by the larger
+    i + j, then the larger i: (1,0) -> slot (0, 1) = lin 1, then (0,1) -> slot (1, 0) = lin 2."""
+    val, lin = pk.product_key_topk(np.array([[1, 1, 0, 0]], np.float32), (2, 2), 2)
+    assert lin.tolist() == [[1, 2]] and val.tolist() == [[1.0, 1.0]]
+
+
+def test_signed_zero_and_nan_order():
+    val, lin = pk.product_key_topk(np.array([[-0.0, 0.0, -1.0]], np.float32), (3,), 1)
+    assert lin.tolist() == [[1]] and math.copysign(1.0, float(val[0, 0])) > 0
+    # NaN counts as -inf and ties with it: larger column first
+    val, lin = pk.product_key_topk(np.array([[np.nan, -np.inf, -5.0]], np.float32), (3,), 2)
+    assert lin.tolist() == [[1, 2]] and val[0, 0] == -np.inf and val[0, 1] == -5.0
+
+
+def test_one_factor_and_k_beyond_the_slots():
+    raw = np.array([[0.5, -2.0, 3.0, 0.25, 3.0]], np.float32)
+    val, lin = pk.product_key_topk(raw, (5,), 3)
+    assert lin.tolist() == [[0, 2, 4]]                       # 3.0 (col 4), 3.0 (col 2), 0.5
+    val, lin = pk.product_key_topk(np.arange(5, dtype=np.float32)[None], (2, 3), 10)
+    assert lin.tolist() == [list(range(6))]                  # kk = 6: every slot
+
+
+def test_bf16_partial_sums_round_before_the_next_factor():
+    """1 + 2^-8 is a bfloat16 tie that rounds to 1 (even): with three bfloat16 factors the
+    partial sum 1 + 2^-8 becomes 1 before the third 2^-8 is added; float32 keeps it."""
+    row = np.array([1.0, 2.0 ** -8, 2.0 ** -8], np.float32)
+    v, _ = pk.topk_row(row, (1, 1, 1), 1, bf16=True)
+    assert v == [np.float32(1.0 + 2.0 ** -8)]
+    v, _ = pk.topk_row(row, (1, 1, 1), 1, bf16=False)
+    assert v == [np.float32(1.0 + 2.0 ** -7)]
+    assert pk.round_bf16(np.float32(1.0 + 2.0 ** -8)) == np.float32(1.0)
+    assert pk.round_bf16(np.float32(1.0 + 3 * 2.0 ** -8)) == np.float32(1.0 + 2.0 ** -6)
+    # two factors: no partial rounding
+    v, _ = pk.topk_row(np.array([1.0, 2.0 ** -8], np.float32), (1, 1), 1, bf16=True)
+    assert v == [np.float32(1.0 + 2.0 ** -8)]
