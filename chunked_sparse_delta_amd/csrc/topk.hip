@@ -11,12 +11,16 @@
 // (i + 1)(j + 1) <= c, exact ties to the larger i + j, then the larger i. The kept slots
 // are returned by ascending linear index, with their scores rounded to the input dtype.
 //
-// One workgroup of 256 threads per row; every ordering is a bitonic sort in LDS of 64-bit
+// General rows: one workgroup of 256 threads per row; every ordering is a bitonic sort in LDS of 64-bit
 // keys whose high word is the float32 order and whose low word encodes the tie rule, so
 // each comparison is one unsigned compare and the result is unique:
 //   factor ranks   key = order(value) << 32 | column               (descending)
 //   stage pairs    key = order(score) << 32 | (i + j) << 8 | i      (descending)
 //   output         key = lin << 8 | position in the last stage      (ascending)
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.h"
 
 namespace sdm {
@@ -171,6 +175,178 @@ __global__ __launch_bounds__(kTopkBlock) void topk_kernel(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Small rows (every factor <= 256 columns, k <= 64): one row per wavefront, four rows per
+// workgroup. The same keys, sorted in registers: element e = r * 64 + lane of a wave's
+// R registers; partners at distance >= 64 are the lane's own registers, nearer ones come
+// by lane shuffles. Only the per-wave LDS tables (factor ranks, stage lists, pair offsets)
+// are shared between lanes, with nothing but the wave's own in-order LDS accesses.
+constexpr int kTopkWaveFactor = 256, kTopkWaveK = 64, kTopkWavePairs = 512;   // >= 64 H(64) = 304
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+    const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(x)), m, 64));
+    const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(x >> 32)), m, 64));
+    return (uint64_t(hi) << 32) | lo;
+}
+
+// Bitonic sort of the 64 R keys held by the wave (element r * 64 + lane in k[r]).
+template <int R>
+__device__ __forceinline__ void wave_bitonic(uint64_t (&k)[R], bool desc, int lane) {
+    constexpr int N = 64 * R;
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 64) {
+                const int rs = stride >> 6;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int r2 = r ^ rs;
+                    if (r2 < r) continue;
+                    const int e = r * 64 + lane;
+                    const bool up = ((e & size) == 0) != desc;
+                    const uint64_t a = k[r], b = k[r2];
+                    if ((a > b) == up) {
+                        k[r] = b;
+                        k[r2] = a;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint64_t o = shfl_xor64(k[r], stride);
+                    const int e = r * 64 + lane;
+                    const bool up = ((e & size) == 0) != desc, lower = (lane & stride) == 0;
+                    // the lower element of the pair keeps the smaller key in an ascending block
+                    k[r] = (lower == up) ? (k[r] < o ? k[r] : o) : (k[r] > o ? k[r] : o);
+                }
+            }
+        }
+    }
+}
+
+struct TopkWaveLds {
+    float rval[kTopkMaxFactors][kTopkWaveK];
+    int32_t rcol[kTopkMaxFactors][kTopkWaveK];
+    float cs[2][kTopkWaveK];
+    int64_t cl[2][kTopkWaveK];
+    int32_t off[kTopkWaveK + 1];
+};
+
+__global__ __launch_bounds__(kTopkBlock) void topk_wave_kernel(TopkArgs a) {
+    constexpr int kWaves = kTopkBlock / 64;
+    __shared__ TopkWaveLds lds_all[kWaves];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = int64_t(blockIdx.x) * kWaves + wv;
+    if (row >= a.rows) return;
+    TopkWaveLds &L = lds_all[wv];
+    const char *rowp = static_cast<const char *>(a.raw) + row * int64_t(a.D) * (a.bf16 ? 2 : 4);
+    auto value = [&](int c) -> float {
+        return a.bf16 ? __uint_as_float(uint32_t(reinterpret_cast<const uint16_t *>(rowp)[c]) << 16)
+                      : reinterpret_cast<const float *>(rowp)[c];
+    };
+    // factor ranks: sort (order(value) << 32 | column) descending, keep the first min(k, w);
+    // the sort spans the fewest registers that hold the factor
+    for (int f = 0; f < a.F; ++f) {
+        const int w = a.fw[f];
+        auto rank = [&](auto rc) {
+            constexpr int R = decltype(rc)::value;
+            uint64_t k[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int c = r * 64 + lane;
+                k[r] = c < w ? (uint64_t(topk_order(value(a.f0[f] + c))) << 32) | uint32_t(c) : 0ull;
+            }
+            wave_bitonic<R>(k, true, lane);
+            if (lane < min(a.k, w)) {
+                const int c = int(uint32_t(k[0]));
+                L.rcol[f][lane] = c;
+                L.rval[f][lane] = value(a.f0[f] + c);
+            }
+        };
+        if (w <= 64) rank(std::integral_constant<int, 1>{});
+        else if (w <= 128) rank(std::integral_constant<int, 2>{});
+        else rank(std::integral_constant<int, 4>{});
+    }
+    __builtin_amdgcn_wave_barrier();
+    int n = min(a.k, a.fw[0]);
+    if (lane < n) {
+        L.cs[0][lane] = L.rval[0][lane];
+        L.cl[0][lane] = L.rcol[0][lane];
+    }
+    __builtin_amdgcn_wave_barrier();
+    int cur = 0;
+    for (int f = 1; f < a.F; ++f) {
+        const int m = min(a.k, a.fw[f]);
+        const int c = min(a.k, n * m);
+        const bool rnd = a.bf16 && a.F > 2 && f < a.F - 1;
+        // pairs of rank i (one lane each): j < min(m, c / (i + 1)); exclusive offsets by a scan
+        const int cnt = lane < n ? min(m, c / (lane + 1)) : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += y;
+        }
+        L.off[lane] = incl - cnt;
+        if (lane == 63) L.off[64] = incl;
+        __builtin_amdgcn_wave_barrier();
+        const int np = L.off[64];
+        // the stage's pairs, sorted over the fewest registers that hold them; leaves the
+        // best pair keys in registers 0 of lanes 0 .. c - 1
+        uint64_t best = 0ull;
+        auto pairs = [&](auto rc) {
+            constexpr int R = decltype(rc)::value;
+            uint64_t k[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int q = r * 64 + lane;
+                k[r] = 0ull;
+                if (q < np) {
+                    int lo = 0, hi = n - 1;   // the rank i whose pairs hold q
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (L.off[mid] <= q) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    const int i = lo, j = q - L.off[i];
+                    float s = L.cs[cur][i] + L.rval[f][j];
+                    if (rnd) s = bf16_round(s);
+                    k[r] = (uint64_t(topk_order(s)) << 32) | uint32_t(((i + j) << 8) | i);
+                }
+            }
+            wave_bitonic<R>(k, true, lane);
+            best = k[0];
+        };
+        if (np <= 64) pairs(std::integral_constant<int, 1>{});
+        else if (np <= 128) pairs(std::integral_constant<int, 2>{});
+        else if (np <= 256) pairs(std::integral_constant<int, 4>{});
+        else pairs(std::integral_constant<int, 8>{});
+        if (lane < c) {
+            const uint32_t lo32 = uint32_t(best);
+            const int i = int(lo32 & 0xFFu), j = int((lo32 >> 8) & 0x1FFu) - i;
+            float s = L.cs[cur][i] + L.rval[f][j];
+            if (rnd) s = bf16_round(s);
+            L.cs[cur ^ 1][lane] = s;
+            L.cl[cur ^ 1][lane] = L.cl[cur][i] * a.fw[f] + L.rcol[f][j];
+        }
+        __builtin_amdgcn_wave_barrier();
+        cur ^= 1;
+        n = c;
+    }
+    // output by ascending linear index
+    uint64_t k1[1];
+    k1[0] = lane < n ? (uint64_t(L.cl[cur][lane]) << 8) | uint32_t(lane) : ~0ull;
+    wave_bitonic<1>(k1, false, lane);
+    if (lane < n) {
+        const int src = int(k1[0] & 0xFFu);
+        const float s = L.cs[cur][src];
+        a.lin[row * a.kk + lane] = L.cl[cur][src];
+        if (a.bf16) reinterpret_cast<uint16_t *>(a.val)[row * a.kk + lane] = uint16_t(__float_as_uint(bf16_round(s)) >> 16);
+        else reinterpret_cast<float *>(a.val)[row * a.kk + lane] = s;
+    }
+}
+
 hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, int32_t D, int32_t F, int32_t k,
                        int32_t kk, bool bf16, const int32_t *fw, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
@@ -190,7 +366,14 @@ hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, i
         a.f0[f] = c0;
         c0 += fw[f];
     }
-    hipLaunchKernelGGL(topk_kernel, dim3(unsigned(rows)), dim3(kTopkBlock), 0, st, a);
+    bool small = k <= kTopkWaveK;
+    for (int f = 0; f < F; ++f) small = small && fw[f] <= kTopkWaveFactor;
+    const char *env = getenv("SDM_TOPK_PATH");   // "block" forces the general kernel (tests)
+    if (env && env[0] == 'b') small = false;
+    if (small)
+        hipLaunchKernelGGL(topk_wave_kernel, dim3(unsigned((rows + 3) / 4)), dim3(kTopkBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL(topk_kernel, dim3(unsigned(rows)), dim3(kTopkBlock), 0, st, a);
     return hipGetLastError();
 }
 

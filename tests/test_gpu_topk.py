@@ -53,11 +53,18 @@ CASES = [("f32", (16, 16), 8), ("f32", (33, 70), 40), ("bf16", (64, 64), 32), ("
          ("f32", (1000, 4096), 64), ("f32", (3, 3, 3), 27), ("f32", (7, 5, 3, 2, 2), 33)]
 
 
+@pytest.mark.parametrize("path", ["auto", "block"])
 @pytest.mark.parametrize("kind", ["normal", "ties", "special"])
 @pytest.mark.parametrize("dtype,factors,k", CASES, ids=[f"{d}-{'x'.join(map(str, f))}-k{k}" for d, f, k in CASES])
-def test_topk_matches_oracle(gpu, dtype, factors, k, kind):
+def test_topk_matches_oracle(gpu, dtype, factors, k, kind, path, monkeypatch):
+    """auto: rows of factors <= 256 columns with k <= 64 run one row per wavefront (sorts in
+    registers), the others one row per workgroup; block: every row on the workgroup kernel."""
     from chunked_sparse_delta_amd import product_key_topk
-    rows = 12
+    if path == "block":
+        monkeypatch.setenv("SDM_TOPK_PATH", "block")
+    else:
+        monkeypatch.delenv("SDM_TOPK_PATH", raising=False)
+    rows = 13   # not a multiple of the four rows of a wavefront workgroup
     x32 = _raw(kind, rows, sum(factors), seed=sum(factors) + 7 * k + len(kind))
     t, exact = _to_dtype(x32, dtype, gpu)
     val, lin = product_key_topk(t, factors, k)
