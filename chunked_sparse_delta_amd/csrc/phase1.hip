@@ -550,6 +550,7 @@ __device__ __forceinline__ void cold_row_at(int C, int nl, const int4 *spk, cons
             // of a token are distinct, clamped so that a call breaking that contract still
             // advances through its rounds
             const int cnt = r.y > r.x ? min(r.y - r.x, kTermCap) : 0;
+            if (__ballot(cnt > 0) == 0) continue;   // no entry here has earlier cold members
             // inclusive prefix of the counts over the lanes
             int incl = cnt;
 #pragma unroll
@@ -562,9 +563,10 @@ __device__ __forceinline__ void cold_row_at(int C, int nl, const int4 *spk, cons
             for (int base = 0; base < total;) {
                 // this round: the lanes (in order) whose terms fit below base + kTermCap
                 const bool in = cnt > 0 && excl >= base && incl <= base + kTermCap;
-                int end = in ? incl : base;
-#pragma unroll
-                for (int d = 32; d >= 1; d >>= 1) end = max(end, __shfl_xor(end, d, 64));
+                // the in-round lanes are consecutive and their prefixes ascend: the round
+                // ends at the last one's prefix
+                const uint64_t inm = __ballot(in);
+                const int end = inm ? __shfl(incl, 63 - __clzll(static_cast<long long>(inm)), 64) : base;
                 if (in) {
                     for (int32_t j0 = 0; j0 < cnt; j0 += 4) {
                         int4 pk[4];
