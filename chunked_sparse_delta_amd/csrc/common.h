@@ -157,14 +157,15 @@ struct ChunkLayout {
     int64_t off_mrec;     // [E] int2: DW member record {token, bits of k exp(L_last - L)}
     int64_t off_gw;       // [E] f32: gather weight k exp(L), entry order
     int64_t off_kid;      // [E] i32: write slot ids of the chunk, entry order (copy of the input)
-    int64_t off_ecr;      // [E] int4 transposed: cold write entry {a, m, bits k, bits L} (a == m: none)
+    int64_t off_ecr;      // [C][W] int4: cold write entry {a, m, bits k, bits L} (a == m: none)
+    int64_t off_sgh;      // [E] int4 per sorted position: {group head, hot index or -1, bits of the head's L if hot, 0}
     int64_t off_ghot;     // [E] i32: hot index of group, or -1
     int64_t off_hgrp;     // [HMAX] i32: group of hot index
     int64_t off_brec;     // [HMAX] int4: DW group records of the groups with >= kHotMin members
     int64_t off_bstart;   // [NB+1] i32: first sorted position of each slot bucket
     int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
     int64_t off_qid;      // [F] i32: read slot ids of the chunk, entry order (copy of the input)
-    int64_t off_rcr;      // [F] int4 transposed: cold read {a, end, bits q, bits Lr} (a == end: none)
+    int64_t off_rcr;      // [C][R] int4: cold read {a, end, bits q, bits Lr} (a == end: none)
     int64_t off_ka;       // [C][HP] f32, HP = meta[5] (<= HCAP): token t's write of hot group h, k exp(L - L_ref)
     int64_t off_kb;       // [C][HP] f32: the same write's k exp(L_ref - L)
     int64_t off_qa;       // [C][HP] f32: token t's reads of hot group h, sum of q exp(Lr - L_ref) in read order
@@ -207,6 +208,7 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_sgrp = take(L.E);
     L.off_gpos = take(L.E + 1);
     L.off_ecr = take(4 * L.E);
+    L.off_sgh = take(4 * L.E);
     L.off_ghot = take(L.E);
     L.off_hgrp = take(L.HMAX);
     L.off_bstart = take(L.NB + 1);

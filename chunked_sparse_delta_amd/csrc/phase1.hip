@@ -288,6 +288,7 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
     int2 *mrec = reinterpret_cast<int2 *>(cb + L.off_mrec);
     float *gw = reinterpret_cast<float *>(cb + L.off_gw);
     int4 *ecr = reinterpret_cast<int4 *>(cb + L.off_ecr);
+    int4 *sgh = reinterpret_cast<int4 *>(cb + L.off_sgh);
     int32_t *ghot = reinterpret_cast<int32_t *>(cb + L.off_ghot);
     float *Ka = reinterpret_cast<float *>(cb + L.off_ka);
     float *Kb = reinterpret_cast<float *>(cb + L.off_kb);
@@ -424,22 +425,24 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
     __syncthreads();
 
     // Pass 4, per sorted position: factored decays of hot members into the dense
-    // operands; the cold pair ranges (earlier members of the group) by token-major
-    // transposed entry.
+    // operands; the cold pair ranges (earlier members of the group) by entry (token-major);
+    // the read lookup's record of the position: group head, hot index, the head's L (hot).
     for (int32_t m = tid; m < El; m += BLOCK) {
         const int4 pk = spk[m];
         const int32_t g = sgrp[m], a = shead[m];
         const int32_t e = int32_t(sval[m]), w = e - pk.y * W;
         int4 rec = make_int4(m, m, 0, 0);
         const int32_t h = ghot[g];
+        const int32_t Lref = h >= 0 ? spk[a].w : 0;   // the read lookup needs it for hot groups only
         if (h >= 0) {
-            const float d = __int_as_float(pk.w) - __int_as_float(spk[a].w), kv = __int_as_float(pk.z);
+            const float d = __int_as_float(pk.w) - __int_as_float(Lref), kv = __int_as_float(pk.z);
             Ka[pk.y * HP + h] = kv * expf(d);
             Kb[pk.y * HP + h] = kv * expf(-d);
         } else {
             rec = make_int4(a, m, pk.z, pk.w);
         }
-        ecr[int64_t(w) * C + pk.y] = rec;
+        ecr[int64_t(pk.y) * W + w] = rec;
+        sgh[m] = make_int4(a, h, Lref, 0);
     }
 }
 
@@ -460,9 +463,7 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
     const int nl = n_live_tokens(pb, p, ti);
     uint32_t *cb = sl.chunk(n);
     const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
-    const int32_t *shead = reinterpret_cast<const int32_t *>(cb + L.off_shead);
-    const int32_t *sgrp = reinterpret_cast<const int32_t *>(cb + L.off_sgrp);
-    const int32_t *ghot = reinterpret_cast<const int32_t *>(cb + L.off_ghot);
+    const int4 *sgh = reinterpret_cast<const int4 *>(cb + L.off_sgh);
     const int32_t *bstart = reinterpret_cast<const int32_t *>(cb + L.off_bstart);
     const int32_t *meta = reinterpret_cast<const int32_t *>(cb + L.off_meta);
     float *gr = reinterpret_cast<float *>(cb + L.off_gr);
@@ -499,17 +500,17 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
                 const int4 pk = spk[pos];
                 if (pk.x == q) {
                     l = __int_as_float(pk.w);
-                    const int32_t a = shead[pos];
-                    h = ghot[sgrp[pos]];
-                    if (h >= 0) rv = qv * expf(l - __int_as_float(spk[a].w));
-                    else cr = make_int4(a, pos + 1, __float_as_int(qv), pk.w);
+                    const int4 gh = sgh[pos];   // group head, hot index, the head's L
+                    h = gh.y;
+                    if (h >= 0) rv = qv * expf(l - __int_as_float(gh.z));
+                    else cr = make_int4(gh.x, pos + 1, __float_as_int(qv), pk.w);
                 }
             }
             g = qv * expf(l);
         }
         if (ok) {
             gr[int64_t(i) * R + r] = g;
-            rcr[int64_t(r) * C + i] = cr;
+            rcr[int64_t(i) * R + r] = cr;
         }
         // hot reads into the row, lanes ascending
         for (uint64_t m = __ballot(h >= 0); m; m &= m - 1) {
@@ -545,7 +546,7 @@ __device__ __forceinline__ void cold_row_at(int C, int nl, const int4 *spk, cons
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int x0 = 0; i < nl && x0 < width; x0 += kWave) {
             const int x = x0 + lane;
-            const int4 r = x < width ? cr[int64_t(x) * C + i] : make_int4(0, 0, 0, 0);
+            const int4 r = x < width ? cr[int64_t(i) * width + x] : make_int4(0, 0, 0, 0);
             // earlier members of the entry's group; at most C - 1 <= 255 when the write slots
             // of a token are distinct, clamped so that a call breaking that contract still
             // advances through its rounds

@@ -125,7 +125,7 @@ typedef struct {
 /*
  * Workspace bytes sdm_fwd needs to run its steps in slabs of `slab_steps` steps
  * (0 = all Nt = ceil(tokens / chunk) steps in one slab). A slab holds every Phase-1
- * quantity and both solve outputs of its P * slab_steps chunks (96 B per write entry,
+ * quantity and both solve outputs of its P * slab_steps chunks (112 B per write entry,
  * 24 B per read entry, 16 B per chunk-matrix element, a slot search index of up to
  * 64 KiB and dense hot-slot operands of up to 12 * chunk * 256 B per chunk) (the pages
  * budget the same kinds of state, SLAB_BYTES in memory_ops.py).

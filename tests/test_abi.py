@@ -59,7 +59,7 @@ def test_workspace_bytes(lib):
     assert f(8, 2048, 8, 8, 8, 64, 0) == 0                # chunk out of range
     assert f(8, 2048, 64, 0, 8, 64, 0) == 0               # W < 1
     assert f(8, 2048, 64, 8, 257, 64, 0) == 0             # R > 256
-    # 96 B per write entry, 24 B per read entry, 16 B per chunk-matrix element, a slot
+    # 112 B per write entry, 24 B per read entry, 16 B per chunk-matrix element, a slot
     # search index of about one word per write entry (a power of two, at most 2^14), 20 B
     # per possible group of >= 16 members and the three dense hot operands [C][HCAP]
     # (HCAP = that count rounded up to 16, at most 256) (+ alignment)
@@ -68,7 +68,7 @@ def test_workspace_bytes(lib):
     NB = 512
     hmax = E // 16 + 1
     hcap = min(256, (hmax + 15) // 16 * 16)
-    base = 96 * E + 24 * F + 16 * C2 + 4 * (NB + 1) + 20 * hmax + 12 * C * hcap
+    base = 112 * E + 24 * F + 16 * C2 + 4 * (NB + 1) + 20 * hmax + 12 * C * hcap
     assert base <= per_chunk <= base + 40 * 256
 
 
