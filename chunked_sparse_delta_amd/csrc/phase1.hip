@@ -454,7 +454,13 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
 constexpr int kReadWaves = 4;
 
 // The reads of token i of chunk n by one wavefront; qr: kHotCap floats of LDS.
-__device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr) {
+// lspk, lsgh, lbst, lqid, lqv: copies of the sorted member records, the lookup records, the
+// bucket starts and the chunk's read ids and weights (in LDS for the fused kernel), or
+// nullptr to read the workspace and the inputs.
+__device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr,
+                                            const int4 *lspk = nullptr, const int4 *lsgh = nullptr,
+                                            const int32_t *lbst = nullptr, const int32_t *lqid = nullptr,
+                                            const float *lqv = nullptr) {
     const int lane = threadIdx.x & 63;
     const ChunkLayout &L = sl.lay;
     const int R = pb.R, C = pb.C;
@@ -462,9 +468,9 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     uint32_t *cb = sl.chunk(n);
-    const int4 *spk = reinterpret_cast<const int4 *>(cb + L.off_spk);
-    const int4 *sgh = reinterpret_cast<const int4 *>(cb + L.off_sgh);
-    const int32_t *bstart = reinterpret_cast<const int32_t *>(cb + L.off_bstart);
+    const int4 *spk = lspk ? lspk : reinterpret_cast<const int4 *>(cb + L.off_spk);
+    const int4 *sgh = lsgh ? lsgh : reinterpret_cast<const int4 *>(cb + L.off_sgh);
+    const int32_t *bstart = lbst ? lbst : reinterpret_cast<const int32_t *>(cb + L.off_bstart);
     const int32_t *meta = reinterpret_cast<const int32_t *>(cb + L.off_meta);
     float *gr = reinterpret_cast<float *>(cb + L.off_gr);
     int4 *rcr = reinterpret_cast<int4 *>(cb + L.off_rcr);
@@ -482,7 +488,7 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
         int32_t h = -1;
         int4 cr = make_int4(0, 0, 0, 0);
         if (ok && i < nl) {
-            const int32_t q = load_id(pb.q_idx, tg * R + r, pb.q_id8);
+            const int32_t q = lqid ? lqid[i * R + r] : load_id(pb.q_idx, tg * R + r, pb.q_id8);
             qid[int64_t(i) * R + r] = q;   // ids in entry order, for Phase 2
             const int32_t b = min(int32_t(uint32_t(q) >> bsh), int32_t(L.NB) - 1);
             const int32_t b0 = bstart[b];
@@ -494,7 +500,7 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
                 else hi = mid;
             }
             const int32_t pos = lo - 1;
-            const float qv = load_weight(pb.q_val, tg * R + r, pb.dtype);
+            const float qv = lqv ? lqv[i * R + r] : load_weight(pb.q_val, tg * R + r, pb.dtype);
             float l = 0.0f;
             if (pos >= b0) {
                 const int4 pk = spk[pos];
@@ -719,6 +725,8 @@ constexpr int kFusedBlock = 1024;
 constexpr int kFusedMaxEntries = 1024;   // write and read entries per chunk of the fused path
 // the cold pass's term lists: two kTermCap arrays per wavefront
 constexpr int kColdTermBytes = (kFusedBlock / kWave) * 2 * kTermCap * 4;
+// the read pass's dense hot rows: kHotCap floats per wavefront
+constexpr int kReadRowBytes = (kFusedBlock / kWave) * kHotCap * 4;
 
 __global__ __launch_bounds__(kFusedBlock) void p1_fused_kernel(Problem pb, Slab sl, WyArgs wa) {
     extern __shared__ __align__(16) char fsm[];
@@ -730,8 +738,35 @@ __global__ __launch_bounds__(kFusedBlock) void p1_fused_kernel(Problem pb, Slab 
     groups_chunk<kFusedBlock>(pb, sl, n, fsm);
     __syncthreads();
     {
+        // The read lookups probe LDS copies of the sorted member records, the lookup records
+        // and the bucket starts: one coalesced sweep instead of dependent memory round trips.
+        const ChunkLayout &L = sl.lay;
+        const uint32_t *cb = sl.chunk(n);
+        int4 *lspk = reinterpret_cast<int4 *>(fsm + kReadRowBytes);
+        int4 *lsgh = lspk + L.E;
+        int32_t *lbst = reinterpret_cast<int32_t *>(lsgh + L.E);
+        const int4 *gspk = reinterpret_cast<const int4 *>(cb + L.off_spk);
+        const int4 *gsgh = reinterpret_cast<const int4 *>(cb + L.off_sgh);
+        const int32_t *gbst = reinterpret_cast<const int32_t *>(cb + L.off_bstart);
+        for (int e = threadIdx.x; e < L.E; e += kFusedBlock) {
+            lspk[e] = gspk[e];
+            lsgh[e] = gsgh[e];
+        }
+        for (int b = threadIdx.x; b <= L.NB; b += kFusedBlock) lbst[b] = gbst[b];
+        int32_t *lqid = lbst + L.NB + 1;
+        float *lqv = reinterpret_cast<float *>(lqid + L.F);
+        {
+            const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
+            const int nlr = n_live_tokens(pb, p, ti) * pb.R;   // read entries of live tokens
+            const int64_t q0 = (int64_t(p) * pb.T + int64_t(ti) * pb.C) * pb.R;
+            for (int e = threadIdx.x; e < nlr; e += kFusedBlock) {
+                lqid[e] = load_id(pb.q_idx, q0 + e, pb.q_id8);
+                lqv[e] = load_weight(pb.q_val, q0 + e, pb.dtype);
+            }
+        }
+        __syncthreads();
         float *qr = reinterpret_cast<float *>(fsm) + wave * kHotCap;
-        for (int i = wave; i < pb.C; i += NW) reads_token(pb, sl, n, i, qr);
+        for (int i = wave; i < pb.C; i += NW) reads_token(pb, sl, n, i, qr, lspk, lsgh, lbst, lqid, lqv);
     }
     __syncthreads();
     {
@@ -770,7 +805,10 @@ __global__ __launch_bounds__(kFusedBlock) void p1_fused_kernel(Problem pb, Slab 
 static size_t fused_smem_bytes(int C) {
     size_t b = sort_smem_bytes<kFusedBlock>();
     b = std::max(b, sizeof(GroupsSmem<kFusedBlock / kWave>));
-    b = std::max(b, size_t(kFusedBlock / kWave) * kHotCap * 4);
+    // read pass: hot rows, then the staged records (E <= kFusedMaxEntries, NB + 1 <= 1025)
+    // and read ids and weights (F <= kFusedMaxEntries)
+    b = std::max(b, size_t(kReadRowBytes) + 32 * size_t(kFusedMaxEntries) + 4 * size_t(kFusedMaxEntries + 1) +
+                        8 * size_t(kFusedMaxEntries));
     b = std::max(b, size_t(kColdTermBytes) + 16 * size_t(2 * kFusedMaxEntries + kFusedMaxEntries));
     return std::max(b, wy_lds_bytes(C));
 }
