@@ -23,7 +23,8 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "product_key_topk", "workspace_bytes", "plan",
+__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
+           "workspace_bytes", "plan",
            "library_path",
            "SDM_ERRORS"]
 
@@ -97,6 +98,8 @@ def _load():
             lib.sdm_fwd_plan.restype = ctypes.c_int
             lib.sdm_product_key_topk.argtypes = [i64, p, i32, p, i32, i32, p, p, p]
             lib.sdm_product_key_topk.restype = ctypes.c_int
+            lib.sdm_product_key_topk_backward.argtypes = [i64, p, p, i32, p, i32, i32, p, p]
+            lib.sdm_product_key_topk_backward.restype = ctypes.c_int
             lib.sdm_error_string.argtypes = [ctypes.c_int]
             lib.sdm_error_string.restype = ctypes.c_char_p
             lib.sdm_last_error.argtypes = []
@@ -319,3 +322,25 @@ def product_key_topk(raw: torch.Tensor, factors, k: int, stream=None):
     _check_rc(lib, lib.sdm_product_key_topk(rows, _ptr(raw), _DTYPES[raw.dtype], fac, len(factors), int(k), _ptr(val),
                                             _ptr(lin), ctypes.byref(ex)))
     return val, lin
+
+
+def product_key_topk_backward(lin: torch.Tensor, grad_val: torch.Tensor, factors, stream=None) -> torch.Tensor:
+    """The gradient with respect to raw of product_key_topk's values
+    (sdm_product_key_topk_backward): lin [..., kk] int64 and grad_val [..., kk] (float32 or
+    bfloat16) on the GPU. Returns grad_raw [..., sum(factors)] in grad_val's dtype."""
+    lib = _load()
+    if grad_val.dtype not in _DTYPES:
+        raise TypeError(f"grad_val must be float32 or bfloat16, got {grad_val.dtype}")
+    factors = [int(f) for f in factors]
+    if lin.dtype != torch.int64 or lin.shape != grad_val.shape or lin.device != grad_val.device:
+        raise ValueError("lin must be int64 with grad_val's shape and device")
+    if grad_val.device.type != "cuda" or not (lin.is_contiguous() and grad_val.is_contiguous()):
+        raise ValueError("lin and grad_val must be contiguous GPU tensors")
+    lead, kk = tuple(lin.shape[:-1]), int(lin.shape[-1])
+    rows = math.prod(lead) if lead else 1
+    graw = torch.empty(lead + (sum(factors),), dtype=grad_val.dtype, device=grad_val.device)
+    fac = (ctypes.c_int32 * max(1, len(factors)))(*factors)
+    ex = _Exec(_stream_ptr(stream), None, 0, None, 0, None)
+    _check_rc(lib, lib.sdm_product_key_topk_backward(rows, _ptr(lin), _ptr(grad_val), _DTYPES[grad_val.dtype], fac,
+                                                     len(factors), kk, _ptr(graw), ctypes.byref(ex)))
+    return graw

@@ -27,6 +27,8 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
 size_t gram_lds_bytes(int C);
 hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, int32_t D, int32_t F, int32_t k,
                        int32_t kk, bool bf16, const int32_t *fw, hipStream_t st);
+hipError_t launch_topk_bwd(const int64_t *lin, const void *gval, void *graw, int64_t rows, int32_t D, int32_t F,
+                           int32_t kk, bool bf16, const int32_t *fw, hipStream_t st);
 constexpr int kTopkMaxK = 256, kTopkMaxFactor = 4096, kTopkMaxFactors = 8;
 size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M);
 int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, int lds_limit);
@@ -296,6 +298,38 @@ int sdm_product_key_topk(int64_t rows, const void *raw, int32_t dtype, const int
     const hipError_t e = launch_topk(raw, val, lin, rows, int32_t(D), num_factors, k, kk, dtype == SDM_BF16, factors,
                                      static_cast<hipStream_t>(exec->stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "top-k launch");
+}
+
+int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *grad_val, int32_t dtype,
+                                  const int32_t *factors, int32_t num_factors, int32_t kk, void *grad_raw,
+                                  const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!exec) return fail(SDM_ERR_NULL, "exec must not be NULL");
+    if (!factors) return fail(SDM_ERR_NULL, "factors must not be NULL");
+    if (dtype != SDM_F32 && dtype != SDM_BF16) return fail(SDM_ERR_DTYPE, "dtype must be SDM_F32 or SDM_BF16, got %d", dtype);
+    if (rows < 0) return fail(SDM_ERR_SHAPE, "rows must be >= 0, got %lld", (long long)rows);
+    if (rows > int64_t(0x7FFFFFFF)) return fail(SDM_ERR_RANGE, "at most 2^31 - 1 rows, got %lld", (long long)rows);
+    if (num_factors < 1 || num_factors > kTopkMaxFactors)
+        return fail(SDM_ERR_SHAPE, "1 to %d factors, got %d", kTopkMaxFactors, num_factors);
+    int64_t D = 0, prod = 1;
+    for (int f = 0; f < num_factors; ++f) {
+        if (factors[f] < 1) return fail(SDM_ERR_SHAPE, "factor %d has %d columns", f, factors[f]);
+        if (factors[f] > kTopkMaxFactor)
+            return fail(SDM_ERR_UNSUPPORTED, "factor %d has %d columns; at most %d", f, factors[f], kTopkMaxFactor);
+        D += factors[f];
+        if (prod > (int64_t(1) << 55) / factors[f])
+            return fail(SDM_ERR_UNSUPPORTED, "the factors address 2^55 or more slots");
+        prod *= factors[f];
+    }
+    if (kk < 1 || kk > kTopkMaxK || kk > prod)
+        return fail(SDM_ERR_SHAPE, "kk must be in 1..min(256, slots), got %d", kk);
+    if (rows > 0 && (!lin || !grad_val || !grad_raw)) return fail(SDM_ERR_NULL, "lin, grad_val and grad_raw must not be NULL");
+    const int es = dtype == SDM_F32 ? 4 : 2;
+    if (!aligned(lin, 8) || !aligned(grad_val, size_t(es)) || !aligned(grad_raw, size_t(es)))
+        return fail(SDM_ERR_ALIGN, "lin must be 8-byte aligned, grad_val and grad_raw aligned to their element size");
+    const hipError_t e = launch_topk_bwd(lin, grad_val, grad_raw, rows, int32_t(D), num_factors, kk, dtype == SDM_BF16,
+                                         factors, static_cast<hipStream_t>(exec->stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "top-k backward launch");
 }
 
 size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t hd, int32_t slab_steps) {

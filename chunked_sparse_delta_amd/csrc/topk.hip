@@ -347,6 +347,77 @@ __global__ __launch_bounds__(kTopkBlock) void topk_wave_kernel(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Backward: d(val)/d(raw) is 1 at each factor column of a selected slot (the roundings of a
+// score pass the gradient through), so the gradient of a raw column is the sum of the
+// output gradients of the selected slots that use it. One row per wavefront: the slots'
+// factor columns are decoded once into LDS, then each lane owns columns and adds, slot by
+// slot in output (ascending index) order, the gradients of the slots that use them, so
+// every sum runs in one fixed order with no atomics. The sums are float32, rounded once.
+struct TopkBwdArgs {
+    const int64_t *lin;       // [rows, kk]
+    const void *gval;         // [rows, kk] in the dtype
+    void *graw;               // [rows, D] in the dtype
+    int64_t rows;
+    int32_t D, F, kk, bf16;
+    int32_t fw[kTopkMaxFactors];
+    int32_t f0[kTopkMaxFactors];
+};
+
+__global__ __launch_bounds__(kTopkBlock) void topk_bwd_kernel(TopkBwdArgs a) {
+    constexpr int kWaves = kTopkBlock / 64;
+    __shared__ int32_t cols[kWaves][kTopkMaxK][kTopkMaxFactors];
+    __shared__ float gsh[kWaves][kTopkMaxK];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = int64_t(blockIdx.x) * kWaves + wv;
+    if (row >= a.rows) return;
+    for (int sidx = lane; sidx < a.kk; sidx += 64) {
+        int64_t l = a.lin[row * a.kk + sidx];
+        for (int f = a.F - 1; f >= 0; --f) {   // lin = (..(c_0 f_1 + c_1) ..) f_{F-1} + c_{F-1}
+            cols[wv][sidx][f] = int32_t(l % a.fw[f]);
+            l /= a.fw[f];
+        }
+        gsh[wv][sidx] = a.bf16 ? __uint_as_float(uint32_t(static_cast<const uint16_t *>(a.gval)[row * a.kk + sidx]) << 16)
+                               : static_cast<const float *>(a.gval)[row * a.kk + sidx];
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int c0 = 0; c0 < a.D; c0 += 64) {
+        const int col = c0 + lane;
+        int f = 0;
+        while (f + 1 < a.F && col >= a.f0[f + 1]) ++f;
+        const int c = col - a.f0[f];
+        float acc = 0.0f;
+        for (int sidx = 0; sidx < a.kk; ++sidx)
+            if (cols[wv][sidx][f] == c) acc += gsh[wv][sidx];
+        if (col < a.D) {
+            if (a.bf16) static_cast<uint16_t *>(a.graw)[row * a.D + col] = uint16_t(__float_as_uint(bf16_round(acc)) >> 16);
+            else static_cast<float *>(a.graw)[row * a.D + col] = acc;
+        }
+    }
+}
+
+hipError_t launch_topk_bwd(const int64_t *lin, const void *gval, void *graw, int64_t rows, int32_t D, int32_t F,
+                           int32_t kk, bool bf16, const int32_t *fw, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    TopkBwdArgs a{};
+    a.lin = lin;
+    a.gval = gval;
+    a.graw = graw;
+    a.rows = rows;
+    a.D = D;
+    a.F = F;
+    a.kk = kk;
+    a.bf16 = bf16 ? 1 : 0;
+    int32_t c0 = 0;
+    for (int f = 0; f < F; ++f) {
+        a.fw[f] = fw[f];
+        a.f0[f] = c0;
+        c0 += fw[f];
+    }
+    hipLaunchKernelGGL(topk_bwd_kernel, dim3(unsigned((rows + 3) / 4)), dim3(kTopkBlock), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, int32_t D, int32_t F, int32_t k,
                        int32_t kk, bool bf16, const int32_t *fw, hipStream_t st) {
     if (rows <= 0) return hipSuccess;

@@ -231,6 +231,21 @@ int sdm_product_key_topk(int64_t rows, const void *raw, int32_t dtype, const int
                          int32_t num_factors, int32_t k, void *val, int64_t *lin,
                          const sdm_exec *exec);
 
+/*
+ * The sparse backward of sdm_product_key_topk (the pages' top-k is differentiable in raw,
+ * with a deterministic backward, page 23, product_key_topk.py): the gradient of a raw column
+ * is the sum of grad_val over the selected slots that use it (d val / d raw is 1 at each
+ * factor column of a slot; roundings pass the gradient through). Sums run in float32 over
+ * the slots in their output order (ascending lin), rounded once to dtype.
+ *   lin: device int64 [rows, kk] as returned by sdm_product_key_topk (entries must be below
+ *   the slot count; not checked). grad_val: device [rows, kk] in dtype. grad_raw: device
+ *   [rows, sum(factors)] in dtype, every element written. factors, num_factors: as for the
+ *   forward; kk: 1..min(256, slot count). exec->stream only.
+ */
+int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *grad_val, int32_t dtype,
+                                  const int32_t *factors, int32_t num_factors, int32_t kk, void *grad_raw,
+                                  const sdm_exec *exec);
+
 /* Static text for an SDM_* code. */
 const char *sdm_error_string(int code);
 

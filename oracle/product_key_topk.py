@@ -121,3 +121,26 @@ def brute_force_topk(row: np.ndarray, factors, k: int):
     scores.sort(reverse=True)
     kk = min(k, math.prod(factors))
     return {lin for _, lin in scores[:kk]}
+
+
+def product_key_topk_backward(lin: np.ndarray, grad_val: np.ndarray, factors, bf16: bool = False) -> np.ndarray:
+    """The sparse backward of the top-k: d(val)/d(raw) is 1 at each factor column of a
+    selected slot (roundings of the score pass the gradient through), so the gradient of a
+    raw column is the sum of grad_val over the selected slots that use it. Sums run in
+    float32 over the slots in output (ascending slot index) order; the result is rounded to
+    the input dtype. lin, grad_val [N, kk] (grad_val exact float32 copies). Returns [N, D]
+    float32 (bfloat16 values when ``bf16``)."""
+    lin = np.asarray(lin, dtype=np.int64)
+    grad_val = np.asarray(grad_val, dtype=np.float32)
+    N, kk = lin.shape
+    starts = np.cumsum([0] + list(factors))[:-1]
+    out = np.zeros((N, sum(factors)), dtype=np.float32)
+    for r in range(N):
+        for s in range(kk):
+            cols = np.unravel_index(int(lin[r, s]), factors)
+            for f, c in enumerate(cols):
+                j = starts[f] + c
+                out[r, j] = np.float32(out[r, j] + grad_val[r, s])
+    if bf16:
+        out = np.vectorize(round_bf16, otypes=[np.float32])(out) if out.size else out
+    return out

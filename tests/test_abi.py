@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["sdm_chunk_mats", "sdm_error_string", "sdm_fwd", "sdm_fwd_plan",
                                     "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_product_key_topk",
-                                    "sdm_wy_solve"]
+                                    "sdm_product_key_topk_backward", "sdm_wy_solve"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -215,3 +215,22 @@ def test_topk_rejects_before_any_launch(lib):
     assert call(raw=None) == NULL and call(lin=None) == NULL
     assert call(raw=fake + 2) == ALIGN and call(dtype=1, raw=fake + 1) == ALIGN and call(lin=fake + 4) == ALIGN
     assert call(rows=0, raw=None, val=None, lin=None) == OK
+
+
+def test_topk_backward_rejects_before_any_launch(lib):
+    from chunked_sparse_delta_amd import _Exec
+    f = lib.sdm_product_key_topk_backward
+    f.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    ex = _Exec(None, None, 0, None, 0, None)
+    fake = Call.FAKE
+
+    def call(rows=4, lin=fake, g=fake, dtype=0, factors=(16, 16), kk=8, out=fake, e=ex):
+        fa = (ctypes.c_int32 * len(factors))(*factors)
+        return f(rows, lin, g, dtype, fa, len(factors), kk, out, None if e is None else ctypes.byref(e))
+
+    assert call(e=None) == NULL and call(dtype=5) == DTYPE and call(rows=-1) == SHAPE
+    assert call(kk=0) == SHAPE and call(kk=257) == SHAPE and call(factors=(2, 3), kk=7) == SHAPE
+    assert call(factors=(5000,)) == UNSUPPORTED and call(lin=None) == NULL
+    assert call(lin=fake + 4) == ALIGN and call(dtype=1, g=fake + 1) == ALIGN
+    assert call(rows=0, lin=None, g=None, out=None) == OK

@@ -86,3 +86,22 @@ def test_topk_leading_dims_and_empty(gpu):
     assert torch.equal(lin.reshape(6, 12), l2) and torch.equal(val.reshape(6, 12), v2)
     v0, l0 = product_key_topk(torch.empty(0, 40, device=gpu), (8, 32), 12)
     assert v0.shape == (0, 12) and l0.shape == (0, 12)
+
+
+@pytest.mark.parametrize("dtype,factors,k", [("f32", (16, 16), 8), ("bf16", (64, 64), 32), ("bf16", (5, 7, 9), 20),
+                                             ("f32", (300,), 17), ("f32", (33, 70), 40), ("bf16", (512, 512), 256)])
+def test_topk_backward_matches_oracle(gpu, dtype, factors, k):
+    """The sparse backward: each raw column's gradient is the sum, in output order, of the
+    gradients of the selected slots that use it (oracle_topk_backward), bit for bit."""
+    from chunked_sparse_delta_amd import product_key_topk, product_key_topk_backward
+    rows = 13
+    x32 = _raw("normal", rows, sum(factors), seed=k + 3)
+    t, _ = _to_dtype(x32, dtype, gpu)
+    _, lin = product_key_topk(t, factors, k)
+    g32 = _raw("ties" if dtype == "f32" else "normal", rows, lin.shape[1], seed=k + 5)
+    gt, gexact = _to_dtype(g32, dtype, gpu)
+    graw = product_key_topk_backward(lin, gt, factors)
+    torch.cuda.synchronize()
+    want = pk.product_key_topk_backward(lin.cpu().numpy(), gexact, factors, bf16=dtype == "bf16")
+    assert graw.shape == (rows, sum(factors)) and graw.dtype == gt.dtype
+    assert np.array_equal(_bits(graw), _oracle_val_bits(want, dtype))

@@ -70,3 +70,30 @@ def test_bf16_partial_sums_round_before_the_next_factor():
     # two factors: no partial rounding
     v, _ = pk.topk_row(np.array([1.0, 2.0 ** -8], np.float32), (1, 1), 1, bf16=True)
     assert v == [np.float32(1.0 + 2.0 ** -8)]
+
+
+def test_backward_scatters_each_slot_gradient_to_its_columns():
+    """Integer gradients sum exactly: each factor's columns receive every selected slot's
+    gradient once (so each factor's column sums equal the total), at the columns of the
+    slot; unselected columns get zero."""
+    factors = (4, 3, 5)
+    lin = np.array([[0, 7, 59], [5, 6, 30]], np.int64)        # slots (0,0,0) (0,1,2) (3,2,4) ...
+    g = np.array([[1, 2, 4], [8, 16, 32]], np.float32)
+    out = pk.product_key_topk_backward(lin, g, factors)
+    assert out.shape == (2, 12)
+    starts = [0, 4, 7]
+    for r in range(2):
+        for f, w in enumerate(factors):
+            assert out[r, starts[f]:starts[f] + w].sum() == g[r].sum()
+    # row 0: slots (0,0,0), (0,1,2), (3,2,4)
+    assert out[0].tolist() == [3, 0, 0, 4, 1, 2, 4, 1, 0, 2, 0, 4]
+    # row 1: slots (0,1,0) -> 5, (0,1,1) -> 6, (2,0,0) -> 30
+    assert out[1].tolist() == [24, 0, 32, 0, 32, 24, 0, 40, 16, 0, 0, 0]
+
+
+def test_backward_rounds_to_bf16_once():
+    lin = np.array([[0, 1]], np.int64)                          # both slots use column 0 of factor 0
+    g = np.array([[1.0, 2.0 ** -8]], np.float32)
+    out = pk.product_key_topk_backward(lin, g, (1, 2), bf16=True)
+    assert out[0, 0] == np.float32(1.0)                         # 1 + 2^-8 rounds to 1 (even)
+    assert out[0, 1] == np.float32(1.0) and out[0, 2] == np.float32(2.0 ** -8)
