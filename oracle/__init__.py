@@ -9,6 +9,8 @@ package shares no code with it; both take their inputs from ``workloads``.
                         rows rounded to bfloat16 once per chunk, readings rounded to
                         bfloat16 (token_loop(..., bf16_chunk=C))
   O2  chunk_algebra.py  the chunked three-part form in fp64, for tiny inputs
+  O3  token_loop_backward.c  the gradient of O1's loop (its statements in reverse, chain
+                        rule on each), fp64: token_loop_backward
   token_loop over a [M, hd] bank: one bank shared by every stream (slot sets disjoint,
                         checked); repeated_write_slots: the pages' count of write entries
                         repeating a slot of their own token
@@ -21,7 +23,10 @@ pinned by its rounding (ties to even, no double rounding, against an independent
 float32 bit-level rounding), by its reduction to O1 with one rounding when one chunk
 spans the stream, and by its equality with O1 when every value is bfloat16-exact. The
 shared-bank loop is pinned to the per-stream loop on interleaved relabeled slots (equal
-bit for bit, O1 and O1b), the repeat count to hand-counted tokens.
+bit for bit, O1 and O1b), the repeat count to hand-counted tokens. O3
+(tests/test_backward_oracle.py) is pinned by central finite differences of O1 for every
+input element, a one-token closed form, linearity in the output gradients, zero gradients
+of padding tokens and the gate-width reduction (G = 1 equals the sum of G = W).
 Parity unpinned: none.
 """
 
@@ -38,7 +43,7 @@ import numpy as np
 from . import chunk_algebra  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "token_loop.c")
+_SRCS = [os.path.join(_HERE, "token_loop.c"), os.path.join(_HERE, "token_loop_backward.c")]
 _LIB = os.path.join(_HERE, "libsdm_oracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -48,10 +53,10 @@ ERRORS = {-1: "slot id out of range", -2: "write slot repeated within a token",
 
 
 def build(force: bool = False) -> str:
-    """Compile token_loop.c with gcc into oracle/libsdm_oracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile token_loop.c and token_loop_backward.c with gcc into oracle/libsdm_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(map(os.path.getmtime, _SRCS)):
         tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-o", tmp, _SRC, "-lm"],
+        subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fno-fast-math", "-o", tmp, *_SRCS, "-lm"],
                        check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -73,6 +78,9 @@ def _load():
             fs = lib.sdm_oracle_token_loop_shared
             fs.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 10
             fs.restype = ctypes.c_int
+            fbw = lib.sdm_oracle_token_loop_backward
+            fbw.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 17
+            fbw.restype = ctypes.c_int
             lib.sdm_oracle_round_bf16.argtypes = [ctypes.c_double]
             lib.sdm_oracle_round_bf16.restype = ctypes.c_double
             _lib = lib
@@ -153,6 +161,56 @@ def token_loop(f64: dict, threads: int = 1, streams=None, bf16_chunk: int | None
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(run, todo))
     return out, bank
+
+
+def token_loop_backward(f64: dict, grad_out, grad_bank_final=None, threads: int = 1, streams=None) -> dict:
+    """O3: the gradient of J = sum(grad_out * readings) + sum(grad_bank_final * final bank)
+    through O1's loop, for fp64 inputs (``as_f64_inputs``, one bank per stream, [P, M, hd]).
+    grad_out [P, T, hd]; grad_bank_final [P, M, hd] or None (zeros). Returns a dict of fp64
+    gradients named like the inputs: bank [P, M, hd] (with respect to the bank the forward
+    started from), k_val, v, beta, g, q_val. ``streams`` restricts the work (other streams'
+    gradients stay zero)."""
+    lib = _load()
+    bank0 = np.ascontiguousarray(f64["bank"], dtype=np.float64)
+    if bank0.ndim != 3:
+        raise ValueError("oracle: the backward takes one bank per stream")
+    k_idx = np.ascontiguousarray(f64["k_idx"], dtype=np.int32)
+    P, T, W = k_idx.shape
+    M, hd = bank0.shape[1], bank0.shape[2]
+    q_idx = np.ascontiguousarray(f64["q_idx"], dtype=np.int32)
+    R = q_idx.shape[2]
+    g = np.ascontiguousarray(f64["g"], dtype=np.float64)
+    G = g.shape[2]
+    k_val = np.ascontiguousarray(f64["k_val"], dtype=np.float64)
+    v = np.ascontiguousarray(f64["v"], dtype=np.float64)
+    beta = np.ascontiguousarray(f64["beta"], dtype=np.float64)
+    q_val = np.ascontiguousarray(f64["q_val"], dtype=np.float64)
+    valid = f64.get("valid")
+    valid = None if valid is None else np.ascontiguousarray(valid, dtype=np.int32)
+    go = np.ascontiguousarray(grad_out, dtype=np.float64)
+    gbf = None if grad_bank_final is None else np.ascontiguousarray(grad_bank_final, dtype=np.float64)
+    if go.shape != (P, T, hd) or (gbf is not None and gbf.shape != bank0.shape):
+        raise ValueError("oracle: gradient shapes do not match the inputs")
+    out = dict(bank=np.zeros_like(bank0), k_val=np.zeros((P, T, W)), v=np.zeros((P, T, hd)),
+               beta=np.zeros((P, T)), g=np.zeros((P, T, G)), q_val=np.zeros((P, T, R)))
+    ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+
+    def run(p):
+        rc = lib.sdm_oracle_token_loop_backward(
+            p, p + 1, T, W, R, G, hd, M, ptr(k_idx), ptr(k_val), ptr(v), ptr(beta), ptr(g), ptr(q_idx),
+            ptr(q_val), ptr(valid), ptr(bank0), ptr(go), ptr(gbf), ptr(out["bank"]), ptr(out["k_val"]),
+            ptr(out["v"]), ptr(out["beta"]), ptr(out["g"]), ptr(out["q_val"]))
+        if rc:
+            raise ValueError(f"oracle: stream {p}: {ERRORS.get(rc, rc)}")
+
+    todo = list(range(P)) if streams is None else [int(p) for p in streams]
+    if threads <= 1:
+        for p in todo:
+            run(p)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, todo))
+    return out
 
 
 def _check_disjoint_streams(k_idx, q_idx, valid) -> None:
