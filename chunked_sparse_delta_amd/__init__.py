@@ -12,6 +12,12 @@ cannot be loaded, every call raises.
 mirrors sdm_write_read's no-grad forward (memory_ops.py, sparse-delta-memory 2.0.0
 wheel, diffend page 21) with per-stream banks: bank [P, M, hd] is advanced in place and
 the readings [P, T, hd] are returned.
+
+    grads = sdm_bwd(bank0, k_idx, k_val, v, beta, log_decay, q_idx, q_val, grad_out)
+
+is the backward for a float32 bank: the gradients of sum(grad_out * readings) (plus
+sum(grad_bank * final bank) when given) with respect to the bank the forward started
+from and every float input.
 """
 
 from __future__ import annotations
@@ -23,7 +29,7 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
+__all__ = ["SdmError", "sdm_fwd", "sdm_bwd", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
            "workspace_bytes", "plan",
            "library_path",
            "SDM_ERRORS"]
@@ -100,6 +106,10 @@ def _load():
             lib.sdm_product_key_topk.restype = ctypes.c_int
             lib.sdm_product_key_topk_backward.argtypes = [i64, p, p, i32, p, i32, i32, p, p]
             lib.sdm_product_key_topk_backward.restype = ctypes.c_int
+            lib.sdm_bwd_workspace_bytes.argtypes = [i32] * 5
+            lib.sdm_bwd_workspace_bytes.restype = ctypes.c_size_t
+            lib.sdm_bwd.argtypes = [i32, i32, p, p, p, p, i32, p, p, p, p, p, p]
+            lib.sdm_bwd.restype = ctypes.c_int
             lib.sdm_error_string.argtypes = [ctypes.c_int]
             lib.sdm_error_string.restype = ctypes.c_char_p
             lib.sdm_last_error.argtypes = []
@@ -248,6 +258,53 @@ def sdm_fwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
                None if repeated_writes is None else repeated_writes.data_ptr())
     rc = lib.sdm_fwd(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
                      _ptr(v), ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
+    _check_rc(lib, rc)
+    return out
+
+
+class _Grads(ctypes.Structure):
+    _fields_ = [("bank", ctypes.c_void_p), ("v", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("log_decay", ctypes.c_void_p), ("write", ctypes.c_void_p), ("read", ctypes.c_void_p)]
+
+
+def bwd_workspace_bytes(P: int, T: int, W: int, R: int, hd: int) -> int:
+    """Workspace bytes sdm_bwd needs (0 for rejected shapes)."""
+    return int(_load().sdm_bwd_workspace_bytes(P, T, W, R, hd))
+
+
+def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+            log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, grad_out: torch.Tensor, *,
+            grad_bank: torch.Tensor | None = None, valid_tokens: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """Backward of sdm_fwd for float32 banks, one per stream. ``bank`` [P, M, hd] holds the
+    bank the forward STARTED from; the call replays the forward on it and restores it
+    exactly. ``grad_out`` [P, T, hd] is the gradient of the readings; ``grad_bank`` (float32
+    [P, M, hd], optional) that of the final bank, and it is overwritten in place with the
+    gradient with respect to the initial bank (a zero tensor is allocated if omitted).
+    Returns dict(bank, v, beta, log_decay, k_val, q_val) of float32 gradients."""
+    lib = _load()
+    if bank.dtype != torch.float32 or bank.dim() != 3:
+        raise TypeError("sdm_bwd takes a float32 bank of one [M, hd] bank per stream")
+    P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
+                                                   valid_tokens)
+    dev = bank.device
+    _expect(grad_out, "grad_out", (P, T, hd), torch.float32, dev)
+    if grad_bank is None:
+        grad_bank = torch.zeros_like(bank)
+    else:
+        _expect(grad_bank, "grad_bank", (P, M, hd), torch.float32, dev)
+    out = dict(bank=grad_bank, v=torch.empty((P, T, hd), dtype=torch.float32, device=dev),
+               beta=torch.empty((P, T), dtype=torch.float32, device=dev),
+               log_decay=torch.empty((P, T, G), dtype=torch.float32, device=dev),
+               k_val=torch.empty((P, T, W), dtype=torch.float32, device=dev),
+               q_val=torch.empty((P, T, R), dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = _workspace(bwd_workspace_bytes(P, T, W, R, hd), dev)
+    gr = _Grads(*(out[k].data_ptr() for k in ("bank", "v", "beta", "log_decay", "k_val", "q_val")))
+    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 0)
+    ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(), None, 0, None)
+    rc = lib.sdm_bwd(P, T, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G, _ptr(v),
+                     ctypes.byref(bk), _ptr(valid_tokens), _ptr(grad_out), ctypes.byref(gr), ctypes.byref(ex))
     _check_rc(lib, rc)
     return out
 

@@ -13,6 +13,7 @@
 #include "sdm.h"
 #include "common.h"
 #include "wy_impl.h"
+#include "backward.h"
 
 namespace sdm {
 hipError_t phase1_prepare();
@@ -88,6 +89,7 @@ int device_info(DeviceInfo **out) {
         if ((e = phase1_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 1)");
         if ((e = phase2_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 2)");
         if ((e = wy_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (solve)");
+        if ((e = bwd_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (backward)");
         d.ready = true;
     }
     *out = &d;
@@ -495,6 +497,89 @@ int sdm_wy_solve(int64_t n, int32_t C, const float *A, const float *beta, const 
     hipError_t e = launch_wy(A, beta, QK, X, QX, C, n, C2, C, static_cast<hipStream_t>(exec->stream));
     if (e != hipSuccess) return hip_fail(e, "solve launch");
     return SDM_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// The backward (backward.hip): one workgroup per (stream, column slice) replays the forward
+// and walks it back; the workspace holds the saved rows, the folded read slots and the
+// per-slice dots.
+// ---------------------------------------------------------------------------------------
+
+namespace {
+
+struct BwdSizes {
+    size_t snap, lead, part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd) {
+    const int S = sdm::bwd_slice_cols(P, hd);
+    const int64_t NS = (hd + S - 1) / S;
+    BwdSizes z{};
+    z.snap = align256(size_t(P) * size_t(T) * size_t(W) * size_t(hd) * 4);
+    z.lead = align256(size_t(P) * size_t(T) * size_t(R) * 8);
+    z.part = align256(size_t(P) * size_t(NS) * size_t(T) * size_t(sdm::bwd_parts(W, R)) * 4);
+    z.total = z.snap + z.lead + z.part;
+    return z;
+}
+
+}  // namespace
+
+size_t sdm_bwd_workspace_bytes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd) {
+    if (check_shape(P, T, 16, W, R, hd) != SDM_OK) return 0;
+    return bwd_sizes(P, T, W, R, hd).total;
+}
+
+int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
+            const float *log_decay, int32_t gate_width, const float *v, const sdm_bank *bank, const int32_t *valid_tokens,
+            const float *grad_out, const sdm_grads *grads, const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!bank || !exec || !grads) return fail(SDM_ERR_NULL, "bank, grads and exec must not be NULL");
+    if (bank->dtype != SDM_F32) return fail(SDM_ERR_DTYPE, "the backward takes a float32 bank, got dtype %d", bank->dtype);
+    if (bank->shared != 0) return fail(SDM_ERR_UNSUPPORTED, "the backward takes one bank per stream (shared = 0)");
+    Checked ck;
+    // chunk 16 only bounds the token count here: the backward has no chunks
+    int rc = check_call(P, T, 16, slots, weights, beta, log_decay, gate_width, v, bank->rows, bank->head_dim,
+                        bank->dtype, bank->data, false, valid_tokens, const_cast<float *>(grad_out), true, &ck);
+    if (rc) return rc;
+    if (!grads->bank || !grads->v || !grads->beta || !grads->log_decay || !grads->write || !grads->read)
+        return fail(SDM_ERR_NULL, "every gradient array must be given");
+    const void *g4[] = {grads->bank, grads->v, grads->beta, grads->log_decay, grads->write, grads->read};
+    for (const void *q : g4)
+        if (!aligned(q, 4)) return fail(SDM_ERR_ALIGN, "gradient arrays must be 4-byte aligned");
+    const int W = slots->W, R = slots->R, hd = bank->head_dim;
+    const int64_t M = bank->rows;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank->data), b1 = b0 + uintptr_t(P) * M * hd * 4;
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grads->bank), g1 = g0 + uintptr_t(P) * M * hd * 4;
+    if (g0 < b1 && b0 < g1) return fail(SDM_ERR_SHAPE, "the bank gradient overlaps the bank");
+    const BwdSizes z = bwd_sizes(P, T, W, R, hd);
+    if (!exec->workspace || exec->workspace_bytes < z.total)
+        return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes the backward needs",
+                    exec->workspace ? exec->workspace_bytes : size_t(0), z.total);
+    if (!aligned(exec->workspace, 256)) return fail(SDM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    DeviceInfo *dev = nullptr;
+    if ((rc = device_info(&dev)) != SDM_OK) return rc;
+    sdm::BwdArgs a{};
+    a.P = P; a.T = T; a.W = W; a.R = R; a.G = gate_width; a.hd = hd; a.M = M;
+    a.S = sdm::bwd_slice_cols(P, hd);
+    a.NS = (hd + a.S - 1) / a.S;
+    if (sdm::bwd_lds_bytes(W, a.S) > size_t(dev->lds_per_block))
+        return fail(SDM_ERR_UNSUPPORTED, "the backward needs %zu bytes of LDS per workgroup, the device has %d",
+                    sdm::bwd_lds_bytes(W, a.S), dev->lds_per_block);
+    a.k_idx = ck.pb.k_idx; a.q_idx = ck.pb.q_idx; a.k_id8 = ck.pb.k_id8; a.q_id8 = ck.pb.q_id8;
+    a.k_val = static_cast<const float *>(weights->write);
+    a.q_val = static_cast<const float *>(weights->read);
+    a.beta = beta; a.g = log_decay; a.v = v; a.go = grad_out; a.valid = valid_tokens;
+    a.bank = static_cast<float *>(bank->data);
+    a.gbank = grads->bank; a.gv = grads->v; a.gk = grads->write; a.gq = grads->read;
+    a.gbeta = grads->beta; a.gg = grads->log_decay;
+    unsigned char *ws = static_cast<unsigned char *>(exec->workspace);
+    a.snap = reinterpret_cast<float *>(ws);
+    a.lead = reinterpret_cast<float2 *>(ws + z.snap);
+    a.part = reinterpret_cast<float *>(ws + z.snap + z.lead);
+    const hipError_t e = sdm::launch_bwd(a, static_cast<hipStream_t>(exec->stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "backward launch");
 }
 
 }  // extern "C"

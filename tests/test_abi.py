@@ -30,7 +30,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sdm_chunk_mats", "sdm_error_string", "sdm_fwd", "sdm_fwd_plan",
+    assert declared_functions() == ["sdm_bwd", "sdm_bwd_workspace_bytes", "sdm_chunk_mats", "sdm_error_string",
+                                    "sdm_fwd", "sdm_fwd_plan",
                                     "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_product_key_topk",
                                     "sdm_product_key_topk_backward", "sdm_wy_solve"]
 
@@ -234,3 +235,46 @@ def test_topk_backward_rejects_before_any_launch(lib):
     assert call(factors=(5000,)) == UNSUPPORTED and call(lin=None) == NULL
     assert call(lin=fake + 4) == ALIGN and call(dtype=1, g=fake + 1) == ALIGN
     assert call(rows=0, lin=None, g=None, out=None) == OK
+
+
+def test_bwd_workspace_bytes(lib):
+    """Saved rows (4 * W * hd bytes per token), folded read slots (8 * R per token) and the
+    per-slice dots (4 * (2W + R + 1) per token and column slice), each 256-byte aligned.
+    Config 1's shapes take 4-column slices (8 streams x 16 slices = 128 workgroups)."""
+    f = lib.sdm_bwd_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int32] * 5
+    snap, lead, part = 8 * 2048 * 8 * 64 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4
+    assert f(8, 2048, 8, 8, 64) == snap + lead + part
+    assert f(0, 2048, 8, 8, 64) == 0 and f(8, 2048, 0, 8, 64) == 0 and f(8, 2048, 8, 257, 64) == 0
+
+
+def test_bwd_rejects_before_any_work(lib):
+    from chunked_sparse_delta_amd import _Bank, _Exec, _Grads, _Slots, _Weights
+    lib.sdm_last_error.restype = ctypes.c_char_p
+    f = lib.sdm_bwd
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 6
+    lib.sdm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.sdm_bwd_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+    fake = Call.FAKE
+    P, T, W, R, hd, M = 2, 100, 4, 3, 64, 50
+    need = lib.sdm_bwd_workspace_bytes(P, T, W, R, hd)
+    ptr = {k: fake + (i << 32) for i, k in enumerate(["kidx", "qidx", "kval", "qval", "beta", "g", "v", "bank", "go",
+                                                      "ws", "gbank", "gv", "gbeta", "gg", "gk", "gq"])}
+
+    def call(dtype=0, shared=0, ws=need, gbank=None, gv=None, G=W, kb=4):
+        slots = _Slots(ptr["kidx"], ptr["qidx"], W, R, kb, 4)
+        weights = _Weights(ptr["kval"], ptr["qval"])
+        bank = _Bank(ptr["bank"], M, hd, dtype, shared)
+        grads = _Grads(ptr["gbank"] if gbank is None else gbank, ptr["gv"] if gv is None else gv, ptr["gbeta"],
+                       ptr["gg"], ptr["gk"], ptr["gq"])
+        ex = _Exec(None, ptr["ws"], ws, None, 0, None)
+        return f(P, T, ctypes.byref(slots), ctypes.byref(weights), ptr["beta"], ptr["g"], G, ptr["v"],
+                 ctypes.byref(bank), None, ptr["go"], ctypes.byref(grads), ctypes.byref(ex))
+
+    assert call(dtype=1) == DTYPE and b"float32" in lib.sdm_last_error()
+    assert call(shared=1) == UNSUPPORTED
+    assert call(ws=need - 1) == WORKSPACE
+    assert call(gv=0) == NULL and call(gv=ptr["gv"] + 2) == ALIGN
+    assert call(gbank=ptr["bank"] + 64) == SHAPE
+    assert call(G=2) == SHAPE and call(kb=3) == DTYPE

@@ -1,0 +1,125 @@
+"""The backward (sdm_bwd through the C ABI) against the backward oracle O3 (the fp64
+adjoint of the token loop, pinned by finite differences of the forward oracle).
+
+Bar: infinity-norm relative error per gradient tensor within 1e-4 (the float32 bar of the
+forward; the emulated float32 error of these sizes is ~1e-6), padding tokens exactly 0,
+the bank restored bit for bit, bitwise-identical reruns."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import small
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+NAMES = {"bank": "bank", "v": "v", "beta": "beta", "log_decay": "g", "k_val": "k_val", "q_val": "q_val"}
+
+
+def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False):
+    inp = gu.generate(wl)
+    if dup_reads and wl.R > 1:
+        inp["q_idx"][:, ::2, -1] = inp["q_idx"][:, ::2, 0]
+    gr = workloads.grad_inputs(wl, seed, bank_grad)
+    t = gu.to_torch(inp, gpu)
+    if id64:
+        t["k_idx"], t["q_idx"] = t["k_idx"].long(), t["q_idx"].long()
+    from chunked_sparse_delta_amd import sdm_bwd
+    bank = t["bank"].clone()
+    gb = None if gr["grad_bank"] is None else torch.from_numpy(gr["grad_bank"]).to(gpu)
+    got = sdm_bwd(bank, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
+                  torch.from_numpy(gr["grad_out"]).to(gpu), grad_bank=gb, valid_tokens=t["valid"])
+    torch.cuda.synchronize()
+    return inp, gr, t, bank, got
+
+
+def _check(inp, gr, got, streams=None):
+    f = oracle.as_f64_inputs(inp)
+    want = oracle.token_loop_backward(f, gr["grad_out"], gr["grad_bank"], threads=8, streams=streams)
+    sel = slice(None) if streams is None else list(streams)
+    for k, ok in NAMES.items():
+        g = gu.f64(got[k])[sel]
+        w = want[ok][sel]
+        assert g.shape == w.shape, k
+        assert gu.rel_err(g, w) <= TOL, (k, gu.rel_err(g, w))
+    valid = inp["valid"]
+    for p in (range(inp["valid"].shape[0]) if streams is None else streams):
+        n = int(valid[p])
+        for k in ("v", "beta", "log_decay", "k_val", "q_val"):
+            assert not gu.f64(got[k])[p, n:].any(), (k, p)
+
+
+CASES = [
+    small(P=2, T=37, C=16, hd=8, M=24, W=3, R=2),
+    small(P=3, T=50, C=16, hd=10, M=9, W=4, R=5, ragged=True, index=11),               # ragged hd, many repeats
+    small(P=2, T=40, C=16, hd=70, M=30, W=5, R=3, gate_width=1, index=12),             # G = 1, several slices
+    small(P=1, T=64, C=16, hd=16, M=6, W=3, R=4, decay_scale=1.5, index=13),           # strong decays
+    small(P=2, T=30, C=16, hd=33, M=300, W=40, R=70, ids="zipf", index=14),            # W, R above one pass
+    small(P=4, T=20, C=16, hd=1, M=5, W=2, R=1, index=15),                             # one column
+    small(P=2, T=25, C=16, hd=64, M=512, W=256, R=256, index=16),                      # widest entries
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_backward_matches_oracle(gpu, wl):
+    inp, gr, t, bank, got = _run(wl, gpu, dup_reads=True)
+    _check(inp, gr, got)
+    assert np.array_equal(gu.bits(bank), gu.bits(t["bank"])), "bank not restored bit for bit"
+
+
+def test_backward_without_bank_gradient_int64_ids(gpu):
+    wl = small(P=2, T=45, C=16, hd=12, M=20, W=3, R=3, ragged=True, index=17)
+    inp, gr, t, bank, got = _run(wl, gpu, bank_grad=False, id64=True)
+    _check(inp, gr, got)
+
+
+def test_backward_all_padding_stream(gpu):
+    wl = small(P=3, T=20, C=16, hd=8, M=10, W=2, R=2, index=18)
+    inp = gu.generate(wl)
+    inp["valid"] = np.array([20, 0, 7], np.int32)
+    gr = workloads.grad_inputs(wl, 1)
+    t = gu.to_torch(inp, gpu)
+    from chunked_sparse_delta_amd import sdm_bwd
+    got = sdm_bwd(t["bank"].clone(), t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"],
+                  t["q_val"], torch.from_numpy(gr["grad_out"]).to(gpu),
+                  grad_bank=torch.from_numpy(gr["grad_bank"]).to(gpu), valid_tokens=t["valid"])
+    torch.cuda.synchronize()
+    _check(inp, gr, got)
+    assert np.array_equal(gu.f64(got["bank"])[1], gr["grad_bank"][1].astype(np.float64))
+
+
+def test_backward_reruns_are_bitwise_and_slices_agree(gpu, monkeypatch):
+    wl = small(P=2, T=60, C=16, hd=96, M=40, W=6, R=5, ragged=True, index=19)
+    runs = []
+    for sl in (None, None, "64", "4"):
+        if sl is None:
+            monkeypatch.delenv("SDM_BWD_SLICE", raising=False)
+        else:
+            monkeypatch.setenv("SDM_BWD_SLICE", sl)
+        runs.append(_run(wl, gpu, seed=3)[4])
+    for k in NAMES:
+        assert np.array_equal(gu.bits(runs[0][k]), gu.bits(runs[1][k])), k
+        for r in runs[2:]:
+            assert gu.rel_err(gu.f64(r[k]), gu.f64(runs[0][k])) <= 1e-5, k
+
+
+def test_backward_config1_shape_full_size(gpu):
+    """The benchmarked backward workload: config 1's shapes (8 streams x 2048 tokens, head 64,
+    4096 rows, 8 + 8 slots) with a float32 bank, every gradient against O3."""
+    wl = workloads.CONFIGS["1"].replace(dtype="f32")
+    inp, gr, t, bank, got = _run(wl, gpu)
+    _check(inp, gr, got)
+    assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
+
+
+def test_backward_rejects_bf16_bank(gpu):
+    from chunked_sparse_delta_amd import sdm_bwd
+    wl = small(P=1, T=16, C=16, hd=8, M=8, W=2, R=2, dtype="bf16")
+    t = gu.to_torch(gu.generate(wl), gpu)
+    with pytest.raises(TypeError):
+        sdm_bwd(t["bank"], t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
+                torch.zeros(1, 16, 8, device=gpu))

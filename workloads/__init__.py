@@ -294,3 +294,12 @@ def per_stream_bank(shared: np.ndarray, P: int) -> np.ndarray:
     """[P, M, hd] view order of a bank interleaved by ``shared_bank_inputs``."""
     MP, hd = shared.shape
     return shared.reshape(MP // P, P, hd).transpose(1, 0, 2)
+
+
+def grad_inputs(wl: Workload, seed: int = 0, bank_grad: bool = True) -> dict:
+    """Seeded gradients to push through the backward: grad_out [P, T, hd] ~ N(0, 1) and,
+    with ``bank_grad``, grad_bank [P, M, hd] ~ N(0, 1) (else None), float32."""
+    rng = np.random.default_rng([wl.index, 7919, seed])
+    go = rng.standard_normal((wl.P, wl.T, wl.hd), dtype=np.float32)
+    gb = rng.standard_normal((wl.P, wl.M, wl.hd), dtype=np.float32) if bank_grad else None
+    return dict(grad_out=go, grad_bank=gb)
