@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu-baseline]
     python bench.py --copy-calibration      # plain 1 GiB device copy, for scaling HBM counters
+    python bench.py --op sdm_bwd [--workload 1]   # the backward (float32 bank)
+    python bench.py --op topk               # the product-key top-k
 
 A step is one sdm_fwd call over the whole workload (every chunk step of every stream)
 with all inputs resident in HBM. The bank is advanced in place from step to step, as a
@@ -49,9 +51,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 launches)")
-    ap.add_argument("--op", default="sdm_fwd", choices=("sdm_fwd", "topk"),
-                    help="sdm_fwd: the memory op (default); topk: the product-key top-k that selects "
-                         "its slots, on the workload TOPK_WORKLOAD")
+    ap.add_argument("--op", default="sdm_fwd", choices=("sdm_fwd", "sdm_bwd", "topk"),
+                    help="sdm_fwd: the memory op (default); sdm_bwd: its backward on the workload's shapes "
+                         "with a float32 bank; topk: the product-key top-k that selects its slots, on the "
+                         "workload TOPK_WORKLOAD")
     return ap.parse_args()
 
 
@@ -199,6 +202,116 @@ def to_torch(inp: dict, device) -> dict:
                 valid=torch.from_numpy(np.ascontiguousarray(inp["valid"], dtype=np.int32)).to(device))
 
 
+BWD_KERNELS = ("bwd_lead", "bwd_sweep", "bwd_reduce")
+
+
+def bench_bwd(args):
+    """One step = one sdm_bwd call over the whole workload (config shapes, float32 bank):
+    the replay of the forward, the reverse sweep and the reduction. The bank comes back
+    bit for bit after each call; grad_bank is carried from call to call (in/out), which
+    changes values, not work."""
+    import torch
+    from chunked_sparse_delta_amd import BWD_TIMING_EVENTS, bwd_workspace_bytes, sdm_bwd
+    wl = workloads.CONFIGS[args.workload].replace(dtype="f32")
+    dev = torch.device("cuda:0")
+    name = "sdm_bwd_" + workloads.workload_name(wl).split("_", 1)[1]
+    print(f"bench: generating workload {name}", file=sys.stderr, flush=True)
+    inp = workloads.generate(wl)
+    gr = workloads.grad_inputs(wl, 0)
+    t = to_torch(inp, dev)
+    go = torch.from_numpy(gr["grad_out"]).to(dev)
+    gbank = torch.from_numpy(gr["grad_bank"]).to(dev)
+    ws = torch.empty(bwd_workspace_bytes(wl.P, wl.T, wl.W, wl.R, wl.hd), dtype=torch.uint8, device=dev)
+    hip = hip_runtime()
+    nev = BWD_TIMING_EVENTS
+    ev_sets = []
+    for _ in range(args.steps):
+        arr = (ctypes.c_void_p * nev)()
+        for k in range(nev):
+            ev = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[k] = ev.value
+        ev_sets.append(arr)
+
+    def step(events=None):
+        sdm_bwd(t["bank"], t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], go,
+                grad_bank=gbank, valid_tokens=t["valid"], workspace=ws, events=events)
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"bench: {args.steps} instrumented steps for the per-kernel times", file=sys.stderr, flush=True)
+    for k in range(args.steps):
+        step(ev_sets[k])
+    torch.cuda.synchronize()
+    per = np.zeros((args.steps, nev - 1))
+    for k, arr in enumerate(ev_sets):
+        for j in range(nev - 1):
+            ms = ctypes.c_float()
+            hip.hipEventElapsedTime(ctypes.byref(ms), arr[j], arr[j + 1])
+            per[k, j] = ms.value
+        for j in range(nev):
+            hip.hipEventDestroy(arr[j])
+    kern_ms = dict(zip(BWD_KERNELS, per.mean(axis=0).round(5).tolist()))
+
+    # Algorithmic bytes of the sweep, per live token (rows of hd float32): the replay reads
+    # the W written rows, saves them and writes them back (3W); the reverse reads the R read
+    # rows, reads and writes the bank gradient of each distinct read slot, reads the W saved
+    # rows, reads and writes the W bank-gradient rows and restores the W bank rows (4W + R +
+    # 2U_r); v twice, grad_out once, grad_v once (4 vectors); plus 4 bytes per token, slice
+    # and dot product (2W + R + 1).
+    S = 4
+    while S < 64 and S < wl.hd:
+        S <<= 1
+    while S > 4 and wl.P * (-(-wl.hd // S)) < 256:
+        S >>= 1
+    NS = -(-wl.hd // S)
+    valid = np.asarray(inp["valid"], dtype=np.int64)
+    tokens = int(valid.sum())
+    ur = sum(len(set(inp["q_idx"][p, t_].tolist())) for p in range(wl.P) for t_ in range(int(valid[p])))
+    row = 4 * wl.hd
+    sweep_bytes = row * (tokens * (7 * wl.W + wl.R + 4) + 2 * ur) + 4 * NS * tokens * (2 * wl.W + wl.R + 1)
+    gbs = sweep_bytes / (kern_ms["bwd_sweep"] * 1e-3) / 1e9
+    res = {
+        "metric": "SDM bwd tokens/sec at 1 MI355X", "value": round(tokens * args.steps / elapsed, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * elapsed / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "streams": wl.P, "tokens": wl.T, "head_dim": wl.hd, "rows": wl.M,
+                   "write_slots": wl.W, "read_slots": wl.R, "bank_dtype": "f32", "ids": wl.ids},
+        "kernel_ms": kern_ms,
+        "roofline": {"bound": "hbm", "kernel": "bwd_sweep", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "bytes_per_launch": int(sweep_bytes), "slice_columns": S,
+                     "note": "token-sequential per column slice: bound by the latency of each token's "
+                             "dependent loads and barriers, not by bandwidth"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        f = oracle.as_f64_inputs(inp)
+        threads = max(1, min(wl.P, os.cpu_count() or 1, 16))
+        oracle.token_loop_backward(f, gr["grad_out"], gr["grad_bank"], threads=threads)
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.token_loop_backward(f, gr["grad_out"], gr["grad_bank"], threads=threads)
+            reps += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": round(reps * tokens / el, 1), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle", "sample": f"the whole workload x {reps} passes of the fp64 "
+                                                           f"backward oracle, {threads} threads, {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(inp: dict, wl, seconds: float) -> dict:
     import oracle
     f = oracle.as_f64_inputs(inp)
@@ -228,6 +341,9 @@ def main():
         sys.exit(2)
     if args.op == "topk":
         bench_topk(args)
+        return
+    if args.op == "sdm_bwd":
+        bench_bwd(args)
         return
     import torch
     from chunked_sparse_delta_amd import TIMING_EVENTS, plan, sdm_fwd, workspace_bytes

@@ -73,6 +73,7 @@ _ID_BYTES = {torch.int32: 4, torch.int64: 8}
 
 
 TIMING_EVENTS = 8   # SDM_TIMING_EVENTS
+BWD_TIMING_EVENTS = 4   # SDM_BWD_TIMING_EVENTS
 
 
 _lock = threading.Lock()
@@ -275,13 +276,14 @@ def bwd_workspace_bytes(P: int, T: int, W: int, R: int, hd: int) -> int:
 def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
             log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, grad_out: torch.Tensor, *,
             grad_bank: torch.Tensor | None = None, valid_tokens: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None, stream=None) -> dict:
+            workspace: torch.Tensor | None = None, stream=None, events=None) -> dict:
     """Backward of sdm_fwd for float32 banks, one per stream. ``bank`` [P, M, hd] holds the
     bank the forward STARTED from; the call replays the forward on it and restores it
     exactly. ``grad_out`` [P, T, hd] is the gradient of the readings; ``grad_bank`` (float32
     [P, M, hd], optional) that of the final bank, and it is overwritten in place with the
     gradient with respect to the initial bank (a zero tensor is allocated if omitted).
-    Returns dict(bank, v, beta, log_decay, k_val, q_val) of float32 gradients."""
+    ``events``: optional ctypes array of BWD_TIMING_EVENTS hipEvent_t recorded at the kernel
+    boundaries. Returns dict(bank, v, beta, log_decay, k_val, q_val) of float32 gradients."""
     lib = _load()
     if bank.dtype != torch.float32 or bank.dim() != 3:
         raise TypeError("sdm_bwd takes a float32 bank of one [M, hd] bank per stream")
@@ -302,7 +304,9 @@ def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
         workspace = _workspace(bwd_workspace_bytes(P, T, W, R, hd), dev)
     gr = _Grads(*(out[k].data_ptr() for k in ("bank", "v", "beta", "log_decay", "k_val", "q_val")))
     bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 0)
-    ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(), None, 0, None)
+    ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+               None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events),
+               None)
     rc = lib.sdm_bwd(P, T, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G, _ptr(v),
                      ctypes.byref(bk), _ptr(valid_tokens), _ptr(grad_out), ctypes.byref(gr), ctypes.byref(ex))
     _check_rc(lib, rc)

@@ -564,9 +564,16 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     a.P = P; a.T = T; a.W = W; a.R = R; a.G = gate_width; a.hd = hd; a.M = M;
     a.S = sdm::bwd_slice_cols(P, hd);
     a.NS = (hd + a.S - 1) / a.S;
-    if (sdm::bwd_lds_bytes(W, a.S) > size_t(dev->lds_per_block))
+    // one wavefront per slice with the slices of the bank and of its gradient in LDS when they fit
+    // and a lane covers its entries in at most 4 (SDM_BWD_RES=0 turns it off)
+    const char *res_env = getenv("SDM_BWD_RES");
+    const size_t res_lds = sdm::bwd_lds_bytes(W, a.S, M, true);
+    const bool res_ok = (!res_env || atoi(res_env) != 0) && res_lds <= size_t(dev->lds_per_block) &&
+                        res_lds <= size_t(sdm::kBwdMaxLds);
+    a.res = res_ok ? sdm::bwd_res_entries(W, R, a.S) : 0;
+    if (!a.res && sdm::bwd_lds_bytes(W, a.S, M, false) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "the backward needs %zu bytes of LDS per workgroup, the device has %d",
-                    sdm::bwd_lds_bytes(W, a.S), dev->lds_per_block);
+                    sdm::bwd_lds_bytes(W, a.S, M, false), dev->lds_per_block);
     a.k_idx = ck.pb.k_idx; a.q_idx = ck.pb.q_idx; a.k_id8 = ck.pb.k_id8; a.q_id8 = ck.pb.q_id8;
     a.k_val = static_cast<const float *>(weights->write);
     a.q_val = static_cast<const float *>(weights->read);
@@ -578,7 +585,9 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     a.snap = reinterpret_cast<float *>(ws);
     a.lead = reinterpret_cast<float2 *>(ws + z.snap);
     a.part = reinterpret_cast<float *>(ws + z.snap + z.lead);
-    const hipError_t e = sdm::launch_bwd(a, static_cast<hipStream_t>(exec->stream));
+    hipEvent_t *ev = nullptr;
+    if (exec->events && exec->num_events >= SDM_BWD_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
+    const hipError_t e = sdm::launch_bwd(a, static_cast<hipStream_t>(exec->stream), ev);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "backward launch");
 }
 

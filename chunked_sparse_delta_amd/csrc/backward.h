@@ -5,9 +5,12 @@
 namespace sdm {
 
 constexpr int kBwdBlock = 256;
+constexpr int kBwdMaxLds = 160 * 1024 - 256;   // LDS a workgroup of the resident sweep may take
 
 struct BwdArgs {
     int32_t P, T, W, R, G, hd, S, NS;   // S columns per slice (power of two, 4..64), NS slices
+    int32_t res;                        // 0: rows in memory; 1, 2, 4: the resident sweep with that
+                                        // many entries of each kind per lane
     int64_t M;
     const void *k_idx, *q_idx;
     int32_t k_id8, q_id8;
@@ -24,9 +27,10 @@ struct BwdArgs {
 
 __host__ __device__ inline int bwd_parts(int W, int R) { return 2 * W + R + 1; }
 
-size_t bwd_lds_bytes(int W, int S);
+size_t bwd_lds_bytes(int W, int S, int64_t M, bool res);
 int bwd_slice_cols(int P, int hd);
+int bwd_res_entries(int W, int R, int S);
 hipError_t bwd_prepare();
-hipError_t launch_bwd(const BwdArgs &a, hipStream_t st);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev);
 
 }  // namespace sdm

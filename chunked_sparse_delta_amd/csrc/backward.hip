@@ -82,23 +82,28 @@ struct BwdSmem {
     // followed by old[W * S] and gbw[W * S] (dynamic)
 };
 
-size_t bwd_lds_bytes(int W, int S) { return sizeof(BwdSmem) + size_t(2) * W * S * sizeof(float); }
+size_t bwd_lds_bytes(int W, int S, int64_t M, bool res) {
+    return res ? kWave * sizeof(float) + size_t(2) * M * S * sizeof(float)
+               : sizeof(BwdSmem) + size_t(2) * W * S * sizeof(float);
+}
 
 // Lanes are (entry e, column c): c = tid % S, entries e, e + E, ... with E = 256 / S.
 // Loads of the token's parameters into LDS (the caller synchronizes afterwards).
+template <int NT>
 __device__ __forceinline__ void load_token(const BwdArgs &a, BwdSmem &sm, int64_t tok, int col, bool colok,
                                            bool reads) {
     const int tid = threadIdx.x;
-    if (tid < a.W) {
-        const int32_t s = clamp_row(load_id(a.k_idx, tok * a.W + tid, a.k_id8), a.M);
-        sm.kid[tid] = s;
-        sm.kv[tid] = a.k_val[tok * a.W + tid];
-        sm.gam[tid] = __expf(a.g[tok * a.G + (a.G == 1 ? 0 : tid)]);
+    for (int w = tid; w < a.W; w += NT) {
+        const int32_t s = clamp_row(load_id(a.k_idx, tok * a.W + w, a.k_id8), a.M);
+        sm.kid[w] = s;
+        sm.kv[w] = a.k_val[tok * a.W + w];
+        sm.gam[w] = __expf(a.g[tok * a.G + (a.G == 1 ? 0 : w)]);
     }
-    if (reads && tid < a.R) {
-        sm.qid[tid] = clamp_row(load_id(a.q_idx, tok * a.R + tid, a.q_id8), a.M);
-        sm.qlead[tid] = a.lead[tok * a.R + tid];
-    }
+    if (reads)
+        for (int r = tid; r < a.R; r += NT) {
+            sm.qid[r] = clamp_row(load_id(a.q_idx, tok * a.R + r, a.q_id8), a.M);
+            sm.qlead[r] = a.lead[tok * a.R + r];
+        }
     if (tid < a.S) {
         const int64_t o = tok * a.hd + (colok ? col : 0);
         sm.lv[tid] = colok ? a.v[o] : 0.0f;
@@ -109,19 +114,20 @@ __device__ __forceinline__ void load_token(const BwdArgs &a, BwdSmem &sm, int64_
 
 // old_w into LDS and the partial retrieval sums of this lane into sm.red. From the bank
 // (forward replay, saving old_w) or from the saved rows (reverse): the same arithmetic, so
-// both passes see the same delta.
-template <bool kReplay>
-__device__ __forceinline__ void retrieve(const BwdArgs &a, BwdSmem &sm, float *old, float *bank, int64_t tok,
-                                         int e, int c, int E, int col, bool colok) {
+// both passes see the same delta. Rows are addressed as bk[row * rs]: bk already points at
+// the lane's column (of the bank in memory, or of the workgroup's slice held in LDS).
+template <bool kReplay, int NT>
+__device__ __forceinline__ void retrieve(const BwdArgs &a, BwdSmem &sm, float *old, float *bk, int64_t rs,
+                                         int64_t tok, int e, int c, int cc, bool colok) {
+    const int E = NT / a.S;
     float acc = 0.0f;
-    const int cc = colok ? col : 0;
     for (int w0 = 0; w0 < a.W; w0 += E) {
         const int w = w0 + e;
         if (w < a.W) {
             float o;
             float *sp = a.snap + (tok * a.W + w) * a.hd + cc;
             if (kReplay) {
-                o = colok ? bank[int64_t(sm.kid[w]) * a.hd + cc] : 0.0f;
+                o = colok ? bk[int64_t(sm.kid[w]) * rs] : 0.0f;
                 if (colok) *sp = o;
             } else {
                 o = colok ? *sp : 0.0f;
@@ -133,46 +139,51 @@ __device__ __forceinline__ void retrieve(const BwdArgs &a, BwdSmem &sm, float *o
     sm.red[threadIdx.x] = acc;
 }
 
-// ret = sum over entry groups in ascending order; delta = beta (v - ret). Lanes tid < S.
+// ret = sum over entry groups in ascending order (groups past the last entry hold 0 and are
+// skipped); delta = beta (v - ret). Lanes tid < S.
 __device__ __forceinline__ void finish_delta(const BwdArgs &a, BwdSmem &sm, int E) {
     const int c = threadIdx.x;
+    const int ne = a.W < E ? a.W : E;
     float ret = 0.0f;
-    for (int e = 0; e < E; ++e) ret += sm.red[e * a.S + c];
+    for (int e = 0; e < ne; ++e) ret += sm.red[e * a.S + c];
     const float vr = sm.lv[c] - ret;
     sm.lvr[c] = vr;
     sm.ldelta[c] = sm.beta * vr;
 }
 
-__global__ void __launch_bounds__(kBwdBlock) bwd_sweep_kernel(BwdArgs a) {
+// The sweep in memory: NT threads per (stream, column slice), rows read and written in the
+// bank and the bank gradient themselves, token values staged through LDS.
+template <int NT>
+__global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     BwdSmem &sm = *reinterpret_cast<BwdSmem *>(smem_raw);
     float *old = reinterpret_cast<float *>(smem_raw + sizeof(BwdSmem));
     float *gbw = old + a.W * a.S;
     const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
-    const int tid = threadIdx.x, S = a.S, E = kBwdBlock / S;
+    const int tid = threadIdx.x, S = a.S, E = NT / S;
     const int c = tid % S, e = tid / S;
     const int col = sl * S + c;
     const bool colok = col < a.hd;
     const int cc = colok ? col : 0;
-    float *bank = a.bank + int64_t(p) * a.M * a.hd;
-    float *gb = a.gbank + int64_t(p) * a.M * a.hd;
+    float *bk = a.bank + int64_t(p) * a.M * a.hd + cc;
+    float *gk = a.gbank + int64_t(p) * a.M * a.hd + cc;
+    const int64_t rs = a.hd;
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
 
     // forward replay
     for (int t = 0; t < n; ++t) {
         const int64_t tok = int64_t(p) * a.T + t;
-        load_token(a, sm, tok, col, colok, false);
+        load_token<NT>(a, sm, tok, col, colok, false);
         __syncthreads();
-        retrieve<true>(a, sm, old, bank, tok, e, c, E, col, colok);
+        retrieve<true, NT>(a, sm, old, bk, rs, tok, e, c, cc, colok);
         __syncthreads();
         if (tid < S) finish_delta(a, sm, E);
         __syncthreads();
         for (int w0 = 0; w0 < a.W; w0 += E) {
             const int w = w0 + e;
             if (w < a.W && colok)
-                bank[int64_t(sm.kid[w]) * a.hd + cc] =
-                    __builtin_fmaf(sm.kv[w], sm.ldelta[c], sm.gam[w] * old[w * S + c]);
+                bk[int64_t(sm.kid[w]) * rs] = __builtin_fmaf(sm.kv[w], sm.ldelta[c], sm.gam[w] * old[w * S + c]);
         }
         __syncthreads();
     }
@@ -181,22 +192,22 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_sweep_kernel(BwdArgs a) {
     for (int t = n - 1; t >= 0; --t) {
         const int64_t tok = int64_t(p) * a.T + t;
         float *pt = a.part + ((int64_t(p) * a.NS + sl) * a.T + t) * J;
-        load_token(a, sm, tok, col, colok, true);
+        load_token<NT>(a, sm, tok, col, colok, true);
         __syncthreads();
         // reading: grad_q_r = <go, bank[s_r]> (bank after the token); gb[s_r] += q_r go
         for (int r0 = 0; r0 < a.R; r0 += E) {
             const int r = r0 + e;
             const int rr = r < a.R ? r : a.R - 1;
-            const int64_t o = int64_t(sm.qid[rr]) * a.hd + cc;
-            const float row = colok ? bank[o] : 0.0f;
+            const int64_t o = int64_t(sm.qid[rr]) * rs;
+            const float row = colok ? bk[o] : 0.0f;
             const float d = group_sum(sm.lgo[c] * row, S);
             const float2 ld = sm.qlead[rr];
             if (r < a.R) {
                 if (c == 0) pt[2 * a.W + r] = d;
-                if (colok && ld.y != 0.0f) gb[o] = __builtin_fmaf(ld.x, sm.lgo[c], gb[o]);
+                if (colok && ld.y != 0.0f) gk[o] = __builtin_fmaf(ld.x, sm.lgo[c], gk[o]);
             }
         }
-        retrieve<false>(a, sm, old, bank, tok, e, c, E, col, colok);
+        retrieve<false, NT>(a, sm, old, bk, rs, tok, e, c, cc, colok);
         __syncthreads();
         if (tid < S) finish_delta(a, sm, E);
         __syncthreads();
@@ -206,7 +217,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_sweep_kernel(BwdArgs a) {
             for (int w0 = 0; w0 < a.W; w0 += E) {
                 const int w = w0 + e;
                 const int ww = w < a.W ? w : a.W - 1;
-                const float x = colok ? gb[int64_t(sm.kid[ww]) * a.hd + cc] : 0.0f;
+                const float x = colok ? gk[int64_t(sm.kid[ww]) * rs] : 0.0f;
                 const float d = group_sum(x * sm.ldelta[c], S);
                 if (w < a.W) {
                     gbw[w * S + c] = x;
@@ -218,8 +229,9 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_sweep_kernel(BwdArgs a) {
         }
         __syncthreads();
         if (tid < S) {
+            const int ne = a.W < E ? a.W : E;
             float gd = 0.0f;
-            for (int q = 0; q < E; ++q) gd += sm.red[q * S + tid];
+            for (int q = 0; q < ne; ++q) gd += sm.red[q * S + tid];
             if (colok) a.gv[tok * a.hd + col] = sm.beta * gd;
             sm.lgret[tid] = -sm.beta * gd;
             const float gbeta = group_sum(gd * sm.lvr[tid], S);
@@ -239,9 +251,9 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_sweep_kernel(BwdArgs a) {
             const float dg = group_sum(gdec * dec, S);
             if (w < a.W) {
                 if (colok) {
-                    const int64_t ro = int64_t(sm.kid[w]) * a.hd + cc;
-                    gb[ro] = sm.gam[w] * gdec;
-                    bank[ro] = o;
+                    const int64_t ro = int64_t(sm.kid[w]) * rs;
+                    gk[ro] = sm.gam[w] * gdec;
+                    bk[ro] = o;
                 }
                 if (c == 0) {
                     pt[w] = sm.lka[w] + dk;
@@ -250,6 +262,229 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_sweep_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Resident sweep: one wavefront per (stream, column slice) whose slices of the bank and of
+// the bank gradient fit in LDS together. Lane (e, c) owns column c of entries e, e + E, ..
+// (E = 64 / S, at most KJ entries of each kind per lane). A token's slot ids, weights and
+// gates, v, grad_out and saved rows are loaded straight into the lanes that use them, one
+// token ahead, so the only memory a token waits on is LDS; sums over the entries of a
+// column go through a small LDS array read back by every lane of the column, sums over
+// the columns of an entry through DPP / lane shuffles. A wavefront's LDS operations take
+// effect in program order, so no workgroup barrier is needed.
+// ---------------------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the S consecutive lanes of a group (S a power of two, 4..64); every lane of the
+// group ends with the same bits (each step adds two equal-shaped partial sums).
+__device__ __forceinline__ float lane_group_sum(float x, int S) {
+    x = dpp_add<0xB1>(x);                 // quad_perm [1, 0, 3, 2]
+    x = dpp_add<0x4E>(x);                 // quad_perm [2, 3, 0, 1]
+    if (S >= 8) x = dpp_add<0x141>(x);    // lane i of 8 reads lane 7 - i
+    if (S >= 16) x = dpp_add<0x140>(x);   // lane i of 16 reads lane 15 - i
+    if (S >= 32) x += __shfl_xor(x, 16, kWave);
+    if (S >= 64) x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
+template <int KJ>
+struct ResTok {
+    int32_t kid[KJ], qid[KJ];
+    float kv[KJ], gam[KJ], ql[KJ], qf[KJ], snap[KJ];
+    float v, go, beta;
+};
+
+// Token tok's values for lane (e, c); every load is issued (indices clamped into range),
+// so the loads never wait on a branch.
+template <int KJ, bool kRev>
+__device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_t tok, int e, int E, int cc) {
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+        const int w = min(e + j * E, a.W - 1);
+        x.kid[j] = clamp_row(load_id(a.k_idx, tok * a.W + w, a.k_id8), a.M);
+        x.kv[j] = a.k_val[tok * a.W + w];
+        x.gam[j] = __expf(a.g[tok * a.G + (a.G == 1 ? 0 : w)]);
+        if (kRev) {
+            const int r = min(e + j * E, a.R - 1);
+            x.qid[j] = clamp_row(load_id(a.q_idx, tok * a.R + r, a.q_id8), a.M);
+            const float2 ld = a.lead[tok * a.R + r];
+            x.ql[j] = ld.x;
+            x.qf[j] = ld.y;
+            x.snap[j] = a.snap[(tok * a.W + w) * a.hd + cc];
+        }
+    }
+    x.v = a.v[tok * a.hd + cc];
+    if (kRev) x.go = a.go[tok * a.hd + cc];
+    x.beta = a.beta[tok];
+}
+
+template <int KJ>
+__global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
+    float *lres = red + kWave;                           // bank slice [M][S], then gradient slice [M][S]
+    const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
+    const int lane = threadIdx.x, S = a.S, E = kWave / S;
+    const int c = lane % S, e = lane / S;
+    const int col = sl * S + c;
+    const bool colok = col < a.hd;
+    const int cc = colok ? col : 0;
+    const int ne = a.W < E ? a.W : E;   // entry groups holding a write entry
+    float *bank_g = a.bank + int64_t(p) * a.M * a.hd;
+    float *gb_g = a.gbank + int64_t(p) * a.M * a.hd;
+    const int64_t MS = a.M * S;
+    {
+        constexpr int kB = 16;
+        for (int64_t i0 = lane; i0 < MS; i0 += int64_t(kB) * kWave) {
+            float xb[kB], xg[kB];
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const int64_t i = i0 + int64_t(k) * kWave;
+                const int cg = sl * S + int(i % S);
+                const bool ok = i < MS && cg < a.hd;
+                const int64_t o = ok ? (i / S) * a.hd + cg : 0;
+                xb[k] = bank_g[o];
+                xg[k] = gb_g[o];
+                xb[k] = ok ? xb[k] : 0.0f;
+                xg[k] = ok ? xg[k] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const int64_t i = i0 + int64_t(k) * kWave;
+                if (i < MS) {
+                    lres[i] = xb[k];
+                    lres[MS + i] = xg[k];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float *bk = lres + c, *gk = lres + MS + c;
+    const int J = bwd_parts(a.W, a.R);
+    const int32_t n = live_tokens(a, p);
+    const int64_t tok0 = int64_t(p) * a.T;
+
+    // ret over the column's entry groups, in ascending group order (every lane of the
+    // column reads the same partials, so all get the same bits)
+    auto column_sum = [&](float part) {
+        red[c * E + e] = part;
+        __builtin_amdgcn_wave_barrier();
+        float s = 0.0f;
+        for (int q = 0; q < ne; ++q) s += red[c * E + q];
+        __builtin_amdgcn_wave_barrier();
+        return s;
+    };
+
+    // forward replay
+    ResTok<KJ> cur, nxt;
+    if (n > 0) res_load<KJ, false>(a, cur, tok0, e, E, cc);
+    for (int t = 0; t < n; ++t) {
+        const int64_t tok = tok0 + t;
+        res_load<KJ, false>(a, nxt, tok0 + (t + 1 < n ? t + 1 : t), e, E, cc);
+        float old[KJ];
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int w = e + j * E;
+            old[j] = colok ? bk[int64_t(cur.kid[j]) * S] : 0.0f;
+            if (w < a.W) {
+                if (colok) a.snap[(tok * a.W + w) * a.hd + cc] = old[j];
+                acc = __builtin_fmaf(cur.kv[j], cur.gam[j] * old[j], acc);
+            }
+        }
+        const float ret = column_sum(acc);
+        const float delta = cur.beta * ((colok ? cur.v : 0.0f) - ret);
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int w = e + j * E;
+            if (w < a.W && colok)
+                bk[int64_t(cur.kid[j]) * S] = __builtin_fmaf(cur.kv[j], delta, cur.gam[j] * old[j]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        cur = nxt;
+    }
+
+    // reverse
+    if (n > 0) res_load<KJ, true>(a, cur, tok0 + n - 1, e, E, cc);
+    for (int t = n - 1; t >= 0; --t) {
+        const int64_t tok = tok0 + t;
+        float *pt = a.part + ((int64_t(p) * a.NS + sl) * a.T + t) * J;
+        res_load<KJ, true>(a, nxt, tok0 + (t > 0 ? t - 1 : 0), e, E, cc);
+        const float go = colok ? cur.go : 0.0f;
+        // reading: grad_q_r = <go, bank[s_r]>; gb[s_r] += (summed q) go at a slot's first entry
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int r = e + j * E;
+            const int64_t o = int64_t(cur.qid[j]) * S;
+            const float d = lane_group_sum(go * (colok ? bk[o] : 0.0f), S);
+            if (r < a.R) {
+                if (c == 0) pt[2 * a.W + r] = d;
+                if (colok && cur.qf[j] != 0.0f) gk[o] = __builtin_fmaf(cur.ql[j], go, gk[o]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // the token's retrieval and delta, recomputed from the saved rows
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int w = e + j * E;
+            const float o = colok ? cur.snap[j] : 0.0f;
+            cur.snap[j] = o;
+            if (w < a.W) acc = __builtin_fmaf(cur.kv[j], cur.gam[j] * o, acc);
+        }
+        const float ret = column_sum(acc);
+        const float vr = (colok ? cur.v : 0.0f) - ret;
+        const float delta = cur.beta * vr;
+        // write: gdelta = sum_w k_w gb[s_w]; grad_k_w = <gb[s_w], delta>
+        float gbw[KJ], lka[KJ];
+        float acc2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int w = e + j * E;
+            gbw[j] = colok ? gk[int64_t(cur.kid[j]) * S] : 0.0f;
+            lka[j] = lane_group_sum(gbw[j] * delta, S);
+            if (w < a.W) acc2 = __builtin_fmaf(cur.kv[j], gbw[j], acc2);
+        }
+        const float gd = column_sum(acc2);
+        const float gret = -cur.beta * gd;
+        const float gbeta = lane_group_sum(gd * vr, S);
+        if (e == 0) {
+            if (colok) a.gv[tok * a.hd + col] = cur.beta * gd;
+            if (c == 0) pt[2 * a.W + a.R] = gbeta;
+        }
+        // retrieval and decay, then the bank row as it was before the token
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int w = e + j * E;
+            const float dec = cur.gam[j] * cur.snap[j];
+            const float gdec = __builtin_fmaf(cur.kv[j], gret, gbw[j]);
+            const float dk = lane_group_sum(gret * dec, S);
+            const float dg = lane_group_sum(gdec * dec, S);
+            if (w < a.W) {
+                if (colok) {
+                    const int64_t ro = int64_t(cur.kid[j]) * S;
+                    gk[ro] = cur.gam[j] * gdec;
+                    bk[ro] = cur.snap[j];
+                }
+                if (c == 0) {
+                    pt[w] = lka[j] + dk;
+                    pt[a.W + w] = dg;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        cur = nxt;
+    }
+    __syncthreads();
+    for (int64_t i = lane; i < MS; i += kWave) {
+        const int cg = sl * S + int(i % S);
+        if (cg < a.hd) gb_g[(i / S) * a.hd + cg] = lres[MS + i];
     }
 }
 
@@ -289,8 +524,24 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_reduce_kernel(BwdArgs a) {
 }
 
 hipError_t bwd_prepare() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_sweep_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, int(bwd_lds_bytes(kMaxWidth, kWave)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_sweep_kernel<kBwdBlock>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(bwd_lds_bytes(kMaxWidth, kWave, 0, false)));
+    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<2>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<4>)};
+    for (const void *f : res)
+        if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdMaxLds);
+    return e;
+}
+
+// Entries of each kind per lane of the resident sweep: the smallest of 1, 2, 4 that covers
+// max(W, R) with 64 / S entry groups, or 0 where none does.
+int bwd_res_entries(int W, int R, int S) {
+    const int E = kWave / S, m = W > R ? W : R;
+    for (int kj = 1; kj <= 4; kj <<= 1)
+        if (kj * E >= m) return kj;
+    return 0;
 }
 
 // Columns per slice: the widest power of two up to 64 (and up to the head) that still
@@ -307,15 +558,27 @@ int bwd_slice_cols(int P, int hd) {
     return S;
 }
 
-hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
     const int64_t toks = int64_t(a.P) * a.T;
+    hipError_t e;
+    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
     bwd_lead_kernel<<<dim3(unsigned(toks)), dim3(kBwdBlock), 0, st>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    bwd_sweep_kernel<<<dim3(unsigned(a.P * a.NS)), dim3(kBwdBlock), bwd_lds_bytes(a.W, a.S), st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+    const dim3 grid(unsigned(a.P * a.NS));
+    const size_t lds = bwd_lds_bytes(a.W, a.S, a.M, a.res != 0);
+    switch (a.res) {
+        case 1: bwd_res_kernel<1><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 2: bwd_res_kernel<2><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 4: bwd_res_kernel<4><<<grid, dim3(kWave), lds, st>>>(a); break;
+        default: bwd_sweep_kernel<kBwdBlock><<<grid, dim3(kBwdBlock), lds, st>>>(a); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
     bwd_reduce_kernel<<<dim3(unsigned(toks)), dim3(kBwdBlock), 0, st>>>(a);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+    return hipSuccess;
 }
 
 }  // namespace sdm

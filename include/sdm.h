@@ -270,10 +270,15 @@ int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *
  * exec->workspace: sdm_bwd_workspace_bytes(...) bytes, 256-byte aligned (it keeps each
  * write entry's row as it was before its token, 4 * W * head_dim bytes per token, plus
  * 8 * R bytes per token and one float per token, column slice and dot product).
+ * exec->events: optional, num_events >= SDM_BWD_TIMING_EVENTS hipEvent_t recorded on the
+ * stream before the read-slot fold, before the replay-and-reverse sweep, before the
+ * reduction of the per-slice dots, and after it. exec->repeated_writes is not used.
  * Arithmetic float32, sums in a fixed order: results are bitwise reproducible.
  * Errors as for sdm_fwd; SDM_ERR_DTYPE for a bfloat16 bank, SDM_ERR_UNSUPPORTED for a
  * shared bank (neither has a backward here).
  */
+#define SDM_BWD_TIMING_EVENTS 4
+
 typedef struct {
     float *bank;
     float *v;

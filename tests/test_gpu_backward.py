@@ -61,11 +61,24 @@ CASES = [
     small(P=2, T=30, C=16, hd=33, M=300, W=40, R=70, ids="zipf", index=14),            # W, R above one pass
     small(P=4, T=20, C=16, hd=1, M=5, W=2, R=1, index=15),                             # one column
     small(P=2, T=25, C=16, hd=64, M=512, W=256, R=256, index=16),                      # widest entries
+    small(P=2, T=40, C=16, hd=12, M=300, W=20, R=30, ragged=True, index=20),           # 2 entries per lane
+    small(P=1, T=30, C=16, hd=20, M=400, W=50, R=64, index=21),                        # 4 entries per lane
 ]
 
 
+@pytest.fixture(params=["lds", "memory"])
+def residency(request, monkeypatch):
+    """lds: the slices of the bank and its gradient held in LDS where they fit (the default);
+    memory: always read and written in memory (SDM_BWD_RES=0)."""
+    if request.param == "memory":
+        monkeypatch.setenv("SDM_BWD_RES", "0")
+    else:
+        monkeypatch.delenv("SDM_BWD_RES", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("wl", CASES, ids=[f"c{i}" for i in range(len(CASES))])
-def test_backward_matches_oracle(gpu, wl):
+def test_backward_matches_oracle(gpu, wl, residency):
     inp, gr, t, bank, got = _run(wl, gpu, dup_reads=True)
     _check(inp, gr, got)
     assert np.array_equal(gu.bits(bank), gu.bits(t["bank"])), "bank not restored bit for bit"
@@ -95,11 +108,12 @@ def test_backward_all_padding_stream(gpu):
 def test_backward_reruns_are_bitwise_and_slices_agree(gpu, monkeypatch):
     wl = small(P=2, T=60, C=16, hd=96, M=40, W=6, R=5, ragged=True, index=19)
     runs = []
-    for sl in (None, None, "64", "4"):
-        if sl is None:
-            monkeypatch.delenv("SDM_BWD_SLICE", raising=False)
-        else:
-            monkeypatch.setenv("SDM_BWD_SLICE", sl)
+    for sl, res in ((None, None), (None, None), ("64", None), ("4", None), (None, "0")):
+        for var, val in (("SDM_BWD_SLICE", sl), ("SDM_BWD_RES", res)):
+            if val is None:
+                monkeypatch.delenv(var, raising=False)
+            else:
+                monkeypatch.setenv(var, val)
         runs.append(_run(wl, gpu, seed=3)[4])
     for k in NAMES:
         assert np.array_equal(gu.bits(runs[0][k]), gu.bits(runs[1][k])), k
@@ -107,9 +121,10 @@ def test_backward_reruns_are_bitwise_and_slices_agree(gpu, monkeypatch):
             assert gu.rel_err(gu.f64(r[k]), gu.f64(runs[0][k])) <= 1e-5, k
 
 
-def test_backward_config1_shape_full_size(gpu):
+def test_backward_config1_shape_full_size(gpu, residency):
     """The benchmarked backward workload: config 1's shapes (8 streams x 2048 tokens, head 64,
-    4096 rows, 8 + 8 slots) with a float32 bank, every gradient against O3."""
+    4096 rows, 8 + 8 slots) with a float32 bank, every gradient against O3 (the bench runs
+    the LDS-resident sweep)."""
     wl = workloads.CONFIGS["1"].replace(dtype="f32")
     inp, gr, t, bank, got = _run(wl, gpu)
     _check(inp, gr, got)
@@ -123,3 +138,20 @@ def test_backward_rejects_bf16_bank(gpu):
     with pytest.raises(TypeError):
         sdm_bwd(t["bank"], t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
                 torch.zeros(1, 16, 8, device=gpu))
+
+
+@pytest.mark.parametrize("S", ["8", "16", "32", "64"])
+def test_backward_wide_slices(gpu, S, monkeypatch):
+    """Slices of 8..64 columns: the resident sweep's column sums take every lane-exchange
+    width (quad swaps, half-row and row mirrors, 16- and 32-lane shuffles); the sweep in
+    memory runs the same shapes."""
+    wl = small(P=2, T=33, C=16, hd=100, M=60, W=3, R=4, ragged=True, index=22)
+    monkeypatch.setenv("SDM_BWD_SLICE", S)
+    for res in (None, "0"):
+        if res is None:
+            monkeypatch.delenv("SDM_BWD_RES", raising=False)
+        else:
+            monkeypatch.setenv("SDM_BWD_RES", res)
+        inp, gr, t, bank, got = _run(wl, gpu, seed=int(S), dup_reads=True)
+        _check(inp, gr, got)
+        assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
