@@ -83,7 +83,7 @@ struct BwdSmem {
 };
 
 size_t bwd_lds_bytes(int W, int S, int64_t M, bool res) {
-    return res ? kWave * sizeof(float) + size_t(2) * M * S * sizeof(float)
+    return res ? kResRed * sizeof(float) + size_t(2) * M * S * sizeof(float)
                : sizeof(BwdSmem) + size_t(2) * W * S * sizeof(float);
 }
 
@@ -269,8 +269,8 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
 // Resident sweep: one wavefront per (stream, column slice) whose slices of the bank and of
 // the bank gradient fit in LDS together. Lane (e, c) owns column c of entries e, e + E, ..
 // (E = 64 / S, at most KJ entries of each kind per lane). A token's slot ids, weights and
-// gates, v, grad_out and saved rows are loaded straight into the lanes that use them, one
-// token ahead, so the only memory a token waits on is LDS; sums over the entries of a
+// gates, v, grad_out and saved rows are loaded straight into the lanes that use them, D
+// tokens ahead, so the only memory a token waits on is LDS; sums over the entries of a
 // column go through a small LDS array read back by every lane of the column, sums over
 // the columns of an entry through DPP / lane shuffles. A wavefront's LDS operations take
 // effect in program order, so no workgroup barrier is needed.
@@ -293,6 +293,12 @@ __device__ __forceinline__ float lane_group_sum(float x, int S) {
     return x;
 }
 
+// Slot id i of an int32 or int64 id array without a branch: ids lie in [0, 2^31), so the
+// low (first, little-endian) word of an int64 id is the id.
+__device__ __forceinline__ int32_t id_word(const void *base, int64_t i, int32_t id8) {
+    return static_cast<const int32_t *>(base)[i << id8];
+}
+
 template <int KJ>
 struct ResTok {
     int32_t kid[KJ], qid[KJ];
@@ -307,12 +313,12 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
         const int w = min(e + j * E, a.W - 1);
-        x.kid[j] = clamp_row(load_id(a.k_idx, tok * a.W + w, a.k_id8), a.M);
+        x.kid[j] = clamp_row(id_word(a.k_idx, tok * a.W + w, a.k_id8), a.M);
         x.kv[j] = a.k_val[tok * a.W + w];
         x.gam[j] = __expf(a.g[tok * a.G + (a.G == 1 ? 0 : w)]);
         if (kRev) {
             const int r = min(e + j * E, a.R - 1);
-            x.qid[j] = clamp_row(load_id(a.q_idx, tok * a.R + r, a.q_id8), a.M);
+            x.qid[j] = clamp_row(id_word(a.q_idx, tok * a.R + r, a.q_id8), a.M);
             const float2 ld = a.lead[tok * a.R + r];
             x.ql[j] = ld.x;
             x.qf[j] = ld.y;
@@ -324,11 +330,11 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
     x.beta = a.beta[tok];
 }
 
-template <int KJ>
+template <int KJ, int D>
 __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
-    float *lres = red + kWave;                           // bank slice [M][S], then gradient slice [M][S]
+    float *lres = red + kResRed;                         // bank slice [M][S], then gradient slice [M][S]
     const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
     const int lane = threadIdx.x, S = a.S, E = kWave / S;
     const int c = lane % S, e = lane / S;
@@ -381,12 +387,9 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
         return s;
     };
 
-    // forward replay
-    ResTok<KJ> cur, nxt;
-    if (n > 0) res_load<KJ, false>(a, cur, tok0, e, E, cc);
-    for (int t = 0; t < n; ++t) {
+    // forward replay of token t from its prefetched values
+    auto fwd_token = [&](ResTok<KJ> &cur, int t) {
         const int64_t tok = tok0 + t;
-        res_load<KJ, false>(a, nxt, tok0 + (t + 1 < n ? t + 1 : t), e, E, cc);
         float old[KJ];
         float acc = 0.0f;
 #pragma unroll
@@ -407,15 +410,12 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
                 bk[int64_t(cur.kid[j]) * S] = __builtin_fmaf(cur.kv[j], delta, cur.gam[j] * old[j]);
         }
         __builtin_amdgcn_wave_barrier();
-        cur = nxt;
-    }
+    };
 
-    // reverse
-    if (n > 0) res_load<KJ, true>(a, cur, tok0 + n - 1, e, E, cc);
-    for (int t = n - 1; t >= 0; --t) {
+    // the reverse of token t, from its prefetched values and saved rows
+    auto rev_token = [&](ResTok<KJ> &cur, int t) {
         const int64_t tok = tok0 + t;
         float *pt = a.part + ((int64_t(p) * a.NS + sl) * a.T + t) * J;
-        res_load<KJ, true>(a, nxt, tok0 + (t > 0 ? t - 1 : 0), e, E, cc);
         const float go = colok ? cur.go : 0.0f;
         // reading: grad_q_r = <go, bank[s_r]>; gb[s_r] += (summed q) go at a slot's first entry
 #pragma unroll
@@ -479,7 +479,45 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
             }
         }
         __builtin_amdgcn_wave_barrier();
-        cur = nxt;
+    };
+
+    // Token values are prefetched D tokens ahead into a ring of registers: the loop runs
+    // whole rounds of D tokens, unrolled, so each slot is a fixed set of registers and every
+    // round issues the same loads (refills past the end reload the last token); slot d of a
+    // round holds the token of the round's d-th step and is refilled with the one D tokens
+    // further on. The last n % D tokens load their values as they go.
+    ResTok<KJ> ring[D];
+    const int last = n > 0 ? n - 1 : 0;
+    const int nfull = n - n % D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) res_load<KJ, false>(a, ring[d], tok0 + min(d, last), e, E, cc);
+    for (int t0 = 0; t0 < nfull; t0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            fwd_token(ring[d], t0 + d);
+            res_load<KJ, false>(a, ring[d], tok0 + min(t0 + d + D, last), e, E, cc);
+        }
+    }
+    for (int t = nfull; t < n; ++t) {
+        ResTok<KJ> x;
+        res_load<KJ, false>(a, x, tok0 + t, e, E, cc);
+        fwd_token(x, t);
+    }
+    // reverse: the first n % D tokens from the end go one by one, then whole rounds
+    for (int t = n - 1; t >= nfull; --t) {
+        ResTok<KJ> x;
+        res_load<KJ, true>(a, x, tok0 + t, e, E, cc);
+        rev_token(x, t);
+    }
+    const int top = nfull - 1;
+#pragma unroll
+    for (int d = 0; d < D; ++d) res_load<KJ, true>(a, ring[d], tok0 + max(top - d, 0), e, E, cc);
+    for (int t0 = top; t0 >= 0; t0 -= D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            rev_token(ring[d], t0 - d);
+            res_load<KJ, true>(a, ring[d], tok0 + max(t0 - d - D, 0), e, E, cc);
+        }
     }
     __syncthreads();
     for (int64_t i = lane; i < MS; i += kWave) {
@@ -527,9 +565,9 @@ hipError_t bwd_prepare() {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_sweep_kernel<kBwdBlock>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(bwd_lds_bytes(kMaxWidth, kWave, 0, false)));
-    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1>),
-                         reinterpret_cast<const void *>(bwd_res_kernel<2>),
-                         reinterpret_cast<const void *>(bwd_res_kernel<4>)};
+    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1, 4>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<2, 2>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<4, 1>)};
     for (const void *f : res)
         if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdMaxLds);
     return e;
@@ -568,9 +606,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
     const dim3 grid(unsigned(a.P * a.NS));
     const size_t lds = bwd_lds_bytes(a.W, a.S, a.M, a.res != 0);
     switch (a.res) {
-        case 1: bwd_res_kernel<1><<<grid, dim3(kWave), lds, st>>>(a); break;
-        case 2: bwd_res_kernel<2><<<grid, dim3(kWave), lds, st>>>(a); break;
-        case 4: bwd_res_kernel<4><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 1: bwd_res_kernel<1, 4><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 2: bwd_res_kernel<2, 2><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 4: bwd_res_kernel<4, 1><<<grid, dim3(kWave), lds, st>>>(a); break;
         default: bwd_sweep_kernel<kBwdBlock><<<grid, dim3(kBwdBlock), lds, st>>>(a); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
