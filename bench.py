@@ -127,14 +127,26 @@ def phase2_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per Phase-2 launch from profiles/traffic_<workload>.md, if it was taken
-    on the current Phase-2 sources; else None."""
+BWD_SOURCES = ("chunked_sparse_delta_amd/csrc/backward.hip", "chunked_sparse_delta_amd/csrc/backward.h")
+
+
+def bwd_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in BWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, field: str = "phase2_source_sha256", current=None):
+    """HBM bytes per launch of the dominant kernel from profiles/traffic_<workload>.md, if it
+    was taken on the current sources of that kernel (Phase 2, or the backward sweep); else
+    None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     fields = dict(re.findall(r"^- (\w+): `([^`]*)`", open(path).read(), flags=re.M))
-    if fields.get("phase2_source_sha256") != phase2_source_hash():
+    if fields.get(field) != (current if current is not None else phase2_source_hash()):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -214,7 +226,7 @@ def bench_bwd(args):
     from chunked_sparse_delta_amd import BWD_TIMING_EVENTS, bwd_workspace_bytes, sdm_bwd
     wl = workloads.CONFIGS[args.workload].replace(dtype="f32")
     dev = torch.device("cuda:0")
-    name = "sdm_bwd_" + workloads.workload_name(wl).split("_", 1)[1]
+    name = workloads.workload_name(wl).replace("sdm_fwd_", "sdm_bwd_", 1)
     print(f"bench: generating workload {name}", file=sys.stderr, flush=True)
     inp = workloads.generate(wl)
     gr = workloads.grad_inputs(wl, 0)
@@ -289,7 +301,8 @@ def bench_bwd(args):
                    "write_slots": wl.W, "read_slots": wl.R, "bank_dtype": "f32", "ids": wl.ids},
         "kernel_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": "bwd_sweep", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
+                     "traffic": measured_traffic(f"bwd_{args.workload}", "bwd_source_sha256", bwd_source_hash()),
                      "bytes_per_launch": int(sweep_bytes), "slice_columns": S,
                      "note": "token-sequential per column slice: bound by the latency of each token's "
                              "dependent loads and barriers, not by bandwidth"},

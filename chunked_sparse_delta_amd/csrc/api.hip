@@ -517,7 +517,7 @@ BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd) {
     const int S = sdm::bwd_slice_cols(P, hd);
     const int64_t NS = (hd + S - 1) / S;
     BwdSizes z{};
-    z.snap = align256(size_t(P) * size_t(T) * size_t(W) * size_t(hd) * 4);
+    z.snap = align256(size_t(P) * size_t(NS) * size_t(S) * size_t(T) * size_t(W) * 4);
     z.lead = align256(size_t(P) * size_t(T) * size_t(R) * 8);
     z.part = align256(size_t(P) * size_t(NS) * size_t(T) * size_t(sdm::bwd_parts(W, R)) * 4);
     z.total = z.snap + z.lead + z.part;

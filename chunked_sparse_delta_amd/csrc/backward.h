@@ -21,7 +21,7 @@ struct BwdArgs {
     float *gbank;    // [P, M, hd], in: gradient of the final bank; out: of the initial bank
     float *gv;       // [P, T, hd]
     float *gk, *gq, *gbeta, *gg;   // [P, T, W], [P, T, R], [P, T], [P, T, G]
-    float *snap;     // [P, T, W, hd]  old_w of every live write entry
+    float *snap;     // [P, NS, T, W, S]  old_w of every live write entry, slice by slice
     float2 *lead;    // [P, T, R]      (summed weight, 1) for a slot's first read entry, else (0, 0)
     float *part;     // [P, NS, T, J]  per-slice dots, J = 2W + R + 1
 };

@@ -118,14 +118,14 @@ __device__ __forceinline__ void load_token(const BwdArgs &a, BwdSmem &sm, int64_
 // the lane's column (of the bank in memory, or of the workgroup's slice held in LDS).
 template <bool kReplay, int NT>
 __device__ __forceinline__ void retrieve(const BwdArgs &a, BwdSmem &sm, float *old, float *bk, int64_t rs,
-                                         int64_t tok, int e, int c, int cc, bool colok) {
+                                         float *snapt, int e, int c, bool colok) {
     const int E = NT / a.S;
     float acc = 0.0f;
     for (int w0 = 0; w0 < a.W; w0 += E) {
         const int w = w0 + e;
         if (w < a.W) {
             float o;
-            float *sp = a.snap + (tok * a.W + w) * a.hd + cc;
+            float *sp = snapt + w * a.S + c;
             if (kReplay) {
                 o = colok ? bk[int64_t(sm.kid[w]) * rs] : 0.0f;
                 if (colok) *sp = o;
@@ -168,6 +168,7 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     float *bk = a.bank + int64_t(p) * a.M * a.hd + cc;
     float *gk = a.gbank + int64_t(p) * a.M * a.hd + cc;
     const int64_t rs = a.hd;
+    float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
 
@@ -176,7 +177,7 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
         const int64_t tok = int64_t(p) * a.T + t;
         load_token<NT>(a, sm, tok, col, colok, false);
         __syncthreads();
-        retrieve<true, NT>(a, sm, old, bk, rs, tok, e, c, cc, colok);
+        retrieve<true, NT>(a, sm, old, bk, rs, snapw + int64_t(t) * a.W * S, e, c, colok);
         __syncthreads();
         if (tid < S) finish_delta(a, sm, E);
         __syncthreads();
@@ -207,7 +208,7 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
                 if (colok && ld.y != 0.0f) gk[o] = __builtin_fmaf(ld.x, sm.lgo[c], gk[o]);
             }
         }
-        retrieve<false, NT>(a, sm, old, bk, rs, tok, e, c, cc, colok);
+        retrieve<false, NT>(a, sm, old, bk, rs, snapw + int64_t(t) * a.W * S, e, c, colok);
         __syncthreads();
         if (tid < S) finish_delta(a, sm, E);
         __syncthreads();
@@ -308,8 +309,12 @@ struct ResTok {
 
 // Token tok's values for lane (e, c); every load is issued (indices clamped into range),
 // so the loads never wait on a branch.
+// Token t of the stream whose first token is tok0; snapw: the slice's saved rows [T][W][S].
 template <int KJ, bool kRev>
-__device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_t tok, int e, int E, int cc) {
+__device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_t tok0, int t, const float *snapw,
+                                         int e, int E, int c, int cc) {
+    const int64_t tok = tok0 + t;
+    const float *snapt = snapw + int64_t(t) * a.W * a.S;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
         const int w = min(e + j * E, a.W - 1);
@@ -322,7 +327,7 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
             const float2 ld = a.lead[tok * a.R + r];
             x.ql[j] = ld.x;
             x.qf[j] = ld.y;
-            x.snap[j] = a.snap[(tok * a.W + w) * a.hd + cc];
+            x.snap[j] = snapt[w * a.S + c];
         }
     }
     x.v = a.v[tok * a.hd + cc];
@@ -375,6 +380,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
     const int64_t tok0 = int64_t(p) * a.T;
+    float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
 
     // ret over the column's entry groups, in ascending group order (every lane of the
     // column reads the same partials, so all get the same bits)
@@ -397,7 +403,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
             const int w = e + j * E;
             old[j] = colok ? bk[int64_t(cur.kid[j]) * S] : 0.0f;
             if (w < a.W) {
-                if (colok) a.snap[(tok * a.W + w) * a.hd + cc] = old[j];
+                if (colok) snapw[(int64_t(t) * a.W + w) * S + c] = old[j];
                 acc = __builtin_fmaf(cur.kv[j], cur.gam[j] * old[j], acc);
             }
         }
@@ -490,33 +496,33 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     const int last = n > 0 ? n - 1 : 0;
     const int nfull = n - n % D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) res_load<KJ, false>(a, ring[d], tok0 + min(d, last), e, E, cc);
+    for (int d = 0; d < D; ++d) res_load<KJ, false>(a, ring[d], tok0, min(d, last), snapw, e, E, c, cc);
     for (int t0 = 0; t0 < nfull; t0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             fwd_token(ring[d], t0 + d);
-            res_load<KJ, false>(a, ring[d], tok0 + min(t0 + d + D, last), e, E, cc);
+            res_load<KJ, false>(a, ring[d], tok0, min(t0 + d + D, last), snapw, e, E, c, cc);
         }
     }
     for (int t = nfull; t < n; ++t) {
         ResTok<KJ> x;
-        res_load<KJ, false>(a, x, tok0 + t, e, E, cc);
+        res_load<KJ, false>(a, x, tok0, t, snapw, e, E, c, cc);
         fwd_token(x, t);
     }
     // reverse: the first n % D tokens from the end go one by one, then whole rounds
     for (int t = n - 1; t >= nfull; --t) {
         ResTok<KJ> x;
-        res_load<KJ, true>(a, x, tok0 + t, e, E, cc);
+        res_load<KJ, true>(a, x, tok0, t, snapw, e, E, c, cc);
         rev_token(x, t);
     }
     const int top = nfull - 1;
 #pragma unroll
-    for (int d = 0; d < D; ++d) res_load<KJ, true>(a, ring[d], tok0 + max(top - d, 0), e, E, cc);
+    for (int d = 0; d < D; ++d) res_load<KJ, true>(a, ring[d], tok0, max(top - d, 0), snapw, e, E, c, cc);
     for (int t0 = top; t0 >= 0; t0 -= D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             rev_token(ring[d], t0 - d);
-            res_load<KJ, true>(a, ring[d], tok0 + max(t0 - d - D, 0), e, E, cc);
+            res_load<KJ, true>(a, ring[d], tok0, max(t0 - d - D, 0), snapw, e, E, c, cc);
         }
     }
     __syncthreads();

@@ -268,8 +268,9 @@ int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *
  * from. The call replays the forward on it and walks it back, restoring every written
  * row from a saved copy: on return it holds exactly its contents at entry.
  * exec->workspace: sdm_bwd_workspace_bytes(...) bytes, 256-byte aligned (it keeps each
- * write entry's row as it was before its token, 4 * W * head_dim bytes per token, plus
- * 8 * R bytes per token and one float per token, column slice and dot product).
+ * write entry's row as it was before its token, 4 * W * head_dim bytes per token, rounded
+ * up to whole column slices of 4..64 columns, plus 8 * R bytes per token and one float per
+ * token, column slice and dot product).
  * exec->events: optional, num_events >= SDM_BWD_TIMING_EVENTS hipEvent_t recorded on the
  * stream before the read-slot fold, before the replay-and-reverse sweep, before the
  * reduction of the per-slice dots, and after it. exec->repeated_writes is not used.

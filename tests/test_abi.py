@@ -244,7 +244,7 @@ def test_bwd_workspace_bytes(lib):
     f = lib.sdm_bwd_workspace_bytes
     f.restype = ctypes.c_size_t
     f.argtypes = [ctypes.c_int32] * 5
-    snap, lead, part = 8 * 2048 * 8 * 64 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4
+    snap, lead, part = 8 * 16 * 4 * 2048 * 8 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4
     assert f(8, 2048, 8, 8, 64) == snap + lead + part
     assert f(0, 2048, 8, 8, 64) == 0 and f(8, 2048, 0, 8, 64) == 0 and f(8, 2048, 8, 257, 64) == 0
 
