@@ -233,7 +233,8 @@ def bench_bwd(args):
     t = to_torch(inp, dev)
     go = torch.from_numpy(gr["grad_out"]).to(dev)
     gbank = torch.from_numpy(gr["grad_bank"]).to(dev)
-    ws = torch.empty(bwd_workspace_bytes(wl.P, wl.T, wl.W, wl.R, wl.hd), dtype=torch.uint8, device=dev)
+    ws = torch.empty(bwd_workspace_bytes(wl.P, wl.T, wl.W, wl.R, wl.hd, wl.M, torch.float32), dtype=torch.uint8,
+                     device=dev)
     hip = hip_runtime()
     nev = BWD_TIMING_EVENTS
     ev_sets = []

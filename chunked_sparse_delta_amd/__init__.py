@@ -15,7 +15,7 @@ the readings [P, T, hd] are returned.
 
     grads = sdm_bwd(bank0, k_idx, k_val, v, beta, log_decay, q_idx, q_val, grad_out)
 
-is the backward for a float32 bank: the gradients of sum(grad_out * readings) (plus
+is the backward: the float32 gradients of sum(grad_out * readings) (plus
 sum(grad_bank * final bank) when given) with respect to the bank the forward started
 from and every float input.
 """
@@ -107,7 +107,7 @@ def _load():
             lib.sdm_product_key_topk.restype = ctypes.c_int
             lib.sdm_product_key_topk_backward.argtypes = [i64, p, p, i32, p, i32, i32, p, p]
             lib.sdm_product_key_topk_backward.restype = ctypes.c_int
-            lib.sdm_bwd_workspace_bytes.argtypes = [i32] * 5
+            lib.sdm_bwd_workspace_bytes.argtypes = [i32] * 5 + [i64, i32, i32]
             lib.sdm_bwd_workspace_bytes.restype = ctypes.c_size_t
             lib.sdm_bwd.argtypes = [i32, i32, p, p, p, p, i32, p, p, p, p, p, p]
             lib.sdm_bwd.restype = ctypes.c_int
@@ -268,42 +268,42 @@ class _Grads(ctypes.Structure):
                 ("log_decay", ctypes.c_void_p), ("write", ctypes.c_void_p), ("read", ctypes.c_void_p)]
 
 
-def bwd_workspace_bytes(P: int, T: int, W: int, R: int, hd: int) -> int:
+def bwd_workspace_bytes(P: int, T: int, W: int, R: int, hd: int, M: int, dtype: torch.dtype = torch.float32,
+                        shared_bank: bool = False) -> int:
     """Workspace bytes sdm_bwd needs (0 for rejected shapes)."""
-    return int(_load().sdm_bwd_workspace_bytes(P, T, W, R, hd))
+    return int(_load().sdm_bwd_workspace_bytes(P, T, W, R, hd, M, _DTYPES.get(dtype, -1), 1 if shared_bank else 0))
 
 
 def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
             log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, grad_out: torch.Tensor, *,
             grad_bank: torch.Tensor | None = None, valid_tokens: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None, stream=None, events=None) -> dict:
-    """Backward of sdm_fwd for float32 banks, one per stream. ``bank`` [P, M, hd] holds the
-    bank the forward STARTED from; the call replays the forward on it and restores it
-    exactly. ``grad_out`` [P, T, hd] is the gradient of the readings; ``grad_bank`` (float32
-    [P, M, hd], optional) that of the final bank, and it is overwritten in place with the
-    gradient with respect to the initial bank (a zero tensor is allocated if omitted).
-    ``events``: optional ctypes array of BWD_TIMING_EVENTS hipEvent_t recorded at the kernel
-    boundaries. Returns dict(bank, v, beta, log_decay, k_val, q_val) of float32 gradients."""
+            workspace: torch.Tensor | None = None, stream=None, events=None, shared_bank: bool = False) -> dict:
+    """Backward of sdm_fwd. ``bank`` (float32 or bfloat16; [P, M, hd], or a shared [M, hd]
+    with ``shared_bank=True``) holds the bank the forward STARTED from; a float32 bank is
+    replayed and restored exactly, a bfloat16 one only read. ``grad_out`` [P, T, hd] (bank
+    dtype) is the gradient of the readings; ``grad_bank`` (float32, the bank's shape,
+    optional) that of the final bank, overwritten in place with the gradient with respect
+    to the initial bank (a zero tensor is allocated if omitted). ``events``: optional ctypes
+    array of BWD_TIMING_EVENTS hipEvent_t recorded at the kernel boundaries. Returns
+    dict(bank, v, beta, log_decay, k_val, q_val) of float32 gradients."""
     lib = _load()
-    if bank.dtype != torch.float32 or bank.dim() != 3:
-        raise TypeError("sdm_bwd takes a float32 bank of one [M, hd] bank per stream")
     P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
-                                                   valid_tokens)
+                                                   valid_tokens, shared_bank)
     dev = bank.device
-    _expect(grad_out, "grad_out", (P, T, hd), torch.float32, dev)
+    _expect(grad_out, "grad_out", (P, T, hd), bank.dtype, dev)
     if grad_bank is None:
-        grad_bank = torch.zeros_like(bank)
+        grad_bank = torch.zeros(bank.shape, dtype=torch.float32, device=dev)
     else:
-        _expect(grad_bank, "grad_bank", (P, M, hd), torch.float32, dev)
+        _expect(grad_bank, "grad_bank", tuple(bank.shape), torch.float32, dev)
     out = dict(bank=grad_bank, v=torch.empty((P, T, hd), dtype=torch.float32, device=dev),
                beta=torch.empty((P, T), dtype=torch.float32, device=dev),
                log_decay=torch.empty((P, T, G), dtype=torch.float32, device=dev),
                k_val=torch.empty((P, T, W), dtype=torch.float32, device=dev),
                q_val=torch.empty((P, T, R), dtype=torch.float32, device=dev))
     if workspace is None:
-        workspace = _workspace(bwd_workspace_bytes(P, T, W, R, hd), dev)
+        workspace = _workspace(bwd_workspace_bytes(P, T, W, R, hd, M, bank.dtype, bank.dim() == 2), dev)
     gr = _Grads(*(out[k].data_ptr() for k in ("bank", "v", "beta", "log_decay", "k_val", "q_val")))
-    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 0)
+    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 1 if bank.dim() == 2 else 0)
     ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events),
                None)

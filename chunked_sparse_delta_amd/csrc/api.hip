@@ -508,40 +508,44 @@ int sdm_wy_solve(int64_t n, int32_t C, const float *A, const float *beta, const 
 namespace {
 
 struct BwdSizes {
-    size_t snap, lead, part, total;
+    size_t snap, lead, part, work, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd) {
+BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64_t M, int32_t dtype, bool shared) {
     const int S = sdm::bwd_slice_cols(P, hd);
     const int64_t NS = (hd + S - 1) / S;
     BwdSizes z{};
     z.snap = align256(size_t(P) * size_t(NS) * size_t(S) * size_t(T) * size_t(W) * 4);
     z.lead = align256(size_t(P) * size_t(T) * size_t(R) * 8);
     z.part = align256(size_t(P) * size_t(NS) * size_t(T) * size_t(sdm::bwd_parts(W, R)) * 4);
-    z.total = z.snap + z.lead + z.part;
+    z.work = dtype == SDM_BF16 ? align256(size_t(shared ? 1 : P) * size_t(M) * size_t(hd) * 4) : 0;
+    z.total = z.snap + z.lead + z.part + z.work;
     return z;
 }
 
 }  // namespace
 
-size_t sdm_bwd_workspace_bytes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd) {
-    if (check_shape(P, T, 16, W, R, hd) != SDM_OK) return 0;
-    return bwd_sizes(P, T, W, R, hd).total;
+size_t sdm_bwd_workspace_bytes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64_t rows, int32_t dtype,
+                               int32_t shared) {
+    if (check_shape(P, T, 16, W, R, hd) != SDM_OK || rows < 1 || (dtype != SDM_F32 && dtype != SDM_BF16) ||
+        (shared != 0 && shared != 1))
+        return 0;
+    return bwd_sizes(P, T, W, R, hd, rows, dtype, shared == 1).total;
 }
 
 int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
-            const float *log_decay, int32_t gate_width, const float *v, const sdm_bank *bank, const int32_t *valid_tokens,
-            const float *grad_out, const sdm_grads *grads, const sdm_exec *exec) {
+            const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank, const int32_t *valid_tokens,
+            const void *grad_out, const sdm_grads *grads, const sdm_exec *exec) {
     g_err[0] = 0;
     if (!bank || !exec || !grads) return fail(SDM_ERR_NULL, "bank, grads and exec must not be NULL");
-    if (bank->dtype != SDM_F32) return fail(SDM_ERR_DTYPE, "the backward takes a float32 bank, got dtype %d", bank->dtype);
-    if (bank->shared != 0) return fail(SDM_ERR_UNSUPPORTED, "the backward takes one bank per stream (shared = 0)");
+    if (bank->shared != 0 && bank->shared != 1) return fail(SDM_ERR_SHAPE, "bank.shared must be 0 or 1, got %d", bank->shared);
+    const bool shared = bank->shared == 1;
     Checked ck;
     // chunk 16 only bounds the token count here: the backward has no chunks
     int rc = check_call(P, T, 16, slots, weights, beta, log_decay, gate_width, v, bank->rows, bank->head_dim,
-                        bank->dtype, bank->data, false, valid_tokens, const_cast<float *>(grad_out), true, &ck);
+                        bank->dtype, bank->data, shared, valid_tokens, const_cast<void *>(grad_out), true, &ck);
     if (rc) return rc;
     if (!grads->bank || !grads->v || !grads->beta || !grads->log_decay || !grads->write || !grads->read)
         return fail(SDM_ERR_NULL, "every gradient array must be given");
@@ -549,11 +553,11 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     for (const void *q : g4)
         if (!aligned(q, 4)) return fail(SDM_ERR_ALIGN, "gradient arrays must be 4-byte aligned");
     const int W = slots->W, R = slots->R, hd = bank->head_dim;
-    const int64_t M = bank->rows;
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank->data), b1 = b0 + uintptr_t(P) * M * hd * 4;
-    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grads->bank), g1 = g0 + uintptr_t(P) * M * hd * 4;
+    const int64_t M = bank->rows, banks = shared ? 1 : P;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank->data), b1 = b0 + uintptr_t(banks) * M * hd * ck.es;
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(grads->bank), g1 = g0 + uintptr_t(banks) * M * hd * 4;
     if (g0 < b1 && b0 < g1) return fail(SDM_ERR_SHAPE, "the bank gradient overlaps the bank");
-    const BwdSizes z = bwd_sizes(P, T, W, R, hd);
+    const BwdSizes z = bwd_sizes(P, T, W, R, hd, M, bank->dtype, shared);
     if (!exec->workspace || exec->workspace_bytes < z.total)
         return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes the backward needs",
                     exec->workspace ? exec->workspace_bytes : size_t(0), z.total);
@@ -562,29 +566,34 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     if ((rc = device_info(&dev)) != SDM_OK) return rc;
     sdm::BwdArgs a{};
     a.P = P; a.T = T; a.W = W; a.R = R; a.G = gate_width; a.hd = hd; a.M = M;
+    a.bf16 = bank->dtype == SDM_BF16;
+    a.bstride = shared ? 0 : M * hd;
     a.S = sdm::bwd_slice_cols(P, hd);
     a.NS = (hd + a.S - 1) / a.S;
     // one wavefront per slice with the slices of the bank and of its gradient in LDS when they fit
     // and a lane covers its entries in at most 4 (SDM_BWD_RES=0 turns it off)
     const char *res_env = getenv("SDM_BWD_RES");
     const size_t res_lds = sdm::bwd_lds_bytes(W, a.S, M, true);
-    const bool res_ok = (!res_env || atoi(res_env) != 0) && res_lds <= size_t(dev->lds_per_block) &&
+    // (never for a shared bank: a workgroup writes its whole gradient slice back at the end,
+    // which would overwrite the rows of the other streams)
+    const bool res_ok = !shared && (!res_env || atoi(res_env) != 0) && res_lds <= size_t(dev->lds_per_block) &&
                         res_lds <= size_t(sdm::kBwdMaxLds);
     a.res = res_ok ? sdm::bwd_res_entries(W, R, a.S) : 0;
     if (!a.res && sdm::bwd_lds_bytes(W, a.S, M, false) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "the backward needs %zu bytes of LDS per workgroup, the device has %d",
                     sdm::bwd_lds_bytes(W, a.S, M, false), dev->lds_per_block);
     a.k_idx = ck.pb.k_idx; a.q_idx = ck.pb.q_idx; a.k_id8 = ck.pb.k_id8; a.q_id8 = ck.pb.q_id8;
-    a.k_val = static_cast<const float *>(weights->write);
-    a.q_val = static_cast<const float *>(weights->read);
+    a.k_val = weights->write;
+    a.q_val = weights->read;
     a.beta = beta; a.g = log_decay; a.v = v; a.go = grad_out; a.valid = valid_tokens;
-    a.bank = static_cast<float *>(bank->data);
+    a.bank = bank->data;
     a.gbank = grads->bank; a.gv = grads->v; a.gk = grads->write; a.gq = grads->read;
     a.gbeta = grads->beta; a.gg = grads->log_decay;
     unsigned char *ws = static_cast<unsigned char *>(exec->workspace);
     a.snap = reinterpret_cast<float *>(ws);
     a.lead = reinterpret_cast<float2 *>(ws + z.snap);
     a.part = reinterpret_cast<float *>(ws + z.snap + z.lead);
+    a.work = a.bf16 ? reinterpret_cast<float *>(ws + z.snap + z.lead + z.part) : static_cast<float *>(bank->data);
     hipEvent_t *ev = nullptr;
     if (exec->events && exec->num_events >= SDM_BWD_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
     const hipError_t e = sdm::launch_bwd(a, static_cast<hipStream_t>(exec->stream), ev);

@@ -12,13 +12,18 @@ struct BwdArgs {
     int32_t P, T, W, R, G, hd, S, NS;   // S columns per slice (power of two, 4..64), NS slices
     int32_t res;                        // 0: rows in memory; 1, 2, 4: the resident sweep with that
                                         // many entries of each kind per lane
+    int32_t bf16;                       // 1: bank, weights, v and grad_out are bfloat16, else float32
     int64_t M;
+    int64_t bstride;                    // elements from one stream's bank to the next (M * hd, or 0 shared)
     const void *k_idx, *q_idx;
     int32_t k_id8, q_id8;
-    const float *k_val, *q_val, *beta, *g, *v, *go;
+    const void *k_val, *q_val, *v, *go;   // in the bank dtype
+    const float *beta, *g;
     const int32_t *valid;
-    float *bank;     // [P, M, hd], replayed and restored
-    float *gbank;    // [P, M, hd], in: gradient of the final bank; out: of the initial bank
+    const void *bank;  // the bank the forward started from (never written)
+    float *work;     // float32 rows the sweep in memory replays and restores: the bank itself
+                     // (float32) or a copy of it in the workspace (bfloat16)
+    float *gbank;    // [P, M, hd] (or [M, hd] shared), in: gradient of the final bank; out: of the initial bank
     float *gv;       // [P, T, hd]
     float *gk, *gq, *gbeta, *gg;   // [P, T, W], [P, T, R], [P, T], [P, T, G]
     float *snap;     // [P, NS, T, W, S]  old_w of every live write entry, slice by slice

@@ -28,6 +28,8 @@
 // Every sum runs in a fixed order: the results are bitwise reproducible.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "backward.h"
 
 namespace sdm {
@@ -35,6 +37,12 @@ namespace sdm {
 __device__ __forceinline__ int32_t live_tokens(const BwdArgs &a, int p) {
     int32_t n = a.valid ? a.valid[p] : a.T;
     return n < 0 ? 0 : (n > a.T ? a.T : n);
+}
+
+// Element i of an array in the bank dtype T, widened to float32.
+template <typename T>
+__device__ __forceinline__ float ldf(const void *p, int64_t i) {
+    return to_f32(static_cast<const T *>(p)[i]);
 }
 
 __device__ __forceinline__ int32_t clamp_row(int32_t s, int64_t M) {
@@ -49,6 +57,7 @@ __device__ __forceinline__ float group_sum(float x, int S) {
 
 // One workgroup per token: fold its read slots (first occurrence carries the sum of the
 // weights of every entry with that slot, in entry order).
+template <typename T>
 __global__ void __launch_bounds__(kBwdBlock) bwd_lead_kernel(BwdArgs a) {
     __shared__ int32_t ids[kMaxWidth];
     const int64_t tok = blockIdx.x;
@@ -65,7 +74,7 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_lead_kernel(BwdArgs a) {
         if (first) {
             float q = 0.0f;
             for (int j = r; j < a.R; ++j)
-                if (ids[j] == s) q += a.q_val[tok * a.R + j];
+                if (ids[j] == s) q += ldf<T>(a.q_val, tok * a.R + j);
             out = make_float2(q, 1.0f);
         }
     }
@@ -89,14 +98,14 @@ size_t bwd_lds_bytes(int W, int S, int64_t M, bool res) {
 
 // Lanes are (entry e, column c): c = tid % S, entries e, e + E, ... with E = 256 / S.
 // Loads of the token's parameters into LDS (the caller synchronizes afterwards).
-template <int NT>
+template <int NT, typename T>
 __device__ __forceinline__ void load_token(const BwdArgs &a, BwdSmem &sm, int64_t tok, int col, bool colok,
                                            bool reads) {
     const int tid = threadIdx.x;
     for (int w = tid; w < a.W; w += NT) {
         const int32_t s = clamp_row(load_id(a.k_idx, tok * a.W + w, a.k_id8), a.M);
         sm.kid[w] = s;
-        sm.kv[w] = a.k_val[tok * a.W + w];
+        sm.kv[w] = ldf<T>(a.k_val, tok * a.W + w);
         sm.gam[w] = __expf(a.g[tok * a.G + (a.G == 1 ? 0 : w)]);
     }
     if (reads)
@@ -106,8 +115,8 @@ __device__ __forceinline__ void load_token(const BwdArgs &a, BwdSmem &sm, int64_
         }
     if (tid < a.S) {
         const int64_t o = tok * a.hd + (colok ? col : 0);
-        sm.lv[tid] = colok ? a.v[o] : 0.0f;
-        if (reads) sm.lgo[tid] = colok ? a.go[o] : 0.0f;
+        sm.lv[tid] = colok ? ldf<T>(a.v, o) : 0.0f;
+        if (reads) sm.lgo[tid] = colok ? ldf<T>(a.go, o) : 0.0f;
     }
     if (tid == 0) sm.beta = a.beta[tok];
 }
@@ -153,7 +162,7 @@ __device__ __forceinline__ void finish_delta(const BwdArgs &a, BwdSmem &sm, int 
 
 // The sweep in memory: NT threads per (stream, column slice), rows read and written in the
 // bank and the bank gradient themselves, token values staged through LDS.
-template <int NT>
+template <int NT, typename T>
 __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     BwdSmem &sm = *reinterpret_cast<BwdSmem *>(smem_raw);
@@ -165,8 +174,8 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     const int col = sl * S + c;
     const bool colok = col < a.hd;
     const int cc = colok ? col : 0;
-    float *bk = a.bank + int64_t(p) * a.M * a.hd + cc;
-    float *gk = a.gbank + int64_t(p) * a.M * a.hd + cc;
+    float *bk = a.work + int64_t(p) * a.bstride + cc;
+    float *gk = a.gbank + int64_t(p) * a.bstride + cc;
     const int64_t rs = a.hd;
     float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
     const int J = bwd_parts(a.W, a.R);
@@ -175,7 +184,7 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     // forward replay
     for (int t = 0; t < n; ++t) {
         const int64_t tok = int64_t(p) * a.T + t;
-        load_token<NT>(a, sm, tok, col, colok, false);
+        load_token<NT, T>(a, sm, tok, col, colok, false);
         __syncthreads();
         retrieve<true, NT>(a, sm, old, bk, rs, snapw + int64_t(t) * a.W * S, e, c, colok);
         __syncthreads();
@@ -193,7 +202,7 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     for (int t = n - 1; t >= 0; --t) {
         const int64_t tok = int64_t(p) * a.T + t;
         float *pt = a.part + ((int64_t(p) * a.NS + sl) * a.T + t) * J;
-        load_token<NT>(a, sm, tok, col, colok, true);
+        load_token<NT, T>(a, sm, tok, col, colok, true);
         __syncthreads();
         // reading: grad_q_r = <go, bank[s_r]> (bank after the token); gb[s_r] += q_r go
         for (int r0 = 0; r0 < a.R; r0 += E) {
@@ -310,7 +319,7 @@ struct ResTok {
 // Token tok's values for lane (e, c); every load is issued (indices clamped into range),
 // so the loads never wait on a branch.
 // Token t of the stream whose first token is tok0; snapw: the slice's saved rows [T][W][S].
-template <int KJ, bool kRev>
+template <int KJ, bool kRev, typename T>
 __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_t tok0, int t, const float *snapw,
                                          int e, int E, int c, int cc) {
     const int64_t tok = tok0 + t;
@@ -319,7 +328,7 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
     for (int j = 0; j < KJ; ++j) {
         const int w = min(e + j * E, a.W - 1);
         x.kid[j] = clamp_row(id_word(a.k_idx, tok * a.W + w, a.k_id8), a.M);
-        x.kv[j] = a.k_val[tok * a.W + w];
+        x.kv[j] = ldf<T>(a.k_val, tok * a.W + w);
         x.gam[j] = __expf(a.g[tok * a.G + (a.G == 1 ? 0 : w)]);
         if (kRev) {
             const int r = min(e + j * E, a.R - 1);
@@ -330,12 +339,12 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
             x.snap[j] = snapt[w * a.S + c];
         }
     }
-    x.v = a.v[tok * a.hd + cc];
-    if (kRev) x.go = a.go[tok * a.hd + cc];
+    x.v = ldf<T>(a.v, tok * a.hd + cc);
+    if (kRev) x.go = ldf<T>(a.go, tok * a.hd + cc);
     x.beta = a.beta[tok];
 }
 
-template <int KJ, int D>
+template <int KJ, int D, typename T>
 __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
@@ -347,8 +356,8 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     const bool colok = col < a.hd;
     const int cc = colok ? col : 0;
     const int ne = a.W < E ? a.W : E;   // entry groups holding a write entry
-    float *bank_g = a.bank + int64_t(p) * a.M * a.hd;
-    float *gb_g = a.gbank + int64_t(p) * a.M * a.hd;
+    const T *bank_g = static_cast<const T *>(a.bank) + int64_t(p) * a.bstride;
+    float *gb_g = a.gbank + int64_t(p) * a.bstride;
     const int64_t MS = a.M * S;
     {
         constexpr int kB = 16;
@@ -360,7 +369,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
                 const int cg = sl * S + int(i % S);
                 const bool ok = i < MS && cg < a.hd;
                 const int64_t o = ok ? (i / S) * a.hd + cg : 0;
-                xb[k] = bank_g[o];
+                xb[k] = to_f32(bank_g[o]);
                 xg[k] = gb_g[o];
                 xb[k] = ok ? xb[k] : 0.0f;
                 xg[k] = ok ? xg[k] : 0.0f;
@@ -496,33 +505,33 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     const int last = n > 0 ? n - 1 : 0;
     const int nfull = n - n % D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) res_load<KJ, false>(a, ring[d], tok0, min(d, last), snapw, e, E, c, cc);
+    for (int d = 0; d < D; ++d) res_load<KJ, false, T>(a, ring[d], tok0, min(d, last), snapw, e, E, c, cc);
     for (int t0 = 0; t0 < nfull; t0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             fwd_token(ring[d], t0 + d);
-            res_load<KJ, false>(a, ring[d], tok0, min(t0 + d + D, last), snapw, e, E, c, cc);
+            res_load<KJ, false, T>(a, ring[d], tok0, min(t0 + d + D, last), snapw, e, E, c, cc);
         }
     }
     for (int t = nfull; t < n; ++t) {
         ResTok<KJ> x;
-        res_load<KJ, false>(a, x, tok0, t, snapw, e, E, c, cc);
+        res_load<KJ, false, T>(a, x, tok0, t, snapw, e, E, c, cc);
         fwd_token(x, t);
     }
     // reverse: the first n % D tokens from the end go one by one, then whole rounds
     for (int t = n - 1; t >= nfull; --t) {
         ResTok<KJ> x;
-        res_load<KJ, true>(a, x, tok0, t, snapw, e, E, c, cc);
+        res_load<KJ, true, T>(a, x, tok0, t, snapw, e, E, c, cc);
         rev_token(x, t);
     }
     const int top = nfull - 1;
 #pragma unroll
-    for (int d = 0; d < D; ++d) res_load<KJ, true>(a, ring[d], tok0, max(top - d, 0), snapw, e, E, c, cc);
+    for (int d = 0; d < D; ++d) res_load<KJ, true, T>(a, ring[d], tok0, max(top - d, 0), snapw, e, E, c, cc);
     for (int t0 = top; t0 >= 0; t0 -= D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             rev_token(ring[d], t0 - d);
-            res_load<KJ, true>(a, ring[d], tok0, max(t0 - d - D, 0), snapw, e, E, c, cc);
+            res_load<KJ, true, T>(a, ring[d], tok0, max(t0 - d - D, 0), snapw, e, E, c, cc);
         }
     }
     __syncthreads();
@@ -567,16 +576,28 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_reduce_kernel(BwdArgs a) {
     }
 }
 
-hipError_t bwd_prepare() {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_sweep_kernel<kBwdBlock>),
+// The float32 working rows of a bfloat16 bank for the sweep in memory.
+__global__ void __launch_bounds__(kBwdBlock) bwd_widen_kernel(const bf16 *bank, float *work, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * kBwdBlock + threadIdx.x; i < n; i += int64_t(gridDim.x) * kBwdBlock)
+        work[i] = to_f32(bank[i]);
+}
+
+template <typename T>
+hipError_t set_bwd_attrs() {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_sweep_kernel<kBwdBlock, T>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(bwd_lds_bytes(kMaxWidth, kWave, 0, false)));
-    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1, 4>),
-                         reinterpret_cast<const void *>(bwd_res_kernel<2, 2>),
-                         reinterpret_cast<const void *>(bwd_res_kernel<4, 1>)};
+    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1, 4, T>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<2, 2, T>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<4, 1, T>)};
     for (const void *f : res)
         if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdMaxLds);
     return e;
+}
+
+hipError_t bwd_prepare() {
+    hipError_t e = set_bwd_attrs<float>();
+    return e == hipSuccess ? set_bwd_attrs<bf16>() : e;
 }
 
 // Entries of each kind per lane of the resident sweep: the smallest of 1, 2, 4 that covers
@@ -602,20 +623,28 @@ int bwd_slice_cols(int P, int hd) {
     return S;
 }
 
-hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
+template <typename T>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
     const int64_t toks = int64_t(a.P) * a.T;
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-    bwd_lead_kernel<<<dim3(unsigned(toks)), dim3(kBwdBlock), 0, st>>>(a);
+    bwd_lead_kernel<T><<<dim3(unsigned(toks)), dim3(kBwdBlock), 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (std::is_same<T, bf16>::value && !a.res) {
+        const int64_t n = (a.bstride ? int64_t(a.P) : 1) * a.M * a.hd;
+        const int64_t blocks = (n + kBwdBlock - 1) / kBwdBlock;
+        bwd_widen_kernel<<<dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(kBwdBlock), 0, st>>>(
+            static_cast<const bf16 *>(a.bank), a.work, n);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     const dim3 grid(unsigned(a.P * a.NS));
     const size_t lds = bwd_lds_bytes(a.W, a.S, a.M, a.res != 0);
     switch (a.res) {
-        case 1: bwd_res_kernel<1, 4><<<grid, dim3(kWave), lds, st>>>(a); break;
-        case 2: bwd_res_kernel<2, 2><<<grid, dim3(kWave), lds, st>>>(a); break;
-        case 4: bwd_res_kernel<4, 1><<<grid, dim3(kWave), lds, st>>>(a); break;
-        default: bwd_sweep_kernel<kBwdBlock><<<grid, dim3(kBwdBlock), lds, st>>>(a); break;
+        case 1: bwd_res_kernel<1, 4, T><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 2: bwd_res_kernel<2, 2, T><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 4: bwd_res_kernel<4, 1, T><<<grid, dim3(kWave), lds, st>>>(a); break;
+        default: bwd_sweep_kernel<kBwdBlock, T><<<grid, dim3(kBwdBlock), lds, st>>>(a); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
@@ -623,6 +652,10 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
     return hipSuccess;
+}
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
+    return a.bf16 ? launch_bwd_t<bf16>(a, st, ev) : launch_bwd_t<float>(a, st, ev);
 }
 
 }  // namespace sdm

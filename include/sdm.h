@@ -247,36 +247,38 @@ int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *
                                   const sdm_exec *exec);
 
 /*
- * The backward of sdm_fwd for a float32 bank (sdm_write_read is differentiable in the
- * slot weights, v, beta, the log-decays and the bank: SDMWriteRead, page 21,
- * memory_ops.py; the pages name their backward's stages without listing them, so this is
- * the derivative of the per-token loop that defines the forward). For the objective
+ * The backward of sdm_fwd (sdm_write_read is differentiable in the slot weights, v, beta,
+ * the log-decays and the bank: SDMWriteRead, page 21, memory_ops.py; the pages name their
+ * backward's stages without listing them, so this is the derivative of the per-token loop
+ * that defines the forward, evaluated in float32). For the objective
  *     J = sum(grad_out * readings) + sum(grad_bank_final * final bank)
  * it returns dJ/d(each float input) at the given inputs:
- *   grads->bank       [P, rows, head_dim]  in: grad_bank_final (zeros for none);
- *                                          out: the gradient w.r.t. the bank the forward
- *                                          started from
+ *   grads->bank       [P, rows, head_dim] ([rows, head_dim] for a shared bank)
+ *                     in: grad_bank_final (zeros for none);
+ *                     out: the gradient w.r.t. the bank the forward started from
  *   grads->v          [P, T, head_dim]
  *   grads->beta       [P, T]
  *   grads->log_decay  [P, T, gate_width]
  *   grads->write      [P, T, W]   (write slot weights)
  *   grads->read       [P, T, R]   (read slot weights)
- * All device float32, every element written (padding tokens: zeros); none may overlap an
- * input. slots, weights (float32), beta, log_decay, gate_width, v (float32), valid_tokens:
- * exactly as given to sdm_fwd. grad_out: device float32 [P, T, head_dim].
- * bank: float32, one bank per stream (shared = 0), holding the bank the forward STARTED
- * from. The call replays the forward on it and walks it back, restoring every written
- * row from a saved copy: on return it holds exactly its contents at entry.
+ * All device float32 whatever the bank dtype, every element written (padding tokens:
+ * zeros); none may overlap an input. slots, weights, beta, log_decay, gate_width, v,
+ * valid_tokens: exactly as given to sdm_fwd (weights and v in the bank dtype).
+ * grad_out: device [P, T, head_dim] in the bank dtype.
+ * bank: as for sdm_fwd (float32 or bfloat16; per stream, or shared with the streams' slot
+ * sets disjoint), holding the bank the forward STARTED from. The call replays the forward
+ * on it in float32 and walks it back, restoring every written row from a saved copy: a
+ * float32 bank is used as the working state and holds exactly its entry contents again on
+ * return; a bfloat16 bank is only read (its rows are widened into float32 working rows).
  * exec->workspace: sdm_bwd_workspace_bytes(...) bytes, 256-byte aligned (it keeps each
  * write entry's row as it was before its token, 4 * W * head_dim bytes per token, rounded
- * up to whole column slices of 4..64 columns, plus 8 * R bytes per token and one float per
- * token, column slice and dot product).
+ * up to whole column slices of 4..64 columns, plus 8 * R bytes per token, one float per
+ * token, column slice and dot product, and for a bfloat16 bank the float32 working rows,
+ * 4 * head_dim bytes per bank row).
  * exec->events: optional, num_events >= SDM_BWD_TIMING_EVENTS hipEvent_t recorded on the
  * stream before the read-slot fold, before the replay-and-reverse sweep, before the
  * reduction of the per-slice dots, and after it. exec->repeated_writes is not used.
- * Arithmetic float32, sums in a fixed order: results are bitwise reproducible.
- * Errors as for sdm_fwd; SDM_ERR_DTYPE for a bfloat16 bank, SDM_ERR_UNSUPPORTED for a
- * shared bank (neither has a backward here).
+ * Sums run in a fixed order: results are bitwise reproducible. Errors as for sdm_fwd.
  */
 #define SDM_BWD_TIMING_EVENTS 4
 
@@ -289,13 +291,15 @@ typedef struct {
     float *read;
 } sdm_grads;
 
-/* Workspace bytes sdm_bwd needs (0 for shapes sdm_bwd rejects with SDM_ERR_SHAPE or
- * SDM_ERR_RANGE). */
-size_t sdm_bwd_workspace_bytes(int32_t streams, int32_t tokens, int32_t W, int32_t R, int32_t head_dim);
+/* Workspace bytes sdm_bwd needs for these shapes, bank rows (per stream, or of the shared
+ * bank), bank dtype and sharing (0 for arguments sdm_bwd rejects with SDM_ERR_SHAPE,
+ * SDM_ERR_RANGE or SDM_ERR_DTYPE). */
+size_t sdm_bwd_workspace_bytes(int32_t streams, int32_t tokens, int32_t W, int32_t R, int32_t head_dim,
+                               int64_t rows, int32_t dtype, int32_t shared);
 
 int sdm_bwd(int32_t streams, int32_t tokens, const sdm_slots *slots, const sdm_weights *weights,
-            const float *beta, const float *log_decay, int32_t gate_width, const float *v,
-            const sdm_bank *bank, const int32_t *valid_tokens, const float *grad_out,
+            const float *beta, const float *log_decay, int32_t gate_width, const void *v,
+            const sdm_bank *bank, const int32_t *valid_tokens, const void *grad_out,
             const sdm_grads *grads, const sdm_exec *exec);
 
 /* Static text for an SDM_* code. */

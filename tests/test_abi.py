@@ -238,15 +238,20 @@ def test_topk_backward_rejects_before_any_launch(lib):
 
 
 def test_bwd_workspace_bytes(lib):
-    """Saved rows (4 * W * hd bytes per token), folded read slots (8 * R per token) and the
-    per-slice dots (4 * (2W + R + 1) per token and column slice), each 256-byte aligned.
-    Config 1's shapes take 4-column slices (8 streams x 16 slices = 128 workgroups)."""
+    """Saved rows (4 * W * hd bytes per token), folded read slots (8 * R per token), the
+    per-slice dots (4 * (2W + R + 1) per token and column slice), each 256-byte aligned, and
+    for a bfloat16 bank its float32 working rows. Config 1's shapes take 4-column slices
+    (8 streams x 16 slices = 128 workgroups)."""
     f = lib.sdm_bwd_workspace_bytes
     f.restype = ctypes.c_size_t
-    f.argtypes = [ctypes.c_int32] * 5
+    f.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
     snap, lead, part = 8 * 16 * 4 * 2048 * 8 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4
-    assert f(8, 2048, 8, 8, 64) == snap + lead + part
-    assert f(0, 2048, 8, 8, 64) == 0 and f(8, 2048, 0, 8, 64) == 0 and f(8, 2048, 8, 257, 64) == 0
+    assert f(8, 2048, 8, 8, 64, 4096, 0, 0) == snap + lead + part
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 0) == snap + lead + part + 8 * 4096 * 64 * 4
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 1) == snap + lead + part + 4096 * 64 * 4
+    assert f(0, 2048, 8, 8, 64, 4096, 0, 0) == 0 and f(8, 2048, 0, 8, 64, 4096, 0, 0) == 0
+    assert f(8, 2048, 8, 257, 64, 4096, 0, 0) == 0 and f(8, 2048, 8, 8, 64, 0, 0, 0) == 0
+    assert f(8, 2048, 8, 8, 64, 4096, 2, 0) == 0 and f(8, 2048, 8, 8, 64, 4096, 0, 2) == 0
 
 
 def test_bwd_rejects_before_any_work(lib):
@@ -255,26 +260,26 @@ def test_bwd_rejects_before_any_work(lib):
     f = lib.sdm_bwd
     f.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 6
     lib.sdm_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.sdm_bwd_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+    lib.sdm_bwd_workspace_bytes.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
     fake = Call.FAKE
     P, T, W, R, hd, M = 2, 100, 4, 3, 64, 50
-    need = lib.sdm_bwd_workspace_bytes(P, T, W, R, hd)
     ptr = {k: fake + (i << 32) for i, k in enumerate(["kidx", "qidx", "kval", "qval", "beta", "g", "v", "bank", "go",
                                                       "ws", "gbank", "gv", "gbeta", "gg", "gk", "gq"])}
 
-    def call(dtype=0, shared=0, ws=need, gbank=None, gv=None, G=W, kb=4):
+    def call(dtype=0, shared=0, ws=None, gbank=None, gv=None, G=W, kb=4, go=None):
+        need = lib.sdm_bwd_workspace_bytes(P, T, W, R, hd, M, dtype if dtype in (0, 1) else 0, shared & 1)
         slots = _Slots(ptr["kidx"], ptr["qidx"], W, R, kb, 4)
         weights = _Weights(ptr["kval"], ptr["qval"])
         bank = _Bank(ptr["bank"], M, hd, dtype, shared)
         grads = _Grads(ptr["gbank"] if gbank is None else gbank, ptr["gv"] if gv is None else gv, ptr["gbeta"],
                        ptr["gg"], ptr["gk"], ptr["gq"])
-        ex = _Exec(None, ptr["ws"], ws, None, 0, None)
+        ex = _Exec(None, ptr["ws"], need if ws is None else ws(need), None, 0, None)
         return f(P, T, ctypes.byref(slots), ctypes.byref(weights), ptr["beta"], ptr["g"], G, ptr["v"],
-                 ctypes.byref(bank), None, ptr["go"], ctypes.byref(grads), ctypes.byref(ex))
+                 ctypes.byref(bank), None, ptr["go"] if go is None else go, ctypes.byref(grads), ctypes.byref(ex))
 
-    assert call(dtype=1) == DTYPE and b"float32" in lib.sdm_last_error()
-    assert call(shared=1) == UNSUPPORTED
-    assert call(ws=need - 1) == WORKSPACE
+    assert call(dtype=2) == DTYPE and call(shared=2) == SHAPE
+    assert call(ws=lambda n: n - 1) == WORKSPACE and call(dtype=1, ws=lambda n: n - 256) == WORKSPACE
     assert call(gv=0) == NULL and call(gv=ptr["gv"] + 2) == ALIGN
-    assert call(gbank=ptr["bank"] + 64) == SHAPE
+    assert call(gbank=ptr["bank"] + 64) == SHAPE and call(go=ptr["bank"] + 64) == SHAPE
+    assert call(dtype=1, go=ptr["go"] + 1) == ALIGN
     assert call(G=2) == SHAPE and call(kb=3) == DTYPE

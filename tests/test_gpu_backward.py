@@ -20,6 +20,15 @@ TOL = 1e-4
 NAMES = {"bank": "bank", "v": "v", "beta": "beta", "log_decay": "g", "k_val": "k_val", "q_val": "q_val"}
 
 
+def _grad_out(gr, dtype, gpu):
+    """grad_out in the bank dtype on the GPU; gr["grad_out"] becomes its exact float32 value."""
+    if dtype == "bf16":
+        bits = workloads.round_bf16_bits(gr["grad_out"])
+        gr["grad_out"] = workloads.bf16_bits_to_f32(bits)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(gpu)
+    return torch.from_numpy(gr["grad_out"]).to(gpu)
+
+
 def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False):
     inp = gu.generate(wl)
     if dup_reads and wl.R > 1:
@@ -32,7 +41,7 @@ def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False):
     bank = t["bank"].clone()
     gb = None if gr["grad_bank"] is None else torch.from_numpy(gr["grad_bank"]).to(gpu)
     got = sdm_bwd(bank, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
-                  torch.from_numpy(gr["grad_out"]).to(gpu), grad_bank=gb, valid_tokens=t["valid"])
+                  _grad_out(gr, wl.dtype, gpu), grad_bank=gb, valid_tokens=t["valid"])
     torch.cuda.synchronize()
     return inp, gr, t, bank, got
 
@@ -63,6 +72,8 @@ CASES = [
     small(P=2, T=25, C=16, hd=64, M=512, W=256, R=256, index=16),                      # widest entries
     small(P=2, T=40, C=16, hd=12, M=300, W=20, R=30, ragged=True, index=20),           # 2 entries per lane
     small(P=1, T=30, C=16, hd=20, M=400, W=50, R=64, index=21),                        # 4 entries per lane
+    small(P=2, T=37, C=16, hd=24, M=30, W=3, R=4, dtype="bf16", ragged=True, index=23),  # bfloat16 bank
+    small(P=3, T=30, C=16, hd=16, M=200, W=20, R=6, dtype="bf16", ids="zipf", gate_width=1, index=24),
 ]
 
 
@@ -131,13 +142,31 @@ def test_backward_config1_shape_full_size(gpu, residency):
     assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
 
 
-def test_backward_rejects_bf16_bank(gpu):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_shared_bank_matches_per_stream_banks(gpu, dtype, monkeypatch):
+    """One bank shared by every stream, the streams' slots interleaved and disjoint (the
+    forward's shared-bank contract): every gradient equals that of per-stream banks bit for
+    bit (the sweep in memory on both sides; a shared bank never takes the resident sweep,
+    whose whole-slice write-back would overwrite the other streams' rows)."""
     from chunked_sparse_delta_amd import sdm_bwd
-    wl = small(P=1, T=16, C=16, hd=8, M=8, W=2, R=2, dtype="bf16")
-    t = gu.to_torch(gu.generate(wl), gpu)
-    with pytest.raises(TypeError):
-        sdm_bwd(t["bank"], t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
-                torch.zeros(1, 16, 8, device=gpu))
+    monkeypatch.setenv("SDM_BWD_RES", "0")
+    wl = small(P=3, T=40, C=16, hd=20, M=25, W=3, R=4, dtype=dtype, ragged=True, index=25)
+    inp, gr, t, bank, got = _run(wl, gpu, dup_reads=True)
+    _check(inp, gr, got)
+    sh = gu.to_torch(dict(workloads.shared_bank_inputs(inp), dtype=dtype), gpu)
+    P, M, hd = wl.P, wl.M, wl.hd
+    gbs = torch.from_numpy(np.ascontiguousarray(
+        workloads.shared_bank_inputs(dict(inp, bank=gr["grad_bank"]))["bank"])).to(gpu)
+    bank_sh = sh["bank"].clone()
+    got2 = sdm_bwd(bank_sh, sh["k_idx"], sh["k_val"], sh["v"], sh["beta"], sh["log_decay"], sh["q_idx"], sh["q_val"],
+                   _grad_out(dict(gr), dtype, gpu), grad_bank=gbs, valid_tokens=sh["valid"], shared_bank=True)
+    torch.cuda.synchronize()
+    assert got2["bank"].shape == (M * P, hd)
+    assert np.array_equal(gu.bits(got2["bank"].reshape(M, P, hd).permute(1, 0, 2).contiguous()),
+                          gu.bits(got["bank"]))
+    for k in ("v", "beta", "log_decay", "k_val", "q_val"):
+        assert np.array_equal(gu.bits(got2[k]), gu.bits(got[k])), k
+    assert np.array_equal(gu.bits(bank_sh), gu.bits(sh["bank"]))
 
 
 @pytest.mark.parametrize("S", ["8", "16", "32", "64"])
