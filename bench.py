@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu-baseline]
     python bench.py --copy-calibration      # plain 1 GiB device copy, for scaling HBM counters
-    python bench.py --op sdm_bwd [--workload 1]   # the backward (float32 bank)
+    python bench.py --op sdm_bwd [--workload 1]   # the backward
     python bench.py --op topk               # the product-key top-k
 
 A step is one sdm_fwd call over the whole workload (every chunk step of every stream)
@@ -218,22 +218,27 @@ BWD_KERNELS = ("bwd_lead", "bwd_sweep", "bwd_reduce")
 
 
 def bench_bwd(args):
-    """One step = one sdm_bwd call over the whole workload (config shapes, float32 bank):
-    the replay of the forward, the reverse sweep and the reduction. The bank comes back
-    bit for bit after each call; grad_bank is carried from call to call (in/out), which
+    """One step = one sdm_bwd call over the whole workload (the config's shapes and bank
+    dtype): the replay of the forward, the reverse sweep and the reduction. The bank comes
+    back bit for bit after each call; grad_bank is carried from call to call (in/out), which
     changes values, not work."""
     import torch
     from chunked_sparse_delta_amd import BWD_TIMING_EVENTS, bwd_workspace_bytes, sdm_bwd
-    wl = workloads.CONFIGS[args.workload].replace(dtype="f32")
+    wl = workloads.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     name = workloads.workload_name(wl).replace("sdm_fwd_", "sdm_bwd_", 1)
     print(f"bench: generating workload {name}", file=sys.stderr, flush=True)
     inp = workloads.generate(wl)
     gr = workloads.grad_inputs(wl, 0)
     t = to_torch(inp, dev)
-    go = torch.from_numpy(gr["grad_out"]).to(dev)
+    if wl.dtype == "bf16":
+        bits = workloads.round_bf16_bits(gr["grad_out"])
+        gr["grad_out"] = workloads.bf16_bits_to_f32(bits)
+        go = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        go = torch.from_numpy(gr["grad_out"]).to(dev)
     gbank = torch.from_numpy(gr["grad_bank"]).to(dev)
-    ws = torch.empty(bwd_workspace_bytes(wl.P, wl.T, wl.W, wl.R, wl.hd, wl.M, torch.float32), dtype=torch.uint8,
+    ws = torch.empty(bwd_workspace_bytes(wl.P, wl.T, wl.W, wl.R, wl.hd, wl.M, t["bank"].dtype), dtype=torch.uint8,
                      device=dev)
     hip = hip_runtime()
     nev = BWD_TIMING_EVENTS
@@ -275,7 +280,7 @@ def bench_bwd(args):
             hip.hipEventDestroy(arr[j])
     kern_ms = dict(zip(BWD_KERNELS, per.mean(axis=0).round(5).tolist()))
 
-    # Algorithmic bytes of the sweep, per live token (rows of hd float32): the replay reads
+    # Algorithmic bytes of the sweep, per live token (rows of hd float32 working values): the replay reads
     # the W written rows, saves them and writes them back (3W); the reverse reads the R read
     # rows, reads and writes the bank gradient of each distinct read slot, reads the W saved
     # rows, reads and writes the W bank-gradient rows and restores the W bank rows (4W + R +
@@ -299,7 +304,7 @@ def bench_bwd(args):
         "ms_per_step": round(1000.0 * elapsed / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": name, "streams": wl.P, "tokens": wl.T, "head_dim": wl.hd, "rows": wl.M,
-                   "write_slots": wl.W, "read_slots": wl.R, "bank_dtype": "f32", "ids": wl.ids},
+                   "write_slots": wl.W, "read_slots": wl.R, "bank_dtype": wl.dtype, "ids": wl.ids},
         "kernel_ms": kern_ms,
         "roofline": {"bound": "hbm", "kernel": "bwd_sweep", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
