@@ -508,7 +508,7 @@ int sdm_wy_solve(int64_t n, int32_t C, const float *A, const float *beta, const 
 namespace {
 
 struct BwdSizes {
-    size_t snap, lead, part, work, total;
+    size_t snap, lead, part, pairs, work, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -520,8 +520,9 @@ BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64
     z.snap = align256(size_t(P) * size_t(NS) * size_t(S) * size_t(T) * size_t(W) * 4);
     z.lead = align256(size_t(P) * size_t(T) * size_t(R) * 8);
     z.part = align256(size_t(P) * size_t(NS) * size_t(T) * size_t(sdm::bwd_parts(W, R)) * 4);
+    z.pairs = align256(size_t(P) * size_t((T + 1) / 2) * 4);
     z.work = dtype == SDM_BF16 ? align256(size_t(shared ? 1 : P) * size_t(M) * size_t(hd) * 4) : 0;
-    z.total = z.snap + z.lead + z.part + z.work;
+    z.total = z.snap + z.lead + z.part + z.pairs + z.work;
     return z;
 }
 
@@ -579,6 +580,10 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     const bool res_ok = !shared && (!res_env || atoi(res_env) != 0) && res_lds <= size_t(dev->lds_per_block) &&
                         res_lds <= size_t(sdm::kBwdMaxLds);
     a.res = res_ok ? sdm::bwd_res_entries(W, R, a.S) : 0;
+    // tokens in pairs when a token's entries fill at most half the entry groups
+    // (SDM_BWD_PAIR=0 turns it off)
+    const char *pair_env = getenv("SDM_BWD_PAIR");
+    a.pair = a.res == 1 && 2 * (W > R ? W : R) <= sdm::kWave / a.S && (!pair_env || atoi(pair_env) != 0);
     if (!a.res && sdm::bwd_lds_bytes(W, a.S, M, false) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "the backward needs %zu bytes of LDS per workgroup, the device has %d",
                     sdm::bwd_lds_bytes(W, a.S, M, false), dev->lds_per_block);
@@ -593,7 +598,9 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     a.snap = reinterpret_cast<float *>(ws);
     a.lead = reinterpret_cast<float2 *>(ws + z.snap);
     a.part = reinterpret_cast<float *>(ws + z.snap + z.lead);
-    a.work = a.bf16 ? reinterpret_cast<float *>(ws + z.snap + z.lead + z.part) : static_cast<float *>(bank->data);
+    a.pairs = reinterpret_cast<int32_t *>(ws + z.snap + z.lead + z.part);
+    a.work = a.bf16 ? reinterpret_cast<float *>(ws + z.snap + z.lead + z.part + z.pairs)
+                    : static_cast<float *>(bank->data);
     hipEvent_t *ev = nullptr;
     if (exec->events && exec->num_events >= SDM_BWD_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
     const hipError_t e = sdm::launch_bwd(a, static_cast<hipStream_t>(exec->stream), ev);

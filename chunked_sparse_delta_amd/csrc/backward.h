@@ -12,6 +12,7 @@ struct BwdArgs {
     int32_t P, T, W, R, G, hd, S, NS;   // S columns per slice (power of two, 4..64), NS slices
     int32_t res;                        // 0: rows in memory; 1, 2, 4: the resident sweep with that
                                         // many entries of each kind per lane
+    int32_t pair;                       // 1: the paired resident sweep (res == 1)
     int32_t bf16;                       // 1: bank, weights, v and grad_out are bfloat16, else float32
     int64_t M;
     int64_t bstride;                    // elements from one stream's bank to the next (M * hd, or 0 shared)
@@ -29,6 +30,7 @@ struct BwdArgs {
     float *snap;     // [P, NS, T, W, S]  old_w of every live write entry, slice by slice
     float2 *lead;    // [P, T, R]      (summed weight, 1) for a slot's first read entry, else (0, 0)
     float *part;     // [P, NS, T, J]  per-slice dots, J = 2W + R + 1
+    int32_t *pairs;  // [P, ceil(T / 2)]  1: tokens 2j, 2j + 1 live and selecting disjoint rows
 };
 
 __host__ __device__ inline int bwd_parts(int W, int R) { return 2 * W + R + 1; }

@@ -541,6 +541,231 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Paired resident sweep: as the resident sweep with one entry of each kind per lane, for
+// shapes where a token's entries fill at most half of the 64 / S entry groups. Tokens go
+// in pairs (2j, 2j + 1), the first half of the entry groups taking token 2j and the second
+// token 2j + 1; a pair whose tokens select disjoint rows (written or read: bwd_pairs_kernel)
+// runs as one step, since neither token then sees a row the other changes; any other pair
+// runs as two steps, one half at a time, in token order (reverse order going back).
+// The sums are those of the resident sweep, term for term, so both give the same bits.
+// ---------------------------------------------------------------------------------------
+
+// pairs[p][j] = 1 if tokens 2j and 2j + 1 of stream p are both live and select disjoint rows.
+__global__ void __launch_bounds__(kBwdBlock) bwd_pairs_kernel(BwdArgs a) {
+    const int npm = (a.T + 1) / 2;
+    const int64_t idx = int64_t(blockIdx.x) * kBwdBlock + threadIdx.x;
+    if (idx >= int64_t(a.P) * npm) return;
+    const int p = int(idx / npm), j = int(idx % npm);
+    const int64_t t0 = int64_t(p) * a.T + 2 * j;
+    int32_t flag = 0;
+    if (2 * j + 1 < live_tokens(a, p)) {
+        flag = 1;
+        auto id_of = [&](int64_t tok, int x) {
+            return x < a.W ? clamp_row(id_word(a.k_idx, tok * a.W + x, a.k_id8), a.M)
+                           : clamp_row(id_word(a.q_idx, tok * a.R + (x - a.W), a.q_id8), a.M);
+        };
+        for (int x = 0; x < a.W + a.R && flag; ++x) {
+            const int32_t s0 = id_of(t0, x);
+            for (int y = 0; y < a.W + a.R; ++y)
+                if (id_of(t0 + 1, y) == s0) { flag = 0; break; }
+        }
+    }
+    a.pairs[idx] = flag;
+}
+
+template <int D, typename T>
+__global__ void __launch_bounds__(kWave) bwd_res_pair_kernel(BwdArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
+    float *lres = red + kResRed;                         // bank slice [M][S], then gradient slice [M][S]
+    const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
+    const int lane = threadIdx.x, S = a.S, E = kWave / S, EH = E / 2;
+    const int c = lane % S, e = lane / S, h = e / EH, eh = e % EH;   // h: which token of the pair
+    const int col = sl * S + c;
+    const bool colok = col < a.hd;
+    const int cc = colok ? col : 0;
+    const int ne = a.W < EH ? a.W : EH;
+    const T *bank_g = static_cast<const T *>(a.bank) + int64_t(p) * a.bstride;
+    float *gb_g = a.gbank + int64_t(p) * a.bstride;
+    const int64_t MS = a.M * S;
+    {
+        constexpr int kB = 16;
+        for (int64_t i0 = lane; i0 < MS; i0 += int64_t(kB) * kWave) {
+            float xb[kB], xg[kB];
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const int64_t i = i0 + int64_t(k) * kWave;
+                const int cg = sl * S + int(i % S);
+                const bool ok = i < MS && cg < a.hd;
+                const int64_t o = ok ? (i / S) * a.hd + cg : 0;
+                xb[k] = to_f32(bank_g[o]);
+                xg[k] = gb_g[o];
+                xb[k] = ok ? xb[k] : 0.0f;
+                xg[k] = ok ? xg[k] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kB; ++k) {
+                const int64_t i = i0 + int64_t(k) * kWave;
+                if (i < MS) {
+                    lres[i] = xb[k];
+                    lres[MS + i] = xg[k];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float *bk = lres + c, *gk = lres + MS + c;
+    const int J = bwd_parts(a.W, a.R);
+    const int32_t n = live_tokens(a, p);
+    const int64_t tok0 = int64_t(p) * a.T;
+    float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
+    const int32_t *pairs = a.pairs + int64_t(p) * ((a.T + 1) / 2);
+
+    // sum over the entry groups of the lane's half, in ascending group order
+    auto column_sum = [&](float part) {
+        red[c * E + e] = part;
+        __builtin_amdgcn_wave_barrier();
+        float s = 0.0f;
+        const int base = c * E + h * EH;
+        for (int q = 0; q < ne; ++q) s += red[base + q];
+        __builtin_amdgcn_wave_barrier();
+        return s;
+    };
+
+    // forward replay of the lane's token t (act: the lane's half takes part in this step)
+    auto fwd_token = [&](ResTok<1> &cur, int t, bool act) {
+        const int w = eh;
+        const bool on = act && w < a.W;
+        const float old = colok ? bk[int64_t(cur.kid[0]) * S] : 0.0f;
+        float acc = 0.0f;
+        if (on) {
+            if (colok) snapw[(int64_t(t) * a.W + w) * S + c] = old;
+            acc = __builtin_fmaf(cur.kv[0], cur.gam[0] * old, acc);
+        }
+        const float ret = column_sum(acc);
+        const float delta = cur.beta * ((colok ? cur.v : 0.0f) - ret);
+        if (on && colok) bk[int64_t(cur.kid[0]) * S] = __builtin_fmaf(cur.kv[0], delta, cur.gam[0] * old);
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // the reverse of the lane's token t
+    auto rev_token = [&](ResTok<1> &cur, int t, bool act) {
+        const int64_t tok = tok0 + t;
+        float *pt = a.part + ((int64_t(p) * a.NS + sl) * a.T + t) * J;
+        const float go = colok ? cur.go : 0.0f;
+        const int w = eh, r = eh;
+        const bool won = act && w < a.W, ron = act && r < a.R;
+        {
+            const int64_t o = int64_t(cur.qid[0]) * S;
+            const float d = lane_group_sum(go * (colok ? bk[o] : 0.0f), S);
+            if (ron) {
+                if (c == 0) pt[2 * a.W + r] = d;
+                if (colok && cur.qf[0] != 0.0f) gk[o] = __builtin_fmaf(cur.ql[0], go, gk[o]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        const float o = colok ? cur.snap[0] : 0.0f;
+        const float ret = column_sum(won ? __builtin_fmaf(cur.kv[0], cur.gam[0] * o, 0.0f) : 0.0f);
+        const float vr = (colok ? cur.v : 0.0f) - ret;
+        const float delta = cur.beta * vr;
+        const float gbw = colok ? gk[int64_t(cur.kid[0]) * S] : 0.0f;
+        const float lka = lane_group_sum(gbw * delta, S);
+        const float gd = column_sum(won ? __builtin_fmaf(cur.kv[0], gbw, 0.0f) : 0.0f);
+        const float gret = -cur.beta * gd;
+        const float gbeta = lane_group_sum(gd * vr, S);
+        if (act && eh == 0) {
+            if (colok) a.gv[tok * a.hd + col] = cur.beta * gd;
+            if (c == 0) pt[2 * a.W + a.R] = gbeta;
+        }
+        const float dec = cur.gam[0] * o;
+        const float gdec = __builtin_fmaf(cur.kv[0], gret, gbw);
+        const float dk = lane_group_sum(gret * dec, S);
+        const float dg = lane_group_sum(gdec * dec, S);
+        if (won) {
+            if (colok) {
+                const int64_t ro = int64_t(cur.kid[0]) * S;
+                gk[ro] = cur.gam[0] * gdec;
+                bk[ro] = o;
+            }
+            if (c == 0) {
+                pt[w] = lka + dk;
+                pt[a.W + w] = dg;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // Pair j's values (the lane's token 2j + h, clamped to the last live one) are prefetched
+    // D pairs ahead into a ring of registers, in whole unrolled rounds as in the resident
+    // sweep; the remaining np % D pairs load as they go.
+    const int last = n > 0 ? n - 1 : 0;
+    const int np = (n + 1) / 2, lastp = np > 0 ? np - 1 : 0, npfull = np - np % D;
+    auto tok_of = [&](int j) { return min(2 * j + h, last); };
+    auto fwd_pair = [&](ResTok<1> &x, int fl, int j) {
+        const int t = 2 * j + h;
+        if (__builtin_amdgcn_readfirstlane(fl)) {
+            fwd_token(x, t, t < n);
+        } else {
+            fwd_token(x, t, h == 0);
+            fwd_token(x, t, h == 1 && t < n);
+        }
+    };
+    auto rev_pair = [&](ResTok<1> &x, int fl, int j) {
+        const int t = 2 * j + h;
+        if (__builtin_amdgcn_readfirstlane(fl)) {
+            rev_token(x, t, t < n);
+        } else {
+            rev_token(x, t, h == 1 && t < n);
+            rev_token(x, t, h == 0);
+        }
+    };
+    ResTok<1> ring[D];
+    int fl[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        res_load<1, false, T>(a, ring[d], tok0, tok_of(min(d, lastp)), snapw, eh, EH, c, cc);
+        fl[d] = pairs[min(d, lastp)];
+    }
+    for (int j0 = 0; j0 < npfull; j0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            fwd_pair(ring[d], fl[d], j0 + d);
+            res_load<1, false, T>(a, ring[d], tok0, tok_of(min(j0 + d + D, lastp)), snapw, eh, EH, c, cc);
+            fl[d] = pairs[min(j0 + d + D, lastp)];
+        }
+    }
+    for (int j = npfull; j < np; ++j) {
+        ResTok<1> x;
+        res_load<1, false, T>(a, x, tok0, tok_of(j), snapw, eh, EH, c, cc);
+        fwd_pair(x, pairs[j], j);
+    }
+    for (int j = np - 1; j >= npfull; --j) {
+        ResTok<1> x;
+        res_load<1, true, T>(a, x, tok0, tok_of(j), snapw, eh, EH, c, cc);
+        rev_pair(x, pairs[j], j);
+    }
+    const int top = npfull - 1;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        res_load<1, true, T>(a, ring[d], tok0, tok_of(max(top - d, 0)), snapw, eh, EH, c, cc);
+        fl[d] = pairs[max(top - d, 0)];
+    }
+    for (int j0 = top; j0 >= 0; j0 -= D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            rev_pair(ring[d], fl[d], j0 - d);
+            res_load<1, true, T>(a, ring[d], tok0, tok_of(max(j0 - d - D, 0)), snapw, eh, EH, c, cc);
+            fl[d] = pairs[max(j0 - d - D, 0)];
+        }
+    }
+    __syncthreads();
+    for (int64_t i = lane; i < MS; i += kWave) {
+        const int cg = sl * S + int(i % S);
+        if (cg < a.hd) gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+    }
+}
+
 // One workgroup per token: the slices' dots summed in ascending slice order; padding
 // tokens get zeros (grad_v too).
 __global__ void __launch_bounds__(kBwdBlock) bwd_reduce_kernel(BwdArgs a) {
@@ -592,6 +817,9 @@ hipError_t set_bwd_attrs() {
                          reinterpret_cast<const void *>(bwd_res_kernel<4, 1, T>)};
     for (const void *f : res)
         if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdMaxLds);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_res_pair_kernel<4, T>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kBwdMaxLds);
     return e;
 }
 
@@ -637,10 +865,16 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
             static_cast<const bf16 *>(a.bank), a.work, n);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    if (a.pair) {
+        const int64_t npairs = int64_t(a.P) * ((a.T + 1) / 2);
+        bwd_pairs_kernel<<<dim3(unsigned((npairs + kBwdBlock - 1) / kBwdBlock)), dim3(kBwdBlock), 0, st>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     const dim3 grid(unsigned(a.P * a.NS));
     const size_t lds = bwd_lds_bytes(a.W, a.S, a.M, a.res != 0);
-    switch (a.res) {
+    if (a.pair) bwd_res_pair_kernel<4, T><<<grid, dim3(kWave), lds, st>>>(a);
+    else switch (a.res) {
         case 1: bwd_res_kernel<1, 4, T><<<grid, dim3(kWave), lds, st>>>(a); break;
         case 2: bwd_res_kernel<2, 2, T><<<grid, dim3(kWave), lds, st>>>(a); break;
         case 4: bwd_res_kernel<4, 1, T><<<grid, dim3(kWave), lds, st>>>(a); break;

@@ -239,16 +239,17 @@ def test_topk_backward_rejects_before_any_launch(lib):
 
 def test_bwd_workspace_bytes(lib):
     """Saved rows (4 * W * hd bytes per token), folded read slots (8 * R per token), the
-    per-slice dots (4 * (2W + R + 1) per token and column slice), each 256-byte aligned, and
-    for a bfloat16 bank its float32 working rows. Config 1's shapes take 4-column slices
+    per-slice dots (4 * (2W + R + 1) per token and column slice), a flag per token pair,
+    each 256-byte aligned, and for a bfloat16 bank its float32 working rows. Config 1's shapes take 4-column slices
     (8 streams x 16 slices = 128 workgroups)."""
     f = lib.sdm_bwd_workspace_bytes
     f.restype = ctypes.c_size_t
     f.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
-    snap, lead, part = 8 * 16 * 4 * 2048 * 8 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4
-    assert f(8, 2048, 8, 8, 64, 4096, 0, 0) == snap + lead + part
-    assert f(8, 2048, 8, 8, 64, 4096, 1, 0) == snap + lead + part + 8 * 4096 * 64 * 4
-    assert f(8, 2048, 8, 8, 64, 4096, 1, 1) == snap + lead + part + 4096 * 64 * 4
+    snap, lead, part, pairs = 8 * 16 * 4 * 2048 * 8 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4, 8 * 1024 * 4
+    base = snap + lead + part + pairs
+    assert f(8, 2048, 8, 8, 64, 4096, 0, 0) == base
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 0) == base + 8 * 4096 * 64 * 4
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 1) == base + 4096 * 64 * 4
     assert f(0, 2048, 8, 8, 64, 4096, 0, 0) == 0 and f(8, 2048, 0, 8, 64, 4096, 0, 0) == 0
     assert f(8, 2048, 8, 257, 64, 4096, 0, 0) == 0 and f(8, 2048, 8, 8, 64, 0, 0, 0) == 0
     assert f(8, 2048, 8, 8, 64, 4096, 2, 0) == 0 and f(8, 2048, 8, 8, 64, 4096, 0, 2) == 0

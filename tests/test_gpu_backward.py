@@ -77,14 +77,17 @@ CASES = [
 ]
 
 
-@pytest.fixture(params=["lds", "memory"])
+@pytest.fixture(params=["pair", "lds", "memory"])
 def residency(request, monkeypatch):
-    """lds: the slices of the bank and its gradient held in LDS where they fit (the default);
-    memory: always read and written in memory (SDM_BWD_RES=0)."""
+    """pair: the default (slices in LDS where they fit, tokens in pairs where a token's entries
+    fill at most half the entry groups); lds: slices in LDS, one token per step
+    (SDM_BWD_PAIR=0); memory: rows always read and written in memory (SDM_BWD_RES=0)."""
+    for var in ("SDM_BWD_RES", "SDM_BWD_PAIR"):
+        monkeypatch.delenv(var, raising=False)
     if request.param == "memory":
         monkeypatch.setenv("SDM_BWD_RES", "0")
-    else:
-        monkeypatch.delenv("SDM_BWD_RES", raising=False)
+    elif request.param == "lds":
+        monkeypatch.setenv("SDM_BWD_PAIR", "0")
     return request.param
 
 
@@ -184,3 +187,25 @@ def test_backward_wide_slices(gpu, S, monkeypatch):
         inp, gr, t, bank, got = _run(wl, gpu, seed=int(S), dup_reads=True)
         _check(inp, gr, got)
         assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
+
+
+@pytest.mark.parametrize("T,M,dtype", [(37, 12, "f32"), (64, 2000, "f32"), (63, 40, "bf16"), (70, 9, "f32"),
+                                       (2, 30, "f32"), (1, 30, "f32")])
+def test_backward_token_pairs_give_the_same_bits(gpu, T, M, dtype, monkeypatch):
+    """Tokens taken in pairs (one step for a pair selecting disjoint rows, two masked steps
+    otherwise; a small bank makes many pairs dependent) give exactly the bits of the resident
+    sweep taking one token per step, for every remainder of pairs modulo the prefetch depth
+    and odd, ragged and single-token streams; both match the oracle."""
+    wl = small(P=3, T=T, C=16, hd=12, M=M, W=4, R=3, dtype=dtype, ragged=T > 2, index=26)
+    runs = []
+    for pair in (None, "0"):
+        monkeypatch.delenv("SDM_BWD_RES", raising=False)
+        if pair is None:
+            monkeypatch.delenv("SDM_BWD_PAIR", raising=False)
+        else:
+            monkeypatch.setenv("SDM_BWD_PAIR", pair)
+        inp, gr, t, bank, got = _run(wl, gpu, seed=T, dup_reads=True)
+        _check(inp, gr, got)
+        runs.append(got)
+    for k in NAMES:
+        assert np.array_equal(gu.bits(runs[0][k]), gu.bits(runs[1][k])), k
