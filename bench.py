@@ -280,23 +280,23 @@ def bench_bwd(args):
             hip.hipEventDestroy(arr[j])
     kern_ms = dict(zip(BWD_KERNELS, per.mean(axis=0).round(5).tolist()))
 
-    # Algorithmic bytes of the sweep, per live token (rows of hd float32 working values): the replay reads
-    # the W written rows, saves them and writes them back (3W); the reverse reads the R read
-    # rows, reads and writes the bank gradient of each distinct read slot, reads the W saved
-    # rows, reads and writes the W bank-gradient rows and restores the W bank rows (4W + R +
-    # 2U_r); v twice, grad_out once, grad_v once (4 vectors); plus 4 bytes per token, slice
-    # and dot product (2W + R + 1).
+    # Algorithmic bytes of the sweep: what any backward of this design-independent form must
+    # move, plus the saved rows an exact restore needs. Per call, the bank read once and the
+    # bank gradient read and written once (float32); per live token, v and grad_out read
+    # once (bank dtype), grad_v written (float32), slot ids and weights read, gates and beta
+    # read, their gradients written (float32), and each write entry's row saved and read back
+    # once (float32 working values).
     S = 4
     while S < 64 and S < wl.hd:
         S <<= 1
     while S > 4 and wl.P * (-(-wl.hd // S)) < 256:
         S >>= 1
-    NS = -(-wl.hd // S)
     valid = np.asarray(inp["valid"], dtype=np.int64)
     tokens = int(valid.sum())
-    ur = sum(len(set(inp["q_idx"][p, t_].tolist())) for p in range(wl.P) for t_ in range(int(valid[p])))
-    row = 4 * wl.hd
-    sweep_bytes = row * (tokens * (7 * wl.W + wl.R + 4) + 2 * ur) + 4 * NS * tokens * (2 * wl.W + wl.R + 1)
+    es = 4 if wl.dtype == "f32" else 2
+    per_token = (wl.hd * (2 * es + 4) + (wl.W + wl.R) * (4 + es) + 4 * wl.G + 4 + 4 * (wl.W + wl.R + wl.G + 1)
+                 + 2 * wl.W * wl.hd * 4)
+    sweep_bytes = wl.P * wl.M * wl.hd * (es + 8) + tokens * per_token
     gbs = sweep_bytes / (kern_ms["bwd_sweep"] * 1e-3) / 1e9
     res = {
         "metric": "SDM bwd tokens/sec at 1 MI355X", "value": round(tokens * args.steps / elapsed, 1),

@@ -49,6 +49,16 @@ __device__ __forceinline__ int32_t clamp_row(int32_t s, int64_t M) {
     return s < 0 ? 0 : (s >= M ? int32_t(M - 1) : s);
 }
 
+// (stream, slice) of a sweep workgroup. Workgroups are dealt to the 8 XCDs round-robin;
+// when their count divides by 8, consecutive slices of one stream go to one XCD, so the
+// stream's token values (read by every slice, twice) are fetched into one L2 only.
+__device__ __forceinline__ void sweep_owner(const BwdArgs &a, int &p, int &sl) {
+    const int nwg = a.P * a.NS, b = blockIdx.x;
+    const int lin = nwg % kXcds == 0 ? (b % kXcds) * (nwg / kXcds) + b / kXcds : b;
+    p = lin / a.NS;
+    sl = lin % a.NS;
+}
+
 // Sum over the S consecutive lanes of a group (butterfly: every lane gets the same bits).
 __device__ __forceinline__ float group_sum(float x, int S) {
     for (int m = S >> 1; m > 0; m >>= 1) x += __shfl_xor(x, m, kWave);
@@ -168,7 +178,8 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     BwdSmem &sm = *reinterpret_cast<BwdSmem *>(smem_raw);
     float *old = reinterpret_cast<float *>(smem_raw + sizeof(BwdSmem));
     float *gbw = old + a.W * a.S;
-    const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
+    int p, sl;
+    sweep_owner(a, p, sl);
     const int tid = threadIdx.x, S = a.S, E = NT / S;
     const int c = tid % S, e = tid / S;
     const int col = sl * S + c;
@@ -349,7 +360,8 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
     float *lres = red + kResRed;                         // bank slice [M][S], then gradient slice [M][S]
-    const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
+    int p, sl;
+    sweep_owner(a, p, sl);
     const int lane = threadIdx.x, S = a.S, E = kWave / S;
     const int c = lane % S, e = lane / S;
     const int col = sl * S + c;
@@ -579,7 +591,8 @@ __global__ void __launch_bounds__(kWave) bwd_res_pair_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
     float *lres = red + kResRed;                         // bank slice [M][S], then gradient slice [M][S]
-    const int sl = blockIdx.x % a.NS, p = blockIdx.x / a.NS;
+    int p, sl;
+    sweep_owner(a, p, sl);
     const int lane = threadIdx.x, S = a.S, E = kWave / S, EH = E / 2;
     const int c = lane % S, e = lane / S, h = e / EH, eh = e % EH;   // h: which token of the pair
     const int col = sl * S + c;
