@@ -49,17 +49,18 @@ def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False):
 def _check(inp, gr, got, streams=None):
     f = oracle.as_f64_inputs(inp)
     want = oracle.token_loop_backward(f, gr["grad_out"], gr["grad_bank"], threads=8, streams=streams)
-    sel = slice(None) if streams is None else list(streams)
+    if streams is not None:
+        want = {k: v[list(streams)] for k, v in want.items()}
     for k, ok in NAMES.items():
-        g = gu.f64(got[k])[sel]
-        w = want[ok][sel]
+        g = gu.f64(got[k] if streams is None else got[k][list(streams)])
+        w = want[ok]
         assert g.shape == w.shape, k
         assert gu.rel_err(g, w) <= TOL, (k, gu.rel_err(g, w))
     valid = inp["valid"]
     for p in (range(inp["valid"].shape[0]) if streams is None else streams):
         n = int(valid[p])
         for k in ("v", "beta", "log_decay", "k_val", "q_val"):
-            assert not gu.f64(got[k])[p, n:].any(), (k, p)
+            assert not gu.f64(got[k][p, n:]).any(), (k, p)
 
 
 CASES = [
@@ -133,6 +134,17 @@ def test_backward_reruns_are_bitwise_and_slices_agree(gpu, monkeypatch):
         assert np.array_equal(gu.bits(runs[0][k]), gu.bits(runs[1][k])), k
         for r in runs[2:]:
             assert gu.rel_err(gu.f64(r[k]), gu.f64(runs[0][k])) <= 1e-5, k
+
+
+@pytest.mark.parametrize("cfg,streams", [("2", (0, 17, 31)), ("3", (0, 9, 15))])
+def test_backward_full_size_sampled_streams(gpu, cfg, streams):
+    """Configs 2 (bfloat16 bank, Zipf slots, 32 + 32 per token) and 3 (float32, ragged, 64 + 64
+    per token) at full size through the 256-thread sweep; every gradient of sampled streams
+    against O3 (each stream's gradients depend on that stream alone)."""
+    wl = workloads.CONFIGS[cfg]
+    inp, gr, t, bank, got = _run(wl, gpu)
+    _check(inp, gr, got, streams=streams)
+    assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
 
 
 def test_backward_config1_shape_full_size(gpu, residency):
