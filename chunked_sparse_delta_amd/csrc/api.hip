@@ -583,7 +583,8 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     // tokens in pairs when a token's entries fill at most half the entry groups
     // (SDM_BWD_PAIR=0 turns it off)
     const char *pair_env = getenv("SDM_BWD_PAIR");
-    a.pair = a.res == 1 && 2 * (W > R ? W : R) <= sdm::kWave / a.S && (!pair_env || atoi(pair_env) != 0);
+    a.pair = a.res == 1 && 2 * (W > R ? W : R) <= sdm::kWave / a.S && (W > R ? W : R) <= sdm::kPairMax &&
+             (!pair_env || atoi(pair_env) != 0);
     if (!a.res && sdm::bwd_lds_bytes(W, a.S, M, false) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "the backward needs %zu bytes of LDS per workgroup, the device has %d",
                     sdm::bwd_lds_bytes(W, a.S, M, false), dev->lds_per_block);

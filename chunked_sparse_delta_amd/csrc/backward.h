@@ -7,6 +7,7 @@ namespace sdm {
 constexpr int kBwdBlock = 256;
 constexpr int kBwdMaxLds = 160 * 1024 - 256;   // LDS a workgroup of the resident sweep may take
 constexpr int kResRed = kWave;                 // words of the resident sweep's partial-sum array
+constexpr int kPairMax = 8;                    // write and read slots per token, at most, for token pairs
 
 struct BwdArgs {
     int32_t P, T, W, R, G, hd, S, NS;   // S columns per slice (power of two, 4..64), NS slices

@@ -564,6 +564,9 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 
 // pairs[p][j] = 1 if tokens 2j and 2j + 1 of stream p are both live and select disjoint rows.
+// Pairs are taken only when W, R <= kPairMax (a token's entries fill at most half of at most
+// 16 entry groups), so both tokens' ids sit in registers.
+
 __global__ void __launch_bounds__(kBwdBlock) bwd_pairs_kernel(BwdArgs a) {
     const int npm = (a.T + 1) / 2;
     const int64_t idx = int64_t(blockIdx.x) * kBwdBlock + threadIdx.x;
@@ -572,16 +575,23 @@ __global__ void __launch_bounds__(kBwdBlock) bwd_pairs_kernel(BwdArgs a) {
     const int64_t t0 = int64_t(p) * a.T + 2 * j;
     int32_t flag = 0;
     if (2 * j + 1 < live_tokens(a, p)) {
-        flag = 1;
-        auto id_of = [&](int64_t tok, int x) {
-            return x < a.W ? clamp_row(id_word(a.k_idx, tok * a.W + x, a.k_id8), a.M)
-                           : clamp_row(id_word(a.q_idx, tok * a.R + (x - a.W), a.q_id8), a.M);
-        };
-        for (int x = 0; x < a.W + a.R && flag; ++x) {
-            const int32_t s0 = id_of(t0, x);
-            for (int y = 0; y < a.W + a.R; ++y)
-                if (id_of(t0 + 1, y) == s0) { flag = 0; break; }
+        int32_t x0[2 * kPairMax], x1[2 * kPairMax];
+#pragma unroll
+        for (int x = 0; x < 2 * kPairMax; ++x) {
+            const bool wr = x < kPairMax;
+            const int k = wr ? x : x - kPairMax;
+            const int kk = min(k, (wr ? a.W : a.R) - 1);   // past the token's entries: repeat its last
+            x0[x] = wr ? clamp_row(id_word(a.k_idx, t0 * a.W + kk, a.k_id8), a.M)
+                       : clamp_row(id_word(a.q_idx, t0 * a.R + kk, a.q_id8), a.M);
+            x1[x] = wr ? clamp_row(id_word(a.k_idx, (t0 + 1) * a.W + kk, a.k_id8), a.M)
+                       : clamp_row(id_word(a.q_idx, (t0 + 1) * a.R + kk, a.q_id8), a.M);
         }
+        bool disjoint = true;
+#pragma unroll
+        for (int x = 0; x < 2 * kPairMax; ++x)
+#pragma unroll
+            for (int y = 0; y < 2 * kPairMax; ++y) disjoint = disjoint && x0[x] != x1[y];
+        flag = disjoint ? 1 : 0;
     }
     a.pairs[idx] = flag;
 }
