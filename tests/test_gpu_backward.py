@@ -75,6 +75,8 @@ CASES = [
     small(P=1, T=30, C=16, hd=20, M=400, W=50, R=64, index=21),                        # 4 entries per lane
     small(P=2, T=37, C=16, hd=24, M=30, W=3, R=4, dtype="bf16", ragged=True, index=23),  # bfloat16 bank
     small(P=3, T=30, C=16, hd=16, M=200, W=20, R=6, dtype="bf16", ids="zipf", gate_width=1, index=24),
+    small(P=1, T=1, C=16, hd=8, M=1, W=1, R=1, index=27),                                # one token, one row
+    small(P=1, T=20, C=16, hd=1024, M=30, W=3, R=3, dtype="bf16", index=28),             # wide head
 ]
 
 

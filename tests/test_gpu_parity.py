@@ -94,6 +94,9 @@ SMALL = [
     small(P=16, T=96, C=48, hd=24, M=100, W=6, R=6, dtype="bf16", index=18),
     small(P=1, T=16, C=16, hd=4, M=2, W=1, R=1, index=19),                                   # one chunk, tiny bank
     small(P=2, T=200, C=64, hd=256, M=300, W=256, R=256, dtype="bf16", weight_scale=-1.0, index=20),  # max width
+    small(P=1, T=1, C=16, hd=8, M=1, W=1, R=1, index=40),                                     # one token, one row
+    small(P=2, T=5, C=64, hd=16, M=10, W=2, R=2, ragged=True, index=41),                     # shorter than a chunk
+    small(P=1, T=40, C=16, hd=1024, M=30, W=3, R=3, dtype="bf16", index=42),                 # wide head
 ]
 
 
