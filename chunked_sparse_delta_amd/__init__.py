@@ -29,7 +29,7 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "sdm_bwd", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
+__all__ = ["SdmError", "sdm_fwd", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
            "workspace_bytes", "plan",
            "library_path",
            "SDM_ERRORS"]
@@ -311,6 +311,55 @@ def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
                      ctypes.byref(bk), _ptr(valid_tokens), _ptr(grad_out), ctypes.byref(gr), ctypes.byref(ex))
     _check_rc(lib, rc)
     return out
+
+
+class _SDMWriteRead(torch.autograd.Function):
+    """sdm_fwd with sdm_bwd as its backward: the bank is state (advanced in place, no
+    gradient); the float inputs get gradients. The forward keeps a copy of the bank as it
+    was, which the backward replays from."""
+
+    @staticmethod
+    def forward(ctx, bank, k_val, v, beta, log_decay, q_val, k_idx, q_idx, chunk, valid_tokens, shared_bank):
+        bank0 = bank.detach().clone()
+        out = sdm_fwd(bank, k_idx, k_val.detach(), v.detach(), beta.detach(), log_decay.detach(), q_idx,
+                      q_val.detach(), chunk=chunk, valid_tokens=valid_tokens, shared_bank=shared_bank)
+        ctx.save_for_backward(bank0, k_val, v, beta, log_decay, q_val, k_idx, q_idx)
+        ctx.valid_tokens, ctx.shared_bank = valid_tokens, shared_bank
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        bank0, k_val, v, beta, log_decay, q_val, k_idx, q_idx = ctx.saved_tensors
+        go = grad_out.to(bank0.dtype).contiguous()
+        g = sdm_bwd(bank0, k_idx, k_val.detach(), v.detach(), beta.detach(), log_decay.detach(), q_idx,
+                    q_val.detach(), go, valid_tokens=ctx.valid_tokens, shared_bank=ctx.shared_bank)
+        need = ctx.needs_input_grad   # (bank, k_val, v, beta, log_decay, q_val, ...)
+        out = [None] * 11
+        for i, (name, like) in enumerate((("k_val", k_val), ("v", v), ("beta", beta), ("log_decay", log_decay),
+                                          ("q_val", q_val)), start=1):
+            if need[i]:
+                out[i] = g[name].to(like.dtype)
+        return tuple(out)
+
+
+def sdm_write_read(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
+                   beta: torch.Tensor, log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, *,
+                   chunk: int = 64, valid_tokens: torch.Tensor | None = None,
+                   shared_bank: bool = False) -> torch.Tensor:
+    """The memory op for autograd: returns the readings and advances ``bank`` in place, as
+    sdm_fwd does; when grad mode is on and k_val, v, beta, log_decay or q_val requires grad,
+    the readings' backward is sdm_bwd (gradients cast to the inputs' dtypes). The bank is
+    state: it receives no gradient here (it must not require grad); sdm_bwd gives the
+    gradient of the initial bank to callers that need it."""
+    needs = torch.is_grad_enabled() and any(t.requires_grad for t in (k_val, v, beta, log_decay, q_val))
+    if bank.requires_grad:
+        raise ValueError("sdm_write_read advances the bank in place: the bank must not require grad "
+                         "(use sdm_bwd for the gradient of the initial bank)")
+    if not needs:
+        return sdm_fwd(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, chunk=chunk,
+                       valid_tokens=valid_tokens, shared_bank=shared_bank)
+    return _SDMWriteRead.apply(bank, k_val, v, beta, log_decay, q_val, k_idx, q_idx, chunk, valid_tokens,
+                               shared_bank)
 
 
 def chunk_mats(k_idx, k_val, beta, log_decay, q_idx, q_val, *, rows: int, head_dim: int, chunk: int,

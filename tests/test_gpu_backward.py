@@ -223,3 +223,33 @@ def test_backward_token_pairs_give_the_same_bits(gpu, T, M, dtype, monkeypatch):
         runs.append(got)
     for k in NAMES:
         assert np.array_equal(gu.bits(runs[0][k]), gu.bits(runs[1][k])), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sdm_write_read_autograd(gpu, dtype):
+    """sdm_write_read under autograd: the readings equal sdm_fwd's bit for bit, the bank is
+    advanced in place the same way, and torch.autograd.grad gives sdm_bwd's gradients (cast
+    to the inputs' dtypes) for the float inputs that require grad."""
+    from chunked_sparse_delta_amd import sdm_bwd, sdm_fwd, sdm_write_read
+    wl = small(P=2, T=45, C=16, hd=16, M=20, W=3, R=4, dtype=dtype, ragged=True, index=29)
+    inp = gu.generate(wl)
+    gr = workloads.grad_inputs(wl, 2, bank_grad=False)
+    t = gu.to_torch(inp, gpu)
+    go = _grad_out(gr, dtype, gpu)
+    leaves = {k: t[k].clone().requires_grad_(True) for k in ("k_val", "v", "beta", "log_decay", "q_val")}
+    bank_a, bank_b, bank_c = t["bank"].clone(), t["bank"].clone(), t["bank"].clone()
+    out = sdm_write_read(bank_a, t["k_idx"], leaves["k_val"], leaves["v"], leaves["beta"], leaves["log_decay"],
+                         t["q_idx"], leaves["q_val"], chunk=16, valid_tokens=t["valid"])
+    grads = torch.autograd.grad(out, [leaves[k] for k in ("k_val", "v", "beta", "log_decay")], grad_outputs=go)
+    ref = sdm_fwd(bank_b, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
+                  chunk=16, valid_tokens=t["valid"])
+    want = sdm_bwd(bank_c, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], go,
+                   valid_tokens=t["valid"])
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits(out), gu.bits(ref)) and np.array_equal(gu.bits(bank_a), gu.bits(bank_b))
+    for g, k in zip(grads, ("k_val", "v", "beta", "log_decay")):
+        assert g.dtype == leaves[k].dtype
+        assert np.array_equal(gu.bits(g), gu.bits(want[k].to(g.dtype))), k
+    with pytest.raises(ValueError, match="must not require grad"):
+        sdm_write_read(t["bank"].clone().requires_grad_(True), t["k_idx"], leaves["k_val"], leaves["v"],
+                       leaves["beta"], leaves["log_decay"], t["q_idx"], leaves["q_val"], chunk=16)
