@@ -286,11 +286,14 @@ def bench_bwd(args):
     # once (bank dtype), grad_v written (float32), slot ids and weights read, gates and beta
     # read, their gradients written (float32), and each write entry's row saved and read back
     # once (float32 working values).
+    # the library's slice width (shapes only): 4 columns when a token has at most 128 slots of
+    # each kind, else the widest power of two up to 64 that still gives 256 workgroups
     S = 4
-    while S < 64 and S < wl.hd:
-        S <<= 1
-    while S > 4 and wl.P * (-(-wl.hd // S)) < 256:
-        S >>= 1
+    if max(wl.W, wl.R) > 128:
+        while S < 64 and S < wl.hd:
+            S <<= 1
+        while S > 4 and wl.P * (-(-wl.hd // S)) < 256:
+            S >>= 1
     valid = np.asarray(inp["valid"], dtype=np.int64)
     tokens = int(valid.sum())
     es = 4 if wl.dtype == "f32" else 2

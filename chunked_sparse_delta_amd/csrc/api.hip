@@ -514,7 +514,7 @@ struct BwdSizes {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64_t M, int32_t dtype, bool shared) {
-    const int S = sdm::bwd_slice_cols(P, hd);
+    const int S = sdm::bwd_slice_cols(P, hd, W, R);
     const int64_t NS = (hd + S - 1) / S;
     BwdSizes z{};
     z.snap = align256(size_t(P) * size_t(NS) * size_t(S) * size_t(T) * size_t(W) * 4);
@@ -569,7 +569,7 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     a.P = P; a.T = T; a.W = W; a.R = R; a.G = gate_width; a.hd = hd; a.M = M;
     a.bf16 = bank->dtype == SDM_BF16;
     a.bstride = shared ? 0 : M * hd;
-    a.S = sdm::bwd_slice_cols(P, hd);
+    a.S = sdm::bwd_slice_cols(P, hd, W, R);
     a.NS = (hd + a.S - 1) / a.S;
     // one wavefront per slice with the slices of the bank and of its gradient in LDS when they fit
     // and a lane covers its entries in at most 4 (SDM_BWD_RES=0 turns it off)
@@ -579,7 +579,11 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     // which would overwrite the rows of the other streams)
     const bool res_ok = !shared && (!res_env || atoi(res_env) != 0) && res_lds <= size_t(dev->lds_per_block) &&
                         res_lds <= size_t(sdm::kBwdMaxLds);
-    a.res = res_ok ? sdm::bwd_res_entries(W, R, a.S) : 0;
+    a.res = res_ok ? sdm::bwd_res_entries(W, R, a.S, 4) : 0;
+    // otherwise one wavefront per slice on rows in memory where a lane covers its entries in
+    // at most 8 (SDM_BWD_WAVE=0 keeps the 256-thread sweep)
+    const char *wave_env = getenv("SDM_BWD_WAVE");
+    if (a.res == 0 && (!wave_env || atoi(wave_env) != 0)) a.res = -sdm::bwd_res_entries(W, R, a.S, 8);
     // tokens in pairs when a token's entries fill at most half the entry groups
     // (SDM_BWD_PAIR=0 turns it off)
     const char *pair_env = getenv("SDM_BWD_PAIR");

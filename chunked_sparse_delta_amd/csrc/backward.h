@@ -8,11 +8,13 @@ constexpr int kBwdBlock = 256;
 constexpr int kBwdMaxLds = 160 * 1024 - 256;   // LDS a workgroup of the resident sweep may take
 constexpr int kResRed = kWave;                 // words of the resident sweep's partial-sum array
 constexpr int kPairMax = 8;                    // write and read slots per token, at most, for token pairs
+constexpr int kWaveMaxSlots = 128;             // slots per token, at most, for the one-wavefront sweeps
 
 struct BwdArgs {
     int32_t P, T, W, R, G, hd, S, NS;   // S columns per slice (power of two, 4..64), NS slices
-    int32_t res;                        // 0: rows in memory; 1, 2, 4: the resident sweep with that
-                                        // many entries of each kind per lane
+    int32_t res;                        // 1, 2, 4: the one-wavefront sweep, rows in LDS, with that
+                                        // many entries of each kind per lane; -1, -2, -4, -8: the
+                                        // same with rows in memory; 0: the 256-thread sweep
     int32_t pair;                       // 1: the paired resident sweep (res == 1)
     int32_t bf16;                       // 1: bank, weights, v and grad_out are bfloat16, else float32
     int64_t M;
@@ -37,8 +39,8 @@ struct BwdArgs {
 __host__ __device__ inline int bwd_parts(int W, int R) { return 2 * W + R + 1; }
 
 size_t bwd_lds_bytes(int W, int S, int64_t M, bool res);
-int bwd_slice_cols(int P, int hd);
-int bwd_res_entries(int W, int R, int S);
+int bwd_slice_cols(int P, int hd, int W, int R);
+int bwd_res_entries(int W, int R, int S, int kj_max);
 hipError_t bwd_prepare();
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t st, hipEvent_t *ev);
 

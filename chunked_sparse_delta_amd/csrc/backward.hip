@@ -355,7 +355,10 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
     x.beta = a.beta[tok];
 }
 
-template <int KJ, int D, typename T>
+// RES: rows in LDS as above; else the same wavefront works on rows in memory (the bank's
+// float32 working rows and the bank gradient, row stride head_dim): a wavefront's memory
+// operations take effect in program order for all its lanes, so it needs no barrier either.
+template <int KJ, int D, typename T, bool RES>
 __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float *red = reinterpret_cast<float *>(smem_raw);   // [S][E] entry-group partial sums
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     const T *bank_g = static_cast<const T *>(a.bank) + int64_t(p) * a.bstride;
     float *gb_g = a.gbank + int64_t(p) * a.bstride;
     const int64_t MS = a.M * S;
-    {
+    if (RES) {
         constexpr int kB = 16;
         for (int64_t i0 = lane; i0 < MS; i0 += int64_t(kB) * kWave) {
             float xb[kB], xg[kB];
@@ -397,7 +400,9 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    float *bk = lres + c, *gk = lres + MS + c;
+    float *bk = RES ? lres + c : a.work + int64_t(p) * a.bstride + cc;
+    float *gk = RES ? lres + MS + c : gb_g + cc;
+    const int64_t rs = RES ? S : a.hd;   // row stride of bk and gk
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
     const int64_t tok0 = int64_t(p) * a.T;
@@ -422,7 +427,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < KJ; ++j) {
             const int w = e + j * E;
-            old[j] = colok ? bk[int64_t(cur.kid[j]) * S] : 0.0f;
+            old[j] = colok ? bk[int64_t(cur.kid[j]) * rs] : 0.0f;
             if (w < a.W) {
                 if (colok) snapw[(int64_t(t) * a.W + w) * S + c] = old[j];
                 acc = __builtin_fmaf(cur.kv[j], cur.gam[j] * old[j], acc);
@@ -434,7 +439,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
         for (int j = 0; j < KJ; ++j) {
             const int w = e + j * E;
             if (w < a.W && colok)
-                bk[int64_t(cur.kid[j]) * S] = __builtin_fmaf(cur.kv[j], delta, cur.gam[j] * old[j]);
+                bk[int64_t(cur.kid[j]) * rs] = __builtin_fmaf(cur.kv[j], delta, cur.gam[j] * old[j]);
         }
         __builtin_amdgcn_wave_barrier();
     };
@@ -448,7 +453,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < KJ; ++j) {
             const int r = e + j * E;
-            const int64_t o = int64_t(cur.qid[j]) * S;
+            const int64_t o = int64_t(cur.qid[j]) * rs;
             const float d = lane_group_sum(go * (colok ? bk[o] : 0.0f), S);
             if (r < a.R) {
                 if (c == 0) pt[2 * a.W + r] = d;
@@ -474,7 +479,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < KJ; ++j) {
             const int w = e + j * E;
-            gbw[j] = colok ? gk[int64_t(cur.kid[j]) * S] : 0.0f;
+            gbw[j] = colok ? gk[int64_t(cur.kid[j]) * rs] : 0.0f;
             lka[j] = lane_group_sum(gbw[j] * delta, S);
             if (w < a.W) acc2 = __builtin_fmaf(cur.kv[j], gbw[j], acc2);
         }
@@ -495,7 +500,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
             const float dg = lane_group_sum(gdec * dec, S);
             if (w < a.W) {
                 if (colok) {
-                    const int64_t ro = int64_t(cur.kid[j]) * S;
+                    const int64_t ro = int64_t(cur.kid[j]) * rs;
                     gk[ro] = cur.gam[j] * gdec;
                     bk[ro] = cur.snap[j];
                 }
@@ -546,10 +551,12 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
             res_load<KJ, true, T>(a, ring[d], tok0, max(t0 - d - D, 0), snapw, e, E, c, cc);
         }
     }
-    __syncthreads();
-    for (int64_t i = lane; i < MS; i += kWave) {
-        const int cg = sl * S + int(i % S);
-        if (cg < a.hd) gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+    if (RES) {
+        __syncthreads();
+        for (int64_t i = lane; i < MS; i += kWave) {
+            const int cg = sl * S + int(i % S);
+            if (cg < a.hd) gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+        }
     }
 }
 
@@ -835,9 +842,9 @@ hipError_t set_bwd_attrs() {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_sweep_kernel<kBwdBlock, T>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(bwd_lds_bytes(kMaxWidth, kWave, 0, false)));
-    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1, 4, T>),
-                         reinterpret_cast<const void *>(bwd_res_kernel<2, 2, T>),
-                         reinterpret_cast<const void *>(bwd_res_kernel<4, 1, T>)};
+    const void *res[] = {reinterpret_cast<const void *>(bwd_res_kernel<1, 4, T, true>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<2, 2, T, true>),
+                         reinterpret_cast<const void *>(bwd_res_kernel<4, 1, T, true>)};
     for (const void *f : res)
         if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdMaxLds);
     if (e == hipSuccess)
@@ -851,23 +858,27 @@ hipError_t bwd_prepare() {
     return e == hipSuccess ? set_bwd_attrs<bf16>() : e;
 }
 
-// Entries of each kind per lane of the resident sweep: the smallest of 1, 2, 4 that covers
-// max(W, R) with 64 / S entry groups, or 0 where none does.
-int bwd_res_entries(int W, int R, int S) {
+// Entries of each kind per lane of the one-wavefront sweep: the smallest power of two up to
+// kj_max that covers max(W, R) with 64 / S entry groups, or 0 where none does.
+int bwd_res_entries(int W, int R, int S, int kj_max) {
     const int E = kWave / S, m = W > R ? W : R;
-    for (int kj = 1; kj <= 4; kj <<= 1)
+    for (int kj = 1; kj <= kj_max; kj <<= 1)
         if (kj * E >= m) return kj;
     return 0;
 }
 
-// Columns per slice: the widest power of two up to 64 (and up to the head) that still
-// gives 256 workgroups, else 4. SDM_BWD_SLICE (4, 8, 16, 32 or 64) overrides it, for tests
-// and tuning sweeps (the results depend on it only through the order of the column sums).
-int bwd_slice_cols(int P, int hd) {
+// Columns per slice, from shapes only: 4 where a token has at most kWaveMaxSlots slots of
+// each kind (the one-wavefront sweeps: 16 entry groups per wavefront, and many workgroups
+// whose chains hide each other's latency); otherwise the widest power of two up to 64 (and
+// up to the head) that still gives 256 workgroups, else 4. SDM_BWD_SLICE (4, 8, 16, 32 or 64)
+// overrides it, for tests and tuning sweeps (the results depend on it only through the
+// order of the column sums).
+int bwd_slice_cols(int P, int hd, int W, int R) {
     if (const char *env = getenv("SDM_BWD_SLICE")) {
         const int s = atoi(env);
         if (s == 4 || s == 8 || s == 16 || s == 32 || s == 64) return s;
     }
+    if ((W > R ? W : R) <= kWaveMaxSlots) return 4;
     int S = 4;
     while (S < 64 && S < hd) S <<= 1;
     while (S > 4 && int64_t(P) * ((hd + S - 1) / S) < 256) S >>= 1;
@@ -881,7 +892,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
     bwd_lead_kernel<T><<<dim3(unsigned(toks)), dim3(kBwdBlock), 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (std::is_same<T, bf16>::value && !a.res) {
+    if (std::is_same<T, bf16>::value && a.res <= 0) {   // rows in memory: widen the bank first
         const int64_t n = (a.bstride ? int64_t(a.P) : 1) * a.M * a.hd;
         const int64_t blocks = (n + kBwdBlock - 1) / kBwdBlock;
         bwd_widen_kernel<<<dim3(unsigned(blocks < 4096 ? blocks : 4096)), dim3(kBwdBlock), 0, st>>>(
@@ -895,12 +906,17 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st, hipEvent_t *ev) {
     }
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     const dim3 grid(unsigned(a.P * a.NS));
-    const size_t lds = bwd_lds_bytes(a.W, a.S, a.M, a.res != 0);
+    const size_t lds = a.res > 0 ? bwd_lds_bytes(a.W, a.S, a.M, true)
+                     : a.res < 0 ? size_t(kResRed) * sizeof(float) : bwd_lds_bytes(a.W, a.S, a.M, false);
     if (a.pair) bwd_res_pair_kernel<4, T><<<grid, dim3(kWave), lds, st>>>(a);
     else switch (a.res) {
-        case 1: bwd_res_kernel<1, 4, T><<<grid, dim3(kWave), lds, st>>>(a); break;
-        case 2: bwd_res_kernel<2, 2, T><<<grid, dim3(kWave), lds, st>>>(a); break;
-        case 4: bwd_res_kernel<4, 1, T><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 1: bwd_res_kernel<1, 4, T, true><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 2: bwd_res_kernel<2, 2, T, true><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case 4: bwd_res_kernel<4, 1, T, true><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case -1: bwd_res_kernel<1, 4, T, false><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case -2: bwd_res_kernel<2, 4, T, false><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case -4: bwd_res_kernel<4, 2, T, false><<<grid, dim3(kWave), lds, st>>>(a); break;
+        case -8: bwd_res_kernel<8, 2, T, false><<<grid, dim3(kWave), lds, st>>>(a); break;
         default: bwd_sweep_kernel<kBwdBlock, T><<<grid, dim3(kBwdBlock), lds, st>>>(a); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;

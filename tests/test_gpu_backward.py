@@ -80,15 +80,19 @@ CASES = [
 ]
 
 
-@pytest.fixture(params=["pair", "lds", "memory"])
+@pytest.fixture(params=["pair", "lds", "memory", "block"])
 def residency(request, monkeypatch):
     """pair: the default (slices in LDS where they fit, tokens in pairs where a token's entries
     fill at most half the entry groups); lds: slices in LDS, one token per step
-    (SDM_BWD_PAIR=0); memory: rows always read and written in memory (SDM_BWD_RES=0)."""
-    for var in ("SDM_BWD_RES", "SDM_BWD_PAIR"):
+    (SDM_BWD_PAIR=0); memory: one wavefront per slice on rows in memory where a lane covers
+    its entries in at most 8, else the 256-thread sweep (SDM_BWD_RES=0); block: always the
+    256-thread sweep (SDM_BWD_RES=0, SDM_BWD_WAVE=0)."""
+    for var in ("SDM_BWD_RES", "SDM_BWD_PAIR", "SDM_BWD_WAVE"):
         monkeypatch.delenv(var, raising=False)
-    if request.param == "memory":
+    if request.param in ("memory", "block"):
         monkeypatch.setenv("SDM_BWD_RES", "0")
+    if request.param == "block":
+        monkeypatch.setenv("SDM_BWD_WAVE", "0")
     elif request.param == "lds":
         monkeypatch.setenv("SDM_BWD_PAIR", "0")
     return request.param
@@ -141,8 +145,8 @@ def test_backward_reruns_are_bitwise_and_slices_agree(gpu, monkeypatch):
 @pytest.mark.parametrize("cfg,streams", [("2", (0, 17, 31)), ("3", (0, 9, 15))])
 def test_backward_full_size_sampled_streams(gpu, cfg, streams):
     """Configs 2 (bfloat16 bank, Zipf slots, 32 + 32 per token) and 3 (float32, ragged, 64 + 64
-    per token) at full size through the 256-thread sweep; every gradient of sampled streams
-    against O3 (each stream's gradients depend on that stream alone)."""
+    per token) at full size through the one-wavefront sweep on rows in memory; every gradient
+    of sampled streams against O3 (each stream's gradients depend on that stream alone)."""
     wl = workloads.CONFIGS[cfg]
     inp, gr, t, bank, got = _run(wl, gpu)
     _check(inp, gr, got, streams=streams)
@@ -193,11 +197,12 @@ def test_backward_wide_slices(gpu, S, monkeypatch):
     memory runs the same shapes."""
     wl = small(P=2, T=33, C=16, hd=100, M=60, W=3, R=4, ragged=True, index=22)
     monkeypatch.setenv("SDM_BWD_SLICE", S)
-    for res in (None, "0"):
-        if res is None:
-            monkeypatch.delenv("SDM_BWD_RES", raising=False)
-        else:
-            monkeypatch.setenv("SDM_BWD_RES", res)
+    for res, wave in ((None, None), ("0", None), ("0", "0")):
+        for var, val in (("SDM_BWD_RES", res), ("SDM_BWD_WAVE", wave)):
+            if val is None:
+                monkeypatch.delenv(var, raising=False)
+            else:
+                monkeypatch.setenv(var, val)
         inp, gr, t, bank, got = _run(wl, gpu, seed=int(S), dup_reads=True)
         _check(inp, gr, got)
         assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
