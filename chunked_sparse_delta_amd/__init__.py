@@ -29,7 +29,7 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
+__all__ = ["SdmError", "sdm_fwd", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
            "workspace_bytes", "plan",
            "library_path",
            "SDM_ERRORS"]
@@ -96,6 +96,9 @@ def _load():
             lib.sdm_fwd_workspace_bytes.argtypes = [i32] * 7
             lib.sdm_fwd_workspace_bytes.restype = sz
             lib.sdm_fwd.argtypes = [i32, i32, i32, p, p, p, p, i32, p, p, p, p, p]
+            for fn in (lib.sdm_fwd_phase1, lib.sdm_fwd_phase2):
+                fn.argtypes = [i32, i32, i32, p, p, p, p, i32, p, p, p, p, p]
+                fn.restype = ctypes.c_int
             lib.sdm_fwd.restype = ctypes.c_int
             lib.sdm_chunk_mats.argtypes = [i32, i32, i32, p, p, p, p, i32, i64, i32, i32, p, p, p, p, p, p, p, p]
             lib.sdm_chunk_mats.restype = ctypes.c_int
@@ -360,6 +363,43 @@ def sdm_write_read(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor,
                        valid_tokens=valid_tokens, shared_bank=shared_bank)
     return _SDMWriteRead.apply(bank, k_val, v, beta, log_decay, q_val, k_idx, q_idx, chunk, valid_tokens,
                                shared_bank)
+
+
+def _fwd_part(part: int, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, chunk, valid_tokens, out,
+              workspace, stream, shared_bank, repeated_writes):
+    lib = _load()
+    P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
+                                                   valid_tokens, shared_bank)
+    if repeated_writes is not None:
+        _expect(repeated_writes, "repeated_writes", (1,), torch.int64, bank.device)
+    if out is not None:
+        _expect(out, "out", (P, T, hd), bank.dtype, bank.device)
+    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 1 if bank.dim() == 2 else 0)
+    ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(), None, 0,
+               None if repeated_writes is None else repeated_writes.data_ptr())
+    fn = lib.sdm_fwd_phase1 if part == 1 else lib.sdm_fwd_phase2
+    rc = fn(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G, _ptr(v),
+            ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
+    _check_rc(lib, rc)
+
+
+def sdm_fwd_phase1(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, workspace: torch.Tensor, chunk: int = 64,
+                   valid_tokens=None, stream=None, shared_bank: bool = False, repeated_writes=None) -> None:
+    """The forward's Phase 1 and solve for every chunk into ``workspace`` (uint8, at least
+    workspace_bytes(..., slab_steps=0)): reads the slot ids, weights, gates, beta and
+    valid_tokens only (the bank gives its shape and dtype). Pair with sdm_fwd_phase2."""
+    _fwd_part(1, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, chunk=chunk, valid_tokens=valid_tokens,
+              out=None, workspace=workspace, stream=stream, shared_bank=shared_bank, repeated_writes=repeated_writes)
+
+
+def sdm_fwd_phase2(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, workspace: torch.Tensor, out: torch.Tensor,
+                   chunk: int = 64, valid_tokens=None, stream=None, shared_bank: bool = False) -> torch.Tensor:
+    """The forward's Phase 2 from a ``workspace`` filled by sdm_fwd_phase1 with the same
+    arguments (ordered before this call): advances ``bank`` in place and writes ``out``;
+    with the phase-1 call it gives exactly sdm_fwd's result."""
+    _fwd_part(2, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, chunk=chunk, valid_tokens=valid_tokens,
+              out=out, workspace=workspace, stream=stream, shared_bank=shared_bank, repeated_writes=None)
+    return out
 
 
 def chunk_mats(k_idx, k_val, beta, log_decay, q_idx, q_val, *, rows: int, head_dim: int, chunk: int,

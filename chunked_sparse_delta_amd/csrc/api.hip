@@ -342,15 +342,23 @@ size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32
     return size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
 }
 
-int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
-            const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank, const int32_t *valid_tokens,
-            void *out, const sdm_exec *exec) {
+}  // extern "C"
+
+namespace {
+
+// The forward's launch sequence. parts: 1 Phase 1 and the solve, 2 Phase 2, 3 both (sdm_fwd).
+// A call of one part needs the workspace to hold every step, so that Phase 1's outputs for
+// all chunks stay there for the Phase-2 call that follows it.
+int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,
+            const float *beta, const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank,
+            const int32_t *valid_tokens, void *out, const sdm_exec *exec) {
     g_err[0] = 0;
     if (!bank || !exec) return fail(SDM_ERR_NULL, "bank and exec must not be NULL");
     Checked ck;
     if (bank->shared != 0 && bank->shared != 1) return fail(SDM_ERR_SHAPE, "bank.shared must be 0 or 1, got %d", bank->shared);
+    const bool p1 = parts & 1, p2 = parts & 2;
     int rc = check_call(P, T, C, slots, weights, beta, log_decay, gate_width, v, bank->rows, bank->head_dim, bank->dtype,
-                        bank->data, bank->shared == 1, valid_tokens, out, true, &ck);
+                        bank->data, bank->shared == 1, valid_tokens, out, p2, &ck);
     if (rc) return rc;
     if (exec->repeated_writes && !aligned(exec->repeated_writes, 8))
         return fail(SDM_ERR_ALIGN, "the repeated-writes counter must be 8-byte aligned");
@@ -373,10 +381,14 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
     const int32_t Nt = ck.pb.Nt;
     int64_t slab64 = int64_t(exec->workspace_bytes / per_step);
     int32_t slab = slab64 > Nt ? Nt : int32_t(slab64);
+    if (parts != 3 && slab < Nt)
+        return fail(SDM_ERR_WORKSPACE, "a split forward needs the workspace of all %d steps (%zu bytes), got %zu", Nt,
+                    per_step * size_t(Nt), exec->workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(exec->stream);
     const bool fused = phase1_fused(ck.lay, C, dev->lds_per_block);
     hipEvent_t *ev = nullptr;
-    if (exec->events && exec->num_events >= SDM_TIMING_EVENTS) ev = reinterpret_cast<hipEvent_t *>(exec->events);
+    if (parts == 3 && exec->events && exec->num_events >= SDM_TIMING_EVENTS)
+        ev = reinterpret_cast<hipEvent_t *>(exec->events);
     for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
         Slab sl{};
         sl.ti0 = ti0;
@@ -387,19 +399,47 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
         float *w = reinterpret_cast<float *>(sl.ws);
         const WyArgs wa{w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X,
                         w + sl.lay.off_QX, C, sl.lay.words, sl.lay.words};
-        hipError_t e = launch_phase1(ck.pb, sl, st, sev, fused, wa);
-        if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
-        if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if (!fused) {
-            e = launch_wy(wa.A, wa.beta, wa.QK, wa.X, wa.QX, C, int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
-            if (e != hipSuccess) return hip_fail(e, "solve launch");
+        hipError_t e = hipSuccess;
+        if (p1) {
+            e = launch_phase1(ck.pb, sl, st, sev, fused, wa);
+            if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
+            if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if (!fused) {
+                e = launch_wy(wa.A, wa.beta, wa.QK, wa.X, wa.QX, C, int64_t(P) * sl.steps, sl.lay.words, sl.lay.words,
+                              st);
+                if (e != hipSuccess) return hip_fail(e, "solve launch");
+            }
         }
         if (sev && (e = hipEventRecord(sev[6], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        e = launch_phase2(ck.pb, sl, ck.V, geom, st);
-        if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
+        if (p2) {
+            e = launch_phase2(ck.pb, sl, ck.V, geom, st);
+            if (e != hipSuccess) return hip_fail(e, "phase 2 launch");
+        }
         if (sev && (e = hipEventRecord(sev[7], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
+            const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank, const int32_t *valid_tokens,
+            void *out, const sdm_exec *exec) {
+    return fwd_run(3, P, T, C, slots, weights, beta, log_decay, gate_width, v, bank, valid_tokens, out, exec);
+}
+
+int sdm_fwd_phase1(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,
+                   const float *beta, const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank,
+                   const int32_t *valid_tokens, void *out, const sdm_exec *exec) {
+    return fwd_run(1, P, T, C, slots, weights, beta, log_decay, gate_width, v, bank, valid_tokens, out, exec);
+}
+
+int sdm_fwd_phase2(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,
+                   const float *beta, const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank,
+                   const int32_t *valid_tokens, void *out, const sdm_exec *exec) {
+    return fwd_run(2, P, T, C, slots, weights, beta, log_decay, gate_width, v, bank, valid_tokens, out, exec);
 }
 
 }  // extern "C"

@@ -155,6 +155,28 @@ int sdm_fwd(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slo
             const int32_t *valid_tokens, void *out, const sdm_exec *exec);
 
 /*
+ * The forward in two calls, for callers that overlap the Phase 1 of one batch with the
+ * Phase 2 of another (Phase 1 reads only the slot ids, weights, gates, beta and
+ * valid_tokens, never the bank, v or out). Both take exactly sdm_fwd's arguments and
+ * checks; exec->workspace must hold all Nt steps (sdm_fwd_workspace_bytes(..., 0)), else
+ * SDM_ERR_WORKSPACE; exec->events is ignored.
+ * sdm_fwd_phase1: Phase 1 and the solve for every chunk, into the workspace (and the
+ *   repeated-writes counter); v, bank->data and out are not accessed (may be NULL).
+ * sdm_fwd_phase2: Phase 2 from that workspace; the caller orders it after the
+ *   sdm_fwd_phase1 call with the same arguments and workspace (same stream, or an event),
+ *   and keeps the workspace unchanged between the two.
+ * The pair computes exactly sdm_fwd's result (same bits).
+ */
+int sdm_fwd_phase1(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
+                   const sdm_weights *weights, const float *beta, const float *log_decay,
+                   int32_t gate_width, const void *v, const sdm_bank *bank,
+                   const int32_t *valid_tokens, void *out, const sdm_exec *exec);
+int sdm_fwd_phase2(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
+                   const sdm_weights *weights, const float *beta, const float *log_decay,
+                   int32_t gate_width, const void *v, const sdm_bank *bank,
+                   const int32_t *valid_tokens, void *out, const sdm_exec *exec);
+
+/*
  * Phase 1 and the solve only, for every chunk, into caller buffers (for checking the
  * intermediates; sdm_fwd keeps them in its workspace). Chunk (p, ti) is n = p * Nt + ti.
  *   rows, head_dim, dtype: the bank the call would run on (rows bounds the ids; dtype is

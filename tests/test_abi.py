@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["sdm_bwd", "sdm_bwd_workspace_bytes", "sdm_chunk_mats", "sdm_error_string",
-                                    "sdm_fwd", "sdm_fwd_plan",
+                                    "sdm_fwd", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_fwd_plan",
                                     "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_product_key_topk",
                                     "sdm_product_key_topk_backward", "sdm_wy_solve"]
 

@@ -332,3 +332,32 @@ def test_repeated_write_counter(gpu, fused, monkeypatch):
     cnt.zero_()
     gu.run(gu.to_torch(gen, gpu), wl.C, repeated_writes=cnt)
     assert int(cnt.item()) == 0
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=3, T=150, C=32, hd=24, M=40, W=5, R=4, dtype="bf16", ids="zipf", ragged=True, index=43),
+    small(P=2, T=130, C=64, hd=16, M=300, W=32, R=32, index=44),
+], ids=["bf16zipf", "w32"])
+def test_split_forward_gives_the_same_bits(gpu, wl):
+    """sdm_fwd_phase1 then sdm_fwd_phase2 (here on two streams ordered by an event, with
+    another call's Phase 2 between them on the second stream) equals sdm_fwd bit for bit;
+    a split call needs the workspace of every step."""
+    from chunked_sparse_delta_amd import SdmError, sdm_fwd_phase1, sdm_fwd_phase2, workspace_bytes
+    t = gu.to_torch(gu.generate(wl), gpu)
+    o_ref, b_ref = gu.run(t, wl.C)
+    ws = torch.empty(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0), dtype=torch.uint8, device=gpu)
+    bank = t["bank"].clone()
+    out = torch.empty_like(o_ref)
+    args = (t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"])
+    s1 = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    with torch.cuda.stream(s1):
+        sdm_fwd_phase1(bank, *args, workspace=ws, chunk=wl.C, valid_tokens=t["valid"], stream=s1)
+        ev.record(s1)
+    torch.cuda.current_stream().wait_event(ev)
+    sdm_fwd_phase2(bank, *args, workspace=ws, out=out, chunk=wl.C, valid_tokens=t["valid"])
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits(out), gu.bits(o_ref)) and np.array_equal(gu.bits(bank), gu.bits(b_ref))
+    small_ws = torch.empty(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 1), dtype=torch.uint8, device=gpu)
+    with pytest.raises(SdmError, match="all"):
+        sdm_fwd_phase1(bank, *args, workspace=small_ws, chunk=wl.C, valid_tokens=t["valid"])
