@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--workload", default="1", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--serial", action="store_true",
+                    help="time serial sdm_fwd calls only (default: batch k+1's Phase 1 overlaps batch k's Phase 2)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 launches)")
     ap.add_argument("--op", default="sdm_fwd", choices=("sdm_fwd", "sdm_bwd", "topk"),
@@ -368,7 +370,7 @@ def main():
         bench_bwd(args)
         return
     import torch
-    from chunked_sparse_delta_amd import TIMING_EVENTS, plan, sdm_fwd, workspace_bytes
+    from chunked_sparse_delta_amd import TIMING_EVENTS, plan, sdm_fwd, sdm_fwd_phase1, sdm_fwd_phase2, workspace_bytes
 
     wl = workloads.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
@@ -394,24 +396,68 @@ def main():
             arr[k] = ev.value
         ev_sets.append(arr)
 
+    fargs = (t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"])
+
     def step(events=None):
-        sdm_fwd(bank, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
-                chunk=wl.C, valid_tokens=t["valid"], out=out, workspace=ws, events=events)
+        sdm_fwd(bank, *fargs, chunk=wl.C, valid_tokens=t["valid"], out=out, workspace=ws, events=events)
+
+    # Overlapped steps: Phase 1 never reads the bank, so batch k+1's Phase 1 runs on a second
+    # stream (and a second workspace) while batch k's Phase 2 runs on the first; every step
+    # still runs both phases in full. Phase 1 of k+1 waits for a marker enqueued right before
+    # Phase 2 of k (so Phase 2's workgroups are placed first) and for Phase 2 of k-1 (which
+    # read the workspace it reuses).
+    ws_pair = [ws, torch.empty_like(ws)] if not args.serial else None
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    p1_done = [torch.cuda.Event(), torch.cuda.Event()]
+    p2_done = [torch.cuda.Event(), torch.cuda.Event()]
+    placed = [torch.cuda.Event(), torch.cuda.Event()]
+    marker = torch.zeros(1, device=dev)
+
+    def overlapped(K):
+        with torch.cuda.stream(side):
+            sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[0], chunk=wl.C, valid_tokens=t["valid"], stream=side)
+            p1_done[0].record(side)
+        for k in range(K):
+            b = k % 2
+            main.wait_event(p1_done[b])
+            marker.add_(1.0)
+            placed[b].record(main)
+            sdm_fwd_phase2(bank, *fargs, workspace=ws_pair[b], out=out, chunk=wl.C, valid_tokens=t["valid"],
+                           stream=main)
+            p2_done[b].record(main)
+            if k + 1 < K:
+                n = (k + 1) % 2
+                with torch.cuda.stream(side):
+                    side.wait_event(placed[b])
+                    if k >= 1:
+                        side.wait_event(p2_done[n])
+                    sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[n], chunk=wl.C, valid_tokens=t["valid"],
+                                   stream=side)
+                    p1_done[n].record(side)
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
+    if not args.serial:
+        overlapped(max(2, args.warmup))
     torch.cuda.synchronize()
     # The timed steps run without instrumentation; a second pass of the same steps records
     # the library's kernel-boundary events for the per-kernel breakdown (recording an event
     # costs GPU time of its own, so it stays out of the timed region).
-    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"bench: timing {args.steps} serial steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_serial = time.perf_counter() - t0
+    elapsed = elapsed_serial
+    if not args.serial:
+        print(f"bench: timing {args.steps} overlapped steps", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        overlapped(args.steps)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     print(f"bench: {args.steps} instrumented steps for the per-kernel times", file=sys.stderr, flush=True)
     for k in range(args.steps):
         step(ev_sets[k])
@@ -452,6 +498,9 @@ def main():
         "config": {"workload": workloads.workload_name(wl), "streams": wl.P, "tokens": wl.T, "chunk": wl.C,
                    "head_dim": wl.hd, "rows_per_stream": wl.M, "bank_dtype": wl.dtype, "W": wl.W, "R": wl.R,
                    "valid_tokens": tokens, "distinct_rows_read": stats["U"], "rows_written": stats["Uw"]},
+        "timing": ("serial sdm_fwd calls" if args.serial else
+                   "two streams: Phase 1 of batch k+1 overlaps Phase 2 of batch k (sdm_fwd_phase1/2, same bits)"),
+        "ms_per_step_serial": round(1000.0 * elapsed_serial / args.steps, 4),
         "kernel_ms": kern_ms,
         "plan": plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, bank.dtype),
         "roofline": roof,

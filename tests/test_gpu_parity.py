@@ -361,3 +361,48 @@ def test_split_forward_gives_the_same_bits(gpu, wl):
     small_ws = torch.empty(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 1), dtype=torch.uint8, device=gpu)
     with pytest.raises(SdmError, match="all"):
         sdm_fwd_phase1(bank, *args, workspace=small_ws, chunk=wl.C, valid_tokens=t["valid"])
+
+
+@pytest.mark.gpu
+def test_overlapped_batches_give_the_same_bits(gpu):
+    """Batches run back to back with batch k+1's Phase 1 on a second stream (and workspace)
+    overlapping batch k's Phase 2 give, batch by batch, sdm_fwd's readings and bank bits."""
+    from chunked_sparse_delta_amd import sdm_fwd_phase1, sdm_fwd_phase2, workspace_bytes
+    base = small(P=3, T=150, C=32, hd=24, M=40, W=5, R=4, dtype="bf16", ids="zipf", ragged=True, index=45)
+    batches = [gu.to_torch(gu.generate(base.replace(index=45 + k)), gpu) for k in range(3)]
+    keys = ("k_idx", "k_val", "v", "beta", "log_decay", "q_idx", "q_val")
+    bank_ref = batches[0]["bank"].clone()
+    refs = []
+    for t in batches:
+        o, _ = gu.run(t, base.C, bank=bank_ref)
+        refs.append((gu.bits(o), gu.bits(bank_ref)))
+    nb = workspace_bytes(base.P, base.T, base.C, base.W, base.R, base.hd, 0)
+    ws = [torch.empty(nb, dtype=torch.uint8, device=gpu) for _ in range(2)]
+    bank = batches[0]["bank"].clone()
+    outs = [torch.empty((base.P, base.T, base.hd), dtype=bank.dtype, device=gpu) for _ in batches]
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    p1_done = [torch.cuda.Event() for _ in batches]
+    p2_done = [torch.cuda.Event() for _ in batches]
+    side.wait_stream(main)
+    # Phase 1 of batch 0, then for each k: Phase 2 of k on main, Phase 1 of k+1 on side
+    with torch.cuda.stream(side):
+        sdm_fwd_phase1(bank, *(batches[0][x] for x in keys), workspace=ws[0], chunk=base.C,
+                       valid_tokens=batches[0]["valid"], stream=side)
+        p1_done[0].record(side)
+    for k, t in enumerate(batches):
+        main.wait_event(p1_done[k])
+        sdm_fwd_phase2(bank, *(t[x] for x in keys), workspace=ws[k % 2], out=outs[k], chunk=base.C,
+                       valid_tokens=t["valid"], stream=main)
+        p2_done[k].record(main)
+        if k + 1 < len(batches):
+            nxt = batches[k + 1]
+            with torch.cuda.stream(side):
+                if k >= 1:
+                    side.wait_event(p2_done[k - 1])
+                sdm_fwd_phase1(bank, *(nxt[x] for x in keys), workspace=ws[(k + 1) % 2], chunk=base.C,
+                               valid_tokens=nxt["valid"], stream=side)
+                p1_done[k + 1].record(side)
+    torch.cuda.synchronize()
+    for k, (o_bits, b_bits) in enumerate(refs):
+        assert np.array_equal(gu.bits(outs[k]), o_bits), f"readings of batch {k}"
+    assert np.array_equal(gu.bits(bank), refs[-1][1])
