@@ -87,6 +87,10 @@ __device__ __forceinline__ T *at(T *base, uint32_t off) {
 __host__ __device__ inline int p2_pitch(int cw) { return ((cw + 3) & ~3) + 4; }
 __host__ __device__ inline int p2_rows(int C) { return (C + 15) & ~15; }
 
+// s_waitcnt immediate of gfx9-family targets for vmcnt(0), expcnt and lgkmcnt left at their
+// maxima (vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Workgroup barrier for data exchanged through LDS only: unlike __syncthreads() it does
 // not wait for this wave's outstanding global stores (the readings, the bank rows).
 __device__ __forceinline__ void lds_barrier() {
@@ -448,8 +452,8 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     const int nu = nstage >> 2;                               // 16-byte units of the staged block
     raw_t *vst = reinterpret_cast<raw_t *>(stg + nstage);
     // Prefetch (SM, a staged block of at most one round of kStageUnits units per thread):
-    // the next step's block and vector of v are loaded into registers during this step's
-    // DW, and stored to LDS after its final barrier.
+    // the next step's block and vector of v are loaded into registers at the start of this
+    // step, and stored to LDS after its final barrier.
     const bool pf = SM && nu <= BLOCK * kStageUnits;
     // RB: [M][CW] elements of the bank slice, after v's vectors
     T *lbank = reinterpret_cast<T *>(reinterpret_cast<char *>(vst) + p2_vst_bytes(C, NV, V, int(sizeof(T))));
@@ -523,6 +527,32 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 lds_store_vec<V>(ub + (nl + i / NV) * pitch + (i % NV) * V, z);
             }
         }
+
+        // the next step's staged block and vector of v, loaded now and held in registers
+        // through the gather, the matmul and the DW (the loads' latency stays off the step)
+        const bool pfn = pf && s + 1 < a.steps;
+        uint4 pf0, pf1, pf2, pf3;
+        raw_t pfv;
+        bool pfvok = false;
+        if constexpr (SM) {
+            // Nothing loaded before this point is still needed. An explicit wait on every
+            // path retires it, so that the compiler's wait tracking (which merges the paths
+            // of predicated loads and stores) cannot make a later instruction of this step
+            // wait for the loads below as well.
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            if (pfn) {
+                // unconditional loads (clamped in-bounds indices), as in the gather
+                const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.words + a.off_stage0);
+                pf0 = src[min(tid, nu - 1)];
+                pf1 = src[min(tid + BLOCK, nu - 1)];
+                pf2 = src[min(tid + 2 * BLOCK, nu - 1)];
+                pf3 = src[min(tid + 3 * BLOCK, nu - 1)];
+                const int rows_n = min(C, a.T - (ti + 1) * C), vt = tid / NV, vv = tid % NV;
+                pfvok = tid < C * NV && vt < rows_n && vv < nvs;
+                pfv = Vec<T, V>::load_raw(at(vin, pfvok ? uint32_t((C + vt) * hd + col0 + vv * V) : uint32_t(C * hd + col0)));
+            }
+        }
+
 
         // ---- gather: u (staged; retrieved otherwise) -> ub, inter -> ib (live tokens)
         {
@@ -691,25 +721,6 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                     *reinterpret_cast<float4 *>(db + ti_row * pitch + co) = make_float4(dacc[q][0], dacc[q][1], dacc[q][2], dacc[q][3]);
             }
             lds_barrier();
-        }
-
-        // the next step's staged block and vector of v, loaded under the DW
-        const bool pfn = pf && s + 1 < a.steps;
-        uint4 pf0, pf1, pf2, pf3;
-        raw_t pfv;
-        bool pfvok = false;
-        if constexpr (SM) {
-            if (pfn) {
-                // unconditional loads (clamped in-bounds indices), as in the gather
-                const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.words + a.off_stage0);
-                pf0 = src[min(tid, nu - 1)];
-                pf1 = src[min(tid + BLOCK, nu - 1)];
-                pf2 = src[min(tid + 2 * BLOCK, nu - 1)];
-                pf3 = src[min(tid + 3 * BLOCK, nu - 1)];
-                const int rows_n = min(C, a.T - (ti + 1) * C), vt = tid / NV, vv = tid % NV;
-                pfvok = tid < C * NV && vt < rows_n && vv < nvs;
-                pfv = Vec<T, V>::load_raw(at(vin, pfvok ? uint32_t((C + vt) * hd + col0 + vv * V) : uint32_t(C * hd + col0)));
-            }
         }
 
         // ---- DW: one writer per written row. Groups with >= kHotMin members go to whole
