@@ -121,6 +121,35 @@ def test_forward_g_positive(gpu):
     gu.parity(out, bank, inp, wl.C, "g>0")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_values(gpu, dtype):
+    """Inputs at the method's degenerate values, mixed in one call: beta = 0 (a token that
+    only decays its rows), beta = 1 with one unit write weight (the row replaced by v),
+    zero write or read weights, zero log-decays (no decay), v = 0, and a bank of zeros in
+    one stream. The oracle decides every case."""
+    wl = small(P=3, T=90, C=32, hd=16, M=24, W=4, R=3, dtype=dtype, index=46)
+    inp = gu.generate(wl)
+    one = 0x3F80 if dtype == "bf16" else 1.0    # bfloat16 arrays hold bit patterns
+    beta = inp["beta"]
+    beta[:, 0::7] = 0.0
+    beta[:, 3::11] = 1.0
+    kv = inp["k_val"]
+    kv[:, 3::11, :] = 0
+    kv[:, 3::11, 0] = one
+    kv[:, 5::9, 1] = 0
+    qv = inp["q_val"]
+    qv[:, 2::5, :] = 0
+    qv[:, 4::13, 1] = 0
+    g = inp["log_decay"]
+    g[:, 10:40] = 0.0
+    g[1] = 0.0
+    v = inp["v"]
+    v[:, 6::8] = 0
+    inp["bank"][2] = 0
+    out, bank = gu.run(gu.to_torch(inp, gpu), wl.C)
+    gu.parity(out, bank, inp, wl.C, f"degenerate {dtype}")
+
+
 def test_all_padding_and_zero_valid(gpu):
     wl = small(P=3, T=40, C=16, hd=8, M=16, W=2, R=2, index=22)
     inp = gu.generate(wl)
