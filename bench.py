@@ -403,37 +403,37 @@ def main():
 
     # Overlapped steps: Phase 1 never reads the bank, so batch k+1's Phase 1 runs on a second
     # stream (and a second workspace) while batch k's Phase 2 runs on the first; every step
-    # still runs both phases in full. Phase 1 of k+1 waits for a marker enqueued right before
-    # Phase 2 of k (so Phase 2's workgroups are placed first) and for Phase 2 of k-1 (which
-    # read the workspace it reuses).
+    # still runs both phases in full. Phase 1 of k+1 waits for Phase 2 of k-1 (which read the
+    # workspace it reuses) and then for a one-element marker kernel on its own stream: by the
+    # time the marker has run, Phase 2 of k (ready since Phase 1 of k ended) has been
+    # dispatched, so Phase 2's workgroups are placed first and Phase 1 fills the idle CUs.
     ws_pair = [ws, torch.empty_like(ws)] if not args.serial else None
     main, side = torch.cuda.current_stream(), torch.cuda.Stream()
     p1_done = [torch.cuda.Event(), torch.cuda.Event()]
     p2_done = [torch.cuda.Event(), torch.cuda.Event()]
-    placed = [torch.cuda.Event(), torch.cuda.Event()]
     marker = torch.zeros(1, device=dev)
 
     def overlapped(K):
+        side.wait_stream(main)
         with torch.cuda.stream(side):
             sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[0], chunk=wl.C, valid_tokens=t["valid"], stream=side)
             p1_done[0].record(side)
         for k in range(K):
             b = k % 2
             main.wait_event(p1_done[b])
-            marker.add_(1.0)
-            placed[b].record(main)
             sdm_fwd_phase2(bank, *fargs, workspace=ws_pair[b], out=out, chunk=wl.C, valid_tokens=t["valid"],
                            stream=main)
             p2_done[b].record(main)
             if k + 1 < K:
                 n = (k + 1) % 2
                 with torch.cuda.stream(side):
-                    side.wait_event(placed[b])
                     if k >= 1:
                         side.wait_event(p2_done[n])
+                    marker.add_(1.0)
                     sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[n], chunk=wl.C, valid_tokens=t["valid"],
                                    stream=side)
                     p1_done[n].record(side)
+        main.wait_stream(side)
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
