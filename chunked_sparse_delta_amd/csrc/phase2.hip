@@ -31,6 +31,7 @@
 //           and the classes combine as ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7));
 //   matmul  16-wide k blocks ascending, each one MFMA chain of four k-steps;
 //   DW      decay term first, then the group's members in token order.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -450,6 +451,9 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     float *stg = ib + (SM ? 2 : 1) * CP * pitch;   // SM: the staged block, then [C][NV] vectors of v
     const int nstage = a.off_stage1 - a.off_stage0;           // words (a multiple of 64)
     const int nu = nstage >> 2;                               // 16-byte units of the staged block
+    // the block starts with the DW's records (group, member and big-group records), read
+    // only by the DW; the gather and matmul inputs follow
+    const int nudw = (a.off_gw - a.off_stage0) >> 2;
     raw_t *vst = reinterpret_cast<raw_t *>(stg + nstage);
     // Prefetch (SM, a staged block of at most one round of kStageUnits units per thread):
     // the next step's block and vector of v are loaded into registers at the start of this
@@ -497,7 +501,9 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         T *out = static_cast<T *>(a.out) + tok0 * hd;
         if constexpr (SM) {
           uint4 *dst = reinterpret_cast<uint4 *>(stg);
-          if (s == 0 || !pf) {   // otherwise the previous step has stored this one's block
+          // otherwise the previous step has stored this one's block: the gather and matmul
+          // inputs during its DW, the DW records after its final barrier
+          if (s == 0 || !pf) {
             const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.off_stage0);
             const int vt = tid / NV, vv = tid % NV;
             const bool vok = tid < C * NV && vt < rows && vv < nvs;
@@ -517,8 +523,8 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 if (u0 + 3 * BLOCK < nu) dst[u0 + 3 * BLOCK] = t3;
             }
             if (vok) vst[tid] = vr;
-          }
             lds_barrier();
+          }
             // u rows of padding tokens and rows C..CP-1: +0 (the gather writes rows < nl)
             for (int i = tid; i < (CP - nl) * NV; i += BLOCK) {
                 float z[V];
@@ -609,6 +615,18 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             lds_store_vec<V>(ur, uu);
         }
         lds_barrier();
+        }
+
+        // Staged, the DW's group counts are read now: the next step's block overwrites the
+        // chunk's meta words during the DW.
+        int32_t dw_ng = 0, dw_nbig = 0;
+        if constexpr (SM) {
+            const int32_t *meta = reinterpret_cast<const int32_t *>(arr(a.off_meta));
+            if (nl > 0) {
+                dw_ng = meta[2];
+                dw_nbig = meta[4];
+            }
+            asm volatile("" : "+v"(dw_ng), "+v"(dw_nbig));
         }
 
         // ---- dual matmul on the matrix cores: readings to memory, delta_v to db
@@ -710,6 +728,18 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         if (full) matmul(std::true_type{});
         else matmul(std::false_type{});
         lds_barrier();
+        if constexpr (SM) {
+            // Every gather and matmul input of this step has been read: the next step's
+            // (units from nudw on, and its vectors of v) take their place during the DW.
+            if (pfn) {
+                uint4 *dst = reinterpret_cast<uint4 *>(stg);
+                if (tid >= nudw && tid < nu) dst[tid] = pf0;
+                if (tid + BLOCK >= nudw && tid + BLOCK < nu) dst[tid + BLOCK] = pf1;
+                if (tid + 2 * BLOCK >= nudw && tid + 2 * BLOCK < nu) dst[tid + 2 * BLOCK] = pf2;
+                if (tid + 3 * BLOCK >= nudw && tid + 3 * BLOCK < nu) dst[tid + 3 * BLOCK] = pf3;
+                if (pfvok) vst[tid] = pfv;
+            }
+        }
         if constexpr (!SM) {   // delta_v over inter, now that every tile has read it
 #pragma unroll
             for (int q = 0; q < Cfg::kMaxTiles; ++q) {
@@ -731,8 +761,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         {
             int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
             asm volatile("" : "+v"(dlane));
-            const int32_t *meta = reinterpret_cast<const int32_t *>(arr(a.off_meta));
-            const int32_t ng = nl > 0 ? meta[2] : 0, nbig = nl > 0 ? meta[4] : 0;
+            if constexpr (!SM) {
+                const int32_t *meta = reinterpret_cast<const int32_t *>(arr(a.off_meta));
+                if (nl > 0) {
+                    dw_ng = meta[2];
+                    dw_nbig = meta[4];
+                }
+            }
+            const int32_t ng = dw_ng, nbig = dw_nbig;
             const int4 *grec = reinterpret_cast<const int4 *>(arr(a.off_grec));
             const int4 *brec = reinterpret_cast<const int4 *>(arr(a.off_brec));
             const int2 *mrec = reinterpret_cast<const int2 *>(arr(a.off_mrec));
@@ -826,13 +862,12 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         }
         step_end_barrier<RB>();   // the DW's bank stores are visible to the next step's gather
         if constexpr (SM) {
-            if (pfn) {   // the DW has read its records: the next step's block takes their place
+            if (pfn) {   // the DW has read its records: the next step's take their place
                 uint4 *dst = reinterpret_cast<uint4 *>(stg);
-                if (tid < nu) dst[tid] = pf0;
-                if (tid + BLOCK < nu) dst[tid + BLOCK] = pf1;
-                if (tid + 2 * BLOCK < nu) dst[tid + 2 * BLOCK] = pf2;
-                if (tid + 3 * BLOCK < nu) dst[tid + 3 * BLOCK] = pf3;
-                if (pfvok) vst[tid] = pfv;
+                if (tid < nudw) dst[tid] = pf0;
+                if (tid + BLOCK < nudw) dst[tid + BLOCK] = pf1;
+                if (tid + 2 * BLOCK < nudw) dst[tid + 2 * BLOCK] = pf2;
+                if (tid + 3 * BLOCK < nudw) dst[tid + 3 * BLOCK] = pf3;
             }
         }
     }
@@ -904,6 +939,14 @@ int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, i
 
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st) {
     const ChunkLayout &L = sl.lay;
+    // The staged modes replace the block's leading DW records and the rest at different
+    // points of a step: the DW reads nothing at or past off_gw, the gather and matmul nothing
+    // before it.
+    const int64_t dw_end = std::max({L.off_grec + 4 * L.E, L.off_mrec + 2 * L.E, L.off_brec + 4 * L.HMAX});
+    if (L.off_grec != L.off_stage0 || dw_end > L.off_gw || L.off_gr < L.off_gw || L.off_kid < L.off_gw ||
+        L.off_qid < L.off_gw || L.off_meta < L.off_gw || L.off_beta < L.off_gw || L.off_X < L.off_gw ||
+        L.off_QX < L.off_gw)
+        return hipErrorInvalidValue;
     P2Args a{};
     a.v = pb.v; a.bank = pb.bank; a.out = pb.out; a.valid = pb.valid;
     a.ws = sl.ws; a.M = pb.M; a.words = L.words; a.bstride = pb.bank_stride;
