@@ -199,8 +199,8 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
 
     // (k, j) of the first slot of the next batch whose pairs are to be loaded
     int pk = 0, pj = 0;
-    int32_t id[kBatch][Q], nid[kBatch][Q];
-    float wt[kBatch][Q], nwt[kBatch][Q];
+    int32_t id[kBatch][Q], nid[kBatch][Q] = {};
+    float wt[kBatch][Q], nwt[kBatch][Q] = {};
     // Every load below is issued unconditionally (an unused slot reads entry 0, row 0 or the
     // slice's first vector, all in bounds), so that the compiler can count the loads in
     // flight exactly; a load under a branch makes it wait for all of them.
@@ -243,7 +243,9 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
                 raw[u][q] = Vec<T, V>::load_raw(
                     at(bank, uint32_t(ok ? id[u][q] : 0) * uint32_t(hd) + (vok ? col : uint32_t(col0))));
             }
-        load_pairs(nid, nwt);
+        // staged, ids and weights come from LDS: a wave-uniform branch skips the loads past
+        // the last batch without making any memory load wait
+        if (!UFT || i0 + kBatch < total) load_pairs(nid, nwt);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             if (i0 + u >= total) continue;
@@ -809,8 +811,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                     mr[u] = two ? x : make_int2(0, 0);
                 }
                 int4 nrec[kB];
+                // records in LDS (staged): the loads past the last batch are skipped
+                if (!SM || gb + kStride < ng) {
 #pragma unroll
-                for (int u = 0; u < kB; ++u) nrec[u] = load_rec(gb + kStride + u * NW * GPI + gs);
+                    for (int u = 0; u < kB; ++u) nrec[u] = load_rec(gb + kStride + u * NW * GPI + gs);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kB; ++u) nrec[u] = make_int4(-1, 0, 0, 0);
+                }
 #pragma unroll
                 for (int u = 0; u < kB; ++u) {
                     if (!small(rec[u])) continue;
