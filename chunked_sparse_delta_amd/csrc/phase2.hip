@@ -67,9 +67,12 @@ struct P2Args {
     int32_t off_kid, off_qid, off_stage0, off_stage1;
 };
 
-__device__ __forceinline__ int32_t live_tokens(const P2Args &a, int p, int ti) {
-    int32_t vt = a.valid ? a.valid[p] : a.T;
-    vt = vt < 0 ? 0 : (vt > a.T ? a.T : vt);
+// Live tokens of stream p (valid_tokens clamped to [0, T]), and of its chunk ti.
+__device__ __forceinline__ int32_t stream_tokens(const P2Args &a, int p) {
+    const int32_t vt = a.valid ? a.valid[p] : a.T;
+    return vt < 0 ? 0 : (vt > a.T ? a.T : vt);
+}
+__device__ __forceinline__ int32_t chunk_tokens(const P2Args &a, int32_t vt, int ti) {
     const int32_t n = vt - ti * a.C;
     return n < 0 ? 0 : (n > a.C ? a.C : n);
 }
@@ -480,6 +483,10 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     // so that every wave gets a similar share of the triangular work.
     const int NIT = CP / 16, NCT = (cwv + 15) / 16, NT = NIT * NCT;
 
+    // the stream's live tokens, read once (the compiler cannot prove that the kernel's own
+    // stores leave valid_tokens unchanged, and would reload it every step)
+    const int32_t vtp = stream_tokens(a, p);
+
     for (int s = 0; s < a.steps; ++s) {
         // Thread ids are re-read opaquely every step, so that the per-lane address
         // arithmetic of all phases is not hoisted out of the step loop (it would be held
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             if constexpr (SM) return reinterpret_cast<const uint32_t *>(stg) + (off - a.off_stage0);
             else return cbg + off;
         };
-        const int nl = live_tokens(a, p, ti);
+        const int nl = chunk_tokens(a, vtp, ti);
         const int rows = min(C, a.T - ti * C);
         const int64_t tok0 = int64_t(p) * a.T + int64_t(ti) * C;
         const T *vin = static_cast<const T *>(a.v) + tok0 * hd;     // this chunk's rows of v and out
