@@ -457,10 +457,11 @@ constexpr int kReadWaves = 4;
 // lspk, lsgh, lbst, lqid, lqv: copies of the sorted member records, the lookup records, the
 // bucket starts and the chunk's read ids and weights (in LDS for the fused kernel), or
 // nullptr to read the workspace and the inputs.
-__device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr,
-                                            const int4 *lspk = nullptr, const int4 *lsgh = nullptr,
-                                            const int32_t *lbst = nullptr, const int32_t *lqid = nullptr,
-                                            const float *lqv = nullptr) {
+// KR: reads per lane (ceil(R / 64), rounded up to 1, 2 or 4).
+template <int KR>
+__device__ __forceinline__ void reads_token_k(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr,
+                                              const int4 *lspk, const int4 *lsgh, const int32_t *lbst,
+                                              const int32_t *lqid, const float *lqv) {
     const int lane = threadIdx.x & 63;
     const ChunkLayout &L = sl.lay;
     const int R = pb.R, C = pb.C;
@@ -481,38 +482,71 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
     __builtin_amdgcn_wave_barrier();
     const int64_t tg = int64_t(p) * pb.T + int64_t(ti) * C + i;
     const int bsh = bucket_shift(pb, L.E);
-    for (int r0 = 0; r0 < R; r0 += kWave) {
-        const int r = r0 + lane;
+    // A lane's reads (r = lane, lane + 64, ...) are looked up together: their loads are
+    // issued side by side and their searches advance in lockstep, so one chain of
+    // dependent round trips serves all of them. Every load reads an in-bounds element
+    // (index 0 for a read without work).
+    const int nr = (R + kWave - 1) / kWave;   // <= KR
+    const bool live = i < nl;
+    int32_t q[KR], lo[KR], hi[KR], b0[KR];
+    float qv[KR];
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        const int r = k * kWave + lane;
+        const bool ok = k < nr && r < R && live;
+        const int64_t x = ok ? tg * R + r : 0;
+        q[k] = lqid ? lqid[ok ? i * R + r : 0] : load_id(pb.q_idx, x, pb.q_id8);
+        qv[k] = lqv ? lqv[ok ? i * R + r : 0] : load_weight(pb.q_val, x, pb.dtype);
+        const int32_t b = min(int32_t(uint32_t(q[k]) >> bsh), int32_t(L.NB) - 1);
+        b0[k] = bstart[b];
+        hi[k] = bstart[b + 1];
+        if (!ok) hi[k] = b0[k];
+        lo[k] = b0[k];
+    }
+    // the last sorted position with (slot, token) <= (q, i), in each read's bucket
+    for (;;) {
+        bool act = false;
+#pragma unroll
+        for (int k = 0; k < KR; ++k) act |= lo[k] < hi[k];
+        if (!__any(act)) break;
+        int4 pk[KR];
+#pragma unroll
+        for (int k = 0; k < KR; ++k) pk[k] = spk[lo[k] < hi[k] ? (lo[k] + hi[k]) >> 1 : 0];
+#pragma unroll
+        for (int k = 0; k < KR; ++k) {
+            if (lo[k] < hi[k]) {
+                const int32_t mid = (lo[k] + hi[k]) >> 1;
+                if (pk[k].x < q[k] || (pk[k].x == q[k] && pk[k].y <= i)) lo[k] = mid + 1;
+                else hi[k] = mid;
+            }
+        }
+    }
+    int4 pk[KR], gh[KR];
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        const int32_t pos = lo[k] - 1;
+        pk[k] = spk[pos >= b0[k] ? pos : 0];
+        gh[k] = sgh[pos >= b0[k] ? pos : 0];   // group head, hot index, the head's L
+    }
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        if (k >= nr) break;
+        const int r = k * kWave + lane;
         const bool ok = r < R;
         float g = 0.0f, rv = 0.0f;
         int32_t h = -1;
         int4 cr = make_int4(0, 0, 0, 0);
-        if (ok && i < nl) {
-            const int32_t q = lqid ? lqid[i * R + r] : load_id(pb.q_idx, tg * R + r, pb.q_id8);
-            qid[int64_t(i) * R + r] = q;   // ids in entry order, for Phase 2
-            const int32_t b = min(int32_t(uint32_t(q) >> bsh), int32_t(L.NB) - 1);
-            const int32_t b0 = bstart[b];
-            int32_t lo = b0, hi = bstart[b + 1];
-            while (lo < hi) {
-                const int32_t mid = (lo + hi) >> 1;
-                const int4 pk = spk[mid];
-                if (pk.x < q || (pk.x == q && pk.y <= i)) lo = mid + 1;
-                else hi = mid;
-            }
-            const int32_t pos = lo - 1;
-            const float qv = lqv ? lqv[i * R + r] : load_weight(pb.q_val, tg * R + r, pb.dtype);
+        if (ok && live) {
+            qid[int64_t(i) * R + r] = q[k];   // ids in entry order, for Phase 2
+            const int32_t pos = lo[k] - 1;
             float l = 0.0f;
-            if (pos >= b0) {
-                const int4 pk = spk[pos];
-                if (pk.x == q) {
-                    l = __int_as_float(pk.w);
-                    const int4 gh = sgh[pos];   // group head, hot index, the head's L
-                    h = gh.y;
-                    if (h >= 0) rv = qv * expf(l - __int_as_float(gh.z));
-                    else cr = make_int4(gh.x, pos + 1, __float_as_int(qv), pk.w);
-                }
+            if (pos >= b0[k] && pk[k].x == q[k]) {
+                l = __int_as_float(pk[k].w);
+                h = gh[k].y;
+                if (h >= 0) rv = qv[k] * expf(l - __int_as_float(gh[k].z));
+                else cr = make_int4(gh[k].x, pos + 1, __float_as_int(qv[k]), pk[k].w);
             }
-            g = qv * expf(l);
+            g = qv[k] * expf(l);
         }
         if (ok) {
             gr[int64_t(i) * R + r] = g;
@@ -527,6 +561,16 @@ __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, i
     }
     __builtin_amdgcn_wave_barrier();
     for (int h = lane; h < HP; h += kWave) Qa[int64_t(i) * HP + h] = qr[h];
+}
+
+__device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr,
+                                            const int4 *lspk = nullptr, const int4 *lsgh = nullptr,
+                                            const int32_t *lbst = nullptr, const int32_t *lqid = nullptr,
+                                            const float *lqv = nullptr) {
+    static_assert(kMaxWidth <= 4 * kWave, "at most four reads per lane");
+    if (pb.R <= kWave) reads_token_k<1>(pb, sl, n, i, qr, lspk, lsgh, lbst, lqid, lqv);
+    else if (pb.R <= 2 * kWave) reads_token_k<2>(pb, sl, n, i, qr, lspk, lsgh, lbst, lqid, lqv);
+    else reads_token_k<4>(pb, sl, n, i, qr, lspk, lsgh, lbst, lqid, lqv);
 }
 
 // The cold part of A (blockIdx.y = 0: write entries) or QK (blockIdx.y = 1: read
