@@ -421,7 +421,6 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
 
     // forward replay of token t from its prefetched values
     auto fwd_token = [&](ResTok<KJ> &cur, int t) {
-        const int64_t tok = tok0 + t;
         float old[KJ];
         float acc = 0.0f;
 #pragma unroll

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kTopkBlock) void topk_kernel(TopkArgs a) {
 // R registers; partners at distance >= 64 are the lane's own registers, nearer ones come
 // by lane shuffles. Only the per-wave LDS tables (factor ranks, stage lists, pair offsets)
 // are shared between lanes, with nothing but the wave's own in-order LDS accesses.
-constexpr int kTopkWaveFactor = 256, kTopkWaveK = 64, kTopkWavePairs = 512;   // >= 64 H(64) = 304
+constexpr int kTopkWaveFactor = 256, kTopkWaveK = 64;
 
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
     const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(x)), m, 64));
