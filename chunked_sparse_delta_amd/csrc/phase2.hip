@@ -413,7 +413,7 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
 //                Rows are held in the bank dtype, so every value is rounded exactly where
 //                the other modes round it on the way to memory: the bits are the same.
 constexpr int kP2Block = 1024;
-constexpr int kStageUnits = 4;   // 16-byte units of the staged block per thread per round
+constexpr int kStageUnits = 8;   // 16-byte units of the staged block per thread per round
 constexpr int kP2Global = 0, kP2Staged = 1, kP2Resident = 2;
 
 // Bytes of the staged copy of C x NV vectors of v, rounded up to 16 bytes.
@@ -463,7 +463,10 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
     // Prefetch (SM, a staged block of at most one round of kStageUnits units per thread):
     // the next step's block and vector of v are loaded into registers at the start of this
     // step, and stored to LDS after its final barrier.
-    const bool pf = SM && nu <= BLOCK * kStageUnits;
+    // Prefetch units per thread: 8 staged; 4 resident, whose blocks that fit beside the bank
+    // slice need no more (the loads of unused units would cost the step their issue time).
+    constexpr int PFU = RB ? 4 : kStageUnits;
+    const bool pf = SM && nu <= BLOCK * PFU;
     // RB: [M][CW] elements of the bank slice, after v's vectors
     T *lbank = reinterpret_cast<T *>(reinterpret_cast<char *>(vst) + p2_vst_bytes(C, NV, V, int(sizeof(T))));
     // the bank the gather and the DW work on: the slice in LDS (row stride CW) or in memory
@@ -521,15 +524,23 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
                 Vec<T, V>::load_raw(at(vin, vok ? uint32_t(vt * hd + col0 + vv * V) : uint32_t(col0)));
             // rounds of kStageUnits 16-byte loads in flight per thread, then their stores
             for (int u0 = tid; u0 < nu; u0 += BLOCK * kStageUnits) {
-                static_assert(kStageUnits == 4, "unrolled by hand");
-                const uint4 t0 = src[u0];
-                const uint4 t1 = src[min(u0 + BLOCK, nu - 1)];
+                static_assert(kStageUnits == 8, "unrolled by hand");
+                const uint4 t0 = src[min(u0 + 0 * BLOCK, nu - 1)];
+                const uint4 t1 = src[min(u0 + 1 * BLOCK, nu - 1)];
                 const uint4 t2 = src[min(u0 + 2 * BLOCK, nu - 1)];
                 const uint4 t3 = src[min(u0 + 3 * BLOCK, nu - 1)];
-                if (u0 < nu) dst[u0] = t0;
-                if (u0 + BLOCK < nu) dst[u0 + BLOCK] = t1;
+                const uint4 t4 = src[min(u0 + 4 * BLOCK, nu - 1)];
+                const uint4 t5 = src[min(u0 + 5 * BLOCK, nu - 1)];
+                const uint4 t6 = src[min(u0 + 6 * BLOCK, nu - 1)];
+                const uint4 t7 = src[min(u0 + 7 * BLOCK, nu - 1)];
+                if (u0 + 0 * BLOCK < nu) dst[u0 + 0 * BLOCK] = t0;
+                if (u0 + 1 * BLOCK < nu) dst[u0 + 1 * BLOCK] = t1;
                 if (u0 + 2 * BLOCK < nu) dst[u0 + 2 * BLOCK] = t2;
                 if (u0 + 3 * BLOCK < nu) dst[u0 + 3 * BLOCK] = t3;
+                if (u0 + 4 * BLOCK < nu) dst[u0 + 4 * BLOCK] = t4;
+                if (u0 + 5 * BLOCK < nu) dst[u0 + 5 * BLOCK] = t5;
+                if (u0 + 6 * BLOCK < nu) dst[u0 + 6 * BLOCK] = t6;
+                if (u0 + 7 * BLOCK < nu) dst[u0 + 7 * BLOCK] = t7;
             }
             if (vok) vst[tid] = vr;
             lds_barrier();
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         // the next step's staged block and vector of v, loaded now and held in registers
         // through the gather, the matmul and the DW (the loads' latency stays off the step)
         const bool pfn = pf && s + 1 < a.steps;
-        uint4 pf0, pf1, pf2, pf3;
+        uint4 pf0, pf1, pf2, pf3, pf4, pf5, pf6, pf7;
         raw_t pfv;
         bool pfvok = false;
         if constexpr (SM) {
@@ -558,10 +569,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             if (pfn) {
                 // unconditional loads (clamped in-bounds indices), as in the gather
                 const uint4 *src = reinterpret_cast<const uint4 *>(cbg + a.words + a.off_stage0);
-                pf0 = src[min(tid, nu - 1)];
-                pf1 = src[min(tid + BLOCK, nu - 1)];
+                pf0 = src[min(tid + 0 * BLOCK, nu - 1)];
+                pf1 = src[min(tid + 1 * BLOCK, nu - 1)];
                 pf2 = src[min(tid + 2 * BLOCK, nu - 1)];
                 pf3 = src[min(tid + 3 * BLOCK, nu - 1)];
+                if constexpr (PFU > 4) pf4 = src[min(tid + 4 * BLOCK, nu - 1)];
+                if constexpr (PFU > 4) pf5 = src[min(tid + 5 * BLOCK, nu - 1)];
+                if constexpr (PFU > 4) pf6 = src[min(tid + 6 * BLOCK, nu - 1)];
+                if constexpr (PFU > 4) pf7 = src[min(tid + 7 * BLOCK, nu - 1)];
                 const int rows_n = min(C, a.T - (ti + 1) * C), vt = tid / NV, vv = tid % NV;
                 pfvok = tid < C * NV && vt < rows_n && vv < nvs;
                 pfv = Vec<T, V>::load_raw(at(vin, pfvok ? uint32_t((C + vt) * hd + col0 + vv * V) : uint32_t(C * hd + col0)));
@@ -742,10 +757,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             // (units from nudw on, and its vectors of v) take their place during the DW.
             if (pfn) {
                 uint4 *dst = reinterpret_cast<uint4 *>(stg);
-                if (tid >= nudw && tid < nu) dst[tid] = pf0;
-                if (tid + BLOCK >= nudw && tid + BLOCK < nu) dst[tid + BLOCK] = pf1;
+                if (tid + 0 * BLOCK >= nudw && tid + 0 * BLOCK < nu) dst[tid + 0 * BLOCK] = pf0;
+                if (tid + 1 * BLOCK >= nudw && tid + 1 * BLOCK < nu) dst[tid + 1 * BLOCK] = pf1;
                 if (tid + 2 * BLOCK >= nudw && tid + 2 * BLOCK < nu) dst[tid + 2 * BLOCK] = pf2;
                 if (tid + 3 * BLOCK >= nudw && tid + 3 * BLOCK < nu) dst[tid + 3 * BLOCK] = pf3;
+                if constexpr (PFU > 4) if (tid + 4 * BLOCK >= nudw && tid + 4 * BLOCK < nu) dst[tid + 4 * BLOCK] = pf4;
+                if constexpr (PFU > 4) if (tid + 5 * BLOCK >= nudw && tid + 5 * BLOCK < nu) dst[tid + 5 * BLOCK] = pf5;
+                if constexpr (PFU > 4) if (tid + 6 * BLOCK >= nudw && tid + 6 * BLOCK < nu) dst[tid + 6 * BLOCK] = pf6;
+                if constexpr (PFU > 4) if (tid + 7 * BLOCK >= nudw && tid + 7 * BLOCK < nu) dst[tid + 7 * BLOCK] = pf7;
                 if (pfvok) vst[tid] = pfv;
             }
         }
@@ -879,10 +898,14 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         if constexpr (SM) {
             if (pfn) {   // the DW has read its records: the next step's take their place
                 uint4 *dst = reinterpret_cast<uint4 *>(stg);
-                if (tid < nudw) dst[tid] = pf0;
-                if (tid + BLOCK < nudw) dst[tid + BLOCK] = pf1;
+                if (tid + 0 * BLOCK < nudw) dst[tid + 0 * BLOCK] = pf0;
+                if (tid + 1 * BLOCK < nudw) dst[tid + 1 * BLOCK] = pf1;
                 if (tid + 2 * BLOCK < nudw) dst[tid + 2 * BLOCK] = pf2;
                 if (tid + 3 * BLOCK < nudw) dst[tid + 3 * BLOCK] = pf3;
+                if constexpr (PFU > 4) if (tid + 4 * BLOCK < nudw) dst[tid + 4 * BLOCK] = pf4;
+                if constexpr (PFU > 4) if (tid + 5 * BLOCK < nudw) dst[tid + 5 * BLOCK] = pf5;
+                if constexpr (PFU > 4) if (tid + 6 * BLOCK < nudw) dst[tid + 6 * BLOCK] = pf6;
+                if constexpr (PFU > 4) if (tid + 7 * BLOCK < nudw) dst[tid + 7 * BLOCK] = pf7;
             }
         }
     }
