@@ -222,6 +222,24 @@ P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int c
     return g;
 }
 
+// The geometry actually launched, and the vector width V it uses. For a bfloat16 bank whose
+// slice is resident in LDS, when slices of one 16-byte vector (8 columns) still leave more
+// than half of the CUs without a workgroup, 8-byte vectors (4 columns) are taken instead:
+// twice the workgroups, each with half the per-entry vector work (the step is bound by
+// instruction issue), and still room beside them for another batch's Phase 1. Slices never
+// change the bits. (Narrower still, 2 columns, measured no faster and fills every CU.)
+P2Geom plan_phase2_v(const Problem &pb, const ChunkLayout &L, int &V, int es, int cus, int lds_limit) {
+    const P2Geom g = plan_phase2(pb, L, V, es, cus, lds_limit);
+    if (es == 2 && V == 8 && g.nv == 1 && g.mode == 2 && int64_t(pb.P) * g.S * 2 <= cus && !getenv("SDM_P2_GEOM")) {
+        const P2Geom g4 = plan_phase2(pb, L, 4, es, cus, lds_limit);
+        if (g4.nv == 1 && g4.mode == 2) {
+            V = 4;
+            return g4;
+        }
+    }
+    return g;
+}
+
 }  // namespace
 
 extern "C" {
@@ -254,12 +272,12 @@ int sdm_fwd_plan(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t 
     DeviceInfo *dev = nullptr;
     if ((rc = device_info(&dev)) != SDM_OK) return rc;
     const int es = dtype == SDM_F32 ? 4 : 2, vec = 16 / es;
-    const int V = hd % vec == 0 ? vec : 1;
+    int V = hd % vec == 0 ? vec : 1;
     Problem pb{};
     pb.P = P; pb.T = T; pb.C = C; pb.W = W; pb.R = R; pb.hd = hd; pb.M = M; pb.dtype = dtype;
     pb.bank_stride = M * hd;   // per-stream banks
     const ChunkLayout lay = make_layout(C, W, R);
-    const P2Geom g = plan_phase2(pb, lay, V, es, dev->cus, dev->lds_per_block);
+    const P2Geom g = plan_phase2_v(pb, lay, V, es, dev->cus, dev->lds_per_block);
     plan->vec = V;
     plan->slice_vectors = g.nv;
     plan->slices = g.S;
@@ -373,7 +391,7 @@ int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, 
     if (gram_lds_bytes(C) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
                     gram_lds_bytes(C), dev->lds_per_block);
-    const P2Geom geom = plan_phase2(ck.pb, ck.lay, ck.V, ck.es, dev->cus, dev->lds_per_block);
+    const P2Geom geom = plan_phase2_v(ck.pb, ck.lay, ck.V, ck.es, dev->cus, dev->lds_per_block);
     const size_t p2lds = phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.mode, ck.pb.M);
     if (p2lds + 256 > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup in phase 2, the device has %d", C,

@@ -86,6 +86,23 @@ template <> struct Vec<bf16, 8> {
         *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 };
+// Four bfloat16 columns (8 bytes): the narrow slices of a resident bank (see plan_phase2).
+template <> struct Vec<bf16, 4> {
+    using raw_t = uint2;
+    static __device__ __forceinline__ raw_t load_raw(const bf16 *p) { return *reinterpret_cast<const uint2 *>(p); }
+    static __device__ __forceinline__ void unpack(const raw_t &x, float (&o)[4]) {
+        o[0] = __uint_as_float(x.x << 16);
+        o[1] = __uint_as_float(x.x & 0xFFFF0000u);
+        o[2] = __uint_as_float(x.y << 16);
+        o[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ void load(const bf16 *p, float (&o)[4]) { unpack(load_raw(p), o); }
+    static __device__ __forceinline__ void store(bf16 *p, const float (&o)[4]) {
+        const uint32_t w0 = uint32_t(f32_to_bf16(o[0]).bits) | (uint32_t(f32_to_bf16(o[1]).bits) << 16);
+        const uint32_t w1 = uint32_t(f32_to_bf16(o[2]).bits) | (uint32_t(f32_to_bf16(o[3]).bits) << 16);
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w0, w1);
+    }
+};
 template <typename T> struct Vec<T, 1> {
     using raw_t = T;
     static __device__ __forceinline__ raw_t load_raw(const T *p) { return *p; }

@@ -934,7 +934,9 @@ static const void *p2_fn_nv(int nv) {
 template <int MODE>
 static const void *phase2_fn_m(int dtype, int V, int nv) {
     if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, MODE>(nv) : p2_fn_nv<float, 1, MODE>(nv);
-    return V == 8 ? p2_fn_nv<bf16, 8, MODE>(nv) : p2_fn_nv<bf16, 1, MODE>(nv);
+    if (V == 8) return p2_fn_nv<bf16, 8, MODE>(nv);
+    if (V == 4) return reinterpret_cast<const void *>(&phase2_kernel<bf16, 4, 1, kP2Resident>);   // see plan_phase2
+    return p2_fn_nv<bf16, 1, MODE>(nv);
 }
 
 static const void *phase2_fn(int dtype, int V, int nv, int mode) {
@@ -954,7 +956,8 @@ hipError_t phase2_prepare() {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
                     if (e != hipSuccess) return e;
                 }
-    return hipSuccess;
+    return hipFuncSetAttribute(phase2_fn(1, 4, 1, kP2Resident), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               160 * 1024 - 256);
 }
 
 // LDS of a Phase-2 workgroup: the row regions (u, inter; staged, delta_v too); staged, the chunk's Phase-2 block and

@@ -255,15 +255,20 @@ def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
 
 def test_plan_reports_phase2_modes(gpu, monkeypatch):
     """The plan query follows the mode cap of the tuning override, and the headline shape
-    (C=64, hd=64 bf16, 4096 rows, W=R=8) keeps its bank slice resident in LDS."""
+    (C=64, hd=64 bf16, 4096 rows, W=R=8) keeps its bank slice resident in LDS, in slices of
+    one 8-byte vector (4 columns: 16 slices per stream) since 8-column slices would leave
+    more than half of the CUs idle; a shape with enough streams keeps 16-byte vectors."""
     from chunked_sparse_delta_amd import plan
     monkeypatch.delenv("SDM_P2_GEOM", raising=False)
     p = plan(8, 2048, 64, 8, 8, 64, 4096, torch.bfloat16)
     assert p["phase2_mode"] == "resident" and p["phase2_lds_bytes"] <= p["lds_limit"], p
+    assert p["vec"] == 4 and p["slice_vectors"] == 1 and p["slices"] == 16, p
+    wide = plan(64, 256, 64, 8, 8, 64, 4096, torch.bfloat16)
+    assert wide["vec"] == 8, wide
     for cap, mode in (("1,1", "staged"), ("1,0", "memory")):
         monkeypatch.setenv("SDM_P2_GEOM", cap)
         q = plan(8, 2048, 64, 8, 8, 64, 4096, torch.bfloat16)
-        assert q["phase2_mode"] == mode and q["slice_vectors"] == 1, q
+        assert q["phase2_mode"] == mode and q["slice_vectors"] == 1 and q["vec"] == 8, q
 
 
 @pytest.mark.parametrize("wl", [
