@@ -632,15 +632,41 @@ __device__ __forceinline__ void cold_row_at(int C, int nl, const int4 *spk, cons
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
-                for (int j = 0; j < end - base; ++j) {
-                    const int c = mcol[j];
-                    const float v = mval[j];
-                    if ((c >> 2) == lane) {
-                        const int q = c & 3;
-                        if (q == 0) acc[0] += v;
-                        else if (q == 1) acc[1] += v;
-                        else if (q == 2) acc[2] += v;
-                        else acc[3] += v;
+                // Replay, 64 terms at a time: the terms go to the lanes that own their columns
+                // in rounds, round r carrying each owner's r-th term of the batch (its terms in
+                // list order), through slots in the batch's own part of the list (its terms are
+                // in registers by then). Every element still sums its terms in list order.
+                const int nt = end - base;
+                for (int j0 = 0; j0 < nt; j0 += kWave) {
+                    const bool ok = j0 + lane < nt;
+                    const int c = ok ? mcol[j0 + lane] : 0;
+                    const float v = ok ? mval[j0 + lane] : 0.0f;
+                    const int own = ok ? (c >> 2) : kWave;   // owner lane of column c (kWave: none)
+                    uint64_t peers = ~uint64_t(0);
+#pragma unroll
+                    for (int b = 0; b < 7; ++b) {
+                        const bool bit = (own >> b) & 1;
+                        const uint64_t bb = __ballot(bit);
+                        peers &= bit ? bb : ~bb;
+                    }
+                    const int rank = __popcll(peers & lanemask_lt(lane));
+                    int32_t *scol = mcol + j0;
+                    float *sval = mval + j0;
+                    for (int rr = 0; __ballot(ok && rank == rr) != 0; ++rr) {
+                        scol[lane] = -1;
+                        __builtin_amdgcn_wave_barrier();
+                        if (ok && rank == rr) {
+                            scol[own] = c & 3;
+                            sval[own] = v;
+                        }
+                        __builtin_amdgcn_wave_barrier();
+                        const int q = scol[lane];
+                        const float w = sval[lane];
+                        if (q == 0) acc[0] += w;
+                        else if (q == 1) acc[1] += w;
+                        else if (q == 2) acc[2] += w;
+                        else if (q == 3) acc[3] += w;
+                        __builtin_amdgcn_wave_barrier();
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
