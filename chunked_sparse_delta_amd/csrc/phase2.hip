@@ -584,6 +584,27 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         }
 
 
+        // From memory, this step's vectors of v, its beta and the DW's group counts are loaded
+        // before the gather, so that their round trip overlaps it (the asm keeps the compiler
+        // from moving the loads down to their uses).
+        [[maybe_unused]] float mv[Cfg::kUItems][V];
+        [[maybe_unused]] float mb[Cfg::kUItems];
+        [[maybe_unused]] int32_t mng = 0, mnbig = 0;
+        if constexpr (!SM) {
+            const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
+#pragma unroll
+            for (int x = 0; x < Cfg::kUItems; ++x) {
+                const int item = tid + BLOCK * x, t = item / NV, vq = item % NV;
+                const bool live = t < CP && t < nl && vq < nvs;
+                Vec<T, V>::load(at(vin, live ? uint32_t(t * hd + col0 + vq * V) : uint32_t(col0)), mv[x]);
+                mb[x] = beta_c[live ? t : 0];
+            }
+            const int32_t *meta = reinterpret_cast<const int32_t *>(arr(a.off_meta));
+            mng = meta[2];
+            mnbig = meta[4];
+            asm volatile("" ::: "memory");
+        }
+
         // ---- gather: u (staged; retrieved otherwise) -> ub, inter -> ib (live tokens)
         {
             const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
@@ -616,7 +637,6 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
         // ---- u = beta (v - retrieved); +0 for padding tokens and rows C..CP-1 (without
         //      staging; staged, the gather has done it)
         if constexpr (!SM) {
-        const float *beta_c = reinterpret_cast<const float *>(arr(a.off_beta));
 #pragma unroll
         for (int x = 0; x < Cfg::kUItems; ++x) {
             const int item = tid + BLOCK * x, t = item / NV, vq = item % NV;
@@ -624,14 +644,11 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             float *ur = ub + t * pitch + vq * V;
             float uu[V];
             const bool live = t < nl && vq < nvs;
-            float vv[V];   // unconditional load (in-bounds fallback), as in the gather
-            Vec<T, V>::load(at(vin, live ? uint32_t(t * hd + col0 + vq * V) : uint32_t(col0)), vv);
-            const float b = beta_c[live ? t : 0];
             if (live) {
                 float rr[V];
                 lds_load_vec<V>(ur, rr);
 #pragma unroll
-                for (int c = 0; c < V; ++c) uu[c] = b * (vv[c] - rr[c]);
+                for (int c = 0; c < V; ++c) uu[c] = mb[x] * (mv[x][c] - rr[c]);
             } else {
 #pragma unroll
                 for (int c = 0; c < V; ++c) uu[c] = 0.0f;
@@ -790,10 +807,9 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
             asm volatile("" : "+v"(dlane));
             if constexpr (!SM) {
-                const int32_t *meta = reinterpret_cast<const int32_t *>(arr(a.off_meta));
                 if (nl > 0) {
-                    dw_ng = meta[2];
-                    dw_nbig = meta[4];
+                    dw_ng = mng;
+                    dw_nbig = mnbig;
                 }
             }
             const int32_t ng = dw_ng, nbig = dw_nbig;
