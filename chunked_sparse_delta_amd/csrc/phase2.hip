@@ -951,7 +951,11 @@ template <int MODE>
 static const void *phase2_fn_m(int dtype, int V, int nv) {
     if (dtype == 0) return V == 4 ? p2_fn_nv<float, 4, MODE>(nv) : p2_fn_nv<float, 1, MODE>(nv);
     if (V == 8) return p2_fn_nv<bf16, 8, MODE>(nv);
-    if (V == 4) return reinterpret_cast<const void *>(&phase2_kernel<bf16, 4, 1, kP2Resident>);   // see plan_phase2
+    // 8-byte vectors only for one-vector slices of a resident bank (the narrow slices the
+    // planner picks for few streams); any other geometry has no kernel
+    if (V == 4)
+        return nv == 1 && MODE == kP2Resident ? reinterpret_cast<const void *>(&phase2_kernel<bf16, 4, 1, kP2Resident>)
+                                               : nullptr;
     return p2_fn_nv<bf16, 1, MODE>(nv);
 }
 
@@ -1017,7 +1021,9 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
     const int es = pb.dtype == 0 ? 4 : 2;
     const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
     void *args[] = {&a};
-    return hipLaunchKernel(phase2_fn(pb.dtype, V, g.nv, g.mode), grid, block, args,
+    const void *fn = phase2_fn(pb.dtype, V, g.nv, g.mode);
+    if (!fn) return hipErrorInvalidValue;
+    return hipLaunchKernel(fn, grid, block, args,
                            phase2_lds_bytes(L, pb.C, g.nv, V, es, g.mode, pb.M), st);
 }
 
