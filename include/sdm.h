@@ -215,7 +215,11 @@ int sdm_wy_solve(int64_t n, int32_t chunk, const float *A, const float *beta, co
  * these shapes (SDM_ERR_SHAPE, SDM_ERR_RANGE, SDM_ERR_DTYPE), or SDM_ERR_HIP.
  */
 typedef struct {
-    int32_t vec;               /* bank elements per vector access */
+    int32_t vec;               /* bank elements per vector access: 16 bytes' worth (4 float32,
+                                  8 bfloat16); 4 bfloat16 (8 bytes) when a bank slice held in
+                                  LDS is narrowed to 4 columns because one 16-byte vector per
+                                  slice would still leave more than half of the CUs idle; 1 when
+                                  head_dim is not a multiple of the 16-byte count */
     int32_t slice_vectors;     /* vectors per column slice of Phase 2 */
     int32_t slices;            /* column slices per stream: Phase 2 runs streams * slices workgroups */
     int32_t phase2_mode;       /* 0: Phase-2 arrays and bank rows read from memory; 1: the chunk's
