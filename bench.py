@@ -413,7 +413,7 @@ def main():
     p2_done = [torch.cuda.Event(), torch.cuda.Event()]
     marker = torch.zeros(1, device=dev)
 
-    def overlapped(K):
+    def overlapped(K, p2cus=0):
         side.wait_stream(main)
         with torch.cuda.stream(side):
             sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[0], chunk=wl.C, valid_tokens=t["valid"], stream=side)
@@ -422,7 +422,7 @@ def main():
             b = k % 2
             main.wait_event(p1_done[b])
             sdm_fwd_phase2(bank, *fargs, workspace=ws_pair[b], out=out, chunk=wl.C, valid_tokens=t["valid"],
-                           stream=main)
+                           stream=main, phase2_cus=p2cus)
             p2_done[b].record(main)
             if k + 1 < K:
                 n = (k + 1) % 2
@@ -438,8 +438,20 @@ def main():
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
+    # The overlapped loop's Phase-2 geometry: planned for all CUs, or for half of them
+    # (leaving the rest to the next batch's Phase 1); the faster over a few warmup steps.
+    p2cus = 0
     if not args.serial:
-        overlapped(max(2, args.warmup))
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        trial = {}
+        for c in (0, cus // 2):
+            overlapped(max(2, args.warmup), c)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            overlapped(8, c)
+            torch.cuda.synchronize()
+            trial[c] = time.perf_counter() - t0
+        p2cus = min(trial, key=trial.get)
     torch.cuda.synchronize()
     # The timed steps run without instrumentation; a second pass of the same steps records
     # the library's kernel-boundary events for the per-kernel breakdown (recording an event
@@ -455,7 +467,7 @@ def main():
     if not args.serial:
         print(f"bench: timing {args.steps} overlapped steps", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
-        overlapped(args.steps)
+        overlapped(args.steps, p2cus)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     print(f"bench: {args.steps} instrumented steps for the per-kernel times", file=sys.stderr, flush=True)
@@ -501,6 +513,7 @@ def main():
         "timing": ("serial sdm_fwd calls" if args.serial else
                    "two streams: Phase 1 of batch k+1 overlaps Phase 2 of batch k (sdm_fwd_phase1/2, same bits)"),
         "ms_per_step_serial": round(1000.0 * elapsed_serial / args.steps, 4),
+        "phase2_cus": p2cus,
         "kernel_ms": kern_ms,
         "plan": plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, bank.dtype),
         "roofline": roof,

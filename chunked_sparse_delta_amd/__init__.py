@@ -66,7 +66,8 @@ class _Bank(ctypes.Structure):
 
 class _Exec(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("events", ctypes.c_void_p), ("num_events", ctypes.c_int32), ("repeated_writes", ctypes.c_void_p)]
+                ("events", ctypes.c_void_p), ("num_events", ctypes.c_int32), ("repeated_writes", ctypes.c_void_p),
+                ("phase2_cus", ctypes.c_int32)]
 
 
 _ID_BYTES = {torch.int32: 4, torch.int64: 8}
@@ -366,7 +367,7 @@ def sdm_write_read(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor,
 
 
 def _fwd_part(part: int, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, chunk, valid_tokens, out,
-              workspace, stream, shared_bank, repeated_writes):
+              workspace, stream, shared_bank, repeated_writes, phase2_cus=0):
     lib = _load()
     P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
                                                    valid_tokens, shared_bank)
@@ -376,7 +377,7 @@ def _fwd_part(part: int, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *
         _expect(out, "out", (P, T, hd), bank.dtype, bank.device)
     bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 1 if bank.dim() == 2 else 0)
     ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(), None, 0,
-               None if repeated_writes is None else repeated_writes.data_ptr())
+               None if repeated_writes is None else repeated_writes.data_ptr(), int(phase2_cus))
     fn = lib.sdm_fwd_phase1 if part == 1 else lib.sdm_fwd_phase2
     rc = fn(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G, _ptr(v),
             ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
@@ -393,12 +394,15 @@ def sdm_fwd_phase1(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, work
 
 
 def sdm_fwd_phase2(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, workspace: torch.Tensor, out: torch.Tensor,
-                   chunk: int = 64, valid_tokens=None, stream=None, shared_bank: bool = False) -> torch.Tensor:
+                   chunk: int = 64, valid_tokens=None, stream=None, shared_bank: bool = False,
+                   phase2_cus: int = 0) -> torch.Tensor:
     """The forward's Phase 2 from a ``workspace`` filled by sdm_fwd_phase1 with the same
     arguments (ordered before this call): advances ``bank`` in place and writes ``out``;
-    with the phase-1 call it gives exactly sdm_fwd's result."""
+    with the phase-1 call it gives exactly sdm_fwd's result. ``phase2_cus`` (0: all) caps
+    the CUs its slice geometry plans for, leaving the rest to a Phase 1 run beside it."""
     _fwd_part(2, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, chunk=chunk, valid_tokens=valid_tokens,
-              out=out, workspace=workspace, stream=stream, shared_bank=shared_bank, repeated_writes=None)
+              out=out, workspace=workspace, stream=stream, shared_bank=shared_bank, repeated_writes=None,
+              phase2_cus=phase2_cus)
     return out
 
 

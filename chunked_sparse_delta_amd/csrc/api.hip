@@ -391,7 +391,9 @@ int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, 
     if (gram_lds_bytes(C) > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup, the device has %d", C,
                     gram_lds_bytes(C), dev->lds_per_block);
-    const P2Geom geom = plan_phase2_v(ck.pb, ck.lay, ck.V, ck.es, dev->cus, dev->lds_per_block);
+    if (exec->phase2_cus < 0) return fail(SDM_ERR_SHAPE, "phase2_cus must be >= 0, got %d", exec->phase2_cus);
+    const int p2cus = exec->phase2_cus > 0 && exec->phase2_cus < dev->cus ? exec->phase2_cus : dev->cus;
+    const P2Geom geom = plan_phase2_v(ck.pb, ck.lay, ck.V, ck.es, p2cus, dev->lds_per_block);
     const size_t p2lds = phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.mode, ck.pb.M);
     if (p2lds + 256 > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup in phase 2, the device has %d", C,

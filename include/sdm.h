@@ -118,6 +118,12 @@ typedef struct {
      * contract and their results are unspecified). Ordered on `stream`; the caller zeroes
      * and reads it. */
     int64_t *repeated_writes;
+    /* CUs the Phase-2 launch geometry may plan for (0 = all of the device; larger values are
+     * clamped to it; negative is SDM_ERR_SHAPE). sdm_fwd and sdm_fwd_phase2 size their
+     * column slices so that Phase 2's workgroups fill this many CUs; a caller that runs
+     * another batch's sdm_fwd_phase1 beside this Phase 2 can leave that Phase 1 the rest of
+     * the device. Results never depend on it. Ignored by the other entry points. */
+    int32_t phase2_cus;
 } sdm_exec;
 
 #define SDM_TIMING_EVENTS 8

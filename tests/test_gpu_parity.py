@@ -440,3 +440,25 @@ def test_overlapped_batches_give_the_same_bits(gpu):
     for k, (o_bits, b_bits) in enumerate(refs):
         assert np.array_equal(gu.bits(outs[k]), o_bits), f"readings of batch {k}"
     assert np.array_equal(gu.bits(bank), refs[-1][1])
+
+
+@pytest.mark.gpu
+def test_phase2_cu_budget_does_not_change_bits(gpu):
+    """sdm_fwd_phase2's phase2_cus (the CUs its slice geometry plans for) changes only the
+    schedule: every budget gives sdm_fwd's bits; a negative budget is rejected."""
+    from chunked_sparse_delta_amd import SdmError, sdm_fwd_phase1, sdm_fwd_phase2, workspace_bytes
+    wl = small(P=8, T=200, C=64, hd=128, M=300, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=47)
+    t = gu.to_torch(gu.generate(wl), gpu)
+    o_ref, b_ref = gu.run(t, wl.C)
+    args = (t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"])
+    ws = torch.empty(workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0), dtype=torch.uint8, device=gpu)
+    for cus in (1, 16, 64, 128, 100000):
+        bank = t["bank"].clone()
+        out = torch.empty_like(o_ref)
+        sdm_fwd_phase1(bank, *args, workspace=ws, chunk=wl.C, valid_tokens=t["valid"])
+        sdm_fwd_phase2(bank, *args, workspace=ws, out=out, chunk=wl.C, valid_tokens=t["valid"], phase2_cus=cus)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.bits(out), gu.bits(o_ref)) and np.array_equal(gu.bits(bank), gu.bits(b_ref)), cus
+    with pytest.raises(SdmError, match="phase2_cus"):
+        sdm_fwd_phase2(t["bank"].clone(), *args, workspace=ws, out=torch.empty_like(o_ref), chunk=wl.C,
+                       valid_tokens=t["valid"], phase2_cus=-1)
