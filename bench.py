@@ -1,16 +1,23 @@
 """Benchmark of the SDM forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu-baseline]
     python bench.py --copy-calibration      # plain 1 GiB device copy, for scaling HBM counters
     python bench.py --op sdm_bwd [--workload 1]   # the backward
     python bench.py --op topk               # the product-key top-k
 
 A step is one sdm_fwd call over the whole workload (every chunk step of every stream)
-with all inputs resident in HBM. The bank is advanced in place from step to step, as a
-caller carrying the memory across calls would; the kernels are data-oblivious, so the
-timing equals that of a restored bank. Prints one JSON line: tokens/s, the per-kernel
-breakdown from HIP events recorded by the library on its stream, the roofline of the
-dominant kernel, and the CPU oracle's throughput on the host as a reference.
+with all inputs resident in HBM. The default workload is config 4 (64 streams x 4096
+tokens, chunk 256, head_dim 256, 131072 bf16 rows per stream, 256 write and 256 read
+slots per token), the largest single-GPU configuration and the one the throughput metric
+is quoted on. Each timed step is bracketed by HIP events on the library's stream; before
+it, outside the timed region, the bank is restored from a pristine copy (the op advances
+it in place) and the 256 MB last-level cache (MALL) is flushed by writing 1 GiB of
+scratch, so every step starts cold from the same state. `ms_per_step` is the median over
+the K steps (the mean is reported beside it, and a warm median taken without the flush).
+Prints one JSON line: tokens/s, the per-kernel breakdown from HIP events recorded by the
+library on its stream, the roofline of the dominant kernel against the 8 TB/s datasheet
+peak and against a device copy measured in the same run, and the CPU oracle's throughput
+on the host as a reference.
 
 The roofline's `traffic` (HBM bytes per Phase-2 launch) comes from the committed counter
 summary profiles/traffic_<workload>.md (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by the
@@ -44,13 +51,14 @@ KERNELS = ("p1_sort", "p1_groups", "p1_reads", "p1_gram_cold", "p1_gram_hot", "w
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="1", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--workload", default="4", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--serial", action="store_true",
-                    help="time serial sdm_fwd calls only (default: batch k+1's Phase 1 overlaps batch k's Phase 2)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time a loop in which batch k+1's Phase 1 overlaps batch k's Phase 2 on a second "
+                         "stream (reported beside the headline; the bank is then advanced in place)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 launches)")
     ap.add_argument("--op", default="sdm_fwd", choices=("sdm_fwd", "sdm_bwd", "topk"),
@@ -336,7 +344,7 @@ def bench_bwd(args):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(inp: dict, wl, seconds: float) -> dict:
+def cpu_baseline(inp: dict, wl, seconds: float, streams_total: int) -> dict:
     import oracle
     f = oracle.as_f64_inputs(inp)
     threads = max(1, min(wl.P, os.cpu_count() or 1, 16))
@@ -349,9 +357,10 @@ def cpu_baseline(inp: dict, wl, seconds: float) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": reps * tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole workload ({wl.P} streams, {tokens} valid tokens) x {reps} passes of the fp64 "
-                      f"token loop, {threads} threads, {el:.1f} s"}
+    return {"value": reps * tokens / el, "unit": "tokens/s", "cores": threads, "host_cores": os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{wl.P} of the workload's {streams_total} streams ({tokens} valid tokens) x {reps} passes "
+                      f"of the fp64 token loop, {threads} threads, {el:.1f} s"}
 
 
 def main():
@@ -397,84 +406,47 @@ def main():
         ev_sets.append(arr)
 
     fargs = (t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"])
+    pristine = bank.clone()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # 4x the 256 MB MALL
+    stream = torch.cuda.current_stream()
 
     def step(events=None):
         sdm_fwd(bank, *fargs, chunk=wl.C, valid_tokens=t["valid"], out=out, workspace=ws, events=events)
 
-    # Overlapped steps: Phase 1 never reads the bank, so batch k+1's Phase 1 runs on a second
-    # stream (and a second workspace) while batch k's Phase 2 runs on the first; every step
-    # still runs both phases in full. Phase 1 of k+1 waits for Phase 2 of k-1 (which read the
-    # workspace it reuses) and then for a one-element marker kernel on its own stream: by the
-    # time the marker has run, Phase 2 of k (ready since Phase 1 of k ended) has been
-    # dispatched, so Phase 2's workgroups are placed first and Phase 1 fills the idle CUs.
-    ws_pair = [ws, torch.empty_like(ws)] if not args.serial else None
-    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
-    p1_done = [torch.cuda.Event(), torch.cuda.Event()]
-    p2_done = [torch.cuda.Event(), torch.cuda.Event()]
-    marker = torch.zeros(1, device=dev)
+    def prepare(cold: bool):
+        # outside the timed region: the pristine bank, and (cold) a MALL flushed by 1 GiB of writes
+        bank.copy_(pristine)
+        if cold:
+            flush.fill_(1)
 
-    def overlapped(K, p2cus=0):
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[0], chunk=wl.C, valid_tokens=t["valid"], stream=side)
-            p1_done[0].record(side)
+    def timed_steps(K: int, cold: bool) -> np.ndarray:
+        """K calls, each from the pristine bank, timed by HIP events on the call's stream."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
         for k in range(K):
-            b = k % 2
-            main.wait_event(p1_done[b])
-            sdm_fwd_phase2(bank, *fargs, workspace=ws_pair[b], out=out, chunk=wl.C, valid_tokens=t["valid"],
-                           stream=main, phase2_cus=p2cus)
-            p2_done[b].record(main)
-            if k + 1 < K:
-                n = (k + 1) % 2
-                with torch.cuda.stream(side):
-                    if k >= 1:
-                        side.wait_event(p2_done[n])
-                    marker.add_(1.0)
-                    sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[n], chunk=wl.C, valid_tokens=t["valid"],
-                                   stream=side)
-                    p1_done[n].record(side)
-        main.wait_stream(side)
+            prepare(cold)
+            evs[k][0].record(stream)
+            step()
+            evs[k][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) for e0, e1 in evs])
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
-    # The overlapped loop's Phase-2 geometry: planned for all CUs, or for half of them
-    # (leaving the rest to the next batch's Phase 1); the faster over a few warmup steps.
-    p2cus = 0
-    if not args.serial:
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        trial = {}
-        for c in (0, cus // 2):
-            overlapped(max(2, args.warmup), c)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            overlapped(8, c)
-            torch.cuda.synchronize()
-            trial[c] = time.perf_counter() - t0
-        p2cus = min(trial, key=trial.get)
-    torch.cuda.synchronize()
-    # The timed steps run without instrumentation; a second pass of the same steps records
-    # the library's kernel-boundary events for the per-kernel breakdown (recording an event
-    # costs GPU time of its own, so it stays out of the timed region).
-    print(f"bench: timing {args.steps} serial steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
+        prepare(True)
         step()
     torch.cuda.synchronize()
-    elapsed_serial = time.perf_counter() - t0
-    elapsed = elapsed_serial
-    if not args.serial:
-        print(f"bench: timing {args.steps} overlapped steps", file=sys.stderr, flush=True)
-        t0 = time.perf_counter()
-        overlapped(args.steps, p2cus)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+    print(f"bench: timing {args.steps} cold steps", file=sys.stderr, flush=True)
+    t_wall = time.perf_counter()
+    cold_ms = timed_steps(args.steps, True)
+    t_wall = time.perf_counter() - t_wall
+    print(f"bench: timing {args.steps} warm steps", file=sys.stderr, flush=True)
+    warm_ms = timed_steps(args.steps, False)
     print(f"bench: {args.steps} instrumented steps for the per-kernel times", file=sys.stderr, flush=True)
     for k in range(args.steps):
+        prepare(True)
         step(ev_sets[k])
     torch.cuda.synchronize()
-
     per = np.zeros((args.steps, nev - 1))
     for k, arr in enumerate(ev_sets):
         for j in range(nev - 1):
@@ -483,11 +455,29 @@ def main():
             per[k, j] = ms.value
         for j in range(nev):
             hip.hipEventDestroy(arr[j])
-    kern_ms = dict(zip(KERNELS, per.mean(axis=0).round(5).tolist()))
+    kern_ms = dict(zip(KERNELS, np.median(per, axis=0).round(5).tolist()))
+
+    # The achievable bandwidth of a plain device copy (1 GiB read + 1 GiB written), same run.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    copy_ms = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * src.numel() / (float(np.median(copy_ms[1:])) * 1e-3) / 1e9
+    del src, dst
+
+    overlapped_ms = None
+    if args.overlap:
+        overlapped_ms = overlapped_loop(args, wl, bank, fargs, ws, out, t, sdm_fwd_phase1, sdm_fwd_phase2)
 
     tokens = stats["live_tokens"]
-    ms_step = 1000.0 * elapsed / args.steps
-    value = tokens * args.steps / elapsed
+    ms_step = float(np.median(cold_ms))
+    value = tokens / (ms_step * 1e-3)
     row = es * wl.hd
     p2_bytes = row * (stats["U"] + stats["Uw"]) + row * tokens + row * wl.P * wl.T
     entry_bytes = tokens * (wl.W * (4 + es + 4) + wl.R * (4 + es) + 4)
@@ -497,7 +487,8 @@ def main():
         achieved = p2_bytes / (kern_ms["phase2"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "phase2", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
-                "bytes_per_launch": int(p2_bytes)}
+                "bytes_per_launch": int(p2_bytes), "copy_gbs": round(copy_gbs, 1),
+                "frac_of_copy": round(achieved / copy_gbs, 4)}
     else:
         roof = {"bound": "alu", "kernel": dom, "achieved": None, "peak": None, "unit": None, "frac": None,
                 "traffic": None, "note": "dominant kernel is a Phase-1 kernel; see kernel_ms"}
@@ -510,24 +501,75 @@ def main():
         "config": {"workload": workloads.workload_name(wl), "streams": wl.P, "tokens": wl.T, "chunk": wl.C,
                    "head_dim": wl.hd, "rows_per_stream": wl.M, "bank_dtype": wl.dtype, "W": wl.W, "R": wl.R,
                    "valid_tokens": tokens, "distinct_rows_read": stats["U"], "rows_written": stats["Uw"]},
-        "timing": ("serial sdm_fwd calls" if args.serial else
-                   "two streams: Phase 1 of batch k+1 overlaps Phase 2 of batch k (sdm_fwd_phase1/2, same bits)"),
-        "ms_per_step_serial": round(1000.0 * elapsed_serial / args.steps, 4),
-        "phase2_cus": p2cus,
+        "timing": ("median of K sdm_fwd calls, each timed by HIP events on its stream, the bank restored from "
+                   "a pristine copy and the MALL flushed (1 GiB written) before each call, outside the timed "
+                   "region; arithmetic in float32 (bank dtype in config)"),
+        "ms_per_step_mean": round(float(np.mean(cold_ms)), 4),
+        "ms_per_step_warm": round(float(np.median(warm_ms)), 4),
+        "wall_s_timed_loop": round(t_wall, 3),
         "kernel_ms": kern_ms,
         "plan": plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, bank.dtype),
         "roofline": roof,
         "path_hbm": {"algorithmic_bytes": int(path_bytes), "achieved": round(path_gbs, 1), "unit": "GB/s",
-                     "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+                     "frac": round(path_gbs / HBM_PEAK_GBS, 4), "frac_of_copy": round(path_gbs / copy_gbs, 4)},
     }
+    if overlapped_ms is not None:
+        res["ms_per_step_overlapped"] = round(overlapped_ms, 4)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         sample = inp
-        if wl.name in ("2", "3", "4", "4p"):
-            keep = [0]
-            sample = workloads.generate(wl.name == "4" and workloads.CONFIGS["4p"] or wl, streams=keep)
-        res["cpu_baseline"] = cpu_baseline(sample, wl.replace(P=len(sample["valid"])), args.cpu_seconds)
+        host = os.cpu_count() or 1
+        if wl.P > min(16, host) or wl.name in ("4", "4p"):
+            keep = list(range(min(wl.P, host, 16)))
+            # config 4 overflows as drawn; its finite twin 4p has the same shapes and cost
+            sample = workloads.generate(workloads.CONFIGS["4p"] if wl.name == "4" else wl, streams=keep)
+        res["cpu_baseline"] = cpu_baseline(sample, wl.replace(P=len(sample["valid"])), args.cpu_seconds, wl.P)
     print(json.dumps(res), flush=True)
+
+
+def overlapped_loop(args, wl, bank, fargs, ws, out, t, sdm_fwd_phase1, sdm_fwd_phase2) -> float:
+    """ms per step of a loop in which batch k+1's Phase 1 runs on a second stream (and a
+    second workspace) while batch k's Phase 2 runs on the first; every step still runs both
+    phases in full, and the bank advances in place from step to step. Phase 1 of k+1 waits
+    for Phase 2 of k-1 (which read the workspace it reuses) and then for a one-element marker
+    kernel on its own stream, so that Phase 2's workgroups are placed first."""
+    import torch
+    dev = bank.device
+    ws_pair = [ws, torch.empty_like(ws)]
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    p1_done = [torch.cuda.Event(), torch.cuda.Event()]
+    p2_done = [torch.cuda.Event(), torch.cuda.Event()]
+    marker = torch.zeros(1, device=dev)
+
+    def loop(K):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[0], chunk=wl.C, valid_tokens=t["valid"], stream=side)
+            p1_done[0].record(side)
+        for k in range(K):
+            b = k % 2
+            main.wait_event(p1_done[b])
+            sdm_fwd_phase2(bank, *fargs, workspace=ws_pair[b], out=out, chunk=wl.C, valid_tokens=t["valid"],
+                           stream=main)
+            p2_done[b].record(main)
+            if k + 1 < K:
+                n = (k + 1) % 2
+                with torch.cuda.stream(side):
+                    if k >= 1:
+                        side.wait_event(p2_done[n])
+                    marker.add_(1.0)
+                    sdm_fwd_phase1(bank, *fargs, workspace=ws_pair[n], chunk=wl.C, valid_tokens=t["valid"],
+                                   stream=side)
+                    p1_done[n].record(side)
+        main.wait_stream(side)
+
+    print(f"bench: timing {args.steps} overlapped steps", file=sys.stderr, flush=True)
+    loop(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop(args.steps)
+    torch.cuda.synchronize()
+    return 1000.0 * (time.perf_counter() - t0) / args.steps
 
 
 if __name__ == "__main__":

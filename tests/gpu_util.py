@@ -9,16 +9,20 @@ import torch
 import workloads
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}   # infinity-norm relative error per output tensor, vs O1
-# bf16 banks are also compared with O1b, the token loop under the bfloat16 storage
-# contract (rows rounded once per chunk, readings rounded). The GPU must stay within
-# bar = max(TOL, SLACK x |O1b - O1|) of O1: the contract itself can exceed TOL on a bank
-# that grows by many orders of magnitude. Against O1b: within TOL_CONTRACT where the
-# contract meets TOL (SLACK x |O1b - O1| <= TOL); where it does not, one-ulp bf16 rounding
-# differences between two correct evaluations of the contract (fp32 chunked on the GPU,
-# fp64 token loop in O1b) compound to the contract's own error, and the bound is the
-# triangle inequality through the exact result, bar + |O1b - O1|.
-TOL_CONTRACT = 2e-2
-SLACK = 1.25
+# bfloat16 banks are also held to O1b, the token loop under the bfloat16 storage contract
+# (rows rounded once per chunk, readings rounded), at the same bar wherever the contract is
+# well conditioned: O1b itself within WELL x TOL of O1. Where it is not (config 2 of the
+# workloads: a Zipf bank growing to ~1e11, O1b 2.09e-2 from O1), a float32 evaluation of the
+# contract (tests/contract_f32.py) lands 1.65e-2 from O1b and its per-row errors reach
+# 230 %; there the contract check is per row instead (check_rows).
+WELL = 0.5
+# Per-row check (bfloat16): each quantile of the GPU's per-row error against O1b stays
+# within ROW_FACTOR x the float32 contract evaluation's same quantile plus ROW_FLOOR (about
+# one bfloat16 ulp, 2^-8). Measured on config 2: the GPU's quantiles 0.5 / 0.9 / 0.99 /
+# 0.999 are 1.07-1.19 x the evaluation's on the bank, 1.08-1.19 x on the readings.
+ROW_QUANTILES = (0.5, 0.9, 0.99, 0.999)
+ROW_FACTOR = 1.5
+ROW_FLOOR = 4e-3
 
 
 def to_torch(inp: dict, device) -> dict:
@@ -69,11 +73,17 @@ def oracle_ref(inp: dict, threads: int = 8, bf16_chunk=None):
 
 
 def parity(out, bank, inp: dict, C: int, what: str = "", threads: int = 8, streams=None):
-    """Check GPU readings and bank against O1 (and, for bf16 banks, O1b) on the given
-    streams of ``inp`` (all by default; ``out``/``bank`` hold exactly those streams)."""
+    """Check GPU readings and bank against O1 (and, for bf16 banks, O1b and the per-row
+    check) on the given streams of ``inp`` (all by default; ``out``/``bank`` hold exactly
+    those streams). Bank rows that no live token writes must keep their input bits."""
     ref = oracle_ref(inp, threads)
     con = oracle_ref(inp, threads, bf16_chunk=C) if inp["dtype"] == "bf16" else None
     check(out, bank, ref, con, inp["dtype"], what)
+    if con is not None and np.asarray(inp["bank"]).ndim == 3:
+        from tests.contract_f32 import token_loop_contract_f32
+        emu = token_loop_contract_f32(inp, C)
+        check_rows(out, bank, con, emu, what)
+    check_untouched_rows(bank, inp, what)
 
 
 def check(out, bank, ref, con, dtype: str, what: str = ""):
@@ -82,18 +92,53 @@ def check(out, bank, ref, con, dtype: str, what: str = ""):
     msg, checks = [], []
     for name, g, r, c in zip(("readings", "bank"), got, ref, con if con is not None else (None, None)):
         e = rel_err(g, r)
-        bar = tol
         line = f"{name} vs O1 {e:.3e}"
         if c is not None:
             e_c, e_m = rel_err(g, c), rel_err(c, r)
-            bar = max(tol, SLACK * e_m)
             line += f", vs O1b {e_c:.3e} (O1b vs O1 {e_m:.3e})"
-            checks.append((e_c, TOL_CONTRACT if SLACK * e_m <= tol else bar + e_m, name + " vs O1b"))
-        checks.append((e, bar, name + " vs O1"))
+            if e_m <= WELL * tol:
+                checks.append((e_c, tol, name + " vs O1b"))
+        checks.append((e, tol, name + " vs O1"))
         msg.append(line)
     print(f"{what}: " + "; ".join(msg) + f" (tol {tol})", flush=True)
     for e, bar, label in checks:
         assert np.isfinite(e) and e <= bar, (what, label, e, bar)
+
+
+def check_rows(out, bank, con, emu, what: str = ""):
+    """Per-row errors against O1b (each row of the readings and each bank row that O1b
+    holds nonzero, relative to that row's own largest element), so that the largest rows
+    of a growing bank cannot hide errors on small ones: every quantile in ROW_QUANTILES
+    within ROW_FACTOR x the float32 contract evaluation's plus ROW_FLOOR."""
+    from tests.contract_f32 import row_rel_err
+    got = [f64(x) if isinstance(x, torch.Tensor) else x for x in (out, bank)]
+    lines = []
+    for name, g, c, e in zip(("readings", "bank"), got, con, emu):
+        rg, re_ = row_rel_err(g, c), row_rel_err(e, c)
+        if rg.size == 0:
+            continue
+        qg, qe = np.quantile(rg, ROW_QUANTILES), np.quantile(re_, ROW_QUANTILES)
+        lines.append(f"{name} rows q{ROW_QUANTILES} gpu {np.array2string(qg, precision=2)} "
+                     f"f32-contract {np.array2string(qe, precision=2)}")
+        for q, a, b in zip(ROW_QUANTILES, qg, qe):
+            assert a <= ROW_FACTOR * b + ROW_FLOOR, (what, name, "row quantile", q, a, b)
+    print(f"{what}: " + "; ".join(lines), flush=True)
+
+
+def check_untouched_rows(bank, inp: dict, what: str = ""):
+    """Rows of the bank that no live token writes are bit for bit the input rows."""
+    b0 = np.asarray(inp["bank"])
+    if not isinstance(bank, torch.Tensor) or b0.ndim != 3 or tuple(bank.shape) != b0.shape:
+        return
+    got = bits(bank)
+    b0 = b0.view(np.int16) if inp["dtype"] == "bf16" else np.ascontiguousarray(b0, dtype=np.float32).view(np.int32)
+    k_idx = np.asarray(inp["k_idx"])
+    P, T, W = k_idx.shape
+    valid = np.clip(np.asarray(inp["valid"], dtype=np.int64), 0, T)
+    for p in range(P):
+        written = np.zeros(b0.shape[1], dtype=bool)
+        written[k_idx[p, :valid[p]].ravel()] = True
+        assert np.array_equal(got[p][~written], b0[p][~written]), (what, "untouched rows changed", p)
 
 
 def assert_parity(out, bank, ref_out, ref_bank, dtype: str, what: str = "", con=None):
