@@ -29,7 +29,7 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
+__all__ = ["SdmError", "sdm_fwd", "sdm_fwd_noalloc", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
            "workspace_bytes", "plan",
            "library_path",
            "SDM_ERRORS"]
@@ -97,7 +97,7 @@ def _load():
             lib.sdm_fwd_workspace_bytes.argtypes = [i32] * 7
             lib.sdm_fwd_workspace_bytes.restype = sz
             lib.sdm_fwd.argtypes = [i32, i32, i32, p, p, p, p, i32, p, p, p, p, p]
-            for fn in (lib.sdm_fwd_phase1, lib.sdm_fwd_phase2):
+            for fn in (lib.sdm_fwd_phase1, lib.sdm_fwd_phase2, lib.sdm_fwd_noalloc):
                 fn.argtypes = [i32, i32, i32, p, p, p, p, i32, p, p, p, p, p]
                 fn.restype = ctypes.c_int
             lib.sdm_fwd.restype = ctypes.c_int
@@ -263,6 +263,37 @@ def sdm_fwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
                None if repeated_writes is None else repeated_writes.data_ptr())
     rc = lib.sdm_fwd(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
                      _ptr(v), ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
+    _check_rc(lib, rc)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SDM_NOALLOC_SCRATCH_BYTES
+
+
+def sdm_fwd_noalloc(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
+                    beta: torch.Tensor, log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, *,
+                    chunk: int = 64, valid_tokens: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                    stream=None, events=None, shared_bank: bool = False,
+                    repeated_writes: torch.Tensor | None = None) -> torch.Tensor:
+    """sdm_fwd on the library's static scratch (sdm_fwd_noalloc): no workspace is allocated
+    or passed; shapes whose single step needs more than NOALLOC_SCRATCH_BYTES are refused.
+    ``out`` is allocated here when omitted (pass it to allocate nothing at all). Calls that
+    overlap on one GPU share its scratch and race."""
+    lib = _load()
+    P, M, hd, T, W, R, G, slots, weights = _inputs(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val,
+                                                   valid_tokens, shared_bank)
+    if repeated_writes is not None:
+        _expect(repeated_writes, "repeated_writes", (1,), torch.int64, bank.device)
+    if out is None:
+        out = torch.empty((P, T, hd), dtype=bank.dtype, device=bank.device)
+    else:
+        _expect(out, "out", (P, T, hd), bank.dtype, bank.device)
+    bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 1 if bank.dim() == 2 else 0)
+    ex = _Exec(_stream_ptr(stream), None, 0,
+               None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events),
+               None if repeated_writes is None else repeated_writes.data_ptr())
+    rc = lib.sdm_fwd_noalloc(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay),
+                             G, _ptr(v), ctypes.byref(bk), _ptr(valid_tokens), _ptr(out), ctypes.byref(ex))
     _check_rc(lib, rc)
     return out
 

@@ -54,12 +54,20 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(SDM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Per-device one-time setup: the large-LDS kernel attributes and the LDS limit.
+// The scratch of sdm_fwd_noalloc: a file-scope device array, one copy per GPU the library
+// runs on, held until the process ends. In host code its name is a host-side stand-in, not
+// a device address: the setup below takes each device's own address of it once
+// (hipGetSymbolAddress, with that device current) and every use goes through that pointer.
+__device__ __align__(256) unsigned char scratch[SDM_NOALLOC_SCRATCH_BYTES];
+
+// Per-device one-time setup: the large-LDS kernel attributes, the LDS limit, and the
+// device address of the static scratch.
 struct DeviceInfo {
     bool ready = false;
     int lds_per_block = 0;   // the limit the plans use
     int lds_default = 0;     // the device's default per-block limit (reported by sdm_fwd_plan)
     int cus = 0;
+    void *scratch = nullptr; // this device's copy of `scratch`
 };
 // The kernels' opt-in LDS attribute is set to at most this many bytes.
 constexpr int kMaxLdsPerBlock = 160 * 1024 - 256;
@@ -90,6 +98,10 @@ int device_info(DeviceInfo **out) {
         if ((e = phase2_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 2)");
         if ((e = wy_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (solve)");
         if ((e = bwd_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (backward)");
+        void *sp = nullptr;
+        if ((e = hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch))) != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress (static scratch)");
+        d.scratch = sp;
         d.ready = true;
     }
     *out = &d;
@@ -367,11 +379,22 @@ namespace {
 // The forward's launch sequence. parts: 1 Phase 1 and the solve, 2 Phase 2, 3 both (sdm_fwd).
 // A call of one part needs the workspace to hold every step, so that Phase 1's outputs for
 // all chunks stay there for the Phase-2 call that follows it.
+// noalloc: the workspace is this device's static scratch (SDM_NOALLOC_SCRATCH_BYTES), not
+// exec->workspace, which must then be NULL with workspace_bytes 0.
 int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,
             const float *beta, const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank,
-            const int32_t *valid_tokens, void *out, const sdm_exec *exec) {
+            const int32_t *valid_tokens, void *out, const sdm_exec *exec_in, bool noalloc = false) {
     g_err[0] = 0;
-    if (!bank || !exec) return fail(SDM_ERR_NULL, "bank and exec must not be NULL");
+    if (!bank || !exec_in) return fail(SDM_ERR_NULL, "bank and exec must not be NULL");
+    sdm_exec exec_static;
+    const sdm_exec *exec = exec_in;
+    if (noalloc) {
+        if (exec_in->workspace || exec_in->workspace_bytes)
+            return fail(SDM_ERR_WORKSPACE, "sdm_fwd_noalloc runs on its static scratch: exec->workspace must be NULL "
+                                           "and exec->workspace_bytes 0");
+        exec_static = *exec_in;
+        exec = &exec_static;
+    }
     Checked ck;
     if (bank->shared != 0 && bank->shared != 1) return fail(SDM_ERR_SHAPE, "bank.shared must be 0 or 1, got %d", bank->shared);
     const bool p1 = parts & 1, p2 = parts & 2;
@@ -382,6 +405,16 @@ int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, 
         return fail(SDM_ERR_ALIGN, "the repeated-writes counter must be 8-byte aligned");
     ck.pb.repeats = reinterpret_cast<unsigned long long *>(exec->repeated_writes);
     const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
+    if (noalloc) {
+        if (per_step > size_t(SDM_NOALLOC_SCRATCH_BYTES))
+            return fail(SDM_ERR_WORKSPACE, "one step of these shapes needs %zu bytes of workspace; the static scratch "
+                                           "of sdm_fwd_noalloc holds %zu (use sdm_fwd with a caller workspace)",
+                        per_step, size_t(SDM_NOALLOC_SCRATCH_BYTES));
+        DeviceInfo *d0 = nullptr;
+        if ((rc = device_info(&d0)) != SDM_OK) return rc;
+        exec_static.workspace = d0->scratch;
+        exec_static.workspace_bytes = SDM_NOALLOC_SCRATCH_BYTES;
+    }
     if (!exec->workspace || exec->workspace_bytes < per_step)
         return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
                     exec->workspace ? exec->workspace_bytes : size_t(0), per_step);
@@ -448,6 +481,12 @@ int sdm_fwd(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_w
             const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank, const int32_t *valid_tokens,
             void *out, const sdm_exec *exec) {
     return fwd_run(3, P, T, C, slots, weights, beta, log_decay, gate_width, v, bank, valid_tokens, out, exec);
+}
+
+int sdm_fwd_noalloc(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,
+                    const float *beta, const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank,
+                    const int32_t *valid_tokens, void *out, const sdm_exec *exec) {
+    return fwd_run(3, P, T, C, slots, weights, beta, log_decay, gate_width, v, bank, valid_tokens, out, exec, true);
 }
 
 int sdm_fwd_phase1(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,

@@ -161,6 +161,25 @@ int sdm_fwd(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slo
             const int32_t *valid_tokens, void *out, const sdm_exec *exec);
 
 /*
+ * sdm_fwd for callers that cannot allocate (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, checks and result bits as sdm_fwd,
+ * but the workspace is a static device array inside the library, SDM_NOALLOC_SCRATCH_BYTES
+ * on each GPU it runs on (held from the library's first call on that device until the
+ * process ends). exec->workspace must be NULL and exec->workspace_bytes 0; the other exec
+ * fields are as for sdm_fwd. The call uses the largest slab of steps that fits the scratch;
+ * shapes whose single step needs more (sdm_fwd_workspace_bytes(..., 1) > the scratch size)
+ * are refused with SDM_ERR_WORKSPACE before any work. Nothing is allocated and the
+ * scratch needs no initial contents (it keeps the last call's). Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (different streams with no
+ * ordering between them) race and give undefined results.
+ */
+#define SDM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sdm_fwd_noalloc(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
+                    const sdm_weights *weights, const float *beta, const float *log_decay,
+                    int32_t gate_width, const void *v, const sdm_bank *bank,
+                    const int32_t *valid_tokens, void *out, const sdm_exec *exec);
+
+/*
  * The forward in two calls, for callers that overlap the Phase 1 of one batch with the
  * Phase 2 of another (Phase 1 reads only the slot ids, weights, gates, beta and
  * valid_tokens, never the bank, v or out). Both take exactly sdm_fwd's arguments and

@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["sdm_bwd", "sdm_bwd_workspace_bytes", "sdm_chunk_mats", "sdm_error_string",
-                                    "sdm_fwd", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_fwd_plan",
+                                    "sdm_fwd", "sdm_fwd_noalloc", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_fwd_plan",
                                     "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_product_key_topk",
                                     "sdm_product_key_topk_backward", "sdm_wy_solve"]
 
@@ -157,6 +157,33 @@ def test_fwd_rejects_out_overlapping_bank(lib):
     c.ptr["out"] = c.ptr["bank"] + 256
     rc, msg = c.run()
     assert rc == SHAPE and "overlap" in msg
+
+
+def test_noalloc_rejects_before_any_work(lib):
+    """sdm_fwd_noalloc takes no workspace (a non-NULL one is refused) and refuses shapes
+    whose single step needs more than its static scratch, both before any HIP call."""
+    from chunked_sparse_delta_amd import NOALLOC_SCRATCH_BYTES, _Bank, _Exec, _Slots, _Weights
+    lib.sdm_fwd_noalloc.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + \
+        [ctypes.c_void_p] * 5
+    lib.sdm_fwd_workspace_bytes.restype = ctypes.c_size_t
+    c = Call(lib)
+
+    def call(P, T, C, W, R, ws, ws_bytes):
+        slots = _Slots(c.ptr["kidx"], c.ptr["qidx"], W, R, 4, 4)
+        weights = _Weights(c.ptr["kval"], c.ptr["qval"])
+        bank = _Bank(c.ptr["bank"], c.M, c.hd, 0, 0)
+        ex = _Exec(None, ws, ws_bytes, None, 0, None)
+        rc = lib.sdm_fwd_noalloc(P, T, C, ctypes.byref(slots), ctypes.byref(weights), c.ptr["beta"], c.ptr["g"], W,
+                                 c.ptr["v"], ctypes.byref(bank), c.ptr["valid"], c.ptr["out"], ctypes.byref(ex))
+        return rc, lib.sdm_last_error().decode()
+
+    rc, msg = call(2, 100, 32, 4, 3, c.ptr["ws"], 1 << 20)
+    assert rc == WORKSPACE and "static scratch" in msg
+    assert lib.sdm_fwd_workspace_bytes(8, 256, 256, 256, 256, 64, 1) > NOALLOC_SCRATCH_BYTES
+    rc, msg = call(8, 256, 256, 256, 256, None, 0)
+    assert rc == WORKSPACE and "static scratch" in msg
+    rc, msg = call(2, 100, 32, 0, 3, None, 0)
+    assert rc == SHAPE, msg
 
 
 def test_fwd_rejects_too_many_token_rows(lib):
