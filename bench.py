@@ -45,7 +45,9 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, datasheet
-KERNELS = ("p1_sort", "p1_groups", "p1_reads", "p1_gram_cold", "p1_gram_hot", "wy_solve", "phase2")
+# kernel-boundary intervals of sdm_exec.events; the first is the partitioned Phase-1 kernel
+# plus the sort (which skips the chunks the partitioned kernel handled), or the fused kernel
+KERNELS = ("p1_partition_sort", "p1_groups", "p1_reads", "p1_gram_cold", "p1_gram_hot", "wy_solve", "phase2")
 
 
 def parse():

@@ -20,8 +20,11 @@ hipError_t phase1_prepare();
 hipError_t phase2_prepare();
 hipError_t wy_prepare();
 hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev, bool fused,
-                         const WyArgs &wa);
+                         const WyArgs &wa, int lognp);
 bool phase1_fused(const ChunkLayout &L, int C, int lds_limit);
+hipError_t part_prepare();
+size_t part_smem_bytes();
+int part_lognp(int64_t E, int64_t F, int key_bits);
 hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
                      int64_t stride, int64_t bstride, hipStream_t st);
 hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom &g, hipStream_t st);
@@ -97,6 +100,7 @@ int device_info(DeviceInfo **out) {
         if ((e = phase1_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 1)");
         if ((e = phase2_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 2)");
         if ((e = wy_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (solve)");
+        if ((e = part_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (phase 1, partitioned)");
         if ((e = bwd_prepare()) != hipSuccess) return hip_fail(e, "hipFuncSetAttribute (backward)");
         void *sp = nullptr;
         if ((e = hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch))) != hipSuccess)
@@ -125,6 +129,21 @@ int sort_passes(int64_t M) {
 int sort_digit(int64_t M) {
     const int p = sort_passes(M), d = (key_bits(M) + p - 1) / p;
     return d < 1 ? 1 : d;
+}
+
+// Phase 1 of chunks that do not run fused: the partitioned kernel (LDS-resident slot
+// partitions) first, unless SDM_P1_PART=0; returns log2 of its partition count (shapes
+// only; SDM_P1_NP_LOG overrides it, for sweeps), or -1 with pb.part_on cleared.
+int plan_part(Problem &pb, const ChunkLayout &L, bool fused) {
+    pb.part_on = 0;
+    if (fused) return -1;
+    const char *env = getenv("SDM_P1_PART");
+    if (env && env[0] == '0') return -1;
+    int lg = part_lognp(L.E, L.F, pb.key_bits);
+    const char *ov = getenv("SDM_P1_NP_LOG");
+    if (ov && ov[0] >= '0' && ov[0] <= '6') lg = ov[0] - '0';
+    pb.part_on = 1;
+    return lg;
 }
 
 struct Checked {
@@ -296,6 +315,8 @@ int sdm_fwd_plan(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t 
     plan->phase2_mode = g.mode;
     plan->phase2_lds_bytes = int32_t(phase2_lds_bytes(lay, C, g.nv, V, es, g.mode, M));
     plan->phase1_fused = phase1_fused(lay, C, dev->lds_per_block) ? 1 : 0;
+    pb.key_bits = key_bits(M);
+    plan->phase1_partitions_log2 = plan_part(pb, lay, plan->phase1_fused != 0);
     plan->lds_limit = dev->lds_per_block;
     plan->lds_default = dev->lds_default;
     return SDM_OK;
@@ -439,6 +460,7 @@ int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, 
                     per_step * size_t(Nt), exec->workspace_bytes);
     hipStream_t st = static_cast<hipStream_t>(exec->stream);
     const bool fused = phase1_fused(ck.lay, C, dev->lds_per_block);
+    const int lognp = plan_part(ck.pb, ck.lay, fused);
     hipEvent_t *ev = nullptr;
     if (parts == 3 && exec->events && exec->num_events >= SDM_TIMING_EVENTS)
         ev = reinterpret_cast<hipEvent_t *>(exec->events);
@@ -454,7 +476,7 @@ int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, 
                         w + sl.lay.off_QX, C, sl.lay.words, sl.lay.words};
         hipError_t e = hipSuccess;
         if (p1) {
-            e = launch_phase1(ck.pb, sl, st, sev, fused, wa);
+            e = launch_phase1(ck.pb, sl, st, sev, fused, wa, lognp);
             if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
             if (sev && (e = hipEventRecord(sev[5], st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
             if (!fused) {
@@ -565,7 +587,8 @@ int sdm_chunk_mats(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, cons
         const WyArgs wa{w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X,
                         w + sl.lay.off_QX, C, sl.lay.words, sl.lay.words};
         const bool fused = phase1_fused(ck.lay, C, dev->lds_per_block);
-        hipError_t e = launch_phase1(ck.pb, sl, st, nullptr, fused, wa);
+        const int lognp = plan_part(ck.pb, ck.lay, fused);
+        hipError_t e = launch_phase1(ck.pb, sl, st, nullptr, fused, wa, lognp);
         if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
         if (!fused) {
             e = launch_wy(wa.A, wa.beta, wa.QK, wa.X, wa.QX, C, int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);

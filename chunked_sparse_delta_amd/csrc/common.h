@@ -12,7 +12,7 @@ constexpr int kMaxWidth = 256;
 constexpr int kXcds = 8;           // MI355X: 8 XCDs of 32 CUs, workgroups dealt round-robin
 constexpr int kHotMin = 16;        // write groups of at least this many members go to the dense Gram
 constexpr float kHotSpan = 60.0f;  // ... if their log-decays stay within this of the first member's
-constexpr int kHotCap = 256;       // at most this many hot groups per chunk (the rest stay cold)
+constexpr int kHotCap = 512;       // at most this many hot groups per chunk (the rest stay cold)
 
 // ---------------------------------------------------------------------------------------
 // Element types. bf16 is carried as its 16-bit pattern.
@@ -111,6 +111,20 @@ template <typename T> struct Vec<T, 1> {
     static __device__ __forceinline__ void store(T *p, const float (&o)[1]) { *p = from_f32<T>(o[0]); }
 };
 
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
+
+// The lanes of the wavefront whose digit (db low bits of d) equals this lane's, among the
+// lanes with ok set: one ballot per digit bit.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool ok, int db) {
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < db; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+    }
+    return peers;
+}
+
 // ---------------------------------------------------------------------------------------
 // Problem description passed by value to every kernel.
 // ---------------------------------------------------------------------------------------
@@ -134,6 +148,8 @@ struct Problem {
     int64_t bank_stride;     // elements from one stream's bank to the next (0: shared bank)
     void *out;               // [P, T, hd]
     unsigned long long *repeats;   // optional device counter of repeated write slots
+    int32_t part_on;         // Phase 1 of this call runs the partitioned kernel first: the sorting
+                             // kernels then handle only the chunks it left to them (meta[7] = 1)
 };
 
 // Slot id i of an int32 or int64 id array (ids of valid calls lie in [0, M), M < 2^31).
@@ -183,11 +199,16 @@ struct ChunkLayout {
     int64_t off_gr;       // [F] f32: gather weight q exp(Lr), read-entry order
     int64_t off_qid;      // [F] i32: read slot ids of the chunk, entry order (copy of the input)
     int64_t off_rcr;      // [C][R] int4: cold read {a, end, bits q, bits Lr} (a == end: none)
-    int64_t off_ka;       // [C][HP] f32, HP = meta[5] (<= HCAP): token t's write of hot group h, k exp(L - L_ref)
-    int64_t off_kb;       // [C][HP] f32: the same write's k exp(L_ref - L)
-    int64_t off_qa;       // [C][HP] f32: token t's reads of hot group h, sum of q exp(Lr - L_ref) in read order
+    int64_t off_ka;       // [C][HCAP] f32: token t's write of hot group h (< HP = meta[5]), k exp(L - L_ref)
+    int64_t off_kb;       // [C][HCAP] f32: the same write's k exp(L_ref - L)
+    int64_t off_qa;       // [C][HCAP] f32: token t's reads of hot group h, sum of q exp(Lr - L_ref) in read order
+    int64_t off_plist;    // [E + F] int4: the partitioned path's slot-partition lists {slot, code, bits of k
+                          //   or q, bits of g}, then the entries' output records in the same slots
+    int64_t off_oval;     // [E + F] u32: the partitioned path's gather weight of each list slot
+    int64_t off_inv;      // [E + F] i32: list slot of each entry (token-major, a token's writes then reads);
+                          //   these three share their words with the arrays only the sorting path uses
     int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups, groups with >= kHotMin members,
-                          //   HP (hot groups rounded up to 16)
+                          //   HP (hot groups rounded up to 16), -, 1 if the chunk took the sorting path
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
     // [stage0, stage1): every array Phase 2 reads (records, weights, ids, meta, beta, X, QX),
@@ -216,19 +237,25 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.HCAP = ((L.HMAX + 15) / 16) * 16 < kHotCap ? ((L.HMAX + 15) / 16) * 16 : kHotCap;
     int64_t o = 0;
     auto take = [&](int64_t n) { int64_t r = o; o += align_words(n); return r; };
+    // the arrays only the sorting path uses, then (in the same words) the partition lists
+    // of the partitioned path: a chunk takes one path or the other
     L.off_key0 = take(L.E);
     L.off_val0 = take(L.E);
     L.off_key1 = take(L.E);
     L.off_val1 = take(L.E);
-    L.off_spk = take(4 * L.E);
     L.off_shead = take(L.E);
     L.off_sgrp = take(L.E);
     L.off_gpos = take(L.E + 1);
-    L.off_ecr = take(4 * L.E);
     L.off_sgh = take(4 * L.E);
     L.off_ghot = take(L.E);
     L.off_hgrp = take(L.HMAX);
     L.off_bstart = take(L.NB + 1);
+    L.off_plist = 0;
+    L.off_oval = align_words(4 * (L.E + L.F));
+    L.off_inv = L.off_oval + align_words(L.E + L.F);
+    if (o < L.off_inv + align_words(L.E + L.F)) o = L.off_inv + align_words(L.E + L.F);
+    L.off_spk = take(4 * L.E);
+    L.off_ecr = take(4 * L.E);
     L.off_rcr = take(4 * L.F);
     L.off_ka = take(int64_t(C) * L.HCAP);
     L.off_kb = take(int64_t(C) * L.HCAP);

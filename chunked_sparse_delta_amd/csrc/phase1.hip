@@ -30,7 +30,6 @@
 
 namespace sdm {
 
-__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
 
 // Stable LSD radix sort of one chunk's write entries by slot id, in passes of at most
 // kSortDigit bits. Wave w owns a fixed contiguous segment of the input of every pass: it
@@ -39,16 +38,6 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) 
 // wave scatters its segment in order, ranking equal digits within a wavefront by lane
 // (ballot match) and advancing its own per-digit positions. Two block barriers per pass.
 constexpr int kSortDigit = 9;
-
-__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool ok, int db) {
-    uint64_t peers = __ballot(ok);
-    for (int b = 0; b < db; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bb = __ballot(bit);
-        peers &= bit ? bb : ~bb;
-    }
-    return peers;
-}
 
 template <int BLOCK>
 constexpr size_t sort_smem_bytes() { return size_t(BLOCK / kWave) * (1 << kSortDigit) * 4 + (1 << kSortDigit) / kWave * 4; }
@@ -418,9 +407,10 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
         meta[4] = nc;
         meta[5] = HP;
     }
-    for (int32_t x = tid; x < C * HP; x += BLOCK) {
-        Ka[x] = 0.0f;
-        Kb[x] = 0.0f;
+    for (int32_t x = tid; x < C * HP; x += BLOCK) {   // rows [C][HCAP], columns < HP read
+        const int32_t r = x / HP, c = x - r * HP;
+        Ka[r * L.HCAP + c] = 0.0f;
+        Kb[r * L.HCAP + c] = 0.0f;
     }
     __syncthreads();
 
@@ -436,8 +426,8 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
         const int32_t Lref = h >= 0 ? spk[a].w : 0;   // the read lookup needs it for hot groups only
         if (h >= 0) {
             const float d = __int_as_float(pk.w) - __int_as_float(Lref), kv = __int_as_float(pk.z);
-            Ka[pk.y * HP + h] = kv * expf(d);
-            Kb[pk.y * HP + h] = kv * expf(-d);
+            Ka[pk.y * L.HCAP + h] = kv * expf(d);
+            Kb[pk.y * L.HCAP + h] = kv * expf(-d);
         } else {
             rec = make_int4(a, m, pk.z, pk.w);
         }
@@ -560,7 +550,7 @@ __device__ __forceinline__ void reads_token_k(const Problem &pb, const Slab &sl,
         }
     }
     __builtin_amdgcn_wave_barrier();
-    for (int h = lane; h < HP; h += kWave) Qa[int64_t(i) * HP + h] = qr[h];
+    for (int h = lane; h < HP; h += kWave) Qa[int64_t(i) * L.HCAP + h] = qr[h];
 }
 
 __device__ __forceinline__ void reads_token(const Problem &pb, const Slab &sl, int64_t n, int i, float *qr,
@@ -739,8 +729,8 @@ __device__ __forceinline__ void hot_tiles(const Problem &pb, const Slab &sl, int
         f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int hb = 0; hb < HP; hb += 16) {
             float4 av = make_float4(0.0f, 0.0f, 0.0f, 0.0f), bv = av;
-            if (ra < C) av = *reinterpret_cast<const float4 *>(Aop + int64_t(ra) * HP + hb + ko);
-            if (rb < C) bv = *reinterpret_cast<const float4 *>(Kb + int64_t(rb) * HP + hb + ko);
+            if (ra < C) av = *reinterpret_cast<const float4 *>(Aop + int64_t(ra) * L.HCAP + hb + ko);
+            if (rb < C) bv = *reinterpret_cast<const float4 *>(Kb + int64_t(rb) * L.HCAP + hb + ko);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
@@ -760,20 +750,29 @@ __device__ __forceinline__ void hot_tiles(const Problem &pb, const Slab &sl, int
 // Kernels: one stage per launch (large chunks), or every stage and the solve in one
 // workgroup per chunk (small chunks), so that a small chunk pays one launch instead of six.
 // ---------------------------------------------------------------------------------------
+// Whether chunk n was handled by the partitioned kernel (phase1_part.hip), which ran first
+// in this call and marked the chunks it left to the sorting kernels with meta[7] = 1.
+__device__ __forceinline__ bool done_by_part(const Problem &pb, const Slab &sl, int64_t n) {
+    return pb.part_on && reinterpret_cast<const int32_t *>(sl.chunk(n) + sl.lay.off_meta)[7] == 0;
+}
+
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void p1_sort_kernel(Problem pb, Slab sl) {
     __shared__ __align__(16) char smem[sort_smem_bytes<BLOCK>()];
+    if (done_by_part(pb, sl, blockIdx.x)) return;
     sort_chunk<BLOCK>(pb, sl, blockIdx.x, smem);
 }
 
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void p1_groups_kernel(Problem pb, Slab sl) {
     __shared__ __align__(16) char smem[sizeof(GroupsSmem<BLOCK / kWave>)];
+    if (done_by_part(pb, sl, blockIdx.x)) return;
     groups_chunk<BLOCK>(pb, sl, blockIdx.x, smem);
 }
 
 __global__ __launch_bounds__(kReadWaves * kWave) void p1_reads_kernel(Problem pb, Slab sl) {
     __shared__ float qrow[kReadWaves][kHotCap];
+    if (done_by_part(pb, sl, blockIdx.y)) return;
     const int wave = threadIdx.x >> 6;
     reads_token(pb, sl, blockIdx.y, blockIdx.x * kReadWaves + wave, qrow[wave]);
 }
@@ -906,11 +905,15 @@ hipError_t phase1_prepare() {
                                hipFuncAttributeMaxDynamicSharedMemorySize, int(fused_smem_bytes(kMaxChunk)));
 }
 
+hipError_t launch_phase1_part(const Problem &pb, const Slab &sl, int lognp, hipStream_t st);
+
 // ev: nullptr, or 5 events recorded before each of the five kernels (fused: the first
-// before the fused kernel, the other four after it). fused: Phase 1 and the solve in one
-// kernel (wa: the solve's arguments); otherwise the caller launches the solve.
+// before the fused kernel, the other four after it; partitioned: the first before the
+// partitioned kernel, whose time counts with the sort's). fused: Phase 1 and the solve in
+// one kernel (wa: the solve's arguments); otherwise the caller launches the solve.
+// lognp >= 0 (with pb.part_on): the partitioned kernel runs first with 2^lognp partitions.
 hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipEvent_t *ev, bool fused,
-                         const WyArgs &wa) {
+                         const WyArgs &wa, int lognp) {
     const unsigned nch = unsigned(int64_t(pb.P) * sl.steps);
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
@@ -919,6 +922,9 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
         for (int k = 1; ev && k < 5; ++k)
             if ((e = hipEventRecord(ev[k], st)) != hipSuccess) return e;
         return hipGetLastError();
+    }
+    if (pb.part_on) {
+        if ((e = launch_phase1_part(pb, sl, lognp, st)) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(p1_sort_kernel<kSortBlock>, dim3(nch), dim3(kSortBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;

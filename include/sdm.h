@@ -252,6 +252,9 @@ typedef struct {
                                   column slice of the bank held in LDS for the whole call */
     int32_t phase2_lds_bytes;  /* LDS per Phase-2 workgroup */
     int32_t phase1_fused;      /* 1: Phase 1 and the solve run as one kernel, one workgroup per chunk */
+    int32_t phase1_partitions_log2; /* >= 0: chunks not fused run Phase 1 in 2^this slot partitions
+                                  held in LDS one after another (one workgroup per chunk); -1: by
+                                  sorting every write entry of a chunk in memory */
     int32_t lds_limit;         /* LDS bytes per workgroup the plan may use */
     int32_t lds_default;       /* the device's default per-workgroup LDS limit */
 } sdm_plan;

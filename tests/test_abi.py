@@ -63,12 +63,12 @@ def test_workspace_bytes(lib):
     # 112 B per write entry, 24 B per read entry, 16 B per chunk-matrix element, a slot
     # search index of about one word per write entry (a power of two, at most 2^14), 20 B
     # per possible group of >= 16 members and the three dense hot operands [C][HCAP]
-    # (HCAP = that count rounded up to 16, at most 256) (+ alignment)
+    # (HCAP = that count rounded up to 16, at most 512) (+ alignment)
     per_chunk = step / 8
     E, F, C2, C = 64 * 8, 64 * 8, 64 * 64, 64
     NB = 512
     hmax = E // 16 + 1
-    hcap = min(256, (hmax + 15) // 16 * 16)
+    hcap = min(512, (hmax + 15) // 16 * 16)
     base = 112 * E + 24 * F + 16 * C2 + 4 * (NB + 1) + 20 * hmax + 12 * C * hcap
     assert base <= per_chunk <= base + 40 * 256
 

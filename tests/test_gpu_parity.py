@@ -53,8 +53,20 @@ def test_wy_solve_matches_inverse(gpu, C):
     small(P=1, T=96, C=48, hd=8, M=40, W=5, R=4, ids="zipf", zipf_s=1.3, ragged=True, index=6),
     # large log-decays: big groups whose decay span exceeds the dense path's bound stay cold
     small(P=1, T=64, C=64, hd=8, M=5, W=2, R=2, decay_scale=4.0, index=8),
-], ids=["tiny", "gate1", "bf16zipf", "allhot", "mixed", "bigdecay"])
-def test_chunk_intermediates_match_chunk_algebra(gpu, wl):
+    # chunks of more than 1024 entries: Phase 1 in slot partitions (or by sorting)
+    small(P=1, T=60, C=32, hd=8, M=300, W=40, R=36, ids="zipf", ragged=True, index=43),
+    small(P=1, T=48, C=48, hd=8, M=500, W=24, R=24, ids="mixed", weight_scale=-1.0, index=44),
+    small(P=1, T=64, C=32, hd=8, M=60, W=40, R=40, index=45),
+], ids=["tiny", "gate1", "bf16zipf", "allhot", "mixed", "bigdecay", "part_zipf", "part_mixed", "part_fewslots"])
+@pytest.mark.parametrize("part", ["1", "1:3", "0"])
+def test_chunk_intermediates_match_chunk_algebra(gpu, wl, part, monkeypatch):
+    """Phase 1 and the solve against O2's chunk algebra, on every Phase-1 path: fused (small
+    chunks), in slot partitions (default count, or 8), and by sorting."""
+    monkeypatch.setenv("SDM_P1_PART", part[0])
+    if ":" in part:
+        monkeypatch.setenv("SDM_P1_NP_LOG", part.split(":")[1])
+    else:
+        monkeypatch.delenv("SDM_P1_NP_LOG", raising=False)
     import oracle
     from oracle import chunk_algebra
     from chunked_sparse_delta_amd import chunk_mats
@@ -277,9 +289,10 @@ def test_plan_reports_phase2_modes(gpu, monkeypatch):
 ], ids=["bf16_P8", "f32_hot"])
 def test_phase1_fusion_does_not_change_bits(gpu, wl, monkeypatch):
     """Phase 1 and the solve fused into one workgroup per chunk give the same bits as the
-    separate kernels (the per-chunk arithmetic is the same; only the launch differs)."""
+    separate sorting kernels (the per-chunk arithmetic is the same; only the launch differs)."""
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
+    monkeypatch.setenv("SDM_P1_PART", "0")
     results = []
     for fused in ("0", "1"):
         monkeypatch.setenv("SDM_P1_FUSED", fused)
@@ -287,6 +300,50 @@ def test_phase1_fusion_does_not_change_bits(gpu, wl, monkeypatch):
         results.append((gu.bits(o), gu.bits(b)))
     gu.parity(o, b, inp, wl.C, "fused phase 1")
     assert np.array_equal(results[0][0], results[1][0]) and np.array_equal(results[0][1], results[1][1])
+
+
+PART = [
+    small(P=3, T=300, C=128, hd=32, M=2000, W=24, R=24, ids="zipf", ragged=True, index=46),
+    small(P=2, T=600, C=256, hd=16, M=4000, W=64, R=48, dtype="bf16", ids="mixed", weight_scale=-1.0, index=47),
+    small(P=4, T=200, C=64, hd=24, M=50, W=48, R=40, ragged=True, weight_scale=-1.0, index=48),  # long groups
+    small(P=2, T=130, C=64, hd=8, M=300, W=32, R=32, gate_width=1, index=49),
+]
+
+
+@pytest.mark.parametrize("wl", PART, ids=["zipf_C128", "mixed_C256_bf16", "fewslots", "gate1"])
+def test_phase1_paths_match_the_oracle(gpu, wl, monkeypatch):
+    """Chunks of more than 1024 entries run Phase 1 in slot partitions held in LDS, one
+    partition after another; any partition count (1 to 64) and the sorting path (also the
+    fallback for a partition larger than the LDS holds: one partition for every slot of a big
+    chunk forces it) give results within the oracle's bar, each bitwise reproducible."""
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    for part, nplog in (("1", None), ("1", "0"), ("1", "3"), ("1", "6"), ("0", None)):
+        monkeypatch.setenv("SDM_P1_PART", part)
+        if nplog is None:
+            monkeypatch.delenv("SDM_P1_NP_LOG", raising=False)
+        else:
+            monkeypatch.setenv("SDM_P1_NP_LOG", nplog)
+        o, b = gu.run(t, wl.C)
+        gu.parity(o, b, inp, wl.C, f"phase 1 part={part} np_log={nplog}")
+        o2, b2 = gu.run(t, wl.C)
+        assert np.array_equal(gu.bits(o), gu.bits(o2)) and np.array_equal(gu.bits(b), gu.bits(b2)), (part, nplog)
+
+
+def test_phase1_partition_overflow_takes_the_sorting_path(gpu, monkeypatch):
+    """A chunk with a partition of more entries than the LDS holds (3072) is left to the
+    sorting kernels by the partitioned kernel: the result is then bit for bit the sorting
+    path's (one partition forced on chunks of 256 x (16 + 16) = 8192 entries)."""
+    wl = small(P=2, T=512, C=256, hd=16, M=3000, W=16, R=16, ids="zipf", index=50)
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    monkeypatch.setenv("SDM_P1_PART", "0")
+    o0, b0 = gu.run(t, wl.C)
+    monkeypatch.setenv("SDM_P1_PART", "1")
+    monkeypatch.setenv("SDM_P1_NP_LOG", "0")
+    o1, b1 = gu.run(t, wl.C)
+    gu.parity(o1, b1, inp, wl.C, "overflow")
+    assert np.array_equal(gu.bits(o0), gu.bits(o1)) and np.array_equal(gu.bits(b0), gu.bits(b1))
 
 
 # ------------------------------------------------------------------ forward variants
@@ -313,19 +370,25 @@ def test_int64_ids_give_the_same_bits(gpu, wl):
     small(P=3, T=100, C=32, hd=20, M=50, W=4, R=3, ragged=True, index=36),
     small(P=2, T=300, C=128, hd=32, M=700, W=16, R=16, index=37),
 ], ids=["bf16_staged", "f32_partial", "f32_memory"])
-def test_shared_bank_matches_per_stream_banks(gpu, wl):
+def test_shared_bank_matches_per_stream_banks(gpu, wl, monkeypatch):
     """One bank shared by every stream (sdm_write_read with shared_bank=True, page 21,
     memory_ops.py docstring), the streams' slots interleaved and disjoint: the readings and
-    each stream's rows equal those of per-stream banks bit for bit. (A workgroup writing a
-    whole slice back, as the resident mode does, would overwrite the other streams' rows.)"""
+    each stream's rows equal those of per-stream banks bit for bit when Phase 1 sorts every
+    chunk (relabeling slot s of stream p as s * P + p keeps each chunk's slot order), and are
+    within the oracle's bar on the default path, whose slot partitions (slot mod 2^k) the
+    relabeling reshuffles. (A workgroup writing a whole slice back, as the resident mode
+    does, would overwrite the other streams' rows.)"""
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
-    o, b = gu.run(t, wl.C)
-    gu.parity(o, b, inp, wl.C, "per-stream banks")
     sh = gu.to_torch(dict(workloads.shared_bank_inputs(inp), dtype=inp["dtype"]), gpu)
     assert sh["bank"].shape == (wl.P * wl.M, wl.hd)
-    o2, b2 = gu.run(sh, wl.C, shared_bank=True)
     P, M, hd = wl.P, wl.M, wl.hd
+    o2, b2 = gu.run(sh, wl.C, shared_bank=True)
+    gu.parity(o2, b2.reshape(M, P, hd).permute(1, 0, 2).contiguous(), inp, wl.C, "shared bank")
+    monkeypatch.setenv("SDM_P1_PART", "0")
+    o, b = gu.run(t, wl.C)
+    gu.parity(o, b, inp, wl.C, "per-stream banks")
+    o2, b2 = gu.run(sh, wl.C, shared_bank=True)
     assert np.array_equal(gu.bits(o2), gu.bits(o))
     assert np.array_equal(gu.bits(b2.reshape(M, P, hd).permute(1, 0, 2).contiguous()), gu.bits(b))
 
