@@ -111,9 +111,9 @@ def _load():
             lib.sdm_product_key_topk.restype = ctypes.c_int
             lib.sdm_product_key_topk_backward.argtypes = [i64, p, p, i32, p, i32, i32, p, p]
             lib.sdm_product_key_topk_backward.restype = ctypes.c_int
-            lib.sdm_bwd_workspace_bytes.argtypes = [i32] * 5 + [i64, i32, i32]
+            lib.sdm_bwd_workspace_bytes.argtypes = [i32] * 5 + [i64, i32, i32, i32]
             lib.sdm_bwd_workspace_bytes.restype = ctypes.c_size_t
-            lib.sdm_bwd.argtypes = [i32, i32, p, p, p, p, i32, p, p, p, p, p, p]
+            lib.sdm_bwd.argtypes = [i32, i32, p, p, p, p, i32, p, p, p, p, p, i32, p]
             lib.sdm_bwd.restype = ctypes.c_int
             lib.sdm_error_string.argtypes = [ctypes.c_int]
             lib.sdm_error_string.restype = ctypes.c_char_p
@@ -304,19 +304,34 @@ class _Grads(ctypes.Structure):
                 ("log_decay", ctypes.c_void_p), ("write", ctypes.c_void_p), ("read", ctypes.c_void_p)]
 
 
+# snapshot_quant modes of sdm_write_read (page 21, memory_ops.py): SDM_SNAP_* of include/sdm.h
+SNAPSHOT_QUANT = {"none": 0, "fp8": 1, "int4": 2, "bf16": 3}
+
+
+def _snap_mode(snapshot_quant: str) -> int:
+    if snapshot_quant not in SNAPSHOT_QUANT:
+        raise ValueError(f"snapshot_quant must be one of {tuple(SNAPSHOT_QUANT)}, got {snapshot_quant!r}")
+    return SNAPSHOT_QUANT[snapshot_quant]
+
+
 def bwd_workspace_bytes(P: int, T: int, W: int, R: int, hd: int, M: int, dtype: torch.dtype = torch.float32,
-                        shared_bank: bool = False) -> int:
-    """Workspace bytes sdm_bwd needs (0 for rejected shapes)."""
-    return int(_load().sdm_bwd_workspace_bytes(P, T, W, R, hd, M, _DTYPES.get(dtype, -1), 1 if shared_bank else 0))
+                        shared_bank: bool = False, snapshot_quant: str = "none") -> int:
+    """Workspace bytes sdm_bwd needs (0 for rejected shapes or snapshot modes)."""
+    return int(_load().sdm_bwd_workspace_bytes(P, T, W, R, hd, M, _DTYPES.get(dtype, -1), 1 if shared_bank else 0,
+                                               _snap_mode(snapshot_quant)))
 
 
 def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
             log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, grad_out: torch.Tensor, *,
             grad_bank: torch.Tensor | None = None, valid_tokens: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None, stream=None, events=None, shared_bank: bool = False) -> dict:
+            workspace: torch.Tensor | None = None, stream=None, events=None, shared_bank: bool = False,
+            snapshot_quant: str = "none") -> dict:
     """Backward of sdm_fwd. ``bank`` (float32 or bfloat16; [P, M, hd], or a shared [M, hd]
     with ``shared_bank=True``) holds the bank the forward STARTED from; a float32 bank is
-    replayed and restored exactly, a bfloat16 one only read. ``grad_out`` [P, T, hd] (bank
+    replayed and restored (exactly with ``snapshot_quant="none"``; with "bf16" its saved rows
+    are bfloat16, the reverse sweep works from them, and the rows the forward wrote come back
+    rounded to bfloat16), a bfloat16 one only read. "fp8" and "int4" are refused (SdmError,
+    SDM_ERR_UNSUPPORTED). ``grad_out`` [P, T, hd] (bank
     dtype) is the gradient of the readings; ``grad_bank`` (float32, the bank's shape,
     optional) that of the final bank, overwritten in place with the gradient with respect
     to the initial bank (a zero tensor is allocated if omitted). ``events``: optional ctypes
@@ -336,15 +351,17 @@ def sdm_bwd(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: tor
                log_decay=torch.empty((P, T, G), dtype=torch.float32, device=dev),
                k_val=torch.empty((P, T, W), dtype=torch.float32, device=dev),
                q_val=torch.empty((P, T, R), dtype=torch.float32, device=dev))
+    mode = _snap_mode(snapshot_quant)
     if workspace is None:
-        workspace = _workspace(bwd_workspace_bytes(P, T, W, R, hd, M, bank.dtype, bank.dim() == 2), dev)
+        need = bwd_workspace_bytes(P, T, W, R, hd, M, bank.dtype, bank.dim() == 2, snapshot_quant)
+        workspace = _workspace(need if need else 256, dev)   # 0: the call itself reports why
     gr = _Grads(*(out[k].data_ptr() for k in ("bank", "v", "beta", "log_decay", "k_val", "q_val")))
     bk = _Bank(bank.data_ptr(), M, hd, _DTYPES[bank.dtype], 1 if bank.dim() == 2 else 0)
     ex = _Exec(_stream_ptr(stream), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                None if events is None else ctypes.cast(events, ctypes.c_void_p), 0 if events is None else len(events),
                None)
     rc = lib.sdm_bwd(P, T, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G, _ptr(v),
-                     ctypes.byref(bk), _ptr(valid_tokens), _ptr(grad_out), ctypes.byref(gr), ctypes.byref(ex))
+                     ctypes.byref(bk), _ptr(valid_tokens), _ptr(grad_out), ctypes.byref(gr), mode, ctypes.byref(ex))
     _check_rc(lib, rc)
     return out
 
@@ -355,12 +372,13 @@ class _SDMWriteRead(torch.autograd.Function):
     was, which the backward replays from."""
 
     @staticmethod
-    def forward(ctx, bank, k_val, v, beta, log_decay, q_val, k_idx, q_idx, chunk, valid_tokens, shared_bank):
+    def forward(ctx, bank, k_val, v, beta, log_decay, q_val, k_idx, q_idx, chunk, valid_tokens, shared_bank,
+                snapshot_quant):
         bank0 = bank.detach().clone()
         out = sdm_fwd(bank, k_idx, k_val.detach(), v.detach(), beta.detach(), log_decay.detach(), q_idx,
                       q_val.detach(), chunk=chunk, valid_tokens=valid_tokens, shared_bank=shared_bank)
         ctx.save_for_backward(bank0, k_val, v, beta, log_decay, q_val, k_idx, q_idx)
-        ctx.valid_tokens, ctx.shared_bank = valid_tokens, shared_bank
+        ctx.valid_tokens, ctx.shared_bank, ctx.snapshot_quant = valid_tokens, shared_bank, snapshot_quant
         return out
 
     @staticmethod
@@ -368,9 +386,10 @@ class _SDMWriteRead(torch.autograd.Function):
         bank0, k_val, v, beta, log_decay, q_val, k_idx, q_idx = ctx.saved_tensors
         go = grad_out.to(bank0.dtype).contiguous()
         g = sdm_bwd(bank0, k_idx, k_val.detach(), v.detach(), beta.detach(), log_decay.detach(), q_idx,
-                    q_val.detach(), go, valid_tokens=ctx.valid_tokens, shared_bank=ctx.shared_bank)
+                    q_val.detach(), go, valid_tokens=ctx.valid_tokens, shared_bank=ctx.shared_bank,
+                    snapshot_quant=ctx.snapshot_quant)
         need = ctx.needs_input_grad   # (bank, k_val, v, beta, log_decay, q_val, ...)
-        out = [None] * 11
+        out = [None] * 12
         for i, (name, like) in enumerate((("k_val", k_val), ("v", v), ("beta", beta), ("log_decay", log_decay),
                                           ("q_val", q_val)), start=1):
             if need[i]:
@@ -381,12 +400,17 @@ class _SDMWriteRead(torch.autograd.Function):
 def sdm_write_read(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor, v: torch.Tensor,
                    beta: torch.Tensor, log_decay: torch.Tensor, q_idx: torch.Tensor, q_val: torch.Tensor, *,
                    chunk: int = 64, valid_tokens: torch.Tensor | None = None,
-                   shared_bank: bool = False) -> torch.Tensor:
+                   shared_bank: bool = False, snapshot_quant: str = "none") -> torch.Tensor:
     """The memory op for autograd: returns the readings and advances ``bank`` in place, as
     sdm_fwd does; when grad mode is on and k_val, v, beta, log_decay or q_val requires grad,
-    the readings' backward is sdm_bwd (gradients cast to the inputs' dtypes). The bank is
-    state: it receives no gradient here (it must not require grad); sdm_bwd gives the
-    gradient of the initial bank to callers that need it."""
+    the readings' backward is sdm_bwd (gradients cast to the inputs' dtypes; its saved rows
+    stored as ``snapshot_quant``, "none" or "bf16"). The bank is state: it receives no
+    gradient here (it must not require grad); sdm_bwd gives the gradient of the initial bank
+    to callers that need it. For a bfloat16 bank the backward is the derivative of the
+    per-token loop at the given inputs, the forward's roundings to bfloat16 taken as the
+    identity (their derivative almost everywhere in the sense that matters for training:
+    the rounding is a storage format, not part of the function the loop defines)."""
+    _snap_mode(snapshot_quant)
     needs = torch.is_grad_enabled() and any(t.requires_grad for t in (k_val, v, beta, log_decay, q_val))
     if bank.requires_grad:
         raise ValueError("sdm_write_read advances the bank in place: the bank must not require grad "
@@ -395,7 +419,7 @@ def sdm_write_read(bank: torch.Tensor, k_idx: torch.Tensor, k_val: torch.Tensor,
         return sdm_fwd(bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, chunk=chunk,
                        valid_tokens=valid_tokens, shared_bank=shared_bank)
     return _SDMWriteRead.apply(bank, k_val, v, beta, log_decay, q_val, k_idx, q_idx, chunk, valid_tokens,
-                               shared_bank)
+                               shared_bank, snapshot_quant)
 
 
 def _fwd_part(part: int, bank, k_idx, k_val, v, beta, log_decay, q_idx, q_val, *, chunk, valid_tokens, out,

@@ -635,11 +635,13 @@ struct BwdSizes {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64_t M, int32_t dtype, bool shared) {
+// snap_es: bytes per saved element (4 float32, 2 bfloat16 snapshot rows)
+BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64_t M, int32_t dtype, bool shared,
+                   int snap_es) {
     const int S = sdm::bwd_slice_cols(P, hd, W, R);
     const int64_t NS = (hd + S - 1) / S;
     BwdSizes z{};
-    z.snap = align256(size_t(P) * size_t(NS) * size_t(S) * size_t(T) * size_t(W) * 4);
+    z.snap = align256(size_t(P) * size_t(NS) * size_t(S) * size_t(T) * size_t(W) * size_t(snap_es));
     z.lead = align256(size_t(P) * size_t(T) * size_t(R) * 8);
     z.part = align256(size_t(P) * size_t(NS) * size_t(T) * size_t(sdm::bwd_parts(W, R)) * 4);
     z.pairs = align256(size_t(P) * size_t((T + 1) / 2) * 4);
@@ -650,19 +652,35 @@ BwdSizes bwd_sizes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64
 
 }  // namespace
 
+// Bytes per saved snapshot element for a supported mode on a bank of dtype: bfloat16 rows
+// on a float32 bank, float32 otherwise (a bfloat16 bank runs "bf16" as "none", the pages'
+// effective_snapshot_quant, page 21); 0 for a mode that is refused.
+static int snap_elem_bytes(int32_t mode, int32_t dtype) {
+    if (mode == SDM_SNAP_NONE) return 4;
+    if (mode == SDM_SNAP_BF16) return dtype == SDM_F32 ? 2 : 4;
+    return 0;
+}
+
 size_t sdm_bwd_workspace_bytes(int32_t P, int32_t T, int32_t W, int32_t R, int32_t hd, int64_t rows, int32_t dtype,
-                               int32_t shared) {
+                               int32_t shared, int32_t snapshot_quant) {
     if (check_shape(P, T, 16, W, R, hd) != SDM_OK || rows < 1 || (dtype != SDM_F32 && dtype != SDM_BF16) ||
-        (shared != 0 && shared != 1))
+        (shared != 0 && shared != 1) || snap_elem_bytes(snapshot_quant, dtype) == 0)
         return 0;
-    return bwd_sizes(P, T, W, R, hd, rows, dtype, shared == 1).total;
+    return bwd_sizes(P, T, W, R, hd, rows, dtype, shared == 1, snap_elem_bytes(snapshot_quant, dtype)).total;
 }
 
 int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
             const float *log_decay, int32_t gate_width, const void *v, const sdm_bank *bank, const int32_t *valid_tokens,
-            const void *grad_out, const sdm_grads *grads, const sdm_exec *exec) {
+            const void *grad_out, const sdm_grads *grads, int32_t snapshot_quant, const sdm_exec *exec) {
     g_err[0] = 0;
     if (!bank || !exec || !grads) return fail(SDM_ERR_NULL, "bank, grads and exec must not be NULL");
+    if (snapshot_quant < SDM_SNAP_NONE || snapshot_quant > SDM_SNAP_BF16)
+        return fail(SDM_ERR_SHAPE, "snapshot_quant must be SDM_SNAP_NONE, _FP8, _INT4 or _BF16, got %d", snapshot_quant);
+    if (snapshot_quant == SDM_SNAP_FP8 || snapshot_quant == SDM_SNAP_INT4)
+        return fail(SDM_ERR_UNSUPPORTED, "snapshot_quant %s: the scaling of %s snapshot rows is not defined; "
+                                         "SDM_SNAP_BF16 and SDM_SNAP_NONE are supported",
+                    snapshot_quant == SDM_SNAP_FP8 ? "fp8" : "int4",
+                    snapshot_quant == SDM_SNAP_FP8 ? "float8_e4m3fn" : "4-bit");
     if (bank->shared != 0 && bank->shared != 1) return fail(SDM_ERR_SHAPE, "bank.shared must be 0 or 1, got %d", bank->shared);
     const bool shared = bank->shared == 1;
     Checked ck;
@@ -680,7 +698,8 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(bank->data), b1 = b0 + uintptr_t(banks) * M * hd * ck.es;
     const uintptr_t g0 = reinterpret_cast<uintptr_t>(grads->bank), g1 = g0 + uintptr_t(banks) * M * hd * 4;
     if (g0 < b1 && b0 < g1) return fail(SDM_ERR_SHAPE, "the bank gradient overlaps the bank");
-    const BwdSizes z = bwd_sizes(P, T, W, R, hd, M, bank->dtype, shared);
+    const int snap_es = snap_elem_bytes(snapshot_quant, bank->dtype);
+    const BwdSizes z = bwd_sizes(P, T, W, R, hd, M, bank->dtype, shared, snap_es);
     if (!exec->workspace || exec->workspace_bytes < z.total)
         return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes the backward needs",
                     exec->workspace ? exec->workspace_bytes : size_t(0), z.total);
@@ -722,7 +741,8 @@ int sdm_bwd(int32_t P, int32_t T, const sdm_slots *slots, const sdm_weights *wei
     a.gbank = grads->bank; a.gv = grads->v; a.gk = grads->write; a.gq = grads->read;
     a.gbeta = grads->beta; a.gg = grads->log_decay;
     unsigned char *ws = static_cast<unsigned char *>(exec->workspace);
-    a.snap = reinterpret_cast<float *>(ws);
+    a.snap = ws;
+    a.snap_bf16 = snap_es == 2;
     a.lead = reinterpret_cast<float2 *>(ws + z.snap);
     a.part = reinterpret_cast<float *>(ws + z.snap + z.lead);
     a.pairs = reinterpret_cast<int32_t *>(ws + z.snap + z.lead + z.part);

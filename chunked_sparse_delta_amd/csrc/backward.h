@@ -30,13 +30,29 @@ struct BwdArgs {
     float *gbank;    // [P, M, hd] (or [M, hd] shared), in: gradient of the final bank; out: of the initial bank
     float *gv;       // [P, T, hd]
     float *gk, *gq, *gbeta, *gg;   // [P, T, W], [P, T, R], [P, T], [P, T, G]
-    float *snap;     // [P, NS, T, W, S]  old_w of every live write entry, slice by slice
+    void *snap;      // [P, NS, T, W, S]  old_w of every live write entry, slice by slice: float32,
+                     // or bfloat16 (snap_bf16: rounded to nearest even, widened back where used)
+    int32_t snap_bf16;
     float2 *lead;    // [P, T, R]      (summed weight, 1) for a slot's first read entry, else (0, 0)
     float *part;     // [P, NS, T, J]  per-slice dots, J = 2W + R + 1
     int32_t *pairs;  // [P, ceil(T / 2)]  1: tokens 2j, 2j + 1 live and selecting disjoint rows
 };
 
 __host__ __device__ inline int bwd_parts(int W, int R) { return 2 * W + R + 1; }
+
+// Element index of the first saved row of slice sl of stream p, and one saved element in
+// and out: the snapshot's element type is float32 or bfloat16 (snap_bf16).
+__device__ __forceinline__ int64_t snap_slice(const BwdArgs &a, int p, int sl) {
+    return (int64_t(p) * a.NS + sl) * a.T * a.W * a.S;
+}
+__device__ __forceinline__ float snap_ld(const BwdArgs &a, int64_t i) {
+    if (a.snap_bf16) return __uint_as_float(uint32_t(static_cast<const uint16_t *>(a.snap)[i]) << 16);
+    return static_cast<const float *>(a.snap)[i];
+}
+__device__ __forceinline__ void snap_st(const BwdArgs &a, int64_t i, float x) {
+    if (a.snap_bf16) static_cast<uint16_t *>(a.snap)[i] = f32_to_bf16(x).bits;
+    else static_cast<float *>(a.snap)[i] = x;
+}
 
 size_t bwd_lds_bytes(int W, int S, int64_t M, bool res);
 int bwd_slice_cols(int P, int hd, int W, int R);

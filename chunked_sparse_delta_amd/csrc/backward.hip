@@ -137,19 +137,19 @@ __device__ __forceinline__ void load_token(const BwdArgs &a, BwdSmem &sm, int64_
 // the lane's column (of the bank in memory, or of the workgroup's slice held in LDS).
 template <bool kReplay, int NT>
 __device__ __forceinline__ void retrieve(const BwdArgs &a, BwdSmem &sm, float *old, float *bk, int64_t rs,
-                                         float *snapt, int e, int c, bool colok) {
+                                         int64_t snapt, int e, int c, bool colok) {
     const int E = NT / a.S;
     float acc = 0.0f;
     for (int w0 = 0; w0 < a.W; w0 += E) {
         const int w = w0 + e;
         if (w < a.W) {
             float o;
-            float *sp = snapt + w * a.S + c;
+            const int64_t sp = snapt + w * a.S + c;
             if (kReplay) {
                 o = colok ? bk[int64_t(sm.kid[w]) * rs] : 0.0f;
-                if (colok) *sp = o;
+                if (colok) snap_st(a, sp, o);
             } else {
-                o = colok ? *sp : 0.0f;
+                o = colok ? snap_ld(a, sp) : 0.0f;
             }
             old[w * a.S + c] = o;
             acc = __builtin_fmaf(sm.kv[w], sm.gam[w] * o, acc);
@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(NT) bwd_sweep_kernel(BwdArgs a) {
     float *bk = a.work + int64_t(p) * a.bstride + cc;
     float *gk = a.gbank + int64_t(p) * a.bstride + cc;
     const int64_t rs = a.hd;
-    float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
+    const int64_t snapw = snap_slice(a, p, sl);   // this slice's saved rows [T][W][S]
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
 
@@ -331,10 +331,10 @@ struct ResTok {
 // so the loads never wait on a branch.
 // Token t of the stream whose first token is tok0; snapw: the slice's saved rows [T][W][S].
 template <int KJ, bool kRev, typename T>
-__device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_t tok0, int t, const float *snapw,
+__device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_t tok0, int t, int64_t snapw,
                                          int e, int E, int c, int cc) {
     const int64_t tok = tok0 + t;
-    const float *snapt = snapw + int64_t(t) * a.W * a.S;
+    const int64_t snapt = snapw + int64_t(t) * a.W * a.S;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
         const int w = min(e + j * E, a.W - 1);
@@ -347,7 +347,7 @@ __device__ __forceinline__ void res_load(const BwdArgs &a, ResTok<KJ> &x, int64_
             const float2 ld = a.lead[tok * a.R + r];
             x.ql[j] = ld.x;
             x.qf[j] = ld.y;
-            x.snap[j] = snapt[w * a.S + c];
+            x.snap[j] = snap_ld(a, snapt + w * a.S + c);
         }
     }
     x.v = ldf<T>(a.v, tok * a.hd + cc);
@@ -406,7 +406,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
     const int64_t tok0 = int64_t(p) * a.T;
-    float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
+    const int64_t snapw = snap_slice(a, p, sl);   // this slice's saved rows [T][W][S]
 
     // ret over the column's entry groups, in ascending group order (every lane of the
     // column reads the same partials, so all get the same bits)
@@ -428,7 +428,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
             const int w = e + j * E;
             old[j] = colok ? bk[int64_t(cur.kid[j]) * rs] : 0.0f;
             if (w < a.W) {
-                if (colok) snapw[(int64_t(t) * a.W + w) * S + c] = old[j];
+                if (colok) snap_st(a, snapw + (int64_t(t) * a.W + w) * S + c, old[j]);
                 acc = __builtin_fmaf(cur.kv[j], cur.gam[j] * old[j], acc);
             }
         }
@@ -552,9 +552,15 @@ __global__ void __launch_bounds__(kWave) bwd_res_kernel(BwdArgs a) {
     }
     if (RES) {
         __syncthreads();
+        // with bfloat16 snapshot rows (float32 banks only) the restored rows differ from the
+        // bank's entry rows: the slice goes back to the bank with the gradient
+        float *wk = a.snap_bf16 ? a.work + int64_t(p) * a.bstride : nullptr;
         for (int64_t i = lane; i < MS; i += kWave) {
             const int cg = sl * S + int(i % S);
-            if (cg < a.hd) gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+            if (cg < a.hd) {
+                gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+                if (wk) wk[(i / S) * a.hd + cg] = lres[i];
+            }
         }
     }
 }
@@ -648,7 +654,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_pair_kernel(BwdArgs a) {
     const int J = bwd_parts(a.W, a.R);
     const int32_t n = live_tokens(a, p);
     const int64_t tok0 = int64_t(p) * a.T;
-    float *snapw = a.snap + (int64_t(p) * a.NS + sl) * a.T * a.W * S;   // this slice's saved rows [T][W][S]
+    const int64_t snapw = snap_slice(a, p, sl);   // this slice's saved rows [T][W][S]
     const int32_t *pairs = a.pairs + int64_t(p) * ((a.T + 1) / 2);
 
     // sum over the entry groups of the lane's half, in ascending group order
@@ -669,7 +675,7 @@ __global__ void __launch_bounds__(kWave) bwd_res_pair_kernel(BwdArgs a) {
         const float old = colok ? bk[int64_t(cur.kid[0]) * S] : 0.0f;
         float acc = 0.0f;
         if (on) {
-            if (colok) snapw[(int64_t(t) * a.W + w) * S + c] = old;
+            if (colok) snap_st(a, snapw + (int64_t(t) * a.W + w) * S + c, old);
             acc = __builtin_fmaf(cur.kv[0], cur.gam[0] * old, acc);
         }
         const float ret = column_sum(acc);
@@ -789,9 +795,13 @@ __global__ void __launch_bounds__(kWave) bwd_res_pair_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+    float *wk = a.snap_bf16 ? a.work + int64_t(p) * a.bstride : nullptr;   // as in the unpaired sweep
     for (int64_t i = lane; i < MS; i += kWave) {
         const int cg = sl * S + int(i % S);
-        if (cg < a.hd) gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+        if (cg < a.hd) {
+            gb_g[(i / S) * a.hd + cg] = lres[MS + i];
+            if (wk) wk[(i / S) * a.hd + cg] = lres[i];
+        }
     }
 }
 

@@ -325,16 +325,32 @@ int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *
  * float32 bank is used as the working state and holds exactly its entry contents again on
  * return; a bfloat16 bank is only read (its rows are widened into float32 working rows).
  * exec->workspace: sdm_bwd_workspace_bytes(...) bytes, 256-byte aligned (it keeps each
- * write entry's row as it was before its token, 4 * W * head_dim bytes per token, rounded
+ * write entry's row as it was before its token, 4 * W * head_dim bytes per token (2 with
+ * bfloat16 snapshot rows), rounded
  * up to whole column slices of 4..64 columns, plus 8 * R bytes per token, one float per
  * token, column slice and dot product, and for a bfloat16 bank the float32 working rows,
  * 4 * head_dim bytes per bank row).
+ * snapshot_quant: storage of the saved rows (the snapshot the pages' sdm_write_read keeps
+ *   for its backward, argument snapshot_quant, page 21, memory_ops.py):
+ *   SDM_SNAP_NONE  float32 rows; the bank is restored exactly.
+ *   SDM_SNAP_BF16  on a float32 bank, bfloat16 rows (round to nearest even, half the snapshot
+ *                  bytes): the reverse sweep recomputes each token's decayed rows from the
+ *                  widened bfloat16 rows and restores every written bank row to them, so the
+ *                  bank holds, on return, its entry rows rounded to bfloat16 where the forward
+ *                  wrote them (its other rows exactly); a bfloat16 bank runs it as NONE.
+ *   SDM_SNAP_FP8, SDM_SNAP_INT4  refused with SDM_ERR_UNSUPPORTED (the pages fix their row
+ *                  widths, head_dim bytes of float8_e4m3fn and (head_dim + 1) / 2 bytes, not
+ *                  how values are scaled into them); any other value is SDM_ERR_SHAPE.
  * exec->events: optional, num_events >= SDM_BWD_TIMING_EVENTS hipEvent_t recorded on the
  * stream before the read-slot fold, before the replay-and-reverse sweep, before the
  * reduction of the per-slice dots, and after it. exec->repeated_writes is not used.
  * Sums run in a fixed order: results are bitwise reproducible. Errors as for sdm_fwd.
  */
 #define SDM_BWD_TIMING_EVENTS 4
+#define SDM_SNAP_NONE 0
+#define SDM_SNAP_FP8 1
+#define SDM_SNAP_INT4 2
+#define SDM_SNAP_BF16 3
 
 typedef struct {
     float *bank;
@@ -346,15 +362,15 @@ typedef struct {
 } sdm_grads;
 
 /* Workspace bytes sdm_bwd needs for these shapes, bank rows (per stream, or of the shared
- * bank), bank dtype and sharing (0 for arguments sdm_bwd rejects with SDM_ERR_SHAPE,
- * SDM_ERR_RANGE or SDM_ERR_DTYPE). */
+ * bank), bank dtype, sharing and snapshot mode (0 for arguments sdm_bwd rejects with
+ * SDM_ERR_SHAPE, SDM_ERR_RANGE, SDM_ERR_DTYPE or SDM_ERR_UNSUPPORTED). */
 size_t sdm_bwd_workspace_bytes(int32_t streams, int32_t tokens, int32_t W, int32_t R, int32_t head_dim,
-                               int64_t rows, int32_t dtype, int32_t shared);
+                               int64_t rows, int32_t dtype, int32_t shared, int32_t snapshot_quant);
 
 int sdm_bwd(int32_t streams, int32_t tokens, const sdm_slots *slots, const sdm_weights *weights,
             const float *beta, const float *log_decay, int32_t gate_width, const void *v,
             const sdm_bank *bank, const int32_t *valid_tokens, const void *grad_out,
-            const sdm_grads *grads, const sdm_exec *exec);
+            const sdm_grads *grads, int32_t snapshot_quant, const sdm_exec *exec);
 
 /* Static text for an SDM_* code. */
 const char *sdm_error_string(int code);

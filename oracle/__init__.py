@@ -81,6 +81,9 @@ def _load():
             fbw = lib.sdm_oracle_token_loop_backward
             fbw.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 17
             fbw.restype = ctypes.c_int
+            fbs = lib.sdm_oracle_token_loop_backward_snap
+            fbs.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64] + [p] * 17 + [i64]
+            fbs.restype = ctypes.c_int
             lib.sdm_oracle_round_bf16.argtypes = [ctypes.c_double]
             lib.sdm_oracle_round_bf16.restype = ctypes.c_double
             _lib = lib
@@ -163,13 +166,18 @@ def token_loop(f64: dict, threads: int = 1, streams=None, bf16_chunk: int | None
     return out, bank
 
 
-def token_loop_backward(f64: dict, grad_out, grad_bank_final=None, threads: int = 1, streams=None) -> dict:
+def token_loop_backward(f64: dict, grad_out, grad_bank_final=None, threads: int = 1, streams=None,
+                        snapshot_quant: str = "none") -> dict:
     """O3: the gradient of J = sum(grad_out * readings) + sum(grad_bank_final * final bank)
     through O1's loop, for fp64 inputs (``as_f64_inputs``, one bank per stream, [P, M, hd]).
     grad_out [P, T, hd]; grad_bank_final [P, M, hd] or None (zeros). Returns a dict of fp64
     gradients named like the inputs: bank [P, M, hd] (with respect to the bank the forward
     started from), k_val, v, beta, g, q_val. ``streams`` restricts the work (other streams'
-    gradients stay zero)."""
+    gradients stay zero). ``snapshot_quant="bf16"``: the saved rows are kept rounded to
+    bfloat16 and the reverse pass works from them (the pages' bf16 snapshot of a float32
+    bank)."""
+    if snapshot_quant not in ("none", "bf16"):
+        raise ValueError(f"oracle: snapshot_quant must be 'none' or 'bf16', got {snapshot_quant!r}")
     lib = _load()
     bank0 = np.ascontiguousarray(f64["bank"], dtype=np.float64)
     if bank0.ndim != 3:
@@ -196,10 +204,10 @@ def token_loop_backward(f64: dict, grad_out, grad_bank_final=None, threads: int 
     ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
 
     def run(p):
-        rc = lib.sdm_oracle_token_loop_backward(
+        rc = lib.sdm_oracle_token_loop_backward_snap(
             p, p + 1, T, W, R, G, hd, M, ptr(k_idx), ptr(k_val), ptr(v), ptr(beta), ptr(g), ptr(q_idx),
             ptr(q_val), ptr(valid), ptr(bank0), ptr(go), ptr(gbf), ptr(out["bank"]), ptr(out["k_val"]),
-            ptr(out["v"]), ptr(out["beta"]), ptr(out["g"]), ptr(out["q_val"]))
+            ptr(out["v"]), ptr(out["beta"]), ptr(out["g"]), ptr(out["q_val"]), 1 if snapshot_quant == "bf16" else 0)
         if rc:
             raise ValueError(f"oracle: stream {p}: {ERRORS.get(rc, rc)}")
 

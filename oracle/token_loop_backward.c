@@ -34,20 +34,30 @@
  *   [P, T], grad_g [P, T, G], grad_q [P, T, R]; every element written (padding tokens 0).
  * Streams [p0, p1). Returns 0, or -1 a slot out of range, -2 a write slot repeated within a
  * token, -3 a bad argument, -4 out of memory.
+ *
+ * Snapshot storage (sdm_oracle_token_loop_backward_snap, snap_bf16 = 1): the pages let
+ * sdm_write_read keep its backward snapshot as bfloat16 rows, rounded to nearest even, on a
+ * float32 bank (argument snapshot_quant "bf16", memory_ops.py, page 21), and restore the bank
+ * to the dequantized snapshot. Here the snapshot is the saved rows old_w: with snap_bf16 each
+ * is stored rounded to bfloat16 (sdm_oracle_round_bf16), and the reverse pass recomputes the
+ * token's decayed rows from the rounded rows and restores the bank to them. The forward
+ * replay itself runs on the exact rows.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-int sdm_oracle_token_loop_backward(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R,
-                                   int64_t G, int64_t hd, int64_t M, const int32_t *k_idx,
-                                   const double *k_val, const double *v, const double *beta,
-                                   const double *g, const int32_t *q_idx, const double *q_val,
-                                   const int32_t *valid, const double *bank0,
-                                   const double *grad_out, const double *grad_bank_final,
-                                   double *grad_bank0, double *grad_k, double *grad_v,
-                                   double *grad_beta, double *grad_g, double *grad_q)
+double sdm_oracle_round_bf16(double x);   /* token_loop.c */
+
+static int backward(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R,
+                    int64_t G, int64_t hd, int64_t M, const int32_t *k_idx,
+                    const double *k_val, const double *v, const double *beta,
+                    const double *g, const int32_t *q_idx, const double *q_val,
+                    const int32_t *valid, const double *bank0,
+                    const double *grad_out, const double *grad_bank_final,
+                    double *grad_bank0, double *grad_k, double *grad_v,
+                    double *grad_beta, double *grad_g, double *grad_q, int snap_bf16)
 {
     if (p0 < 0 || p1 < p0 || T < 0 || W < 1 || R < 1 || hd < 1 || M < 1 || (G != 1 && G != W))
         return -3;
@@ -94,7 +104,8 @@ int sdm_oracle_token_loop_backward(int64_t p0, int64_t p1, int64_t T, int64_t W,
             for (int64_t w = 0; w < W; ++w) {
                 double *row = B + (int64_t)ks[w] * hd;
                 const double gamma = exp(g[tok * G + (G == 1 ? 0 : w)]);
-                memcpy(old + (t * W + w) * hd, row, sizeof(double) * (size_t)hd);
+                for (int64_t c = 0; c < hd; ++c)
+                    old[(t * W + w) * hd + c] = snap_bf16 ? sdm_oracle_round_bf16(row[c]) : row[c];
                 for (int64_t c = 0; c < hd; ++c) {
                     row[c] *= gamma;
                     ret[c] += kv[w] * row[c];
@@ -185,4 +196,33 @@ int sdm_oracle_token_loop_backward(int64_t p0, int64_t p1, int64_t T, int64_t W,
     free(gdelta);
     free(gret);
     return rc;
+}
+
+int sdm_oracle_token_loop_backward(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R,
+                                   int64_t G, int64_t hd, int64_t M, const int32_t *k_idx,
+                                   const double *k_val, const double *v, const double *beta,
+                                   const double *g, const int32_t *q_idx, const double *q_val,
+                                   const int32_t *valid, const double *bank0,
+                                   const double *grad_out, const double *grad_bank_final,
+                                   double *grad_bank0, double *grad_k, double *grad_v,
+                                   double *grad_beta, double *grad_g, double *grad_q)
+{
+    return backward(p0, p1, T, W, R, G, hd, M, k_idx, k_val, v, beta, g, q_idx, q_val, valid, bank0,
+                    grad_out, grad_bank_final, grad_bank0, grad_k, grad_v, grad_beta, grad_g, grad_q, 0);
+}
+
+int sdm_oracle_token_loop_backward_snap(int64_t p0, int64_t p1, int64_t T, int64_t W, int64_t R,
+                                        int64_t G, int64_t hd, int64_t M, const int32_t *k_idx,
+                                        const double *k_val, const double *v, const double *beta,
+                                        const double *g, const int32_t *q_idx, const double *q_val,
+                                        const int32_t *valid, const double *bank0,
+                                        const double *grad_out, const double *grad_bank_final,
+                                        double *grad_bank0, double *grad_k, double *grad_v,
+                                        double *grad_beta, double *grad_g, double *grad_q,
+                                        int64_t snap_bf16)
+{
+    if (snap_bf16 != 0 && snap_bf16 != 1) return -3;
+    return backward(p0, p1, T, W, R, G, hd, M, k_idx, k_val, v, beta, g, q_idx, q_val, valid, bank0,
+                    grad_out, grad_bank_final, grad_bank0, grad_k, grad_v, grad_beta, grad_g, grad_q,
+                    (int)snap_bf16);
 }

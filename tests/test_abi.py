@@ -271,31 +271,40 @@ def test_bwd_workspace_bytes(lib):
     (8 streams x 16 slices = 128 workgroups)."""
     f = lib.sdm_bwd_workspace_bytes
     f.restype = ctypes.c_size_t
-    f.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    f.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     snap, lead, part, pairs = 8 * 16 * 4 * 2048 * 8 * 4, 8 * 2048 * 8 * 8, 8 * 16 * 2048 * 25 * 4, 8 * 1024 * 4
     base = snap + lead + part + pairs
-    assert f(8, 2048, 8, 8, 64, 4096, 0, 0) == base
-    assert f(8, 2048, 8, 8, 64, 4096, 1, 0) == base + 8 * 4096 * 64 * 4
-    assert f(8, 2048, 8, 8, 64, 4096, 1, 1) == base + 4096 * 64 * 4
-    assert f(0, 2048, 8, 8, 64, 4096, 0, 0) == 0 and f(8, 2048, 0, 8, 64, 4096, 0, 0) == 0
-    assert f(8, 2048, 8, 257, 64, 4096, 0, 0) == 0 and f(8, 2048, 8, 8, 64, 0, 0, 0) == 0
-    assert f(8, 2048, 8, 8, 64, 4096, 2, 0) == 0 and f(8, 2048, 8, 8, 64, 4096, 0, 2) == 0
+    NONE, FP8, INT4, BF16 = 0, 1, 2, 3
+    assert f(8, 2048, 8, 8, 64, 4096, 0, 0, NONE) == base
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 0, NONE) == base + 8 * 4096 * 64 * 4
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 1, NONE) == base + 4096 * 64 * 4
+    # bfloat16 snapshot rows halve the saved rows of a float32 bank; a bfloat16 bank runs it as none
+    assert f(8, 2048, 8, 8, 64, 4096, 0, 0, BF16) == base - snap // 2
+    assert f(8, 2048, 8, 8, 64, 4096, 1, 0, BF16) == f(8, 2048, 8, 8, 64, 4096, 1, 0, NONE)
+    assert f(8, 2048, 8, 8, 64, 4096, 0, 0, FP8) == 0 and f(8, 2048, 8, 8, 64, 4096, 0, 0, INT4) == 0
+    assert f(8, 2048, 8, 8, 64, 4096, 0, 0, 4) == 0 and f(8, 2048, 8, 8, 64, 4096, 0, 0, -1) == 0
+    assert f(0, 2048, 8, 8, 64, 4096, 0, 0, NONE) == 0 and f(8, 2048, 0, 8, 64, 4096, 0, 0, NONE) == 0
+    assert f(8, 2048, 8, 257, 64, 4096, 0, 0, NONE) == 0 and f(8, 2048, 8, 8, 64, 0, 0, 0, NONE) == 0
+    assert f(8, 2048, 8, 8, 64, 4096, 2, 0, NONE) == 0 and f(8, 2048, 8, 8, 64, 4096, 0, 2, NONE) == 0
 
 
 def test_bwd_rejects_before_any_work(lib):
     from chunked_sparse_delta_amd import _Bank, _Exec, _Grads, _Slots, _Weights
     lib.sdm_last_error.restype = ctypes.c_char_p
     f = lib.sdm_bwd
-    f.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 6
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_int32] + [ctypes.c_void_p] * 5 + \
+        [ctypes.c_int32, ctypes.c_void_p]
     lib.sdm_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.sdm_bwd_workspace_bytes.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    lib.sdm_bwd_workspace_bytes.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                                   ctypes.c_int32]
     fake = Call.FAKE
     P, T, W, R, hd, M = 2, 100, 4, 3, 64, 50
     ptr = {k: fake + (i << 32) for i, k in enumerate(["kidx", "qidx", "kval", "qval", "beta", "g", "v", "bank", "go",
                                                       "ws", "gbank", "gv", "gbeta", "gg", "gk", "gq"])}
 
-    def call(dtype=0, shared=0, ws=None, gbank=None, gv=None, G=W, kb=4, go=None):
-        need = lib.sdm_bwd_workspace_bytes(P, T, W, R, hd, M, dtype if dtype in (0, 1) else 0, shared & 1)
+    def call(dtype=0, shared=0, ws=None, gbank=None, gv=None, G=W, kb=4, go=None, snap=0):
+        need = lib.sdm_bwd_workspace_bytes(P, T, W, R, hd, M, dtype if dtype in (0, 1) else 0, shared & 1,
+                                           snap if snap in (0, 3) else 0)
         slots = _Slots(ptr["kidx"], ptr["qidx"], W, R, kb, 4)
         weights = _Weights(ptr["kval"], ptr["qval"])
         bank = _Bank(ptr["bank"], M, hd, dtype, shared)
@@ -303,7 +312,7 @@ def test_bwd_rejects_before_any_work(lib):
                        ptr["gg"], ptr["gk"], ptr["gq"])
         ex = _Exec(None, ptr["ws"], need if ws is None else ws(need), None, 0, None)
         return f(P, T, ctypes.byref(slots), ctypes.byref(weights), ptr["beta"], ptr["g"], G, ptr["v"],
-                 ctypes.byref(bank), None, ptr["go"] if go is None else go, ctypes.byref(grads), ctypes.byref(ex))
+                 ctypes.byref(bank), None, ptr["go"] if go is None else go, ctypes.byref(grads), snap, ctypes.byref(ex))
 
     assert call(dtype=2) == DTYPE and call(shared=2) == SHAPE
     assert call(ws=lambda n: n - 1) == WORKSPACE and call(dtype=1, ws=lambda n: n - 256) == WORKSPACE
@@ -311,3 +320,8 @@ def test_bwd_rejects_before_any_work(lib):
     assert call(gbank=ptr["bank"] + 64) == SHAPE and call(go=ptr["bank"] + 64) == SHAPE
     assert call(dtype=1, go=ptr["go"] + 1) == ALIGN
     assert call(G=2) == SHAPE and call(kb=3) == DTYPE
+    # snapshot modes: fp8 and int4 refused, unknown values are bad arguments; bf16 rows take
+    # half the saved-row bytes of a float32 bank (a workspace one byte short is refused)
+    assert call(snap=1) == UNSUPPORTED and call(snap=2) == UNSUPPORTED
+    assert call(snap=4) == SHAPE and call(snap=-1) == SHAPE
+    assert call(snap=3, ws=lambda n: n - 1) == WORKSPACE

@@ -129,3 +129,79 @@ def test_rejects_repeated_write_slots():
     inp["k_idx"][0, 1, 1] = inp["k_idx"][0, 1, 0]
     with pytest.raises(ValueError, match="repeated"):
         oracle.token_loop_backward(inp, np.zeros_like(inp["v"]))
+
+
+# ------------------------------------------------------------------ bfloat16 snapshot rows
+
+def _write_once_inputs(seed, P=2, T=6, W=3, R=3, hd=4):
+    """fp64 inputs in which every slot is written by at most one token of its stream (slot
+    ids of token t are t * W .. t * W + W - 1, shuffled), so that each saved row is the row
+    the forward started from."""
+    rng = np.random.default_rng(seed)
+    M = T * W + 3
+    k_idx = np.stack([np.stack([rng.permutation(np.arange(t * W, t * W + W)) for t in range(T)])
+                      for _ in range(P)]).astype(np.int32)
+    return dict(
+        bank=rng.normal(size=(P, M, hd)), k_idx=k_idx, k_val=rng.normal(size=(P, T, W)),
+        v=rng.normal(size=(P, T, hd)), beta=1 / (1 + np.exp(-rng.normal(size=(P, T)))),
+        g=rng.normal(-0.4, 0.3, (P, T, W)), q_idx=rng.integers(0, M, size=(P, T, R)).astype(np.int32),
+        q_val=rng.normal(size=(P, T, R)), valid=np.array([T, T - 1][:P], dtype=np.int32))
+
+
+SNAP_NAMES = ("bank", "k_val", "v", "beta", "g")   # every gradient but the read weights'
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_bf16_snapshot_is_the_gradient_from_rounded_saved_rows(seed):
+    """With every slot written at most once, each saved row is the initial bank row, so
+    keeping the snapshot as bfloat16 rows means working backwards from the bank rounded to
+    bfloat16: every gradient except the read weights' equals plain O3 run on the rounded bank,
+    bit for bit. A read weight's gradient is a dot product with the row read: a slot that a
+    later token writes has been restored from its rounded saved row by then (O3 on the rounded
+    bank reads the same value); any other row read is the forward's own (plain O3)."""
+    inp = _write_once_inputs(seed)
+    rng = np.random.default_rng(50 + seed)
+    go = rng.normal(size=inp["v"].shape)
+    gbf = rng.normal(size=inp["bank"].shape)
+    got = oracle.token_loop_backward(inp, go, gbf, snapshot_quant="bf16")
+    rounded = dict(inp, bank=oracle.round_bf16(inp["bank"]))
+    want = oracle.token_loop_backward(rounded, go, gbf)
+    plain = oracle.token_loop_backward(inp, go, gbf)
+    assert not np.array_equal(rounded["bank"], inp["bank"])
+    for name in SNAP_NAMES:
+        assert np.array_equal(got[name], want[name]), name
+    P, T, R = inp["q_idx"].shape
+    for p in range(P):
+        for t in range(int(inp["valid"][p])):
+            later = set(inp["k_idx"][p, t + 1:int(inp["valid"][p])].ravel().tolist())
+            for r in range(R):
+                ref = want if int(inp["q_idx"][p, t, r]) in later else plain
+                assert got["q_val"][p, t, r] == ref["q_val"][p, t, r], (p, t, r)
+    assert any(not np.array_equal(got[n], plain[n]) for n in SNAP_NAMES)
+
+
+def test_bf16_snapshot_of_a_bf16_exact_bank_reduces_to_o3():
+    """Saved rows that are bfloat16 already (every slot written at most once, bank rows
+    bfloat16-exact) are stored unchanged: the bf16 snapshot gives plain O3's gradients."""
+    inp = _write_once_inputs(7)
+    inp["bank"] = oracle.round_bf16(inp["bank"])
+    rng = np.random.default_rng(57)
+    go = rng.normal(size=inp["v"].shape)
+    gbf = rng.normal(size=inp["bank"].shape)
+    got = oracle.token_loop_backward(inp, go, gbf, snapshot_quant="bf16")
+    want = oracle.token_loop_backward(inp, go, gbf)
+    for name in FD_NAMES:
+        assert np.array_equal(got[name], want[name]), name
+
+
+def test_bf16_snapshot_changes_gradients_by_rounding_only():
+    """Slots rewritten many times (M small): the rounded saved rows differ from the exact ones,
+    so the gradients differ, by about the bfloat16 rounding of the rows (2^-8 relative)."""
+    inp = _inputs(11, T=9, M=4)
+    rng = np.random.default_rng(61)
+    go = rng.normal(size=inp["v"].shape)
+    gbf = rng.normal(size=inp["bank"].shape)
+    got = oracle.token_loop_backward(inp, go, gbf, snapshot_quant="bf16")
+    want = oracle.token_loop_backward(inp, go, gbf)
+    diff = [np.max(np.abs(got[n] - want[n])) / max(np.max(np.abs(want[n])), 1e-300) for n in FD_NAMES]
+    assert max(diff) > 0 and max(diff) < 3e-2, diff

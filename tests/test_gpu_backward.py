@@ -29,10 +29,15 @@ def _grad_out(gr, dtype, gpu):
     return torch.from_numpy(gr["grad_out"]).to(gpu)
 
 
-def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False):
+def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False, snapshot_quant="none", write_once=False):
     inp = gu.generate(wl)
     if dup_reads and wl.R > 1:
         inp["q_idx"][:, ::2, -1] = inp["q_idx"][:, ::2, 0]
+    if write_once:   # token t writes slots t W .. t W + W - 1 (shuffled): each row written at most once
+        assert wl.M >= wl.T * wl.W
+        rng = np.random.default_rng(wl.index)
+        inp["k_idx"] = np.stack([np.stack([rng.permutation(np.arange(t * wl.W, (t + 1) * wl.W)) for t in range(wl.T)])
+                                 for _ in range(wl.P)]).astype(np.int32)
     gr = workloads.grad_inputs(wl, seed, bank_grad)
     t = gu.to_torch(inp, gpu)
     if id64:
@@ -41,21 +46,22 @@ def _run(wl, gpu, seed=0, bank_grad=True, dup_reads=False, id64=False):
     bank = t["bank"].clone()
     gb = None if gr["grad_bank"] is None else torch.from_numpy(gr["grad_bank"]).to(gpu)
     got = sdm_bwd(bank, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"],
-                  _grad_out(gr, wl.dtype, gpu), grad_bank=gb, valid_tokens=t["valid"])
+                  _grad_out(gr, wl.dtype, gpu), grad_bank=gb, valid_tokens=t["valid"], snapshot_quant=snapshot_quant)
     torch.cuda.synchronize()
     return inp, gr, t, bank, got
 
 
-def _check(inp, gr, got, streams=None):
+def _check(inp, gr, got, streams=None, snapshot_quant="none", tol=TOL):
     f = oracle.as_f64_inputs(inp)
-    want = oracle.token_loop_backward(f, gr["grad_out"], gr["grad_bank"], threads=8, streams=streams)
+    want = oracle.token_loop_backward(f, gr["grad_out"], gr["grad_bank"], threads=8, streams=streams,
+                                      snapshot_quant=snapshot_quant)
     if streams is not None:
         want = {k: v[list(streams)] for k, v in want.items()}
     for k, ok in NAMES.items():
         g = gu.f64(got[k] if streams is None else got[k][list(streams)])
         w = want[ok]
         assert g.shape == w.shape, k
-        assert gu.rel_err(g, w) <= TOL, (k, gu.rel_err(g, w))
+        assert gu.rel_err(g, w) <= tol, (k, gu.rel_err(g, w))
     valid = inp["valid"]
     for p in (range(inp["valid"].shape[0]) if streams is None else streams):
         n = int(valid[p])
@@ -258,3 +264,87 @@ def test_sdm_write_read_autograd(gpu, dtype):
     with pytest.raises(ValueError, match="must not require grad"):
         sdm_write_read(t["bank"].clone().requires_grad_(True), t["k_idx"], leaves["k_val"], leaves["v"],
                        leaves["beta"], leaves["log_decay"], t["q_idx"], leaves["q_val"], chunk=16)
+
+
+# ------------------------------------------------------------------ bfloat16 snapshot rows
+
+# Where a saved row is the result of arithmetic (a row written before), the kernel rounds
+# its float32 value to bfloat16 and the oracle its fp64 value: the two sides can land on
+# neighbouring bfloat16 values when the exact row sits within float32 error of a rounding
+# boundary, so a restored element may differ by one bfloat16 ulp (2^-8 relative). Rows
+# written once are saved as the bank's own rows (no arithmetic): both sides round the same
+# value, and the float32 bar holds.
+TOL_SNAP = 2.0 ** -8
+
+SNAP_CASES = [
+    small(P=3, T=50, C=16, hd=10, M=9, W=4, R=5, ragged=True, index=11),               # rows rewritten often
+    small(P=2, T=40, C=16, hd=70, M=30, W=5, R=3, gate_width=1, index=12),             # several slices
+    small(P=2, T=30, C=16, hd=33, M=300, W=40, R=70, ids="zipf", index=14),            # W, R above one pass
+    small(P=2, T=40, C=16, hd=12, M=300, W=20, R=30, ragged=True, index=20),           # 2 entries per lane
+]
+ONCE_CASES = [
+    small(P=2, T=40, C=16, hd=24, M=200, W=4, R=5, ragged=True, index=31),
+    small(P=2, T=12, C=16, hd=33, M=500, W=40, R=70, index=32),
+]
+
+
+def _check_restored_bank(inp, wl, bank):
+    """The bank comes back with the rows the forward wrote rounded to bfloat16 (nearest
+    even) and the others bit for bit."""
+    b0 = np.ascontiguousarray(inp["bank"], dtype=np.float32)
+    want = b0.copy()
+    for p in range(wl.P):
+        rows = np.unique(inp["k_idx"][p, :int(inp["valid"][p])])
+        want[p, rows] = workloads.bf16_bits_to_f32(workloads.round_bf16_bits(b0[p, rows]))
+    assert np.array_equal(gu.bits(bank), want.view(np.int32)), "bank not restored to the rounded snapshot rows"
+
+
+@pytest.mark.parametrize("wl", SNAP_CASES, ids=[f"c{i}" for i in range(len(SNAP_CASES))])
+def test_backward_bf16_snapshot_matches_oracle(gpu, wl, residency):
+    """snapshot_quant="bf16" on a float32 bank (sdm_write_read's argument, page 21): the saved
+    rows are bfloat16, the gradients match the oracle's bf16-snapshot mode within one
+    bfloat16 ulp of the saved rows, the bank comes back with the written rows rounded, and a
+    rerun gives the same bits."""
+    inp, gr, t, bank, got = _run(wl, gpu, dup_reads=True, snapshot_quant="bf16")
+    _check(inp, gr, got, snapshot_quant="bf16", tol=TOL_SNAP)
+    _check_restored_bank(inp, wl, bank)
+    inp2, gr2, t2, bank2, got2 = _run(wl, gpu, dup_reads=True, snapshot_quant="bf16")
+    for k in NAMES:
+        assert np.array_equal(gu.bits(got[k]), gu.bits(got2[k])), k
+
+
+@pytest.mark.parametrize("wl", ONCE_CASES, ids=[f"c{i}" for i in range(len(ONCE_CASES))])
+def test_backward_bf16_snapshot_write_once_at_the_float32_bar(gpu, wl, residency):
+    """Every row written at most once: the saved rows are the bank's rows, rounded the same way
+    on both sides, and the bf16-snapshot gradients meet the float32 bar (1e-4)."""
+    inp, gr, t, bank, got = _run(wl, gpu, dup_reads=True, snapshot_quant="bf16", write_once=True)
+    _check(inp, gr, got, snapshot_quant="bf16")
+    _check_restored_bank(inp, wl, bank)
+
+
+def test_backward_bf16_snapshot_of_a_bf16_bank_is_none(gpu):
+    """A bfloat16 bank runs snapshot_quant="bf16" as "none" (the pages' effective snapshot
+    mode: its rows are bfloat16 already): the same bits."""
+    wl = small(P=2, T=37, C=16, hd=24, M=30, W=3, R=4, dtype="bf16", ragged=True, index=23)
+    _, _, _, _, a = _run(wl, gpu, snapshot_quant="none")
+    _, _, _, _, b = _run(wl, gpu, snapshot_quant="bf16")
+    for k in NAMES:
+        assert np.array_equal(gu.bits(a[k]), gu.bits(b[k])), k
+
+
+@pytest.mark.parametrize("mode", ["fp8", "int4"])
+def test_backward_refuses_unscaled_snapshot_modes(gpu, mode):
+    """fp8 and int4 snapshot rows are refused before any work (the pages give their row
+    widths, not how values are scaled into them)."""
+    from chunked_sparse_delta_amd import SdmError
+    wl = small(P=1, T=10, C=16, hd=8, M=10, W=2, R=2, index=30)
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    from chunked_sparse_delta_amd import sdm_bwd
+    bank = t["bank"].clone()
+    go = torch.ones_like(t["v"])
+    with pytest.raises(SdmError) as ei:
+        sdm_bwd(bank, t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], go,
+                valid_tokens=t["valid"], snapshot_quant=mode)
+    assert ei.value.code == -7
+    assert np.array_equal(gu.bits(bank), gu.bits(t["bank"]))
