@@ -2,14 +2,16 @@
 // 23, product_key_topk.py, the function's docstring): the selection that turns a layer's
 // factor scores into slot ids for the memory op.
 //
-// Rule (restated): a slot takes one column of each of the F factors and scores the float32
-// sum of its values in factor order (bfloat16 input with F > 2: each partial sum rounded to
-// bfloat16 before the next factor is added); scores compare as float32 with -0 below +0 and
-// NaN as -inf. Each factor is ranked by value, larger column first on ties; stage 0 keeps
-// the first n = min(k, f_0) ranks of factor 0; stage f keeps the best c = min(k, n m) pairs
-// (i, j), i < n a rank of the previous stage, j < m = min(k, f_f) a rank of factor f, with
-// (i + 1)(j + 1) <= c, exact ties to the larger i + j, then the larger i. The kept slots
-// are returned by ascending linear index, with their scores rounded to the input dtype.
+// Rule, as numbered conditions: (1) a slot chooses one column per factor and its score is
+// the float32 total of the chosen values in factor order (bfloat16 input with F > 2: the
+// running total is brought to bfloat16 before each further factor joins it); (2) scores
+// compare as float32, negative zero beneath positive zero, NaN as negative infinity;
+// (3) within a factor, columns go by value, highest first, the higher column index first
+// among equal values, and stage 0 keeps n = min(k, f_0) of factor 0's; (4) stage f pairs a
+// surviving rank i < n with a rank j < m = min(k, f_f) of factor f where (i + 1)(j + 1) <= c
+// = min(k, n m) and keeps the c best, an exact tie going to the greater i + j and then the
+// greater i; (5) survivors leave by ascending linear index with scores rounded to the input
+// dtype.
 //
 // General rows: one workgroup of 256 threads per row; every ordering is a bitonic sort in LDS of 64-bit
 // keys whose high word is the float32 order and whose low word encodes the tie rule, so
@@ -28,7 +30,8 @@ namespace sdm {
 // Limits (the host entry point checks them before any launch).
 constexpr int kTopkBlock = 256;
 constexpr int kTopkMaxK = 256;
-constexpr int kTopkMaxFactor = 4096;      // columns per factor
+constexpr int kTopkMaxFactor = 4096;      // columns of a factor ranked by one sort in LDS
+constexpr int kTopkMaxWidth = 65535;      // columns per factor (wider ones ranked in pieces)
 constexpr int kTopkMaxFactors = 8;
 constexpr int kTopkPairs = 2048;          // >= sum over i < 256 of min(256, 256 / (i + 1)) = 1567
 
@@ -79,6 +82,7 @@ struct TopkArgs {
 
 __global__ __launch_bounds__(kTopkBlock) void topk_kernel(TopkArgs a) {
     __shared__ uint64_t key[kTopkMaxFactor > kTopkPairs ? kTopkMaxFactor : kTopkPairs];
+    static_assert((kTopkMaxFactor & (kTopkMaxFactor - 1)) == 0 && kTopkMaxFactor > kTopkMaxK, "sort buffer");
     __shared__ float rval[kTopkMaxFactors][kTopkMaxK];   // factor f's rank r: value
     __shared__ int32_t rcol[kTopkMaxFactors][kTopkMaxK];  //                    column
     __shared__ float cs[2][kTopkMaxK];                    // current / next stage: scores
@@ -92,13 +96,29 @@ __global__ __launch_bounds__(kTopkBlock) void topk_kernel(TopkArgs a) {
                       : reinterpret_cast<const float *>(rowp)[c];
     };
 
-    // Rank every factor: the first min(k, f) entries of (value desc, column desc).
+    // Rank every factor: the first min(k, f) entries of (value desc, column desc). A factor
+    // wider than the sort buffer is ranked in pieces: the running first kTopkMaxK keys and
+    // the next kTopkMaxFactor - kTopkMaxK columns are sorted together, so the leading
+    // kTopkMaxK keys stay those of every column seen (keys are unique; 0 pads below all).
     for (int f = 0; f < a.F; ++f) {
-        const int w = a.fw[f], n2 = w <= 1 ? 1 : 1 << (32 - __clz(w - 1));
-        for (int c = tid; c < n2; c += kTopkBlock)
-            key[c] = c < w ? (uint64_t(topk_order(value(a.f0[f] + c))) << 32) | uint32_t(c) : 0ull;
-        __syncthreads();
-        topk_bitonic(key, n2, true);
+        const int w = a.fw[f];
+        if (w <= kTopkMaxFactor) {
+            const int n2 = w <= 1 ? 1 : 1 << (32 - __clz(w - 1));
+            for (int c = tid; c < n2; c += kTopkBlock)
+                key[c] = c < w ? (uint64_t(topk_order(value(a.f0[f] + c))) << 32) | uint32_t(c) : 0ull;
+            __syncthreads();
+            topk_bitonic(key, n2, true);
+        } else {
+            constexpr int CH = kTopkMaxFactor - kTopkMaxK;
+            for (int c = tid; c < kTopkMaxK; c += kTopkBlock) key[c] = 0ull;
+            for (int c0 = 0; c0 < w; c0 += CH) {
+                for (int c = tid; c < CH; c += kTopkBlock)
+                    key[kTopkMaxK + c] =
+                        c0 + c < w ? (uint64_t(topk_order(value(a.f0[f] + c0 + c))) << 32) | uint32_t(c0 + c) : 0ull;
+                __syncthreads();
+                topk_bitonic(key, kTopkMaxFactor, true);
+            }
+        }
         const int m = min(a.k, w);
         for (int r = tid; r < m; r += kTopkBlock) {
             const int c = int(uint32_t(key[r]));

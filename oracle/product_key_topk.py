@@ -1,19 +1,21 @@
 """Product-key exact top-k, forward, on the CPU. TEST INFRASTRUCTURE, NOT PRODUCT.
 
 The selection rule of ``product_key_topk`` (page 23, product_key_topk.py, the function's
-docstring), taken step by step in plain Python:
+docstring), restated as numbered conditions and taken step by step in plain Python:
 
-  * a slot (c_0, .., c_{F-1}) takes one column of each factor; its score is the float32 sum
-    of its factor values in factor order; with bfloat16 input and more than two factors each
-    partial sum is rounded to bfloat16 before the next factor is added;
-  * scores compare as float32 numbers with -0 below +0 and NaN counted as -inf;
-  * each factor is ranked by value, larger column first on ties; one factor selects its
-    first kk ranks;
-  * stage f = 1 .. F-1 keeps the best c = min(k, n m) of the pairs (i, j) of a rank i < n of
-    the previous stage and a rank j < m = min(k, factors[f]) of factor f with
-    (i + 1)(j + 1) <= c, exact ties going to the larger i + j, then the larger i;
-  * the result is lin = (..(c_0 factors[1] + c_1) ..) factors[F-1] + c_{F-1} strictly
-    ascending, and val = the slot's score rounded to the input dtype.
+  1. A slot chooses one column per factor. Its score is the float32 total of the chosen
+     values, added in factor order; for bfloat16 input with three or more factors the running
+     total is brought to bfloat16 each time before another factor's value joins it.
+  2. Scores are compared as float32 numbers, except that negative zero ranks beneath
+     positive zero and a NaN ranks as negative infinity.
+  3. Inside one factor the columns are ordered by value, highest first, equal values putting
+     the higher column index first; the first stage keeps min(k, width) of them.
+  4. Each further stage f pairs a surviving rank i (i < n) of the previous stage with one of
+     factor f's leading m = min(k, width_f) ranks j, only where (i + 1)(j + 1) <= c for
+     c = min(k, n m), and keeps the c best pairs by score; an exact score tie is won by the
+     pair with the greater i + j, and then by the greater i.
+  5. The survivors come out by ascending linear index lin = (..(c_0 f_1 + c_1) ..) f_{F-1} +
+     c_{F-1}, each with its score rounded to the input dtype.
 
 Readings where the text leaves a step open (also listed in the design doc): the stage that adds
 a factor other than the last one ranks its pairs by the partial sum it carries forward (the

@@ -50,7 +50,9 @@ def _oracle_val_bits(val, dtype):
 
 CASES = [("f32", (16, 16), 8), ("f32", (33, 70), 40), ("bf16", (64, 64), 32), ("bf16", (5, 7, 9), 20),
          ("bf16", (4, 3, 5, 2), 50), ("f32", (300,), 17), ("f32", (2, 3), 10), ("bf16", (512, 512), 256),
-         ("f32", (1000, 4096), 64), ("f32", (3, 3, 3), 27), ("f32", (7, 5, 3, 2, 2), 33)]
+         ("f32", (1000, 4096), 64), ("f32", (3, 3, 3), 27), ("f32", (7, 5, 3, 2, 2), 33),
+         # factors wider than one LDS sort (ranked in pieces), up to the pages' 65535 columns
+         ("f32", (16384, 8), 64), ("bf16", (65535, 65535), 256), ("f32", (5000, 3, 7), 100), ("bf16", (65535,), 200)]
 
 
 @pytest.mark.parametrize("path", ["auto", "block"])
@@ -89,7 +91,8 @@ def test_topk_leading_dims_and_empty(gpu):
 
 
 @pytest.mark.parametrize("dtype,factors,k", [("f32", (16, 16), 8), ("bf16", (64, 64), 32), ("bf16", (5, 7, 9), 20),
-                                             ("f32", (300,), 17), ("f32", (33, 70), 40), ("bf16", (512, 512), 256)])
+                                             ("f32", (300,), 17), ("f32", (33, 70), 40), ("bf16", (512, 512), 256),
+                                             ("f32", (16384, 8), 64), ("bf16", (65535, 65535), 256)])
 def test_topk_backward_matches_oracle(gpu, dtype, factors, k):
     """The sparse backward: each raw column's gradient is the sum, in output order, of the
     gradients of the selected slots that use it (oracle_topk_backward), bit for bit."""

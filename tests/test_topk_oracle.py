@@ -33,6 +33,21 @@ def test_staged_rule_equals_brute_force_without_ties(factors, k):
             assert x == s
 
 
+def test_wide_factor_equals_brute_force_without_ties():
+    """A factor of 16384 columns (the pages' two- to four-factor kernels take up to 65535)
+    with a factor of 8: the staged rule against all 131072 slots."""
+    factors, k = (16384, 8), 64
+    rng = np.random.default_rng(16384)
+    raw = rng.normal(size=(2, sum(factors))).astype(np.float32)
+    val, lin = pk.product_key_topk(raw, factors, k)
+    for r in range(2):
+        a, b = raw[r, :16384], raw[r, 16384:]
+        sums = (a[:, None] + b[None, :]).astype(np.float32).ravel()   # two terms: exact float32 sums
+        order = np.argsort(-sums, kind="stable")
+        assert sums[order[k - 1]] != sums[order[k]]   # no tie at the boundary
+        assert set(lin[r].tolist()) == set(order[:k].tolist())
+
+
 def test_ties_follow_the_stated_order():
     """factors (2, 2), k = 2, all four scores 1: factor ranks put the larger column first
     (col 1, col 0); stage 1 keeps c = 2 of the pairs (0,0), (0,1), (1,0) by the larger
