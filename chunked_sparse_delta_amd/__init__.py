@@ -29,7 +29,7 @@ import threading
 
 import torch
 
-__all__ = ["SdmError", "sdm_fwd", "sdm_fwd_noalloc", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "wy_solve", "product_key_topk", "product_key_topk_backward",
+__all__ = ["SdmError", "sdm_fwd", "sdm_fwd_noalloc", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_bwd", "sdm_write_read", "bwd_workspace_bytes", "chunk_mats", "chunk_records", "wy_solve", "product_key_topk", "product_key_topk_backward",
            "workspace_bytes", "plan",
            "library_path",
            "SDM_ERRORS"]
@@ -103,6 +103,8 @@ def _load():
             lib.sdm_fwd.restype = ctypes.c_int
             lib.sdm_chunk_mats.argtypes = [i32, i32, i32, p, p, p, p, i32, i64, i32, i32, p, p, p, p, p, p, p, p]
             lib.sdm_chunk_mats.restype = ctypes.c_int
+            lib.sdm_chunk_records.argtypes = [i32, i32, i32, p, p, p, p, i32, i64, i32, i32, p, p, p, p, p, p, p]
+            lib.sdm_chunk_records.restype = ctypes.c_int
             lib.sdm_wy_solve.argtypes = [i64, i32, p, p, p, p, p, p]
             lib.sdm_wy_solve.restype = ctypes.c_int
             lib.sdm_fwd_plan.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, p]
@@ -487,6 +489,36 @@ def chunk_mats(k_idx, k_val, beta, log_decay, q_idx, q_val, *, rows: int, head_d
     rc = lib.sdm_chunk_mats(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay), G,
                             rows, head_dim, _DTYPES[k_val.dtype], _ptr(valid_tokens), _ptr(res["A"]), _ptr(res["QK"]),
                             _ptr(res["X"]), _ptr(res["QX"]), _ptr(res["gw"]), _ptr(res["gr"]), ctypes.byref(ex))
+    _check_rc(lib, rc)
+    return res
+
+
+def chunk_records(k_idx, k_val, beta, log_decay, q_idx, q_val, *, rows: int, head_dim: int, chunk: int,
+                  valid_tokens=None, stream=None) -> dict:
+    """Phase 1's integer records of every chunk (sdm_chunk_records; chunk n = p * Nt + ti):
+    meta int32 [N, 8], spk and grec int32 [N, C * W, 4], ecr int32 [N, C, W, 4], rcr int32
+    [N, C, R, 4] (formats in include/sdm.h)."""
+    lib = _load()
+    if k_val.dtype not in _DTYPES:
+        raise TypeError(f"k_val must be float32 or bfloat16, got {k_val.dtype}")
+    P, T, W = k_idx.shape
+    R = q_idx.shape[2]
+    dev = k_idx.device
+    dummy = torch.empty((P, 1, head_dim), dtype=k_val.dtype, device=dev)
+    _, _, _, _, W, R, G, slots, weights = _inputs(dummy, k_idx, k_val, torch.empty((P, T, head_dim),
+                                                  dtype=k_val.dtype, device=dev), beta, log_decay, q_idx, q_val,
+                                                  valid_tokens)
+    N = P * (-(-T // chunk))
+    i = dict(dtype=torch.int32, device=dev)
+    res = dict(meta=torch.empty((N, 8), **i), spk=torch.empty((N, chunk * W, 4), **i),
+               grec=torch.empty((N, chunk * W, 4), **i), ecr=torch.empty((N, chunk, W, 4), **i),
+               rcr=torch.empty((N, chunk, R, 4), **i))
+    ws = _workspace(workspace_bytes(P, T, chunk, W, R, head_dim, 1), dev)
+    ex = _Exec(_stream_ptr(stream), ws.data_ptr(), ws.numel(), None, 0, None)
+    rc = lib.sdm_chunk_records(P, T, chunk, ctypes.byref(slots), ctypes.byref(weights), _ptr(beta), _ptr(log_decay),
+                               G, rows, head_dim, _DTYPES[k_val.dtype], _ptr(valid_tokens), _ptr(res["meta"]),
+                               _ptr(res["spk"]), _ptr(res["grec"]), _ptr(res["ecr"]), _ptr(res["rcr"]),
+                               ctypes.byref(ex))
     _check_rc(lib, rc)
     return res
 

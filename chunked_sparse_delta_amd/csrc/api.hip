@@ -33,7 +33,7 @@ hipError_t launch_topk(const void *raw, void *val, int64_t *lin, int64_t rows, i
                        int32_t kk, bool bf16, const int32_t *fw, hipStream_t st);
 hipError_t launch_topk_bwd(const int64_t *lin, const void *gval, void *graw, int64_t rows, int32_t D, int32_t F,
                            int32_t kk, bool bf16, const int32_t *fw, hipStream_t st);
-constexpr int kTopkMaxK = 256, kTopkMaxFactor = 4096, kTopkMaxFactors = 8;
+constexpr int kTopkMaxK = 256, kTopkMaxWidth = 65535, kTopkMaxFactors = 8;
 size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M);
 int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, int lds_limit);
 }  // namespace sdm
@@ -336,8 +336,8 @@ int sdm_product_key_topk(int64_t rows, const void *raw, int32_t dtype, const int
     int64_t D = 0, prod = 1;
     for (int f = 0; f < num_factors; ++f) {
         if (factors[f] < 1) return fail(SDM_ERR_SHAPE, "factor %d has %d columns", f, factors[f]);
-        if (factors[f] > kTopkMaxFactor)
-            return fail(SDM_ERR_UNSUPPORTED, "factor %d has %d columns; at most %d", f, factors[f], kTopkMaxFactor);
+        if (factors[f] > kTopkMaxWidth)
+            return fail(SDM_ERR_UNSUPPORTED, "factor %d has %d columns; at most %d", f, factors[f], kTopkMaxWidth);
         D += factors[f];
         if (prod > (int64_t(1) << 55) / factors[f])
             return fail(SDM_ERR_UNSUPPORTED, "the factors address 2^55 or more slots");
@@ -367,8 +367,8 @@ int sdm_product_key_topk_backward(int64_t rows, const int64_t *lin, const void *
     int64_t D = 0, prod = 1;
     for (int f = 0; f < num_factors; ++f) {
         if (factors[f] < 1) return fail(SDM_ERR_SHAPE, "factor %d has %d columns", f, factors[f]);
-        if (factors[f] > kTopkMaxFactor)
-            return fail(SDM_ERR_UNSUPPORTED, "factor %d has %d columns; at most %d", f, factors[f], kTopkMaxFactor);
+        if (factors[f] > kTopkMaxWidth)
+            return fail(SDM_ERR_UNSUPPORTED, "factor %d has %d columns; at most %d", f, factors[f], kTopkMaxWidth);
         D += factors[f];
         if (prod > (int64_t(1) << 55) / factors[f])
             return fail(SDM_ERR_UNSUPPORTED, "the factors address 2^55 or more slots");
@@ -550,9 +550,90 @@ __global__ void copy_mats_kernel(Slab sl, int32_t P, int32_t Nt, MatsOut o) {
     for (int64_t k = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; k < L.F; k += int64_t(gridDim.x) * blockDim.x)
         o.gr[dst * L.F + k] = cb[L.off_gr + k];
 }
+struct RecsOut {
+    int32_t *meta, *spk, *grec, *ecr, *rcr;
+};
+
+// Phase 1's integer records of every chunk of the slab, copied out verbatim.
+__global__ void copy_recs_kernel(Slab sl, int32_t P, int32_t Nt, RecsOut o) {
+    const int64_t n = blockIdx.y;
+    const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
+    const int64_t dst = int64_t(p) * Nt + ti;
+    const ChunkLayout &L = sl.lay;
+    const int32_t *cb = reinterpret_cast<const int32_t *>(sl.chunk(n));
+    const int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x, step = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t k = i0; k < 8; k += step) o.meta[dst * 8 + k] = cb[L.off_meta + k];
+    for (int64_t k = i0; k < 4 * L.E; k += step) {
+        o.spk[dst * 4 * L.E + k] = cb[L.off_spk + k];
+        o.grec[dst * 4 * L.E + k] = cb[L.off_grec + k];
+        o.ecr[dst * 4 * L.E + k] = cb[L.off_ecr + k];
+    }
+    for (int64_t k = i0; k < 4 * L.F; k += step) o.rcr[dst * 4 * L.F + k] = cb[L.off_rcr + k];
+}
 }  // namespace sdm
 
+namespace {
+
+// Phase 1 and the solve over every slab of the chunk-intermediate queries, then copy(sl, st).
+template <typename CopyF>
+int run_phase1_slabs(const Checked &ck0, int32_t P, int32_t C, const sdm_exec *exec, CopyF copy) {
+    Checked ck = ck0;
+    const size_t per_step = size_t(ck.lay.words) * 4 * size_t(P);
+    if (!exec->workspace || exec->workspace_bytes < per_step)
+        return fail(SDM_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes one step needs",
+                    exec->workspace ? exec->workspace_bytes : size_t(0), per_step);
+    if (!aligned(exec->workspace, 256)) return fail(SDM_ERR_ALIGN, "workspace must be 256-byte aligned");
+    DeviceInfo *dev = nullptr;
+    int rc = device_info(&dev);
+    if (rc != SDM_OK) return rc;
+    const int32_t Nt = ck.pb.Nt;
+    int32_t slab = int32_t(exec->workspace_bytes / per_step);
+    if (slab > Nt) slab = Nt;
+    hipStream_t st = static_cast<hipStream_t>(exec->stream);
+    for (int32_t ti0 = 0; ti0 < Nt; ti0 += slab) {
+        Slab sl{};
+        sl.ti0 = ti0;
+        sl.steps = Nt - ti0 < slab ? Nt - ti0 : slab;
+        sl.ws = static_cast<uint32_t *>(exec->workspace);
+        sl.lay = ck.lay;
+        float *w = reinterpret_cast<float *>(sl.ws);
+        const WyArgs wa{w + sl.lay.off_A, w + sl.lay.off_beta, w + sl.lay.off_QK, w + sl.lay.off_X,
+                        w + sl.lay.off_QX, C, sl.lay.words, sl.lay.words};
+        const bool fused = phase1_fused(ck.lay, C, dev->lds_per_block);
+        const int lognp = plan_part(ck.pb, ck.lay, fused);
+        hipError_t e = launch_phase1(ck.pb, sl, st, nullptr, fused, wa, lognp);
+        if (e != hipSuccess) return hip_fail(e, "phase 1 launch");
+        if (!fused) {
+            e = launch_wy(wa.A, wa.beta, wa.QK, wa.X, wa.QX, C, int64_t(P) * sl.steps, sl.lay.words, sl.lay.words, st);
+            if (e != hipSuccess) return hip_fail(e, "solve launch");
+        }
+        copy(sl, st);
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "copy launch");
+    }
+    return SDM_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+int sdm_chunk_records(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights,
+                      const float *beta, const float *log_decay, int32_t gate_width, int64_t rows, int32_t head_dim,
+                      int32_t dtype, const int32_t *valid_tokens, int32_t *meta, int32_t *spk, int32_t *grec,
+                      int32_t *ecr, int32_t *rcr, const sdm_exec *exec) {
+    g_err[0] = 0;
+    if (!exec) return fail(SDM_ERR_NULL, "exec must not be NULL");
+    if (!meta || !spk || !grec || !ecr || !rcr) return fail(SDM_ERR_NULL, "output arrays must not be NULL");
+    Checked ck;
+    int rc = check_call(P, T, C, slots, weights, beta, log_decay, gate_width, nullptr, rows, head_dim, dtype, nullptr,
+                        false, valid_tokens, nullptr, false, &ck);
+    if (rc) return rc;
+    const RecsOut o{meta, spk, grec, ecr, rcr};
+    const int32_t Nt = ck.pb.Nt;
+    return run_phase1_slabs(ck, P, C, exec, [&](const Slab &sl, hipStream_t st) {
+        hipLaunchKernelGGL(copy_recs_kernel, dim3(64, unsigned(int64_t(P) * sl.steps)), dim3(256), 0, st, sl, P, Nt, o);
+    });
+}
 
 int sdm_chunk_mats(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sdm_weights *weights, const float *beta,
                    const float *log_decay, int32_t gate_width, int64_t rows, int32_t head_dim, int32_t dtype,

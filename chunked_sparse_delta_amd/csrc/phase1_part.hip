@@ -707,6 +707,14 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
             }
             __syncthreads();
         }
+        // padding tokens' rows: +0 (the dense products cover every row of the chunk, and a
+        // 0 x NaN of stale memory would reach the live rows through the solve's products)
+        const int npad = C - nl;
+        for (int x = tid; x < 3 * npad * HP; x += kPartBlock) {
+            const int k = x / (npad * HP), rem = x - k * npad * HP, tt = rem / HP, h = rem - tt * HP;
+            float *dst = k == 0 ? Ka : (k == 1 ? Kb : Qa);
+            dst[(nl + tt) * HC + h] = 0.0f;
+        }
     }
 
     __syncthreads();

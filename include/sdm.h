@@ -222,6 +222,33 @@ int sdm_chunk_mats(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slo
                    float *gw, float *gr, const sdm_exec *exec);
 
 /*
+ * Phase 1's integer records of every chunk, verbatim (for checking the grouping, dedup and
+ * read lookups exactly; sdm_fwd keeps them in its workspace). Same arguments and checks as
+ * sdm_chunk_mats; E = chunk * W, F = chunk * R; chunk (p, ti) is n = p * Nt + ti.
+ *   meta: device int32 [P * Nt, 8]: live tokens, live write entries, write groups (the
+ *     writes of one slot in the chunk), hot groups, groups of at least 16 members, the hot
+ *     count rounded up to 16, -, 1 if the chunk's Phase 1 sorted every write entry in memory
+ *     (else it ran in LDS slot partitions).
+ *   spk: device int32 [P * Nt, E, 4]: the write entries in group order, each group's members
+ *     in token order (positions < live write entries): {slot, token, bits of k, bits of L}.
+ *   grec: device int32 [P * Nt, E, 4]: group g < meta[2]: {slot, first member's position |
+ *     (members - 1) << 16 | first member's token << 24, bits of exp(L_last), bits of the first
+ *     member's k exp(L_last - L)}.
+ *   ecr: device int32 [P * Nt, C, W, 4]: live write entry (t, w) at position m: {position of
+ *     its group's first member, m, bits of k, bits of L}, or {m, m, 0, 0} if its group is hot
+ *     (its pair terms go to the dense products).
+ *   rcr: device int32 [P * Nt, C, R, 4]: read entry (t, r) whose slot has a write at a token
+ *     <= t in a group that is not hot: {first member's position, 1 + position of the latest
+ *     such write, bits of q, bits of that write's L}; otherwise zeros.
+ * Entries past meta[1] / meta[2] and of padding tokens are unspecified (rcr: zeros).
+ */
+int sdm_chunk_records(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
+                      const sdm_weights *weights, const float *beta, const float *log_decay,
+                      int32_t gate_width, int64_t rows, int32_t head_dim, int32_t dtype,
+                      const int32_t *valid_tokens, int32_t *meta, int32_t *spk, int32_t *grec,
+                      int32_t *ecr, int32_t *rcr, const sdm_exec *exec);
+
+/*
  * The per-chunk solve on its own (wy_solve, wy_solve.py, page 23):
  *   X = (I + tril(beta[:, None] * A, -1))^-1 and QX = QK @ X for each of n chunks.
  *   A, QK: device float32 [n, C, C]; only the strict lower triangle of A and the lower
@@ -267,17 +294,20 @@ int sdm_fwd_plan(int32_t streams, int32_t tokens, int32_t chunk, int32_t W, int3
  * page 23, product_key_topk.py docstring): the slot selection that feeds write and read
  * slot ids.
  *   raw: device [rows, sum(factors)] in dtype (SDM_F32 or SDM_BF16), the factors side by
- *     side. factors: HOST array of num_factors (1..8) widths, each 1..4096 columns, their
- *     product below 2^55. k: 1..256; kk = min(k, product of the factors).
+ *     side. factors: HOST array of num_factors (1..8) widths, each 1..65535 columns (the
+ *     pages' two- to four-factor kernels take up to 65535), their product below 2^55.
+ *     k: 1..256; kk = min(k, product of the factors).
  *   val: device [rows, kk] in dtype: the selected slots' scores (float32 sums of their
  *     factor values in factor order; bfloat16 with more than two factors rounds each
  *     partial sum to bfloat16 before the next factor), rounded to dtype.
  *   lin: device int64 [rows, kk]: the selected slots (c_0 .. c_{F-1}) as
  *     (..(c_0 factors[1] + c_1) ..) factors[F-1] + c_{F-1}, strictly ascending per row.
- *   Selection rule (exact ties included): scores compare as float32, -0 below +0, NaN as
- *   -inf; each factor is ranked by value, larger column first on ties; stage f = 1.. keeps
- *   the best c = min(k, n m) pairs (i, j) of a previous rank i < n and a rank j < m =
- *   min(k, factors[f]) with (i + 1)(j + 1) <= c, ties to the larger i + j, then larger i.
+ *   Selection (exact ties included): (1) scores compare as float32 with negative zero
+ *   beneath positive zero and NaN as negative infinity; (2) a factor's columns are ordered
+ *   by value, highest first, the higher column index first among equal values; (3) stage
+ *   f >= 1 pairs a surviving rank i < n with a rank j < m = min(k, factors[f]) of factor f
+ *   where (i + 1)(j + 1) <= c = min(k, n m) and keeps the c best; an exact tie goes to the
+ *   greater i + j, then to the greater i.
  *   exec->stream only (no workspace). rows = 0 does nothing. Returns SDM_OK or a negative
  *   SDM_ERR_* before any launch (SDM_ERR_UNSUPPORTED for factors past the limits).
  */

@@ -30,7 +30,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["sdm_bwd", "sdm_bwd_workspace_bytes", "sdm_chunk_mats", "sdm_error_string",
+    assert declared_functions() == ["sdm_bwd", "sdm_bwd_workspace_bytes", "sdm_chunk_mats", "sdm_chunk_records",
+                                    "sdm_error_string",
                                     "sdm_fwd", "sdm_fwd_noalloc", "sdm_fwd_phase1", "sdm_fwd_phase2", "sdm_fwd_plan",
                                     "sdm_fwd_workspace_bytes", "sdm_last_error", "sdm_product_key_topk",
                                     "sdm_product_key_topk_backward", "sdm_wy_solve"]
@@ -238,7 +239,7 @@ def test_topk_rejects_before_any_launch(lib):
     assert call(factors=()) == SHAPE and call(factors=(2,) * 9) == SHAPE
     assert call(factors=(16, 0)) == SHAPE
     assert call(k=0) == SHAPE and call(k=257) == SHAPE
-    assert call(factors=(4097, 2)) == UNSUPPORTED
+    assert call(factors=(65536, 2)) == UNSUPPORTED
     assert call(factors=(4096,) * 5) == UNSUPPORTED         # 2^60 slots
     assert call(raw=None) == NULL and call(lin=None) == NULL
     assert call(raw=fake + 2) == ALIGN and call(dtype=1, raw=fake + 1) == ALIGN and call(lin=fake + 4) == ALIGN
@@ -259,7 +260,7 @@ def test_topk_backward_rejects_before_any_launch(lib):
 
     assert call(e=None) == NULL and call(dtype=5) == DTYPE and call(rows=-1) == SHAPE
     assert call(kk=0) == SHAPE and call(kk=257) == SHAPE and call(factors=(2, 3), kk=7) == SHAPE
-    assert call(factors=(5000,)) == UNSUPPORTED and call(lin=None) == NULL
+    assert call(factors=(65536,)) == UNSUPPORTED and call(lin=None) == NULL
     assert call(lin=fake + 4) == ALIGN and call(dtype=1, g=fake + 1) == ALIGN
     assert call(rows=0, lin=None, g=None, out=None) == OK
 

@@ -92,6 +92,118 @@ def test_chunk_intermediates_match_chunk_algebra(gpu, wl, part, monkeypatch):
             assert np.all(res["A"][n][np.triu_indices(wl.C)] == 0)
 
 
+def _check_records(rec, n, kc, qc, nl, want_groups, want_only, what):
+    """Phase 1's integer records of chunk n against the definition: the write groups (each
+    slot's write entries in token order), the single-member flags, each write entry's place
+    and group, and each read's latest write of its slot at or before its token, exactly."""
+    C, W = kc.shape
+    R = qc.shape[1]
+    meta = rec["meta"][n]
+    El = nl * W
+    assert meta[0] == nl and meta[1] == El and meta[2] == len(want_groups), (what, meta)
+    spk = rec["spk"][n][:El]
+    grec = rec["grec"][n][:meta[2]]
+    got, first_of, size_of, covered = {}, {}, {}, np.zeros(El, dtype=np.int64)
+    for r in grec:
+        slot, y = int(r[0]), int(r[1])
+        first, cnt, t0 = y & 0xFFFF, ((y >> 16) & 0xFF) + 1, (y >> 24) & 0xFF
+        mem = spk[first:first + cnt]
+        assert np.all(mem[:, 0] == slot) and int(mem[0, 1]) == t0, (what, slot)
+        got[slot] = [int(t) for t in mem[:, 1]]
+        first_of[slot], size_of[slot] = first, cnt
+        covered[first:first + cnt] += 1
+    assert np.all(covered == 1), what   # the groups tile the sorted positions
+    assert got == {s: [t for t, _ in m] for s, m in want_groups.items()}, what
+    hot = set()
+    for t in range(nl):
+        for w in range(W):
+            slot = int(kc[t, w])
+            assert (size_of[slot] == 1) == bool(want_only[t, w]), (what, t, w)
+            e = rec["ecr"][n][t, w]
+            m = int(e[1])
+            assert int(spk[m, 0]) == slot and int(spk[m, 1]) == t, (what, t, w)
+            if int(e[0]) == m and int(e[2]) == 0 and int(e[3]) == 0:
+                hot.add(slot)
+            else:
+                assert int(e[0]) == first_of[slot] and slot not in hot, (what, t, w)
+    assert len(hot) == meta[3] and all(size_of[s] >= 16 for s in hot), what
+    for t in range(C):
+        for r in range(R):
+            e = rec["rcr"][n][t, r]
+            if t >= nl:
+                assert not e.any(), (what, t, r)
+                continue
+            q = int(qc[t, r])
+            latest = max([tt for tt, _ in want_groups.get(q, []) if tt <= t], default=None)
+            if e.any():
+                assert latest is not None and q not in hot, (what, t, r)
+                assert int(e[0]) == first_of[q], (what, t, r)
+                assert int(spk[int(e[1]) - 1, 0]) == q and int(spk[int(e[1]) - 1, 1]) == latest, (what, t, r)
+            else:
+                assert latest is None or q in hot, (what, t, r)
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=2, T=37, C=16, hd=8, M=12, W=3, R=2),
+    small(P=2, T=33, C=32, hd=8, M=30, W=5, R=4, dtype="bf16", ids="zipf", index=4),
+    small(P=2, T=70, C=64, hd=8, M=6, W=3, R=3, index=5),
+    small(P=1, T=96, C=48, hd=8, M=40, W=5, R=4, ids="zipf", zipf_s=1.3, ragged=True, index=6),
+    small(P=1, T=60, C=32, hd=8, M=300, W=40, R=36, ids="zipf", ragged=True, index=43),
+    small(P=1, T=64, C=32, hd=8, M=60, W=40, R=40, index=45),
+], ids=["tiny", "bf16zipf", "allhot", "mixed", "part_zipf", "part_fewslots"])
+@pytest.mark.parametrize("part", ["1", "1:3", "0"])
+def test_phase1_records_match_the_chunk_algebra(gpu, wl, part, monkeypatch):
+    """Phase 1's integer outputs bit-exactly against O2's groups and single-member flags, on
+    every Phase-1 path (fused small chunks, slot partitions, sorting)."""
+    import oracle
+    from oracle import chunk_algebra
+    from chunked_sparse_delta_amd import chunk_records
+    monkeypatch.setenv("SDM_P1_PART", part[0])
+    if ":" in part:
+        monkeypatch.setenv("SDM_P1_NP_LOG", part.split(":")[1])
+    else:
+        monkeypatch.delenv("SDM_P1_NP_LOG", raising=False)
+    inp = gu.generate(wl)
+    f = oracle.as_f64_inputs(inp)
+    _, _, inter = chunk_algebra.forward(f, wl.C, emit=True)
+    t = gu.to_torch(inp, gpu)
+    rec = chunk_records(t["k_idx"], t["k_val"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], rows=wl.M,
+                        head_dim=wl.hd, chunk=wl.C, valid_tokens=t["valid"])
+    rec = {k: v.cpu().numpy() for k, v in rec.items()}
+    for p in range(wl.P):
+        nv = int(inp["valid"][p])
+        for ti in range(wl.Nt):
+            nl = max(0, min(wl.C, nv - ti * wl.C))
+            kc = np.zeros((wl.C, wl.W), np.int64)
+            qc = np.zeros((wl.C, wl.R), np.int64)
+            kc[:nl] = inp["k_idx"][p, ti * wl.C:ti * wl.C + nl]
+            qc[:nl] = inp["q_idx"][p, ti * wl.C:ti * wl.C + nl]
+            c = inter[p][ti]
+            _check_records(rec, p * wl.Nt + ti, kc, qc, nl, c["groups"], c["is_only"], (p, ti))
+
+
+def test_phase1_records_of_a_full_size_config_4p_stream(gpu):
+    """Config 4's shapes (chunk 256, 256 write and 256 read slots per token, half Zipf): the
+    records of every chunk of one stream against the grouping computed from the ids directly."""
+    from chunked_sparse_delta_amd import chunk_records
+    wl = workloads.CONFIGS["4p"]
+    inp = gu.generate(wl, streams=[0])
+    t = gu.to_torch(inp, gpu)
+    rec = chunk_records(t["k_idx"], t["k_val"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], rows=wl.M,
+                        head_dim=wl.hd, chunk=wl.C, valid_tokens=t["valid"])
+    rec = {k: v.cpu().numpy() for k, v in rec.items()}
+    assert rec["meta"][:, 7].max() == 0   # every chunk ran in LDS slot partitions
+    for ti in (0, 7, wl.Nt - 1):
+        kc = inp["k_idx"][0, ti * wl.C:(ti + 1) * wl.C].astype(np.int64)
+        qc = inp["q_idx"][0, ti * wl.C:(ti + 1) * wl.C].astype(np.int64)
+        groups = {}
+        for tt in range(wl.C):
+            for w in range(wl.W):
+                groups.setdefault(int(kc[tt, w]), []).append((tt, w))
+        only = np.vectorize(lambda s: len(groups[int(s)]) == 1)(kc)
+        _check_records(rec, ti, kc, qc, wl.C, groups, only, ("4p", ti))
+
+
 # ------------------------------------------------------------------ end to end, small shapes
 
 SMALL = [
@@ -201,14 +313,27 @@ def test_bitwise_reruns_workspace_and_stream_independence(gpu):
     assert np.array_equal(gu.bits(o5[0]), gu.bits(o1[5])) and np.array_equal(gu.bits(b5[0]), gu.bits(b1[5]))
 
 
-def test_poisoned_output_and_workspace(gpu):
-    wl = small(P=2, T=90, C=32, hd=32, M=40, W=4, R=4, ragged=True, index=25)
+@pytest.mark.parametrize("wl,part", [
+    (small(P=2, T=90, C=32, hd=32, M=40, W=4, R=4, ragged=True, index=25), "1"),                  # fused
+    (small(P=1, T=300, C=128, hd=16, M=300, W=16, R=8, ids="zipf", ragged=True, weight_scale=-1.0,
+           index=14), "1"),                                                                          # partitions
+    (small(P=1, T=300, C=128, hd=16, M=300, W=16, R=8, ids="zipf", ragged=True, weight_scale=-1.0,
+           index=14), "0"),                                                                          # sorting
+    (small(P=3, T=150, C=64, hd=64, M=200, W=24, R=24, dtype="bf16", ids="zipf", ragged=True, index=53), "1"),
+], ids=["fused", "partitioned", "sorting", "bf16_partitioned"])
+def test_poisoned_output_and_workspace(gpu, wl, part, monkeypatch):
+    """A workspace of 0xFF bytes (NaN words, -1 ints) and a NaN-filled output give the bits
+    of a zeroed workspace, on every Phase-1 path: nothing reads workspace memory the call did
+    not write first (padding tokens included)."""
+    monkeypatch.setenv("SDM_P1_PART", part)
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
-    o1, b1 = gu.run(t, wl.C)
     from chunked_sparse_delta_amd import workspace_bytes
-    ws = torch.full((workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0),), 0xFF, dtype=torch.uint8, device=gpu)
-    out = torch.full((wl.P, wl.T, wl.hd), float("nan"), dtype=torch.float32, device=gpu)
+    n = workspace_bytes(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, 0)
+    o1, b1 = gu.run(t, wl.C, workspace=torch.zeros((n,), dtype=torch.uint8, device=gpu))
+    gu.parity(o1, b1, inp, wl.C, f"poison baseline {part}")
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=gpu)
+    out = torch.full((wl.P, wl.T, wl.hd), float("nan"), dtype=t["bank"].dtype, device=gpu)
     o2, b2 = gu.run(t, wl.C, out=out, workspace=ws)
     assert np.array_equal(gu.bits(o1), gu.bits(o2)) and np.array_equal(gu.bits(b1), gu.bits(b2))
 
@@ -253,7 +378,7 @@ def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
     inp = gu.generate(wl)
     t = gu.to_torch(inp, gpu)
     results = []
-    for geom in (None, "1", "2", "4", "8", "1,1", "8,1", "1,0", "8,0"):
+    for geom in (None, "1", "2", "4", "8", "1,1", "2,1", "4,1", "8,1", "1,0", "2,0", "4,0", "8,0"):
         if geom is None:
             monkeypatch.delenv("SDM_P2_GEOM", raising=False)
         else:
@@ -506,11 +631,17 @@ def test_overlapped_batches_give_the_same_bits(gpu):
 
 
 @pytest.mark.gpu
-def test_phase2_cu_budget_does_not_change_bits(gpu):
+@pytest.mark.parametrize("wl", [
+    small(P=8, T=200, C=64, hd=128, M=300, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=47),
+    # bank slices too large for LDS: staged blocks (bf16, config 2's widths) and memory mode (f32)
+    small(P=8, T=200, C=64, hd=128, M=16384, W=32, R=32, dtype="bf16", ids="zipf", index=51),
+    small(P=4, T=300, C=128, hd=128, M=4000, W=24, R=24, ragged=True, index=52),
+], ids=["resident", "staged", "memory"])
+def test_phase2_cu_budget_does_not_change_bits(gpu, wl):
     """sdm_fwd_phase2's phase2_cus (the CUs its slice geometry plans for) changes only the
-    schedule: every budget gives sdm_fwd's bits; a negative budget is rejected."""
+    schedule: every budget gives sdm_fwd's bits (resident, staged and memory geometries); a
+    negative budget is rejected."""
     from chunked_sparse_delta_amd import SdmError, sdm_fwd_phase1, sdm_fwd_phase2, workspace_bytes
-    wl = small(P=8, T=200, C=64, hd=128, M=300, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=47)
     t = gu.to_torch(gu.generate(wl), gpu)
     o_ref, b_ref = gu.run(t, wl.C)
     args = (t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"])
