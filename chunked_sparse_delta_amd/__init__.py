@@ -160,7 +160,7 @@ def workspace_bytes(P: int, T: int, C: int, W: int, R: int, hd: int, slab_steps:
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("vec", "slice_vectors", "slices", "phase2_mode",
                                                "phase2_lds_bytes", "phase1_fused", "phase1_partitions_log2",
-                                               "lds_limit", "lds_default")]
+                                               "lds_limit", "lds_default", "phase2_team")]
 
 
 PHASE2_MODES = ("memory", "staged", "resident")

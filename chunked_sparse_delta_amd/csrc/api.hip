@@ -35,6 +35,8 @@ hipError_t launch_topk_bwd(const int64_t *lin, const void *gval, void *graw, int
                            int32_t kk, bool bf16, const int32_t *fw, hipStream_t st);
 constexpr int kTopkMaxK = 256, kTopkMaxWidth = 65535, kTopkMaxFactors = 8;
 size_t phase2_lds_bytes(const ChunkLayout &L, int C, int nv, int V, int es, int mode, int64_t M);
+size_t phase2_team_lds_bytes(int C, int V, int team);
+bool phase2_teams_share_l2(int32_t *buf);
 int phase2_mode(const ChunkLayout &L, int C, int nv, int V, int es, int64_t M, int lds_limit);
 }  // namespace sdm
 
@@ -71,6 +73,7 @@ struct DeviceInfo {
     int lds_default = 0;     // the device's default per-block limit (reported by sdm_fwd_plan)
     int cus = 0;
     void *scratch = nullptr; // this device's copy of `scratch`
+    bool teams = false;      // blocks congruent mod 8 share an XCD (Phase-2 teams allowed)
 };
 // The kernels' opt-in LDS attribute is set to at most this many bytes.
 constexpr int kMaxLdsPerBlock = 160 * 1024 - 256;
@@ -106,6 +109,8 @@ int device_info(DeviceInfo **out) {
         if ((e = hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch))) != hipSuccess)
             return hip_fail(e, "hipGetSymbolAddress (static scratch)");
         d.scratch = sp;
+        // nothing else uses the scratch before this setup returns
+        d.teams = phase2_teams_share_l2(static_cast<int32_t *>(sp));
         d.ready = true;
     }
     *out = &d;
@@ -214,7 +219,7 @@ int check_call(int32_t P, int32_t T, int32_t C, const sdm_slots *slots, const sd
     pb.bank_stride = shared ? 0 : M * hd;
     pb.repeats = nullptr;
     ck->pb = pb;
-    ck->lay = make_layout(C, W, R);
+    ck->lay = make_layout(C, W, R, hd);
     ck->V = V;
     ck->es = es;
     return SDM_OK;
@@ -245,6 +250,7 @@ P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int c
         }
     }
     g.S = (hv + g.nv - 1) / g.nv;
+    g.team = 1;
     g.mode = phase2_mode(L, pb.C, g.nv, V, es, pb.M, lds_limit);
     // A shared bank is never held resident: each workgroup writes its whole slice back at
     // the end of a slab, which would overwrite the rows of the other streams.
@@ -259,8 +265,39 @@ P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int c
 // twice the workgroups, each with half the per-entry vector work (the step is bound by
 // instruction issue), and still room beside them for another batch's Phase 1. Slices never
 // change the bits. (Narrower still, 2 columns, measured no faster and fills every CU.)
+// Teams: when slices of one 128-byte line per row (8 vectors of 16 bytes) leave CUs idle and
+// the bank stays in memory, 4 (else 2) workgroups share each (stream, slice) instead of
+// narrowing the slices (whole lines per request: a quarter of the requests of 32-byte
+// slices for the same bytes). Needs streams in whole groups of 8 (a team on one XCD),
+// pieces of whole 16-token tiles, and room for the team's LDS. SDM_P2_TEAM=0 turns teams
+// off, =2 or =4 asks for that size only; SDM_P2_GEOM alone turns them off (geometry sweeps).
+bool plan_team(const Problem &pb, const ChunkLayout &L, int V, int es, int cus, int lds_limit, P2Geom &g) {
+    DeviceInfo *dev = nullptr;
+    if (device_info(&dev) != SDM_OK || !dev->teams) return false;
+    const char *env = getenv("SDM_P2_TEAM");
+    const int want = env ? atoi(env) : -1;
+    if (want == 0 || (want < 0 && getenv("SDM_P2_GEOM"))) return false;
+    if (V * es != 16 || pb.P % kXcds != 0) return false;
+    const int hv = pb.hd / V, S8 = (hv + 7) / 8;
+    if (S8 > kTeamMaxSlices) return false;
+    // asked for by size: any shape the kernel takes (for tests and sweeps)
+    if (want < 0 && (int64_t(pb.P) * S8 >= cus || phase2_mode(L, pb.C, 8, V, es, pb.M, lds_limit) != 0)) return false;
+    for (int t = 4; t >= 2; t /= 2) {
+        if (want > 0 && want != t) continue;
+        if ((want < 0 && int64_t(pb.P) * S8 * t > cus) || pb.C % (16 * t) != 0 || pb.C / t * 8 > 1024) continue;
+        if (phase2_team_lds_bytes(pb.C, V, t) + 256 > size_t(lds_limit)) continue;
+        g.nv = 8;
+        g.S = S8;
+        g.mode = 0;
+        g.team = t;
+        return true;
+    }
+    return false;
+}
+
 P2Geom plan_phase2_v(const Problem &pb, const ChunkLayout &L, int &V, int es, int cus, int lds_limit) {
-    const P2Geom g = plan_phase2(pb, L, V, es, cus, lds_limit);
+    P2Geom g = plan_phase2(pb, L, V, es, cus, lds_limit);
+    if (plan_team(pb, L, V, es, cus, lds_limit, g)) return g;
     if (es == 2 && V == 8 && g.nv == 1 && g.mode == 2 && int64_t(pb.P) * g.S * 2 <= cus && !getenv("SDM_P2_GEOM")) {
         const P2Geom g4 = plan_phase2(pb, L, 4, es, cus, lds_limit);
         if (g4.nv == 1 && g4.mode == 2) {
@@ -307,13 +344,15 @@ int sdm_fwd_plan(int32_t P, int32_t T, int32_t C, int32_t W, int32_t R, int32_t 
     Problem pb{};
     pb.P = P; pb.T = T; pb.C = C; pb.W = W; pb.R = R; pb.hd = hd; pb.M = M; pb.dtype = dtype;
     pb.bank_stride = M * hd;   // per-stream banks
-    const ChunkLayout lay = make_layout(C, W, R);
+    const ChunkLayout lay = make_layout(C, W, R, hd);
     const P2Geom g = plan_phase2_v(pb, lay, V, es, dev->cus, dev->lds_per_block);
     plan->vec = V;
     plan->slice_vectors = g.nv;
     plan->slices = g.S;
     plan->phase2_mode = g.mode;
-    plan->phase2_lds_bytes = int32_t(phase2_lds_bytes(lay, C, g.nv, V, es, g.mode, M));
+    plan->phase2_team = g.team;
+    plan->phase2_lds_bytes = int32_t(g.team > 1 ? phase2_team_lds_bytes(C, V, g.team)
+                                                 : phase2_lds_bytes(lay, C, g.nv, V, es, g.mode, M));
     plan->phase1_fused = phase1_fused(lay, C, dev->lds_per_block) ? 1 : 0;
     pb.key_bits = key_bits(M);
     plan->phase1_partitions_log2 = plan_part(pb, lay, plan->phase1_fused != 0);
@@ -389,7 +428,7 @@ size_t sdm_fwd_workspace_bytes(int32_t P, int32_t T, int32_t C, int32_t W, int32
     if (check_shape(P, T, C, W, R, hd) != SDM_OK) return 0;
     const int32_t Nt = int32_t((int64_t(T) + C - 1) / C);
     if (slab_steps <= 0 || slab_steps > Nt) slab_steps = Nt;
-    const ChunkLayout lay = make_layout(C, W, R);
+    const ChunkLayout lay = make_layout(C, W, R, hd);
     return size_t(lay.words) * 4 * size_t(P) * size_t(slab_steps);
 }
 
@@ -448,7 +487,8 @@ int fwd_run(int parts, int32_t P, int32_t T, int32_t C, const sdm_slots *slots, 
     if (exec->phase2_cus < 0) return fail(SDM_ERR_SHAPE, "phase2_cus must be >= 0, got %d", exec->phase2_cus);
     const int p2cus = exec->phase2_cus > 0 && exec->phase2_cus < dev->cus ? exec->phase2_cus : dev->cus;
     const P2Geom geom = plan_phase2_v(ck.pb, ck.lay, ck.V, ck.es, p2cus, dev->lds_per_block);
-    const size_t p2lds = phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.mode, ck.pb.M);
+    const size_t p2lds = geom.team > 1 ? phase2_team_lds_bytes(C, ck.V, geom.team)
+                                       : phase2_lds_bytes(ck.lay, C, geom.nv, ck.V, ck.es, geom.mode, ck.pb.M);
     if (p2lds + 256 > size_t(dev->lds_per_block))
         return fail(SDM_ERR_UNSUPPORTED, "chunk %d needs %zu bytes of LDS per workgroup in phase 2, the device has %d", C,
                     p2lds, dev->lds_per_block);

@@ -207,8 +207,12 @@ struct ChunkLayout {
     int64_t off_oval;     // [E + F] u32: the partitioned path's gather weight of each list slot
     int64_t off_inv;      // [E + F] i32: list slot of each entry (token-major, a token's writes then reads);
                           //   these three share their words with the arrays only the sorting path uses
-    int64_t off_meta;     // [8] i32: n_live, E_live, ngroups, hot groups, groups with >= kHotMin members,
-                          //   HP (hot groups rounded up to 16), -, 1 if the chunk took the sorting path
+    int64_t off_meta;     // [64] i32: n_live, E_live, ngroups, hot groups, groups with >= kHotMin members,
+                          //   HP (hot groups rounded up to 16), -, 1 if the chunk took the sorting path;
+                          //   [8 + 2 slice], [9 + 2 slice]: the Phase-2 team words of each column slice
+                          //   (gather pieces, then DW pieces: claim and done bits), zeroed by Phase 1
+    int64_t off_xu;       // [S][2][C][CW] f32: Phase-2 teams' exchange, per column slice of CW columns:
+                          //   u of every token, then inter; S * CW <= head_dim rounded up to 64
     int64_t off_beta;     // [C] f32: beta (0 for padding)
     int64_t off_A, off_QK, off_X, off_QX;   // [C, C] f32
     // [stage0, stage1): every array Phase 2 reads (records, weights, ids, meta, beta, X, QX),
@@ -227,7 +231,9 @@ __host__ __device__ inline int bucket_bits(int64_t E) {
     return b;
 }
 
-inline ChunkLayout make_layout(int C, int W, int R) {
+constexpr int kTeamMaxSlices = 28;   // column slices with team words in a chunk's meta (8 + 2 x 28 = 64)
+
+inline ChunkLayout make_layout(int C, int W, int R, int hd) {
     ChunkLayout L{};
     L.E = int64_t(C) * W;
     L.F = int64_t(C) * R;
@@ -270,21 +276,24 @@ inline ChunkLayout make_layout(int C, int W, int R) {
     L.off_gr = take(L.F);
     L.off_kid = take(L.E);
     L.off_qid = take(L.F);
-    L.off_meta = take(8);
+    L.off_meta = take(64);
     L.off_beta = take(C);
     L.off_X = take(L.C2);
     L.off_QX = take(L.C2);
     L.off_stage1 = o;
+    L.off_xu = take(2 * int64_t(C) * ((hd + 63) / 64) * 64);
     L.words = o;
     return L;
 }
 
 // Phase-2 launch geometry: vectors per column slice, slices per row, and the mode: 0 all
 // from memory, 1 the chunk's Phase-2 block staged in LDS, 2 staged and the bank slice
-// resident in LDS.
+// resident in LDS; team: workgroups per (stream, slice) (1: one; 2 or 4 share its tokens,
+// memory mode only).
 struct P2Geom {
     int nv, S;
     int mode;
+    int team;
 };
 
 struct Slab {

@@ -344,6 +344,7 @@ __device__ __forceinline__ void groups_chunk(const Problem &pb, const Slab &sl, 
         const int32_t bl = El > 0 ? min(int32_t(skey[El - 1] >> bsh), NB - 1) : -1;
         for (int32_t b = bl + 1 + tid; b <= NB; b += BLOCK) bstart[b] = El;
     }
+    for (int x = 8 + tid; x < 64; x += BLOCK) meta[x] = 0;   // Phase-2 team barrier counters
     if (tid == 0) {
         gpos[ng] = El;
         meta[0] = nl;

@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
     }
     __syncthreads();
     if (s.fallback) return;
+    for (int x = 8 + tid; x < 64; x += kPartBlock) meta[x] = 0;   // Phase-2 team barrier counters
 
     // ---- chunk prologue: beta, the ids in entry order (Phase 2 reads them), padding
     //      weights and records

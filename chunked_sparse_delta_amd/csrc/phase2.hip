@@ -32,6 +32,7 @@
 //   matmul  16-wide k blocks ascending, each one MFMA chain of four k-steps;
 //   DW      decay term first, then the group's members in token order.
 #include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -65,6 +66,8 @@ struct P2Args {
     int32_t ti0, steps;             // the slab
     int32_t off_gw, off_gr, off_beta, off_X, off_QX, off_meta, off_grec, off_mrec, off_brec;   // words within a chunk
     int32_t off_kid, off_qid, off_stage0, off_stage1;
+    int32_t off_xu;                 // teams: the exchange area of a chunk
+    uint32_t steal_ticks;           // teams: wait before claiming another workgroup's piece (100 MHz ticks)
 };
 
 // Live tokens of stream p (valid_tokens clamped to [0, T]), and of its chunk ti.
@@ -397,6 +400,110 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
 #pragma unroll
         for (int c = 0; c < V; ++c) b[c] = b[c] * dec + acc[c];
         Vec<T, V>::store(at(bank, uint32_t(rec.x) * uint32_t(hd) + col), b);
+    }
+}
+
+// DW of the groups grec[0, ng) and of the groups with >= kHotMin members brec[0, nbig): one
+// writer per written row. The many-member groups go to whole wavefronts (dw_big_group); the
+// others are summed in token order by the NV lanes of their slice: lane (gs, vq) of slot u
+// takes group gb + u * NW * GPI + gs of each batch, the first member rides in the group
+// record, the second loads with the bank row, the rest four at a time. kB groups per lane
+// are in flight; SM: the records are in LDS (the loads past the last batch are skipped).
+template <typename T, int V, int NV, int NW, int kB, bool SM>
+__device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, int32_t ng, const int4 *brec,
+                                          int32_t nbig, const int2 *mrec, const float *db, int pitch, int nvs,
+                                          int wave) {
+    int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
+    asm volatile("" : "+v"(dlane));
+    for (int32_t bi = wave; bi < nbig; bi += NW) {
+        const int4 rec = *at(brec, uint32_t(bi));
+        dw_big_group<T, V>(bank, bst, rec, mrec, db, pitch, 0, nvs, dlane);
+    }
+    constexpr int GPI = kWave / NV;                       // groups per load instruction
+    constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
+    const int gs = dlane / NV, vq = dlane % NV;
+    const bool vok = vq < nvs;
+    const uint32_t col = uint32_t(vq * V);
+    // a record of a group with fewer than kHotMin members (slot -1: no group)
+    auto small = [](const int4 &r) { return r.x >= 0 && ((r.y >> 16) & 0xFF) < kHotMin - 1; };
+    // slot u of a batch takes groups gb + u * NW * GPI + gs: the instructions of a batch
+    // are dealt to all waves first, so that a few groups still keep every wave busy
+    // loads unconditional (in-bounds fallbacks), as in the gather
+    auto load_rec = [&](int32_t g) {
+        const int4 x = *at(grec, uint32_t(g < ng ? g : 0));
+        return g < ng ? x : make_int4(-1, 0, 0, 0);
+    };
+    int4 rec[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) rec[u] = load_rec(wave * GPI + u * NW * GPI + gs);
+    for (int32_t gb = wave * GPI; gb < ng; gb += kStride) {
+        typename Vec<T, V>::raw_t raw[kB];
+        int2 mr[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const bool sm = small(rec[u]);
+            raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
+            const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
+            const bool two = sm && n1 > 0;
+            const int2 x = *at(mrec, uint32_t(two ? m0 + 1 : 0));
+            mr[u] = two ? x : make_int2(0, 0);
+        }
+        int4 nrec[kB];
+        // records in LDS (staged): the loads past the last batch are skipped
+        if (!SM || gb + kStride < ng) {
+#pragma unroll
+            for (int u = 0; u < kB; ++u) nrec[u] = load_rec(gb + kStride + u * NW * GPI + gs);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kB; ++u) nrec[u] = make_int4(-1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            if (!small(rec[u])) continue;
+            const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF, t0 = (rec[u].y >> 24) & 0xFF;
+            float acc[V];
+            if (vok) {
+                Vec<T, V>::unpack(raw[u], acc);
+            } else {
+#pragma unroll
+                for (int c = 0; c < V; ++c) acc[c] = 0.0f;
+            }
+            const float dec = __int_as_float(rec[u].z);
+#pragma unroll
+            for (int c = 0; c < V; ++c) acc[c] *= dec;
+            {
+                const float cwv = __int_as_float(rec[u].w);
+                float dv[V];
+                lds_load_vec<V>(db + t0 * pitch + vq * V, dv);
+#pragma unroll
+                for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+            }
+            if (n1 > 0) {
+                const float cwv = __int_as_float(mr[u].y);
+                float dv[V];
+                lds_load_vec<V>(db + mr[u].x * pitch + vq * V, dv);
+#pragma unroll
+                for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+            }
+            // members 2.. (at most kHotMin - 2 of them), four records at a time
+            for (int32_t m = m0 + 2; m <= m0 + n1; m += 4) {
+                int2 mb[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) mb[q] = *at(mrec, uint32_t(min(m + q, m0 + n1)));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (m + q > m0 + n1) break;
+                    const float cwv = __int_as_float(mb[q].y);
+                    float dv[V];
+                    lds_load_vec<V>(db + mb[q].x * pitch + vq * V, dv);
+#pragma unroll
+                    for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+                }
+            }
+            if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
     }
 }
 
@@ -798,117 +905,20 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             lds_barrier();
         }
 
-        // ---- DW: one writer per written row. Groups with >= kHotMin members go to whole
-        //      wavefronts (dw_big_group, from the list of their records); the others are
-        //      summed in token order by the NV lanes of their slice: lane (gs, vq) of slot u
-        //      takes group gb + u * NW * GPI + gs of each batch, the first member rides in
-        //      the group record, the second loads with the bank row, the rest four at a time.
+        // ---- DW: one writer per written row
         {
-            int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
-            asm volatile("" : "+v"(dlane));
             if constexpr (!SM) {
                 if (nl > 0) {
                     dw_ng = mng;
                     dw_nbig = mnbig;
                 }
             }
-            const int32_t ng = dw_ng, nbig = dw_nbig;
-            const int4 *grec = reinterpret_cast<const int4 *>(arr(a.off_grec));
-            const int4 *brec = reinterpret_cast<const int4 *>(arr(a.off_brec));
-            const int2 *mrec = reinterpret_cast<const int2 *>(arr(a.off_mrec));
-            for (int32_t bi = wave; bi < nbig; bi += NW) {
-                const int4 rec = *at(brec, uint32_t(bi));
-                dw_big_group<T, V>(bank, bst, rec, mrec, db, pitch, 0, nvs, dlane);
-            }
-            constexpr int GPI = kWave / NV;                       // groups per load instruction
             // groups per lane in flight: the bank in LDS needs no batching; staged, two leave
             // room for the prefetch registers
             constexpr int kB = RB ? 1 : (SM ? 2 : Cfg::kDwBatch);
-            constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
-            const int gs = dlane / NV, vq = dlane % NV;
-            const bool vok = vq < nvs;
-            const uint32_t col = uint32_t(vq * V);
-            // a record of a group with fewer than kHotMin members (slot -1: no group)
-            auto small = [](const int4 &r) { return r.x >= 0 && ((r.y >> 16) & 0xFF) < kHotMin - 1; };
-            // slot u of a batch takes groups gb + u * NW * GPI + gs: the instructions of a batch
-            // are dealt to all waves first, so that a few groups still keep every wave busy
-            // loads unconditional (in-bounds fallbacks), as in the gather
-            auto load_rec = [&](int32_t g) {
-                const int4 x = *at(grec, uint32_t(g < ng ? g : 0));
-                return g < ng ? x : make_int4(-1, 0, 0, 0);
-            };
-            int4 rec[kB];
-#pragma unroll
-            for (int u = 0; u < kB; ++u) rec[u] = load_rec(wave * GPI + u * NW * GPI + gs);
-            for (int32_t gb = wave * GPI; gb < ng; gb += kStride) {
-                typename Vec<T, V>::raw_t raw[kB];
-                int2 mr[kB];
-#pragma unroll
-                for (int u = 0; u < kB; ++u) {
-                    const bool sm = small(rec[u]);
-                    raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
-                    const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
-                    const bool two = sm && n1 > 0;
-                    const int2 x = *at(mrec, uint32_t(two ? m0 + 1 : 0));
-                    mr[u] = two ? x : make_int2(0, 0);
-                }
-                int4 nrec[kB];
-                // records in LDS (staged): the loads past the last batch are skipped
-                if (!SM || gb + kStride < ng) {
-#pragma unroll
-                    for (int u = 0; u < kB; ++u) nrec[u] = load_rec(gb + kStride + u * NW * GPI + gs);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < kB; ++u) nrec[u] = make_int4(-1, 0, 0, 0);
-                }
-#pragma unroll
-                for (int u = 0; u < kB; ++u) {
-                    if (!small(rec[u])) continue;
-                    const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF, t0 = (rec[u].y >> 24) & 0xFF;
-                    float acc[V];
-                    if (vok) {
-                        Vec<T, V>::unpack(raw[u], acc);
-                    } else {
-#pragma unroll
-                        for (int c = 0; c < V; ++c) acc[c] = 0.0f;
-                    }
-                    const float dec = __int_as_float(rec[u].z);
-#pragma unroll
-                    for (int c = 0; c < V; ++c) acc[c] *= dec;
-                    {
-                        const float cwv = __int_as_float(rec[u].w);
-                        float dv[V];
-                        lds_load_vec<V>(db + t0 * pitch + vq * V, dv);
-#pragma unroll
-                        for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
-                    }
-                    if (n1 > 0) {
-                        const float cwv = __int_as_float(mr[u].y);
-                        float dv[V];
-                        lds_load_vec<V>(db + mr[u].x * pitch + vq * V, dv);
-#pragma unroll
-                        for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
-                    }
-                    // members 2.. (at most kHotMin - 2 of them), four records at a time
-                    for (int32_t m = m0 + 2; m <= m0 + n1; m += 4) {
-                        int2 mb[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) mb[q] = *at(mrec, uint32_t(min(m + q, m0 + n1)));
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            if (m + q > m0 + n1) break;
-                            const float cwv = __int_as_float(mb[q].y);
-                            float dv[V];
-                            lds_load_vec<V>(db + mb[q].x * pitch + vq * V, dv);
-#pragma unroll
-                            for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
-                        }
-                    }
-                    if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
-                }
-#pragma unroll
-                for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
-            }
+            dw_groups<T, V, NV, NW, kB, SM>(bank, bst, reinterpret_cast<const int4 *>(arr(a.off_grec)), dw_ng,
+                                            reinterpret_cast<const int4 *>(arr(a.off_brec)), dw_nbig,
+                                            reinterpret_cast<const int2 *>(arr(a.off_mrec)), db, pitch, nvs, wave);
         }
         step_end_barrier<RB>();   // the DW's bank stores are visible to the next step's gather
         if constexpr (SM) {
@@ -930,6 +940,318 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             const int row = i / NV, vq = i % NV;
             if (vq < nvs) *reinterpret_cast<raw_t *>(at(gbank, uint32_t(row) * uint32_t(hd) + uint32_t(vq * V))) =
                 *reinterpret_cast<const raw_t *>(lbank + row * CW + vq * V);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Teams (memory mode). When slices of one 128-byte line per row leave most CUs idle (few
+// streams), TEAM workgroups share one (stream, slice) instead of narrowing the slices: the
+// chunk's tokens are cut into TEAM pieces of CT = C / TEAM tokens (whole 16-token tiles)
+// and its DW groups into TEAM shares of consecutive records. A step has two phases of
+// TEAM pieces each:
+//   G(k)  gather of piece k's tokens, whole lines per row; u = beta (v - retrieved) and
+//         inter of those tokens go to the chunk's exchange area
+//   D(k)  after every G piece: delta_v = X u over all tokens, the readings of piece k's
+//         tokens (QX u + inter), the DW of share k
+// Every piece runs the same arithmetic as the one-workgroup kernel on the same operands,
+// so the bits do not depend on the team size or on which workgroup runs which piece.
+//
+// Pieces are claimed with an atomic OR on the team's word for the phase (bit k claims
+// piece k, bit 8 + k marks it done). A workgroup claims its own piece first and then waits
+// for the others; a piece nobody has claimed after kTeamStealTicks is claimed and run by
+// the waiting workgroup. A wait is therefore only ever on a piece that a running
+// workgroup holds: a team does not need all of its workgroups on CUs at once (another
+// kernel may hold some CUs), and every wait ends.
+//
+// Memory ordering. A team's workgroups sit on one XCD (blocks are dealt to the XCDs
+// round-robin and a team's block ids are congruent mod 8; the library checks that
+// placement on each device before it plans teams), so they share one L2, and the L1 is
+// write-through: a piece's stores are complete in that L2 once every wave has waited for
+// them (s_waitcnt vmcnt(0)), before its done bit is set. The words are only touched by
+// atomics and agent-scope loads. A workgroup that has seen every done bit of a phase
+// invalidates its L1 (the agent-scope acquire, buffer_inv sc1) before it reads what the
+// others wrote. The agent-scope release (an L2 write-back, for readers on other XCDs) is
+// not needed between workgroups of one L2, and would cost a quarter of the step.
+constexpr uint32_t kTeamStealTicks = 2000;         // 20 us of the 100 MHz real-time counter
+constexpr uint64_t kTeamGiveUpTicks = 200000000;   // 2 s: the bound of a workgroup's team waits
+constexpr uint32_t kTeamGaveUp = 1u << 31;         // set in a word whose wait gave up
+
+
+// Thread 0: the piece this workgroup runs next (claimed for it), or -1 once every piece of
+// the phase is done. `first`: try the workgroup's own piece before waiting. A wait ends at
+// the latest when the workgroup's waits have taken kTeamGiveUpTicks in all (`waited`);
+// that cannot happen while every claimed piece completes, and it is then marked in the
+// word (kTeamGaveUp) and every later wait of the workgroup returns at once.
+template <int TEAM>
+__device__ int team_next(uint32_t *word, int own, bool first, uint32_t steal_ticks, uint64_t &waited) {
+    constexpr uint32_t kAllDone = ((1u << TEAM) - 1u) << 8;
+    if (first) {
+        const uint32_t old = __hip_atomic_fetch_or(word, 1u << own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!(old & (1u << own))) return own;
+    }
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        const uint32_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v & kAllDone) == kAllDone) break;
+        const uint64_t dt = __builtin_amdgcn_s_memrealtime() - t0;
+        if (dt >= steal_ticks) {
+            for (int k = 0; k < TEAM; ++k) {
+                if (v & (1u << k)) continue;
+                const uint32_t old = __hip_atomic_fetch_or(word, 1u << k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!(old & (1u << k))) {
+                    waited += dt;
+                    return k;
+                }
+            }
+        }
+        if (waited + dt > kTeamGiveUpTicks) {
+            __hip_atomic_fetch_or(word, kTeamGaveUp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            waited = kTeamGiveUpTicks + 1;
+            return -1;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    waited += __builtin_amdgcn_s_memrealtime() - t0;
+    return -1;
+}
+
+template <typename T, int V>
+__device__ __forceinline__ void store_zero(T *p) {
+    float z[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) z[c] = 0.0f;
+    Vec<T, V>::store(p, z);
+}
+
+template <int V>
+__device__ __forceinline__ void gmem_store_f32(float *p, const float (&x)[V]) {
+#pragma unroll
+    for (int c = 0; c < V; c += 4) *reinterpret_cast<float4 *>(p + c) = make_float4(x[c], x[c + 1], x[c + 2], x[c + 3]);
+}
+
+template <int V>
+__device__ __forceinline__ void gmem_load_f32(const float *p, float (&x)[V]) {
+#pragma unroll
+    for (int c = 0; c < V; c += 4) {
+        const float4 y = *reinterpret_cast<const float4 *>(p + c);
+        x[c] = y.x; x[c + 1] = y.y; x[c + 2] = y.z; x[c + 3] = y.w;
+    }
+}
+
+template <typename T, int V, int TEAM>
+__global__ __launch_bounds__(kP2Block) void phase2_team_kernel(P2Args a) {
+    constexpr int BLOCK = kP2Block, NV = 8, CW = V * NV;
+    static_assert(V % 4 == 0, "slices of whole 16-byte float groups");
+    using Cfg = P2Cfg<BLOCK, V>;
+    constexpr int NW = Cfg::NW;
+    extern __shared__ float lds[];
+    // the piece thread 0 has claimed for the workgroup (-1: the phase is done), one word per
+    // phase: thread 0 may claim the next step's first G piece while a wave still reads the
+    // end of this step's D phase
+    __shared__ int sel[2];
+    const int C = a.C, hd = a.hd, S = a.S;
+    const int CT = C / TEAM;                  // tokens per piece: whole 16-token tiles
+    const int pitch = p2_pitch(CW);
+
+    // Decode (stream, slice, member): block ids of one team are congruent mod 8 (one XCD).
+    const int bid = blockIdx.x;
+    const int xcd = bid % kXcds, m = bid / kXcds, unit = m / TEAM, me = m % TEAM;
+    const int p = xcd + kXcds * (unit / S), slice = unit % S;
+    const int vq0 = slice * NV;
+    const int nvs = min(NV, a.hv - vq0);
+    const int cwv = nvs * V;
+    const int col0 = vq0 * V;
+    T *gbank = static_cast<T *>(a.bank) + int64_t(p) * a.bstride + col0;
+
+    float *ub = lds;                  // [C][pitch]: retrieved of a G piece's tokens, then u of every token
+    float *db = lds + C * pitch;      // [C][pitch]: delta_v
+    float *ib = db + C * pitch;       // [CT][pitch]: inter of one piece's tokens
+    const int NIT = C / 16, NCT = (cwv + 15) / 16, NT = NIT * NCT;
+    const int32_t vtp = stream_tokens(a, p);
+    uint64_t waited = 0;   // thread 0: time spent in team waits
+
+    for (int s = 0; s < a.steps; ++s) {
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        asm volatile("" : "+s"(wave));
+        int lane = tid & 63;
+        const int ti = a.ti0 + s;
+        uint32_t *cb = const_cast<uint32_t *>(a.ws) + (int64_t(p) * a.steps + s) * a.words;
+        const int nl = chunk_tokens(a, vtp, ti);
+        const int rows = min(C, a.T - ti * C);
+        const int64_t tok0 = int64_t(p) * a.T + int64_t(ti) * C;
+        const T *vin = static_cast<const T *>(a.v) + tok0 * hd;
+        T *out = static_cast<T *>(a.out) + tok0 * hd;
+        if (nl == 0) {
+            // past the stream's live tokens: no row changes; the readings of this member's
+            // piece are zeros (each member's own piece: every member runs every step)
+            for (int i = tid; i < CT * NV; i += BLOCK) {
+                const int t = me * CT + i / NV, vq = i % NV;
+                if (t < rows && vq < nvs) store_zero<T, V>(at(out, uint32_t(t * hd + col0 + vq * V)));
+            }
+            continue;
+        }
+        uint32_t *words = cb + a.off_meta + 8 + 2 * slice;     // [0]: G pieces, [1]: D pieces
+        float *xus = reinterpret_cast<float *>(cb + a.off_xu) + int64_t(slice) * 2 * C * CW;   // [C][CW] u
+        float *xis = xus + C * CW;                                                             // [C][CW] inter
+        const float *beta_c = reinterpret_cast<const float *>(cb + a.off_beta);
+
+        // ---- phase G
+        for (bool first = true;; first = false) {
+            if (tid == 0) {
+                const int k = team_next<TEAM>(words, me, first, a.steal_ticks, waited);
+                if (k < 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                sel[0] = k;
+            }
+            __syncthreads();
+            const int k = sel[0];
+            if (k < 0) break;
+            const int t0 = k * CT, nlk = min(max(nl - t0, 0), CT);
+            // v and beta of the piece's tokens, loaded before the gather (their round trip
+            // overlaps it; the asm keeps the compiler from moving them down to their use)
+            const int it_t = t0 + tid / NV, it_v = tid % NV;
+            const bool mine = tid < CT * NV;
+            const bool live = mine && it_t < t0 + nlk && it_v < nvs;
+            float mv[V];
+            Vec<T, V>::load(at(vin, live ? uint32_t(it_t * hd + col0 + it_v * V) : uint32_t(col0)), mv);
+            const float mb = beta_c[live ? it_t : 0];
+            asm volatile("" ::: "memory");
+            {
+                const float *gw = reinterpret_cast<const float *>(cb + a.off_gw);
+                const float *gr = reinterpret_cast<const float *>(cb + a.off_gr);
+                const int32_t *kid = reinterpret_cast<const int32_t *>(cb + a.off_kid);
+                const int32_t *qid = reinterpret_cast<const int32_t *>(cb + a.off_qid);
+                int nww = (NW * a.W + (a.W + a.R) / 2) / (a.W + a.R);
+                nww = nww < 1 ? 1 : (nww > NW - 1 ? NW - 1 : nww);
+                const bool wr = wave < nww;
+                const int32_t *rid = wr ? kid + t0 * a.W : qid + t0 * a.R;
+                const float *rwt = wr ? gw + t0 * a.W : gr + t0 * a.R;
+                const int rwidth = wr ? a.W : a.R, rwave = wr ? wave : wave - nww, rnw = wr ? nww : NW - nww;
+                float *rdst = wr ? ub + t0 * pitch : ib;
+                if (((a.W | a.R) & 31) == 0)
+                    gather_region<T, V, NV, 2, 4, false>(gbank, hd, rid, rwt, rwidth, nlk, 0, nvs, rdst, pitch, rwave,
+                                                         rnw, lane, false, nullptr, nullptr);
+                else
+                    gather_region<T, V, NV, Cfg::kBatch, 1, false>(gbank, hd, rid, rwt, rwidth, nlk, 0, nvs, rdst,
+                                                                   pitch, rwave, rnw, lane, false, nullptr, nullptr);
+            }
+            lds_barrier();
+            if (mine) {   // u and inter of the piece's rows (zeros for padding tokens) to the exchange
+                float uu[V], ii[V];
+                if (live) {
+                    float rr[V];
+                    lds_load_vec<V>(ub + it_t * pitch + it_v * V, rr);
+                    lds_load_vec<V>(ib + (it_t - t0) * pitch + it_v * V, ii);
+#pragma unroll
+                    for (int c = 0; c < V; ++c) uu[c] = mb * (mv[c] - rr[c]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < V; ++c) uu[c] = ii[c] = 0.0f;
+                }
+                gmem_store_f32<V>(xus + it_t * CW + it_v * V, uu);
+                gmem_store_f32<V>(xis + it_t * CW + it_v * V, ii);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_or(words, 1u << (8 + k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // ---- u of every token
+        for (int i = tid; i < C * NV; i += BLOCK) {
+            float x[V];
+            gmem_load_f32<V>(xus + (i / NV) * CW + (i % NV) * V, x);
+            lds_store_vec<V>(ub + (i / NV) * pitch + (i % NV) * V, x);
+        }
+        __syncthreads();
+
+        // ---- phase D
+        const float *QX = reinterpret_cast<const float *>(cb + a.off_QX);
+        const float *X = reinterpret_cast<const float *>(cb + a.off_X);
+        bool have_d = false;
+        for (bool first = true;; first = false) {
+            if (tid == 0) {
+                const int k = team_next<TEAM>(words + 1, me, first, a.steal_ticks, waited);
+                if (k < 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                sel[1] = k;
+            }
+            __syncthreads();
+            const int k = sel[1];
+            if (k < 0) break;
+            const int t0 = k * CT;
+            for (int i = tid; i < CT * NV; i += BLOCK) {
+                float x[V];
+                gmem_load_f32<V>(xis + (t0 + i / NV) * CW + (i % NV) * V, x);
+                lds_store_vec<V>(ib + (i / NV) * pitch + (i % NV) * V, x);
+            }
+            lds_barrier();
+            // delta_v of every token (first piece only) and the readings of piece k, on the
+            // matrix cores: the same tiles, k blocks and MFMA chains as the one-workgroup kernel
+            asm volatile("" : "+v"(lane));
+            const bool dod = !have_d;
+            const int iy0 = t0 / 16, iy1 = (t0 + CT) / 16;
+#pragma unroll
+            for (int q = 0; q < Cfg::kMaxTiles; ++q) {
+                const int tau = q * NW + ((q & 1) ? NW - 1 - wave : wave);
+                if (tau >= NT) continue;
+                const int it = tau / NCT, ct = tau - it * NCT;
+                const bool cy = it >= iy0 && it < iy1;
+                if (!cy && !dod) continue;
+                const int ti_row = 16 * it + (lane & 15);
+                const int cu = 16 * ct + (lane & 15);
+                const int co = 16 * ct + 4 * (lane >> 4);
+                const int ko = 4 * (lane >> 4);
+                f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (cy && co < cwv) {
+                    const float4 iv = *reinterpret_cast<const float4 *>(ib + (ti_row - t0) * pitch + co);
+                    y = f32x4{iv.x, iv.y, iv.z, iv.w};
+                }
+                f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int kb = 0; kb <= it; kb += Cfg::kMmDepth) {
+                    // zero-initialized: operands loaded under a condition would otherwise stay
+                    // live across the step loop (and spill)
+                    float bq[Cfg::kMmDepth][4] = {}, bx[Cfg::kMmDepth][4] = {}, av[Cfg::kMmDepth][4] = {};
+#pragma unroll
+                    for (int j = 0; j < Cfg::kMmDepth; ++j) {
+                        if (kb + j > it) continue;
+                        if (cy) load_bop<true>(QX, C, ti_row, 16 * (kb + j) + ko, true, bq[j]);
+                        if (dod) load_bop<true>(X, C, ti_row, 16 * (kb + j) + ko, true, bx[j]);
+                        load_aop(ub + (16 * (kb + j) + ko) * pitch + cu, pitch, cu < cwv, av[j]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < Cfg::kMmDepth; ++j) {
+                        if (kb + j > it) continue;
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            if (cy) y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][kk], bq[j][kk], y, 0, 0, 0);
+                            if (dod) d = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j][kk], bx[j][kk], d, 0, 0, 0);
+                        }
+                    }
+                }
+                if (dod && co < cwv)
+                    *reinterpret_cast<float4 *>(db + ti_row * pitch + co) = make_float4(d[0], d[1], d[2], d[3]);
+                if (cy && ti_row < rows && co < cwv) {
+                    if (ti_row >= nl) y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    store_out4<T>(at(out, uint32_t(ti_row * hd + col0 + co)), y, min(4, cwv - co));
+                }
+            }
+            have_d = true;
+            lds_barrier();
+            // DW of share k: group records [g0, g1) and many-member records [b0, b1)
+            {
+                const int32_t *meta = reinterpret_cast<const int32_t *>(cb + a.off_meta);
+                const int32_t ng = meta[2], nbig = meta[4];
+                const int32_t g0 = int32_t(int64_t(ng) * k / TEAM), g1 = int32_t(int64_t(ng) * (k + 1) / TEAM);
+                const int32_t b0 = int32_t(int64_t(nbig) * k / TEAM), b1 = int32_t(int64_t(nbig) * (k + 1) / TEAM);
+                dw_groups<T, V, NV, NW, Cfg::kDwBatch, false>(
+                    gbank, hd, reinterpret_cast<const int4 *>(cb + a.off_grec) + g0, g1 - g0,
+                    reinterpret_cast<const int4 *>(cb + a.off_brec) + b0, b1 - b0,
+                    reinterpret_cast<const int2 *>(cb + a.off_mrec), db, pitch, nvs, wave);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_or(words + 1, 1u << (8 + k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -967,6 +1289,53 @@ static const void *phase2_fn(int dtype, int V, int nv, int mode) {
     }
 }
 
+template <typename T, int V>
+static const void *p2_team_fn_t(int team) {
+    return team == 2 ? reinterpret_cast<const void *>(&phase2_team_kernel<T, V, 2>)
+                     : reinterpret_cast<const void *>(&phase2_team_kernel<T, V, 4>);
+}
+
+// Team kernels: float banks in 16-byte vectors of 4, bfloat16 banks in vectors of 8.
+static const void *phase2_team_fn(int dtype, int team) {
+    return dtype == 0 ? p2_team_fn_t<float, 4>(team) : p2_team_fn_t<bf16, 8>(team);
+}
+
+// LDS of a team workgroup: u and delta_v of every token, inter of one piece's tokens.
+size_t phase2_team_lds_bytes(int C, int V, int team) {
+    return size_t(2 * C + C / team) * p2_pitch(8 * V) * sizeof(float);
+}
+
+// One workgroup of 64 threads per block id: the XCD it runs on.
+__global__ __launch_bounds__(64) void xcd_probe_kernel(int32_t *xcc) {
+    uint32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    if (threadIdx.x == 0) xcc[blockIdx.x] = int32_t(x);
+}
+
+// Whether blocks whose ids are congruent mod 8 run on one XCD (teams share an L2 only
+// then): one launch of 4096 blocks on a private stream, its XCD ids compared. `buf`:
+// 4096 int32 of device memory. Any failure answers false.
+bool phase2_teams_share_l2(int32_t *buf) {
+    constexpr int kBlocks = 4096;
+    hipStream_t st = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    static int32_t host[kBlocks];
+    hipLaunchKernelGGL(xcd_probe_kernel, dim3(kBlocks), dim3(64), 0, st, buf);
+    const bool ok = hipGetLastError() == hipSuccess && hipMemcpyAsync(host, buf, sizeof(host), hipMemcpyDeviceToHost, st) == hipSuccess &&
+         hipStreamSynchronize(st) == hipSuccess;
+    (void)hipStreamDestroy(st);
+    if (!ok) {
+        (void)hipGetLastError();
+        return false;
+    }
+    for (int b = kXcds; b < kBlocks; ++b)
+        if (host[b] != host[b % kXcds]) return false;
+    return true;
+}
+
 hipError_t phase2_prepare() {
     for (int dt = 0; dt < 2; ++dt)
         for (int V : {1, dt == 0 ? 4 : 8})
@@ -976,6 +1345,12 @@ hipError_t phase2_prepare() {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 256);
                     if (e != hipSuccess) return e;
                 }
+    for (int dt = 0; dt < 2; ++dt)
+        for (int team : {2, 4}) {
+            hipError_t e = hipFuncSetAttribute(phase2_team_fn(dt, team), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               160 * 1024 - 256);
+            if (e != hipSuccess) return e;
+        }
     return hipFuncSetAttribute(phase2_fn(1, 4, 1, kP2Resident), hipFuncAttributeMaxDynamicSharedMemorySize,
                                160 * 1024 - 256);
 }
@@ -1018,9 +1393,22 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
     a.off_grec = int32_t(L.off_grec); a.off_mrec = int32_t(L.off_mrec); a.off_brec = int32_t(L.off_brec);
     a.off_kid = int32_t(L.off_kid); a.off_qid = int32_t(L.off_qid);
     a.off_stage0 = int32_t(L.off_stage0); a.off_stage1 = int32_t(L.off_stage1);
+    a.off_xu = int32_t(L.off_xu);
     const int es = pb.dtype == 0 ? 4 : 2;
-    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
     void *args[] = {&a};
+    if (g.team > 1) {
+        // the planner's conditions, checked again where the kernel's indexing depends on them
+        if (g.mode != kP2Global || g.nv != 8 || V * es != 16 || pb.P % kXcds != 0 || pb.C % (16 * g.team) != 0 ||
+            pb.C / g.team * 8 > kP2Block || g.S > kTeamMaxSlices || int64_t(g.S) * 8 * V > ((pb.hd + 63) & ~63))
+            return hipErrorInvalidValue;
+        // SDM_P2_TEAM_STEAL: the steal wait in ticks (0: claim any unclaimed piece at once)
+        const char *se = getenv("SDM_P2_TEAM_STEAL");
+        a.steal_ticks = se ? uint32_t(strtoul(se, nullptr, 10)) : kTeamStealTicks;
+        const void *fn = phase2_team_fn(pb.dtype, g.team);
+        return hipLaunchKernel(fn, dim3(unsigned(int64_t(pb.P) * g.S * g.team)), dim3(kP2Block), args,
+                               phase2_team_lds_bytes(pb.C, V, g.team), st);
+    }
+    const dim3 grid(unsigned(int64_t(pb.P) * g.S)), block(kP2Block);
     const void *fn = phase2_fn(pb.dtype, V, g.nv, g.mode);
     if (!fn) return hipErrorInvalidValue;
     return hipLaunchKernel(fn, grid, block, args,

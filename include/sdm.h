@@ -189,7 +189,9 @@ int sdm_fwd_noalloc(int32_t streams, int32_t tokens, int32_t chunk, const sdm_sl
  *   repeated-writes counter); v, bank->data and out are not accessed (may be NULL).
  * sdm_fwd_phase2: Phase 2 from that workspace; the caller orders it after the
  *   sdm_fwd_phase1 call with the same arguments and workspace (same stream, or an event),
- *   and keeps the workspace unchanged between the two.
+ *   and keeps the workspace unchanged between the two. Phase 2 keeps bookkeeping of its
+ *   own in the workspace: every sdm_fwd_phase2 call needs an sdm_fwd_phase1 call of its
+ *   own before it.
  * The pair computes exactly sdm_fwd's result (same bits).
  */
 int sdm_fwd_phase1(int32_t streams, int32_t tokens, int32_t chunk, const sdm_slots *slots,
@@ -273,7 +275,7 @@ typedef struct {
                                   slice would still leave more than half of the CUs idle; 1 when
                                   head_dim is not a multiple of the 16-byte count */
     int32_t slice_vectors;     /* vectors per column slice of Phase 2 */
-    int32_t slices;            /* column slices per stream: Phase 2 runs streams * slices workgroups */
+    int32_t slices;            /* column slices per stream */
     int32_t phase2_mode;       /* 0: Phase-2 arrays and bank rows read from memory; 1: the chunk's
                                   Phase-2 block staged in LDS; 2: staged, and the workgroup's
                                   column slice of the bank held in LDS for the whole call */
@@ -284,6 +286,10 @@ typedef struct {
                                   sorting every write entry of a chunk in memory */
     int32_t lds_limit;         /* LDS bytes per workgroup the plan may use */
     int32_t lds_default;       /* the device's default per-workgroup LDS limit */
+    int32_t phase2_team;       /* workgroups per (stream, slice): Phase 2 runs streams * slices *
+                                  phase2_team workgroups; 2 or 4 (memory mode only) split each
+                                  chunk's tokens and DW groups among them, exchanging u through
+                                  the workspace */
 } sdm_plan;
 
 int sdm_fwd_plan(int32_t streams, int32_t tokens, int32_t chunk, int32_t W, int32_t R, int32_t head_dim,

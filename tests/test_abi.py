@@ -63,14 +63,17 @@ def test_workspace_bytes(lib):
     assert f(8, 2048, 64, 8, 257, 64, 0) == 0             # R > 256
     # 112 B per write entry, 24 B per read entry, 16 B per chunk-matrix element, a slot
     # search index of about one word per write entry (a power of two, at most 2^14), 20 B
-    # per possible group of >= 16 members and the three dense hot operands [C][HCAP]
-    # (HCAP = that count rounded up to 16, at most 512) (+ alignment)
+    # per possible group of >= 16 members, the three dense hot operands [C][HCAP]
+    # (HCAP = that count rounded up to 16, at most 512), 64 words of counts and team words,
+    # and the Phase-2 team exchange of u and inter, 2 x C x head_dim (rounded up to 64)
+    # floats (+ alignment)
     per_chunk = step / 8
-    E, F, C2, C = 64 * 8, 64 * 8, 64 * 64, 64
+    E, F, C2, C, hd = 64 * 8, 64 * 8, 64 * 64, 64, 64
     NB = 512
     hmax = E // 16 + 1
     hcap = min(512, (hmax + 15) // 16 * 16)
-    base = 112 * E + 24 * F + 16 * C2 + 4 * (NB + 1) + 20 * hmax + 12 * C * hcap
+    base = (112 * E + 24 * F + 16 * C2 + 4 * (NB + 1) + 20 * hmax + 12 * C * hcap + 4 * 64
+            + 8 * C * ((hd + 63) // 64 * 64))
     assert base <= per_chunk <= base + 40 * 256
 
 
