@@ -266,8 +266,8 @@ P2Geom plan_phase2(const Problem &pb, const ChunkLayout &L, int V, int es, int c
 // instruction issue), and still room beside them for another batch's Phase 1. Slices never
 // change the bits. (Narrower still, 2 columns, measured no faster and fills every CU.)
 // Teams: when slices of one 128-byte line per row (8 vectors of 16 bytes) leave CUs idle and
-// the bank stays in memory, 4 (else 2) workgroups share each (stream, slice) instead of
-// narrowing the slices (whole lines per request: a quarter of the requests of 32-byte
+// the narrower slices planned instead read the bank from memory, 4 (else 2) workgroups
+// share each (stream, slice) (whole lines per request: a quarter of the requests of 32-byte
 // slices for the same bytes). Needs streams in whole groups of 8 (a team on one XCD),
 // pieces of whole 16-token tiles, and room for the team's LDS. SDM_P2_TEAM=0 turns teams
 // off, =2 or =4 asks for that size only; SDM_P2_GEOM alone turns them off (geometry sweeps).
@@ -280,8 +280,10 @@ bool plan_team(const Problem &pb, const ChunkLayout &L, int V, int es, int cus, 
     if (V * es != 16 || pb.P % kXcds != 0) return false;
     const int hv = pb.hd / V, S8 = (hv + 7) / 8;
     if (S8 > kTeamMaxSlices) return false;
-    // asked for by size: any shape the kernel takes (for tests and sweeps)
-    if (want < 0 && (int64_t(pb.P) * S8 >= cus || phase2_mode(L, pb.C, 8, V, es, pb.M, lds_limit) != 0)) return false;
+    // unasked, teams only replace narrow slices that read the bank from memory (narrow
+    // slices that stage the chunk's arrays or hold the bank in LDS are faster); asked for
+    // by size, any shape the kernel takes (for tests and sweeps)
+    if (want < 0 && (int64_t(pb.P) * S8 >= cus || g.mode != 0)) return false;
     for (int t = 4; t >= 2; t /= 2) {
         if (want > 0 && want != t) continue;
         if ((want < 0 && int64_t(pb.P) * S8 * t > cus) || pb.C % (16 * t) != 0 || pb.C / t * 8 > 1024) continue;

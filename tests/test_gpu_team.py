@@ -97,3 +97,15 @@ def test_full_size_config_3_teams(gpu, monkeypatch):
     assert np.array_equal(gu.bits(o_def), gu.bits(o_one)) and np.array_equal(gu.bits(b_def), gu.bits(b_one))
     o_st, b_st = _run_env(monkeypatch, t, wl.C, SDM_P2_TEAM_STEAL="0")
     assert np.array_equal(gu.bits(o_st), gu.bits(o_one)) and np.array_equal(gu.bits(b_st), gu.bits(b_one))
+
+
+def test_teams_only_replace_narrow_memory_mode_slices(gpu, monkeypatch):
+    """Unasked, teams stand in only for narrow slices that would read the bank from memory:
+    config 2's shapes (narrow slices stage the chunk's arrays in LDS) keep one workgroup
+    per slice."""
+    from chunked_sparse_delta_amd import plan
+    monkeypatch.delenv("SDM_P2_TEAM", raising=False)
+    monkeypatch.delenv("SDM_P2_GEOM", raising=False)
+    wl = workloads.CONFIGS["2"]
+    p = plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, torch.bfloat16)
+    assert p["phase2_team"] == 1 and p["phase2_mode"] != "memory", p
