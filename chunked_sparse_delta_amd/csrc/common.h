@@ -152,9 +152,11 @@ struct Problem {
                              // kernels then handle only the chunks it left to them (meta[7] = 1)
 };
 
-// Slot id i of an int32 or int64 id array (ids of valid calls lie in [0, M), M < 2^31).
+// Slot id i of an int32 or int64 id array (ids of valid calls lie in [0, M), M < 2^31): one
+// 32-bit load either way (an int64 id's low word), with no branch on the width, so that
+// loads of several ids issue back to back.
 __device__ __forceinline__ int32_t load_id(const void *base, int64_t i, int32_t id8) {
-    return id8 ? int32_t(static_cast<const int64_t *>(base)[i]) : static_cast<const int32_t *>(base)[i];
+    return *reinterpret_cast<const int32_t *>(static_cast<const char *>(base) + (id8 ? 8 * i : 4 * i));
 }
 
 __device__ __forceinline__ int32_t n_live_tokens(const Problem &pb, int p, int ti) {
@@ -164,8 +166,13 @@ __device__ __forceinline__ int32_t n_live_tokens(const Problem &pb, int p, int t
     return n < 0 ? 0 : (n > pb.C ? pb.C : n);
 }
 
+// Element i of a float32 (dtype 0) or bfloat16 array as a float, from one aligned 32-bit load
+// with no branch on the dtype (a bfloat16 is the half of its aligned word at its address;
+// the word lies inside the element's 4-byte aligned page-internal span, so it is mapped).
 __device__ __forceinline__ float load_weight(const void *base, int64_t i, int32_t dtype) {
-    return dtype == 0 ? static_cast<const float *>(base)[i] : to_f32(static_cast<const bf16 *>(base)[i]);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(base) + uintptr_t(dtype ? 2 * i : 4 * i);
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(a & ~uintptr_t(3));
+    return dtype ? __uint_as_float((a & 2) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -695,7 +695,6 @@ __device__ __forceinline__ void cold_row(const Problem &pb, const Slab &sl, int6
 // e^(L_t - L_t'). Each wavefront takes lower 16 x 16 tiles of A and QK in turn and
 // accumulates them with v_mfma_f32_16x16x4_f32 over h in blocks of 16 ascending (a fixed
 // order), operands read straight from memory, then adds them to the cold part.
-constexpr int kHotBlock = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -786,9 +785,106 @@ __global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Sl
     for (int i = wave; i < pb.C; i += NW) cold_row(pb, sl, blockIdx.x, blockIdx.y != 0, i, tcol[wave], tval[wave]);
 }
 
-__global__ __launch_bounds__(kHotBlock) void p1_gram_hot_kernel(Problem pb, Slab sl) {
-    constexpr int NWAVE = kHotBlock / kWave;
-    hot_tiles(pb, sl, blockIdx.x, blockIdx.y * NWAVE + (threadIdx.x >> 6), gridDim.y * NWAVE);
+// The hot pair terms of large chunks, one workgroup per (chunk, matrix): blockIdx.y = 0
+// computes A's lower tiles from Ka and Kb, 1 QK's from Qa and Kb. The operands' columns are
+// staged in LDS kHotKb at a time, each read once from memory (the next block's loads are in
+// flight during this block's products), and each wavefront accumulates its tiles over every
+// column block in registers with the MFMA chains of hot_tiles (16 columns at a time, lane
+// group l / 16 taking columns 4 (l / 16) .. + 3, h ascending): the same bits.
+constexpr int kHotLdsBlock = 1024;
+constexpr int kHotKb = 32;                 // hot columns per staged block
+constexpr int kHotPitch = kHotKb + 4;      // LDS row pitch (floats): 16-byte rows 4 banks apart
+constexpr int kHotMaxT = ((kMaxChunk / 16) * (kMaxChunk / 16 + 1) / 2 + kHotLdsBlock / kWave - 1) / (kHotLdsBlock / kWave);
+constexpr int kHotU = (2 * kMaxChunk * (kHotKb / 4) + kHotLdsBlock - 1) / kHotLdsBlock;   // 16-byte units per thread
+
+size_t hot_lds_bytes(int C) { return size_t(2) * ((C + 15) & ~15) * kHotPitch * sizeof(float); }
+
+__global__ __launch_bounds__(kHotLdsBlock) void p1_gram_hot_kernel(Problem pb, Slab sl) {
+    extern __shared__ float hl[];   // [2][CP][kHotPitch]: Kb's staged columns, then Ka's or Qa's
+    constexpr int NW = kHotLdsBlock / kWave;
+    const int64_t n = blockIdx.x;
+    const bool isA = blockIdx.y == 0;
+    const ChunkLayout &L = sl.lay;
+    uint32_t *cb = sl.chunk(n);
+    const int32_t *meta = reinterpret_cast<const int32_t *>(cb + L.off_meta);
+    const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
+    if (n_live_tokens(pb, p, ti) == 0) return;
+    const int nhot = meta[3], HP = meta[5];
+    if (nhot == 0) return;
+    const int C = pb.C, CP = (C + 15) & ~15, nt = CP / 16, T1 = nt * (nt + 1) / 2;
+    const float *Kb = reinterpret_cast<const float *>(cb + L.off_kb);
+    const float *Aop = reinterpret_cast<const float *>(cb + (isA ? L.off_ka : L.off_qa));
+    float *bl = hl, *al = hl + CP * kHotPitch;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ko = 4 * (lane >> 4);
+    const int nq = CP * (kHotKb / 4);   // 16-byte units of one staged operand block
+
+    // unit i: operand i / nq (0 Kb, 1 Ka or Qa), row, column quad; rows past C and
+    // columns past HP stage as 0 (loads unconditional, clamped in bounds)
+    float4 st[kHotU];
+    auto load = [&](int hb) {
+#pragma unroll
+        for (int u = 0; u < kHotU; ++u) {
+            const int i = tid + u * kHotLdsBlock, w = i / nq, rem = i - w * nq;
+            const int r = rem / (kHotKb / 4), col = hb + 4 * (rem % (kHotKb / 4));
+            const bool ok = i < 2 * nq && r < C && col < HP;
+            const float *src = (w == 0 ? Kb : Aop) + (ok ? int64_t(r) * L.HCAP + col : 0);
+            const float4 x = *reinterpret_cast<const float4 *>(src);
+            st[u] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < kHotU; ++u) {
+            const int i = tid + u * kHotLdsBlock, w = i / nq, rem = i - w * nq;
+            if (i < 2 * nq)
+                *reinterpret_cast<float4 *>(hl + (w * CP + rem / (kHotKb / 4)) * kHotPitch + 4 * (rem % (kHotKb / 4))) =
+                    st[u];
+        }
+    };
+    f32x4 acc[kHotMaxT];
+#pragma unroll
+    for (int q = 0; q < kHotMaxT; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    load(0);
+    for (int hb = 0; hb < HP; hb += kHotKb) {
+        __syncthreads();   // the previous block's products are done with the LDS
+        store();
+        __syncthreads();
+        if (hb + kHotKb < HP) load(hb + kHotKb);
+        const int nsb = min(kHotKb, HP - hb) / 16;   // 16-column sub-blocks (HP is a multiple of 16)
+#pragma unroll
+        for (int q = 0; q < kHotMaxT; ++q) {
+            const int t = wave + q * NW;
+            if (t >= T1) break;
+            int I = 0;
+            while ((I + 1) * (I + 2) / 2 <= t) ++I;
+            const int J = t - I * (I + 1) / 2;
+            const float *ar = al + (16 * I + (lane & 15)) * kHotPitch + ko;
+            const float *br = bl + (16 * J + (lane & 15)) * kHotPitch + ko;
+            for (int sb = 0; sb < nsb; ++sb) {
+                const float4 av = *reinterpret_cast<const float4 *>(ar + 16 * sb);
+                const float4 bv = *reinterpret_cast<const float4 *>(br + 16 * sb);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[q], 0, 0, 0);
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[q], 0, 0, 0);
+            }
+        }
+    }
+    // Add the hot part to the cold part, inside the triangle only.
+    float *M = reinterpret_cast<float *>(cb + (isA ? L.off_A : L.off_QK));
+#pragma unroll
+    for (int q = 0; q < kHotMaxT; ++q) {
+        const int t = wave + q * NW;
+        if (t >= T1) break;
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= t) ++I;
+        const int J = t - I * (I + 1) / 2;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * I + 4 * (lane >> 4) + v, c = 16 * J + (lane & 15);
+            if (r < C && c < C && (isA ? c < r : c <= r)) M[int64_t(r) * C + c] += acc[q][v];
+        }
+    }
 }
 
 constexpr int kFusedBlock = 1024;
@@ -902,8 +998,11 @@ size_t gram_lds_bytes(int) { return 0; }   // the cold Gram uses static LDS only
 
 
 hipError_t phase1_prepare() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_fused_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, int(fused_smem_bytes(kMaxChunk)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_fused_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(fused_smem_bytes(kMaxChunk)));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_gram_hot_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(hot_lds_bytes(kMaxChunk)));
 }
 
 hipError_t launch_phase1_part(const Problem &pb, const Slab &sl, int lognp, hipStream_t st);
@@ -936,10 +1035,7 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
     if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_gram_cold_kernel, dim3(nch, 2), dim3(kColdBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
-    // tiles of A and QK split over enough workgroups per chunk to fill the device
-    const int nt = (pb.C + 15) / 16, tiles = nt * (nt + 1);
-    const unsigned gy = unsigned(min(8, max(1, tiles / (2 * (kHotBlock / kWave)))));
-    hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch, gy), dim3(kHotBlock), 0, st, pb, sl);
+    hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch, 2), dim3(kHotLdsBlock), hot_lds_bytes(pb.C), st, pb, sl);
     return hipGetLastError();
 }
 

@@ -72,18 +72,11 @@ size_t part_smem_bytes() { return sizeof(PartSmem); }
 
 constexpr int kPartBatch = 8;   // global loads in flight per thread in the streaming loops
 
-// Slot id of the chunk's combined entry x (token-major: a token's W writes, then its R
-// reads); past ne, the chunk's first write id (an in-bounds load whose value is unused).
-__device__ __forceinline__ int32_t entry_id(const Problem &pb, int64_t tok0, int WR, int32_t ne, int32_t x) {
-    const int32_t xx = x < ne ? x : 0;
-    const int t = xx / WR, o = xx - t * WR;
-    const bool w = o < pb.W;
-    return load_id(w ? pb.k_idx : pb.q_idx, w ? (tok0 + t) * pb.W + o : (tok0 + t) * pb.R + (o - pb.W),
-                   w ? pb.k_id8 : pb.q_id8);
-}
-
-// dst[i] = id i of base + off, i < n (int32 or int64 ids), kPartBatch loads in flight per thread.
-__device__ __forceinline__ void copy_ids(const void *base, int32_t id8, int64_t off, int32_t n, uint32_t *dst) {
+// dst[i] = id i of base + off, i < n (int32 or int64 ids), kPartBatch loads in flight per
+// thread; each id also counted in its partition, pcnt[id & pmask] (the LDS atomics are
+// unconditional, adding 0 past n: a branch would make each of them wait for every load).
+__device__ __forceinline__ void copy_count_ids(const void *base, int32_t id8, int64_t off, int32_t n, uint32_t *dst,
+                                               int32_t *pcnt, uint32_t pmask) {
     const int tid = threadIdx.x;
     for (int32_t x0 = 0; x0 < n; x0 += kPartBlock * kPartBatch) {
         int32_t v[kPartBatch];
@@ -96,6 +89,7 @@ __device__ __forceinline__ void copy_ids(const void *base, int32_t id8, int64_t 
         for (int u = 0; u < kPartBatch; ++u) {
             const int32_t x = x0 + u * kPartBlock + tid;
             if (x < n) dst[x] = uint32_t(v[u]);
+            atomicAdd(&pcnt[uint32_t(v[u]) & pmask], x < n ? 1 : 0);
         }
     }
 }
@@ -216,25 +210,22 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
     const int p = int(n / sl.steps), ti = sl.ti0 + int(n % sl.steps);
     const int nl = n_live_tokens(pb, p, ti);
     const int W = pb.W, R = pb.R, C = pb.C, WR = W + R;
-    const int32_t El = nl * W, Fl = nl * R, NE = nl * WR;
+    const int32_t El = nl * W, Fl = nl * R;
     const int64_t tok0 = int64_t(p) * pb.T + int64_t(ti) * C;
     const int tid = threadIdx.x;
     const int NP = 1 << pa.lognp;
     const uint32_t pmask = uint32_t(NP - 1);
     int32_t *meta = reinterpret_cast<int32_t *>(cb + L.off_meta);
 
-    // ---- count the entries of each partition; a partition past the LDS leaves the chunk
-    //      to the sorting path
+    // ---- count the entries of each partition while copying the ids in entry order (Phase 2
+    //      reads them); a partition past the LDS leaves the chunk to the sorting path (which
+    //      writes the same copies again)
+    uint32_t *kid = cb + L.off_kid;
+    uint32_t *qid = cb + L.off_qid;
     for (int d = tid; d < NP; d += kPartBlock) s.pcnt[d] = 0;
     __syncthreads();
-    for (int32_t x0 = 0; x0 < NE; x0 += kPartBlock * kPartBatch) {
-        int32_t ids[kPartBatch];
-#pragma unroll
-        for (int u = 0; u < kPartBatch; ++u) ids[u] = entry_id(pb, tok0, WR, NE, x0 + u * kPartBlock + tid);
-#pragma unroll
-        for (int u = 0; u < kPartBatch; ++u)
-            if (x0 + u * kPartBlock + tid < NE) atomicAdd(&s.pcnt[uint32_t(ids[u]) & pmask], 1);
-    }
+    copy_count_ids(pb.k_idx, pb.k_id8, tok0 * W, El, kid, s.pcnt, pmask);
+    copy_count_ids(pb.q_idx, pb.q_id8, tok0 * R, Fl, qid, s.pcnt, pmask);
     __syncthreads();
     if (tid == 0) {
         int32_t o = 0, fb = 0;
@@ -254,17 +245,12 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
     if (s.fallback) return;
     for (int x = 8 + tid; x < 64; x += kPartBlock) meta[x] = 0;   // Phase-2 team barrier counters
 
-    // ---- chunk prologue: beta, the ids in entry order (Phase 2 reads them), padding
-    //      weights and records
+    // ---- chunk prologue: beta, padding weights and records
     float *beta_c = reinterpret_cast<float *>(cb + L.off_beta);
-    uint32_t *kid = cb + L.off_kid;
-    uint32_t *qid = cb + L.off_qid;
     float *gw = reinterpret_cast<float *>(cb + L.off_gw);
     float *gr = reinterpret_cast<float *>(cb + L.off_gr);
     int4 *rcr = reinterpret_cast<int4 *>(cb + L.off_rcr);
     for (int i = tid; i < C; i += kPartBlock) beta_c[i] = i < nl ? pb.beta[tok0 + i] : 0.0f;
-    copy_ids(pb.k_idx, pb.k_id8, tok0 * W, El, kid);
-    copy_ids(pb.q_idx, pb.q_id8, tok0 * R, Fl, qid);
     for (int64_t e = El + tid; e < L.E; e += kPartBlock) gw[e] = 0.0f;
     for (int64_t f = Fl + tid; f < L.F; f += kPartBlock) {
         gr[f] = 0.0f;

@@ -30,8 +30,8 @@ namespace sdm {
 // Limits (the host entry point checks them before any launch).
 constexpr int kTopkBlock = 256;
 constexpr int kTopkMaxK = 256;
-constexpr int kTopkMaxFactor = 4096;      // columns of a factor ranked by one sort in LDS
-constexpr int kTopkMaxWidth = 65535;      // columns per factor (wider ones ranked in pieces)
+constexpr int kTopkMaxFactor = 4096;      // columns of a factor ranked by one sort in LDS (wider
+                                          // factors, up to the host's limit of 65535, in pieces)
 constexpr int kTopkMaxFactors = 8;
 constexpr int kTopkPairs = 2048;          // >= sum over i < 256 of min(256, 256 / (i + 1)) = 1567
 
