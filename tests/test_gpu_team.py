@@ -109,3 +109,27 @@ def test_teams_only_replace_narrow_memory_mode_slices(gpu, monkeypatch):
     wl = workloads.CONFIGS["2"]
     p = plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, torch.bfloat16)
     assert p["phase2_team"] == 1 and p["phase2_mode"] != "memory", p
+
+
+def test_two_team_launches_at_once_give_their_own_bits(gpu, monkeypatch):
+    """Two calls planned with teams of 4 on two streams at once (2 x 256 workgroups for 256
+    CUs, so some teams are not all on CUs together; waiting workgroups claim the absent
+    members' pieces): each call gives the bits it gives alone."""
+    from chunked_sparse_delta_amd import plan, sdm_fwd
+    monkeypatch.setenv("SDM_P2_TEAM", "4")
+    wls = [small(P=16, T=1024, C=128, hd=128, M=20000, W=64, R=64, ragged=True, index=70 + i) for i in range(2)]
+    ts = [gu.to_torch(gu.generate(wl), gpu) for wl in wls]
+    assert plan(16, 1024, 128, 64, 64, 128, 20000, torch.float32)["phase2_team"] == 4
+    alone = [gu.run(t, wl.C) for t, wl in zip(ts, wls)]
+    banks = [t["bank"].clone() for t in ts]
+    outs = [None, None]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for i, (t, wl) in enumerate(zip(ts, wls)):
+        with torch.cuda.stream(streams[i]):
+            outs[i] = sdm_fwd(banks[i], t["k_idx"], t["k_val"], t["v"], t["beta"], t["log_decay"], t["q_idx"],
+                              t["q_val"], chunk=wl.C, valid_tokens=t["valid"], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert np.array_equal(gu.bits(outs[i]), gu.bits(alone[i][0])), i
+        assert np.array_equal(gu.bits(banks[i]), gu.bits(alone[i][1])), i
