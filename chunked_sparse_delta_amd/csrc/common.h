@@ -170,9 +170,12 @@ __device__ __forceinline__ int32_t n_live_tokens(const Problem &pb, int p, int t
 // with no branch on the dtype (a bfloat16 is the half of its aligned word at its address;
 // the word lies inside the element's 4-byte aligned page-internal span, so it is mapped).
 __device__ __forceinline__ float load_weight(const void *base, int64_t i, int32_t dtype) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(base) + uintptr_t(dtype ? 2 * i : 4 * i);
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(a & ~uintptr_t(3));
-    return dtype ? __uint_as_float((a & 2) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
+    // the address stays derived from base (a global load, not a flat one)
+    const char *b = static_cast<const char *>(base);
+    const int64_t off = dtype ? 2 * i : 4 * i;
+    const int mis = int((reinterpret_cast<uintptr_t>(b) + uintptr_t(off)) & 2);
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(b + (off - mis));
+    return dtype ? __uint_as_float(mis ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
 }
 
 // ---------------------------------------------------------------------------------------

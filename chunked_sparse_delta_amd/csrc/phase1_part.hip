@@ -274,13 +274,15 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
                 const bool ok = i < nt;
                 const int t = t0 + (ok ? i / WR : 0), o = ok ? i % WR : 0;
                 const bool w = o < W;
-                const int64_t xw = (tok0 + t) * W + (w ? o : 0), xr = (tok0 + t) * R + (w ? 0 : o - W);
-                const int32_t iw = load_id(pb.k_idx, xw, pb.k_id8), ir = load_id(pb.q_idx, xr, pb.q_id8);
-                const float kw = load_weight(pb.k_val, xw, pb.dtype), qr = load_weight(pb.q_val, xr, pb.dtype);
+                // one load per value from a selected address (no branch: the loads of all
+                // items issue back to back)
+                const int64_t x = w ? (tok0 + t) * W + o : (tok0 + t) * R + (o - W);
+                const int32_t id = load_id(w ? pb.k_idx : pb.q_idx, x, w ? pb.k_id8 : pb.q_id8);
+                const float kq = load_weight(w ? pb.k_val : pb.q_val, x, pb.dtype);
                 const float gv = pb.g[(tok0 + t) * pb.G + (pb.G == 1 ? 0 : (w ? o : 0))];
-                sid[u] = uint32_t(w ? iw : ir);
+                sid[u] = uint32_t(id);
                 c[u] = w ? uint32_t(t << 8 | o) : 0x80000000u | uint32_t(t << 8 | (o - W));
-                a[u] = __float_as_uint(w ? kw : qr);
+                a[u] = __float_as_uint(kq);
                 b[u] = w ? __float_as_uint(gv) : 0u;
             }
 #pragma unroll
