@@ -201,7 +201,7 @@ struct PartArgs {
     int32_t sort_bits;  // slot bits above the partition bits
 };
 
-__global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl, PartArgs pa) {
+__global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab sl, PartArgs pa) {
     extern __shared__ __align__(16) char part_lds[];
     PartSmem &s = *reinterpret_cast<PartSmem *>(part_lds);
     const int64_t n = blockIdx.x;
@@ -337,17 +337,26 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
     const int HC = int(L.HCAP);
     const int lane = tid & 63, wv = tid >> 6;
     int32_t nrep = 0;
-    for (int pp = 0; pp < NP; ++pp) {
-        const int nn = s.pcnt[pp];
-        if (nn == 0) continue;
-        {
-            int4 rr[kPartIpt];
-            const int32_t base = s.poff[pp];
+    // each partition's list is loaded into registers while the partition before it is
+    // processed (its records go back to its own list slots, never the next one's)
+    auto next_part = [&](int q) {
+        while (q < NP && s.pcnt[q] == 0) ++q;
+        return q;
+    };
+    auto load_list = [&](int q, int4 (&dst)[kPartIpt]) {
+        const int32_t base = s.poff[q], nq = s.pcnt[q];
 #pragma unroll
-            for (int u = 0; u < kPartIpt; ++u) {
-                const int32_t i = u * kPartBlock + tid;
-                rr[u] = plist[base + (i < nn ? i : 0)];
-            }
+        for (int u = 0; u < kPartIpt; ++u) {
+            const int32_t i = u * kPartBlock + tid;
+            dst[u] = plist[base + (i < nq ? i : 0)];
+        }
+    };
+    int4 rr[kPartIpt];
+    int pnext = next_part(0);
+    if (pnext < NP) load_list(pnext, rr);
+    for (int pp = pnext; pp < NP; pp = pnext) {
+        const int nn = s.pcnt[pp];
+        {
 #pragma unroll
             for (int u = 0; u < kPartIpt; ++u) {
                 const int32_t i = u * kPartBlock + tid;
@@ -361,6 +370,8 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
             }
         }
         __syncthreads();
+        pnext = next_part(pp + 1);
+        if (pnext < NP) load_list(pnext, rr);
         // stable LSD radix sort by the slot bits above the partition bits
         int cur = 0;
         {
@@ -643,18 +654,21 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
         float *hrow = reinterpret_cast<float *>(s.slot);   // [3][TE][HP] dense rows of the tile (LDS)
         const int TE = max(1, min(nl, int(sizeof(s.slot) * 4 / (3 * sizeof(float) * (HP ? HP : 1)))));
         const int TE2 = min(TE, TT);
-        for (int t0 = 0; t0 < nl; t0 += TE2) {
-            const int ntok = min(TE2, nl - t0);
-            const int nt = ntok * WR;
-            const int32_t xb = t0 * WR;
-            for (int x = tid; x < 3 * ntok * HP; x += kPartBlock) hrow[x] = 0.0f;
-            __syncthreads();
-            int32_t sl_[kPartIpt];
+        // each tile's list slots are loaded during the tile before it, so that a tile waits
+        // for one round trip (its records) instead of two
+        auto load_slots = [&](int t0_, int32_t (&dst)[kPartIpt]) {
+            const int nt_ = min(TE2, nl - t0_) * WR;
 #pragma unroll
             for (int u = 0; u < kPartIpt; ++u) {
                 const int32_t i = u * kPartBlock + tid;
-                sl_[u] = inv[xb + (i < nt ? i : 0)];
+                dst[u] = inv[t0_ * WR + (i < nt_ ? i : 0)];
             }
+        };
+        int32_t sl_[kPartIpt];
+        if (nl > 0) load_slots(0, sl_);
+        for (int t0 = 0; t0 < nl; t0 += TE2) {
+            const int ntok = min(TE2, nl - t0);
+            const int nt = ntok * WR;
             int4 rec[kPartIpt];
             uint32_t ovv[kPartIpt];
 #pragma unroll
@@ -662,6 +676,9 @@ __global__ __launch_bounds__(kPartBlock) void p1_part_kernel(Problem pb, Slab sl
                 rec[u] = plist[sl_[u]];
                 ovv[u] = oval[sl_[u]];
             }
+            if (t0 + TE2 < nl) load_slots(t0 + TE2, sl_);
+            for (int x = tid; x < 3 * ntok * HP; x += kPartBlock) hrow[x] = 0.0f;
+            __syncthreads();
 #pragma unroll
             for (int u = 0; u < kPartIpt; ++u) {
                 const int32_t i = u * kPartBlock + tid;
