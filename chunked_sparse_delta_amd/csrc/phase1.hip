@@ -791,6 +791,17 @@ __global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Sl
 // flight during this block's products), and each wavefront accumulates its tiles over every
 // column block in registers with the MFMA chains of hot_tiles (16 columns at a time, lane
 // group l / 16 taking columns 4 (l / 16) .. + 3, h ascending): the same bits.
+// Chunks of fewer than kHotLdsMinC tokens have too few tiles for a workgroup per matrix:
+// there each wavefront takes tiles straight from memory (hot_tiles), kHotBlock threads per
+// workgroup, the tiles of a chunk split over up to eight workgroups. Both give the same bits.
+constexpr int kHotBlock = 256;
+constexpr int kHotLdsMinC = 128;
+
+__global__ __launch_bounds__(kHotBlock) void p1_gram_hot_tiles_kernel(Problem pb, Slab sl) {
+    constexpr int NWAVE = kHotBlock / kWave;
+    hot_tiles(pb, sl, blockIdx.x, blockIdx.y * NWAVE + (threadIdx.x >> 6), gridDim.y * NWAVE);
+}
+
 constexpr int kHotLdsBlock = 1024;
 constexpr int kHotKb = 32;                 // hot columns per staged block
 constexpr int kHotPitch = kHotKb + 4;      // LDS row pitch (floats): 16-byte rows 4 banks apart
@@ -1035,7 +1046,17 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
     if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
     hipLaunchKernelGGL(p1_gram_cold_kernel, dim3(nch, 2), dim3(kColdBlock), 0, st, pb, sl);
     if (ev && (e = hipEventRecord(ev[4], st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch, 2), dim3(kHotLdsBlock), hot_lds_bytes(pb.C), st, pb, sl);
+    // SDM_P1_HOT_LDS=1 / 0 takes the staged / the per-tile kernel whatever the chunk (tests)
+    const char *hot_env = getenv("SDM_P1_HOT_LDS");
+    const bool hot_lds = hot_env ? hot_env[0] == '1' : pb.C >= kHotLdsMinC;
+    if (hot_lds) {
+        hipLaunchKernelGGL(p1_gram_hot_kernel, dim3(nch, 2), dim3(kHotLdsBlock), hot_lds_bytes(pb.C), st, pb, sl);
+    } else {
+        // tiles of A and QK split over enough workgroups per chunk to fill the device
+        const int nt = (pb.C + 15) / 16, tiles = nt * (nt + 1);
+        const unsigned gy = unsigned(min(8, max(1, tiles / (2 * (kHotBlock / kWave)))));
+        hipLaunchKernelGGL(p1_gram_hot_tiles_kernel, dim3(nch, gy), dim3(kHotBlock), 0, st, pb, sl);
+    }
     return hipGetLastError();
 }
 

@@ -656,3 +656,23 @@ def test_phase2_cu_budget_does_not_change_bits(gpu, wl):
     with pytest.raises(SdmError, match="phase2_cus"):
         sdm_fwd_phase2(t["bank"].clone(), *args, workspace=ws, out=torch.empty_like(o_ref), chunk=wl.C,
                        valid_tokens=t["valid"], phase2_cus=-1)
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=2, T=256, C=128, hd=8, M=40, W=24, R=24, ids="zipf", ragged=True, index=80),
+    small(P=2, T=130, C=64, hd=8, M=12, W=6, R=5, index=81),
+], ids=["C128_zipf", "C64_allhot"])
+def test_hot_gram_kernels_give_the_same_bits(gpu, wl, monkeypatch):
+    """The hot Gram staged in LDS (one workgroup per chunk and matrix) and the per-tile kernel
+    (operands from memory) run the same MFMA chains: identical A and QK."""
+    from chunked_sparse_delta_amd import chunk_mats
+    monkeypatch.setenv("SDM_P1_FUSED", "0")
+    t = gu.to_torch(gu.generate(wl), gpu)
+    res = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("SDM_P1_HOT_LDS", mode)
+        r = chunk_mats(t["k_idx"], t["k_val"], t["beta"], t["log_decay"], t["q_idx"], t["q_val"], rows=wl.M,
+                       head_dim=wl.hd, chunk=wl.C, valid_tokens=t["valid"])
+        res[mode] = {k: gu.bits(v) for k, v in r.items()}
+    for k in res["1"]:
+        assert np.array_equal(res["1"][k], res["0"][k]), k
