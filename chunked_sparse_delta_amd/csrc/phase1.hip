@@ -736,12 +736,20 @@ __device__ __forceinline__ void hot_tiles(const Problem &pb, const Slab &sl, int
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
         }
-        // Add the hot part to the cold part, inside the triangles only.
+        // Add the hot part to the cold part, inside the triangles only (the four cold values
+        // loaded before any sum is stored).
         float *M = isA ? A : QK;
+        float cold[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * I + 4 * (lane >> 4) + v, c = 16 * J + (lane & 15);
-            if (r < C && c < C && (isA ? c < r : c <= r)) M[int64_t(r) * C + c] += acc[v];
+            const bool in = r < C && c < C && (isA ? c < r : c <= r);
+            cold[v] = M[in ? int64_t(r) * C + c : 0];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * I + 4 * (lane >> 4) + v, c = 16 * J + (lane & 15);
+            if (r < C && c < C && (isA ? c < r : c <= r)) M[int64_t(r) * C + c] = cold[v] + acc[v];
         }
     }
 }
@@ -881,21 +889,31 @@ __global__ __launch_bounds__(kHotLdsBlock) void p1_gram_hot_kernel(Problem pb, S
             }
         }
     }
-    // Add the hot part to the cold part, inside the triangle only.
+    // Add the hot part to the cold part, inside the triangle only: every element's cold
+    // value is loaded before any sum is stored (the compiler cannot tell that the elements
+    // differ, and would otherwise wait for each load in turn)
     float *M = reinterpret_cast<float *>(cb + (isA ? L.off_A : L.off_QK));
+    int32_t at_[kHotMaxT][4];
+    float cold[kHotMaxT][4];
 #pragma unroll
     for (int q = 0; q < kHotMaxT; ++q) {
         const int t = wave + q * NW;
-        if (t >= T1) break;
         int I = 0;
         while ((I + 1) * (I + 2) / 2 <= t) ++I;
         const int J = t - I * (I + 1) / 2;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * I + 4 * (lane >> 4) + v, c = 16 * J + (lane & 15);
-            if (r < C && c < C && (isA ? c < r : c <= r)) M[int64_t(r) * C + c] += acc[q][v];
+            const bool in = t < T1 && r < C && c < C && (isA ? c < r : c <= r);
+            at_[q][v] = in ? r * C + c : -1;
+            cold[q][v] = M[in ? r * C + c : 0];
         }
     }
+#pragma unroll
+    for (int q = 0; q < kHotMaxT; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (at_[q][v] >= 0) M[at_[q][v]] = cold[q][v] + acc[q][v];
 }
 
 constexpr int kFusedBlock = 1024;
