@@ -23,7 +23,6 @@ hipError_t launch_phase1(const Problem &pb, const Slab &sl, hipStream_t st, hipE
                          const WyArgs &wa, int lognp);
 bool phase1_fused(const ChunkLayout &L, int C, int lds_limit);
 hipError_t part_prepare();
-size_t part_smem_bytes();
 int part_lognp(int64_t E, int64_t F, int key_bits);
 hipError_t launch_wy(const float *A, const float *beta, const float *QK, float *X, float *QX, int C, int64_t n,
                      int64_t stride, int64_t bstride, hipStream_t st);
@@ -146,7 +145,7 @@ int plan_part(Problem &pb, const ChunkLayout &L, bool fused) {
     if (env && env[0] == '0') return -1;
     int lg = part_lognp(L.E, L.F, pb.key_bits);
     const char *ov = getenv("SDM_P1_NP_LOG");
-    if (ov && ov[0] >= '0' && ov[0] <= '6') lg = ov[0] - '0';
+    if (ov && ov[0] >= '0' && ov[0] <= '7') lg = ov[0] - '0';
     pb.part_on = 1;
     return lg;
 }

@@ -35,15 +35,35 @@
 
 namespace sdm {
 
-constexpr int kPartBlock = 512;                     // two workgroups per CU hide each other's stalls
-constexpr int kPartNW = kPartBlock / kWave;
-constexpr int kPartCap = 3072;                      // entries of one partition held in LDS
-constexpr int kPartIpt = (kPartCap + kPartBlock - 1) / kPartBlock;   // positions per thread
-constexpr int kPartMaxLogNP = 6;                    // at most 64 partitions
+// Two sizes of the kernel: chunks of at least kPartBigEntries entries take 512-thread
+// workgroups holding partitions of up to 3072 entries (at most 64 partitions, two workgroups
+// per CU); smaller chunks take 256-thread workgroups with half of that LDS (up to 128
+// partitions of 1536 entries, four workgroups per CU), whose barrier stalls overlap more.
+// The configuration, like the partition count, is a function of the shapes only.
+template <int BLOCK, int CAP, int MAXLOGNP>
+struct PartCfg {
+    static constexpr int kBlock = BLOCK;
+    static constexpr int kNW = BLOCK / kWave;
+    static constexpr int kCap = CAP;                          // entries of one partition held in LDS
+    static constexpr int kIpt = (CAP + BLOCK - 1) / BLOCK;    // positions per thread
+    static constexpr int kMaxLogNP = MAXLOGNP;
+    static constexpr int kCand = CAP / kHotMin + 1;           // big groups of one partition, at most
+};
+using PartBig = PartCfg<512, 3072, 6>;
+using PartSmall = PartCfg<256, 1536, 7>;
+constexpr int64_t kPartBigEntries = 65536;
 constexpr int kPartDigit = 7;                       // radix digit bits
-constexpr int kPartCand = kPartCap / kHotMin + 1;   // big groups of one partition, at most
 
+// The constants of configuration Cfg under their short names, in a kernel or helper body.
+#define PART_CFG_NAMES(Cfg)                                                                   \
+    constexpr int kPartBlock = Cfg::kBlock, kPartNW = Cfg::kNW, kPartCap = Cfg::kCap,        \
+                  kPartIpt = Cfg::kIpt, kPartMaxLogNP = Cfg::kMaxLogNP, kPartCand = Cfg::kCand; \
+    (void)kPartBlock; (void)kPartNW; (void)kPartCap; (void)kPartIpt; (void)kPartMaxLogNP; (void)kPartCand
+
+template <class Cfg>
 struct PartSmem {
+    static constexpr int kPartCap = Cfg::kCap, kPartNW = Cfg::kNW, kPartMaxLogNP = Cfg::kMaxLogNP,
+                         kPartCand = Cfg::kCand;
     uint32_t slot[kPartCap];
     uint32_t code[kPartCap];     // read << 31 | group id << 16 (writes, once known) | token << 8 | entry in token
     uint32_t v1[kPartCap];       // bits of k (write) or q (read), float32
@@ -68,15 +88,15 @@ struct PartSmem {
     int32_t nrep, fallback;
 };
 
-size_t part_smem_bytes() { return sizeof(PartSmem); }
-
 constexpr int kPartBatch = 8;   // global loads in flight per thread in the streaming loops
 
 // dst[i] = id i of base + off, i < n (int32 or int64 ids), kPartBatch loads in flight per
 // thread; each id also counted in its partition, pcnt[id & pmask] (the LDS atomics are
 // unconditional, adding 0 past n: a branch would make each of them wait for every load).
+template <class Cfg>
 __device__ __forceinline__ void copy_count_ids(const void *base, int32_t id8, int64_t off, int32_t n, uint32_t *dst,
                                                int32_t *pcnt, uint32_t pmask) {
+    PART_CFG_NAMES(Cfg);
     const int tid = threadIdx.x;
     for (int32_t x0 = 0; x0 < n; x0 += kPartBlock * kPartBatch) {
         int32_t v[kPartBatch];
@@ -99,8 +119,9 @@ __device__ __forceinline__ void copy_count_ids(const void *base, int32_t id8, in
 // owns a contiguous segment of the items; per (wave, digit) counts, turned into first
 // positions (digits ascending, waves in order), ranks within a wavefront by ballot match.
 // Also fills s.dstart[d] (first position of digit d). Ends with a barrier.
-template <typename DigitF, typename EmitF>
-__device__ __forceinline__ void part_scatter(PartSmem &s, int n, int db, DigitF digit, EmitF emit) {
+template <class Cfg, typename DigitF, typename EmitF>
+__device__ __forceinline__ void part_scatter(PartSmem<Cfg> &s, int n, int db, DigitF digit, EmitF emit) {
+    PART_CFG_NAMES(Cfg);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nd = 1 << db;
     const uint64_t lt = lanemask_lt(lane);
@@ -157,7 +178,9 @@ __device__ __forceinline__ void part_scatter(PartSmem &s, int n, int db, DigitF 
 
 // Inclusive block scan of one int per thread (thread order); *total gets the sum.
 // Two barriers; wi is one of the s.wi rows.
+template <class Cfg>
 __device__ __forceinline__ int32_t part_scan_int(int32_t x, int32_t *wi, int32_t *total) {
+    PART_CFG_NAMES(Cfg);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int32_t incl = x;
 #pragma unroll
@@ -201,9 +224,11 @@ struct PartArgs {
     int32_t sort_bits;  // slot bits above the partition bits
 };
 
-__global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab sl, PartArgs pa) {
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Slab sl, PartArgs pa) {
+    PART_CFG_NAMES(Cfg);
     extern __shared__ __align__(16) char part_lds[];
-    PartSmem &s = *reinterpret_cast<PartSmem *>(part_lds);
+    PartSmem<Cfg> &s = *reinterpret_cast<PartSmem<Cfg> *>(part_lds);
     const int64_t n = blockIdx.x;
     const ChunkLayout &L = sl.lay;
     uint32_t *cb = sl.chunk(n);
@@ -224,8 +249,8 @@ __global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab
     uint32_t *qid = cb + L.off_qid;
     for (int d = tid; d < NP; d += kPartBlock) s.pcnt[d] = 0;
     __syncthreads();
-    copy_count_ids(pb.k_idx, pb.k_id8, tok0 * W, El, kid, s.pcnt, pmask);
-    copy_count_ids(pb.q_idx, pb.q_id8, tok0 * R, Fl, qid, s.pcnt, pmask);
+    copy_count_ids<Cfg>(pb.k_idx, pb.k_id8, tok0 * W, El, kid, s.pcnt, pmask);
+    copy_count_ids<Cfg>(pb.q_idx, pb.q_id8, tok0 * R, Fl, qid, s.pcnt, pmask);
     __syncthreads();
     if (tid == 0) {
         int32_t o = 0, fb = 0;
@@ -495,7 +520,7 @@ __global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab
             nhd += r == 0 || s.slot[ord[wpos[r]]] != s.slot[ord[wpos[r - 1]]];
         }
         int32_t ngt = 0;
-        int32_t gcur = part_scan_int(nhd, s.wi[0], &ngt) - nhd;   // groups before this thread's ranks
+        int32_t gcur = part_scan_int<Cfg>(nhd, s.wi[0], &ngt) - nhd;   // groups before this thread's ranks
         for (int u = 0; u < ipw; ++u) {
             const int r = r0 + u;
             if (r >= nw) break;
@@ -524,7 +549,7 @@ __global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab
             ncl += s.gpos[g + 1] - s.gpos[g] >= kHotMin;
         }
         int32_t nct = 0;
-        int32_t ccur = part_scan_int(ncl, s.wi[1], &nct) - ncl;
+        int32_t ccur = part_scan_int<Cfg>(ncl, s.wi[1], &nct) - ncl;
         for (int u = 0; u < ipg; ++u) {
             const int g = g0 + u;
             if (g >= ng) break;
@@ -563,7 +588,7 @@ __global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab
         {
             const bool h = tid < nc && s.cand_ok[tid];
             int32_t nht = 0;
-            const int32_t rk = part_scan_int(h ? 1 : 0, s.wi[2], &nht) - (h ? 1 : 0);
+            const int32_t rk = part_scan_int<Cfg>(h ? 1 : 0, s.wi[2], &nht) - (h ? 1 : 0);
             if (h && s.ho + rk < HC) s.hotr[s.gpos[s.cand[tid]]] = int16_t(s.ho + rk);   // past the cap: cold
             if (tid == 0) s.nh = nht;
         }
@@ -737,23 +762,39 @@ __global__ __launch_bounds__(kPartBlock, 4) void p1_part_kernel(Problem pb, Slab
 }
 
 hipError_t part_prepare() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_part_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(PartSmem)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_part_kernel<PartBig>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(PartSmem<PartBig>)));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&p1_part_kernel<PartSmall>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(PartSmem<PartSmall>)));
 }
 
 // log2 of the partition count for chunks of E write and F read entries: the smallest that
-// leaves about two thirds of kPartCap per partition on average, at most 64 partitions, and
-// no more partitions than slot values (key_bits).
-int part_lognp(int64_t E, int64_t F, int key_bits) {
+// leaves about two thirds of the configuration's partition capacity per partition on average,
+// at most its partition limit, and no more partitions than slot values (key_bits).
+template <class Cfg>
+static int part_lognp_cfg(int64_t E, int64_t F, int key_bits) {
     int lg = 0;
-    while (lg < kPartMaxLogNP && lg < key_bits && (E + F) > (int64_t(kPartCap) * 2 / 3) << lg) ++lg;
+    while (lg < Cfg::kMaxLogNP && lg < key_bits && (E + F) > (int64_t(Cfg::kCap) * 2 / 3) << lg) ++lg;
     return lg;
+}
+
+int part_lognp(int64_t E, int64_t F, int key_bits) {
+    return E + F >= kPartBigEntries ? part_lognp_cfg<PartBig>(E, F, key_bits) : part_lognp_cfg<PartSmall>(E, F, key_bits);
 }
 
 hipError_t launch_phase1_part(const Problem &pb, const Slab &sl, int lognp, hipStream_t st) {
     PartArgs pa{lognp, pb.key_bits > lognp ? pb.key_bits - lognp : 0};
     const unsigned nch = unsigned(int64_t(pb.P) * sl.steps);
-    hipLaunchKernelGGL(p1_part_kernel, dim3(nch), dim3(kPartBlock), sizeof(PartSmem), st, pb, sl, pa);
+    if (sl.lay.E + sl.lay.F >= kPartBigEntries) {
+        if (lognp > PartBig::kMaxLogNP) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(p1_part_kernel<PartBig>, dim3(nch), dim3(PartBig::kBlock), sizeof(PartSmem<PartBig>), st,
+                           pb, sl, pa);
+    } else {
+        if (lognp > PartSmall::kMaxLogNP) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(p1_part_kernel<PartSmall>, dim3(nch), dim3(PartSmall::kBlock), sizeof(PartSmem<PartSmall>),
+                           st, pb, sl, pa);
+    }
     return hipGetLastError();
 }
 
