@@ -350,23 +350,39 @@ __device__ __forceinline__ void load_aop(const float *p, int pitch, bool ok, flo
 // vector p of the slice; the eight classes combine as in the gather, and the decay term
 // comes first: B[s] = exp(L_last) B[s] + ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)). The member
 // records (at most 256) are loaded once, four per lane, and broadcast by lane shuffles.
+// big_issue loads a group's row and member records; big_finish sums and stores them, so
+// that the next group's loads can be in flight while this one is summed.
 template <typename T, int V>
-__device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, const int2 *mrec, const float *dl,
-                                             int pitch, int col0, int nvs, int lane) {
-    const int r = lane >> 3, p = lane & 7;
+struct BigLoads {
+    typename Vec<T, V>::raw_t raw;
+    int32_t rt[4], rc[4];
+};
+
+template <typename T, int V>
+__device__ __forceinline__ void big_issue(const T *bank, int hd, const int4 &rec, const int2 *mrec, int col0, int nvs,
+                                          int lane, BigLoads<T, V> &L) {
+    const int p = lane & 7;
     const bool pok = p < nvs;
     const int32_t m0 = rec.y & 0xFFFF, n = ((rec.y >> 16) & 0xFF) + 1;
     const uint32_t col = uint32_t(col0 + p * V);
     // loads unconditional (in-bounds fallbacks), as in the gather
-    const typename Vec<T, V>::raw_t raw = Vec<T, V>::load_raw(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
-    int32_t rt[4], rc[4];
+    L.raw = Vec<T, V>::load_raw(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int m = lane + 64 * q;
         const int2 x = *at(mrec, uint32_t(m0 + (m < n ? m : 0)));
-        rt[q] = m < n ? x.x : 0;
-        rc[q] = m < n ? x.y : 0;
+        L.rt[q] = m < n ? x.x : 0;
+        L.rc[q] = m < n ? x.y : 0;
     }
+}
+
+template <typename T, int V>
+__device__ __forceinline__ void big_finish(T *bank, int hd, const int4 &rec, const BigLoads<T, V> &L, const float *dl,
+                                           int pitch, int col0, int nvs, int lane) {
+    const int r = lane >> 3, p = lane & 7;
+    const bool pok = p < nvs;
+    const int32_t n = ((rec.y >> 16) & 0xFF) + 1;
+    const uint32_t col = uint32_t(col0 + p * V);
     float acc[V];
 #pragma unroll
     for (int c = 0; c < V; ++c) acc[c] = 0.0f;
@@ -377,8 +393,8 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             const int src = r + 8 * jj;
-            const int32_t t = __shfl(rt[q], src, 64);
-            const float cw = __int_as_float(__shfl(rc[q], src, 64));
+            const int32_t t = __shfl(L.rt[q], src, 64);
+            const float cw = __int_as_float(__shfl(L.rc[q], src, 64));
             if (64 * q + src < n && pok) {
                 float dv[V];
                 lds_load_vec<V>(dl + t * pitch + p * V, dv);
@@ -395,7 +411,7 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
     for (int c = 0; c < V; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
     if (r == 0 && pok) {
         float b[V];
-        Vec<T, V>::unpack(raw, b);
+        Vec<T, V>::unpack(L.raw, b);
         const float dec = __int_as_float(rec.z);
 #pragma unroll
         for (int c = 0; c < V; ++c) b[c] = b[c] * dec + acc[c];
@@ -404,20 +420,36 @@ __device__ __forceinline__ void dw_big_group(T *bank, int hd, const int4 &rec, c
 }
 
 // DW of the groups grec[0, ng) and of the groups with >= kHotMin members brec[0, nbig): one
-// writer per written row. The many-member groups go to whole wavefronts (dw_big_group); the
-// others are summed in token order by the NV lanes of their slice: lane (gs, vq) of slot u
-// takes group gb + u * NW * GPI + gs of each batch, the first member rides in the group
-// record, the second loads with the bank row, the rest four at a time. kB groups per lane
-// are in flight; SM: the records are in LDS (the loads past the last batch are skipped).
+// writer per written row. The many-member groups go to whole wavefronts (big_issue /
+// big_finish: the records two groups ahead, the rows and member records one group ahead);
+// the others are summed in token order by the NV lanes of their slice: lane (gs, vq) of
+// slot u takes group gb + u * NW * GPI + gs of each batch, the first member rides in the
+// group record, the second loads with the bank row, and (records in memory) the next NV
+// with it too, one per lane of the group (broadcast by lane shuffles), so that most groups
+// need no load while they are summed; any further members come four at a time. kB groups
+// per lane are in flight; SM: the records are in LDS (the loads past the last batch are
+// skipped, and every member beyond the second is read from LDS where it is summed).
 template <typename T, int V, int NV, int NW, int kB, bool SM>
 __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, int32_t ng, const int4 *brec,
                                           int32_t nbig, const int2 *mrec, const float *db, int pitch, int nvs,
                                           int wave) {
     int dlane = threadIdx.x & 63;                        // opaque: nothing of the DW moves up
     asm volatile("" : "+v"(dlane));
-    for (int32_t bi = wave; bi < nbig; bi += NW) {
-        const int4 rec = *at(brec, uint32_t(bi));
-        dw_big_group<T, V>(bank, bst, rec, mrec, db, pitch, 0, nvs, dlane);
+    if (wave < nbig) {
+        // unconditional (clamped) loads: a big group past the end reloads the last one
+        auto brec_at = [&](int32_t bi) { return *at(brec, uint32_t(bi < nbig ? bi : nbig - 1)); };
+        int4 rc0 = brec_at(wave), rc1 = brec_at(wave + NW);
+        BigLoads<T, V> cur;
+        big_issue<T, V>(bank, bst, rc0, mrec, 0, nvs, dlane, cur);
+        for (int32_t bi = wave; bi < nbig; bi += NW) {
+            BigLoads<T, V> nxt;
+            big_issue<T, V>(bank, bst, rc1, mrec, 0, nvs, dlane, nxt);
+            const int4 rc2 = brec_at(bi + 2 * NW);
+            big_finish<T, V>(bank, bst, rc0, cur, db, pitch, 0, nvs, dlane);
+            cur = nxt;
+            rc0 = rc1;
+            rc1 = rc2;
+        }
     }
     constexpr int GPI = kWave / NV;                       // groups per load instruction
     constexpr int kStride = NW * GPI * kB;                 // groups per workgroup batch
@@ -439,6 +471,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
     for (int32_t gb = wave * GPI; gb < ng; gb += kStride) {
         typename Vec<T, V>::raw_t raw[kB];
         int2 mr[kB];
+        [[maybe_unused]] int2 mw[kB];   // records in memory: member 2 + vq of the group
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             const bool sm = small(rec[u]);
@@ -447,6 +480,10 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
             const bool two = sm && n1 > 0;
             const int2 x = *at(mrec, uint32_t(two ? m0 + 1 : 0));
             mr[u] = two ? x : make_int2(0, 0);
+            if constexpr (!SM) {
+                const bool inw = sm && n1 >= 2 + vq;
+                mw[u] = *at(mrec, uint32_t(inw ? m0 + 2 + vq : 0));
+            }
         }
         int4 nrec[kB];
         // records in LDS (staged): the loads past the last batch are skipped
@@ -459,10 +496,10 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            if (!small(rec[u])) continue;
-            const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF, t0 = (rec[u].y >> 24) & 0xFF;
+            const bool sm = small(rec[u]);
+            const int32_t m0 = rec[u].y & 0xFFFF, n1 = sm ? (rec[u].y >> 16) & 0xFF : 0, t0 = (rec[u].y >> 24) & 0xFF;
             float acc[V];
-            if (vok) {
+            if (vok && sm) {
                 Vec<T, V>::unpack(raw[u], acc);
             } else {
 #pragma unroll
@@ -471,7 +508,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
             const float dec = __int_as_float(rec[u].z);
 #pragma unroll
             for (int c = 0; c < V; ++c) acc[c] *= dec;
-            {
+            if (sm) {
                 const float cwv = __int_as_float(rec[u].w);
                 float dv[V];
                 lds_load_vec<V>(db + t0 * pitch + vq * V, dv);
@@ -485,8 +522,27 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
 #pragma unroll
                 for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
             }
-            // members 2.. (at most kHotMin - 2 of them), four records at a time
-            for (int32_t m = m0 + 2; m <= m0 + n1; m += 4) {
+            int32_t mfirst = m0 + 2;   // the first member still to be summed from the records
+            if constexpr (!SM) {
+                // members 2 .. NV + 1 from the window, lane gs * NV + j holding member 2 + j;
+                // the shuffles run with every lane active (wave-uniform trip count)
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    if (__ballot(n1 >= 2 + j) == 0) break;
+                    const int src = gs * NV + j;
+                    const int32_t t = __shfl(mw[u].x, src, 64);
+                    const float cwv = __int_as_float(__shfl(mw[u].y, src, 64));
+                    if (n1 >= 2 + j) {
+                        float dv[V];
+                        lds_load_vec<V>(db + t * pitch + vq * V, dv);
+#pragma unroll
+                        for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
+                    }
+                }
+                mfirst = m0 + 2 + NV;
+            }
+            // the members past those, four records at a time
+            for (int32_t m = mfirst; m <= m0 + n1; m += 4) {
                 int2 mb[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) mb[q] = *at(mrec, uint32_t(min(m + q, m0 + n1)));
@@ -500,7 +556,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
                     for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                 }
             }
-            if (vok) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
+            if (vok && sm) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
