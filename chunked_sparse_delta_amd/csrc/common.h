@@ -24,15 +24,20 @@ struct bf16 {
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x.bits) << 16); }
 
+// Two floats -> two bf16 (low half first), round to nearest even, a NaN quieted (its top
+// 16 bits with the quiet bit set): gfx950's packed conversion instruction, one per pair.
+// Its result equals the integer rule (u + 0x7FFF + ((u >> 16) & 1)) >> 16 for every
+// non-NaN input, denormals included, and (u >> 16) | 0x40 for every NaN.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // float -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ bf16 f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
     bf16 r;
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) {
-        r.bits = uint16_t((u >> 16) | 0x40u);
-    } else {
-        r.bits = uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-    }
+    r.bits = uint16_t(f32x2_to_bf16x2(f, 0.0f));
     return r;
 }
 
@@ -82,7 +87,7 @@ template <> struct Vec<bf16, 8> {
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w[i] = uint32_t(f32_to_bf16(o[2 * i]).bits) | (uint32_t(f32_to_bf16(o[2 * i + 1]).bits) << 16);
+            w[i] = f32x2_to_bf16x2(o[2 * i], o[2 * i + 1]);
         *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 };
@@ -98,8 +103,8 @@ template <> struct Vec<bf16, 4> {
     }
     static __device__ __forceinline__ void load(const bf16 *p, float (&o)[4]) { unpack(load_raw(p), o); }
     static __device__ __forceinline__ void store(bf16 *p, const float (&o)[4]) {
-        const uint32_t w0 = uint32_t(f32_to_bf16(o[0]).bits) | (uint32_t(f32_to_bf16(o[1]).bits) << 16);
-        const uint32_t w1 = uint32_t(f32_to_bf16(o[2]).bits) | (uint32_t(f32_to_bf16(o[3]).bits) << 16);
+        const uint32_t w0 = f32x2_to_bf16x2(o[0], o[1]);
+        const uint32_t w1 = f32x2_to_bf16x2(o[2], o[3]);
         *reinterpret_cast<uint2 *>(p) = make_uint2(w0, w1);
     }
 };

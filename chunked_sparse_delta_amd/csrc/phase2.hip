@@ -308,8 +308,8 @@ __device__ __forceinline__ void store_out4(T *p, const f32x4 &y, int n) {
     } else {
         if (n == 4) {
             uint2 w;
-            w.x = uint32_t(f32_to_bf16(y[0]).bits) | (uint32_t(f32_to_bf16(y[1]).bits) << 16);
-            w.y = uint32_t(f32_to_bf16(y[2]).bits) | (uint32_t(f32_to_bf16(y[3]).bits) << 16);
+            w.x = f32x2_to_bf16x2(y[0], y[1]);
+            w.y = f32x2_to_bf16x2(y[2], y[3]);
             *reinterpret_cast<uint2 *>(p) = w;
             return;
         }
