@@ -400,7 +400,11 @@ def test_workload_4_literal_properties(gpu):
     small(P=8, T=300, C=64, hd=64, M=200, W=8, R=8, dtype="bf16", ids="zipf", ragged=True, index=26),
     small(P=3, T=260, C=128, hd=32, M=300, W=16, R=16, ragged=True, index=27),
     small(P=2, T=100, C=48, hd=40, M=80, W=5, R=3, ids="zipf", index=28),
-], ids=["bf16_P8", "f32_P3", "f32_partial_slice"])
+    # 16 writes per token over 160 Zipf rows: write groups of every size, from one member to the
+    # whole chunk (the DW's member windows, its four-at-a-time loop and its whole-wavefront
+    # groups in every slice width)
+    small(P=8, T=256, C=64, hd=64, M=160, W=16, R=16, dtype="bf16", ids="zipf", ragged=True, index=31),
+], ids=["bf16_P8", "f32_P3", "f32_partial_slice", "bf16_groups_of_every_size"])
 def test_phase2_geometry_does_not_change_bits(gpu, wl, monkeypatch):
     """The column slicing, the LDS staging and the LDS-resident bank slice change only the schedule:
     every geometry gives the same bits (the gather, matmul and DW sums run in orders fixed by W, R
