@@ -12,17 +12,19 @@
 // Workgroups of one stream are placed on one XCD (blocks are dealt round-robin to the
 // 8 XCDs) so that its slices share one L2 for the chunk's ids, weights and matrices.
 //
-// Per step, with 8 wavefronts of up to 256 VGPRs each:
+// Per step, with 16 wavefronts of up to 128 VGPRs each:
 //   gather   a wavefront takes whole tokens; each load instruction fetches one slice of
-//            64 / NV rows (8 entry classes x 8 / NV tokens), 12 to 16 instructions in
+//            64 / NV rows (8 entry classes x 8 / NV tokens), several instructions in
 //            flight, the next batch's ids and weights loaded under the current batch's rows
 //   u        u = beta (v - retrieved) in LDS
 //   matmul   D^T = u^T QX^T and u^T X^T on v_mfma_f32_16x16x4f32: 16 x 16 output tiles
 //            (16 columns x 16 tokens), lower-triangular tiles only; readings (+ inter)
 //            go straight to memory, delta_v to LDS
-//   DW       64 / NV groups per load instruction, eight in flight per lane; the first
-//            member rides in the group record, the second comes with the bank row, the
-//            rest four at a time; the next batch's records load under the current one
+//   DW       64 / NV groups per load instruction, four in flight per lane; the first
+//            member rides in the group record, the second comes with the bank row (and,
+//            records in memory, the next NV too, one per lane of the group), the rest four
+//            at a time; the next batch's records load under the current one; groups of 16
+//            or more members by whole wavefronts, the next one's loads under this one's sums
 //
 // Determinism: each output element has exactly one writer, and every sum runs in an order
 // fixed by the shapes W, R and C only (never by the slicing or the launch):
