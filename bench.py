@@ -346,7 +346,7 @@ def bench_bwd(args):
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(inp: dict, wl, seconds: float, streams_total: int) -> dict:
+def cpu_baseline(inp: dict, wl, seconds: float, streams_total: int, twin: str = "") -> dict:
     import oracle
     f = oracle.as_f64_inputs(inp)
     threads = max(1, min(wl.P, os.cpu_count() or 1, 16))
@@ -361,8 +361,8 @@ def cpu_baseline(inp: dict, wl, seconds: float, streams_total: int) -> dict:
             break
     return {"value": reps * tokens / el, "unit": "tokens/s", "cores": threads, "host_cores": os.cpu_count(),
             "kind": "oracle",
-            "sample": f"{wl.P} of the workload's {streams_total} streams ({tokens} valid tokens) x {reps} passes "
-                      f"of the fp64 token loop, {threads} threads, {el:.1f} s"}
+            "sample": f"{wl.P} of the workload's {streams_total} streams{twin} ({tokens} valid tokens) x {reps} "
+                      f"passes of the fp64 token loop, {threads} threads, {el:.1f} s"}
 
 
 def main():
@@ -525,7 +525,8 @@ def main():
             keep = list(range(min(wl.P, host, 16)))
             # config 4 overflows as drawn; its finite twin 4p has the same shapes and cost
             sample = workloads.generate(workloads.CONFIGS["4p"] if wl.name == "4" else wl, streams=keep)
-        res["cpu_baseline"] = cpu_baseline(sample, wl.replace(P=len(sample["valid"])), args.cpu_seconds, wl.P)
+        twin = " (of its finite twin 4p: the same shapes and ids, weights / sqrt(W))" if wl.name == "4" else ""
+        res["cpu_baseline"] = cpu_baseline(sample, wl.replace(P=len(sample["valid"])), args.cpu_seconds, wl.P, twin)
     print(json.dumps(res), flush=True)
 
 
