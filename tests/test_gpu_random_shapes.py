@@ -1,5 +1,6 @@
 """Random small shapes (a fixed seed): the HIP path against the oracle, and the same bits
-under every Phase-2 slice width, mode cap and team size the plan override allows.
+under every Phase-2 slice width, mode cap and team size the plan override allows; and the
+backward against its oracle on random shapes, in both of its sweeps.
 
 Shapes are drawn within the documented limits (chunk 16-256 including sizes that are not
 multiples of 16, head widths 1-256, up to 256 write and read slots, 1-16 streams, ragged
@@ -77,3 +78,48 @@ def test_random_shapes(gpu, monkeypatch):
     _set(monkeypatch)
     print(f"{N_CASES} cases, {skipped} skipped (oracle beyond float32)", flush=True)
     assert skipped <= N_CASES // 4
+
+
+N_BWD_CASES = 30
+BWD_SEED = 20261204
+
+
+def _bwd_cases():
+    rng = np.random.default_rng(BWD_SEED)
+    out = []
+    for i in range(N_BWD_CASES):
+        hd = int(rng.choice([1, 3, 8, 16, 24, 40, 64, 72, 128, 200, 256, 512]))
+        M = int(rng.integers(1, 3000))
+        W = int(min(M, rng.choice([1, 2, 3, 5, 8, 16, 24, 32, 40, 64, 100, 128, 200, 256])))
+        R = int(min(M, rng.choice([1, 2, 4, 8, 16, 32, 48, 64, 128, 256])))
+        P = int(rng.choice([1, 2, 3, 4, 8]))
+        T = int(rng.integers(1, 300))
+        if P * T * (W + R) * hd > 1e8:   # keeps the backward oracle to a fraction of a second
+            T = max(1, int(1e8 / (P * (W + R) * hd)))
+        wl = workloads.small(
+            P=P, T=T, C=16, hd=hd, M=M, W=W, R=R, dtype=str(rng.choice(["f32", "bf16"])),
+            ids=str(rng.choice(["uniform", "zipf", "mixed"])), ragged=bool(rng.integers(0, 2)),
+            gate_width=int(rng.choice([0, 1])),
+            weight_scale=float(rng.choice([1.0, -1.0])) if W <= 8 else -1.0, index=4000 + i)
+        out.append((wl, bool(rng.integers(0, 2))))
+    return out
+
+
+def test_random_shapes_backward(gpu, monkeypatch):
+    """sdm_bwd against O3 at the backward's bar (1e-4 per gradient tensor, padding tokens
+    exactly 0), the bank restored bit for bit, with the default sweep and with rows in
+    memory; half of the cases repeat a read slot within a token."""
+    from tests.test_gpu_backward import _check, _run
+    for wl, dup in _bwd_cases():
+        tag = (f"P{wl.P} T{wl.T} hd{wl.hd} M{wl.M} W{wl.W} R{wl.R} {wl.dtype} {wl.ids} ragged={wl.ragged} "
+               f"G={'1' if wl.gate_width == 1 else 'W'} repeated reads={dup}")
+        for res in (None, "0"):
+            print(f"{tag} SDM_BWD_RES={res}", flush=True)
+            if res is None:
+                monkeypatch.delenv("SDM_BWD_RES", raising=False)
+            else:
+                monkeypatch.setenv("SDM_BWD_RES", res)
+            inp, gr, t, bank, got = _run(wl, gpu, dup_reads=dup)
+            _check(inp, gr, got)
+            assert np.array_equal(gu.bits(bank), gu.bits(t["bank"])), (tag, res, "bank not restored")
+    monkeypatch.delenv("SDM_BWD_RES", raising=False)
