@@ -108,3 +108,46 @@ def test_topk_backward_matches_oracle(gpu, dtype, factors, k):
     want = pk.product_key_topk_backward(lin.cpu().numpy(), gexact, factors, bf16=dtype == "bf16")
     assert graw.shape == (rows, sum(factors)) and graw.dtype == gt.dtype
     assert np.array_equal(_bits(graw), _oracle_val_bits(want, dtype))
+
+
+def test_random_factor_shapes(gpu, monkeypatch):
+    """30 random shapes (a fixed seed) within the documented limits: 1 to 8 factors of 1 to
+    65535 columns (product below 2^55), k from 1 to 256, 1 to 39 rows, both dtypes, normal,
+    tied and special values, either kernel; the forward and the sparse backward bit for bit."""
+    from chunked_sparse_delta_amd import product_key_topk, product_key_topk_backward
+    rng = np.random.default_rng(20261205)
+    for i in range(30):
+        F = int(rng.choice([1, 2, 2, 2, 3, 3, 4, 4, 5, 6, 8]))
+        while True:
+            f = tuple(max(1, min(65535, int(np.exp(rng.uniform(0, np.log(65535 if F <= 2 else 2000))))))
+                      for _ in range(F))
+            if np.prod([float(x) for x in f]) < 2.0 ** 55:
+                break
+        k = int(rng.choice([1, 2, 7, 16, 32, 64, 100, 200, 256]))
+        rows = int(rng.integers(1, 40))
+        rows = min(rows, max(1, int(4e5 / sum(f))))   # keeps the oracle to a second or so
+        dtype = str(rng.choice(["f32", "bf16"]))
+        kind = str(rng.choice(["normal", "ties", "special"]))
+        path = str(rng.choice(["auto", "block"]))
+        tag = f"factors {f} k{k} rows{rows} {dtype} {kind} {path}"
+        print(tag, flush=True)
+        if path == "block":
+            monkeypatch.setenv("SDM_TOPK_PATH", "block")
+        else:
+            monkeypatch.delenv("SDM_TOPK_PATH", raising=False)
+        x32 = _raw(kind, rows, sum(f), seed=9000 + i)
+        t, exact = _to_dtype(x32, dtype, gpu)
+        val, lin = product_key_topk(t, f, k)
+        torch.cuda.synchronize()
+        ov, ol = pk.product_key_topk(exact, f, k, bf16=dtype == "bf16")
+        assert lin.shape == ol.shape and np.array_equal(lin.cpu().numpy(), ol), tag
+        got, want = _bits(val), _oracle_val_bits(ov, dtype)
+        both_nan = np.isnan(val.float().cpu().numpy()) & np.isnan(ov)
+        assert np.array_equal(np.where(both_nan, 0, got), np.where(both_nan, 0, want)), tag
+        g32 = _raw("normal", rows, lin.shape[1], seed=9500 + i)
+        gt, gexact = _to_dtype(g32, dtype, gpu)
+        graw = product_key_topk_backward(lin, gt, f)
+        torch.cuda.synchronize()
+        wantb = pk.product_key_topk_backward(lin.cpu().numpy(), gexact, f, bf16=dtype == "bf16")
+        assert np.array_equal(_bits(graw), _oracle_val_bits(wantb, dtype)), tag
+    monkeypatch.delenv("SDM_TOPK_PATH", raising=False)
