@@ -798,7 +798,9 @@ __global__ __launch_bounds__(kColdBlock) void p1_gram_cold_kernel(Problem pb, Sl
 // staged in LDS kHotKb at a time, each read once from memory (the next block's loads are in
 // flight during this block's products), and each wavefront accumulates its tiles over every
 // column block in registers with the MFMA chains of hot_tiles (16 columns at a time, lane
-// group l / 16 taking columns 4 (l / 16) .. + 3, h ascending): the same bits.
+// group l / 16 taking columns 4 (l / 16) .. + 3, h ascending): the same bits. The chains of
+// three tiles are interleaved step by step, so that the matrix unit always has an independent
+// product to start while a dependent one is in flight.
 // Chunks of fewer than kHotLdsMinC tokens have too few tiles for a workgroup per matrix:
 // there each wavefront takes tiles straight from memory (hot_tiles), kHotBlock threads per
 // workgroup, the tiles of a chunk split over up to eight workgroups. Both give the same bits.
@@ -813,6 +815,10 @@ __global__ __launch_bounds__(kHotBlock) void p1_gram_hot_tiles_kernel(Problem pb
 constexpr int kHotLdsBlock = 1024;
 constexpr int kHotKb = 32;                 // hot columns per staged block
 constexpr int kHotPitch = kHotKb + 4;      // LDS row pitch (floats): 16-byte rows 4 banks apart
+constexpr int kHotIl = 3;                  // tiles whose MFMA chains interleave
+
+// Component k (0..3, a constant after unrolling) of a float4.
+__device__ __forceinline__ float f4_at(const float4 &v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
 constexpr int kHotMaxT = ((kMaxChunk / 16) * (kMaxChunk / 16 + 1) / 2 + kHotLdsBlock / kWave - 1) / (kHotLdsBlock / kWave);
 constexpr int kHotU = (2 * kMaxChunk * (kHotKb / 4) + kHotLdsBlock - 1) / kHotLdsBlock;   // 16-byte units per thread
 
@@ -841,9 +847,13 @@ __global__ __launch_bounds__(kHotLdsBlock) void p1_gram_hot_kernel(Problem pb, S
     // columns past HP stage as 0 (loads unconditional, clamped in bounds)
     float4 st[kHotU];
     auto load = [&](int hb) {
+        // the thread id re-read opaquely, so that the loads' 64-bit addresses are formed
+        // here and not held across the block loop (they would spill)
+        int tio = threadIdx.x;
+        asm volatile("" : "+v"(tio));
 #pragma unroll
         for (int u = 0; u < kHotU; ++u) {
-            const int i = tid + u * kHotLdsBlock, w = i / nq, rem = i - w * nq;
+            const int i = tio + u * kHotLdsBlock, w = i / nq, rem = i - w * nq;
             const int r = rem / (kHotKb / 4), col = hb + 4 * (rem % (kHotKb / 4));
             const bool ok = i < 2 * nq && r < C && col < HP;
             const float *src = (w == 0 ? Kb : Aop) + (ok ? int64_t(r) * L.HCAP + col : 0);
@@ -863,6 +873,22 @@ __global__ __launch_bounds__(kHotLdsBlock) void p1_gram_hot_kernel(Problem pb, S
     f32x4 acc[kHotMaxT];
 #pragma unroll
     for (int q = 0; q < kHotMaxT; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // The wavefront's tiles t = wave + q NW: the LDS row offsets of their operands (wave-
+    // uniform, held in scalar registers); tiles past the triangle repeat its last tile, whose
+    // products are computed and never stored.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int aof[kHotMaxT], bof[kHotMaxT];
+#pragma unroll
+    for (int q = 0; q < kHotMaxT; ++q) {
+        const int t = min(wv + q * NW, T1 - 1);
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= t) ++I;
+        const int J = t - I * (I + 1) / 2;
+        aof[q] = __builtin_amdgcn_readfirstlane(16 * I * kHotPitch);
+        bof[q] = __builtin_amdgcn_readfirstlane(16 * J * kHotPitch);
+    }
+    const int lof = (lane & 15) * kHotPitch + ko;
+    const int ntw = wv < T1 ? (T1 - wv + NW - 1) / NW : 0;
     load(0);
     for (int hb = 0; hb < HP; hb += kHotKb) {
         __syncthreads();   // the previous block's products are done with the LDS
@@ -870,22 +896,26 @@ __global__ __launch_bounds__(kHotLdsBlock) void p1_gram_hot_kernel(Problem pb, S
         __syncthreads();
         if (hb + kHotKb < HP) load(hb + kHotKb);
         const int nsb = min(kHotKb, HP - hb) / 16;   // 16-column sub-blocks (HP is a multiple of 16)
+        // kHotIl tiles at a time, their MFMA chains interleaved step by step: each tile's
+        // chain is the same (sub-blocks ascending, four k-steps each), so are the bits
+        for (int sb = 0; sb < nsb; ++sb) {
 #pragma unroll
-        for (int q = 0; q < kHotMaxT; ++q) {
-            const int t = wave + q * NW;
-            if (t >= T1) break;
-            int I = 0;
-            while ((I + 1) * (I + 2) / 2 <= t) ++I;
-            const int J = t - I * (I + 1) / 2;
-            const float *ar = al + (16 * I + (lane & 15)) * kHotPitch + ko;
-            const float *br = bl + (16 * J + (lane & 15)) * kHotPitch + ko;
-            for (int sb = 0; sb < nsb; ++sb) {
-                const float4 av = *reinterpret_cast<const float4 *>(ar + 16 * sb);
-                const float4 bv = *reinterpret_cast<const float4 *>(br + 16 * sb);
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[q], 0, 0, 0);
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[q], 0, 0, 0);
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[q], 0, 0, 0);
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[q], 0, 0, 0);
+            for (int q0 = 0; q0 < kHotMaxT; q0 += kHotIl) {
+                if (q0 >= ntw) break;
+                float4 av[kHotIl], bv[kHotIl];
+#pragma unroll
+                for (int j = 0; j < kHotIl; ++j) {
+                    const int q = q0 + j < kHotMaxT ? q0 + j : kHotMaxT - 1;
+                    av[j] = *reinterpret_cast<const float4 *>(al + lof + aof[q] + 16 * sb);
+                    bv[j] = *reinterpret_cast<const float4 *>(bl + lof + bof[q] + 16 * sb);
+                }
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int j = 0; j < kHotIl; ++j)
+                        if (q0 + j < kHotMaxT)
+                            acc[q0 + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(av[j], kk), f4_at(bv[j], kk),
+                                                                              acc[q0 + j], 0, 0, 0);
             }
         }
     }

@@ -695,7 +695,11 @@ def test_phase2_cu_budget_does_not_change_bits(gpu, wl):
 @pytest.mark.parametrize("wl", [
     small(P=2, T=256, C=128, hd=8, M=40, W=24, R=24, ids="zipf", ragged=True, index=80),
     small(P=2, T=130, C=64, hd=8, M=12, W=6, R=5, index=81),
-], ids=["C128_zipf", "C64_allhot"])
+    # nine tiles per wavefront (three interleaved groups), hot columns over several blocks
+    small(P=1, T=512, C=256, hd=8, M=400, W=32, R=32, ids="zipf", index=82),
+    # a ragged tile count (C = 200: 91 tiles, five or six per wavefront)
+    small(P=2, T=300, C=200, hd=8, M=300, W=16, R=16, ids="mixed", ragged=True, index=83),
+], ids=["C128_zipf", "C64_allhot", "C256_zipf", "C200_mixed"])
 def test_hot_gram_kernels_give_the_same_bits(gpu, wl, monkeypatch):
     """The hot Gram staged in LDS (one workgroup per chunk and matrix) and the per-tile kernel
     (operands from memory) run the same MFMA chains: identical A and QK."""
