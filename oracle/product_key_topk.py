@@ -63,7 +63,7 @@ def topk_row(row: np.ndarray, factors, k: int, bf16: bool):
     ranks = []
     for f, w in enumerate(factors):
         vals = [np.float32(row[starts[f] + c]) for c in range(w)]
-        # value descending, larger column first on ties
+        # descending by value; among equal values the higher column index comes first
         order = sorted(range(w), key=lambda c: (order_key(vals[c]), c), reverse=True)
         ranks.append([(vals[c], c) for c in order])
     kk = min(k, math.prod(factors))
@@ -83,7 +83,7 @@ def topk_row(row: np.ndarray, factors, k: int, bf16: bool):
                 if bf16 and F > 2 and f < F - 1:
                     s = round_bf16(s)
                 pairs.append((s, i, j))
-        # score descending; exact ties to the larger i + j, then the larger i
+        # descending by score; equal scores: the higher i + j first, then the higher i
         pairs.sort(key=lambda q: (order_key(q[0]), q[1] + q[2], q[1]), reverse=True)
         cur = [(s, cur[i][1] * factors[f] + ranks[f][j][1]) for s, i, j in pairs[:c]]
     assert len(cur) == kk
