@@ -359,10 +359,24 @@ def cpu_baseline(inp: dict, wl, seconds: float, streams_total: int, twin: str = 
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # one thread on the sample's first stream alone (its own bank: no other stream's rows copied)
+    f1 = {k: np.ascontiguousarray(v[:1]) for k, v in f.items()}
+    tok1 = int(np.sum(f1["valid"]))
+    oracle.token_loop(f1, threads=1)
+    reps1, t1 = 0, time.perf_counter()
+    while True:
+        oracle.token_loop(f1, threads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 3:
+            break
     return {"value": reps * tokens / el, "unit": "tokens/s", "cores": threads, "host_cores": os.cpu_count(),
             "kind": "oracle",
             "sample": f"{wl.P} of the workload's {streams_total} streams{twin} ({tokens} valid tokens) x {reps} "
-                      f"passes of the fp64 token loop, {threads} threads, {el:.1f} s"}
+                      f"passes of the fp64 token loop, {threads} threads, {el:.1f} s",
+            "one_thread": {"value": reps1 * tok1 / el1, "unit": "tokens/s",
+                           "sample": f"stream 0 of that sample ({tok1} valid tokens) x {reps1} passes, 1 thread, "
+                                     f"{el1:.1f} s"}}
 
 
 def main():
