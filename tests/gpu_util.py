@@ -17,12 +17,15 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}   # infinity-norm relative error per output te
 # 230 %; there the contract check is per row instead (check_rows).
 WELL = 0.5
 # Per-row check (bfloat16): each quantile of the GPU's per-row error against O1b stays
-# within ROW_FACTOR x the float32 contract evaluation's same quantile plus ROW_FLOOR (about
-# one bfloat16 ulp, 2^-8). Measured on config 2: the GPU's quantiles 0.5 / 0.9 / 0.99 /
-# 0.999 are 1.07-1.19 x the evaluation's on the bank, 1.08-1.19 x on the readings.
+# within ROW_FACTOR x the float32 contract evaluation's same quantile plus ROW_FLOOR, one
+# bfloat16 ulp where it is widest relative to the value (2^-7, at a power of two): a
+# float32 result within float32 error of a rounding boundary may round to the neighbouring
+# bfloat16 value, which in a row of one column is that row's whole error. Measured on
+# config 2: the GPU's quantiles 0.5 / 0.9 / 0.99 / 0.999 are 1.07-1.19 x the evaluation's
+# on the bank, 1.08-1.19 x on the readings.
 ROW_QUANTILES = (0.5, 0.9, 0.99, 0.999)
 ROW_FACTOR = 1.5
-ROW_FLOOR = 4e-3
+ROW_FLOOR = 2.0 ** -7
 
 
 def to_torch(inp: dict, device) -> dict:

@@ -221,6 +221,10 @@ SMALL = [
     small(P=1, T=1, C=16, hd=8, M=1, W=1, R=1, index=40),                                     # one token, one row
     small(P=2, T=5, C=64, hd=16, M=10, W=2, R=2, ragged=True, index=41),                     # shorter than a chunk
     small(P=1, T=40, C=16, hd=1024, M=30, W=3, R=3, dtype="bf16", index=42),                 # wide head
+    # bfloat16 rows of one column: one reading rounded to the neighbouring bfloat16 value is
+    # a whole row's error, one ulp (up to 2^-7 of the value)
+    small(P=1, T=259, C=16, hd=1, M=834, W=128, R=48, dtype="bf16", ids="mixed", gate_width=1, weight_scale=-1.0,
+          index=1020),
 ]
 
 
