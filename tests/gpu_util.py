@@ -23,9 +23,15 @@ WELL = 0.5
 # bfloat16 value, which in a row of one column is that row's whole error. Measured on
 # config 2: the GPU's quantiles 0.5 / 0.9 / 0.99 / 0.999 are 1.07-1.19 x the evaluation's
 # on the bank, 1.08-1.19 x on the readings.
+# A quantile is compared only where at least ROW_MIN_ABOVE rows lie above it: higher up it
+# is the extreme of a handful of rows (the largest, at 0.999 of a few hundred rows), and
+# where single rounding flips, or a reading that cancels to near zero (its float32 noise then
+# large relative to it), fall differs between any two float32 evaluations of the contract
+# (two summation orders of the same evaluation give 0 and 7e-3 at such a quantile).
 ROW_QUANTILES = (0.5, 0.9, 0.99, 0.999)
 ROW_FACTOR = 1.5
 ROW_FLOOR = 2.0 ** -7
+ROW_MIN_ABOVE = 10
 
 
 def to_torch(inp: dict, device) -> dict:
@@ -111,8 +117,9 @@ def check(out, bank, ref, con, dtype: str, what: str = ""):
 def check_rows(out, bank, con, emu, what: str = ""):
     """Per-row errors against O1b (each row of the readings and each bank row that O1b
     holds nonzero, relative to that row's own largest element), so that the largest rows
-    of a growing bank cannot hide errors on small ones: every quantile in ROW_QUANTILES
-    within ROW_FACTOR x the float32 contract evaluation's plus ROW_FLOOR."""
+    of a growing bank cannot hide errors on small ones: every quantile in ROW_QUANTILES with
+    at least ROW_MIN_ABOVE rows above it within ROW_FACTOR x the float32 contract
+    evaluation's plus ROW_FLOOR."""
     from tests.contract_f32 import row_rel_err
     got = [f64(x) if isinstance(x, torch.Tensor) else x for x in (out, bank)]
     lines = []
@@ -120,10 +127,13 @@ def check_rows(out, bank, con, emu, what: str = ""):
         rg, re_ = row_rel_err(g, c), row_rel_err(e, c)
         if rg.size == 0:
             continue
-        qg, qe = np.quantile(rg, ROW_QUANTILES), np.quantile(re_, ROW_QUANTILES)
-        lines.append(f"{name} rows q{ROW_QUANTILES} gpu {np.array2string(qg, precision=2)} "
+        qs = tuple(q for q in ROW_QUANTILES if rg.size * (1.0 - q) >= ROW_MIN_ABOVE)
+        if not qs:
+            continue
+        qg, qe = np.quantile(rg, qs), np.quantile(re_, qs)
+        lines.append(f"{name} rows ({rg.size}) q{qs} gpu {np.array2string(qg, precision=2)} "
                      f"f32-contract {np.array2string(qe, precision=2)}")
-        for q, a, b in zip(ROW_QUANTILES, qg, qe):
+        for q, a, b in zip(qs, qg, qe):
             assert a <= ROW_FACTOR * b + ROW_FLOOR, (what, name, "row quantile", q, a, b)
     print(f"{what}: " + "; ".join(lines), flush=True)
 
