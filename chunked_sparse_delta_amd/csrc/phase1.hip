@@ -816,11 +816,11 @@ constexpr int kHotLdsBlock = 1024;
 constexpr int kHotKb = 32;                 // hot columns per staged block
 constexpr int kHotPitch = kHotKb + 4;      // LDS row pitch (floats): 16-byte rows 4 banks apart
 constexpr int kHotIl = 3;                  // tiles whose MFMA chains interleave
+constexpr int kHotMaxT = ((kMaxChunk / 16) * (kMaxChunk / 16 + 1) / 2 + kHotLdsBlock / kWave - 1) / (kHotLdsBlock / kWave);
+constexpr int kHotU = (2 * kMaxChunk * (kHotKb / 4) + kHotLdsBlock - 1) / kHotLdsBlock;   // 16-byte units per thread
 
 // Component k (0..3, a constant after unrolling) of a float4.
 __device__ __forceinline__ float f4_at(const float4 &v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; }
-constexpr int kHotMaxT = ((kMaxChunk / 16) * (kMaxChunk / 16 + 1) / 2 + kHotLdsBlock / kWave - 1) / (kHotLdsBlock / kWave);
-constexpr int kHotU = (2 * kMaxChunk * (kHotKb / 4) + kHotLdsBlock - 1) / kHotLdsBlock;   // 16-byte units per thread
 
 size_t hot_lds_bytes(int C) { return size_t(2) * ((C + 15) & ~15) * kHotPitch * sizeof(float); }
 
