@@ -62,6 +62,16 @@ template <> struct Vec<float, 4> {
     static __device__ __forceinline__ void store(float *p, const float (&o)[4]) {
         *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
     }
+    // the same with the non-temporal hint (the line is not kept for reuse)
+    static __device__ __forceinline__ raw_t load_raw_nt(const float *p) {
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        const f4_t x = __builtin_nontemporal_load(reinterpret_cast<const f4_t *>(p));
+        return make_float4(x[0], x[1], x[2], x[3]);
+    }
+    static __device__ __forceinline__ void store_nt(float *p, const float (&o)[4]) {
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f4_t{o[0], o[1], o[2], o[3]}, reinterpret_cast<f4_t *>(p));
+    }
 };
 template <> struct Vec<bf16, 8> {
     using raw_t = uint4;
@@ -89,6 +99,20 @@ template <> struct Vec<bf16, 8> {
         for (int i = 0; i < 4; ++i)
             w[i] = f32x2_to_bf16x2(o[2 * i], o[2 * i + 1]);
         *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // the same with the non-temporal hint (the line is not kept for reuse)
+    static __device__ __forceinline__ raw_t load_raw_nt(const bf16 *p) {
+        typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+        const u4_t x = __builtin_nontemporal_load(reinterpret_cast<const u4_t *>(p));
+        return make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    static __device__ __forceinline__ void store_nt(bf16 *p, const float (&o)[8]) {
+        typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+        u4_t w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = f32x2_to_bf16x2(o[2 * i], o[2 * i + 1]);
+        __builtin_nontemporal_store(w, reinterpret_cast<u4_t *>(p));
     }
 };
 // Four bfloat16 columns (8 bytes): the narrow slices of a resident bank (see plan_phase2).

@@ -24,7 +24,8 @@
 //            member rides in the group record, the second comes with the bank row (and,
 //            records in memory, the next NV too, one per lane of the group), the rest four
 //            at a time; the next batch's records load under the current one; groups of 16
-//            or more members by whole wavefronts, the next one's loads under this one's sums
+//            or more members by whole wavefronts, the next one's loads under this one's sums;
+//            a bank in memory has its DW rows loaded and stored with the non-temporal hint
 //
 // Determinism: each output element has exactly one writer, and every sum runs in an order
 // fixed by the shapes W, R and C only (never by the slicing or the launch):
@@ -347,6 +348,24 @@ __device__ __forceinline__ void load_aop(const float *p, int pitch, bool ok, flo
     for (int kk = 0; kk < 4; ++kk) a[kk] = ok ? a[kk] : 0.0f;
 }
 
+// Bank row loads and stores of the DW. With NT (a bank in memory: it exceeds every cache)
+// the row's line is streamed with the non-temporal hint: the DW's second read of a written
+// row and its store are not used again within the step, and kept lines would displace the
+// rows the gather reuses. 16-byte vectors only; narrower ones load and store plainly.
+template <typename T, int V>
+constexpr bool kHasNt = (std::is_same<T, bf16>::value && V == 8) || (std::is_same<T, float>::value && V == 4);
+
+template <typename T, int V, bool NT>
+__device__ __forceinline__ typename Vec<T, V>::raw_t dw_load(const T *p) {
+    if constexpr (NT && kHasNt<T, V>) return Vec<T, V>::load_raw_nt(p);
+    else return Vec<T, V>::load_raw(p);
+}
+template <typename T, int V, bool NT>
+__device__ __forceinline__ void dw_store(T *p, const float (&o)[V]) {
+    if constexpr (NT && kHasNt<T, V>) Vec<T, V>::store_nt(p, o);
+    else Vec<T, V>::store(p, o);
+}
+
 // DW of one group with many members (>= kHotMin) by a whole wavefront: lane (r, p) =
 // (lane / 8, lane % 8) sums the members m = r, r + 8, ... of the group in token order for
 // vector p of the slice; the eight classes combine as in the gather, and the decay term
@@ -360,7 +379,7 @@ struct BigLoads {
     int32_t rt[4], rc[4];
 };
 
-template <typename T, int V>
+template <typename T, int V, bool NT>
 __device__ __forceinline__ void big_issue(const T *bank, int hd, const int4 &rec, const int2 *mrec, int col0, int nvs,
                                           int lane, BigLoads<T, V> &L) {
     const int p = lane & 7;
@@ -368,7 +387,7 @@ __device__ __forceinline__ void big_issue(const T *bank, int hd, const int4 &rec
     const int32_t m0 = rec.y & 0xFFFF, n = ((rec.y >> 16) & 0xFF) + 1;
     const uint32_t col = uint32_t(col0 + p * V);
     // loads unconditional (in-bounds fallbacks), as in the gather
-    L.raw = Vec<T, V>::load_raw(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
+    L.raw = dw_load<T, V, NT>(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int m = lane + 64 * q;
@@ -378,7 +397,7 @@ __device__ __forceinline__ void big_issue(const T *bank, int hd, const int4 &rec
     }
 }
 
-template <typename T, int V>
+template <typename T, int V, bool NT>
 __device__ __forceinline__ void big_finish(T *bank, int hd, const int4 &rec, const BigLoads<T, V> &L, const float *dl,
                                            int pitch, int col0, int nvs, int lane) {
     const int r = lane >> 3, p = lane & 7;
@@ -417,7 +436,7 @@ __device__ __forceinline__ void big_finish(T *bank, int hd, const int4 &rec, con
         const float dec = __int_as_float(rec.z);
 #pragma unroll
         for (int c = 0; c < V; ++c) b[c] = b[c] * dec + acc[c];
-        Vec<T, V>::store(at(bank, uint32_t(rec.x) * uint32_t(hd) + col), b);
+        dw_store<T, V, NT>(at(bank, uint32_t(rec.x) * uint32_t(hd) + col), b);
     }
 }
 
@@ -442,12 +461,12 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
         auto brec_at = [&](int32_t bi) { return *at(brec, uint32_t(bi < nbig ? bi : nbig - 1)); };
         int4 rc0 = brec_at(wave), rc1 = brec_at(wave + NW);
         BigLoads<T, V> cur;
-        big_issue<T, V>(bank, bst, rc0, mrec, 0, nvs, dlane, cur);
+        big_issue<T, V, !SM>(bank, bst, rc0, mrec, 0, nvs, dlane, cur);
         for (int32_t bi = wave; bi < nbig; bi += NW) {
             BigLoads<T, V> nxt;
-            big_issue<T, V>(bank, bst, rc1, mrec, 0, nvs, dlane, nxt);
+            big_issue<T, V, !SM>(bank, bst, rc1, mrec, 0, nvs, dlane, nxt);
             const int4 rc2 = brec_at(bi + 2 * NW);
-            big_finish<T, V>(bank, bst, rc0, cur, db, pitch, 0, nvs, dlane);
+            big_finish<T, V, !SM>(bank, bst, rc0, cur, db, pitch, 0, nvs, dlane);
             cur = nxt;
             rc0 = rc1;
             rc1 = rc2;
@@ -477,7 +496,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             const bool sm = small(rec[u]);
-            raw[u] = Vec<T, V>::load_raw(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
+            raw[u] = dw_load<T, V, !SM>(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
             const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
             const bool two = sm && n1 > 0;
             const int2 x = *at(mrec, uint32_t(two ? m0 + 1 : 0));
@@ -558,7 +577,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
                     for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                 }
             }
-            if (vok && sm) Vec<T, V>::store(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
+            if (vok && sm) dw_store<T, V, !SM>(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
