@@ -1,6 +1,8 @@
 // Internal definitions shared by the SDM kernels and the C-ABI host code (gfx950).
 #pragma once
 
+#include <cstdlib>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -142,6 +144,12 @@ template <typename T> struct Vec<T, 1> {
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (uint64_t(1) << lane) - 1; }
 
+// Bit 30 of a slot id in a chunk's id copies (ids stay below 2^30: the host refuses a stream
+// bank of 2 GiB or more): the partitioned Phase 1 sets it where no other entry of the chunk
+// has the slot, and Phase 2 streams that row with the non-temporal hint on large workloads.
+constexpr int32_t kIdOnce = 1 << 30;
+constexpr int32_t kIdMask = kIdOnce - 1;
+
 // The lanes of the wavefront whose digit (db low bits of d) equals this lane's, among the
 // lanes with ok set: one ballot per digit bit.
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool ok, int db) {
@@ -180,6 +188,20 @@ struct Problem {
     int32_t part_on;         // Phase 1 of this call runs the partitioned kernel first: the sorting
                              // kernels then handle only the chunks it left to them (meta[7] = 1)
 };
+
+// Whether rows that one entry of a chunk alone reads are streamed with the non-temporal hint
+// (the partitioned Phase 1 marks their ids with kIdOnce, the Phase-2 gather of a bank in
+// memory loads them so): when a step's rows, P C (W + R) of head_dim columns, exceed the
+// memory-side cache; beyond it their kept lines only displace rows the gather reuses, below
+// it keeping every line measured faster. SDM_P2_NT = 0 / 1 turns it off / on whatever the
+// shapes (tests: the bits are the same either way).
+constexpr int64_t kMallBytes = int64_t(256) << 20;   // MI355X's memory-side (Infinity) cache
+inline bool once_rows_streamed(const Problem &pb) {
+    const char *e = getenv("SDM_P2_NT");
+    if (e) return e[0] == '1';
+    const double b = double(pb.P) * pb.C * (pb.W + pb.R) * pb.hd * (pb.dtype == 0 ? 4 : 2);
+    return b > double(kMallBytes);
+}
 
 // Slot id i of an int32 or int64 id array (ids of valid calls lie in [0, M), M < 2^31): one
 // 32-bit load either way (an int64 id's low word), with no branch on the width, so that

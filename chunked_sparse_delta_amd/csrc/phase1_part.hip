@@ -90,12 +90,13 @@ struct PartSmem {
 
 constexpr int kPartBatch = 8;   // global loads in flight per thread in the streaming loops
 
-// dst[i] = id i of base + off, i < n (int32 or int64 ids), kPartBatch loads in flight per
-// thread; each id also counted in its partition, pcnt[id & pmask] (the LDS atomics are
-// unconditional, adding 0 past n: a branch would make each of them wait for every load).
+// Count ids base + off .. + n - 1 (int32 or int64) in their partitions, pcnt[id & pmask], and
+// with copy store them to dst in entry order (Phase 2 reads them); kPartBatch loads in flight
+// per thread (the LDS atomics are unconditional, adding 0 past n: a branch would make each
+// of them wait for every load).
 template <class Cfg>
-__device__ __forceinline__ void copy_count_ids(const void *base, int32_t id8, int64_t off, int32_t n, uint32_t *dst,
-                                               int32_t *pcnt, uint32_t pmask) {
+__device__ __forceinline__ void count_ids(const void *base, int32_t id8, int64_t off, int32_t n, bool copy,
+                                          uint32_t *dst, int32_t *pcnt, uint32_t pmask) {
     PART_CFG_NAMES(Cfg);
     const int tid = threadIdx.x;
     for (int32_t x0 = 0; x0 < n; x0 += kPartBlock * kPartBatch) {
@@ -108,7 +109,7 @@ __device__ __forceinline__ void copy_count_ids(const void *base, int32_t id8, in
 #pragma unroll
         for (int u = 0; u < kPartBatch; ++u) {
             const int32_t x = x0 + u * kPartBlock + tid;
-            if (x < n) dst[x] = uint32_t(v[u]);
+            if (copy && x < n) dst[x] = uint32_t(v[u]);
             atomicAdd(&pcnt[uint32_t(v[u]) & pmask], x < n ? 1 : 0);
         }
     }
@@ -222,6 +223,8 @@ __device__ __forceinline__ SegAcc seg_op(const SegAcc &a, const SegAcc &b) {
 struct PartArgs {
     int32_t lognp;      // log2 of the partition count
     int32_t sort_bits;  // slot bits above the partition bits
+    int32_t once;       // the emit stage writes the id copies, marking ids with kIdOnce (else the
+                        // count stage copies them unmarked)
 };
 
 template <class Cfg>
@@ -242,15 +245,16 @@ __global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Sla
     const uint32_t pmask = uint32_t(NP - 1);
     int32_t *meta = reinterpret_cast<int32_t *>(cb + L.off_meta);
 
-    // ---- count the entries of each partition while copying the ids in entry order (Phase 2
-    //      reads them); a partition past the LDS leaves the chunk to the sorting path (which
-    //      writes the same copies again)
+    // ---- count the entries of each partition (copying the ids in entry order unless the emit
+    //      stage writes them marked); a partition past the LDS leaves the chunk to the sorting
+    //      path (which writes the copies itself)
     uint32_t *kid = cb + L.off_kid;
     uint32_t *qid = cb + L.off_qid;
+    const bool once = pa.once != 0;
     for (int d = tid; d < NP; d += kPartBlock) s.pcnt[d] = 0;
     __syncthreads();
-    copy_count_ids<Cfg>(pb.k_idx, pb.k_id8, tok0 * W, El, kid, s.pcnt, pmask);
-    copy_count_ids<Cfg>(pb.q_idx, pb.q_id8, tok0 * R, Fl, qid, s.pcnt, pmask);
+    count_ids<Cfg>(pb.k_idx, pb.k_id8, tok0 * W, El, !once, kid, s.pcnt, pmask);
+    count_ids<Cfg>(pb.q_idx, pb.q_id8, tok0 * R, Fl, !once, qid, s.pcnt, pmask);
     __syncthreads();
     if (tid == 0) {
         int32_t o = 0, fb = 0;
@@ -603,6 +607,8 @@ __global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Sla
         //          run of this token's reads of the slot (which carries the run's sum of
         //          q e^(Lr - L_ref), in read order), bits of that sum, 0}, no write before: 0;
         //   oval   the gather weight, k e^L or q e^Lr.
+        // Bit 30 of .y (free in every record: positions stay below 2^17) marks an entry whose
+        // slot no other entry of the chunk has; the emit stage moves it to the id copy.
         const int32_t lbase = s.poff[pp];
 #pragma unroll
         for (int u = 0; u < kPartIpt; ++u) {
@@ -657,6 +663,9 @@ __global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Sla
             } else {
                 ov = v1 * expf(0.0f);
             }
+            const bool once = (j == 0 || s.slot[ord[j - 1]] != s.slot[idx]) &&
+                              (j + 1 == nn || s.slot[ord[j + 1]] != s.slot[idx]);
+            orec.y |= once ? kIdOnce : 0;
             plist[lbase + idx] = orec;
             oval[lbase + idx] = __float_as_uint(ov);
         }
@@ -696,10 +705,17 @@ __global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Sla
             const int nt = ntok * WR;
             int4 rec[kPartIpt];
             uint32_t ovv[kPartIpt];
+            int32_t idv[kPartIpt] = {};
 #pragma unroll
             for (int u = 0; u < kPartIpt; ++u) {
                 rec[u] = plist[sl_[u]];
                 ovv[u] = oval[sl_[u]];
+                // this entry's slot id from the input (entry 0 of the tile past its end)
+                const int32_t i = u * kPartBlock + tid;
+                const int tt = i < nt ? i / WR : 0, o = i < nt ? i - tt * WR : 0;
+                if (once)
+                    idv[u] = o < W ? load_id(pb.k_idx, (tok0 + t0 + tt) * W + o, pb.k_id8)
+                                   : load_id(pb.q_idx, (tok0 + t0 + tt) * R + (o - W), pb.q_id8);
             }
             if (t0 + TE2 < nl) load_slots(t0 + TE2, sl_);
             for (int x = tid; x < 3 * ntok * HP; x += kPartBlock) hrow[x] = 0.0f;
@@ -709,8 +725,11 @@ __global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Sla
                 const int32_t i = u * kPartBlock + tid;
                 if (i >= nt) break;
                 const int tt = i / WR, o = i - tt * WR, t = t0 + tt;
-                const int4 r = rec[u];
+                int4 r = rec[u];
+                const int32_t single = r.y & kIdOnce;
+                r.y &= ~kIdOnce;
                 if (o < W) {
+                    if (once) kid[t * W + o] = uint32_t(idv[u] | single);
                     gw[t * W + o] = __uint_as_float(ovv[u]);
                     if (r.x < 0) {
                         ecr[t * W + o] = make_int4(r.y, r.y, 0, 0);
@@ -721,6 +740,7 @@ __global__ __launch_bounds__(Cfg::kBlock, 4) void p1_part_kernel(Problem pb, Sla
                         ecr[t * W + o] = r;
                     }
                 } else {
+                    if (once) qid[t * R + (o - W)] = uint32_t(idv[u] | single);
                     gr[t * R + (o - W)] = __uint_as_float(ovv[u]);
                     if (r.x < 0) {
                         rcr[t * R + (o - W)] = make_int4(0, 0, 0, 0);
@@ -784,7 +804,7 @@ int part_lognp(int64_t E, int64_t F, int key_bits) {
 }
 
 hipError_t launch_phase1_part(const Problem &pb, const Slab &sl, int lognp, hipStream_t st) {
-    PartArgs pa{lognp, pb.key_bits > lognp ? pb.key_bits - lognp : 0};
+    PartArgs pa{lognp, pb.key_bits > lognp ? pb.key_bits - lognp : 0, once_rows_streamed(pb) ? 1 : 0};
     const unsigned nch = unsigned(int64_t(pb.P) * sl.steps);
     if (sl.lay.E + sl.lay.F >= kPartBigEntries) {
         if (lognp > PartBig::kMaxLogNP) return hipErrorInvalidValue;

@@ -71,6 +71,7 @@ struct P2Args {
     int32_t off_kid, off_qid, off_stage0, off_stage1;
     int32_t off_xu;                 // teams: the exchange area of a chunk
     uint32_t steal_ticks;           // teams: wait before claiming another workgroup's piece (100 MHz ticks)
+    int32_t nt_gather;              // rows of ids marked kIdOnce load with the non-temporal hint
 };
 
 // Live tokens of stream p (valid_tokens clamped to [0, T]), and of its chunk ti.
@@ -176,6 +177,26 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
     }
 }
 
+// Bank row loads and stores that may take the non-temporal hint (NT): the line is streamed,
+// not kept for reuse. The DW of a bank in memory (it exceeds every cache) uses it for its
+// second read of each written row and for the row's store, neither used again within the
+// step, whose kept lines would displace the rows the gather reuses; the gather uses it, on
+// large workloads, for rows that one entry of the chunk alone reads. 16-byte vectors only;
+// narrower ones load and store plainly.
+template <typename T, int V>
+constexpr bool kHasNt = (std::is_same<T, bf16>::value && V == 8) || (std::is_same<T, float>::value && V == 4);
+
+template <typename T, int V, bool NT>
+__device__ __forceinline__ typename Vec<T, V>::raw_t dw_load(const T *p) {
+    if constexpr (NT && kHasNt<T, V>) return Vec<T, V>::load_raw_nt(p);
+    else return Vec<T, V>::load_raw(p);
+}
+template <typename T, int V, bool NT>
+__device__ __forceinline__ void dw_store(T *p, const float (&o)[V]) {
+    if constexpr (NT && kHasNt<T, V>) Vec<T, V>::store_nt(p, o);
+    else Vec<T, V>::store(p, o);
+}
+
 // Weighted row sums of one region (the write entries or the read entries) for the live
 // tokens of the chunk, into dst[t * pitch + vq * V + c]. Lane layout: vq = lane % NV (the
 // vector of the slice), class r = (lane / NV) % 8, ts = lane / (8 NV) (the token within a
@@ -188,12 +209,13 @@ __device__ __forceinline__ void lds_load_vec(const float *p, float (&x)[V]) {
 // batch's ids and weights load under the current batch's rows). The calling waves are
 // wave = 0 .. nw - 1 of the region.
 // UFT && uf: the sums are the write entries' retrieved rows, and u = beta (v - retrieved)
-// is stored in their place (v from vsrc[t * NV + vq], beta from beta[t]).
+// is stored in their place (v from vsrc[t * NV + vq], beta from beta[t]). Ids carry the
+// kIdOnce bit; with ntg, the rows of ids that have it load with the non-temporal hint.
 template <typename T, int V, int NV, int kBatch, int Q, bool UFT>
 __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32_t *ids, const float *wts, int width,
                                               int nl, int col0, int nvs, float *dst, int pitch, int wave, int nw,
                                               int lane, bool uf, const typename Vec<T, V>::raw_t *vsrc,
-                                              const float *beta) {
+                                              const float *beta, bool ntg) {
     static_assert(Q == 1 || Q == 4, "one or four entries per id load");
     constexpr int TPI = 8 / NV;
     const int vq = lane % NV, r = (lane / NV) & 7, ts = lane / (8 * NV);
@@ -249,8 +271,8 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
                 const bool ok = id[u][q] >= 0 && vok;
-                raw[u][q] = Vec<T, V>::load_raw(
-                    at(bank, uint32_t(ok ? id[u][q] : 0) * uint32_t(hd) + (vok ? col : uint32_t(col0))));
+                const T *rp = at(bank, uint32_t(ok ? id[u][q] & kIdMask : 0) * uint32_t(hd) + (vok ? col : uint32_t(col0)));
+                raw[u][q] = ntg && (id[u][q] & kIdOnce) ? dw_load<T, V, true>(rp) : Vec<T, V>::load_raw(rp);
             }
         // staged, ids and weights come from LDS: a wave-uniform branch skips the loads past
         // the last batch without making any memory load wait
@@ -346,24 +368,6 @@ __device__ __forceinline__ void load_aop(const float *p, int pitch, bool ok, flo
     for (int kk = 0; kk < 4; ++kk) a[kk] = p[kk * pitch];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) a[kk] = ok ? a[kk] : 0.0f;
-}
-
-// Bank row loads and stores of the DW. With NT (a bank in memory: it exceeds every cache)
-// the row's line is streamed with the non-temporal hint: the DW's second read of a written
-// row and its store are not used again within the step, and kept lines would displace the
-// rows the gather reuses. 16-byte vectors only; narrower ones load and store plainly.
-template <typename T, int V>
-constexpr bool kHasNt = (std::is_same<T, bf16>::value && V == 8) || (std::is_same<T, float>::value && V == 4);
-
-template <typename T, int V, bool NT>
-__device__ __forceinline__ typename Vec<T, V>::raw_t dw_load(const T *p) {
-    if constexpr (NT && kHasNt<T, V>) return Vec<T, V>::load_raw_nt(p);
-    else return Vec<T, V>::load_raw(p);
-}
-template <typename T, int V, bool NT>
-__device__ __forceinline__ void dw_store(T *p, const float (&o)[V]) {
-    if constexpr (NT && kHasNt<T, V>) Vec<T, V>::store_nt(p, o);
-    else Vec<T, V>::store(p, o);
 }
 
 // DW of one group with many members (>= kHotMin) by a whole wavefront: lane (r, p) =
@@ -809,12 +813,13 @@ __global__ __launch_bounds__(kP2Block) void phase2_kernel(P2Args a) {
             const float *rwt = wr ? gw : gr;
             const int rwidth = wr ? a.W : a.R, rwave = wr ? wave : wave - nww, rnw = wr ? nww : NW - nww;
             float *rdst = wr ? ub : ib;
+            const bool ntg = !SM && a.nt_gather;   // a bank in memory only
             if (((a.W | a.R) & 31) == 0)
                 gather_region<T, V, NV, RB ? 1 : 2, 4, SM>(bank, bst, rid, rwt, rwidth, nl, 0, nvs, rdst, pitch,
-                                                          rwave, rnw, lane, wr, vst, beta_c);
+                                                          rwave, rnw, lane, wr, vst, beta_c, ntg);
             else
                 gather_region<T, V, NV, RB ? 1 : Cfg::kBatch, 1, SM>(bank, bst, rid, rwt, rwidth, nl, 0, nvs, rdst,
-                                                                    pitch, rwave, rnw, lane, wr, vst, beta_c);
+                                                                    pitch, rwave, rnw, lane, wr, vst, beta_c, ntg);
         }
         lds_barrier();
 
@@ -1209,10 +1214,11 @@ __global__ __launch_bounds__(kP2Block) void phase2_team_kernel(P2Args a) {
                 float *rdst = wr ? ub + t0 * pitch : ib;
                 if (((a.W | a.R) & 31) == 0)
                     gather_region<T, V, NV, 2, 4, false>(gbank, hd, rid, rwt, rwidth, nlk, 0, nvs, rdst, pitch, rwave,
-                                                         rnw, lane, false, nullptr, nullptr);
+                                                         rnw, lane, false, nullptr, nullptr, a.nt_gather != 0);
                 else
                     gather_region<T, V, NV, Cfg::kBatch, 1, false>(gbank, hd, rid, rwt, rwidth, nlk, 0, nvs, rdst,
-                                                                   pitch, rwave, rnw, lane, false, nullptr, nullptr);
+                                                                   pitch, rwave, rnw, lane, false, nullptr, nullptr,
+                                                                   a.nt_gather != 0);
             }
             lds_barrier();
             if (mine) {   // u and inter of the piece's rows (zeros for padding tokens) to the exchange
@@ -1472,6 +1478,7 @@ hipError_t launch_phase2(const Problem &pb, const Slab &sl, int V, const P2Geom 
     a.off_stage0 = int32_t(L.off_stage0); a.off_stage1 = int32_t(L.off_stage1);
     a.off_xu = int32_t(L.off_xu);
     const int es = pb.dtype == 0 ? 4 : 2;
+    a.nt_gather = once_rows_streamed(pb) ? 1 : 0;
     void *args[] = {&a};
     if (g.team > 1) {
         // the planner's conditions, checked again where the kernel's indexing depends on them

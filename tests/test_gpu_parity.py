@@ -720,3 +720,30 @@ def test_hot_gram_kernels_give_the_same_bits(gpu, wl, monkeypatch):
         res[mode] = {k: gu.bits(v) for k, v in r.items()}
     for k in res["1"]:
         assert np.array_equal(res["1"][k], res["0"][k]), k
+
+
+@pytest.mark.parametrize("wl", [
+    small(P=8, T=300, C=128, hd=64, M=3000, W=32, R=32, ids="mixed", weight_scale=-1.0, ragged=True, index=90),
+    small(P=8, T=256, C=64, hd=128, M=5000, W=64, R=32, dtype="bf16", ids="zipf", weight_scale=-1.0, index=91),
+], ids=["f32_mixed", "bf16_zipf"])
+def test_non_temporal_gather_gives_the_same_bits(gpu, wl, monkeypatch):
+    """Rows that one entry of a chunk alone reads (marked by the partitioned Phase 1) load with
+    the non-temporal hint on large workloads: the same bits with it on and off, in memory mode
+    with one workgroup per slice and with teams, and the oracle agrees."""
+    from chunked_sparse_delta_amd import plan
+    inp = gu.generate(wl)
+    t = gu.to_torch(inp, gpu)
+    for k in ("SDM_P2_TEAM", "SDM_P2_NT"):
+        monkeypatch.delenv(k, raising=False)
+    monkeypatch.setenv("SDM_P2_GEOM", "8,0")
+    assert plan(wl.P, wl.T, wl.C, wl.W, wl.R, wl.hd, wl.M, t["bank"].dtype)["phase2_mode"] == "memory"
+    runs = {}
+    for team in ("0", "4"):
+        monkeypatch.setenv("SDM_P2_TEAM", team)
+        for nt in ("0", "1"):
+            monkeypatch.setenv("SDM_P2_NT", nt)
+            runs[(team, nt)] = gu.run(t, wl.C)
+    o_ref, b_ref = runs[("0", "0")]
+    for key, (o, b) in runs.items():
+        assert np.array_equal(gu.bits(o), gu.bits(o_ref)) and np.array_equal(gu.bits(b), gu.bits(b_ref)), key
+    gu.parity(*runs[("0", "1")], inp, wl.C, "non-temporal gather")
