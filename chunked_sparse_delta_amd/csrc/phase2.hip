@@ -187,12 +187,12 @@ template <typename T, int V>
 constexpr bool kHasNt = (std::is_same<T, bf16>::value && V == 8) || (std::is_same<T, float>::value && V == 4);
 
 template <typename T, int V, bool NT>
-__device__ __forceinline__ typename Vec<T, V>::raw_t dw_load(const T *p) {
+__device__ __forceinline__ typename Vec<T, V>::raw_t bank_load(const T *p) {
     if constexpr (NT && kHasNt<T, V>) return Vec<T, V>::load_raw_nt(p);
     else return Vec<T, V>::load_raw(p);
 }
 template <typename T, int V, bool NT>
-__device__ __forceinline__ void dw_store(T *p, const float (&o)[V]) {
+__device__ __forceinline__ void bank_store(T *p, const float (&o)[V]) {
     if constexpr (NT && kHasNt<T, V>) Vec<T, V>::store_nt(p, o);
     else Vec<T, V>::store(p, o);
 }
@@ -272,7 +272,7 @@ __device__ __forceinline__ void gather_region(const T *bank, int hd, const int32
             for (int q = 0; q < Q; ++q) {
                 const bool ok = id[u][q] >= 0 && vok;
                 const T *rp = at(bank, uint32_t(ok ? id[u][q] & kIdMask : 0) * uint32_t(hd) + (vok ? col : uint32_t(col0)));
-                raw[u][q] = ntg && (id[u][q] & kIdOnce) ? dw_load<T, V, true>(rp) : Vec<T, V>::load_raw(rp);
+                raw[u][q] = ntg && (id[u][q] & kIdOnce) ? bank_load<T, V, true>(rp) : Vec<T, V>::load_raw(rp);
             }
         // staged, ids and weights come from LDS: a wave-uniform branch skips the loads past
         // the last batch without making any memory load wait
@@ -391,7 +391,7 @@ __device__ __forceinline__ void big_issue(const T *bank, int hd, const int4 &rec
     const int32_t m0 = rec.y & 0xFFFF, n = ((rec.y >> 16) & 0xFF) + 1;
     const uint32_t col = uint32_t(col0 + p * V);
     // loads unconditional (in-bounds fallbacks), as in the gather
-    L.raw = dw_load<T, V, NT>(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
+    L.raw = bank_load<T, V, NT>(at(bank, uint32_t(rec.x) * uint32_t(hd) + (pok ? col : uint32_t(col0))));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int m = lane + 64 * q;
@@ -440,7 +440,7 @@ __device__ __forceinline__ void big_finish(T *bank, int hd, const int4 &rec, con
         const float dec = __int_as_float(rec.z);
 #pragma unroll
         for (int c = 0; c < V; ++c) b[c] = b[c] * dec + acc[c];
-        dw_store<T, V, NT>(at(bank, uint32_t(rec.x) * uint32_t(hd) + col), b);
+        bank_store<T, V, NT>(at(bank, uint32_t(rec.x) * uint32_t(hd) + col), b);
     }
 }
 
@@ -500,7 +500,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
             const bool sm = small(rec[u]);
-            raw[u] = dw_load<T, V, !SM>(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
+            raw[u] = bank_load<T, V, !SM>(at(bank, uint32_t(sm ? rec[u].x : 0) * uint32_t(bst) + (vok ? col : 0u)));
             const int32_t m0 = rec[u].y & 0xFFFF, n1 = (rec[u].y >> 16) & 0xFF;
             const bool two = sm && n1 > 0;
             const int2 x = *at(mrec, uint32_t(two ? m0 + 1 : 0));
@@ -581,7 +581,7 @@ __device__ __forceinline__ void dw_groups(T *bank, int bst, const int4 *grec, in
                     for (int c = 0; c < V; ++c) acc[c] = fmaf(cwv, dv[c], acc[c]);
                 }
             }
-            if (vok && sm) dw_store<T, V, !SM>(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
+            if (vok && sm) bank_store<T, V, !SM>(at(bank, uint32_t(rec[u].x) * uint32_t(bst) + col), acc);
         }
 #pragma unroll
         for (int u = 0; u < kB; ++u) rec[u] = nrec[u];
