@@ -587,7 +587,14 @@ __device__ __forceinline__ void cold_row_at(int C, int nl, const int4 *spk, cons
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int x0 = 0; i < nl && x0 < width; x0 += kWave) {
             const int x = x0 + lane;
-            const int4 r = x < width ? cr[int64_t(i) * width + x] : make_int4(0, 0, 0, 0);
+            // the row's own records are read once: streamed with the non-temporal hint, so
+            // that the earlier members' records, which several rows read, stay cached
+            int4 r = make_int4(0, 0, 0, 0);
+            if (x < width) {
+                typedef int32_t i4_t __attribute__((ext_vector_type(4)));
+                const i4_t v = __builtin_nontemporal_load(reinterpret_cast<const i4_t *>(cr + int64_t(i) * width + x));
+                r = make_int4(v[0], v[1], v[2], v[3]);
+            }
             // earlier members of the entry's group; at most C - 1 <= 255 when the write slots
             // of a token are distinct, clamped so that a call breaking that contract still
             // advances through its rounds
